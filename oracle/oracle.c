@@ -1,0 +1,298 @@
+/*
+ * oracle.c -- plain, slow CPU reference for the MoE expert layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library links, loads or
+ * calls this file; only the test suite, the smoke check and the benchmark's
+ * CPU-baseline leg do.  It shares no code, header, table or constant with
+ * the GPU kernels.
+ *
+ * What it computes, step by step, with the passage each step follows:
+ *
+ *   The source pages are
+ *     [MS]  "Muse Spark Open を段階的に分解する" (animemo.app), sections ①-⑭
+ *     [TS]  "TensorSharp ... Muse Spark 816B" benchmark article (devotd.net),
+ *           section "性能" / "Performance"
+ *     [DG]  "DGX Spark MoE inference optimizations" article (devotd.net),
+ *           section 2
+ *
+ *   O1  x is bf16; it is widened to double exactly.
+ *   O2  router score of token t for expert e: one matrix product of the
+ *       token vector with the router matrix, done in FP32 ([MS] section ⑧).
+ *       Reading: the score is the fp32 rounding of the exact dot product
+ *       (accumulated here in double in index order, every product exact).
+ *   O3  each token picks the 8 (k) best-scoring experts ([MS] section ⑧);
+ *       reading: order by score descending, then expert id ascending.
+ *   O4  the chosen experts' outputs are weighted by the router's scores and
+ *       the weights of one token sum to one ([MS] section ⑨ figure);
+ *       reading: softmax over the k chosen scores, in double.
+ *   O5  tokens are gathered per expert so each expert runs its batch at once
+ *       ([MS] section ⑫); reading: slot id t*k+j, ordered by
+ *       (expert asc, token asc); offsets = exclusive prefix of counts.
+ *   O6  each expert is gate / up / down ([MS] section ⑨): gate decides what
+ *       passes, up how much, down maps back.  Reading: SwiGLU,
+ *       a_f = silu(g_f) * u_f with silu(z) = z / (1 + exp(-z)).
+ *       Weights are block-scaled 4-bit ([MS] section ⑪, MXFP4 named in [DG]
+ *       section 2): FP4 E2M1 codes (sign bit 3, exponent bits 2..1 with bias
+ *       1, mantissa bit 0; exponent 0 is the subnormal 0 / 0.5) times an
+ *       E8M0 scale 2^(s-127) shared by 32 consecutive K elements of a row.
+ *       Byte b of a row holds element 2b in its low nibble, 2b+1 in its high.
+ *   O7  every expert output is normalised before the weighted sum
+ *       ([MS] section ⑨; [TS] "性能": the per-expert normalisation is why
+ *       tensor parallelism moves 8x the data).  Reading: RMSNorm over d with
+ *       eps inside the square root and no learned gain.
+ *   O8  y_t = sum_j w_tj * n_tj (j in order), and the gated residual
+ *       s = alpha * x + beta * y, alpha and beta learned per dimension
+ *       ([MS] section ③).  Output kept in double.
+ *
+ * Expert weight layout (per expert e, all row-major):
+ *   bytes  at e*(3dF/2):  gate [F][d/2] | up [F][d/2] | down [d][F/2]
+ *   scales at e*(3dF/32): gate [F][d/32] | up [F][d/32] | down [d][F/32]
+ *
+ * Every function is deterministic for any OpenMP thread count: parallel
+ * loops only run independent rows/slots and write disjoint outputs.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ---- O1 / O6: number formats ------------------------------------------ */
+
+double oracle_bf16_to_double(uint16_t bits)
+{
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* fp64 -> bf16 bits, round to nearest, ties to even (finite inputs). */
+uint16_t oracle_double_to_bf16(double v)
+{
+    /* bf16 keeps 8 significant bits; find the two neighbours and pick. */
+    if (v == 0.0) return signbit(v) ? 0x8000u : 0u;
+    if (isnan(v)) return 0x7FC0u;
+    int neg = v < 0;
+    double a = neg ? -v : v;
+    int ex;
+    frexp(a, &ex);                 /* a = m * 2^ex, m in [0.5, 1) */
+    int e = ex - 1;                /* a in [2^e, 2^(e+1)) */
+    if (e < -126) e = -126;        /* bf16 subnormal range: fixed quantum */
+    double q = ldexp(1.0, e - 7);  /* spacing of bf16 values near a */
+    double lo = floor(a / q) * q;
+    double hi = lo + q;
+    double r;
+    if (a - lo < hi - a) r = lo;
+    else if (a - lo > hi - a) r = hi;
+    else r = (fmod(lo / q, 2.0) == 0.0) ? lo : hi;
+    float f = (float)r;            /* exact: r has <= 8 significant bits */
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    uint16_t b = (uint16_t)(u >> 16);
+    if (isinf(f)) b = 0x7F80u;
+    return (uint16_t)(b | (neg ? 0x8000u : 0u));
+}
+
+double oracle_e2m1(unsigned code)
+{
+    unsigned s = (code >> 3) & 1u, e = (code >> 1) & 3u, m = code & 1u;
+    double mag = (e == 0) ? 0.5 * (double)m : ldexp(1.0 + 0.5 * (double)m, (int)e - 1);
+    return s ? -mag : mag;
+}
+
+double oracle_e8m0(unsigned s)
+{
+    if (s == 255u) return NAN;
+    return ldexp(1.0, (int)s - 127);
+}
+
+/* value tables filled from the two functions above when the library loads */
+static double e2m1_tab[16], e8m0_tab[256];
+
+__attribute__((constructor)) static void fill_tables(void)
+{
+    for (unsigned c = 0; c < 16; ++c) e2m1_tab[c] = oracle_e2m1(c);
+    for (unsigned s = 0; s < 256; ++s) e8m0_tab[s] = oracle_e8m0(s);
+}
+
+/* element i of a packed row of K elements */
+static double fp4_elem(const uint8_t *row, const uint8_t *srow, int64_t i)
+{
+    uint8_t byte = row[i / 2];
+    unsigned code = (i & 1) ? (unsigned)(byte >> 4) : (unsigned)(byte & 15u);
+    return e2m1_tab[code] * e8m0_tab[srow[i / 32]];
+}
+
+void oracle_dequant_rows(int64_t rows, int64_t K, const uint8_t *codes,
+                         const uint8_t *scales, double *out)
+{
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t i = 0; i < K; ++i)
+            out[r * K + i] = fp4_elem(codes + r * (K / 2), scales + r * (K / 32), i);
+}
+
+/* ---- O2: router scores ------------------------------------------------- */
+
+void oracle_router_scores(int T, int d, int E, const uint16_t *x, const float *wr,
+                          float *scores)
+{
+#pragma omp parallel for schedule(static)
+    for (int t = 0; t < T; ++t)
+        for (int e = 0; e < E; ++e) {
+            double acc = 0.0;
+            for (int i = 0; i < d; ++i)
+                acc += oracle_bf16_to_double(x[(int64_t)t * d + i]) * (double)wr[(int64_t)e * d + i];
+            scores[(int64_t)t * E + e] = (float)acc;
+        }
+}
+
+/* ---- O3 / O4: top-k and weights ---------------------------------------- */
+
+void oracle_topk_softmax(int T, int E, int k, const float *scores, int32_t *ids, double *w)
+{
+    char *taken = (char *)malloc((size_t)E);
+    for (int t = 0; t < T; ++t) {
+        const float *l = scores + (int64_t)t * E;
+        memset(taken, 0, (size_t)E);
+        for (int j = 0; j < k; ++j) {
+            int best = -1;
+            for (int e = 0; e < E; ++e) {
+                if (taken[e]) continue;
+                if (best < 0 || l[e] > l[best]) best = e;  /* ties keep the lower id */
+            }
+            taken[best] = 1;
+            ids[(int64_t)t * k + j] = best;
+        }
+        double l0 = (double)l[ids[(int64_t)t * k]];
+        double z = 0.0;
+        for (int j = 0; j < k; ++j) z += exp((double)l[ids[(int64_t)t * k + j]] - l0);
+        for (int j = 0; j < k; ++j)
+            w[(int64_t)t * k + j] = exp((double)l[ids[(int64_t)t * k + j]] - l0) / z;
+    }
+    free(taken);
+}
+
+/* ---- O5: grouping by expert --------------------------------------------- */
+
+void oracle_group(int T, int E, int k, const int32_t *ids, int32_t *counts,
+                  int32_t *offsets, int32_t *perm, int32_t *inv)
+{
+    for (int e = 0; e < E; ++e) counts[e] = 0;
+    for (int64_t s = 0; s < (int64_t)T * k; ++s) counts[ids[s]]++;
+    offsets[0] = 0;
+    for (int e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + counts[e];
+    int64_t pos = 0;
+    for (int e = 0; e < E; ++e)
+        for (int t = 0; t < T; ++t)
+            for (int j = 0; j < k; ++j)
+                if (ids[(int64_t)t * k + j] == e) {
+                    perm[pos] = t * k + j;
+                    inv[t * k + j] = (int32_t)pos;
+                    ++pos;
+                }
+}
+
+/* ---- O6 / O7: one expert on one token ----------------------------------- */
+
+/*
+ * x: d doubles.  w_e / s_e: the expert's packed bytes and scales.
+ * o_out (d) receives the down projection, n_out (d) its RMS-normalised form;
+ * either may be NULL.  Returns the mean square of o.
+ */
+double oracle_expert(int d, int F, const uint8_t *w_e, const uint8_t *s_e, const double *x,
+                     double eps, double *o_out, double *n_out)
+{
+    const uint8_t *gate = w_e;
+    const uint8_t *up = w_e + (int64_t)F * (d / 2);
+    const uint8_t *down = w_e + (int64_t)2 * F * (d / 2);
+    const uint8_t *sgate = s_e;
+    const uint8_t *sup = s_e + (int64_t)F * (d / 32);
+    const uint8_t *sdown = s_e + (int64_t)2 * F * (d / 32);
+
+    double *a = (double *)malloc(sizeof(double) * (size_t)F);
+    double *o = (double *)malloc(sizeof(double) * (size_t)d);
+    for (int f = 0; f < F; ++f) {
+        double g = 0.0, u = 0.0;
+        for (int i = 0; i < d; ++i) {
+            g += fp4_elem(gate + (int64_t)f * (d / 2), sgate + (int64_t)f * (d / 32), i) * x[i];
+            u += fp4_elem(up + (int64_t)f * (d / 2), sup + (int64_t)f * (d / 32), i) * x[i];
+        }
+        a[f] = g / (1.0 + exp(-g)) * u;
+    }
+    double ss = 0.0;
+    for (int i = 0; i < d; ++i) {
+        double acc = 0.0;
+        for (int f = 0; f < F; ++f)
+            acc += fp4_elem(down + (int64_t)i * (F / 2), sdown + (int64_t)i * (F / 32), f) * a[f];
+        o[i] = acc;
+        ss += acc * acc;
+    }
+    double ms = ss / (double)d;
+    double r = 1.0 / sqrt(ms + eps);
+    for (int i = 0; i < d; ++i) {
+        if (o_out) o_out[i] = o[i];
+        if (n_out) n_out[i] = o[i] * r;
+    }
+    free(a);
+    free(o);
+    return ms;
+}
+
+/* ---- whole layer on a set of tokens -------------------------------------- */
+
+/*
+ * Runs O1-O8 for the tokens listed in sel (n_sel of them; sel == NULL means
+ * all T tokens in order).  s_out: [n_sel][d] doubles.  ids_out [n_sel][k]
+ * and w_out [n_sel][k] receive the routing when non-NULL.
+ * Returns 0, or -1 on bad arguments / allocation failure.
+ */
+int oracle_moe_forward(int T, int d, int E, int F, int k, double eps,
+                       const uint16_t *x, const float *wr, const uint8_t *wpk,
+                       const uint8_t *sc, const float *alpha, const float *beta,
+                       int n_sel, const int32_t *sel, double *s_out,
+                       int32_t *ids_out, double *w_out)
+{
+    if (T < 0 || d <= 0 || E <= 0 || F <= 0 || k < 1 || k > E || d % 32 || F % 32) return -1;
+    if (sel == NULL) n_sel = T;
+    if (n_sel <= 0) return 0;
+    const int64_t eb = (int64_t)3 * d * F / 2, esb = (int64_t)3 * d * F / 32;
+
+    uint16_t *xs = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)n_sel * d);
+    float *scores = (float *)malloc(sizeof(float) * (size_t)n_sel * E);
+    int32_t *ids = (int32_t *)malloc(sizeof(int32_t) * (size_t)n_sel * k);
+    double *w = (double *)malloc(sizeof(double) * (size_t)n_sel * k);
+    double *n = (double *)malloc(sizeof(double) * (size_t)n_sel * k * d);
+    if (!xs || !scores || !ids || !w || !n) {
+        free(xs); free(scores); free(ids); free(w); free(n);
+        return -1;
+    }
+    for (int r = 0; r < n_sel; ++r) {
+        int t = sel ? sel[r] : r;
+        memcpy(xs + (int64_t)r * d, x + (int64_t)t * d, sizeof(uint16_t) * (size_t)d);
+    }
+    oracle_router_scores(n_sel, d, E, xs, wr, scores);
+    oracle_topk_softmax(n_sel, E, k, scores, ids, w);
+
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t q = 0; q < (int64_t)n_sel * k; ++q) {
+        int64_t r = q / k;
+        int e = ids[q];
+        double *xd = (double *)malloc(sizeof(double) * (size_t)d);
+        for (int i = 0; i < d; ++i) xd[i] = oracle_bf16_to_double(xs[r * d + i]);
+        oracle_expert(d, F, wpk + (int64_t)e * eb, sc + (int64_t)e * esb, xd, eps, NULL,
+                      n + q * d);
+        free(xd);
+    }
+
+    for (int64_t r = 0; r < n_sel; ++r)
+        for (int i = 0; i < d; ++i) {
+            double y = 0.0;
+            for (int j = 0; j < k; ++j) y += w[r * k + j] * n[(r * k + j) * d + i];
+            s_out[r * d + i] = (double)alpha[i] * oracle_bf16_to_double(xs[r * d + i]) +
+                               (double)beta[i] * y;
+        }
+    if (ids_out) memcpy(ids_out, ids, sizeof(int32_t) * (size_t)n_sel * k);
+    if (w_out) memcpy(w_out, w, sizeof(double) * (size_t)n_sel * k);
+    free(xs); free(scores); free(ids); free(w); free(n);
+    return 0;
+}

@@ -1,0 +1,77 @@
+"""The seeded input generator: determinism, value distributions, the router
+margin precondition and the skewed workload's load share."""
+import numpy as np
+
+from mixture_experts_gemm_amd import synth
+
+
+def test_deterministic_and_prefix_stable():
+    a = synth.make_layer("tiny")
+    b = synth.make_layer("tiny")
+    for f in ("x", "router_w", "w_packed", "scales", "alpha", "beta"):
+        np.testing.assert_array_equal(getattr(a, f), getattr(b, f))
+    w = synth.WORKLOADS["prefill"]
+    wr = synth.make_router(w)
+    x64 = synth.make_tokens(w, wr, T=64)
+    x16 = synth.make_tokens(w, wr, T=16)
+    np.testing.assert_array_equal(x64[:16], x16)
+
+
+def test_value_distributions():
+    L = synth.make_layer("tiny")
+    nib = np.concatenate([L.w_packed.ravel() & 15, L.w_packed.ravel() >> 4])
+    h = np.bincount(nib, minlength=16) / nib.size
+    assert np.all(np.abs(h - 1 / 16) < 0.01)
+    assert L.scales.min() == synth.SCALE_LO and L.scales.max() == synth.SCALE_HI
+    assert 0.5 <= L.alpha.min() and L.alpha.max() < 1.5
+    assert 0.5 <= L.beta.min() and L.beta.max() < 1.5
+    x = synth.bf16_bits_to_f32(L.x)
+    assert abs(x.mean()) < 0.05 and abs(x.std() - 1) < 0.05
+    assert abs(L.router_w.std() - 0.02) < 0.001
+
+
+def _gaps(x_bits, wr, k):
+    sc = synth.bf16_bits_to_f32(x_bits).astype(np.float64) @ wr.astype(np.float64).T
+    top = -np.sort(-sc, axis=1)[:, : k + 1]
+    return top[:, :-1] - top[:, 1:]
+
+
+def test_router_margin_holds():
+    for name, T in (("tiny", None), ("decode4", None), ("prefill", 512), ("skewed", 256)):
+        w = synth.WORKLOADS[name]
+        wr = synth.make_router(w)
+        x = synth.make_tokens(w, wr, T=T)
+        assert _gaps(x, wr, w.shape.k).min() >= synth.GAP_DEFAULT, name
+
+
+def test_margin_redraw_replaces_only_violators():
+    w = synth.WORKLOADS["prefill"]
+    wr = synth.make_router(w)
+    raw = synth.make_tokens(w, wr, T=2048, gap=0)
+    fixed = synth.make_tokens(w, wr, T=2048)
+    bad = _gaps(raw, wr, 8).min(axis=1) < synth.GAP_DEFAULT
+    assert bad.any()
+    np.testing.assert_array_equal(raw[~bad], fixed[~bad])
+    assert np.all(np.any(raw[bad] != fixed[bad], axis=1))
+
+
+def test_skewed_top8_share_near_40_percent():
+    w = synth.WORKLOADS["skewed"]
+    wr = synth.make_router(w)
+    x = synth.make_tokens(w, wr, T=4096)
+    assert np.all(synth.bf16_bits_to_f32(x[:, 0]) == 1.0)
+    sc = synth.bf16_bits_to_f32(x).astype(np.float64) @ wr.astype(np.float64).T
+    ids = np.argsort(-sc, axis=1, kind="stable")[:, :8]
+    cnt = np.sort(np.bincount(ids.ravel(), minlength=256))[::-1]
+    share = cnt[:8].sum() / ids.size
+    assert 0.37 <= share <= 0.43, share
+
+
+def test_uniform_prefill_loads():
+    w = synth.WORKLOADS["prefill"]
+    wr = synth.make_router(w)
+    x = synth.make_tokens(w, wr)
+    sc = synth.bf16_bits_to_f32(x).astype(np.float64) @ wr.astype(np.float64).T
+    ids = np.argsort(-sc, axis=1, kind="stable")[:, :8]
+    cnt = np.bincount(ids.ravel(), minlength=256)
+    assert cnt.sum() == 4096 * 8 and 80 <= cnt.min() and cnt.max() <= 180
