@@ -1,0 +1,229 @@
+#!/usr/bin/env python3
+"""Throughput of the MoE expert layer on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload decode4|decode1|prefill|skewed]
+
+One step = one moe_layer_forward call (router, top-k, grouping, gate/up +
+SwiGLU, down + row sums of squares, RMSNorm/combine/gate) over one batch of
+synthetic tokens whose inputs already sit in HBM.  Decode steps rotate over
+four independent weight sets (27 GB) and a pool of token rows, so the 256 MB
+Infinity Cache cannot serve the expert weights.
+
+Prints ONE JSON line: tokens/s for the named workload, the roofline of the
+dominant kernel (gate/up), measured live with HIP events recorded by the
+library on the benchmark's stream, the CPU oracle on a bounded sample, and
+the other shapes under "also".
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s (T=1/4 decode, T=4096 prefill) + % HBM / MFMA roofline"
+WORKLOAD_TEXT = {
+    "decode4": "Muse-shaped decode, 4 concurrent requests (T=4, d=8192, E=256, top-8, F=2048, MXFP4)",
+    "decode1": "Muse-shaped decode, single request (T=1, d=8192, E=256, top-8, F=2048, MXFP4)",
+    "prefill": "Muse-shaped prefill micro-batch (T=4096, d=8192, E=256, top-8, F=2048, MXFP4, uniform routing)",
+    "skewed": "Skewed-routing prefill (T=16384, Zipf(1.2) router bias, top-8 experts ~40% of slots)",
+}
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", default="decode4", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--also", default="decode1,prefill",
+                    help="comma list of extra workloads timed after the main one ('' for none)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    return ap.parse_args()
+
+
+def make_sets(name, nsets, device):
+    """Weight sets (layer 0 from the shared generator, the rest drawn on the GPU)."""
+    import numpy as np
+    import torch
+
+    from mixture_experts_gemm_amd import synth
+
+    w = synth.WORKLOADS[name]
+    s = w.shape
+    pool = 256 if s.T < 64 else s.T  # decode: a pool of token rows, 64 or more batches
+    host = synth.make_layer(w, layer=0, T=pool, threads=16)
+    sets = []
+    for i in range(nsets):
+        if i == 0:
+            W = torch.from_numpy(host.w_packed).to(device)
+            S = torch.from_numpy(host.scales).to(device)
+            wr = torch.from_numpy(host.router_w).to(device)
+            a = torch.from_numpy(host.alpha).to(device)
+            b = torch.from_numpy(host.beta).to(device)
+        else:
+            g = torch.Generator(device=device)
+            g.manual_seed(1000 * w.seed + i)
+            W = torch.randint(0, 256, (s.E, s.expert_bytes), dtype=torch.uint8, device=device, generator=g)
+            S = torch.randint(synth.SCALE_LO, synth.SCALE_HI + 1, (s.E, s.expert_scale_bytes),
+                              dtype=torch.uint8, device=device, generator=g)
+            wr = torch.from_numpy(synth.make_router(w, layer=i)).to(device)
+            a, b = (torch.from_numpy(v).to(device) for v in synth.make_gates(w, layer=i))
+        sets.append(dict(w=W, s=S, wr=wr, alpha=a, beta=b))
+    x = torch.from_numpy(host.x.view(np.int16)).to(device).view(torch.bfloat16)
+    return w, host, sets, x
+
+
+def time_workload(name, steps, warmup, device):
+    import torch
+
+    from mixture_experts_gemm_amd import binding as B
+    from mixture_experts_gemm_amd import roofline as R
+
+    decode = name.startswith("decode")
+    nsets = 4 if decode else 1
+    log(f"generating {name}: {nsets} weight set(s)")
+    w, host, sets, xpool = make_sets(name, nsets, device)
+    s = w.shape
+    T = s.T
+    npool = xpool.shape[0] // T
+    ws = B.workspace_for(T, s.d, s.E, s.F, s.k, device=device)
+    out = torch.empty(T, s.d, dtype=torch.bfloat16, device=device)
+    offsets = torch.empty(s.E + 1, dtype=torch.int32, device=device)
+
+    def call(i, debug=None):
+        st = sets[i % nsets]
+        xb = xpool[(i % npool) * T:(i % npool + 1) * T]
+        B.moe_layer_forward(xb, st["wr"], st["w"], st["s"], st["alpha"], st["beta"], s.k, F=s.F,
+                            s_out=out, workspace=ws, debug=debug)
+
+    # accounting pass (untimed): distinct experts per step, from the library's own grouping
+    U = []
+    for i in range(steps):
+        call(i, debug=dict(offsets=offsets))
+        off = offsets.cpu()
+        U.append(int(((off[1:] - off[:-1]) > 0).sum()))
+    assert torch.isfinite(out.float()).all(), "non-finite layer output"
+    for i in range(warmup):
+        call(i)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for a, b in evs:  # create the underlying HIP events before handing them over
+        a.record()
+        b.record()
+    torch.cuda.synchronize()
+    log(f"timing {name}: {steps} steps after {warmup} warmup")
+    t0 = time.perf_counter()
+    for i in range(steps):
+        call(i, debug=dict(events={"gemm1": evs[i]}))
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    g1_ms = sum(a.elapsed_time(b) for a, b in evs) / steps
+    out_ok = bool(torch.isfinite(out.float()).all())
+    S = T * s.k
+    u_mean = sum(U) / len(U)
+    res = dict(
+        T=T, steps=steps, ms_per_step=elapsed / steps * 1e3, tokens_per_s=T * steps / elapsed,
+        gemm1_ms=g1_ms, distinct_experts_mean=u_mean, finite=out_ok,
+    )
+    if decode:
+        nbytes = sum(R.mxfp4_w1_bytes(s.d, s.F) * u + T * s.d * 2 + S * s.F * 2 for u in U) / steps
+        achieved = nbytes / (g1_ms * 1e-3)
+        res["roofline"] = dict(bound="hbm", achieved=achieved / 1e9, peak=R.MI355X_HBM_BYTES_PER_S / 1e9,
+                               unit="GB/s", frac=achieved / R.MI355X_HBM_BYTES_PER_S, traffic=None,
+                               kernel="gemm1_kernel (gate/up + SwiGLU)",
+                               algorithmic_bytes_per_launch=nbytes)
+        lb = sum(R.layer_bytes(T, s.d, s.E, s.F, u) for u in U) / steps
+        res["layer_hbm_frac"] = lb / (elapsed / steps) / R.MI355X_HBM_BYTES_PER_S
+    else:
+        flops = R.gemm1_flops(S, s.d, s.F)
+        achieved = flops / (g1_ms * 1e-3)
+        res["roofline"] = dict(bound="mfma", achieved=achieved / 1e12, peak=R.MI355X_BF16_FLOPS_PER_S / 1e12,
+                               unit="TFLOP/s", frac=achieved / R.MI355X_BF16_FLOPS_PER_S, traffic=None,
+                               kernel="gemm1_kernel (gate/up + SwiGLU)",
+                               algorithmic_flops_per_launch=flops)
+        res["layer_mfma_frac"] = R.layer_flops(T, s.d, s.k, s.F) / (elapsed / steps) / R.MI355X_BF16_FLOPS_PER_S
+    log(json.dumps(res))
+    return res, host, T
+
+
+def cpu_baseline(host, T, seconds):
+    """The oracle as it is, on the host cores, over whole steps of the same workload."""
+    import oracle
+
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.moe_forward(host.x[:T], host.router_w, host.w_packed, host.scales, host.alpha,
+                           host.beta, host.k, eps=host.eps)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return dict(value=n * T / el, unit="tokens/s", cores=cores, kind="oracle",
+                sample=f"{n} full steps of the workload ({n * T} tokens, weight set 0), {el:.1f} s")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the layer's multi-GPU sharding is described in DESIGN.md but not built", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    device = "cuda:0"
+    torch.cuda.set_device(0)
+    decode = args.workload.startswith("decode")
+    steps = args.steps or (200 if decode else 20)
+    warmup = args.warmup if args.warmup is not None else (10 if decode else 3)
+    main_res, host, T = time_workload(args.workload, steps, warmup, device)
+    also = {}
+    for extra in [e for e in args.also.split(",") if e and e != args.workload]:
+        d2 = extra.startswith("decode")
+        r, _, _ = time_workload(extra, 200 if d2 else 10, 10 if d2 else 2, device)
+        also[extra] = r
+        torch.cuda.empty_cache()
+    cpu = None
+    if not args.no_cpu:
+        log("timing the CPU oracle")
+        cpu = cpu_baseline(host, T, args.cpu_seconds)
+    s = host.shape
+    line = {
+        "metric": METRIC,
+        "value": main_res["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": main_res["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD_TEXT[args.workload], "T": T, "d": s.d, "E": s.E,
+                   "k": s.k, "F": s.F, "weights": "MXFP4 (E2M1 + E8M0 per 32)",
+                   "weight_sets": 4 if decode else 1,
+                   "distinct_experts_mean": main_res["distinct_experts_mean"]},
+        "roofline": {k: v for k, v in main_res["roofline"].items()
+                     if k in ("bound", "achieved", "peak", "unit", "frac", "traffic")},
+        "cpu_baseline": cpu,
+        "also": {k: {kk: vv for kk, vv in v.items()} for k, v in also.items()},
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,160 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) MoE expert-layer library, libmoe.so.
+ *
+ * One call runs the whole expert layer of a sparse LLM on the GPU:
+ *
+ *   1. router scores  l[t][e] = sum_i x[t][i] * router_w[e][i], in fp32
+ *      ("Muse Spark Open を段階的に分解する" (animemo.app), section ⑧: one
+ *      matrix product per token, kept in FP32 because a wrong choice is
+ *      costly);
+ *   2. top-k experts per token, ordered by score (descending) then expert id
+ *      (ascending), weights = softmax over the k chosen scores (section ⑧:
+ *      top 8 of 256, no shared expert; section ⑨: outputs weighted by the
+ *      router's scores, weights of a token summing to one);
+ *   3. grouping of the token slots by expert, a stable counting sort by
+ *      (expert, token) (section ⑫: each expert's tokens are gathered and
+ *      computed together);
+ *   4. per expert, a SwiGLU FFN h = silu(x W_gate^T) * (x W_up^T),
+ *      o = h W_down^T on block-scaled 4-bit weights (section ⑨: gate, up and
+ *      down matrices; section ⑪: 4-bit values sharing a scale per block,
+ *      expanded to BF16 for the multiply);
+ *   5. RMS normalisation of every expert output over d, eps inside the
+ *      square root, no learned gain (section ⑨: each expert's output is
+ *      normalised before the weighted sum);
+ *   6. y[t] = sum_j w[t][j] * norm(o[t][j]) and the gated residual
+ *      s_out = alpha * x + beta * y with per-dimension alpha, beta
+ *      (section ③: s <- alpha*s + beta*(.)), rounded to bf16 (nearest even).
+ *
+ * All pointers passed to moe_layer_forward are DEVICE pointers on the
+ * current HIP device unless stated otherwise; the caller allocates and owns
+ * them, including the workspace.  The library allocates no device memory,
+ * keeps no pointer after returning, and queues all work asynchronously on
+ * `stream` (a hipStream_t; NULL = the null stream).  Buffers must stay valid
+ * until that work completes.  Calls on distinct workspaces are independent.
+ *
+ * Status codes: every entry point returns MOE_OK (0) or a negative MOE_ERR_*
+ * code and never aborts, prints or throws.  Argument errors are detected
+ * before anything is queued.  Faults inside kernels surface as errors of a
+ * later HIP synchronisation on the stream.  Weight contents are not checked:
+ * an E8M0 scale byte of 0xFF (NaN) gives undefined results.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    MOE_OK = 0,
+    MOE_ERR_NULL = -1,      /* a required pointer is NULL                        */
+    MOE_ERR_SHAPE = -2,     /* T < 0, d or F not a positive multiple of 128,
+                               E < 1 or E > 1024, k not in [1, E], eps < 0 or
+                               not finite, or sizes that overflow int32 indexing */
+    MOE_ERR_WORKSPACE = -3, /* workspace_bytes below moe_layer_workspace_size()  */
+    MOE_ERR_ARCH = -4,      /* current device is not gfx950                      */
+    MOE_ERR_HIP = -5        /* a HIP runtime call or kernel launch failed        */
+};
+
+typedef struct moe_dims {
+    int32_t T;   /* tokens in this call (0 = no-op)                 */
+    int32_t d;   /* token width (hidden size)                       */
+    int32_t E;   /* experts                                         */
+    int32_t F;   /* expert FFN width                                */
+    float eps;   /* RMSNorm epsilon, added to the mean square (1e-6) */
+} moe_dims_t;
+
+/* Stages of one forward call, in queue order. */
+enum {
+    MOE_STAGE_ROUTER = 0,  /* router scores                          */
+    MOE_STAGE_TOPK = 1,    /* top-k and softmax weights              */
+    MOE_STAGE_GROUP = 2,   /* counting sort by expert, tile list     */
+    MOE_STAGE_GEMM1 = 3,   /* gate/up projections + SwiGLU           */
+    MOE_STAGE_GEMM2 = 4,   /* down projection + row sums of squares  */
+    MOE_STAGE_COMBINE = 5, /* RMSNorm, weighted sum, gated residual  */
+    MOE_NUM_STAGES = 6
+};
+
+/*
+ * Optional copies of the routing decisions (device pointers, any may be
+ * NULL; pass NULL for the whole struct in production):
+ *   ids     int32 [T][k]  chosen experts, best first
+ *   weights fp32  [T][k]  softmax weights, same order
+ *   offsets int32 [E+1]   segment start of each expert; offsets[E] = T*k
+ *   perm    int32 [T*k]   slot id t*k+j at each grouped position
+ *   inv     int32 [T*k]   grouped position of each slot (inverse of perm)
+ * and optional timing events (hipEvent_t handles created by the caller, any
+ * may be NULL): stage_begin[s] / stage_end[s] are recorded on the stream
+ * right before the first and right after the last kernel of stage s.
+ */
+typedef struct moe_debug {
+    int32_t *ids;
+    float *weights;
+    int32_t *offsets;
+    int32_t *perm;
+    int32_t *inv;
+    void *stage_begin[MOE_NUM_STAGES];
+    void *stage_end[MOE_NUM_STAGES];
+} moe_debug_t;
+
+/*
+ * Bytes of device workspace moe_layer_forward needs for these sizes and k.
+ * Returns 0 when the sizes are invalid (see MOE_ERR_SHAPE).  The value only
+ * depends on (T, d, E, F, k); it grows linearly with T (the largest parts
+ * are the grouped intermediates: T*k*F*2 + T*k*d*2 bytes).
+ */
+size_t moe_layer_workspace_size(const moe_dims_t *dims, int32_t k);
+
+/*
+ * The expert layer, steps 1-6 above.
+ *
+ *   x               bf16 [T][d], row-major (bf16 = upper 16 bits of fp32)
+ *   router_w        fp32 [E][d], row-major
+ *   expert_w_packed uint8, expert e at byte offset e*(3*d*F/2):
+ *                     gate [F][d/2] | up [F][d/2] | down [d][F/2]
+ *                   each row holds its K elements as FP4 E2M1 codes, two per
+ *                   byte: element 2b in the low nibble of byte b, 2b+1 in the
+ *                   high nibble (sign bit 3, exponent bits 2..1 bias 1,
+ *                   mantissa bit 0)
+ *   scales          uint8 E8M0, expert e at byte offset e*(3*d*F/32):
+ *                     gate [F][d/32] | up [F][d/32] | down [d][F/32]
+ *                   scale byte s multiplies a block of 32 consecutive
+ *                   elements of one row by 2^(s-127)
+ *   alpha, beta     fp32 [d]
+ *   k               experts per token, 1 <= k <= E
+ *   s_out           bf16 [T][d]; may be the same buffer as x (in place)
+ *   workspace       device scratch of workspace_bytes, 256-byte aligned
+ *   stream          hipStream_t to queue on
+ *   debug           optional routing copies (see moe_debug_t) or NULL
+ *
+ * Deterministic: the same inputs and launch give bitwise identical outputs
+ * (no floating-point atomics, fixed reduction orders).
+ */
+int moe_layer_forward(const moe_dims_t *dims, const void *x, const float *router_w,
+                      const uint8_t *expert_w_packed, const uint8_t *scales,
+                      const float *alpha, const float *beta, int32_t k, void *s_out,
+                      void *workspace, size_t workspace_bytes, void *stream,
+                      const moe_debug_t *debug);
+
+/*
+ * Expands `rows` rows of K MXFP4 elements (layout as one matrix of
+ * expert_w_packed: codes [rows][K/2], scales [rows][K/32], device pointers)
+ * into bf16 out [rows][K] (device), with the same conversion the expert
+ * kernels use ("Muse Spark Open を段階的に分解する", section ⑪: 4-bit values
+ * are expanded to BF16 before the multiply).  Exact for every code and for
+ * scale bytes 1..254.  K must be a positive multiple of 32.
+ */
+int moe_dequant_mxfp4(const uint8_t *codes, const uint8_t *scales, int64_t rows, int32_t K,
+                      void *out_bf16, void *stream);
+
+/* Static, human-readable text for a status code. */
+const char *moe_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -1,0 +1,187 @@
+// api.hip -- the C ABI declared in include/moe.h: argument checks, the
+// workspace layout, and the kernel sequence on the caller's stream.
+#include <math.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "../../include/moe.h"
+#include "internal.h"
+
+namespace moe {
+
+static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+Workspace carve_workspace(const Shape &s, void *base)
+{
+    Workspace w;
+    memset(&w, 0, sizeof w);
+    const int64_t S = s.S();
+    const int chunk = group_chunk_tokens(s.k);
+    const int64_t nchunks = (s.T + chunk - 1) / chunk;
+    size_t off = 0;
+    char *b = static_cast<char *>(base);
+    auto take = [&](size_t bytes) -> void * {
+        void *p = b ? b + off : nullptr;
+        off += align256(bytes);
+        return p;
+    };
+    w.scores = (float *)take(sizeof(float) * (size_t)s.T * s.E);
+    w.ids = (int32_t *)take(sizeof(int32_t) * (size_t)S);
+    w.wts = (float *)take(sizeof(float) * (size_t)S);
+    w.chunk_base = (int32_t *)take(sizeof(int32_t) * (size_t)(nchunks * s.E));
+    w.counts = (int32_t *)take(sizeof(int32_t) * (size_t)s.E);
+    w.offsets = (int32_t *)take(sizeof(int32_t) * (size_t)(s.E + 1));
+    w.perm = (int32_t *)take(sizeof(int32_t) * (size_t)S);
+    w.inv = (int32_t *)take(sizeof(int32_t) * (size_t)S);
+    w.tiles = (Tile *)take(sizeof(Tile) * (size_t)max_tiles(s));
+    w.ntiles = (int32_t *)take(sizeof(int32_t) * 4);
+    w.h = (uint16_t *)take(sizeof(uint16_t) * (size_t)S * s.F);
+    w.o = (uint16_t *)take(sizeof(uint16_t) * (size_t)S * s.d);
+    w.ssq = (float *)take(sizeof(float) * (size_t)S * (s.d / kSsqCols));
+    w.bytes = off;
+    return w;
+}
+
+// Shape limits: every index fits int32 where the kernels use int32.
+static bool shape_ok(const moe_dims_t *dm, int32_t k)
+{
+    if (dm->T < 0 || dm->d <= 0 || dm->F <= 0 || dm->E < 1 || dm->E > 1024) return false;
+    if (dm->d % 128 || dm->F % 128) return false;
+    if (k < 1 || k > dm->E) return false;
+    if (!(dm->eps >= 0.0f) || !isfinite(dm->eps)) return false;
+    const int64_t S = (int64_t)dm->T * k;
+    if (S > INT32_MAX / 2) return false;
+    if (S * (int64_t)dm->F > ((int64_t)1 << 40) || S * (int64_t)dm->d > ((int64_t)1 << 40))
+        return false;
+    return true;
+}
+
+static Shape to_shape(const moe_dims_t *dm, int32_t k)
+{
+    Shape s;
+    s.T = dm->T;
+    s.d = dm->d;
+    s.E = dm->E;
+    s.F = dm->F;
+    s.k = k;
+    s.eps = dm->eps;
+    return s;
+}
+
+// gfx950 check, cached per device (0 unknown, 1 ok, 2 other arch).
+static std::atomic<int> g_arch_ok[64];
+
+static int check_arch()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+    if (dev < 0 || dev >= 64) return MOE_ERR_ARCH;
+    int st = g_arch_ok[dev].load(std::memory_order_relaxed);
+    if (st == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MOE_ERR_HIP;
+        st = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+        g_arch_ok[dev].store(st, std::memory_order_relaxed);
+    }
+    return st == 1 ? MOE_OK : MOE_ERR_ARCH;
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" size_t moe_layer_workspace_size(const moe_dims_t *dims, int32_t k)
+{
+    if (!dims || !shape_ok(dims, k)) return 0;
+    return carve_workspace(to_shape(dims, k), nullptr).bytes;
+}
+
+extern "C" int moe_layer_forward(const moe_dims_t *dims, const void *x, const float *router_w,
+                                 const uint8_t *expert_w_packed, const uint8_t *scales,
+                                 const float *alpha, const float *beta, int32_t k, void *s_out,
+                                 void *workspace, size_t workspace_bytes, void *stream,
+                                 const moe_debug_t *debug)
+{
+    if (!dims) return MOE_ERR_NULL;
+    if (!shape_ok(dims, k)) return MOE_ERR_SHAPE;
+    if (dims->T == 0) return MOE_OK;
+    if (!x || !router_w || !expert_w_packed || !scales || !alpha || !beta || !s_out || !workspace)
+        return MOE_ERR_NULL;
+    const Shape s = to_shape(dims, k);
+    const Workspace need = carve_workspace(s, nullptr);
+    if (workspace_bytes < need.bytes) return MOE_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return MOE_ERR_WORKSPACE;
+    int rc = check_arch();
+    if (rc != MOE_OK) return rc;
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const Workspace ws = carve_workspace(s, workspace);
+    const uint16_t *xb = static_cast<const uint16_t *>(x);
+    (void)hipGetLastError();  // start from a clean error state
+
+    auto mark = [&](void *const *evs, int stage) -> bool {
+        if (!debug || !evs[stage]) return true;
+        return hipEventRecord(static_cast<hipEvent_t>(evs[stage]), st) == hipSuccess;
+    };
+    auto stage = [&](int id, auto &&fn) -> bool {
+        if (!mark(debug ? debug->stage_begin : nullptr, id)) return false;
+        if (fn() != hipSuccess) return false;
+        return mark(debug ? debug->stage_end : nullptr, id);
+    };
+    uint16_t *out = static_cast<uint16_t *>(s_out);
+    if (!stage(MOE_STAGE_ROUTER, [&] { return launch_router(s, xb, router_w, ws.scores, st); }) ||
+        !stage(MOE_STAGE_TOPK, [&] { return launch_topk(s, ws.scores, ws.ids, ws.wts, st); }) ||
+        !stage(MOE_STAGE_GROUP, [&] { return launch_group(s, ws, st); }) ||
+        !stage(MOE_STAGE_GEMM1,
+               [&] { return launch_gemm1(s, ws, xb, expert_w_packed, scales, st); }) ||
+        !stage(MOE_STAGE_GEMM2, [&] { return launch_gemm2(s, ws, expert_w_packed, scales, st); }) ||
+        !stage(MOE_STAGE_COMBINE,
+               [&] { return launch_combine(s, ws, xb, alpha, beta, out, st); }))
+        return MOE_ERR_HIP;
+
+    if (debug) {
+        const size_t S4 = sizeof(int32_t) * (size_t)s.S();
+        struct {
+            void *dst;
+            const void *src;
+            size_t n;
+        } cp[5] = {{debug->ids, ws.ids, S4},
+                   {debug->weights, ws.wts, S4},
+                   {debug->offsets, ws.offsets, sizeof(int32_t) * (size_t)(s.E + 1)},
+                   {debug->perm, ws.perm, S4},
+                   {debug->inv, ws.inv, S4}};
+        for (auto &c : cp)
+            if (c.dst && hipMemcpyAsync(c.dst, c.src, c.n, hipMemcpyDeviceToDevice, st) != hipSuccess)
+                return MOE_ERR_HIP;
+    }
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+extern "C" int moe_dequant_mxfp4(const uint8_t *codes, const uint8_t *scales, int64_t rows,
+                                 int32_t K, void *out_bf16, void *stream)
+{
+    if (!codes || !scales || !out_bf16) return rows == 0 ? MOE_OK : MOE_ERR_NULL;
+    if (rows < 0 || K <= 0 || K % 32) return MOE_ERR_SHAPE;
+    if (rows == 0) return MOE_OK;
+    int rc = check_arch();
+    if (rc != MOE_OK) return rc;
+    (void)hipGetLastError();
+    if (launch_dequant(codes, scales, rows, K, static_cast<uint16_t *>(out_bf16),
+                       static_cast<hipStream_t>(stream)) != hipSuccess)
+        return MOE_ERR_HIP;
+    return MOE_OK;
+}
+
+extern "C" const char *moe_status_string(int status)
+{
+    switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL: return "a required pointer is NULL";
+    case MOE_ERR_SHAPE: return "invalid sizes (T, d, E, F, k or eps)";
+    case MOE_ERR_WORKSPACE: return "workspace too small or not 256-byte aligned";
+    case MOE_ERR_ARCH: return "current device is not gfx950";
+    case MOE_ERR_HIP: return "HIP runtime or kernel launch error";
+    default: return "unknown status";
+    }
+}

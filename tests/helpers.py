@@ -1,0 +1,77 @@
+"""Shared test helpers: device upload of generated inputs, the GPU call through
+the C ABI, and the floating-point comparison metrics.
+
+Tolerances for the layer output s (bf16) against the oracle's float64 s_ref:
+  rel_max  = max |a - b| / max(|b|, rms of b's row)   <= 2e-2
+  normwise = ||a - b||_F / ||b||_F                     <= 5e-3
+Routing ids, offsets, perm and inv must match exactly; weights to 1e-5.
+"""
+import numpy as np
+import torch
+
+REL_MAX_TOL = 2e-2
+NORMWISE_TOL = 5e-3
+WEIGHT_TOL = 1e-5
+
+
+def metrics(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    rms = np.sqrt(np.mean(b * b, axis=-1, keepdims=True))
+    rel = np.abs(a - b) / np.maximum(np.abs(b), rms)
+    return dict(rel_max=float(rel.max()),
+                normwise=float(np.linalg.norm(a - b) / np.linalg.norm(b)),
+                plain=float(np.abs(a - b).max() / np.abs(b).max()))
+
+
+def assert_close(a, b, label=""):
+    m = metrics(a, b)
+    assert m["rel_max"] <= REL_MAX_TOL and m["normwise"] <= NORMWISE_TOL, (label, m)
+    return m
+
+
+def bf16_tensor(bits: np.ndarray, device="cuda"):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(device).view(torch.bfloat16)
+
+
+def bf16_bits(t: torch.Tensor) -> np.ndarray:
+    return t.detach().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def upload(L, device="cuda"):
+    return dict(
+        x=bf16_tensor(L.x, device),
+        router_w=torch.from_numpy(L.router_w).to(device),
+        w=torch.from_numpy(L.w_packed).to(device),
+        s=torch.from_numpy(L.scales).to(device),
+        alpha=torch.from_numpy(L.alpha).to(device),
+        beta=torch.from_numpy(L.beta).to(device),
+    )
+
+
+def debug_buffers(T, E, k, device="cuda"):
+    S = T * k
+    return dict(ids=torch.empty(S, dtype=torch.int32, device=device),
+                weights=torch.empty(S, dtype=torch.float32, device=device),
+                offsets=torch.empty(E + 1, dtype=torch.int32, device=device),
+                perm=torch.empty(S, dtype=torch.int32, device=device),
+                inv=torch.empty(S, dtype=torch.int32, device=device))
+
+
+def run_layer(L, dev=None, debug=True, x=None, **kw):
+    """GPU layer through the C ABI.  Returns (s_out bits [T][d], debug numpy dict)."""
+    from mixture_experts_gemm_amd import binding as B
+    dev = dev or upload(L)
+    s = L.shape
+    xin = dev["x"] if x is None else x
+    T = xin.shape[0]
+    dbg = debug_buffers(T, s.E, s.k) if debug else None
+    out = B.moe_layer_forward(xin, dev["router_w"], dev["w"], dev["s"], dev["alpha"], dev["beta"],
+                              s.k, F=s.F, eps=L.eps, debug=dbg, **kw)
+    torch.cuda.synchronize()
+    res = None
+    if debug:
+        res = {n: t.cpu().numpy() for n, t in dbg.items()}
+        res["ids"] = res["ids"].reshape(T, s.k)
+        res["weights"] = res["weights"].reshape(T, s.k)
+    return bf16_bits(out), res

@@ -1,0 +1,78 @@
+"""CPU checks of the C ABI: the library loads, exports every function the
+header declares, sizes its workspace, names its status codes, and rejects bad
+arguments before queuing any GPU work."""
+import ctypes as C
+
+import pytest
+
+from mixture_experts_gemm_amd import binding as B
+
+
+@pytest.fixture(scope="module")
+def L():
+    return B.lib()
+
+
+def test_exports_every_declared_function(L):
+    names = B.declared_functions()
+    assert set(names) == {"moe_layer_workspace_size", "moe_layer_forward", "moe_dequant_mxfp4",
+                          "moe_status_string"}
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    for code in (0, -1, -2, -3, -4, -5):
+        assert B.moe_status_string(code) and B.moe_status_string(code) != "unknown status"
+    assert B.moe_status_string(7) == "unknown status"
+
+
+def test_workspace_size():
+    ws = B.moe_layer_workspace_size
+    assert ws(0, 256, 8, 512, 2) > 0
+    a, b = ws(64, 256, 8, 512, 2), ws(128, 256, 8, 512, 2)
+    assert 0 < a < b
+    big = ws(4096, 8192, 256, 2048, 8)
+    S = 4096 * 8
+    assert big >= S * 2048 * 2 + S * 8192 * 2
+    assert ws(64, 250, 8, 512, 2) == 0       # d not a multiple of 128
+    assert ws(64, 256, 8, 500, 2) == 0       # F not a multiple of 128
+    assert ws(64, 256, 8, 512, 9) == 0       # k > E
+    assert ws(64, 256, 8, 512, 0) == 0
+    assert ws(64, 256, 1025, 512, 2) == 0    # E > 1024
+    assert ws(-1, 256, 8, 512, 2) == 0
+    assert ws(64, 256, 8, 512, 2, eps=float("nan")) == 0
+
+
+def _call(dims, k=2, ws_bytes=1 << 30, null=None, ws_ptr=1 << 20):
+    p = C.c_void_p(1 << 20)  # never dereferenced: every case below fails the checks first
+    args = dict(x=p, router_w=p, w=p, s=p, alpha=p, beta=p, s_out=p, ws=C.c_void_p(ws_ptr))
+    if null:
+        args[null] = None
+    return B.lib().moe_layer_forward(C.byref(dims) if dims is not None else None, args["x"],
+                                     args["router_w"], args["w"], args["s"], args["alpha"],
+                                     args["beta"], k, args["s_out"], args["ws"], ws_bytes, None, None)
+
+
+def test_argument_errors():
+    good = B.moe_dims_t(64, 256, 8, 512, 1e-6)
+    assert _call(None) == B.MOE_ERR_NULL
+    for name in ("x", "router_w", "w", "s", "alpha", "beta", "s_out", "ws"):
+        assert _call(good, null=name) == B.MOE_ERR_NULL, name
+    assert _call(B.moe_dims_t(64, 200, 8, 512, 1e-6)) == B.MOE_ERR_SHAPE
+    assert _call(good, k=9) == B.MOE_ERR_SHAPE
+    assert _call(B.moe_dims_t(64, 256, 8, 512, -1.0)) == B.MOE_ERR_SHAPE
+    assert _call(good, ws_bytes=1024) == B.MOE_ERR_WORKSPACE
+    assert _call(good, ws_ptr=(1 << 20) + 64) == B.MOE_ERR_WORKSPACE
+    # T = 0 is a successful no-op even with NULL buffers
+    zero = B.moe_dims_t(0, 256, 8, 512, 1e-6)
+    assert _call(zero, null="x") == B.MOE_OK
+
+
+def test_dequant_argument_errors():
+    f = B.lib().moe_dequant_mxfp4
+    p = C.c_void_p(1 << 20)
+    assert f(None, p, 4, 64, p, None) == B.MOE_ERR_NULL
+    assert f(p, p, 4, 48, p, None) == B.MOE_ERR_SHAPE
+    assert f(p, p, -1, 64, p, None) == B.MOE_ERR_SHAPE
+    assert f(p, p, 0, 64, p, None) == B.MOE_OK

@@ -1,0 +1,239 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Routing (ids, offsets, perm, inv) must match bit for bit, weights to 1e-5,
+and the layer output within rel_max 2e-2 / normwise 5e-3 (tests/helpers.py).
+Small workloads are compared on every token; the full-size ones on every
+token for routing and on a seeded sample of tokens for the output (the layer
+is token-separable, so a sampled row is checked exactly as in a full run).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mixture_experts_gemm_amd import synth
+
+from helpers import (WEIGHT_TOL, assert_close, bf16_bits, bf16_tensor, metrics, run_layer,
+                     upload)
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print("[gpu-case]", *a, flush=True)
+
+
+def _check_routing(L, dbg, label):
+    r = oracle.route(L.x, L.router_w, L.k)
+    np.testing.assert_array_equal(dbg["ids"], r["ids"], err_msg=label)
+    np.testing.assert_array_equal(dbg["offsets"], r["offsets"], err_msg=label)
+    np.testing.assert_array_equal(dbg["perm"], r["perm"], err_msg=label)
+    np.testing.assert_array_equal(dbg["inv"], r["inv"], err_msg=label)
+    assert np.abs(dbg["weights"] - r["w"]).max() <= WEIGHT_TOL, label
+    return r
+
+
+def _check_tokens(L, out_bits, tokens, label):
+    ref, _, _ = oracle.moe_forward(L.x, L.router_w, L.w_packed, L.scales, L.alpha, L.beta, L.k,
+                                   eps=L.eps, tokens=np.asarray(tokens, np.int32))
+    got = synth.bf16_bits_to_f32(out_bits[tokens]).astype(np.float64)
+    m = assert_close(got, ref, label)
+    _say(label, "tokens", len(tokens), m)
+    return m
+
+
+# ------------------------------------------------------------------ dequant
+
+def test_dequant_every_code_and_scale():
+    from mixture_experts_gemm_amd import binding as B
+    K = 32
+    codes = np.array([(((2 * b + 1) % 16) << 4) | ((2 * b) % 16) for b in range(K // 2)], np.uint8)
+    rows = np.tile(codes, (254, 1))
+    scales = np.arange(1, 255, dtype=np.uint8).reshape(254, 1)
+    _say("dequant exhaustive")
+    out = B.moe_dequant_mxfp4(torch.from_numpy(rows).cuda(), torch.from_numpy(scales).cuda(), K)
+    got = synth.bf16_bits_to_f32(bf16_bits(out)).astype(np.float64)
+    want = oracle.dequant_rows(rows, scales, K)
+    np.testing.assert_array_equal(got, want)
+
+
+def test_dequant_random_rows():
+    from mixture_experts_gemm_amd import binding as B
+    rng = np.random.default_rng(7)
+    K = 2048
+    codes = rng.integers(0, 256, size=(33, K // 2), dtype=np.uint8)
+    scales = rng.integers(100, 150, size=(33, K // 32), dtype=np.uint8)
+    _say("dequant random")
+    out = B.moe_dequant_mxfp4(torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda(), K)
+    got = synth.bf16_bits_to_f32(bf16_bits(out)).astype(np.float64)
+    np.testing.assert_array_equal(got, oracle.dequant_rows(codes, scales, K))
+
+
+# ------------------------------------------------------------------ small workloads, every token
+
+@pytest.mark.parametrize("T", [64, 37, 1, 200])
+def test_tiny_layer_all_tokens(T):
+    L = synth.make_layer("tiny", T=T)
+    _say("tiny", T)
+    out, dbg = run_layer(L)
+    _check_routing(L, dbg, f"tiny T={T}")
+    _check_tokens(L, out, np.arange(T), f"tiny T={T}")
+
+
+@pytest.mark.parametrize("k", [1, 8])
+def test_tiny_k_extremes(k):
+    w = synth.custom_workload(T=50, d=256, E=8, k=k, F=512, seed=21)
+    L = synth.make_layer(w)
+    _say("tiny k", k)
+    out, dbg = run_layer(L)
+    _check_routing(L, dbg, f"k={k}")
+    _check_tokens(L, out, np.arange(50), f"k={k}")
+
+
+def test_all_tokens_to_one_expert_and_empty_experts():
+    # channel 0 of x carries 1.0 and expert 5's router column 0 a large bias:
+    # every token picks expert 5 first; 6 experts are pushed out of every top-2
+    w = synth.custom_workload(T=70, d=256, E=16, k=2, F=256, seed=22, zipf=True)
+    wr = synth.make_router(w)
+    wr[:, 0] = 0.0
+    wr[[0, 11, 12, 13, 14, 15], 0] = -50.0
+    wr[5, 0] = 50.0
+    x = synth.make_tokens(w, wr)
+    W, S = synth.make_experts(w)
+    a, b = synth.make_gates(w)
+    L = synth.LayerInputs(w.shape, x, wr, W, S, a, b, w.shape.k)
+    _say("one hot expert")
+    out, dbg = run_layer(L)
+    r = _check_routing(L, dbg, "hot expert")
+    assert np.all(dbg["ids"][:, 0] == 5)
+    assert (r["counts"] == 0).sum() >= 6
+    _check_tokens(L, out, np.arange(70), "hot expert")
+
+
+@pytest.mark.parametrize("name", ["decode1", "decode4"])
+def test_decode_all_tokens(name):
+    L = synth.make_layer(name)
+    _say(name)
+    out, dbg = run_layer(L)
+    _check_routing(L, dbg, name)
+    _check_tokens(L, out, np.arange(L.shape.T), name)
+
+
+# ------------------------------------------------------------------ invariants
+
+def test_gate_identity_bitwise():
+    L = synth.make_layer("tiny")
+    L.alpha[:] = 1.0
+    L.beta[:] = 0.0
+    _say("alpha=1 beta=0")
+    out, _ = run_layer(L, debug=False)
+    np.testing.assert_array_equal(out, L.x)
+
+
+def test_in_place_and_deterministic():
+    from mixture_experts_gemm_amd import binding as B
+    L = synth.make_layer("tiny")
+    dev = upload(L)
+    _say("determinism x3 + in place")
+    outs = [run_layer(L, dev, debug=False)[0] for _ in range(3)]
+    assert all(np.array_equal(outs[0], o) for o in outs[1:]), "reruns differ bitwise"
+    xin = dev["x"].clone()
+    B.moe_layer_forward(xin, dev["router_w"], dev["w"], dev["s"], dev["alpha"], dev["beta"], L.k,
+                        F=L.shape.F, s_out=xin)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bf16_bits(xin), outs[0])
+
+
+def test_down_scale_invariance():
+    L = synth.make_layer("tiny")
+    _say("scale invariance")
+    base, _ = run_layer(L, debug=False)
+    d, F = L.shape.d, L.shape.F
+    L.scales[:, F * d // 16:] += 1  # every expert's down rows doubled
+    moved, _ = run_layer(L, debug=False)
+    a = synth.bf16_bits_to_f32(moved).astype(np.float64)
+    b = synth.bf16_bits_to_f32(base).astype(np.float64)
+    m = metrics(a, b)
+    assert m["normwise"] <= 2e-3, m
+
+
+def test_t_zero_is_noop():
+    from mixture_experts_gemm_amd import binding as B
+    L = synth.make_layer("tiny", T=1)
+    dev = upload(L)
+    x0 = dev["x"][:0]
+    out = B.moe_layer_forward(x0, dev["router_w"], dev["w"], dev["s"], dev["alpha"], dev["beta"],
+                              L.k, F=L.shape.F)
+    assert out.shape == (0, L.shape.d)
+
+
+# ------------------------------------------------------------------ full sizes
+
+def _sample(T, n, seed, extra=()):
+    rng = np.random.default_rng(seed)
+    pick = set(rng.choice(T, size=min(n, T), replace=False).tolist()) | {0, T - 1} | set(extra)
+    return np.array(sorted(pick), np.int32)
+
+
+def test_prefill_full_size():
+    L = synth.make_layer("prefill")
+    _say("prefill T=4096")
+    out, dbg = run_layer(L)
+    r = _check_routing(L, dbg, "prefill")
+    _check_tokens(L, out, _sample(4096, 14, 2), "prefill")
+    assert int(r["counts"].sum()) == 4096 * 8
+
+
+def test_skewed_full_size():
+    L = synth.make_layer("skewed")
+    _say("skewed T=16384")
+    out, dbg = run_layer(L)
+    r = _check_routing(L, dbg, "skewed")
+    hot = int(np.argmax(r["counts"]))
+    share = np.sort(r["counts"])[::-1][:8].sum() / (16384 * 8)
+    _say("skewed top-8 share", share, "largest segment", r["counts"].max())
+    hot_tokens = np.nonzero(np.any(r["ids"] == hot, axis=1))[0][:4]
+    _check_tokens(L, out, _sample(16384, 10, 3, hot_tokens), "skewed")
+
+
+def test_stack_of_four_layers():
+    """Chained layers: each layer's bf16 output is the next layer's input.
+
+    The oracle runs its own chain (its bf16 rounding between layers); GPU and
+    oracle inputs of layer 2+ then differ by bf16 rounding, so routing must
+    agree exactly only where the oracle's top-(k+1) margin is >= 1e-2, and
+    errors are measured on tokens whose routing agreed at every layer.
+    """
+    w = synth.WORKLOADS["stack"]
+    T = w.shape.T
+    tokens = _sample(T, 12, 4)
+    x_gpu = None
+    ref_in = None
+    agree = np.ones(len(tokens), bool)
+    for layer in range(w.layers):
+        _say("stack layer", layer)
+        L = synth.make_layer(w, layer=layer, with_tokens=(layer == 0))
+        dev = upload(L)
+        xin = dev["x"] if layer == 0 else x_gpu
+        out, dbg = run_layer(L, dev, x=xin)
+        if layer == 0:
+            ref_in = L.x[tokens]
+            _check_routing(L, dbg, "stack layer 0")
+        sc = oracle.router_scores(ref_in, L.router_w)
+        ids_ref, _ = oracle.topk_softmax(sc, L.k)
+        top = -np.sort(-sc.astype(np.float64), axis=1)[:, : L.k + 1]
+        margin = (top[:, :-1] - top[:, 1:]).min(axis=1)
+        same = np.all(dbg["ids"][tokens] == ids_ref, axis=1)
+        assert np.all(same[margin >= 1e-2]), f"layer {layer}: confident routing differs"
+        agree &= same
+        s_ref, _, _ = oracle.moe_forward(ref_in, L.router_w, L.w_packed, L.scales, L.alpha,
+                                         L.beta, L.k, eps=L.eps)
+        got = synth.bf16_bits_to_f32(out[tokens]).astype(np.float64)
+        m = metrics(got[agree], s_ref[agree])
+        _say("stack layer", layer, "agree", int(agree.sum()), "of", len(tokens), m)
+        bound = 5e-3 if layer == 0 else 2e-2
+        assert m["normwise"] <= bound and m["rel_max"] <= 4 * bound, (layer, m)
+        ref_in = oracle.doubles_to_bf16(s_ref)
+        x_gpu = bf16_tensor(out)
+        del dev, L
+        torch.cuda.empty_cache()
