@@ -144,8 +144,9 @@ int moe_layer_forward(const moe_dims_t *dims, const void *x, const float *router
  * expert_w_packed: codes [rows][K/2], scales [rows][K/32], device pointers)
  * into bf16 out [rows][K] (device), with the same conversion the expert
  * kernels use ("Muse Spark Open を段階的に分解する", section ⑪: 4-bit values
- * are expanded to BF16 before the multiply).  Exact for every code and for
- * scale bytes 1..254.  K must be a positive multiple of 32.
+ * are expanded to BF16 before the multiply).  Exact for every code and
+ * scale bytes 1..252; above that the largest codes exceed the bf16 range and
+ * give +-inf.  K must be a positive multiple of 32.
  */
 int moe_dequant_mxfp4(const uint8_t *codes, const uint8_t *scales, int64_t rows, int32_t K,
                       void *out_bf16, void *stream);

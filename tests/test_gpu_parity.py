@@ -52,9 +52,12 @@ def test_dequant_every_code_and_scale():
     scales = np.arange(1, 255, dtype=np.uint8).reshape(254, 1)
     _say("dequant exhaustive")
     out = B.moe_dequant_mxfp4(torch.from_numpy(rows).cuda(), torch.from_numpy(scales).cuda(), K)
-    got = synth.bf16_bits_to_f32(bf16_bits(out)).astype(np.float64)
     want = oracle.dequant_rows(rows, scales, K)
-    np.testing.assert_array_equal(got, want)
+    # scale bytes 1..252: every value is representable in bf16 and must be exact
+    got = synth.bf16_bits_to_f32(bf16_bits(out)).astype(np.float64)
+    np.testing.assert_array_equal(got[:252], want[:252])
+    # 253, 254: 3 * 2^127 and up exceed bf16; the result is the bf16 rounding (+-inf)
+    np.testing.assert_array_equal(bf16_bits(out), oracle.doubles_to_bf16(want))
 
 
 def test_dequant_random_rows():
