@@ -17,8 +17,7 @@ Workspace carve_workspace(const Shape &s, void *base)
     Workspace w;
     memset(&w, 0, sizeof w);
     const int64_t S = s.S();
-    const int chunk = group_chunk_tokens(s.k);
-    const int64_t nchunks = (s.T + chunk - 1) / chunk;
+    const int64_t nchunks = num_chunks(s);
     size_t off = 0;
     char *b = static_cast<char *>(base);
     auto take = [&](size_t bytes) -> void * {
@@ -29,16 +28,17 @@ Workspace carve_workspace(const Shape &s, void *base)
     w.scores = (float *)take(sizeof(float) * (size_t)s.T * s.E);
     w.ids = (int32_t *)take(sizeof(int32_t) * (size_t)S);
     w.wts = (float *)take(sizeof(float) * (size_t)S);
+    w.masks = (uint64_t *)take(sizeof(uint64_t) * (size_t)(nchunks * s.E));
     w.chunk_base = (int32_t *)take(sizeof(int32_t) * (size_t)(nchunks * s.E));
     w.counts = (int32_t *)take(sizeof(int32_t) * (size_t)s.E);
     w.offsets = (int32_t *)take(sizeof(int32_t) * (size_t)(s.E + 1));
     w.perm = (int32_t *)take(sizeof(int32_t) * (size_t)S);
     w.inv = (int32_t *)take(sizeof(int32_t) * (size_t)S);
-    w.tiles = (Tile *)take(sizeof(Tile) * (size_t)max_tiles(s));
+    w.tiles = (Tile *)take(sizeof(Tile) * (size_t)max_tiles(s, 16));
     w.ntiles = (int32_t *)take(sizeof(int32_t) * 4);
     w.h = (uint16_t *)take(sizeof(uint16_t) * (size_t)S * s.F);
     w.o = (uint16_t *)take(sizeof(uint16_t) * (size_t)S * s.d);
-    w.ssq = (float *)take(sizeof(float) * (size_t)S * (s.d / kSsqCols));
+    w.ssq = (float *)take(sizeof(float) * (size_t)S * (s.d / 64));
     w.bytes = off;
     return w;
 }
@@ -130,14 +130,15 @@ extern "C" int moe_layer_forward(const moe_dims_t *dims, const void *x, const fl
         return mark(debug ? debug->stage_end : nullptr, id);
     };
     uint16_t *out = static_cast<uint16_t *>(s_out);
+    const Plan p = make_plan(s);
     if (!stage(MOE_STAGE_ROUTER, [&] { return launch_router(s, xb, router_w, ws.scores, st); }) ||
-        !stage(MOE_STAGE_TOPK, [&] { return launch_topk(s, ws.scores, ws.ids, ws.wts, st); }) ||
-        !stage(MOE_STAGE_GROUP, [&] { return launch_group(s, ws, st); }) ||
+        !stage(MOE_STAGE_TOPK, [&] { return launch_topk(s, p, ws, st); }) ||
+        !stage(MOE_STAGE_GROUP, [&] { return launch_group(s, p, ws, st); }) ||
         !stage(MOE_STAGE_GEMM1,
-               [&] { return launch_gemm1(s, ws, xb, expert_w_packed, scales, st); }) ||
-        !stage(MOE_STAGE_GEMM2, [&] { return launch_gemm2(s, ws, expert_w_packed, scales, st); }) ||
+               [&] { return launch_gemm1(s, p, ws, xb, expert_w_packed, scales, st); }) ||
+        !stage(MOE_STAGE_GEMM2, [&] { return launch_gemm2(s, p, ws, expert_w_packed, scales, st); }) ||
         !stage(MOE_STAGE_COMBINE,
-               [&] { return launch_combine(s, ws, xb, alpha, beta, out, st); }))
+               [&] { return launch_combine(s, p, ws, xb, alpha, beta, out, st); }))
         return MOE_ERR_HIP;
 
     if (debug) {

@@ -1,5 +1,5 @@
-// internal.h -- kernel launchers and the workspace layout shared by the
-// library's translation units (not part of the public ABI).
+// internal.h -- kernel launchers, the launch plan and the workspace layout
+// shared by the library's translation units (not part of the public ABI).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -17,10 +17,8 @@ struct Tile {
     int32_t pad;
 };
 
-// Rows per tile of the tile list.
-constexpr int kTileRows = 16;
-// Columns of o covered by one partial sum of squares.
-constexpr int kSsqCols = 16;
+// Tokens per chunk of the counting sort (one 64-bit token mask per expert).
+constexpr int kChunkTokens = 64;
 
 struct Shape {
     int T, d, E, F, k;
@@ -28,27 +26,43 @@ struct Shape {
     int64_t S() const { return (int64_t)T * k; }
 };
 
-// Tokens per chunk of the counting sort: chunk*k slot ids stay in LDS.
-inline int group_chunk_tokens(int k)
+// Which kernels run.  Few rows per expert (decode): 16-row tiles, one wave
+// per 16 output columns streaming weights.  Many rows per expert (prefill):
+// 128-row tiles staged through LDS and shared by a workgroup.
+struct Plan {
+    bool tiled;
+    int tile_rows;  // rows per tile of the tile list
+    int ssq_cols;   // columns of o per partial sum of squares
+    bool small_route;  // single-workgroup routing (T <= 64 and T*k <= 4096)
+};
+
+inline Plan make_plan(const Shape &s)
 {
-    int c = 2048 / k;
-    if (c > 256) c = 256;
-    if (c < 1) c = 1;
-    return c;
+    Plan p;
+    const int64_t S = s.S();
+    p.tiled = S >= (int64_t)32 * s.E && s.d % 256 == 0 && s.F % 128 == 0;
+    p.tile_rows = p.tiled ? 128 : 16;
+    p.ssq_cols = 64;  // both down kernels reduce o^2 over 64-column groups
+    p.small_route = s.T <= kChunkTokens && S <= 4096;
+    return p;
 }
 
-inline int64_t max_tiles(const Shape &s)
+// Upper bound of the tile count for any plan (16-row tiles give the most).
+inline int64_t max_tiles(const Shape &s, int tile_rows = 16)
 {
     int64_t S = s.S();
     int64_t u = S < s.E ? S : s.E;
-    return S / kTileRows + u + 1;
+    return S / tile_rows + u + 1;
 }
+
+inline int64_t num_chunks(const Shape &s) { return (s.T + kChunkTokens - 1) / kChunkTokens; }
 
 struct Workspace {
     float *scores;        // [T][E]
     int32_t *ids;         // [S]
     float *wts;           // [S]
-    int32_t *chunk_base;  // [nchunks][E]
+    uint64_t *masks;      // [nchunks][E] token bits of each expert in a chunk
+    int32_t *chunk_base;  // [nchunks][E] first grouped position of (chunk, expert)
     int32_t *counts;      // [E]
     int32_t *offsets;     // [E+1]
     int32_t *perm;        // [S]
@@ -57,7 +71,7 @@ struct Workspace {
     int32_t *ntiles;      // [1]
     uint16_t *h;          // bf16 [S][F]
     uint16_t *o;          // bf16 [S][d]
-    float *ssq;           // [S][d / kSsqCols]
+    float *ssq;           // [S][d / 64]
     size_t bytes;
 };
 
@@ -67,14 +81,13 @@ Workspace carve_workspace(const Shape &s, void *base);
 // ---- launchers (all asynchronous on `st`) ---------------------------------
 hipError_t launch_router(const Shape &s, const uint16_t *x, const float *wr, float *scores,
                          hipStream_t st);
-hipError_t launch_topk(const Shape &s, const float *scores, int32_t *ids, float *wts,
-                       hipStream_t st);
-hipError_t launch_group(const Shape &s, const Workspace &ws, hipStream_t st);
-hipError_t launch_gemm1(const Shape &s, const Workspace &ws, const uint16_t *x,
+hipError_t launch_topk(const Shape &s, const Plan &p, const Workspace &ws, hipStream_t st);
+hipError_t launch_group(const Shape &s, const Plan &p, const Workspace &ws, hipStream_t st);
+hipError_t launch_gemm1(const Shape &s, const Plan &p, const Workspace &ws, const uint16_t *x,
                         const uint8_t *wpk, const uint8_t *sc, hipStream_t st);
-hipError_t launch_gemm2(const Shape &s, const Workspace &ws, const uint8_t *wpk,
+hipError_t launch_gemm2(const Shape &s, const Plan &p, const Workspace &ws, const uint8_t *wpk,
                         const uint8_t *sc, hipStream_t st);
-hipError_t launch_combine(const Shape &s, const Workspace &ws, const uint16_t *x,
+hipError_t launch_combine(const Shape &s, const Plan &p, const Workspace &ws, const uint16_t *x,
                           const float *alpha, const float *beta, uint16_t *s_out,
                           hipStream_t st);
 hipError_t launch_dequant(const uint8_t *codes, const uint8_t *scales, int64_t rows, int K,

@@ -8,7 +8,13 @@
 //              (weights of a token sum to one: softmax over the chosen k);
 //   section ⑫  tokens are batched per expert and each expert's tokens are
 //              gathered and computed together (here: grouped order sorted by
-//              (expert, token), built without order-dependent atomics).
+//              (expert, token)).
+//
+// Grouping without order-dependent atomics: tokens are cut into chunks of
+// 64; for every (chunk, expert) an LDS 64-bit mask records which tokens of
+// the chunk chose the expert (atomic OR: the result does not depend on the
+// order the ORs land in).  A slot's place inside its expert segment is then
+// the segment base plus the popcount of the mask bits of earlier tokens.
 #include "device.h"
 #include "internal.h"
 
@@ -16,33 +22,63 @@ namespace moe {
 
 // ---------------------------------------------------------------------------
 // Router scores, few tokens: one workgroup per expert streams that expert's
-// fp32 router row once per token; fixed-order block reduction.
+// fp32 router row; all tokens are accumulated in registers and reduced once.
 // ---------------------------------------------------------------------------
+template <int NT>
 __global__ __launch_bounds__(256) void router_gemv_kernel(const uint16_t *__restrict__ x,
                                                           const float *__restrict__ wr,
                                                           float *__restrict__ scores, int T,
                                                           int d, int E)
 {
-    __shared__ float part[4];
+    // blockIdx.x: expert; blockIdx.y: group of NT tokens.  Every load of a
+    // 8192-wide slice is issued before the first multiply-add.
+    constexpr int R = 8;  // float4 per thread per 8192-element slice
+    __shared__ float part[4][NT];
     const int e = blockIdx.x;
+    const int t0 = blockIdx.y * NT;
     const float *w = wr + (int64_t)e * d;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    for (int t = 0; t < T; ++t) {
-        const uint16_t *xt = x + (int64_t)t * d;
-        float acc = 0.f;
-        for (int i = threadIdx.x * 4; i < d; i += 1024) {
-            float4 wq = *reinterpret_cast<const float4 *>(w + i);
-            uint2 xq = *reinterpret_cast<const uint2 *>(xt + i);
-            acc = fmaf(__uint_as_float(xq.x << 16), wq.x, acc);
-            acc = fmaf(__uint_as_float(xq.x & 0xFFFF0000u), wq.y, acc);
-            acc = fmaf(__uint_as_float(xq.y << 16), wq.z, acc);
-            acc = fmaf(__uint_as_float(xq.y & 0xFFFF0000u), wq.w, acc);
+    float acc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = 0.f;
+    for (int base = 0; base < d; base += 1024 * R) {
+        float4 wq[R];
+        uint2 xq[NT][R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int i = base + r * 1024 + threadIdx.x * 4;
+            wq[r] = i < d ? *reinterpret_cast<const float4 *>(w + i) : make_float4(0, 0, 0, 0);
         }
-        acc = wave_sum(acc);
-        if (lane == 0) part[wv] = acc;
-        __syncthreads();
-        if (threadIdx.x == 0) scores[(int64_t)t * E + e] = (part[0] + part[1]) + (part[2] + part[3]);
-        __syncthreads();
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const int64_t tt = min(t0 + t, T - 1);  // clamped: rows past T are computed, not stored
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const int i = base + r * 1024 + threadIdx.x * 4;
+                xq[t][r] = i < d ? *reinterpret_cast<const uint2 *>(x + tt * d + i) : make_uint2(0, 0);
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                float a = acc[t];
+                a = fmaf(__uint_as_float(xq[t][r].x << 16), wq[r].x, a);
+                a = fmaf(__uint_as_float(xq[t][r].x & 0xFFFF0000u), wq[r].y, a);
+                a = fmaf(__uint_as_float(xq[t][r].y << 16), wq[r].z, a);
+                a = fmaf(__uint_as_float(xq[t][r].y & 0xFFFF0000u), wq[r].w, a);
+                acc[t] = a;
+            }
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        const float v = wave_sum(acc[t]);
+        if (lane == 0) part[wv][t] = v;
+    }
+    __syncthreads();
+    if (threadIdx.x < NT && t0 + (int)threadIdx.x < T) {
+        const int t = threadIdx.x;
+        scores[(int64_t)(t0 + t) * E + e] = (part[0][t] + part[1][t]) + (part[2][t] + part[3][t]);
     }
 }
 
@@ -60,6 +96,8 @@ __device__ __forceinline__ void split3(float w, uint16_t &hi, uint16_t &mid, uin
     float r2 = r1 - bf16_to_f32(mid);
     lo = f32_to_bf16(r2);
 }
+
+__device__ __forceinline__ uint32_t pack2(uint16_t a, uint16_t b) { return a | (uint32_t)b << 16; }
 
 __global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t *__restrict__ x,
                                                           const float *__restrict__ wr,
@@ -84,22 +122,20 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t *__rest
         uint16_t hi[8], mi[8], lo[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) split3(wv[i], hi[i], mi[i], lo[i]);
-        uint4 bh, bm, bl;
-        bh.x = hi[0] | (uint32_t)hi[1] << 16; bh.y = hi[2] | (uint32_t)hi[3] << 16;
-        bh.z = hi[4] | (uint32_t)hi[5] << 16; bh.w = hi[6] | (uint32_t)hi[7] << 16;
-        bm.x = mi[0] | (uint32_t)mi[1] << 16; bm.y = mi[2] | (uint32_t)mi[3] << 16;
-        bm.z = mi[4] | (uint32_t)mi[5] << 16; bm.w = mi[6] | (uint32_t)mi[7] << 16;
-        bl.x = lo[0] | (uint32_t)lo[1] << 16; bl.y = lo[2] | (uint32_t)lo[3] << 16;
-        bl.z = lo[4] | (uint32_t)lo[5] << 16; bl.w = lo[6] | (uint32_t)lo[7] << 16;
-        bf16x8_t a = as_bf16x8(xa);
+        const uint4 bh = make_uint4(pack2(hi[0], hi[1]), pack2(hi[2], hi[3]), pack2(hi[4], hi[5]),
+                                    pack2(hi[6], hi[7]));
+        const uint4 bm = make_uint4(pack2(mi[0], mi[1]), pack2(mi[2], mi[3]), pack2(mi[4], mi[5]),
+                                    pack2(mi[6], mi[7]));
+        const uint4 bl = make_uint4(pack2(lo[0], lo[1]), pack2(lo[2], lo[3]), pack2(lo[4], lo[5]),
+                                    pack2(lo[6], lo[7]));
+        const bf16x8_t a = as_bf16x8(xa);
         acc = mfma16(a, as_bf16x8(bl), acc);
         acc = mfma16(a, as_bf16x8(bm), acc);
         acc = mfma16(a, as_bf16x8(bh), acc);
     }
-    // lane holds scores for tokens t0 + g*4 + i, expert e0 + r
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        int t = t0 + g * 4 + i;
+        const int t = t0 + g * 4 + i;
         if (t < T && ev) scores[(int64_t)t * E + e0 + r] = acc[i];
     }
 }
@@ -107,11 +143,13 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t *__rest
 hipError_t launch_router(const Shape &s, const uint16_t *x, const float *wr, float *scores,
                          hipStream_t st)
 {
-    if (s.T <= 32) {
-        router_gemv_kernel<<<s.E, 256, 0, st>>>(x, wr, scores, s.T, s.d, s.E);
+    if (s.T == 1) {
+        router_gemv_kernel<1><<<s.E, 256, 0, st>>>(x, wr, scores, s.T, s.d, s.E);
+    } else if (s.T <= 32) {
+        router_gemv_kernel<4><<<dim3(s.E, (s.T + 3) / 4), 256, 0, st>>>(x, wr, scores, s.T, s.d, s.E);
     } else {
-        int eblocks = (s.E + 15) / 16;
-        int64_t waves = (int64_t)((s.T + 15) / 16) * eblocks;
+        const int eblocks = (s.E + 15) / 16;
+        const int64_t waves = (int64_t)((s.T + 15) / 16) * eblocks;
         router_mfma_kernel<<<(unsigned)((waves + 3) / 4), 256, 0, st>>>(x, wr, scores, s.T, s.d,
                                                                           s.E, eblocks);
     }
@@ -119,15 +157,101 @@ hipError_t launch_router(const Shape &s, const uint16_t *x, const float *wr, flo
 }
 
 // ---------------------------------------------------------------------------
-// Top-k + softmax: one wave per token.  Each lane keeps E/64 scores in
-// registers; k rounds of a wave-wide arg-max under the order
-// (score descending, expert id ascending).
+// Top-k + softmax for one token, by one wave.  Each lane keeps SLOTS scores
+// (expert lane + 64*q); k rounds of a wave-wide arg-max under
+// (score desc, id asc) -- DPP steps inside rows of 16 lanes, then the four
+// row winners are compared from readlane.  The j-th choice is parked in lane
+// j%64, slot j/64; the softmax over the chosen scores is one wave sum.
+// NaN scores are treated as -inf so every choice is a valid expert id.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ bool better(float va, int ia, float vb, int ib)
 {
     return va > vb || (va == vb && ia < ib);
 }
 
+constexpr int kNone = 0x7FFFFFFF;
+
+template <int C>
+__device__ __forceinline__ void argmax_step(float &v, int &id)
+{
+    const float ov = dpp_f<C>(v);
+    const int oi = dpp_i<C>(id);
+    if (better(ov, oi, v, id)) { v = ov; id = oi; }
+}
+
+__device__ __forceinline__ void wave_argmax(float &v, int &id)
+{
+    argmax_step<0xB1>(v, id);
+    argmax_step<0x4E>(v, id);
+    argmax_step<0x141>(v, id);
+    argmax_step<0x140>(v, id);
+    float bv = readlane_f(v, 0);
+    int bi = __builtin_amdgcn_readlane(id, 0);
+#pragma unroll
+    for (int r = 16; r < 64; r += 16) {
+        const float ov = readlane_f(v, r);
+        const int oi = __builtin_amdgcn_readlane(id, r);
+        if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+    }
+    v = bv;
+    id = bi;
+}
+
+template <int SLOTS>
+__device__ void topk_row(const float *__restrict__ l, int E, int k, int32_t *__restrict__ ids_out,
+                         float *__restrict__ w_out, int32_t *sid_out, int lane)
+{
+    float v[SLOTS];
+#pragma unroll
+    for (int q = 0; q < SLOTS; ++q) {
+        const int e = lane + 64 * q;
+        const float x = e < E ? l[e] : -INFINITY;
+        v[q] = x == x ? x : -INFINITY;
+    }
+    uint32_t avail = 0;
+#pragma unroll
+    for (int q = 0; q < SLOTS; ++q)
+        if (lane + 64 * q < E) avail |= 1u << q;
+    float mysc[SLOTS];
+    int myid[SLOTS];
+    float top0 = 0.f;
+    for (int j = 0; j < k; ++j) {
+        float bv = -INFINITY;
+        int bi = kNone;
+#pragma unroll
+        for (int q = 0; q < SLOTS; ++q)
+            if (((avail >> q) & 1u) && better(v[q], lane + 64 * q, bv, bi)) {
+                bv = v[q];
+                bi = lane + 64 * q;
+            }
+        wave_argmax(bv, bi);
+        if ((bi & 63) == lane) avail &= ~(1u << (bi >> 6));
+        if (j == 0) top0 = bv;
+#pragma unroll
+        for (int q = 0; q < SLOTS; ++q)
+            if ((j >> 6) == q && (j & 63) == lane) { mysc[q] = bv; myid[q] = bi; }
+    }
+    float z = 0.f;
+    float ex[SLOTS];
+#pragma unroll
+    for (int q = 0; q < SLOTS; ++q) {
+        ex[q] = (lane + 64 * q < k) ? expf(mysc[q] - top0) : 0.f;
+        z += ex[q];
+    }
+    z = wave_sum(z);
+    const float inv = 1.0f / z;
+#pragma unroll
+    for (int q = 0; q < SLOTS; ++q) {
+        const int j = lane + 64 * q;
+        if (j < k) {
+            ids_out[j] = myid[q];
+            w_out[j] = ex[q] * inv;
+            if (sid_out) sid_out[j] = myid[q];
+        }
+    }
+}
+
+template <int SLOTS>
 __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ scores,
                                                    int32_t *__restrict__ ids,
                                                    float *__restrict__ wts, int T, int E, int k)
@@ -135,166 +259,214 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ sco
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
-    const float *l = scores + (int64_t)t * E;
-    float v[16];
-    uint32_t avail = 0;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        int e = lane + 64 * j;
-        v[j] = e < E ? l[e] : 0.f;
-        if (e < E) avail |= 1u << j;
-    }
-    float top0 = 0.f;
-    for (int j = 0; j < k; ++j) {
-        float bv = 0.f;
-        int bi = 0x7FFFFFFF;
-#pragma unroll
-        for (int q = 0; q < 16; ++q)
-            if ((avail >> q) & 1u) {
-                int e = lane + 64 * q;
-                if (bi == 0x7FFFFFFF || better(v[q], e, bv, bi)) { bv = v[q]; bi = e; }
-            }
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-            float ov = __shfl_xor(bv, off);
-            int oi = __shfl_xor(bi, off);
-            if (oi != 0x7FFFFFFF && (bi == 0x7FFFFFFF || better(ov, oi, bv, bi))) { bv = ov; bi = oi; }
-        }
-        if ((bi & 63) == lane) avail &= ~(1u << (bi >> 6));
-        if (j == 0) top0 = bv;
-        if (lane == 0) {
-            ids[(int64_t)t * k + j] = bi;
-            wts[(int64_t)t * k + j] = bv;  // the score for now; normalised below
-        }
-    }
-    // softmax over the chosen scores, in choice order (lane 0 owns the row)
-    if (lane == 0) {
-        float *wt = wts + (int64_t)t * k;
-        float z = 0.f;
-        for (int j = 0; j < k; ++j) z += expf(wt[j] - top0);
-        const float inv = 1.0f / z;
-        for (int j = 0; j < k; ++j) wt[j] = expf(wt[j] - top0) * inv;
-    }
-}
-
-hipError_t launch_topk(const Shape &s, const float *scores, int32_t *ids, float *wts,
-                       hipStream_t st)
-{
-    topk_kernel<<<(s.T + 3) / 4, 256, 0, st>>>(scores, ids, wts, s.T, s.E, s.k);
-    return hipGetLastError();
+    topk_row<SLOTS>(scores + (int64_t)t * E, E, k, ids + (int64_t)t * k, wts + (int64_t)t * k,
+                    nullptr, lane);
 }
 
 // ---------------------------------------------------------------------------
-// Grouping: stable counting sort of slots t*k+j by (expert, token).
-//   count:   per chunk of tokens, per-expert counts (LDS integer atomics;
-//            counts do not depend on the order the atomics land in)
-//   scan:    per expert, exclusive prefix over chunks; offsets = exclusive
-//            prefix over experts; tile list of <= kTileRows rows per tile
-//   scatter: per chunk, thread e walks the chunk's tokens in order and
-//            places every slot that chose e
+// Block-wide exclusive prefix sum of a[0..n), n <= 1024, in LDS, by 256
+// threads; returns the total.  Integer, so order-free.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void group_count_kernel(const int32_t *__restrict__ ids,
-                                                          int32_t *__restrict__ chunk_base,
-                                                          int T, int E, int k, int chunk)
+__device__ int block_exclusive_scan(int32_t *a, int n, int32_t *wtot)
 {
-    __shared__ int32_t hist[1024];
-    const int c = blockIdx.x;
-    for (int e = threadIdx.x; e < E; e += 256) hist[e] = 0;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    int v[4];
+    int sum = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int i = tid * 4 + q;
+        v[q] = i < n ? a[i] : 0;
+        sum += v[q];
+    }
+    int incl = sum;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(incl, off);
+        if (lane >= off) incl += y;
+    }
+    if (lane == 63) wtot[wv] = incl;
     __syncthreads();
-    int64_t s0 = (int64_t)c * chunk * k;
-    int64_t s1 = (int64_t)min(T, (c + 1) * chunk) * k;
-    for (int64_t s = s0 + threadIdx.x; s < s1; s += 256) atomicAdd(&hist[ids[s]], 1);
+    int base = 0;
+    for (int w = 0; w < wv; ++w) base += wtot[w];
+    const int total = wtot[0] + wtot[1] + wtot[2] + wtot[3];
+    int run = base + incl - sum;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int i = tid * 4 + q;
+        if (i < n) a[i] = run;
+        run += v[q];
+    }
     __syncthreads();
-    for (int e = threadIdx.x; e < E; e += 256) chunk_base[(int64_t)c * E + e] = hist[e];
+    return total;
 }
 
-__global__ __launch_bounds__(1024) void group_scan_kernel(int32_t *__restrict__ chunk_base,
-                                                          int32_t *__restrict__ counts,
-                                                          int32_t *__restrict__ offsets,
-                                                          Tile *__restrict__ tiles,
-                                                          int32_t *__restrict__ ntiles, int E,
-                                                          int nchunks)
+// offsets / counts / tile list from per-expert counts cnt[] (LDS, E entries);
+// cnt is replaced by the exclusive offsets.
+__device__ void finish_offsets(int32_t *cnt, int32_t *toff, int32_t *wtot, int E, int tile_rows,
+                               int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
+                               Tile *__restrict__ tiles, int32_t *__restrict__ ntiles, int *c_out)
 {
-    __shared__ int32_t cnt[1024];
-    __shared__ int32_t off[1025];
-    __shared__ int32_t toff[1025];
-    const int e = threadIdx.x;
-    int total = 0;
-    if (e < E) {
-        for (int c = 0; c < nchunks; ++c) {
-            int h = chunk_base[(int64_t)c * E + e];
-            chunk_base[(int64_t)c * E + e] = total;
-            total += h;
-        }
-        cnt[e] = total;
+    const int tid = threadIdx.x;
+    for (int e = tid; e < E; e += 256) {
+        c_out[e / 256] = cnt[e];
+        toff[e] = (cnt[e] + tile_rows - 1) / tile_rows;
     }
     __syncthreads();
-    if (e == 0) {
-        int acc = 0, tacc = 0;
-        for (int q = 0; q < E; ++q) {
-            off[q] = acc;
-            toff[q] = tacc;
-            acc += cnt[q];
-            tacc += (cnt[q] + kTileRows - 1) / kTileRows;
-        }
-        off[E] = acc;
-        toff[E] = tacc;
-        offsets[E] = acc;
-        *ntiles = tacc;
+    const int total = block_exclusive_scan(cnt, E, wtot);
+    const int ntot = block_exclusive_scan(toff, E, wtot);
+    if (tid == 0) {
+        offsets[E] = total;
+        *ntiles = ntot;
     }
-    __syncthreads();
-    if (e < E) {
-        counts[e] = total;
-        offsets[e] = off[e];
-        for (int c = 0; c < nchunks; ++c) chunk_base[(int64_t)c * E + e] += off[e];
-        int nt = (total + kTileRows - 1) / kTileRows;
+    for (int e = tid, q = 0; e < E; e += 256, ++q) {
+        const int c = c_out[q];
+        counts[e] = c;
+        offsets[e] = cnt[e];
+        const int nt = (c + tile_rows - 1) / tile_rows;
         for (int i = 0; i < nt; ++i) {
             Tile tl;
             tl.expert = e;
-            tl.row0 = off[e] + i * kTileRows;
-            tl.nrows = min(kTileRows, total - i * kTileRows);
+            tl.row0 = cnt[e] + i * tile_rows;
+            tl.nrows = min(tile_rows, c - i * tile_rows);
             tl.pad = 0;
             tiles[toff[e] + i] = tl;
         }
     }
 }
 
-__global__ __launch_bounds__(256) void group_scatter_kernel(const int32_t *__restrict__ ids,
-                                                            const int32_t *__restrict__ chunk_base,
-                                                            int32_t *__restrict__ perm,
-                                                            int32_t *__restrict__ inv, int T,
-                                                            int E, int k, int chunk)
+// ---------------------------------------------------------------------------
+// Few tokens (T <= 64, T*k <= 4096): top-k, weights, grouping and the tile
+// list in one workgroup.
+// ---------------------------------------------------------------------------
+template <int SLOTS>
+__global__ __launch_bounds__(256) void route_small_kernel(
+    const float *__restrict__ scores, int32_t *__restrict__ ids, float *__restrict__ wts,
+    int32_t *__restrict__ counts, int32_t *__restrict__ offsets, int32_t *__restrict__ perm,
+    int32_t *__restrict__ inv, Tile *__restrict__ tiles, int32_t *__restrict__ ntiles, int T,
+    int E, int k, int tile_rows)
 {
-    __shared__ int32_t cids[2048];
-    const int c = blockIdx.x;
-    const int t0 = c * chunk;
-    const int nt = min(T, t0 + chunk) - t0;
-    const int64_t s0 = (int64_t)t0 * k;
-    for (int q = threadIdx.x; q < nt * k; q += 256) cids[q] = ids[s0 + q];
+    __shared__ unsigned long long mask[1024];
+    __shared__ int32_t sid[4096];
+    __shared__ int32_t cnt[1024];
+    __shared__ int32_t toff[1024];
+    __shared__ int32_t wtot[4];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int S = T * k;
+    for (int e = tid; e < E; e += 256) mask[e] = 0ull;
+    for (int t = wv; t < T; t += 4)
+        topk_row<SLOTS>(scores + (int64_t)t * E, E, k, ids + (int64_t)t * k, wts + (int64_t)t * k,
+                        sid + t * k, lane);
     __syncthreads();
-    for (int e = threadIdx.x; e < E; e += 256) {
-        int pos = chunk_base[(int64_t)c * E + e];
-        for (int t = 0; t < nt; ++t)
-            for (int j = 0; j < k; ++j)
-                if (cids[t * k + j] == e) {
-                    int64_t slot = s0 + (int64_t)t * k + j;
-                    perm[pos] = (int32_t)slot;
-                    inv[slot] = pos;
-                    ++pos;
-                    break;
-                }
+    for (int s = tid; s < S; s += 256) atomicOr(&mask[sid[s]], 1ull << (s / k));
+    __syncthreads();
+    for (int e = tid; e < E; e += 256) cnt[e] = __popcll(mask[e]);
+    __syncthreads();
+    int c_own[4];
+    finish_offsets(cnt, toff, wtot, E, tile_rows, counts, offsets, tiles, ntiles, c_own);
+    for (int s = tid; s < S; s += 256) {
+        const int e = sid[s];
+        const int t = s / k;
+        const int pos = cnt[e] + __popcll(mask[e] & ((1ull << t) - 1ull));
+        perm[pos] = s;
+        inv[s] = pos;
     }
 }
 
-hipError_t launch_group(const Shape &s, const Workspace &ws, hipStream_t st)
+// ---------------------------------------------------------------------------
+// Many tokens: per-chunk masks, one scan block, per-chunk scatter.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void group_mask_kernel(const int32_t *__restrict__ ids,
+                                                         uint64_t *__restrict__ masks, int T,
+                                                         int E, int k)
 {
-    const int chunk = group_chunk_tokens(s.k);
-    const int nchunks = (s.T + chunk - 1) / chunk;
-    group_count_kernel<<<nchunks, 256, 0, st>>>(ws.ids, ws.chunk_base, s.T, s.E, s.k, chunk);
-    group_scan_kernel<<<1, 1024, 0, st>>>(ws.chunk_base, ws.counts, ws.offsets, ws.tiles,
-                                          ws.ntiles, s.E, nchunks);
-    group_scatter_kernel<<<nchunks, 256, 0, st>>>(ws.ids, ws.chunk_base, ws.perm, ws.inv, s.T,
-                                                  s.E, s.k, chunk);
+    __shared__ unsigned long long mask[1024];
+    const int c = blockIdx.x;
+    for (int e = threadIdx.x; e < E; e += 256) mask[e] = 0ull;
+    __syncthreads();
+    const int t0 = c * kChunkTokens;
+    const int nt = min(T - t0, kChunkTokens);
+    const int64_t s0 = (int64_t)t0 * k;
+    for (int q = threadIdx.x; q < nt * k; q += 256)
+        atomicOr(&mask[ids[s0 + q]], 1ull << (q / k));
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += 256) masks[(int64_t)c * E + e] = mask[e];
+}
+
+__global__ __launch_bounds__(256) void group_scan_kernel(
+    const uint64_t *__restrict__ masks, int32_t *__restrict__ chunk_base,
+    int32_t *__restrict__ counts, int32_t *__restrict__ offsets, Tile *__restrict__ tiles,
+    int32_t *__restrict__ ntiles, int E, int nchunks, int tile_rows)
+{
+    __shared__ int32_t cnt[1024];
+    __shared__ int32_t toff[1024];
+    __shared__ int32_t wtot[4];
+    const int tid = threadIdx.x;
+    for (int e = tid; e < E; e += 256) {
+        int run = 0;
+        for (int c = 0; c < nchunks; ++c) {
+            chunk_base[(int64_t)c * E + e] = run;
+            run += __popcll(masks[(int64_t)c * E + e]);
+        }
+        cnt[e] = run;
+    }
+    __syncthreads();
+    int c_own[4];
+    finish_offsets(cnt, toff, wtot, E, tile_rows, counts, offsets, tiles, ntiles, c_own);
+    for (int e = tid; e < E; e += 256) {
+        const int base = cnt[e];
+        for (int c = 0; c < nchunks; ++c) chunk_base[(int64_t)c * E + e] += base;
+    }
+}
+
+__global__ __launch_bounds__(256) void group_scatter_kernel(
+    const int32_t *__restrict__ ids, const uint64_t *__restrict__ masks,
+    const int32_t *__restrict__ chunk_base, int32_t *__restrict__ perm, int32_t *__restrict__ inv,
+    int T, int E, int k)
+{
+    const int c = blockIdx.x;
+    const int t0 = c * kChunkTokens;
+    const int nt = min(T - t0, kChunkTokens);
+    const int64_t s0 = (int64_t)t0 * k;
+    for (int q = threadIdx.x; q < nt * k; q += 256) {
+        const int64_t s = s0 + q;
+        const int e = ids[s];
+        const int tl = q / k;
+        const int64_t ce = (int64_t)c * E + e;
+        const int pos = chunk_base[ce] + __popcll(masks[ce] & ((1ull << tl) - 1ull));
+        perm[pos] = (int32_t)s;
+        inv[s] = pos;
+    }
+}
+
+template <int SLOTS>
+static void launch_topk_slots(const Shape &s, const Plan &p, const Workspace &ws, hipStream_t st)
+{
+    if (p.small_route) {
+        route_small_kernel<SLOTS><<<1, 256, 0, st>>>(ws.scores, ws.ids, ws.wts, ws.counts,
+                                                     ws.offsets, ws.perm, ws.inv, ws.tiles,
+                                                     ws.ntiles, s.T, s.E, s.k, p.tile_rows);
+    } else {
+        topk_kernel<SLOTS><<<(s.T + 3) / 4, 256, 0, st>>>(ws.scores, ws.ids, ws.wts, s.T, s.E, s.k);
+    }
+}
+
+hipError_t launch_topk(const Shape &s, const Plan &p, const Workspace &ws, hipStream_t st)
+{
+    if (s.E <= 64) launch_topk_slots<1>(s, p, ws, st);
+    else if (s.E <= 256) launch_topk_slots<4>(s, p, ws, st);
+    else launch_topk_slots<16>(s, p, ws, st);
+    return hipGetLastError();
+}
+
+hipError_t launch_group(const Shape &s, const Plan &p, const Workspace &ws, hipStream_t st)
+{
+    if (p.small_route) return hipSuccess;  // done by route_small_kernel
+    const int nchunks = (int)num_chunks(s);
+    group_mask_kernel<<<nchunks, 256, 0, st>>>(ws.ids, ws.masks, s.T, s.E, s.k);
+    group_scan_kernel<<<1, 256, 0, st>>>(ws.masks, ws.chunk_base, ws.counts, ws.offsets, ws.tiles,
+                                         ws.ntiles, s.E, nchunks, p.tile_rows);
+    group_scatter_kernel<<<nchunks, 256, 0, st>>>(ws.ids, ws.masks, ws.chunk_base, ws.perm, ws.inv,
+                                                  s.T, s.E, s.k);
     return hipGetLastError();
 }
 
