@@ -18,6 +18,8 @@
 // 16-byte weight load per lane is exactly one 32-element scale block, and
 // four MFMA steps consume it.  The order of k inside the instruction does not
 // matter because A and B use the same map.
+#include <type_traits>
+
 #include "device.h"
 #include "internal.h"
 
@@ -283,20 +285,29 @@ __global__ __launch_bounds__(256) void gemm2_decode_kernel(
 }
 
 // =========================================================================
-// Tiled kernels: tiles of <= 128 grouped rows.  The workgroup stages A
-// (128 rows x 128 K, bf16) through LDS, double-buffered, with an XOR swizzle
-// of the 16-byte slots so the MFMA fragment reads are conflict-free; every
-// wave reads its own weight rows straight from HBM/L2 into registers and
-// covers all 128 rows x 64 columns.  Workgroup w runs on XCD w % 8; tiles are
-// handed out in contiguous ranges per XCD so neighbouring tiles (same rows,
-// same expert) share that XCD's L2.
+// Tiled kernels: tiles of <= 128 grouped rows x 256 weight rows, all of K.
+//
+// Three-stage LDS ring per 128-wide K chunk, filled by direct-to-LDS loads
+// (global_load_lds_dwordx4: each lane's 16 bytes land at base + 16*lane):
+//   A  128 rows x 256 B bf16, 16-byte slot c of row r stored at c ^ (r & 15)
+//      so the MFMA fragment reads of 16 rows hit 16 different slots;
+//   B  256 weight rows x 64 B of FP4 codes, row-major (a fragment read of
+//      16 rows x 4 lanes is one contiguous KB);
+//   S  256 x 4 E8M0 bytes (the chunk's 4 scale blocks of each row).
+// Chunk kc+2 is in flight while chunk kc is multiplied.  Waits are explicit
+// (s_waitcnt on the wave's own outstanding loads, then s_barrier): a plain
+// __syncthreads would also drain the loads of the next chunk.
+//
+// Waves: 2 x 2, each 64 rows x 128 weight rows (4 x 8 MFMA blocks).
+// Workgroup w runs on XCD w % 8; tiles are handed out in contiguous ranges
+// per XCD so neighbouring tiles (same rows, same expert) share its L2.
 // =========================================================================
-#ifndef MOE_TILED_WAVES
-#define MOE_TILED_WAVES 2
-#endif
 constexpr int kTM = 128;                // rows per tile
-constexpr int kSlots = kKStep / 8;      // 16-byte slots per A row per chunk
-constexpr int kMB = kTM / 16;           // 16-row MFMA blocks per tile
+constexpr int kTN = 256;                // weight rows per tile
+constexpr int kSlots = kKStep / 8;      // 16-byte slots per A row per chunk (16)
+constexpr int kALoads = kTM * kSlots / 256;        // 16-byte A loads per thread per chunk (8)
+constexpr int kBLoads = kTN * (kKStep / 32) / 256; // 16-byte B loads per thread per chunk (4)
+constexpr int kChunkLoads = kALoads + kBLoads + 1; // + one 4-byte scale load
 
 // Contiguous per-XCD tile ranges; returns false for surplus workgroups.
 __device__ __forceinline__ bool xcd_tile(int total, int &idx)
@@ -308,166 +319,215 @@ __device__ __forceinline__ bool xcd_tile(int total, int &idx)
     return idx < total;
 }
 
-template <bool GATE_UP>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MOE_TILED_WAVES, MOE_TILED_WAVES))) void gemm_tiled_kernel(
-    const uint16_t *__restrict__ act, const int32_t *__restrict__ perm,
-    const Tile *__restrict__ tiles, const int32_t *__restrict__ ntiles,
-    const uint8_t *__restrict__ wpk, const uint8_t *__restrict__ sc,
-    uint16_t *__restrict__ out, float *__restrict__ ssq, int d, int F, int k, int ntn)
+// LDS byte offset of a __shared__ object.
+__device__ __forceinline__ uint32_t lds_off(const void *p)
 {
-    __shared__ uint4 As[2][kTM * kSlots];  // 64 KB
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void *)p;
+}
+
+// Direct-to-LDS loads.  Issued from inline asm so the compiler does not
+// guard later LDS reads with a blanket vmcnt(0) (it cannot tell the ring
+// stages apart); every wait on these loads is the explicit one in
+// chunk_sync().  lds (wave-uniform) is the byte offset the lane-0 data lands
+// at; lane i's data lands at lds + i*size.  The kernels using these read no
+// M0-dependent instruction of their own.
+__device__ __forceinline__ void dma16(const void *g, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :: "s"(lds), "v"(g) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void *g, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
+                 :: "s"(lds), "v"(g) : "memory", "m0");
+}
+
+// Wait until at most N of this wave's loads are outstanding, then barrier.
+template <int N>
+__device__ __forceinline__ void chunk_sync()
+{
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" :: "n"(N) : "memory");
+}
+
+struct PipeArgs {
+    const uint16_t *act;   // A rows: x (gathered) or h (grouped order)
+    const int32_t *perm;
+    const Tile *tiles;
+    const int32_t *ntiles;
+    const uint8_t *wpk;
+    const uint8_t *sc;
+    uint16_t *out;         // h or o
+    float *ssq;
+    int d, F, k, ntn;
+};
+
+template <bool GATE_UP>
+__global__ __launch_bounds__(256) void gemm_tiled_kernel(const PipeArgs pa)
+{
+    __shared__ uint4 As0[kTM * kSlots], As1[kTM * kSlots], As2[kTM * kSlots];
+    __shared__ uint4 Bs0[kTN * 4], Bs1[kTN * 4], Bs2[kTN * 4];
+    __shared__ uint32_t Ss0[kTN], Ss1[kTN], Ss2[kTN];
+
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int d = pa.d, F = pa.F;
     int idx;
-    if (!xcd_tile(*ntiles * ntn, idx)) return;
-    const int mt = idx / ntn, nt = idx - mt * ntn;
-    const Tile tl = tiles[mt];
-    const int mb_act = (tl.nrows + 15) >> 4;
-    const int K = GATE_UP ? d : F;            // contraction length
-    const int row_elems = GATE_UP ? d : F;    // A row length
+    if (!xcd_tile(*pa.ntiles * pa.ntn, idx)) return;
+    const int mt = idx / pa.ntn, nt = idx - mt * pa.ntn;
+    const Tile tl = pa.tiles[mt];
+    const int K = GATE_UP ? d : F;
     const int64_t ebytes = (int64_t)3 * d * F / 2, escales = (int64_t)3 * d * F / 32;
 
-    // A loader: thread copies 16-byte slot ac of rows ar + 16*i
-    const int ar = tid >> 4, ac = tid & 15;
-    int64_t aoff[kMB];
+    // ---- load assignment ----------------------------------------------------
+    // A: load i of this wave fills LDS rows 16i + 4*wv + lane/16, stored slot lane%16
+    const int a_rlo = 4 * wv + (lane >> 4);                 // row & 15 for every i
+    const int a_slot = (lane & 15) ^ a_rlo;                 // logical 16-byte slot
+    const uint16_t *asrc[kALoads];
 #pragma unroll
-    for (int i = 0; i < kMB; ++i) {
-        const int r = ar + 16 * i;
-        if (r < tl.nrows) {
-            const int64_t src = GATE_UP ? (int64_t)(perm[tl.row0 + r] / k) : (int64_t)(tl.row0 + r);
-            aoff[i] = src * row_elems + ac * 8;
-        } else {
-            aoff[i] = -1;
-        }
+    for (int i = 0; i < kALoads; ++i) {
+        const int r = 16 * i + a_rlo;
+        const int rr = r < tl.nrows ? r : 0;
+        const int64_t row = GATE_UP ? (int64_t)(pa.perm[tl.row0 + rr] / pa.k) : (int64_t)(tl.row0 + rr);
+        asrc[i] = pa.act + row * (GATE_UP ? d : F) + a_slot * 8;
     }
-    // B rows of this wave: 4 blocks of 16 columns
-    const int n = lane & 15, g = lane >> 4;
-    const uint8_t *bp[4];
-    const uint8_t *sp[4];
-    const uint8_t *eb = wpk + tl.expert * ebytes;
-    const uint8_t *es = sc + tl.expert * escales;
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-        int64_t row;
+    // B: load i fills LDS rows 16*(4i + wv) + lane/4, slot lane%4; scale: row 64*wv + lane
+    auto wrow_of = [&](int rho) -> int64_t {
         if (GATE_UP) {
-            // nb 0,1: gate features f0+16*nb+n; nb 2,3: up rows of the same features
-            const int f = nt * 128 + wv * 32 + (nb & 1) * 16 + n;
-            row = nb < 2 ? f : F + f;
-            bp[nb] = eb + row * (d / 2) + g * 16;
-            sp[nb] = es + row * (d / 32) + g;
-        } else {
-            row = (int64_t)nt * 256 + wv * 64 + nb * 16 + n;
-            bp[nb] = eb + (int64_t)2 * F * (d / 2) + row * (F / 2) + g * 16;
-            sp[nb] = es + (int64_t)2 * F * (d / 32) + row * (F / 32) + g;
+            const int f = nt * 128 + (rho >> 7) * 64 + ((rho >> 4) & 3) * 16 + (rho & 15);
+            return ((rho >> 6) & 1) ? (int64_t)F + f : (int64_t)f;  // blocks 4..7 of a half: up
         }
-    }
-
-    floatx4_t acc[kMB][4];
-#pragma unroll
-    for (int mb = 0; mb < kMB; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-
-    const int nk = K / kKStep;
-    uint4 areg[kMB];
-    uint4 b[4];
-    uint32_t sb[4];
-    auto load_a = [&](int kc) {
-#pragma unroll
-        for (int i = 0; i < kMB; ++i)
-            areg[i] = aoff[i] >= 0 ? *reinterpret_cast<const uint4 *>(act + aoff[i] + kc * kKStep)
-                                   : make_uint4(0, 0, 0, 0);
+        return (int64_t)nt * kTN + rho;
     };
-    auto store_a = [&](int stage) {
+    const uint8_t *eb = pa.wpk + tl.expert * ebytes;
+    const uint8_t *es = pa.sc + tl.expert * escales;
+    const int64_t wbase = GATE_UP ? 0 : (int64_t)2 * F * (d / 2);
+    const int64_t sbase = GATE_UP ? 0 : (int64_t)2 * F * (d / 32);
+    const uint8_t *bsrc[kBLoads];
 #pragma unroll
-        for (int i = 0; i < kMB; ++i) As[stage][(ar + 16 * i) * kSlots + (ac ^ ar)] = areg[i];
-    };
-    load_a(0);
-    store_a(0);
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-        b[nb] = *reinterpret_cast<const uint4 *>(bp[nb]);
-        sb[nb] = sp[nb][0];
+    for (int i = 0; i < kBLoads; ++i) {
+        const int rho = 16 * (4 * i + wv) + (lane >> 2);
+        bsrc[i] = eb + wbase + wrow_of(rho) * (K / 2) + (lane & 3) * 16;
     }
-    for (int kc = 0; kc < nk; ++kc) {
-        __syncthreads();
-        uint4 bn[4];
-        uint32_t sbn[4];
-        const bool more = kc + 1 < nk;
-        if (more) {
-            load_a(kc + 1);
+    const uint8_t *ssrc = es + sbase + wrow_of(64 * wv + lane) * (K / 32);
+
+    const int wvu = __builtin_amdgcn_readfirstlane(wv);  // wave-uniform copy for LDS bases
+    // every lane issues every load (rows past nrows re-read row 0), so each
+    // wave has exactly kChunkLoads loads per chunk for the vmcnt accounting
+    auto issue = [&](int kc, uint4 *As, uint4 *Bs, uint32_t *Ss) {
 #pragma unroll
-            for (int nb = 0; nb < 4; ++nb) {
-                bn[nb] = *reinterpret_cast<const uint4 *>(bp[nb] + (int64_t)(kc + 1) * (kKStep / 2));
-                sbn[nb] = sp[nb][(kc + 1) * (kKStep / 32)];
-            }
+        for (int i = 0; i < kALoads; ++i)
+            dma16(asrc[i] + kc * kKStep, lds_off(As + (16 * i + 4 * wvu) * kSlots));
+#pragma unroll
+        for (int i = 0; i < kBLoads; ++i)
+            dma16(bsrc[i] + kc * (kKStep / 2), lds_off(Bs + (4 * i + wvu) * 64));
+        dma4(ssrc + kc * (kKStep / 32), lds_off(Ss + 64 * wvu));
+    };
+
+    // ---- compute assignment -------------------------------------------------
+    const int wm = wv & 1, wn = wv >> 1;
+    const int n16 = lane & 15, g = lane >> 4;
+    int mb_act = (tl.nrows - wm * 64 + 15) >> 4;
+    mb_act = mb_act < 0 ? 0 : (mb_act > 4 ? 4 : mb_act);
+
+    floatx4_t acc[4][8];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) acc[mb][nb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+
+    // one K chunk from one ring stage; FULL: all four 16-row blocks of the
+    // wave are live (no per-block branches, A fragments read up front)
+    auto compute = [&](const uint4 *As, const uint4 *Bs, const uint32_t *Ss, auto full) {
+        uint4 bw[8];
+        float scale[8];
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) {
+            const int rho = wn * 128 + nb * 16 + n16;
+            bw[nb] = Bs[rho * 4 + g];
+            scale[nb] = e8m0_to_f32((Ss[rho] >> (8 * g)) & 0xFFu);
         }
-        const uint4 *Ab = As[kc & 1];
-        float scale[4];
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) scale[nb] = e8m0_to_f32(sb[nb]);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            bf16x8_t bq[4];
+            uint4 av[4];
 #pragma unroll
-            for (int nb = 0; nb < 4; ++nb) {
-                const uint32_t w = s == 0 ? b[nb].x : s == 1 ? b[nb].y : s == 2 ? b[nb].z : b[nb].w;
+            for (int mb = 0; mb < 4; ++mb)
+                if (decltype(full)::value || mb < mb_act)
+                    av[mb] = As[(wm * 64 + mb * 16 + n16) * kSlots + ((4 * g + s) ^ n16)];
+            bf16x8_t bq[8];
+#pragma unroll
+            for (int nb = 0; nb < 8; ++nb) {
+                const uint32_t w = s == 0 ? bw[nb].x : s == 1 ? bw[nb].y : s == 2 ? bw[nb].z : bw[nb].w;
                 bq[nb] = fp4x8_to_bf16(w, scale[nb]);
             }
 #pragma unroll
-            for (int mb = 0; mb < kMB; ++mb) {
-                if (mb < mb_act) {
-                    const uint4 av = Ab[(mb * 16 + n) * kSlots + ((4 * g + s) ^ n)];
+            for (int mb = 0; mb < 4; ++mb) {
+                if (decltype(full)::value || mb < mb_act) {
 #pragma unroll
-                    for (int nb = 0; nb < 4; ++nb)
-                        acc[mb][nb] = mfma16(as_bf16x8(av), bq[nb], acc[mb][nb]);
+                    for (int nb = 0; nb < 8; ++nb)
+                        acc[mb][nb] = mfma16(as_bf16x8(av[mb]), bq[nb], acc[mb][nb]);
                 }
             }
         }
-        if (more) {
-            store_a((kc + 1) & 1);
-#pragma unroll
-            for (int nb = 0; nb < 4; ++nb) {
-                b[nb] = bn[nb];
-                sb[nb] = sbn[nb];
-            }
-        }
+    };
+
+    // ---- pipeline --------------------------------------------------------------
+    const int nk = K / kKStep;
+    issue(0, As0, Bs0, Ss0);
+    if (nk > 1) issue(1, As1, Bs1, Ss1);
+    const bool full = mb_act == 4;
+    auto step = [&](int kc, uint4 *Ac, uint4 *Bc, uint32_t *Sc, uint4 *An, uint4 *Bn, uint32_t *Sn) {
+        if (kc + 1 < nk) chunk_sync<kChunkLoads>();
+        else chunk_sync<0>();
+        if (kc + 2 < nk) issue(kc + 2, An, Bn, Sn);
+        if (full) compute(Ac, Bc, Sc, std::true_type{});
+        else if (mb_act > 0) compute(Ac, Bc, Sc, std::false_type{});
+    };
+    for (int kc = 0; kc < nk; kc += 3) {
+        step(kc, As0, Bs0, Ss0, As2, Bs2, Ss2);
+        if (kc + 1 < nk) step(kc + 1, As1, Bs1, Ss1, As0, Bs0, Ss0);
+        if (kc + 2 < nk) step(kc + 2, As2, Bs2, Ss2, As1, Bs1, Ss1);
     }
 
+    // ---- epilogue ----------------------------------------------------------
     if (GATE_UP) {
-        const int fbase = nt * 128 + wv * 32;
+        const int fbase = nt * 128 + wn * 64;
 #pragma unroll
-        for (int mb = 0; mb < kMB; ++mb) {
+        for (int mb = 0; mb < 4; ++mb) {
             if (mb >= mb_act) continue;
 #pragma unroll
-            for (int hb = 0; hb < 2; ++hb)
+            for (int hb = 0; hb < 4; ++hb)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int row = mb * 16 + g * 4 + r;
+                    const int row = wm * 64 + mb * 16 + g * 4 + r;
                     if (row < tl.nrows)
-                        out[(int64_t)(tl.row0 + row) * F + fbase + hb * 16 + n] =
-                            f32_to_bf16(silu(acc[mb][hb][r]) * acc[mb][hb + 2][r]);
+                        pa.out[(int64_t)(tl.row0 + row) * F + fbase + hb * 16 + n16] =
+                            f32_to_bf16(silu(acc[mb][hb][r]) * acc[mb][hb + 4][r]);
                 }
         }
     } else {
         const int P = d / 64;
-        const int pcol = nt * 4 + wv;
-        const int cbase = nt * 256 + wv * 64;
+        const int cbase = nt * kTN + wn * 128;
 #pragma unroll
-        for (int mb = 0; mb < kMB; ++mb) {
+        for (int mb = 0; mb < 4; ++mb) {
             if (mb >= mb_act) continue;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int row = mb * 16 + g * 4 + r;
-                float ss = 0.f;
+                const int row = wm * 64 + mb * 16 + g * 4 + r;
+                float ss0 = 0.f, ss1 = 0.f;
 #pragma unroll
-                for (int nb = 0; nb < 4; ++nb) ss += acc[mb][nb][r] * acc[mb][nb][r];
-                ss = sum16(ss);
+                for (int nb = 0; nb < 4; ++nb) ss0 += acc[mb][nb][r] * acc[mb][nb][r];
+#pragma unroll
+                for (int nb = 4; nb < 8; ++nb) ss1 += acc[mb][nb][r] * acc[mb][nb][r];
+                ss0 = sum16(ss0);
+                ss1 = sum16(ss1);
                 if (row < tl.nrows) {
 #pragma unroll
-                    for (int nb = 0; nb < 4; ++nb)
-                        out[(int64_t)(tl.row0 + row) * d + cbase + nb * 16 + n] =
+                    for (int nb = 0; nb < 8; ++nb)
+                        pa.out[(int64_t)(tl.row0 + row) * d + cbase + nb * 16 + n16] =
                             f32_to_bf16(acc[mb][nb][r]);
-                    if (n == 0) ssq[(int64_t)(tl.row0 + row) * P + pcol] = ss;
+                    if (n16 == 0) {
+                        pa.ssq[(int64_t)(tl.row0 + row) * P + cbase / 64] = ss0;
+                        pa.ssq[(int64_t)(tl.row0 + row) * P + cbase / 64 + 1] = ss1;
+                    }
                 }
             }
         }
@@ -492,10 +552,9 @@ hipError_t launch_gemm1(const Shape &s, const Plan &p, const Workspace &ws, cons
                         const uint8_t *wpk, const uint8_t *sc, hipStream_t st)
 {
     if (p.tiled) {
-        const int ntn = s.F / 128;
-        const int64_t grid = 8 * ((max_tiles(s, p.tile_rows) * ntn + 7) / 8);
-        gemm_tiled_kernel<true><<<(unsigned)grid, 256, 0, st>>>(
-            x, ws.perm, ws.tiles, ws.ntiles, wpk, sc, ws.h, nullptr, s.d, s.F, s.k, ntn);
+        PipeArgs pa{x, ws.perm, ws.tiles, ws.ntiles, wpk, sc, ws.h, nullptr, s.d, s.F, s.k, s.F / 128};
+        const int64_t grid = 8 * ((max_tiles(s, p.tile_rows) * pa.ntn + 7) / 8);
+        gemm_tiled_kernel<true><<<(unsigned)grid, 256, 0, st>>>(pa);
     } else {
         const int groups = s.F / (16 * kG1NBP);
         const int64_t grid = max_tiles(s, p.tile_rows) * groups;
@@ -514,10 +573,9 @@ hipError_t launch_gemm2(const Shape &s, const Plan &p, const Workspace &ws, cons
                         const uint8_t *sc, hipStream_t st)
 {
     if (p.tiled) {
-        const int ntn = s.d / 256;
-        const int64_t grid = 8 * ((max_tiles(s, p.tile_rows) * ntn + 7) / 8);
-        gemm_tiled_kernel<false><<<(unsigned)grid, 256, 0, st>>>(
-            ws.h, nullptr, ws.tiles, ws.ntiles, wpk, sc, ws.o, ws.ssq, s.d, s.F, s.k, ntn);
+        PipeArgs pa{ws.h, nullptr, ws.tiles, ws.ntiles, wpk, sc, ws.o, ws.ssq, s.d, s.F, s.k, s.d / 256};
+        const int64_t grid = 8 * ((max_tiles(s, p.tile_rows) * pa.ntn + 7) / 8);
+        gemm_tiled_kernel<false><<<(unsigned)grid, 256, 0, st>>>(pa);
     } else {
         const int wgs = s.d / (64 * kG2NB);
         const int64_t grid = max_tiles(s, p.tile_rows) * wgs;
