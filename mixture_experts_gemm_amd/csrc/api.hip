@@ -39,6 +39,14 @@ Workspace carve_workspace(const Shape &s, void *base)
     w.h = (uint16_t *)take(sizeof(uint16_t) * (size_t)S * s.F);
     w.o = (uint16_t *)take(sizeof(uint16_t) * (size_t)S * s.d);
     w.ssq = (float *)take(sizeof(float) * (size_t)S * (s.d / 64));
+    w.xhi = (uint8_t *)take((size_t)s.T * s.d);
+    w.xlo = (uint8_t *)take((size_t)s.T * s.d);
+    w.xshi = (uint8_t *)take((size_t)s.T * s.d / 32);
+    w.xslo = (uint8_t *)take((size_t)s.T * s.d / 32);
+    w.hhi = (uint8_t *)take((size_t)S * s.F);
+    w.hlo = (uint8_t *)take((size_t)S * s.F);
+    w.hshi = (uint8_t *)take((size_t)S * s.F / 32);
+    w.hslo = (uint8_t *)take((size_t)S * s.F / 32);
     w.bytes = off;
     return w;
 }

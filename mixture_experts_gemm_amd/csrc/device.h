@@ -97,4 +97,45 @@ __device__ __forceinline__ float wave_sum(float v)
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
 
+// ---- exact split of bf16 into two FP8 E4M3 parts --------------------------
+// For a block of 32 bf16 values with largest magnitude M = 2^E * 1.f:
+//   hi = RNE_e4m3(v / 2^sh), sh = E - 7 (|v / 2^sh| < 256 <= 448, no clipping)
+//   lo = RNE_e4m3((v - hi * 2^sh) / 2^sl), sl = sh - 5
+// bf16 keeps 8 significant bits and hi keeps the top 4 (rounded), so the
+// residual has at most 4 significant bits: v == hi*2^sh + lo*2^sl exactly
+// whenever |v| >= 2^(E-14) (lower values keep an error below 2^(E-22)).
+// Scales are returned as E8M0 bytes (exponent + 127).
+__device__ __forceinline__ float pow2f(int e) { return __uint_as_float((uint32_t)(e + 127) << 23); }
+
+__device__ __forceinline__ void split_e4m3_block(const float *v, uint32_t *hi, uint32_t *lo,
+                                                 uint32_t &shi, uint32_t &slo)
+{
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    int E = (int)((__float_as_uint(amax) >> 23) & 0xFF) - 127;  // amax == 0 or subnormal: clamp below
+    int sh = E - 7;
+    if (sh < -120) sh = -120;
+    const int sl = sh - 5;
+    const float ih = pow2f(-sh), il = pow2f(-sl), fh = pow2f(sh);
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+        int ph = 0, pl = 0;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const float a = v[4 * w + 2 * half], b = v[4 * w + 2 * half + 1];
+            const int h2 = __builtin_amdgcn_cvt_pk_fp8_f32(a * ih, b * ih, 0, false);
+            const float ra = a - __builtin_amdgcn_cvt_f32_fp8(h2, 0) * fh;
+            const float rb = b - __builtin_amdgcn_cvt_f32_fp8(h2, 1) * fh;
+            const int l2 = __builtin_amdgcn_cvt_pk_fp8_f32(ra * il, rb * il, 0, false);
+            ph |= (h2 & 0xFFFF) << (16 * half);
+            pl |= (l2 & 0xFFFF) << (16 * half);
+        }
+        hi[w] = (uint32_t)ph;
+        lo[w] = (uint32_t)pl;
+    }
+    shi = (uint32_t)(sh + 127);
+    slo = (uint32_t)(sl + 127);
+}
+
 }  // namespace moe

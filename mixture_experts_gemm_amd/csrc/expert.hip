@@ -25,6 +25,10 @@
 
 namespace moe {
 
+#ifndef MOE_TILED_MX
+#define MOE_TILED_MX 1  // prefill tiles on the scaled MX MFMA (0: bf16 MFMA with FP4 expansion)
+#endif
+
 constexpr int kKStep = 128;  // K elements per chunk
 constexpr int kUnroll = 4;   // chunks in flight per wave (decode kernels)
 
@@ -291,8 +295,9 @@ __global__ __launch_bounds__(256) void gemm2_decode_kernel(
 // (global_load_lds_dwordx4: each lane's 16 bytes land at base + 16*lane):
 //   A  128 rows x 256 B bf16, 16-byte slot c of row r stored at c ^ (r & 15)
 //      so the MFMA fragment reads of 16 rows hit 16 different slots;
-//   B  256 weight rows x 64 B of FP4 codes, row-major (a fragment read of
-//      16 rows x 4 lanes is one contiguous KB);
+//   B  256 weight rows x 64 B of FP4 codes; 16-byte slot g of row r stored
+//      at g ^ ((r>>1 ^ r>>3) & 3), so a fragment read (16 rows x 4 slots)
+//      touches every bank once;
 //   S  256 x 4 E8M0 bytes (the chunk's 4 scale blocks of each row).
 // Chunk kc+2 is in flight while chunk kc is multiplied.  Waits are explicit
 // (s_waitcnt on the wave's own outstanding loads, then s_barrier): a plain
@@ -349,6 +354,9 @@ __device__ __forceinline__ void chunk_sync()
     asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" :: "n"(N) : "memory");
 }
 
+// B slot swizzle: row r's 16-byte slot g lives at g ^ bswz(r).
+__device__ __forceinline__ int bswz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+
 struct PipeArgs {
     const uint16_t *act;   // A rows: x (gathered) or h (grouped order)
     const int32_t *perm;
@@ -367,6 +375,9 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(const PipeArgs pa)
     __shared__ uint4 As0[kTM * kSlots], As1[kTM * kSlots], As2[kTM * kSlots];
     __shared__ uint4 Bs0[kTN * 4], Bs1[kTN * 4], Bs2[kTN * 4];
     __shared__ uint32_t Ss0[kTN], Ss1[kTN], Ss2[kTN];
+#if MOE_BPF
+    __shared__ uint32_t Pf[256];
+#endif
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int d = pa.d, F = pa.F;
@@ -405,7 +416,8 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(const PipeArgs pa)
 #pragma unroll
     for (int i = 0; i < kBLoads; ++i) {
         const int rho = 16 * (4 * i + wv) + (lane >> 2);
-        bsrc[i] = eb + wbase + wrow_of(rho) * (K / 2) + (lane & 3) * 16;
+        const int gsrc = (lane & 3) ^ bswz(rho);  // logical slot stored at this lane's place
+        bsrc[i] = eb + wbase + wrow_of(rho) * (K / 2) + gsrc * 16;
     }
     const uint8_t *ssrc = es + sbase + wrow_of(64 * wv + lane) * (K / 32);
 
@@ -442,7 +454,7 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(const PipeArgs pa)
 #pragma unroll
         for (int nb = 0; nb < 8; ++nb) {
             const int rho = wn * 128 + nb * 16 + n16;
-            bw[nb] = Bs[rho * 4 + g];
+            bw[nb] = Bs[rho * 4 + (g ^ bswz(rho))];
             scale[nb] = e8m0_to_f32((Ss[rho] >> (8 * g)) & 0xFFu);
         }
 #pragma unroll
@@ -534,6 +546,285 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(const PipeArgs pa)
     }
 }
 
+// =========================================================================
+// MX tiled kernels (prefill): same tiles, ring and wave layout as above, but
+// the multiply is the gfx950 scaled MX MFMA (16x16x128, f8f6f4): the FP4
+// weights and their E8M0 scales go into the instruction as they are stored,
+// so nothing is expanded in registers.  The bf16 activations arrive split
+// into two FP8 E4M3 parts (split_rows_kernel): a = hi*2^sh + lo*2^sl, exact
+// for every value above 2^-13 of its 32-block maximum, and every 16x16x128
+// block takes two MFMAs (hi, lo).  Accumulation stays fp32.
+//
+// Operand map of the scaled MFMA (probed on the hardware): lanes l/16 = g.
+//   B (FP4, 16 bytes/lane): row n = l%16, the 32 values of weight block g of
+//     the chunk, scale_b = that block's E8M0 byte.
+//   A (FP8, 32 bytes/lane): row m = l%16, bytes 0-15 = K 16g..16g+15 and
+//     bytes 16-31 = K 64+16g..64+16g+15 of the chunk; scale_a of lane group
+//     g applies to the A values that meet B block g, i.e. activation block g
+//     (K 32g..32g+31), so the activation split uses the natural 32-blocks.
+// LDS per stage: A hi and lo 128 rows x 128 B each (16-byte slot c of row r
+// at c ^ (r & 7)), A scales 128 x (hi word, lo word), B and B scales as in
+// the bf16 kernel.  150.5 KB for three stages.
+// =========================================================================
+typedef int v8i_t __attribute__((__vector_size__(8 * sizeof(int))));
+
+constexpr int kAHLoads = kTM * 8 / 256;                      // 4 per part per thread
+#ifndef MOE_BPF
+#define MOE_BPF 0  // chunks ahead that B rows are touched in L2 (0: off)
+#endif
+constexpr int kMxChunkLoads = 2 * kAHLoads + 1 + kBLoads + 1 + (MOE_BPF > 0);  // A hi, A lo, A scales, B, B scales[, B touch]
+
+struct MxArgs {
+    const uint8_t *ahi, *alo;     // activation parts [rows][K] (FP8)
+    const uint8_t *ashi, *aslo;   // their E8M0 scales [rows][K/32]
+    const int32_t *perm;
+    const Tile *tiles;
+    const int32_t *ntiles;
+    const uint8_t *wpk;
+    const uint8_t *sc;
+    uint16_t *out;                // h or o (bf16)
+    float *ssq;
+    int d, F, k, ntn;
+};
+
+__device__ __forceinline__ floatx4_t mfma_mx(const uint4 &a0, const uint4 &a1, const uint4 &b,
+                                             uint32_t sa, uint32_t sb, floatx4_t c)
+{
+    const v8i_t av = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
+                      (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+    const v8i_t bv = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
+    // format codes: 0 = FP8 E4M3 (A), 4 = FP4 E2M1 (B)
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 0, 4, 0, (int)sa, 0, (int)sb);
+}
+
+template <bool GATE_UP>
+__global__ __launch_bounds__(256) void gemm_mx_kernel(const MxArgs pa)
+{
+    __shared__ uint4 Ah0[kTM * 8], Ah1[kTM * 8], Ah2[kTM * 8];
+    __shared__ uint4 Al0[kTM * 8], Al1[kTM * 8], Al2[kTM * 8];
+    __shared__ uint32_t Ac0[kTM * 2], Ac1[kTM * 2], Ac2[kTM * 2];
+    __shared__ uint4 Bs0[kTN * 4], Bs1[kTN * 4], Bs2[kTN * 4];
+    __shared__ uint32_t Ss0[kTN], Ss1[kTN], Ss2[kTN];
+#if MOE_BPF
+    __shared__ uint32_t Pf[256];
+#endif
+
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int d = pa.d, F = pa.F;
+    int idx;
+    if (!xcd_tile(*pa.ntiles * pa.ntn, idx)) return;
+    const int mt = idx / pa.ntn, nt = idx - mt * pa.ntn;
+    const Tile tl = pa.tiles[mt];
+    const int K = GATE_UP ? d : F;
+    const int64_t ebytes = (int64_t)3 * d * F / 2, escales = (int64_t)3 * d * F / 32;
+    auto src_row = [&](int r) -> int64_t {
+        const int rr = r < tl.nrows ? r : 0;  // rows past nrows re-read row 0 (never stored)
+        return GATE_UP ? (int64_t)(pa.perm[tl.row0 + rr] / pa.k) : (int64_t)(tl.row0 + rr);
+    };
+
+    // ---- load assignment ----------------------------------------------------
+    // A parts: load i of this wave fills rows 8*(4i + wv) + lane/8, stored slot lane%8
+    const int a_row_lo = lane >> 3;
+    const uint8_t *ahsrc[kAHLoads], *alsrc[kAHLoads];
+#pragma unroll
+    for (int i = 0; i < kAHLoads; ++i) {
+        const int r = 8 * (4 * i + wv) + a_row_lo;
+        const int slot = (lane & 7) ^ (r & 7);
+        const int64_t off = src_row(r) * K + slot * 16;
+        ahsrc[i] = pa.ahi + off;
+        alsrc[i] = pa.alo + off;
+    }
+    // A scales: dword 64*wv + lane = (row, part) with row = that / 2
+    const int asr = (64 * wv + lane) >> 1;
+    const uint8_t *acsrc = ((lane & 1) ? pa.aslo : pa.ashi) + src_row(asr) * (K / 32);
+    // B as in the bf16 kernel
+    auto wrow_of = [&](int rho) -> int64_t {
+        if (GATE_UP) {
+            const int f = nt * 128 + (rho >> 7) * 64 + ((rho >> 4) & 3) * 16 + (rho & 15);
+            return ((rho >> 6) & 1) ? (int64_t)F + f : (int64_t)f;
+        }
+        return (int64_t)nt * kTN + rho;
+    };
+    const uint8_t *eb = pa.wpk + tl.expert * ebytes;
+    const uint8_t *es = pa.sc + tl.expert * escales;
+    const int64_t wbase = GATE_UP ? 0 : (int64_t)2 * F * (d / 2);
+    const int64_t sbase = GATE_UP ? 0 : (int64_t)2 * F * (d / 32);
+    const uint8_t *bsrc[kBLoads];
+#pragma unroll
+    for (int i = 0; i < kBLoads; ++i) {
+        const int rho = 16 * (4 * i + wv) + (lane >> 2);
+        const int gsrc = (lane & 3) ^ bswz(rho);
+        bsrc[i] = eb + wbase + wrow_of(rho) * (K / 2) + gsrc * 16;
+    }
+    const uint8_t *ssrc = es + sbase + wrow_of(64 * wv + lane) * (K / 32);
+    const int nk = K / kKStep;
+#if MOE_BPF
+    const uint8_t *pfsrc = eb + wbase + wrow_of(64 * wv + lane) * (K / 2);
+#endif
+
+    const int wvu = __builtin_amdgcn_readfirstlane(wv);
+    auto issue = [&](int kc, uint4 *Ah, uint4 *Al, uint32_t *Ac, uint4 *Bs, uint32_t *Ss) {
+#pragma unroll
+        for (int i = 0; i < kAHLoads; ++i) dma16(ahsrc[i] + kc * kKStep, lds_off(Ah + (4 * i + wvu) * 64));
+#pragma unroll
+        for (int i = 0; i < kAHLoads; ++i) dma16(alsrc[i] + kc * kKStep, lds_off(Al + (4 * i + wvu) * 64));
+        dma4(acsrc + kc * 4, lds_off(Ac + 64 * wvu));
+#pragma unroll
+        for (int i = 0; i < kBLoads; ++i) dma16(bsrc[i] + kc * (kKStep / 2), lds_off(Bs + (4 * i + wvu) * 64));
+        dma4(ssrc + kc * (kKStep / 32), lds_off(Ss + 64 * wvu));
+#if MOE_BPF
+        const int pc = kc + MOE_BPF < nk ? kc + MOE_BPF : nk - 1;
+        dma4(pfsrc + pc * (kKStep / 2), lds_off(Pf + 64 * wvu));
+#endif
+    };
+
+    // ---- compute assignment -------------------------------------------------
+    const int wm = wv & 1, wn = wv >> 1;
+    const int n16 = lane & 15, g = lane >> 4;
+    int mb_act = (tl.nrows - wm * 64 + 15) >> 4;
+    mb_act = mb_act < 0 ? 0 : (mb_act > 4 ? 4 : mb_act);
+
+    floatx4_t acc[4][8];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) acc[mb][nb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+
+    auto compute = [&](const uint4 *Ah, const uint4 *Al, const uint32_t *Ac, const uint4 *Bs,
+                       const uint32_t *Ss, auto full) {
+        constexpr bool F_ = decltype(full)::value;
+        uint4 bw[8];
+        uint32_t bsc[8];
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) {
+            const int rho = wn * 128 + nb * 16 + n16;
+            bw[nb] = Bs[rho * 4 + (g ^ bswz(rho))];
+            bsc[nb] = (Ss[rho] >> (8 * g)) & 0xFFu;
+        }
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+            if (F_ || mb < mb_act) {
+                const int row = wm * 64 + mb * 16 + n16;
+                const int sw = row & 7;
+                const uint4 h0 = Ah[row * 8 + (g ^ sw)], h1 = Ah[row * 8 + ((4 + g) ^ sw)];
+                const uint4 l0 = Al[row * 8 + (g ^ sw)], l1 = Al[row * 8 + ((4 + g) ^ sw)];
+                const uint32_t sh = (Ac[row * 2] >> (8 * g)) & 0xFFu;
+                const uint32_t sl = (Ac[row * 2 + 1] >> (8 * g)) & 0xFFu;
+#pragma unroll
+                for (int nb = 0; nb < 8; ++nb) {
+                    acc[mb][nb] = mfma_mx(h0, h1, bw[nb], sh, bsc[nb], acc[mb][nb]);
+                    acc[mb][nb] = mfma_mx(l0, l1, bw[nb], sl, bsc[nb], acc[mb][nb]);
+                }
+            }
+        }
+    };
+
+    // ---- pipeline --------------------------------------------------------------
+    issue(0, Ah0, Al0, Ac0, Bs0, Ss0);
+    if (nk > 1) issue(1, Ah1, Al1, Ac1, Bs1, Ss1);
+    const bool full = mb_act == 4;
+    auto step = [&](int kc, uint4 *Ahc, uint4 *Alc, uint32_t *Acc, uint4 *Bc, uint32_t *Sc,
+                    uint4 *Ahn, uint4 *Aln, uint32_t *Acn, uint4 *Bn, uint32_t *Sn) {
+        if (kc + 1 < nk) chunk_sync<kMxChunkLoads>();
+        else chunk_sync<0>();
+        if (kc + 2 < nk) issue(kc + 2, Ahn, Aln, Acn, Bn, Sn);
+        if (full) compute(Ahc, Alc, Acc, Bc, Sc, std::true_type{});
+        else if (mb_act > 0) compute(Ahc, Alc, Acc, Bc, Sc, std::false_type{});
+    };
+    for (int kc = 0; kc < nk; kc += 3) {
+        step(kc, Ah0, Al0, Ac0, Bs0, Ss0, Ah2, Al2, Ac2, Bs2, Ss2);
+        if (kc + 1 < nk) step(kc + 1, Ah1, Al1, Ac1, Bs1, Ss1, Ah0, Al0, Ac0, Bs0, Ss0);
+        if (kc + 2 < nk) step(kc + 2, Ah2, Al2, Ac2, Bs2, Ss2, Ah1, Al1, Ac1, Bs1, Ss1);
+    }
+
+    // ---- epilogue (same as the bf16 kernel) ---------------------------------
+    if (GATE_UP) {
+        const int fbase = nt * 128 + wn * 64;
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+            if (mb >= mb_act) continue;
+#pragma unroll
+            for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = wm * 64 + mb * 16 + g * 4 + r;
+                    if (row < tl.nrows)
+                        pa.out[(int64_t)(tl.row0 + row) * F + fbase + hb * 16 + n16] =
+                            f32_to_bf16(silu(acc[mb][hb][r]) * acc[mb][hb + 4][r]);
+                }
+        }
+    } else {
+        const int P = d / 64;
+        const int cbase = nt * kTN + wn * 128;
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+            if (mb >= mb_act) continue;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = wm * 64 + mb * 16 + g * 4 + r;
+                float ss0 = 0.f, ss1 = 0.f;
+#pragma unroll
+                for (int nb = 0; nb < 4; ++nb) ss0 += acc[mb][nb][r] * acc[mb][nb][r];
+#pragma unroll
+                for (int nb = 4; nb < 8; ++nb) ss1 += acc[mb][nb][r] * acc[mb][nb][r];
+                ss0 = sum16(ss0);
+                ss1 = sum16(ss1);
+                if (row < tl.nrows) {
+#pragma unroll
+                    for (int nb = 0; nb < 8; ++nb)
+                        pa.out[(int64_t)(tl.row0 + row) * d + cbase + nb * 16 + n16] =
+                            f32_to_bf16(acc[mb][nb][r]);
+                    if (n16 == 0) {
+                        pa.ssq[(int64_t)(tl.row0 + row) * P + cbase / 64] = ss0;
+                        pa.ssq[(int64_t)(tl.row0 + row) * P + cbase / 64 + 1] = ss1;
+                    }
+                }
+            }
+        }
+    }
+}
+
+// bf16 rows -> FP8 E4M3 hi/lo parts + E8M0 scales per 32-block (one thread per block).
+__global__ __launch_bounds__(256) void split_rows_kernel(const uint16_t *__restrict__ src,
+                                                         int64_t nblk, uint8_t *__restrict__ hi,
+                                                         uint8_t *__restrict__ lo,
+                                                         uint8_t *__restrict__ shi,
+                                                         uint8_t *__restrict__ slo)
+{
+    const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (b >= nblk) return;
+    const uint4 *p = reinterpret_cast<const uint4 *>(src + b * 32);
+    float v[32];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint4 w = p[q];
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[8 * q + 2 * i] = __uint_as_float(ws[i] << 16);
+            v[8 * q + 2 * i + 1] = __uint_as_float(ws[i] & 0xFFFF0000u);
+        }
+    }
+    uint32_t h[8], l[8], sh, sl;
+    split_e4m3_block(v, h, l, sh, sl);
+    uint4 *ph = reinterpret_cast<uint4 *>(hi + b * 32);
+    uint4 *pl = reinterpret_cast<uint4 *>(lo + b * 32);
+    ph[0] = make_uint4(h[0], h[1], h[2], h[3]);
+    ph[1] = make_uint4(h[4], h[5], h[6], h[7]);
+    pl[0] = make_uint4(l[0], l[1], l[2], l[3]);
+    pl[1] = make_uint4(l[4], l[5], l[6], l[7]);
+    shi[b] = (uint8_t)sh;
+    slo[b] = (uint8_t)sl;
+}
+
+static hipError_t launch_split(const uint16_t *src, int64_t rows, int K, uint8_t *hi, uint8_t *lo,
+                               uint8_t *shi, uint8_t *slo, hipStream_t st)
+{
+    const int64_t nblk = rows * (K / 32);
+    split_rows_kernel<<<(unsigned)((nblk + 255) / 256), 256, 0, st>>>(src, nblk, hi, lo, shi, slo);
+    return hipGetLastError();
+}
+
 // LDS budget for the decode kernels' staged activation rows.
 #ifndef MOE_DEC_LDS
 #define MOE_DEC_LDS (32 * 1024)
@@ -552,9 +843,18 @@ hipError_t launch_gemm1(const Shape &s, const Plan &p, const Workspace &ws, cons
                         const uint8_t *wpk, const uint8_t *sc, hipStream_t st)
 {
     if (p.tiled) {
+#if MOE_TILED_MX
+        hipError_t e = launch_split(x, s.T, s.d, ws.xhi, ws.xlo, ws.xshi, ws.xslo, st);
+        if (e != hipSuccess) return e;
+        MxArgs pa{ws.xhi, ws.xlo, ws.xshi, ws.xslo, ws.perm, ws.tiles, ws.ntiles, wpk, sc,
+                  ws.h, nullptr, s.d, s.F, s.k, s.F / 128};
+        const int64_t grid = 8 * ((max_tiles(s, p.tile_rows) * pa.ntn + 7) / 8);
+        gemm_mx_kernel<true><<<(unsigned)grid, 256, 0, st>>>(pa);
+#else
         PipeArgs pa{x, ws.perm, ws.tiles, ws.ntiles, wpk, sc, ws.h, nullptr, s.d, s.F, s.k, s.F / 128};
         const int64_t grid = 8 * ((max_tiles(s, p.tile_rows) * pa.ntn + 7) / 8);
         gemm_tiled_kernel<true><<<(unsigned)grid, 256, 0, st>>>(pa);
+#endif
     } else {
         const int groups = s.F / (16 * kG1NBP);
         const int64_t grid = max_tiles(s, p.tile_rows) * groups;
@@ -573,9 +873,18 @@ hipError_t launch_gemm2(const Shape &s, const Plan &p, const Workspace &ws, cons
                         const uint8_t *sc, hipStream_t st)
 {
     if (p.tiled) {
+#if MOE_TILED_MX
+        hipError_t e = launch_split(ws.h, s.S(), s.F, ws.hhi, ws.hlo, ws.hshi, ws.hslo, st);
+        if (e != hipSuccess) return e;
+        MxArgs pa{ws.hhi, ws.hlo, ws.hshi, ws.hslo, nullptr, ws.tiles, ws.ntiles, wpk, sc,
+                  ws.o, ws.ssq, s.d, s.F, s.k, s.d / 256};
+        const int64_t grid = 8 * ((max_tiles(s, p.tile_rows) * pa.ntn + 7) / 8);
+        gemm_mx_kernel<false><<<(unsigned)grid, 256, 0, st>>>(pa);
+#else
         PipeArgs pa{ws.h, nullptr, ws.tiles, ws.ntiles, wpk, sc, ws.o, ws.ssq, s.d, s.F, s.k, s.d / 256};
         const int64_t grid = 8 * ((max_tiles(s, p.tile_rows) * pa.ntn + 7) / 8);
         gemm_tiled_kernel<false><<<(unsigned)grid, 256, 0, st>>>(pa);
+#endif
     } else {
         const int wgs = s.d / (64 * kG2NB);
         const int64_t grid = max_tiles(s, p.tile_rows) * wgs;

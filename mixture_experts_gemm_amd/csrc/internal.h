@@ -72,6 +72,11 @@ struct Workspace {
     uint16_t *h;          // bf16 [S][F]
     uint16_t *o;          // bf16 [S][d]
     float *ssq;           // [S][d / 64]
+    // FP8 E4M3 hi/lo parts of x and h with E8M0 scales per 32-block
+    uint8_t *xhi, *xlo;   // [T][d]
+    uint8_t *xshi, *xslo; // [T][d/32]
+    uint8_t *hhi, *hlo;   // [S][F]
+    uint8_t *hshi, *hslo; // [S][F/32]
     size_t bytes;
 };
 
