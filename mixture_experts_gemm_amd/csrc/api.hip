@@ -34,7 +34,7 @@ Workspace carve_workspace(const Shape &s, void *base)
     w.offsets = (int32_t *)take(sizeof(int32_t) * (size_t)(s.E + 1));
     w.perm = (int32_t *)take(sizeof(int32_t) * (size_t)S);
     w.inv = (int32_t *)take(sizeof(int32_t) * (size_t)S);
-    w.tiles = (Tile *)take(sizeof(Tile) * (size_t)max_tiles(s, 16));
+    w.tiles = (Tile *)take(sizeof(Tile) * (size_t)max_tiles(s, 1));
     w.ntiles = (int32_t *)take(sizeof(int32_t) * 4);
     w.h = (uint16_t *)take(sizeof(uint16_t) * (size_t)S * s.F);
     w.o = (uint16_t *)take(sizeof(uint16_t) * (size_t)S * s.d);
@@ -139,7 +139,7 @@ extern "C" int moe_layer_forward(const moe_dims_t *dims, const void *x, const fl
     };
     uint16_t *out = static_cast<uint16_t *>(s_out);
     const Plan p = make_plan(s);
-    if (!stage(MOE_STAGE_ROUTER, [&] { return launch_router(s, xb, router_w, ws.scores, st); }) ||
+    if (!stage(MOE_STAGE_ROUTER, [&] { return launch_router(s, p, ws, xb, router_w, st); }) ||
         !stage(MOE_STAGE_TOPK, [&] { return launch_topk(s, p, ws, st); }) ||
         !stage(MOE_STAGE_GROUP, [&] { return launch_group(s, p, ws, st); }) ||
         !stage(MOE_STAGE_GEMM1,

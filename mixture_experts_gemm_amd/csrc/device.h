@@ -138,4 +138,33 @@ __device__ __forceinline__ void split_e4m3_block(const float *v, uint32_t *hi, u
     slo = (uint32_t)(sl + 127);
 }
 
+// One 32-element bf16 block -> FP8 E4M3 hi and lo parts (32 bytes each) and
+// their E8M0 scales (split_e4m3_block).
+__device__ __forceinline__ void split_bf16_block(const uint16_t *src, uint8_t *hi, uint8_t *lo,
+                                                 uint8_t *shi, uint8_t *slo)
+{
+    const uint4 *p = reinterpret_cast<const uint4 *>(src);
+    float v[32];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint4 w = p[q];
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[8 * q + 2 * i] = __uint_as_float(ws[i] << 16);
+            v[8 * q + 2 * i + 1] = __uint_as_float(ws[i] & 0xFFFF0000u);
+        }
+    }
+    uint32_t h[8], l[8], sh, sl;
+    split_e4m3_block(v, h, l, sh, sl);
+    uint4 *ph = reinterpret_cast<uint4 *>(hi);
+    uint4 *pl = reinterpret_cast<uint4 *>(lo);
+    ph[0] = make_uint4(h[0], h[1], h[2], h[3]);
+    ph[1] = make_uint4(h[4], h[5], h[6], h[7]);
+    pl[0] = make_uint4(l[0], l[1], l[2], l[3]);
+    pl[1] = make_uint4(l[4], l[5], l[6], l[7]);
+    *shi = (uint8_t)sh;
+    *slo = (uint8_t)sl;
+}
+
 }  // namespace moe

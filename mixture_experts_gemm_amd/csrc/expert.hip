@@ -18,6 +18,7 @@
 // 16-byte weight load per lane is exactly one 32-element scale block, and
 // four MFMA steps consume it.  The order of k inside the instruction does not
 // matter because A and B use the same map.
+#include <mutex>
 #include <type_traits>
 
 #include "device.h"
@@ -27,6 +28,10 @@ namespace moe {
 
 #ifndef MOE_TILED_MX
 #define MOE_TILED_MX 1  // prefill tiles on the scaled MX MFMA (0: bf16 MFMA with FP4 expansion)
+#endif
+
+#ifndef MOE_G1DB
+#define MOE_G1DB 0  // gate/up decode: double-buffered weight batches
 #endif
 
 constexpr int kKStep = 128;  // K elements per chunk
@@ -86,12 +91,14 @@ __global__ __launch_bounds__(256) void gemm1_decode_kernel(
     const int rowq = d / 8;  // 16-byte units per activation row
     const int nc = d / kKStep;
     const int c_begin = wv * nc / 4, c_end = (wv + 1) * nc / 4;
-    // first batch of weight loads goes out before the activations are staged
-    uint4 b[U][NB];
-    uint32_t sw[U][NB];
+    // weights stream through two register batches of U chunks: while one is
+    // consumed the other is in flight.  The first batches go out before the
+    // activations are staged.
+    uint4 b0[U][NB], b1[U][NB];
+    uint32_t s0[U][NB], s1[U][NB];
     // scale words: one 16-byte load covers 4 chunks when rows and batches align
     const bool svec = U == 4 && (d / 32) % 16 == 0 && c_begin % 4 == 0;
-    auto load_b = [&](int c) {
+    auto load_b = [&](uint4 (&b)[U][NB], uint32_t (&sw)[U][NB], int c) {
 #pragma unroll
         for (int u = 0; u < U; ++u)
             if (c + u < c_end) {
@@ -117,7 +124,8 @@ __global__ __launch_bounds__(256) void gemm1_decode_kernel(
                 }
         }
     };
-    load_b(c_begin);
+    load_b(b0, s0, c_begin);
+    if (MOE_G1DB && c_begin + U < c_end) load_b(b1, s1, c_begin + U);
     if (use_lds) {
         for (int q = threadIdx.x; q < tl.nrows * rowq; q += 256) {
             const int r = q / rowq, c = q - r * rowq;
@@ -132,7 +140,7 @@ __global__ __launch_bounds__(256) void gemm1_decode_kernel(
     floatx4_t acc[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[nb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-    for (int c = c_begin; c < c_end; c += U) {
+    auto consume = [&](const uint4 (&b)[U][NB], const uint32_t (&sw)[U][NB], int c) {
 #pragma unroll
         for (int u = 0; u < U; ++u)
             if (c + u < c_end) {
@@ -148,8 +156,24 @@ __global__ __launch_bounds__(256) void gemm1_decode_kernel(
                     acc[nb] = mfma_chunk(a, b[u][nb], e8m0_to_f32((sw[u][nb] >> (8 * g)) & 0xFFu),
                                          acc[nb]);
             }
-        if (c + U < c_end) load_b(c + U);
+    };
+#if MOE_G1DB
+    for (int c = c_begin; c < c_end; c += 2 * U) {
+        consume(b0, s0, c);
+        if (c + 2 * U < c_end) load_b(b0, s0, c + 2 * U);
+        if (c + U < c_end) {
+            consume(b1, s1, c + U);
+            if (c + 3 * U < c_end) load_b(b1, s1, c + 3 * U);
+        }
     }
+#else
+    (void)b1;
+    (void)s1;
+    for (int c = c_begin; c < c_end; c += U) {
+        consume(b0, s0, c);
+        if (c + U < c_end) load_b(b0, s0, c + U);
+    }
+#endif
     if (wv > 0) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) red[wv - 1][nb][lane] = acc[nb];
@@ -352,6 +376,13 @@ template <int N>
 __device__ __forceinline__ void chunk_sync()
 {
     asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" :: "n"(N) : "memory");
+}
+
+// Workgroup barrier for LDS data only: waits for this wave's LDS operations,
+// not for its outstanding global loads (which __syncthreads would drain).
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // B slot swizzle: row r's 16-byte slot g lives at g ^ bswz(r).
@@ -793,28 +824,7 @@ __global__ __launch_bounds__(256) void split_rows_kernel(const uint16_t *__restr
 {
     const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (b >= nblk) return;
-    const uint4 *p = reinterpret_cast<const uint4 *>(src + b * 32);
-    float v[32];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const uint4 w = p[q];
-        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            v[8 * q + 2 * i] = __uint_as_float(ws[i] << 16);
-            v[8 * q + 2 * i + 1] = __uint_as_float(ws[i] & 0xFFFF0000u);
-        }
-    }
-    uint32_t h[8], l[8], sh, sl;
-    split_e4m3_block(v, h, l, sh, sl);
-    uint4 *ph = reinterpret_cast<uint4 *>(hi + b * 32);
-    uint4 *pl = reinterpret_cast<uint4 *>(lo + b * 32);
-    ph[0] = make_uint4(h[0], h[1], h[2], h[3]);
-    ph[1] = make_uint4(h[4], h[5], h[6], h[7]);
-    pl[0] = make_uint4(l[0], l[1], l[2], l[3]);
-    pl[1] = make_uint4(l[4], l[5], l[6], l[7]);
-    shi[b] = (uint8_t)sh;
-    slo[b] = (uint8_t)sl;
+    split_bf16_block(src + b * 32, hi + b * 32, lo + b * 32, shi + b, slo + b);
 }
 
 static hipError_t launch_split(const uint16_t *src, int64_t rows, int K, uint8_t *hi, uint8_t *lo,
@@ -823,6 +833,179 @@ static hipError_t launch_split(const uint16_t *src, int64_t rows, int K, uint8_t
     const int64_t nblk = rows * (K / 32);
     split_rows_kernel<<<(unsigned)((nblk + 255) / 256), 256, 0, st>>>(src, nblk, hi, lo, shi, slo);
     return hipGetLastError();
+}
+
+// =========================================================================
+// Streaming gate/up kernel for a few tokens (decode).  The time is the read
+// of the chosen experts' FP4 weights, so the kernel is built to keep that
+// read going without gaps:
+//  * persistent workgroups: each takes a contiguous run of work items
+//    (tile, 16 features) and walks it, so there is no per-item launch,
+//    start-up load chain or tail of short workgroups;
+//  * the weights of the next batch of chunks are in flight while the current
+//    batch is multiplied (two register buffers), also across item borders;
+//  * the scaled MX MFMA takes the FP4 codes and E8M0 scales as stored, so no
+//    vector ALU work is spent per weight;
+//  * the tile's activation rows are split into FP8 hi/lo parts with their
+//    E8M0 scales (exact, as in split_rows_kernel) while they are copied to
+//    LDS, once per tile.
+// The 4 waves take quarters of K; their partial sums meet in LDS (two
+// buffers, alternating per item, one barrier per item) and wave 0 writes
+// silu(gate) * up.  Requirements (checked by the launcher): d % 2048 == 0,
+// tiles of at most R rows.
+// =========================================================================
+template <int U>
+__global__ __launch_bounds__(256) void gemm1_stream_kernel(
+    const uint8_t *__restrict__ ghi, const uint8_t *__restrict__ glo,
+    const uint8_t *__restrict__ gsh, const uint8_t *__restrict__ gsl,
+    const int32_t *__restrict__ perm, const Tile *__restrict__ tiles,
+    const int32_t *__restrict__ ntiles, const uint8_t *__restrict__ wpk,
+    const uint8_t *__restrict__ sc, uint16_t *__restrict__ h, int d, int F, int k, int R)
+{
+    constexpr int NB = 2;  // gate block, up block
+    extern __shared__ uint4 xs4[];
+    __shared__ floatx4_t red[2][3][NB][64];
+    uint8_t *xs = reinterpret_cast<uint8_t *>(xs4);
+    uint8_t *xhi = xs, *xlo = xs + (size_t)R * d;
+    uint8_t *xsh = xs + (size_t)2 * R * d, *xsl = xsh + (size_t)R * (d / 32);
+
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int n = lane & 15, g = lane >> 4;
+    const int groups = F / 16;
+    const int64_t nitems = (int64_t)*ntiles * groups;
+    const int i0 = (int)(nitems * blockIdx.x / gridDim.x);
+    const int i1 = (int)(nitems * (blockIdx.x + 1) / gridDim.x);
+    if (i0 >= i1) return;
+    const int cw = d / kKStep / 4;  // chunks per wave
+    const int c_begin = wv * cw;
+    const int nbat = cw / U;
+    const int total = (i1 - i0) * nbat;
+    const int64_t ebytes = (int64_t)3 * d * F / 2, escales = (int64_t)3 * d * F / 32;
+
+    // ---- weight loads (one batch = U chunks of the gate and the up block) --
+    uint4 b0[U][NB], b1[U][NB];
+    uint32_t s0[U][NB], s1[U][NB];
+    int l_ti = -1;
+    Tile l_tl{0, 0, 0, 0};
+    auto load = [&](uint4 (&b)[U][NB], uint32_t (&sv)[U][NB], int st) {
+        const int it = i0 + st / nbat, bt = st % nbat;
+        const int ti = it / groups, grp = it - ti * groups;
+        if (ti != l_ti) {
+            l_tl = tiles[ti];
+            l_ti = ti;
+        }
+        const int c = c_begin + bt * U;
+        const int f = grp * 16 + n;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const int64_t row = nb == 0 ? f : F + f;
+            const uint8_t *bp = wpk + l_tl.expert * ebytes + row * (d / 2) + (int64_t)c * (kKStep / 2) + g * 16;
+#pragma unroll
+            for (int u = 0; u < U; ++u) b[u][nb] = *reinterpret_cast<const uint4 *>(bp + u * (kKStep / 2));
+            const uint8_t *spp = sc + l_tl.expert * escales + row * (d / 32) + c * 4;
+            if constexpr (U == 4) {
+                const uint4 v = *reinterpret_cast<const uint4 *>(spp);
+                sv[0][nb] = v.x;
+                sv[1 % U][nb] = v.y;
+                sv[2 % U][nb] = v.z;
+                sv[3 % U][nb] = v.w;
+            } else if constexpr (U == 2) {
+                const uint2 v = *reinterpret_cast<const uint2 *>(spp);
+                sv[0][nb] = v.x;
+                sv[1 % U][nb] = v.y;
+            } else {
+                sv[0][nb] = *reinterpret_cast<const uint32_t *>(spp);
+            }
+        }
+    };
+
+    // ---- activation staging: the tile's FP8 rows and scales -> LDS --------
+    int c_ti = -1;
+    Tile c_tl{0, 0, 0, 0};
+    auto stage = [&](int ti) {
+        c_tl = tiles[ti];
+        c_ti = ti;
+        const int q = d / 16, qs = d / 32 / 16;  // 16-byte units per part row / scale row
+        for (int r = 0; r < c_tl.nrows; ++r) {
+            const int64_t tok = perm[c_tl.row0 + r] / k;
+            const uint4 *sh = reinterpret_cast<const uint4 *>(ghi + tok * d);
+            const uint4 *sl = reinterpret_cast<const uint4 *>(glo + tok * d);
+            uint4 *dh = reinterpret_cast<uint4 *>(xhi + (size_t)r * d);
+            uint4 *dl = reinterpret_cast<uint4 *>(xlo + (size_t)r * d);
+            for (int j = threadIdx.x; j < q; j += 256) {
+                dh[j] = sh[j];
+                dl[j] = sl[j];
+            }
+            const uint4 *ssh = reinterpret_cast<const uint4 *>(gsh + tok * (d / 32));
+            const uint4 *ssl = reinterpret_cast<const uint4 *>(gsl + tok * (d / 32));
+            if ((int)threadIdx.x < qs) {
+                reinterpret_cast<uint4 *>(xsh + (size_t)r * (d / 32))[threadIdx.x] = ssh[threadIdx.x];
+                reinterpret_cast<uint4 *>(xsl + (size_t)r * (d / 32))[threadIdx.x] = ssl[threadIdx.x];
+            }
+        }
+        lds_barrier();
+    };
+
+    floatx4_t acc[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[nb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+
+    auto consume = [&](const uint4 (&b)[U][NB], const uint32_t (&sv)[U][NB], int st) {
+        const int it = i0 + st / nbat, bt = st % nbat;
+        const int ti = it / groups, grp = it - ti * groups;
+        // a new tile's rows replace the old ones: every wave has passed the
+        // previous item's barrier, so no wave still reads them
+        if (ti != c_ti) stage(ti);
+        const int m = n < c_tl.nrows ? n : 0;  // rows past nrows are computed on row 0, never stored
+        const int c = c_begin + bt * U;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint4 *hp = reinterpret_cast<const uint4 *>(xhi + (size_t)m * d + (c + u) * kKStep);
+            const uint4 *lp = reinterpret_cast<const uint4 *>(xlo + (size_t)m * d + (c + u) * kKStep);
+            const uint4 h0 = hp[g], h1 = hp[4 + g], l0 = lp[g], l1 = lp[4 + g];
+            const int sidx = m * (d / 32) + (c + u) * 4 + g;
+            const uint32_t sah = xsh[sidx], sal = xsl[sidx];
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                const uint32_t sb = (sv[u][nb] >> (8 * g)) & 0xFFu;
+                acc[nb] = mfma_mx(h0, h1, b[u][nb], sah, sb, acc[nb]);
+                acc[nb] = mfma_mx(l0, l1, b[u][nb], sal, sb, acc[nb]);
+            }
+        }
+        if (bt == nbat - 1) {
+            const int par = (it - i0) & 1;
+            if (wv > 0) {
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) red[par][wv - 1][nb][lane] = acc[nb];
+            }
+            lds_barrier();
+            if (wv == 0) {
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+                    acc[nb] = ((acc[nb] + red[par][0][nb][lane]) + red[par][1][nb][lane]) + red[par][2][nb][lane];
+                const int fcol = grp * 16 + n;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = g * 4 + r;
+                    if (row < c_tl.nrows)
+                        h[(int64_t)(c_tl.row0 + row) * F + fcol] = f32_to_bf16(silu(acc[0][r]) * acc[1][r]);
+                }
+            }
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) acc[nb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+        }
+    };
+
+    load(b0, s0, 0);
+    if (total > 1) load(b1, s1, 1);
+    for (int st = 0; st < total; st += 2) {
+        consume(b0, s0, st);
+        if (st + 2 < total) load(b0, s0, st + 2);
+        if (st + 1 < total) {
+            consume(b1, s1, st + 1);
+            if (st + 3 < total) load(b1, s1, st + 3);
+        }
+    }
 }
 
 // LDS budget for the decode kernels' staged activation rows.
@@ -838,6 +1021,36 @@ constexpr int kDecodeLdsBytes = MOE_DEC_LDS;
 #endif
 constexpr int kG1NBP = MOE_G1NBP, kG1U = MOE_G1U;  // gate/up decode: 16*NBP features per workgroup
 constexpr int kG2NB = MOE_G2NB, kG2U = MOE_G2U;    // down decode: 64*NB columns per workgroup
+
+#ifndef MOE_G1SU
+#define MOE_G1SU 4
+#endif
+constexpr int kG1StreamU = MOE_G1SU;  // chunks per weight batch of the streaming kernel
+
+// Workgroups that fit on the device at once for a 256-thread kernel with
+// `lds` bytes of dynamic LDS (cached per device, kernel and size; 0 on error).
+static int persistent_grid(const void *kfn, size_t lds)
+{
+    struct Entry {
+        const void *fn;
+        size_t lds;
+        int dev, grid;
+    };
+    static std::mutex mu;
+    static Entry cache[32];
+    static int used = 0;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    std::lock_guard<std::mutex> lock(mu);
+    for (int i = 0; i < used; ++i)
+        if (cache[i].fn == kfn && cache[i].lds == lds && cache[i].dev == dev) return cache[i].grid;
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kfn, 256, lds) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    const int grid = per_cu * cus;
+    if (used < 32) cache[used++] = Entry{kfn, lds, dev, grid};
+    return grid;
+}
 
 hipError_t launch_gemm1(const Shape &s, const Plan &p, const Workspace &ws, const uint16_t *x,
                         const uint8_t *wpk, const uint8_t *sc, hipStream_t st)
@@ -855,6 +1068,14 @@ hipError_t launch_gemm1(const Shape &s, const Plan &p, const Workspace &ws, cons
         const int64_t grid = 8 * ((max_tiles(s, p.tile_rows) * pa.ntn + 7) / 8);
         gemm_tiled_kernel<true><<<(unsigned)grid, 256, 0, st>>>(pa);
 #endif
+    } else if (p.stream) {
+        const int R = p.tile_rows;
+        const size_t lds = (size_t)R * (2 * s.d + 2 * (s.d / 32));
+        auto kfn = gemm1_stream_kernel<kG1StreamU>;
+        const int grid = persistent_grid(reinterpret_cast<const void *>(kfn), lds);
+        if (grid <= 0) return hipErrorInvalidConfiguration;
+        kfn<<<grid, 256, lds, st>>>(ws.xhi, ws.xlo, ws.xshi, ws.xslo, ws.perm, ws.tiles, ws.ntiles,
+                                    wpk, sc, ws.h, s.d, s.F, s.k, R);
     } else {
         const int groups = s.F / (16 * kG1NBP);
         const int64_t grid = max_tiles(s, p.tile_rows) * groups;

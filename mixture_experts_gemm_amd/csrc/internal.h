@@ -29,8 +29,15 @@ struct Shape {
 // Which kernels run.  Few rows per expert (decode): 16-row tiles, one wave
 // per 16 output columns streaming weights.  Many rows per expert (prefill):
 // 128-row tiles staged through LDS and shared by a workgroup.
+// Very few tokens (at most kStreamMaxT, d a multiple of 2048): the gate/up
+// product runs as a persistent streaming kernel whose tiles hold at most
+// kStreamRows rows (an expert chosen by more tokens gets several tiles).
+constexpr int kStreamMaxT = 8;
+constexpr int kStreamRows = 2;
+
 struct Plan {
     bool tiled;
+    bool stream;    // persistent streaming gate/up kernel (decode)
     int tile_rows;  // rows per tile of the tile list
     int ssq_cols;   // columns of o per partial sum of squares
     bool small_route;  // single-workgroup routing (T <= 64 and T*k <= 4096)
@@ -41,14 +48,16 @@ inline Plan make_plan(const Shape &s)
     Plan p;
     const int64_t S = s.S();
     p.tiled = S >= (int64_t)32 * s.E && s.d % 256 == 0 && s.F % 128 == 0;
-    p.tile_rows = p.tiled ? 128 : 16;
+    p.stream = !p.tiled && s.d % 2048 == 0 && s.T <= kStreamMaxT;
+    p.tile_rows = p.tiled ? 128 : p.stream ? (s.T < kStreamRows ? s.T : kStreamRows) : 16;
+    if (p.tile_rows < 1) p.tile_rows = 1;
     p.ssq_cols = 64;  // both down kernels reduce o^2 over 64-column groups
     p.small_route = s.T <= kChunkTokens && S <= 4096;
     return p;
 }
 
-// Upper bound of the tile count for any plan (16-row tiles give the most).
-inline int64_t max_tiles(const Shape &s, int tile_rows = 16)
+// Upper bound of the tile count for tiles of tile_rows rows (1: any plan).
+inline int64_t max_tiles(const Shape &s, int tile_rows)
 {
     int64_t S = s.S();
     int64_t u = S < s.E ? S : s.E;
@@ -84,8 +93,8 @@ struct Workspace {
 Workspace carve_workspace(const Shape &s, void *base);
 
 // ---- launchers (all asynchronous on `st`) ---------------------------------
-hipError_t launch_router(const Shape &s, const uint16_t *x, const float *wr, float *scores,
-                         hipStream_t st);
+hipError_t launch_router(const Shape &s, const Plan &p, const Workspace &ws, const uint16_t *x,
+                         const float *wr, hipStream_t st);
 hipError_t launch_topk(const Shape &s, const Plan &p, const Workspace &ws, hipStream_t st);
 hipError_t launch_group(const Shape &s, const Plan &p, const Workspace &ws, hipStream_t st);
 hipError_t launch_gemm1(const Shape &s, const Plan &p, const Workspace &ws, const uint16_t *x,

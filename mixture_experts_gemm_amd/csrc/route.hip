@@ -28,10 +28,15 @@ template <int NT>
 __global__ __launch_bounds__(256) void router_gemv_kernel(const uint16_t *__restrict__ x,
                                                           const float *__restrict__ wr,
                                                           float *__restrict__ scores, int T,
-                                                          int d, int E)
+                                                          int d, int E, uint8_t *__restrict__ xhi,
+                                                          uint8_t *__restrict__ xlo,
+                                                          uint8_t *__restrict__ xsh,
+                                                          uint8_t *__restrict__ xsl)
 {
     // blockIdx.x: expert; blockIdx.y: group of NT tokens.  Every load of a
-    // 8192-wide slice is issued before the first multiply-add.
+    // 8192-wide slice is issued before the first multiply-add.  When xhi is
+    // set, the workgroups also split the group's x rows into FP8 hi/lo parts
+    // (block j of the group by workgroup j % E) for the expert kernels.
     constexpr int R = 8;  // float4 per thread per 8192-element slice
     __shared__ float part[4][NT];
     const int e = blockIdx.x;
@@ -79,6 +84,14 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(const uint16_t *__rest
     if (threadIdx.x < NT && t0 + (int)threadIdx.x < T) {
         const int t = threadIdx.x;
         scores[(int64_t)(t0 + t) * E + e] = (part[0][t] + part[1][t]) + (part[2][t] + part[3][t]);
+    }
+    if (xhi) {
+        const int64_t nblk = (int64_t)min(NT, T - t0) * (d / 32);
+        const int64_t gb0 = (int64_t)t0 * (d / 32);
+        for (int64_t j = (int64_t)threadIdx.x * E + e; j < nblk; j += (int64_t)256 * E) {
+            const int64_t b = gb0 + j;
+            split_bf16_block(x + b * 32, xhi + b * 32, xlo + b * 32, xsh + b, xsl + b);
+        }
     }
 }
 
@@ -140,17 +153,21 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t *__rest
     }
 }
 
-hipError_t launch_router(const Shape &s, const uint16_t *x, const float *wr, float *scores,
-                         hipStream_t st)
+hipError_t launch_router(const Shape &s, const Plan &p, const Workspace &ws, const uint16_t *x,
+                         const float *wr, hipStream_t st)
 {
+    // the streaming gate/up kernel reads x as FP8 hi/lo parts, split here
+    uint8_t *xhi = p.stream ? ws.xhi : nullptr;
     if (s.T == 1) {
-        router_gemv_kernel<1><<<s.E, 256, 0, st>>>(x, wr, scores, s.T, s.d, s.E);
+        router_gemv_kernel<1><<<s.E, 256, 0, st>>>(x, wr, ws.scores, s.T, s.d, s.E, xhi, ws.xlo,
+                                                   ws.xshi, ws.xslo);
     } else if (s.T <= 32) {
-        router_gemv_kernel<4><<<dim3(s.E, (s.T + 3) / 4), 256, 0, st>>>(x, wr, scores, s.T, s.d, s.E);
+        router_gemv_kernel<4><<<dim3(s.E, (s.T + 3) / 4), 256, 0, st>>>(
+            x, wr, ws.scores, s.T, s.d, s.E, xhi, ws.xlo, ws.xshi, ws.xslo);
     } else {
         const int eblocks = (s.E + 15) / 16;
         const int64_t waves = (int64_t)((s.T + 15) / 16) * eblocks;
-        router_mfma_kernel<<<(unsigned)((waves + 3) / 4), 256, 0, st>>>(x, wr, scores, s.T, s.d,
+        router_mfma_kernel<<<(unsigned)((waves + 3) / 4), 256, 0, st>>>(x, wr, ws.scores, s.T, s.d,
                                                                           s.E, eblocks);
     }
     return hipGetLastError();

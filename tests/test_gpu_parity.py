@@ -122,6 +122,25 @@ def test_decode_all_tokens(name):
     _check_tokens(L, out, np.arange(L.shape.T), name)
 
 
+@pytest.mark.parametrize("T,d", [(3, 2048), (5, 2048), (8, 4096)])
+def test_few_tokens_hot_expert(T, d):
+    # every token picks expert 3 first, so its segment holds all T tokens and
+    # is cut into several tiles on the few-token (streaming) path
+    w = synth.custom_workload(T=T, d=d, E=16, k=4, F=256, seed=23 + T, zipf=True)
+    wr = synth.make_router(w)
+    wr[:, 0] = 0.0
+    wr[3, 0] = 50.0
+    x = synth.make_tokens(w, wr)
+    W, S = synth.make_experts(w)
+    a, b = synth.make_gates(w)
+    L = synth.LayerInputs(w.shape, x, wr, W, S, a, b, w.shape.k)
+    _say("few tokens hot expert", T, d)
+    out, dbg = run_layer(L)
+    _check_routing(L, dbg, f"hot T={T} d={d}")
+    assert np.all(dbg["ids"][:, 0] == 3)
+    _check_tokens(L, out, np.arange(T), f"hot T={T} d={d}")
+
+
 # ------------------------------------------------------------------ invariants
 
 def test_gate_identity_bitwise():
