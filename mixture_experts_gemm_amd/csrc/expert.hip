@@ -406,9 +406,6 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(const PipeArgs pa)
     __shared__ uint4 As0[kTM * kSlots], As1[kTM * kSlots], As2[kTM * kSlots];
     __shared__ uint4 Bs0[kTN * 4], Bs1[kTN * 4], Bs2[kTN * 4];
     __shared__ uint32_t Ss0[kTN], Ss1[kTN], Ss2[kTN];
-#if MOE_BPF
-    __shared__ uint32_t Pf[256];
-#endif
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int d = pa.d, F = pa.F;
@@ -599,11 +596,10 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(const PipeArgs pa)
 // =========================================================================
 typedef int v8i_t __attribute__((__vector_size__(8 * sizeof(int))));
 
-constexpr int kAHLoads = kTM * 8 / 256;                      // 4 per part per thread
-#ifndef MOE_BPF
-#define MOE_BPF 0  // chunks ahead that B rows are touched in L2 (0: off)
+#ifndef MOE_MX_WAVES
+#define MOE_MX_WAVES 8  // waves per workgroup of the MX tiled kernel (4 or 8)
 #endif
-constexpr int kMxChunkLoads = 2 * kAHLoads + 1 + kBLoads + 1 + (MOE_BPF > 0);  // A hi, A lo, A scales, B, B scales[, B touch]
+constexpr int kMxWaves = MOE_MX_WAVES;
 
 struct MxArgs {
     const uint8_t *ahi, *alo;     // activation parts [rows][K] (FP8)
@@ -628,17 +624,19 @@ __device__ __forceinline__ floatx4_t mfma_mx(const uint4 &a0, const uint4 &a1, c
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 0, 4, 0, (int)sa, 0, (int)sb);
 }
 
-template <bool GATE_UP>
-__global__ __launch_bounds__(256) void gemm_mx_kernel(const MxArgs pa)
+template <bool GATE_UP, int NW>
+__global__ __launch_bounds__(64 * NW) void gemm_mx_kernel(const MxArgs pa)
 {
+    // NW waves: WM along M (rows), 2 along N; each wave owns RW rows x 128 columns
+    constexpr int WM = NW / 2, RW = kTM / WM, MB = RW / 16;
+    constexpr int AL = kTM * 8 / (64 * NW);  // A-part loads per thread per chunk (each part)
+    constexpr int BL = kTN * 4 / (64 * NW);  // B loads per thread per chunk
+    constexpr int NLOADS = 2 * AL + BL + (NW == 4 ? 2 : 1);
     __shared__ uint4 Ah0[kTM * 8], Ah1[kTM * 8], Ah2[kTM * 8];
     __shared__ uint4 Al0[kTM * 8], Al1[kTM * 8], Al2[kTM * 8];
     __shared__ uint32_t Ac0[kTM * 2], Ac1[kTM * 2], Ac2[kTM * 2];
     __shared__ uint4 Bs0[kTN * 4], Bs1[kTN * 4], Bs2[kTN * 4];
     __shared__ uint32_t Ss0[kTN], Ss1[kTN], Ss2[kTN];
-#if MOE_BPF
-    __shared__ uint32_t Pf[256];
-#endif
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int d = pa.d, F = pa.F;
@@ -654,21 +652,16 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(const MxArgs pa)
     };
 
     // ---- load assignment ----------------------------------------------------
-    // A parts: load i of this wave fills rows 8*(4i + wv) + lane/8, stored slot lane%8
-    const int a_row_lo = lane >> 3;
-    const uint8_t *ahsrc[kAHLoads], *alsrc[kAHLoads];
+    // A parts: load i of this wave fills rows 8*(NW*i + wv) + lane/8, stored slot lane%8
+    const uint8_t *ahsrc[AL], *alsrc[AL];
 #pragma unroll
-    for (int i = 0; i < kAHLoads; ++i) {
-        const int r = 8 * (4 * i + wv) + a_row_lo;
+    for (int i = 0; i < AL; ++i) {
+        const int r = 8 * (NW * i + wv) + (lane >> 3);
         const int slot = (lane & 7) ^ (r & 7);
         const int64_t off = src_row(r) * K + slot * 16;
         ahsrc[i] = pa.ahi + off;
         alsrc[i] = pa.alo + off;
     }
-    // A scales: dword 64*wv + lane = (row, part) with row = that / 2
-    const int asr = (64 * wv + lane) >> 1;
-    const uint8_t *acsrc = ((lane & 1) ? pa.aslo : pa.ashi) + src_row(asr) * (K / 32);
-    // B as in the bf16 kernel
     auto wrow_of = [&](int rho) -> int64_t {
         if (GATE_UP) {
             const int f = nt * 128 + (rho >> 7) * 64 + ((rho >> 4) & 3) * 16 + (rho & 15);
@@ -680,44 +673,42 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(const MxArgs pa)
     const uint8_t *es = pa.sc + tl.expert * escales;
     const int64_t wbase = GATE_UP ? 0 : (int64_t)2 * F * (d / 2);
     const int64_t sbase = GATE_UP ? 0 : (int64_t)2 * F * (d / 32);
-    const uint8_t *bsrc[kBLoads];
+    const uint8_t *bsrc[BL];
 #pragma unroll
-    for (int i = 0; i < kBLoads; ++i) {
-        const int rho = 16 * (4 * i + wv) + (lane >> 2);
+    for (int i = 0; i < BL; ++i) {
+        const int rho = 16 * (NW * i + wv) + (lane >> 2);
         const int gsrc = (lane & 3) ^ bswz(rho);
         bsrc[i] = eb + wbase + wrow_of(rho) * (K / 2) + gsrc * 16;
     }
-    const uint8_t *ssrc = es + sbase + wrow_of(64 * wv + lane) * (K / 32);
+    // scales: A dword q = (row q/2, hi or lo part by q%2); B dword q = row q.
+    // 4 waves: every thread loads one of each; 8 waves: waves 0-3 A, 4-7 B.
+    const int q = (NW == 4 ? 64 * wv : 64 * (wv & 3)) + lane;
+    const uint8_t *acsrc = ((lane & 1) ? pa.aslo : pa.ashi) + src_row(q >> 1) * (K / 32);
+    const uint8_t *ssrc = es + sbase + wrow_of(q) * (K / 32);
     const int nk = K / kKStep;
-#if MOE_BPF
-    const uint8_t *pfsrc = eb + wbase + wrow_of(64 * wv + lane) * (K / 2);
-#endif
 
     const int wvu = __builtin_amdgcn_readfirstlane(wv);
+    const int qwu = NW == 4 ? wvu : (wvu & 3);
     auto issue = [&](int kc, uint4 *Ah, uint4 *Al, uint32_t *Ac, uint4 *Bs, uint32_t *Ss) {
 #pragma unroll
-        for (int i = 0; i < kAHLoads; ++i) dma16(ahsrc[i] + kc * kKStep, lds_off(Ah + (4 * i + wvu) * 64));
+        for (int i = 0; i < AL; ++i) dma16(ahsrc[i] + kc * kKStep, lds_off(Ah + (NW * i + wvu) * 64));
 #pragma unroll
-        for (int i = 0; i < kAHLoads; ++i) dma16(alsrc[i] + kc * kKStep, lds_off(Al + (4 * i + wvu) * 64));
-        dma4(acsrc + kc * 4, lds_off(Ac + 64 * wvu));
+        for (int i = 0; i < AL; ++i) dma16(alsrc[i] + kc * kKStep, lds_off(Al + (NW * i + wvu) * 64));
+        if (NW == 4 || wvu < 4) dma4(acsrc + kc * 4, lds_off(Ac + 64 * qwu));
 #pragma unroll
-        for (int i = 0; i < kBLoads; ++i) dma16(bsrc[i] + kc * (kKStep / 2), lds_off(Bs + (4 * i + wvu) * 64));
-        dma4(ssrc + kc * (kKStep / 32), lds_off(Ss + 64 * wvu));
-#if MOE_BPF
-        const int pc = kc + MOE_BPF < nk ? kc + MOE_BPF : nk - 1;
-        dma4(pfsrc + pc * (kKStep / 2), lds_off(Pf + 64 * wvu));
-#endif
+        for (int i = 0; i < BL; ++i) dma16(bsrc[i] + kc * (kKStep / 2), lds_off(Bs + (NW * i + wvu) * 64));
+        if (NW == 4 || wvu >= 4) dma4(ssrc + kc * (kKStep / 32), lds_off(Ss + 64 * qwu));
     };
 
     // ---- compute assignment -------------------------------------------------
-    const int wm = wv & 1, wn = wv >> 1;
+    const int wm = wv % WM, wn = wv / WM;
     const int n16 = lane & 15, g = lane >> 4;
-    int mb_act = (tl.nrows - wm * 64 + 15) >> 4;
-    mb_act = mb_act < 0 ? 0 : (mb_act > 4 ? 4 : mb_act);
+    int mb_act = (tl.nrows - wm * RW + 15) >> 4;
+    mb_act = mb_act < 0 ? 0 : (mb_act > MB ? MB : mb_act);
 
-    floatx4_t acc[4][8];
+    floatx4_t acc[MB][8];
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int nb = 0; nb < 8; ++nb) acc[mb][nb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
@@ -733,19 +724,18 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(const MxArgs pa)
             bsc[nb] = (Ss[rho] >> (8 * g)) & 0xFFu;
         }
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
+        for (int mb = 0; mb < MB; ++mb) {
             if (F_ || mb < mb_act) {
-                const int row = wm * 64 + mb * 16 + n16;
+                const int row = wm * RW + mb * 16 + n16;
                 const int sw = row & 7;
                 const uint4 h0 = Ah[row * 8 + (g ^ sw)], h1 = Ah[row * 8 + ((4 + g) ^ sw)];
                 const uint4 l0 = Al[row * 8 + (g ^ sw)], l1 = Al[row * 8 + ((4 + g) ^ sw)];
                 const uint32_t sh = (Ac[row * 2] >> (8 * g)) & 0xFFu;
                 const uint32_t sl = (Ac[row * 2 + 1] >> (8 * g)) & 0xFFu;
 #pragma unroll
-                for (int nb = 0; nb < 8; ++nb) {
-                    acc[mb][nb] = mfma_mx(h0, h1, bw[nb], sh, bsc[nb], acc[mb][nb]);
-                    acc[mb][nb] = mfma_mx(l0, l1, bw[nb], sl, bsc[nb], acc[mb][nb]);
-                }
+                for (int nb = 0; nb < 8; ++nb) acc[mb][nb] = mfma_mx(h0, h1, bw[nb], sh, bsc[nb], acc[mb][nb]);
+#pragma unroll
+                for (int nb = 0; nb < 8; ++nb) acc[mb][nb] = mfma_mx(l0, l1, bw[nb], sl, bsc[nb], acc[mb][nb]);
             }
         }
     };
@@ -753,10 +743,10 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(const MxArgs pa)
     // ---- pipeline --------------------------------------------------------------
     issue(0, Ah0, Al0, Ac0, Bs0, Ss0);
     if (nk > 1) issue(1, Ah1, Al1, Ac1, Bs1, Ss1);
-    const bool full = mb_act == 4;
+    const bool full = mb_act == MB;
     auto step = [&](int kc, uint4 *Ahc, uint4 *Alc, uint32_t *Acc, uint4 *Bc, uint32_t *Sc,
                     uint4 *Ahn, uint4 *Aln, uint32_t *Acn, uint4 *Bn, uint32_t *Sn) {
-        if (kc + 1 < nk) chunk_sync<kMxChunkLoads>();
+        if (kc + 1 < nk) chunk_sync<NLOADS>();
         else chunk_sync<0>();
         if (kc + 2 < nk) issue(kc + 2, Ahn, Aln, Acn, Bn, Sn);
         if (full) compute(Ahc, Alc, Acc, Bc, Sc, std::true_type{});
@@ -772,13 +762,13 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(const MxArgs pa)
     if (GATE_UP) {
         const int fbase = nt * 128 + wn * 64;
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
+        for (int mb = 0; mb < MB; ++mb) {
             if (mb >= mb_act) continue;
 #pragma unroll
             for (int hb = 0; hb < 4; ++hb)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int row = wm * 64 + mb * 16 + g * 4 + r;
+                    const int row = wm * RW + mb * 16 + g * 4 + r;
                     if (row < tl.nrows)
                         pa.out[(int64_t)(tl.row0 + row) * F + fbase + hb * 16 + n16] =
                             f32_to_bf16(silu(acc[mb][hb][r]) * acc[mb][hb + 4][r]);
@@ -788,11 +778,11 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(const MxArgs pa)
         const int P = d / 64;
         const int cbase = nt * kTN + wn * 128;
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
+        for (int mb = 0; mb < MB; ++mb) {
             if (mb >= mb_act) continue;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int row = wm * 64 + mb * 16 + g * 4 + r;
+                const int row = wm * RW + mb * 16 + g * 4 + r;
                 float ss0 = 0.f, ss1 = 0.f;
 #pragma unroll
                 for (int nb = 0; nb < 4; ++nb) ss0 += acc[mb][nb][r] * acc[mb][nb][r];
@@ -1062,7 +1052,7 @@ hipError_t launch_gemm1(const Shape &s, const Plan &p, const Workspace &ws, cons
         MxArgs pa{ws.xhi, ws.xlo, ws.xshi, ws.xslo, ws.perm, ws.tiles, ws.ntiles, wpk, sc,
                   ws.h, nullptr, s.d, s.F, s.k, s.F / 128};
         const int64_t grid = 8 * ((max_tiles(s, p.tile_rows) * pa.ntn + 7) / 8);
-        gemm_mx_kernel<true><<<(unsigned)grid, 256, 0, st>>>(pa);
+        gemm_mx_kernel<true, kMxWaves><<<(unsigned)grid, 64 * kMxWaves, 0, st>>>(pa);
 #else
         PipeArgs pa{x, ws.perm, ws.tiles, ws.ntiles, wpk, sc, ws.h, nullptr, s.d, s.F, s.k, s.F / 128};
         const int64_t grid = 8 * ((max_tiles(s, p.tile_rows) * pa.ntn + 7) / 8);
@@ -1100,7 +1090,7 @@ hipError_t launch_gemm2(const Shape &s, const Plan &p, const Workspace &ws, cons
         MxArgs pa{ws.hhi, ws.hlo, ws.hshi, ws.hslo, nullptr, ws.tiles, ws.ntiles, wpk, sc,
                   ws.o, ws.ssq, s.d, s.F, s.k, s.d / 256};
         const int64_t grid = 8 * ((max_tiles(s, p.tile_rows) * pa.ntn + 7) / 8);
-        gemm_mx_kernel<false><<<(unsigned)grid, 256, 0, st>>>(pa);
+        gemm_mx_kernel<false, kMxWaves><<<(unsigned)grid, 64 * kMxWaves, 0, st>>>(pa);
 #else
         PipeArgs pa{ws.h, nullptr, ws.tiles, ws.ntiles, wpk, sc, ws.o, ws.ssq, s.d, s.F, s.k, s.d / 256};
         const int64_t grid = 8 * ((max_tiles(s, p.tile_rows) * pa.ntn + 7) / 8);
