@@ -55,6 +55,7 @@ def make_sets(name, nsets, device):
     import numpy as np
     import torch
 
+    from mixture_experts_gemm_amd import binding as B
     from mixture_experts_gemm_amd import synth
 
     w = synth.WORKLOADS[name]
@@ -77,7 +78,11 @@ def make_sets(name, nsets, device):
                               dtype=torch.uint8, device=device, generator=g)
             wr = torch.from_numpy(synth.make_router(w, layer=i)).to(device)
             a, b = (torch.from_numpy(v).to(device) for v in synth.make_gates(w, layer=i))
-        sets.append(dict(w=W, s=S, wr=wr, alpha=a, beta=b))
+        # the layer reads the packed weight layout; packing is a one-time load step
+        Wp, Sp = B.moe_pack_weights(W, S, s.d, s.F)
+        torch.cuda.synchronize()
+        del W, S
+        sets.append(dict(w=Wp, s=Sp, wr=wr, alpha=a, beta=b))
     x = torch.from_numpy(host.x.view(np.int16)).to(device).view(torch.bfloat16)
     return w, host, sets, x
 

@@ -51,12 +51,14 @@ extern "C" {
 enum {
     MOE_OK = 0,
     MOE_ERR_NULL = -1,      /* a required pointer is NULL                        */
-    MOE_ERR_SHAPE = -2,     /* T < 0, d or F not a positive multiple of 128,
-                               E < 1 or E > 1024, k not in [1, E], eps < 0 or
-                               not finite, or sizes that overflow int32 indexing */
+    MOE_ERR_SHAPE = -2,     /* T < 0, d not a positive multiple of 256, F not a
+                               positive multiple of 128, E < 1 or E > 1024, k not
+                               in [1, E], eps < 0 or not finite, or sizes that
+                               overflow int32 indexing                           */
     MOE_ERR_WORKSPACE = -3, /* workspace_bytes below moe_layer_workspace_size()  */
     MOE_ERR_ARCH = -4,      /* current device is not gfx950                      */
-    MOE_ERR_HIP = -5        /* a HIP runtime call or kernel launch failed        */
+    MOE_ERR_HIP = -5,       /* a HIP runtime call or kernel launch failed        */
+    MOE_ERR_ALIGN = -6      /* a device pointer is not 16-byte aligned           */
 };
 
 typedef struct moe_dims {
@@ -109,26 +111,59 @@ typedef struct moe_debug {
 size_t moe_layer_workspace_size(const moe_dims_t *dims, int32_t k);
 
 /*
+ * Natural MXFP4 expert weights (the input of moe_pack_weights):
+ *   codes  uint8, expert e at byte offset e*(3*d*F/2):
+ *            gate [F][d/2] | up [F][d/2] | down [d][F/2]
+ *          each row holds its K elements as FP4 E2M1 codes, two per byte:
+ *          element 2b in the low nibble of byte b, 2b+1 in the high nibble
+ *          (sign bit 3, exponent bits 2..1 bias 1, mantissa bit 0)
+ *   scales uint8 E8M0, expert e at byte offset e*(3*d*F/32):
+ *            gate [F][d/32] | up [F][d/32] | down [d][F/32]
+ *          scale byte s multiplies a block of 32 consecutive elements of one
+ *          row by 2^(s-127)
+ *
+ * Rearranges natural weights of E experts (dims->E, d, F; T and eps are not
+ * used) into the packed layout moe_layer_forward reads: the same bytes, with
+ * each 128-element K chunk of 256 consecutive weight rows stored as one
+ * contiguous 16 KB tile ("Muse Spark Open を段階的に分解する", section ⑬:
+ * at decode batch sizes the layer time is the read of the expert weights, so
+ * the format is chosen for that read).  Exact layout, per expert:
+ *   W1 = gate and up, K = d: tiles (nt, kc), nt < F/128, kc < d/128, at byte
+ *        (nt*(d/128) + kc)*16384; tile row r (0..255) is feature
+ *        f = nt*128 + (r/128)*64 + (r%64) of the up matrix if (r/64) is odd,
+ *        else of the gate matrix;
+ *   W2 = down, K = F: at byte d*F, tiles (nt, kc), nt < d/256, kc < F/128,
+ *        tile row r is output row nt*256 + r;
+ *   a tile row is 64 bytes: the codes of K elements 128kc..128kc+127 as four
+ *   16-byte blocks of 32 elements, block b stored in slot
+ *   b ^ (((r >> 1) ^ (r >> 3)) & 3);
+ *   scales: the same tiles, 1024 bytes each (W2 at byte d*F/16): tile row r
+ *   holds the 4 E8M0 bytes of its blocks 4kc..4kc+3 in order.
+ * Device pointers, 16-byte aligned, packed buffers of the same sizes as the
+ * natural ones and not overlapping them.  Asynchronous on `stream`; weights
+ * are packed once and reused by every layer call.
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (d, F, E rules of moe_layer_forward),
+ * MOE_ERR_ALIGN, MOE_ERR_ARCH, MOE_ERR_HIP.
+ */
+int moe_pack_weights(const moe_dims_t *dims, const uint8_t *codes, const uint8_t *scales,
+                     uint8_t *codes_packed, uint8_t *scales_packed, void *stream);
+
+/*
  * The expert layer, steps 1-6 above.
  *
  *   x               bf16 [T][d], row-major (bf16 = upper 16 bits of fp32)
  *   router_w        fp32 [E][d], row-major
- *   expert_w_packed uint8, expert e at byte offset e*(3*d*F/2):
- *                     gate [F][d/2] | up [F][d/2] | down [d][F/2]
- *                   each row holds its K elements as FP4 E2M1 codes, two per
- *                   byte: element 2b in the low nibble of byte b, 2b+1 in the
- *                   high nibble (sign bit 3, exponent bits 2..1 bias 1,
- *                   mantissa bit 0)
- *   scales          uint8 E8M0, expert e at byte offset e*(3*d*F/32):
- *                     gate [F][d/32] | up [F][d/32] | down [d][F/32]
- *                   scale byte s multiplies a block of 32 consecutive
- *                   elements of one row by 2^(s-127)
+ *   expert_w_packed uint8 [E][3*d*F/2]: the codes in the packed layout
+ *                   written by moe_pack_weights
+ *   scales          uint8 [E][3*d*F/32]: the E8M0 scales in the packed layout
  *   alpha, beta     fp32 [d]
  *   k               experts per token, 1 <= k <= E
  *   s_out           bf16 [T][d]; may be the same buffer as x (in place)
  *   workspace       device scratch of workspace_bytes, 256-byte aligned
  *   stream          hipStream_t to queue on
  *   debug           optional routing copies (see moe_debug_t) or NULL
+ *
+ * Every device pointer must be 16-byte aligned (MOE_ERR_ALIGN otherwise).
  *
  * Deterministic: the same inputs and launch give bitwise identical outputs
  * (no floating-point atomics, fixed reduction orders).
@@ -140,10 +175,10 @@ int moe_layer_forward(const moe_dims_t *dims, const void *x, const float *router
                       const moe_debug_t *debug);
 
 /*
- * Expands `rows` rows of K MXFP4 elements (layout as one matrix of
- * expert_w_packed: codes [rows][K/2], scales [rows][K/32], device pointers)
- * into bf16 out [rows][K] (device), with the same conversion the expert
- * kernels use ("Muse Spark Open を段階的に分解する", section ⑪: 4-bit values
+ * Expands `rows` rows of K MXFP4 elements in the natural layout (one matrix
+ * of the moe_pack_weights input: codes [rows][K/2], scales [rows][K/32],
+ * device pointers) into bf16 out [rows][K] (device), with the conversion the
+ * few-token expert kernels use ("Muse Spark Open を段階的に分解する", section ⑪: 4-bit values
  * are expanded to BF16 before the multiply).  Exact for every code and
  * scale bytes 1..252; above that the largest codes exceed the bf16 range and
  * give +-inf.  K must be a positive multiple of 32.

@@ -23,6 +23,7 @@ MOE_ERR_SHAPE = -2
 MOE_ERR_WORKSPACE = -3
 MOE_ERR_ARCH = -4
 MOE_ERR_HIP = -5
+MOE_ERR_ALIGN = -6
 
 
 class MoeError(RuntimeError):
@@ -62,6 +63,8 @@ def lib() -> C.CDLL:
         L.moe_layer_forward.argtypes = [C.POINTER(moe_dims_t), P, P, P, P, P, P, C.c_int32, P, P,
                                         C.c_size_t, P, C.POINTER(moe_debug_t)]
         L.moe_layer_forward.restype = C.c_int
+        L.moe_pack_weights.argtypes = [C.POINTER(moe_dims_t), P, P, P, P, P]
+        L.moe_pack_weights.restype = C.c_int
         L.moe_dequant_mxfp4.argtypes = [P, P, C.c_int64, C.c_int32, P, P]
         L.moe_dequant_mxfp4.restype = C.c_int
         L.moe_status_string.argtypes = [C.c_int]
@@ -117,13 +120,37 @@ def workspace_for(T, d, E, F, k, eps=1e-6, device=None) -> torch.Tensor:
     return torch.empty(max(n, 256), dtype=torch.uint8, device=device or "cuda")
 
 
+def moe_pack_weights(codes, scales, d, F, *, codes_packed=None, scales_packed=None, stream=None):
+    """Natural MXFP4 expert weights -> the packed layout moe_layer_forward reads.
+
+    codes uint8 [E][3dF/2], scales uint8 [E][3dF/32] (natural row-major
+    matrices gate | up | down per expert); returns (codes_packed, scales_packed)
+    of the same shapes.
+    """
+    E = codes.shape[0]
+    _check(codes, "codes", torch.uint8, (E, 3 * d * F // 2))
+    _check(scales, "scales", torch.uint8, (E, 3 * d * F // 32))
+    if codes_packed is None:
+        codes_packed = torch.empty_like(codes)
+    if scales_packed is None:
+        scales_packed = torch.empty_like(scales)
+    _check(codes_packed, "codes_packed", torch.uint8, (E, 3 * d * F // 2))
+    _check(scales_packed, "scales_packed", torch.uint8, (E, 3 * d * F // 32))
+    rc = lib().moe_pack_weights(C.byref(_dims(0, d, E, F, 1e-6)), _ptr(codes), _ptr(scales),
+                                _ptr(codes_packed), _ptr(scales_packed), _stream(stream))
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_pack_weights")
+    return codes_packed, scales_packed
+
+
 def moe_layer_forward(x, router_w, expert_w_packed, scales, alpha, beta, k, *, F=None,
                       eps=1e-6, s_out=None, workspace=None, stream=None, debug=None):
     """Runs the layer; returns s_out (bf16 [T][d]).
 
-    x bf16 [T][d]; router_w fp32 [E][d]; expert_w_packed uint8 [E][3dF/2];
-    scales uint8 [E][3dF/32]; alpha, beta fp32 [d].  debug: optional dict of
-    preallocated device tensors among ids/weights/offsets/perm/inv.
+    x bf16 [T][d]; router_w fp32 [E][d]; expert_w_packed uint8 [E][3dF/2] and
+    scales uint8 [E][3dF/32], both as written by moe_pack_weights; alpha,
+    beta fp32 [d].  debug: optional dict of preallocated device tensors among
+    ids/weights/offsets/perm/inv, and "events": {stage: (begin, end)}.
     """
     T, d = x.shape
     E = router_w.shape[0]

@@ -4,6 +4,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <initializer_list>
 
 #include "../../include/moe.h"
 #include "internal.h"
@@ -55,7 +56,7 @@ Workspace carve_workspace(const Shape &s, void *base)
 static bool shape_ok(const moe_dims_t *dm, int32_t k)
 {
     if (dm->T < 0 || dm->d <= 0 || dm->F <= 0 || dm->E < 1 || dm->E > 1024) return false;
-    if (dm->d % 128 || dm->F % 128) return false;
+    if (dm->d % 256 || dm->F % 128) return false;
     if (k < 1 || k > dm->E) return false;
     if (!(dm->eps >= 0.0f) || !isfinite(dm->eps)) return false;
     const int64_t S = (int64_t)dm->T * k;
@@ -95,6 +96,13 @@ static int check_arch()
     return st == 1 ? MOE_OK : MOE_ERR_ARCH;
 }
 
+static bool aligned16(std::initializer_list<const void *> ptrs)
+{
+    for (const void *p : ptrs)
+        if (reinterpret_cast<uintptr_t>(p) & 15) return false;
+    return true;
+}
+
 }  // namespace moe
 
 using namespace moe;
@@ -116,6 +124,8 @@ extern "C" int moe_layer_forward(const moe_dims_t *dims, const void *x, const fl
     if (dims->T == 0) return MOE_OK;
     if (!x || !router_w || !expert_w_packed || !scales || !alpha || !beta || !s_out || !workspace)
         return MOE_ERR_NULL;
+    if (!aligned16({x, router_w, expert_w_packed, scales, alpha, beta, s_out}))
+        return MOE_ERR_ALIGN;
     const Shape s = to_shape(dims, k);
     const Workspace need = carve_workspace(s, nullptr);
     if (workspace_bytes < need.bytes) return MOE_ERR_WORKSPACE;
@@ -167,6 +177,26 @@ extern "C" int moe_layer_forward(const moe_dims_t *dims, const void *x, const fl
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
+extern "C" int moe_pack_weights(const moe_dims_t *dims, const uint8_t *codes, const uint8_t *scales,
+                                uint8_t *codes_packed, uint8_t *scales_packed, void *stream)
+{
+    if (!dims) return MOE_ERR_NULL;
+    if (dims->d <= 0 || dims->F <= 0 || dims->d % 256 || dims->F % 128 || dims->E < 1 ||
+        dims->E > 1024)
+        return MOE_ERR_SHAPE;
+    if ((int64_t)dims->E * 3 * dims->d * (int64_t)dims->F / 32 >= ((int64_t)1 << 40))
+        return MOE_ERR_SHAPE;
+    if (!codes || !scales || !codes_packed || !scales_packed) return MOE_ERR_NULL;
+    if (!aligned16({codes, scales, codes_packed, scales_packed})) return MOE_ERR_ALIGN;
+    int rc = check_arch();
+    if (rc != MOE_OK) return rc;
+    (void)hipGetLastError();
+    if (launch_pack(codes, scales, dims->E, dims->d, dims->F, codes_packed, scales_packed,
+                    static_cast<hipStream_t>(stream)) != hipSuccess)
+        return MOE_ERR_HIP;
+    return MOE_OK;
+}
+
 extern "C" int moe_dequant_mxfp4(const uint8_t *codes, const uint8_t *scales, int64_t rows,
                                  int32_t K, void *out_bf16, void *stream)
 {
@@ -191,6 +221,7 @@ extern "C" const char *moe_status_string(int status)
     case MOE_ERR_WORKSPACE: return "workspace too small or not 256-byte aligned";
     case MOE_ERR_ARCH: return "current device is not gfx950";
     case MOE_ERR_HIP: return "HIP runtime or kernel launch error";
+    case MOE_ERR_ALIGN: return "a device pointer is not 16-byte aligned";
     default: return "unknown status";
     }
 }

@@ -5,37 +5,43 @@
 //              what passes, up how much, down maps back to the token width
 //              (here SwiGLU: h = silu(g) * u, o = h W_down^T);
 //   section ⑪  the weights are 4-bit values sharing a small scale per block
-//              and are expanded to BF16 for the multiply (here the gfx950
-//              scaled convert expands FP4 E2M1 x E8M0 straight into bf16
-//              MFMA operands in registers);
+//              and are expanded to BF16 for the multiply.  Here the few-row
+//              kernels expand FP4 E2M1 x E8M0 into bf16 MFMA operands with the
+//              gfx950 scaled convert; the streaming and tiled kernels feed the
+//              codes and scales unexpanded to the scaled MX MFMA, with the
+//              bf16 activations split exactly into two FP8 parts;
 //   section ⑬  below ~58 tokens per expert the time is the weight read, above
 //              it the multiply: the decode kernels are built to keep weight
 //              bytes in flight, the tiled kernels to keep the MFMA pipe busy.
 //
-// Operand layout shared by every kernel here (mfma 16x16x32 bf16): lane l
-// holds A[m = l%16][k] and B[k][n = l%16] for the 8 k of k-group l/16 and
-// step s: k = 32*(l/16) + 8*s + [0..8) inside a 128-wide K chunk.  So one
-// 16-byte weight load per lane is exactly one 32-element scale block, and
-// four MFMA steps consume it.  The order of k inside the instruction does not
-// matter because A and B use the same map.
+// Weights are read in the packed tile layout of layout.h.
+//
+// bf16 operand layout (mfma 16x16x32 bf16): lane l holds A[m = l%16][k] and
+// B[k][n = l%16] for the 8 k of k-group l/16 and step s: k = 32*(l/16) + 8*s
+// + [0..8) inside a 128-wide K chunk.  So one 16-byte weight load per lane is
+// exactly one 32-element scale block, and four MFMA steps consume it.
 #include <mutex>
 #include <type_traits>
 
 #include "device.h"
 #include "internal.h"
+#include "layout.h"
 
 namespace moe {
 
-#ifndef MOE_TILED_MX
-#define MOE_TILED_MX 1  // prefill tiles on the scaled MX MFMA (0: bf16 MFMA with FP4 expansion)
+#ifndef MOE_DEC_LDS
+#define MOE_DEC_LDS (32 * 1024)  // LDS for the staged activation rows of the decode kernels
 #endif
-
-#ifndef MOE_G1DB
-#define MOE_G1DB 0  // gate/up decode: double-buffered weight batches
+#ifndef MOE_G1SU
+#define MOE_G1SU 4  // chunks per weight batch of the streaming gate/up kernel
 #endif
-
-constexpr int kKStep = 128;  // K elements per chunk
-constexpr int kUnroll = 4;   // chunks in flight per wave (decode kernels)
+#ifndef MOE_MX_WAVES
+#define MOE_MX_WAVES 8  // waves per workgroup of the MX tiled kernel (4 or 8)
+#endif
+constexpr int kDecodeLdsBytes = MOE_DEC_LDS;
+constexpr int kG1StreamU = MOE_G1SU;
+constexpr int kMxWaves = MOE_MX_WAVES;
+constexpr int kUnroll = 4;  // chunks per weight batch of the decode kernels
 
 __device__ __forceinline__ floatx4_t mfma_chunk(const uint4 *a, uint4 b, float scale, floatx4_t acc)
 {
@@ -46,299 +52,11 @@ __device__ __forceinline__ floatx4_t mfma_chunk(const uint4 *a, uint4 b, float s
     return acc;
 }
 
-// =========================================================================
-// Decode kernels: tiles of <= 16 grouped rows, weights streamed once.
-//
-// The tile's activation rows (usually 1-4 valid rows) are copied once into
-// LDS when they fit (rows_fit rows); each lane then reads its A fragment
-// from LDS instead of issuing per-chunk global loads, so the vector-memory
-// path carries almost only weight bytes.  Each wave streams NB blocks of 16
-// weight rows with U chunks of loads in flight.
-// =========================================================================
+// ---- small device helpers ---------------------------------------------------
 
-// gate/up: a workgroup owns 16*NBP features (NBP gate blocks + the NBP up
-// blocks of the same features); its 4 waves take quarters of the K chunks and
-// their partial sums are added in LDS in a fixed order.
-template <int NBP, int U>
-__global__ __launch_bounds__(256) void gemm1_decode_kernel(
-    const uint16_t *__restrict__ x, const int32_t *__restrict__ perm,
-    const Tile *__restrict__ tiles, const int32_t *__restrict__ ntiles,
-    const uint8_t *__restrict__ wpk, const uint8_t *__restrict__ sc, uint16_t *__restrict__ h,
-    int d, int F, int k, int groups, int rows_fit)
-{
-    constexpr int NB = 2 * NBP;
-    extern __shared__ uint4 arows[];  // [rows_fit][d/8]
-    __shared__ floatx4_t red[3][NB][64];
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const int64_t tile = blockIdx.x / groups;
-    const int grp = (int)(blockIdx.x % groups);
-    if (tile >= *ntiles) return;
-    const Tile tl = tiles[tile];
-    const int n = lane & 15, g = lane >> 4;
-    const int fbase = grp * 16 * NBP;
-    const int64_t ebytes = (int64_t)3 * d * F / 2, escales = (int64_t)3 * d * F / 32;
-    const uint8_t *bp[NB];
-    const uint32_t *sp[NB];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-        const int f = fbase + 16 * (nb % NBP) + n;
-        const int64_t row = nb < NBP ? f : F + f;
-        bp[nb] = wpk + tl.expert * ebytes + row * (d / 2) + g * 16;
-        sp[nb] = reinterpret_cast<const uint32_t *>(sc + tl.expert * escales + row * (d / 32));
-    }
-    const bool valid = n < tl.nrows;
-    const bool use_lds = tl.nrows <= rows_fit;
-    const int rowq = d / 8;  // 16-byte units per activation row
-    const int nc = d / kKStep;
-    const int c_begin = wv * nc / 4, c_end = (wv + 1) * nc / 4;
-    // weights stream through two register batches of U chunks: while one is
-    // consumed the other is in flight.  The first batches go out before the
-    // activations are staged.
-    uint4 b0[U][NB], b1[U][NB];
-    uint32_t s0[U][NB], s1[U][NB];
-    // scale words: one 16-byte load covers 4 chunks when rows and batches align
-    const bool svec = U == 4 && (d / 32) % 16 == 0 && c_begin % 4 == 0;
-    auto load_b = [&](uint4 (&b)[U][NB], uint32_t (&sw)[U][NB], int c) {
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-            if (c + u < c_end) {
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb)
-                    b[u][nb] = *reinterpret_cast<const uint4 *>(bp[nb] + (int64_t)(c + u) * (kKStep / 2));
-            }
-        if (svec && c + U <= c_end) {
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-                const uint4 v = *reinterpret_cast<const uint4 *>(sp[nb] + c);
-                sw[0][nb] = v.x;
-                sw[1 % U][nb] = v.y;
-                sw[2 % U][nb] = v.z;
-                sw[3 % U][nb] = v.w;
-            }
-        } else {
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-                if (c + u < c_end) {
-#pragma unroll
-                    for (int nb = 0; nb < NB; ++nb) sw[u][nb] = sp[nb][c + u];
-                }
-        }
-    };
-    load_b(b0, s0, c_begin);
-    if (MOE_G1DB && c_begin + U < c_end) load_b(b1, s1, c_begin + U);
-    if (use_lds) {
-        for (int q = threadIdx.x; q < tl.nrows * rowq; q += 256) {
-            const int r = q / rowq, c = q - r * rowq;
-            const int tok = perm[tl.row0 + r] / k;
-            arows[q] = *reinterpret_cast<const uint4 *>(x + (int64_t)tok * d + c * 8);
-        }
-        __syncthreads();
-    }
-    const uint16_t *ap = x + (int64_t)(valid ? perm[tl.row0 + n] / k : 0) * d + g * 32;
-    const uint4 *al = arows + n * rowq + g * 4;
-
-    floatx4_t acc[NB];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) acc[nb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-    auto consume = [&](const uint4 (&b)[U][NB], const uint32_t (&sw)[U][NB], int c) {
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-            if (c + u < c_end) {
-                uint4 a[4];
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    if (!valid) a[s] = make_uint4(0, 0, 0, 0);
-                    else if (use_lds) a[s] = al[(c + u) * (kKStep / 8) + s];
-                    else a[s] = *reinterpret_cast<const uint4 *>(ap + (c + u) * kKStep + s * 8);
-                }
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb)
-                    acc[nb] = mfma_chunk(a, b[u][nb], e8m0_to_f32((sw[u][nb] >> (8 * g)) & 0xFFu),
-                                         acc[nb]);
-            }
-    };
-#if MOE_G1DB
-    for (int c = c_begin; c < c_end; c += 2 * U) {
-        consume(b0, s0, c);
-        if (c + 2 * U < c_end) load_b(b0, s0, c + 2 * U);
-        if (c + U < c_end) {
-            consume(b1, s1, c + U);
-            if (c + 3 * U < c_end) load_b(b1, s1, c + 3 * U);
-        }
-    }
-#else
-    (void)b1;
-    (void)s1;
-    for (int c = c_begin; c < c_end; c += U) {
-        consume(b0, s0, c);
-        if (c + U < c_end) load_b(b0, s0, c + U);
-    }
-#endif
-    if (wv > 0) {
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) red[wv - 1][nb][lane] = acc[nb];
-    }
-    __syncthreads();
-    if (wv != 0) return;
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-        acc[nb] = ((acc[nb] + red[0][nb][lane]) + red[1][nb][lane]) + red[2][nb][lane];
-    // lane holds C[g*4 + r][n] of every block; gate block nb pairs with up block nb + NBP
-#pragma unroll
-    for (int nb = 0; nb < NBP; ++nb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int row = g * 4 + r;
-            if (row < tl.nrows)
-                h[(int64_t)(tl.row0 + row) * F + fbase + 16 * nb + n] =
-                    f32_to_bf16(silu(acc[nb][r]) * acc[nb + NBP][r]);
-        }
-}
-
-// down: a workgroup owns 64*NB output columns, NB 16-column blocks per wave,
-// each wave runs all of K.  The tile's h rows (contiguous in the grouped
-// order) are copied to LDS when they fit.  Epilogue: bf16 o and the sum of o^2
-// over each 16-column block.
-template <int NB, int U>
-__global__ __launch_bounds__(256) void gemm2_decode_kernel(
-    const uint16_t *__restrict__ h, const Tile *__restrict__ tiles,
-    const int32_t *__restrict__ ntiles, const uint8_t *__restrict__ wpk,
-    const uint8_t *__restrict__ sc, uint16_t *__restrict__ o, float *__restrict__ ssq, int d,
-    int F, int wgs_per_tile, int rows_fit)
-{
-    extern __shared__ uint4 arows[];  // [rows_fit][F/8]
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const int64_t tile = blockIdx.x / wgs_per_tile;
-    const int blk0 = ((int)(blockIdx.x % wgs_per_tile) * 4 + wv) * NB;
-    if (tile >= *ntiles) return;
-    const Tile tl = tiles[tile];
-    const int n = lane & 15, g = lane >> 4;
-    const int64_t ebytes = (int64_t)3 * d * F / 2, escales = (int64_t)3 * d * F / 32;
-    const uint8_t *bp[NB];
-    const uint32_t *sp[NB];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-        const int64_t row = (int64_t)(blk0 + nb) * 16 + n;
-        bp[nb] = wpk + tl.expert * ebytes + (int64_t)2 * F * (d / 2) + row * (F / 2) + g * 16;
-        sp[nb] = reinterpret_cast<const uint32_t *>(sc + tl.expert * escales +
-                                                    (int64_t)2 * F * (d / 32) + row * (F / 32));
-    }
-    const bool valid = n < tl.nrows;
-    const bool use_lds = tl.nrows <= rows_fit;
-    const int rowq = F / 8;
-    const int nc = F / kKStep;
-    uint4 b[U][NB];
-    uint32_t sw[U][NB];
-    const bool svec = U == 4 && (F / 32) % 16 == 0;
-    auto load_b = [&](int c) {
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-            if (c + u < nc) {
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb)
-                    b[u][nb] = *reinterpret_cast<const uint4 *>(bp[nb] + (int64_t)(c + u) * (kKStep / 2));
-            }
-        if (svec && c + U <= nc) {
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-                const uint4 v = *reinterpret_cast<const uint4 *>(sp[nb] + c);
-                sw[0][nb] = v.x;
-                sw[1 % U][nb] = v.y;
-                sw[2 % U][nb] = v.z;
-                sw[3 % U][nb] = v.w;
-            }
-        } else {
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-                if (c + u < nc) {
-#pragma unroll
-                    for (int nb = 0; nb < NB; ++nb) sw[u][nb] = sp[nb][c + u];
-                }
-        }
-    };
-    load_b(0);
-    if (use_lds) {
-        const uint4 *src = reinterpret_cast<const uint4 *>(h + (int64_t)tl.row0 * F);
-        for (int q = threadIdx.x; q < tl.nrows * rowq; q += 256) arows[q] = src[q];
-        __syncthreads();
-    }
-    const uint16_t *ap = h + (int64_t)(tl.row0 + (valid ? n : 0)) * F + g * 32;
-    const uint4 *al = arows + n * rowq + g * 4;
-
-    floatx4_t acc[NB];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) acc[nb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-    for (int c = 0; c < nc; c += U) {
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-            if (c + u < nc) {
-                uint4 a[4];
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    if (!valid) a[s] = make_uint4(0, 0, 0, 0);
-                    else if (use_lds) a[s] = al[(c + u) * (kKStep / 8) + s];
-                    else a[s] = *reinterpret_cast<const uint4 *>(ap + (c + u) * kKStep + s * 8);
-                }
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb)
-                    acc[nb] = mfma_chunk(a, b[u][nb], e8m0_to_f32((sw[u][nb] >> (8 * g)) & 0xFFu),
-                                         acc[nb]);
-            }
-        if (c + U < nc) load_b(c + U);
-    }
-    // sum of o^2 over the workgroup's 64*NB columns: per wave over its blocks
-    // (DPP within 16-lane rows), then the four waves in LDS in a fixed order
-    __shared__ float wsum[4][16];
-    const int P = d / (64 * NB);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        float ss = 0.f;
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            const float v = acc[nb][r];
-            ss += v * v;
-            const int row = g * 4 + r;
-            if (row < tl.nrows)
-                o[(int64_t)(tl.row0 + row) * d + (blk0 + nb) * 16 + n] = f32_to_bf16(v);
-        }
-        ss = sum16(ss);
-        if (n == 0) wsum[wv][g * 4 + r] = ss;
-    }
-    __syncthreads();
-    if (threadIdx.x < 16 && (int)threadIdx.x < tl.nrows) {
-        const int row = threadIdx.x;
-        const float t = (wsum[0][row] + wsum[1][row]) + (wsum[2][row] + wsum[3][row]);
-        ssq[(int64_t)(tl.row0 + row) * P + (int)(blockIdx.x % wgs_per_tile)] = t;
-    }
-}
-
-// =========================================================================
-// Tiled kernels: tiles of <= 128 grouped rows x 256 weight rows, all of K.
-//
-// Three-stage LDS ring per 128-wide K chunk, filled by direct-to-LDS loads
-// (global_load_lds_dwordx4: each lane's 16 bytes land at base + 16*lane):
-//   A  128 rows x 256 B bf16, 16-byte slot c of row r stored at c ^ (r & 15)
-//      so the MFMA fragment reads of 16 rows hit 16 different slots;
-//   B  256 weight rows x 64 B of FP4 codes; 16-byte slot g of row r stored
-//      at g ^ ((r>>1 ^ r>>3) & 3), so a fragment read (16 rows x 4 slots)
-//      touches every bank once;
-//   S  256 x 4 E8M0 bytes (the chunk's 4 scale blocks of each row).
-// Chunk kc+2 is in flight while chunk kc is multiplied.  Waits are explicit
-// (s_waitcnt on the wave's own outstanding loads, then s_barrier): a plain
-// __syncthreads would also drain the loads of the next chunk.
-//
-// Waves: 2 x 2, each 64 rows x 128 weight rows (4 x 8 MFMA blocks).
-// Workgroup w runs on XCD w % 8; tiles are handed out in contiguous ranges
-// per XCD so neighbouring tiles (same rows, same expert) share its L2.
-// =========================================================================
-constexpr int kTM = 128;                // rows per tile
-constexpr int kTN = 256;                // weight rows per tile
-constexpr int kSlots = kKStep / 8;      // 16-byte slots per A row per chunk (16)
-constexpr int kALoads = kTM * kSlots / 256;        // 16-byte A loads per thread per chunk (8)
-constexpr int kBLoads = kTN * (kKStep / 32) / 256; // 16-byte B loads per thread per chunk (4)
-constexpr int kChunkLoads = kALoads + kBLoads + 1; // + one 4-byte scale load
-
-// Contiguous per-XCD tile ranges; returns false for surplus workgroups.
+// Contiguous per-XCD tile ranges (workgroup w runs on XCD w % 8, so
+// neighbouring tiles -- same rows, same expert -- share that XCD's L2);
+// returns false for surplus workgroups.
 __device__ __forceinline__ bool xcd_tile(int total, int &idx)
 {
     const int per = (total + 7) >> 3;
@@ -385,198 +103,188 @@ __device__ __forceinline__ void lds_barrier()
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// B slot swizzle: row r's 16-byte slot g lives at g ^ bswz(r).
-__device__ __forceinline__ int bswz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+// =========================================================================
+// Few-row kernels (bf16 MFMA): tiles of <= 16 grouped rows, weights streamed
+// once.  The tile's activation rows (usually 1-4 valid rows) are copied once
+// into LDS when they fit (rows_fit rows); each lane then reads its A
+// fragment from LDS, so the vector-memory path carries almost only weight
+// bytes.  Each wave keeps U chunks of weight loads in flight.
+// =========================================================================
 
-struct PipeArgs {
-    const uint16_t *act;   // A rows: x (gathered) or h (grouped order)
-    const int32_t *perm;
-    const Tile *tiles;
-    const int32_t *ntiles;
-    const uint8_t *wpk;
-    const uint8_t *sc;
-    uint16_t *out;         // h or o
-    float *ssq;
-    int d, F, k, ntn;
-};
-
-template <bool GATE_UP>
-__global__ __launch_bounds__(256) void gemm_tiled_kernel(const PipeArgs pa)
+// gate/up: a workgroup owns 16 features (their gate block and up block); its
+// 4 waves take quarters of the K chunks and their partial sums are added in
+// LDS in a fixed order.
+template <int U>
+__global__ __launch_bounds__(256) void gemm1_decode_kernel(
+    const uint16_t *__restrict__ x, const int32_t *__restrict__ perm,
+    const Tile *__restrict__ tiles, const int32_t *__restrict__ ntiles,
+    const uint8_t *__restrict__ wpk, const uint8_t *__restrict__ sc, uint16_t *__restrict__ h,
+    int d, int F, int k, int groups, int rows_fit)
 {
-    __shared__ uint4 As0[kTM * kSlots], As1[kTM * kSlots], As2[kTM * kSlots];
-    __shared__ uint4 Bs0[kTN * 4], Bs1[kTN * 4], Bs2[kTN * 4];
-    __shared__ uint32_t Ss0[kTN], Ss1[kTN], Ss2[kTN];
-
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int d = pa.d, F = pa.F;
-    int idx;
-    if (!xcd_tile(*pa.ntiles * pa.ntn, idx)) return;
-    const int mt = idx / pa.ntn, nt = idx - mt * pa.ntn;
-    const Tile tl = pa.tiles[mt];
-    const int K = GATE_UP ? d : F;
-    const int64_t ebytes = (int64_t)3 * d * F / 2, escales = (int64_t)3 * d * F / 32;
-
-    // ---- load assignment ----------------------------------------------------
-    // A: load i of this wave fills LDS rows 16i + 4*wv + lane/16, stored slot lane%16
-    const int a_rlo = 4 * wv + (lane >> 4);                 // row & 15 for every i
-    const int a_slot = (lane & 15) ^ a_rlo;                 // logical 16-byte slot
-    const uint16_t *asrc[kALoads];
+    constexpr int NB = 2;  // gate block, up block
+    extern __shared__ uint4 arows[];  // [rows_fit][d/8]
+    __shared__ floatx4_t red[3][NB][64];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int64_t tile = blockIdx.x / groups;
+    const int grp = (int)(blockIdx.x % groups);
+    if (tile >= *ntiles) return;
+    const Tile tl = tiles[tile];
+    const int n = lane & 15, g = lane >> 4;
+    const WView v = w1_view(wpk, sc, tl.expert, d, F);
+    const int f = grp * 16 + n, nt = f >> 7;
+    const int rho[NB] = {w1_rho(f, false), w1_rho(f, true)};
+    const bool valid = n < tl.nrows;
+    const bool use_lds = tl.nrows <= rows_fit;
+    const int rowq = d / 8;  // 16-byte units per activation row
+    const int nc = d / kKStep;
+    const int c_begin = wv * nc / 4, c_end = (wv + 1) * nc / 4;
+    uint4 b[U][NB];
+    uint32_t sw[U][NB];
+    auto load_b = [&](int c) {
 #pragma unroll
-    for (int i = 0; i < kALoads; ++i) {
-        const int r = 16 * i + a_rlo;
-        const int rr = r < tl.nrows ? r : 0;
-        const int64_t row = GATE_UP ? (int64_t)(pa.perm[tl.row0 + rr] / pa.k) : (int64_t)(tl.row0 + rr);
-        asrc[i] = pa.act + row * (GATE_UP ? d : F) + a_slot * 8;
-    }
-    // B: load i fills LDS rows 16*(4i + wv) + lane/4, slot lane%4; scale: row 64*wv + lane
-    auto wrow_of = [&](int rho) -> int64_t {
-        if (GATE_UP) {
-            const int f = nt * 128 + (rho >> 7) * 64 + ((rho >> 4) & 3) * 16 + (rho & 15);
-            return ((rho >> 6) & 1) ? (int64_t)F + f : (int64_t)f;  // blocks 4..7 of a half: up
-        }
-        return (int64_t)nt * kTN + rho;
-    };
-    const uint8_t *eb = pa.wpk + tl.expert * ebytes;
-    const uint8_t *es = pa.sc + tl.expert * escales;
-    const int64_t wbase = GATE_UP ? 0 : (int64_t)2 * F * (d / 2);
-    const int64_t sbase = GATE_UP ? 0 : (int64_t)2 * F * (d / 32);
-    const uint8_t *bsrc[kBLoads];
+        for (int u = 0; u < U; ++u)
+            if (c + u < c_end) {
 #pragma unroll
-    for (int i = 0; i < kBLoads; ++i) {
-        const int rho = 16 * (4 * i + wv) + (lane >> 2);
-        const int gsrc = (lane & 3) ^ bswz(rho);  // logical slot stored at this lane's place
-        bsrc[i] = eb + wbase + wrow_of(rho) * (K / 2) + gsrc * 16;
-    }
-    const uint8_t *ssrc = es + sbase + wrow_of(64 * wv + lane) * (K / 32);
-
-    const int wvu = __builtin_amdgcn_readfirstlane(wv);  // wave-uniform copy for LDS bases
-    // every lane issues every load (rows past nrows re-read row 0), so each
-    // wave has exactly kChunkLoads loads per chunk for the vmcnt accounting
-    auto issue = [&](int kc, uint4 *As, uint4 *Bs, uint32_t *Ss) {
-#pragma unroll
-        for (int i = 0; i < kALoads; ++i)
-            dma16(asrc[i] + kc * kKStep, lds_off(As + (16 * i + 4 * wvu) * kSlots));
-#pragma unroll
-        for (int i = 0; i < kBLoads; ++i)
-            dma16(bsrc[i] + kc * (kKStep / 2), lds_off(Bs + (4 * i + wvu) * 64));
-        dma4(ssrc + kc * (kKStep / 32), lds_off(Ss + 64 * wvu));
-    };
-
-    // ---- compute assignment -------------------------------------------------
-    const int wm = wv & 1, wn = wv >> 1;
-    const int n16 = lane & 15, g = lane >> 4;
-    int mb_act = (tl.nrows - wm * 64 + 15) >> 4;
-    mb_act = mb_act < 0 ? 0 : (mb_act > 4 ? 4 : mb_act);
-
-    floatx4_t acc[4][8];
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 8; ++nb) acc[mb][nb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-
-    // one K chunk from one ring stage; FULL: all four 16-row blocks of the
-    // wave are live (no per-block branches, A fragments read up front)
-    auto compute = [&](const uint4 *As, const uint4 *Bs, const uint32_t *Ss, auto full) {
-        uint4 bw[8];
-        float scale[8];
-#pragma unroll
-        for (int nb = 0; nb < 8; ++nb) {
-            const int rho = wn * 128 + nb * 16 + n16;
-            bw[nb] = Bs[rho * 4 + (g ^ bswz(rho))];
-            scale[nb] = e8m0_to_f32((Ss[rho] >> (8 * g)) & 0xFFu);
-        }
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            uint4 av[4];
-#pragma unroll
-            for (int mb = 0; mb < 4; ++mb)
-                if (decltype(full)::value || mb < mb_act)
-                    av[mb] = As[(wm * 64 + mb * 16 + n16) * kSlots + ((4 * g + s) ^ n16)];
-            bf16x8_t bq[8];
-#pragma unroll
-            for (int nb = 0; nb < 8; ++nb) {
-                const uint32_t w = s == 0 ? bw[nb].x : s == 1 ? bw[nb].y : s == 2 ? bw[nb].z : bw[nb].w;
-                bq[nb] = fp4x8_to_bf16(w, scale[nb]);
-            }
-#pragma unroll
-            for (int mb = 0; mb < 4; ++mb) {
-                if (decltype(full)::value || mb < mb_act) {
-#pragma unroll
-                    for (int nb = 0; nb < 8; ++nb)
-                        acc[mb][nb] = mfma16(as_bf16x8(av[mb]), bq[nb], acc[mb][nb]);
+                for (int nb = 0; nb < NB; ++nb) {
+                    b[u][nb] = *reinterpret_cast<const uint4 *>(v.slot(nt, c + u, rho[nb], g));
+                    sw[u][nb] = *v.scales(nt, c + u, rho[nb]);
                 }
             }
+    };
+    // the first batch of weight loads goes out before the activations are staged
+    load_b(c_begin);
+    if (use_lds) {
+        for (int q = threadIdx.x; q < tl.nrows * rowq; q += 256) {
+            const int r = q / rowq, c = q - r * rowq;
+            const int tok = perm[tl.row0 + r] / k;
+            arows[q] = *reinterpret_cast<const uint4 *>(x + (int64_t)tok * d + c * 8);
         }
-    };
-
-    // ---- pipeline --------------------------------------------------------------
-    const int nk = K / kKStep;
-    issue(0, As0, Bs0, Ss0);
-    if (nk > 1) issue(1, As1, Bs1, Ss1);
-    const bool full = mb_act == 4;
-    auto step = [&](int kc, uint4 *Ac, uint4 *Bc, uint32_t *Sc, uint4 *An, uint4 *Bn, uint32_t *Sn) {
-        if (kc + 1 < nk) chunk_sync<kChunkLoads>();
-        else chunk_sync<0>();
-        if (kc + 2 < nk) issue(kc + 2, An, Bn, Sn);
-        if (full) compute(Ac, Bc, Sc, std::true_type{});
-        else if (mb_act > 0) compute(Ac, Bc, Sc, std::false_type{});
-    };
-    for (int kc = 0; kc < nk; kc += 3) {
-        step(kc, As0, Bs0, Ss0, As2, Bs2, Ss2);
-        if (kc + 1 < nk) step(kc + 1, As1, Bs1, Ss1, As0, Bs0, Ss0);
-        if (kc + 2 < nk) step(kc + 2, As2, Bs2, Ss2, As1, Bs1, Ss1);
+        __syncthreads();
     }
+    const uint16_t *ap = x + (int64_t)(valid ? perm[tl.row0 + n] / k : 0) * d + g * 32;
+    const uint4 *al = arows + n * rowq + g * 4;
 
-    // ---- epilogue ----------------------------------------------------------
-    if (GATE_UP) {
-        const int fbase = nt * 128 + wn * 64;
+    floatx4_t acc[NB];
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
-            if (mb >= mb_act) continue;
+    for (int nb = 0; nb < NB; ++nb) acc[nb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    for (int c = c_begin; c < c_end; c += U) {
 #pragma unroll
-            for (int hb = 0; hb < 4; ++hb)
+        for (int u = 0; u < U; ++u)
+            if (c + u < c_end) {
+                uint4 a[4];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = wm * 64 + mb * 16 + g * 4 + r;
-                    if (row < tl.nrows)
-                        pa.out[(int64_t)(tl.row0 + row) * F + fbase + hb * 16 + n16] =
-                            f32_to_bf16(silu(acc[mb][hb][r]) * acc[mb][hb + 4][r]);
+                for (int s = 0; s < 4; ++s) {
+                    if (!valid) a[s] = make_uint4(0, 0, 0, 0);
+                    else if (use_lds) a[s] = al[(c + u) * (kKStep / 8) + s];
+                    else a[s] = *reinterpret_cast<const uint4 *>(ap + (c + u) * kKStep + s * 8);
                 }
-        }
-    } else {
-        const int P = d / 64;
-        const int cbase = nt * kTN + wn * 128;
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
-            if (mb >= mb_act) continue;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = wm * 64 + mb * 16 + g * 4 + r;
-                float ss0 = 0.f, ss1 = 0.f;
-#pragma unroll
-                for (int nb = 0; nb < 4; ++nb) ss0 += acc[mb][nb][r] * acc[mb][nb][r];
-#pragma unroll
-                for (int nb = 4; nb < 8; ++nb) ss1 += acc[mb][nb][r] * acc[mb][nb][r];
-                ss0 = sum16(ss0);
-                ss1 = sum16(ss1);
-                if (row < tl.nrows) {
-#pragma unroll
-                    for (int nb = 0; nb < 8; ++nb)
-                        pa.out[(int64_t)(tl.row0 + row) * d + cbase + nb * 16 + n16] =
-                            f32_to_bf16(acc[mb][nb][r]);
-                    if (n16 == 0) {
-                        pa.ssq[(int64_t)(tl.row0 + row) * P + cbase / 64] = ss0;
-                        pa.ssq[(int64_t)(tl.row0 + row) * P + cbase / 64 + 1] = ss1;
-                    }
-                }
+                for (int nb = 0; nb < NB; ++nb)
+                    acc[nb] = mfma_chunk(a, b[u][nb], e8m0_to_f32((sw[u][nb] >> (8 * g)) & 0xFFu),
+                                         acc[nb]);
             }
-        }
+        if (c + U < c_end) load_b(c + U);
+    }
+    if (wv > 0) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) red[wv - 1][nb][lane] = acc[nb];
+    }
+    __syncthreads();
+    if (wv != 0) return;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+        acc[nb] = ((acc[nb] + red[0][nb][lane]) + red[1][nb][lane]) + red[2][nb][lane];
+    // lane holds C[g*4 + r][n] of both blocks
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int row = g * 4 + r;
+        if (row < tl.nrows)
+            h[(int64_t)(tl.row0 + row) * F + f] = f32_to_bf16(silu(acc[0][r]) * acc[1][r]);
+    }
+}
+
+// down: a workgroup owns 64 output columns, one 16-column block per wave,
+// each wave runs all of K.  The tile's h rows (contiguous in the grouped
+// order) are copied to LDS when they fit.  Epilogue: bf16 o and the sum of
+// o^2 over the workgroup's 64 columns.
+template <int U>
+__global__ __launch_bounds__(256) void gemm2_decode_kernel(
+    const uint16_t *__restrict__ h, const Tile *__restrict__ tiles,
+    const int32_t *__restrict__ ntiles, const uint8_t *__restrict__ wpk,
+    const uint8_t *__restrict__ sc, uint16_t *__restrict__ o, float *__restrict__ ssq, int d,
+    int F, int wgs_per_tile, int rows_fit)
+{
+    extern __shared__ uint4 arows[];  // [rows_fit][F/8]
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int64_t tile = blockIdx.x / wgs_per_tile;
+    const int col0 = ((int)(blockIdx.x % wgs_per_tile) * 4 + wv) * 16;
+    if (tile >= *ntiles) return;
+    const Tile tl = tiles[tile];
+    const int n = lane & 15, g = lane >> 4;
+    const WView v = w2_view(wpk, sc, tl.expert, d, F);
+    const int orow = col0 + n, nt = orow >> 8, rho = orow & 255;
+    const bool valid = n < tl.nrows;
+    const bool use_lds = tl.nrows <= rows_fit;
+    const int rowq = F / 8;
+    const int nc = F / kKStep;
+    uint4 b[U];
+    uint32_t sw[U];
+    auto load_b = [&](int c) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (c + u < nc) {
+                b[u] = *reinterpret_cast<const uint4 *>(v.slot(nt, c + u, rho, g));
+                sw[u] = *v.scales(nt, c + u, rho);
+            }
+    };
+    load_b(0);
+    if (use_lds) {
+        const uint4 *src = reinterpret_cast<const uint4 *>(h + (int64_t)tl.row0 * F);
+        for (int q = threadIdx.x; q < tl.nrows * rowq; q += 256) arows[q] = src[q];
+        __syncthreads();
+    }
+    const uint16_t *ap = h + (int64_t)(tl.row0 + (valid ? n : 0)) * F + g * 32;
+    const uint4 *al = arows + n * rowq + g * 4;
+
+    floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < nc; c += U) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (c + u < nc) {
+                uint4 a[4];
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    if (!valid) a[s] = make_uint4(0, 0, 0, 0);
+                    else if (use_lds) a[s] = al[(c + u) * (kKStep / 8) + s];
+                    else a[s] = *reinterpret_cast<const uint4 *>(ap + (c + u) * kKStep + s * 8);
+                }
+                acc = mfma_chunk(a, b[u], e8m0_to_f32((sw[u] >> (8 * g)) & 0xFFu), acc);
+            }
+        if (c + U < nc) load_b(c + U);
+    }
+    // sum of o^2 over the workgroup's 64 columns: per wave over its block
+    // (DPP within 16-lane rows), then the four waves in LDS in a fixed order
+    __shared__ float wsum[4][16];
+    const int P = d / 64;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const float val = acc[r];
+        const int row = g * 4 + r;
+        if (row < tl.nrows) o[(int64_t)(tl.row0 + row) * d + col0 + n] = f32_to_bf16(val);
+        const float ss = sum16(val * val);
+        if (n == 0) wsum[wv][g * 4 + r] = ss;
+    }
+    __syncthreads();
+    if (threadIdx.x < 16 && (int)threadIdx.x < tl.nrows) {
+        const int row = threadIdx.x;
+        const float t = (wsum[0][row] + wsum[1][row]) + (wsum[2][row] + wsum[3][row]);
+        ssq[(int64_t)(tl.row0 + row) * P + (int)(blockIdx.x % wgs_per_tile)] = t;
     }
 }
 
 // =========================================================================
-// MX tiled kernels (prefill): same tiles, ring and wave layout as above, but
-// the multiply is the gfx950 scaled MX MFMA (16x16x128, f8f6f4): the FP4
+// MX tiled kernels (prefill): tiles of <= 128 grouped rows x 256 weight rows,
+// all of K, on the gfx950 scaled MX MFMA (16x16x128, f8f6f4).  The FP4
 // weights and their E8M0 scales go into the instruction as they are stored,
 // so nothing is expanded in registers.  The bf16 activations arrive split
 // into two FP8 E4M3 parts (split_rows_kernel): a = hi*2^sh + lo*2^sl, exact
@@ -590,16 +298,18 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(const PipeArgs pa)
 //     bytes 16-31 = K 64+16g..64+16g+15 of the chunk; scale_a of lane group
 //     g applies to the A values that meet B block g, i.e. activation block g
 //     (K 32g..32g+31), so the activation split uses the natural 32-blocks.
-// LDS per stage: A hi and lo 128 rows x 128 B each (16-byte slot c of row r
-// at c ^ (r & 7)), A scales 128 x (hi word, lo word), B and B scales as in
-// the bf16 kernel.  150.5 KB for three stages.
+//
+// Three-stage LDS ring per 128-wide K chunk, filled by direct-to-LDS loads:
+// A hi and lo 128 rows x 128 B each (16-byte slot c of row r at c ^ (r & 7)),
+// A scales 128 x (hi word, lo word), and the chunk's weight tile and scale
+// tile copied linearly (the packed layout is already the LDS layout).
+// 150.5 KB for three stages; chunk kc+2 is in flight while chunk kc is
+// multiplied.  Waits are explicit vmcnt counts.
 // =========================================================================
-typedef int v8i_t __attribute__((__vector_size__(8 * sizeof(int))));
+constexpr int kTM = 128;  // rows per tile
+constexpr int kTN = 256;  // weight rows per tile (one packed weight tile)
 
-#ifndef MOE_MX_WAVES
-#define MOE_MX_WAVES 8  // waves per workgroup of the MX tiled kernel (4 or 8)
-#endif
-constexpr int kMxWaves = MOE_MX_WAVES;
+typedef int v8i_t __attribute__((__vector_size__(8 * sizeof(int))));
 
 struct MxArgs {
     const uint8_t *ahi, *alo;     // activation parts [rows][K] (FP8)
@@ -630,7 +340,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_mx_kernel(const MxArgs pa)
     // NW waves: WM along M (rows), 2 along N; each wave owns RW rows x 128 columns
     constexpr int WM = NW / 2, RW = kTM / WM, MB = RW / 16;
     constexpr int AL = kTM * 8 / (64 * NW);  // A-part loads per thread per chunk (each part)
-    constexpr int BL = kTN * 4 / (64 * NW);  // B loads per thread per chunk
+    constexpr int BL = kTN * 4 / (64 * NW);  // weight-tile loads per thread per chunk
     constexpr int NLOADS = 2 * AL + BL + (NW == 4 ? 2 : 1);
     __shared__ uint4 Ah0[kTM * 8], Ah1[kTM * 8], Ah2[kTM * 8];
     __shared__ uint4 Al0[kTM * 8], Al1[kTM * 8], Al2[kTM * 8];
@@ -645,7 +355,6 @@ __global__ __launch_bounds__(64 * NW) void gemm_mx_kernel(const MxArgs pa)
     const int mt = idx / pa.ntn, nt = idx - mt * pa.ntn;
     const Tile tl = pa.tiles[mt];
     const int K = GATE_UP ? d : F;
-    const int64_t ebytes = (int64_t)3 * d * F / 2, escales = (int64_t)3 * d * F / 32;
     auto src_row = [&](int r) -> int64_t {
         const int rr = r < tl.nrows ? r : 0;  // rows past nrows re-read row 0 (never stored)
         return GATE_UP ? (int64_t)(pa.perm[tl.row0 + rr] / pa.k) : (int64_t)(tl.row0 + rr);
@@ -662,29 +371,15 @@ __global__ __launch_bounds__(64 * NW) void gemm_mx_kernel(const MxArgs pa)
         ahsrc[i] = pa.ahi + off;
         alsrc[i] = pa.alo + off;
     }
-    auto wrow_of = [&](int rho) -> int64_t {
-        if (GATE_UP) {
-            const int f = nt * 128 + (rho >> 7) * 64 + ((rho >> 4) & 3) * 16 + (rho & 15);
-            return ((rho >> 6) & 1) ? (int64_t)F + f : (int64_t)f;
-        }
-        return (int64_t)nt * kTN + rho;
-    };
-    const uint8_t *eb = pa.wpk + tl.expert * ebytes;
-    const uint8_t *es = pa.sc + tl.expert * escales;
-    const int64_t wbase = GATE_UP ? 0 : (int64_t)2 * F * (d / 2);
-    const int64_t sbase = GATE_UP ? 0 : (int64_t)2 * F * (d / 32);
-    const uint8_t *bsrc[BL];
-#pragma unroll
-    for (int i = 0; i < BL; ++i) {
-        const int rho = 16 * (NW * i + wv) + (lane >> 2);
-        const int gsrc = (lane & 3) ^ bswz(rho);
-        bsrc[i] = eb + wbase + wrow_of(rho) * (K / 2) + gsrc * 16;
-    }
+    // weight tile nt of this matrix: load i fills 16-byte unit 64*(NW*i + wv) + lane
+    const WView v = GATE_UP ? w1_view(pa.wpk, pa.sc, tl.expert, d, F)
+                            : w2_view(pa.wpk, pa.sc, tl.expert, d, F);
+    const uint8_t *bsrc = v.tile(nt, 0) + (64 * wv + lane) * 16;
     // scales: A dword q = (row q/2, hi or lo part by q%2); B dword q = row q.
     // 4 waves: every thread loads one of each; 8 waves: waves 0-3 A, 4-7 B.
     const int q = (NW == 4 ? 64 * wv : 64 * (wv & 3)) + lane;
     const uint8_t *acsrc = ((lane & 1) ? pa.aslo : pa.ashi) + src_row(q >> 1) * (K / 32);
-    const uint8_t *ssrc = es + sbase + wrow_of(q) * (K / 32);
+    const uint8_t *ssrc = v.stile(nt, 0) + q * 4;
     const int nk = K / kKStep;
 
     const int wvu = __builtin_amdgcn_readfirstlane(wv);
@@ -696,8 +391,9 @@ __global__ __launch_bounds__(64 * NW) void gemm_mx_kernel(const MxArgs pa)
         for (int i = 0; i < AL; ++i) dma16(alsrc[i] + kc * kKStep, lds_off(Al + (NW * i + wvu) * 64));
         if (NW == 4 || wvu < 4) dma4(acsrc + kc * 4, lds_off(Ac + 64 * qwu));
 #pragma unroll
-        for (int i = 0; i < BL; ++i) dma16(bsrc[i] + kc * (kKStep / 2), lds_off(Bs + (NW * i + wvu) * 64));
-        if (NW == 4 || wvu >= 4) dma4(ssrc + kc * (kKStep / 32), lds_off(Ss + 64 * qwu));
+        for (int i = 0; i < BL; ++i)
+            dma16(bsrc + (int64_t)kc * kWTileBytes + i * NW * 1024, lds_off(Bs + (NW * i + wvu) * 64));
+        if (NW == 4 || wvu >= 4) dma4(ssrc + kc * kWTileScaleBytes, lds_off(Ss + 64 * qwu));
     };
 
     // ---- compute assignment -------------------------------------------------
@@ -758,8 +454,10 @@ __global__ __launch_bounds__(64 * NW) void gemm_mx_kernel(const MxArgs pa)
         if (kc + 2 < nk) step(kc + 2, Ah2, Al2, Ac2, Bs2, Ss2, Ah1, Al1, Ac1, Bs1, Ss1);
     }
 
-    // ---- epilogue (same as the bf16 kernel) ---------------------------------
+    // ---- epilogue ----------------------------------------------------------------
+    // lane holds C[g*4 + r][n16] of every 16x16 block
     if (GATE_UP) {
+        // column block nb < 4: gate features wn*64 + 16nb + n16 of N-tile nt; nb + 4: up
         const int fbase = nt * 128 + wn * 64;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
@@ -775,6 +473,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_mx_kernel(const MxArgs pa)
                 }
         }
     } else {
+        // bf16 o and the sum of o^2 over each 64-column half of the wave's columns
         const int P = d / 64;
         const int cbase = nt * kTN + wn * 128;
 #pragma unroll
@@ -834,14 +533,14 @@ static hipError_t launch_split(const uint16_t *src, int64_t rows, int K, uint8_t
 //    start-up load chain or tail of short workgroups;
 //  * the weights of the next batch of chunks are in flight while the current
 //    batch is multiplied (two register buffers), also across item borders;
+//    in the packed layout a wave's 16 rows of one chunk are 1 KB contiguous;
 //  * the scaled MX MFMA takes the FP4 codes and E8M0 scales as stored, so no
 //    vector ALU work is spent per weight;
-//  * the tile's activation rows are split into FP8 hi/lo parts with their
-//    E8M0 scales (exact, as in split_rows_kernel) while they are copied to
-//    LDS, once per tile.
+//  * the tile's activation rows arrive as FP8 hi/lo parts with their E8M0
+//    scales (split by the router pass) and are copied to LDS once per tile.
 // The 4 waves take quarters of K; their partial sums meet in LDS (two
 // buffers, alternating per item, one barrier per item) and wave 0 writes
-// silu(gate) * up.  Requirements (checked by the launcher): d % 2048 == 0,
+// silu(gate) * up.  Requirements (checked by the plan): d % 2048 == 0,
 // tiles of at most R rows.
 // =========================================================================
 template <int U>
@@ -870,7 +569,6 @@ __global__ __launch_bounds__(256) void gemm1_stream_kernel(
     const int c_begin = wv * cw;
     const int nbat = cw / U;
     const int total = (i1 - i0) * nbat;
-    const int64_t ebytes = (int64_t)3 * d * F / 2, escales = (int64_t)3 * d * F / 32;
 
     // ---- weight loads (one batch = U chunks of the gate and the up block) --
     uint4 b0[U][NB], b1[U][NB];
@@ -884,27 +582,16 @@ __global__ __launch_bounds__(256) void gemm1_stream_kernel(
             l_tl = tiles[ti];
             l_ti = ti;
         }
+        const WView v = w1_view(wpk, sc, l_tl.expert, d, F);
         const int c = c_begin + bt * U;
-        const int f = grp * 16 + n;
+        const int f = grp * 16 + n, nt = f >> 7;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-            const int64_t row = nb == 0 ? f : F + f;
-            const uint8_t *bp = wpk + l_tl.expert * ebytes + row * (d / 2) + (int64_t)c * (kKStep / 2) + g * 16;
+            const int rho = w1_rho(f, nb == 1);
 #pragma unroll
-            for (int u = 0; u < U; ++u) b[u][nb] = *reinterpret_cast<const uint4 *>(bp + u * (kKStep / 2));
-            const uint8_t *spp = sc + l_tl.expert * escales + row * (d / 32) + c * 4;
-            if constexpr (U == 4) {
-                const uint4 v = *reinterpret_cast<const uint4 *>(spp);
-                sv[0][nb] = v.x;
-                sv[1 % U][nb] = v.y;
-                sv[2 % U][nb] = v.z;
-                sv[3 % U][nb] = v.w;
-            } else if constexpr (U == 2) {
-                const uint2 v = *reinterpret_cast<const uint2 *>(spp);
-                sv[0][nb] = v.x;
-                sv[1 % U][nb] = v.y;
-            } else {
-                sv[0][nb] = *reinterpret_cast<const uint32_t *>(spp);
+            for (int u = 0; u < U; ++u) {
+                b[u][nb] = *reinterpret_cast<const uint4 *>(v.slot(nt, c + u, rho, g));
+                sv[u][nb] = *v.scales(nt, c + u, rho);
             }
         }
     };
@@ -998,25 +685,6 @@ __global__ __launch_bounds__(256) void gemm1_stream_kernel(
     }
 }
 
-// LDS budget for the decode kernels' staged activation rows.
-#ifndef MOE_DEC_LDS
-#define MOE_DEC_LDS (32 * 1024)
-#endif
-constexpr int kDecodeLdsBytes = MOE_DEC_LDS;
-#ifndef MOE_G1NBP
-#define MOE_G1NBP 1
-#define MOE_G1U 4
-#define MOE_G2NB 1  // the sum-of-squares partials assume 64 columns per workgroup
-#define MOE_G2U 4
-#endif
-constexpr int kG1NBP = MOE_G1NBP, kG1U = MOE_G1U;  // gate/up decode: 16*NBP features per workgroup
-constexpr int kG2NB = MOE_G2NB, kG2U = MOE_G2U;    // down decode: 64*NB columns per workgroup
-
-#ifndef MOE_G1SU
-#define MOE_G1SU 4
-#endif
-constexpr int kG1StreamU = MOE_G1SU;  // chunks per weight batch of the streaming kernel
-
 // Workgroups that fit on the device at once for a 256-thread kernel with
 // `lds` bytes of dynamic LDS (cached per device, kernel and size; 0 on error).
 static int persistent_grid(const void *kfn, size_t lds)
@@ -1042,22 +710,18 @@ static int persistent_grid(const void *kfn, size_t lds)
     return grid;
 }
 
+// ---- launchers ----------------------------------------------------------------
+
 hipError_t launch_gemm1(const Shape &s, const Plan &p, const Workspace &ws, const uint16_t *x,
                         const uint8_t *wpk, const uint8_t *sc, hipStream_t st)
 {
     if (p.tiled) {
-#if MOE_TILED_MX
         hipError_t e = launch_split(x, s.T, s.d, ws.xhi, ws.xlo, ws.xshi, ws.xslo, st);
         if (e != hipSuccess) return e;
         MxArgs pa{ws.xhi, ws.xlo, ws.xshi, ws.xslo, ws.perm, ws.tiles, ws.ntiles, wpk, sc,
                   ws.h, nullptr, s.d, s.F, s.k, s.F / 128};
         const int64_t grid = 8 * ((max_tiles(s, p.tile_rows) * pa.ntn + 7) / 8);
         gemm_mx_kernel<true, kMxWaves><<<(unsigned)grid, 64 * kMxWaves, 0, st>>>(pa);
-#else
-        PipeArgs pa{x, ws.perm, ws.tiles, ws.ntiles, wpk, sc, ws.h, nullptr, s.d, s.F, s.k, s.F / 128};
-        const int64_t grid = 8 * ((max_tiles(s, p.tile_rows) * pa.ntn + 7) / 8);
-        gemm_tiled_kernel<true><<<(unsigned)grid, 256, 0, st>>>(pa);
-#endif
     } else if (p.stream) {
         const int R = p.tile_rows;
         const size_t lds = (size_t)R * (2 * s.d + 2 * (s.d / 32));
@@ -1067,14 +731,14 @@ hipError_t launch_gemm1(const Shape &s, const Plan &p, const Workspace &ws, cons
         kfn<<<grid, 256, lds, st>>>(ws.xhi, ws.xlo, ws.xshi, ws.xslo, ws.perm, ws.tiles, ws.ntiles,
                                     wpk, sc, ws.h, s.d, s.F, s.k, R);
     } else {
-        const int groups = s.F / (16 * kG1NBP);
+        const int groups = s.F / 16;
         const int64_t grid = max_tiles(s, p.tile_rows) * groups;
         // a tile holds at most min(T, 16) rows (a token picks an expert once)
         int rows_fit = kDecodeLdsBytes / (s.d * 2);
         rows_fit = rows_fit < s.T ? rows_fit : s.T;
         if (rows_fit > 16) rows_fit = 16;
         const size_t lds = (size_t)rows_fit * s.d * 2;
-        gemm1_decode_kernel<kG1NBP, kG1U><<<(unsigned)grid, 256, lds, st>>>(
+        gemm1_decode_kernel<kUnroll><<<(unsigned)grid, 256, lds, st>>>(
             x, ws.perm, ws.tiles, ws.ntiles, wpk, sc, ws.h, s.d, s.F, s.k, groups, rows_fit);
     }
     return hipGetLastError();
@@ -1084,51 +748,22 @@ hipError_t launch_gemm2(const Shape &s, const Plan &p, const Workspace &ws, cons
                         const uint8_t *sc, hipStream_t st)
 {
     if (p.tiled) {
-#if MOE_TILED_MX
         hipError_t e = launch_split(ws.h, s.S(), s.F, ws.hhi, ws.hlo, ws.hshi, ws.hslo, st);
         if (e != hipSuccess) return e;
         MxArgs pa{ws.hhi, ws.hlo, ws.hshi, ws.hslo, nullptr, ws.tiles, ws.ntiles, wpk, sc,
                   ws.o, ws.ssq, s.d, s.F, s.k, s.d / 256};
         const int64_t grid = 8 * ((max_tiles(s, p.tile_rows) * pa.ntn + 7) / 8);
         gemm_mx_kernel<false, kMxWaves><<<(unsigned)grid, 64 * kMxWaves, 0, st>>>(pa);
-#else
-        PipeArgs pa{ws.h, nullptr, ws.tiles, ws.ntiles, wpk, sc, ws.o, ws.ssq, s.d, s.F, s.k, s.d / 256};
-        const int64_t grid = 8 * ((max_tiles(s, p.tile_rows) * pa.ntn + 7) / 8);
-        gemm_tiled_kernel<false><<<(unsigned)grid, 256, 0, st>>>(pa);
-#endif
     } else {
-        const int wgs = s.d / (64 * kG2NB);
+        const int wgs = s.d / 64;
         const int64_t grid = max_tiles(s, p.tile_rows) * wgs;
         int rows_fit = kDecodeLdsBytes / (s.F * 2);
         rows_fit = rows_fit < s.T ? rows_fit : s.T;
         if (rows_fit > 16) rows_fit = 16;
         const size_t lds = (size_t)rows_fit * s.F * 2;
-        gemm2_decode_kernel<kG2NB, kG2U><<<(unsigned)grid, 256, lds, st>>>(
+        gemm2_decode_kernel<kUnroll><<<(unsigned)grid, 256, lds, st>>>(
             ws.h, ws.tiles, ws.ntiles, wpk, sc, ws.o, ws.ssq, s.d, s.F, wgs, rows_fit);
     }
-    return hipGetLastError();
-}
-
-// MXFP4 rows -> bf16 rows with the conversion the kernels above use.
-__global__ __launch_bounds__(256) void dequant_kernel(const uint8_t *__restrict__ codes,
-                                                      const uint8_t *__restrict__ scales,
-                                                      int64_t n8, int K, uint4 *__restrict__ out)
-{
-    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;  // group of 8 elements
-    if (q >= n8) return;
-    const int64_t e = q * 8;
-    const int64_t row = e / K, col = e % K;
-    const uint32_t c = *reinterpret_cast<const uint32_t *>(codes + row * (K / 2) + col / 2);
-    const float scale = e8m0_to_f32(scales[row * (K / 32) + col / 32]);
-    out[q] = __builtin_bit_cast(uint4, fp4x8_to_bf16(c, scale));
-}
-
-hipError_t launch_dequant(const uint8_t *codes, const uint8_t *scales, int64_t rows, int K,
-                          uint16_t *out, hipStream_t st)
-{
-    const int64_t n8 = rows * K / 8;
-    dequant_kernel<<<(unsigned)((n8 + 255) / 256), 256, 0, st>>>(codes, scales, n8, K,
-                                                                 reinterpret_cast<uint4 *>(out));
     return hipGetLastError();
 }
 

@@ -104,6 +104,8 @@ hipError_t launch_gemm2(const Shape &s, const Plan &p, const Workspace &ws, cons
 hipError_t launch_combine(const Shape &s, const Plan &p, const Workspace &ws, const uint16_t *x,
                           const float *alpha, const float *beta, uint16_t *s_out,
                           hipStream_t st);
+hipError_t launch_pack(const uint8_t *w, const uint8_t *s, int E, int d, int F, uint8_t *wp,
+                       uint8_t *sp, hipStream_t st);
 hipError_t launch_dequant(const uint8_t *codes, const uint8_t *scales, int64_t rows, int K,
                           uint16_t *out, hipStream_t st);
 

@@ -39,11 +39,19 @@ def bf16_bits(t: torch.Tensor) -> np.ndarray:
 
 
 def upload(L, device="cuda"):
+    """Device copies of a generated layer; the expert weights go through the
+    library's packing entry point (natural rows -> packed tiles)."""
+    from mixture_experts_gemm_amd import binding as B
+    w_nat = torch.from_numpy(L.w_packed).to(device)
+    s_nat = torch.from_numpy(L.scales).to(device)
+    w, s = B.moe_pack_weights(w_nat, s_nat, L.shape.d, L.shape.F)
+    torch.cuda.synchronize()
+    del w_nat, s_nat
     return dict(
         x=bf16_tensor(L.x, device),
         router_w=torch.from_numpy(L.router_w).to(device),
-        w=torch.from_numpy(L.w_packed).to(device),
-        s=torch.from_numpy(L.scales).to(device),
+        w=w,
+        s=s,
         alpha=torch.from_numpy(L.alpha).to(device),
         beta=torch.from_numpy(L.beta).to(device),
     )

@@ -15,14 +15,14 @@ def L():
 
 def test_exports_every_declared_function(L):
     names = B.declared_functions()
-    assert set(names) == {"moe_layer_workspace_size", "moe_layer_forward", "moe_dequant_mxfp4",
-                          "moe_status_string"}
+    assert set(names) == {"moe_layer_workspace_size", "moe_layer_forward", "moe_pack_weights",
+                          "moe_dequant_mxfp4", "moe_status_string"}
     for n in names:
         assert hasattr(L, n), n
 
 
 def test_status_strings():
-    for code in (0, -1, -2, -3, -4, -5):
+    for code in (0, -1, -2, -3, -4, -5, -6):
         assert B.moe_status_string(code) and B.moe_status_string(code) != "unknown status"
     assert B.moe_status_string(7) == "unknown status"
 
@@ -35,7 +35,8 @@ def test_workspace_size():
     big = ws(4096, 8192, 256, 2048, 8)
     S = 4096 * 8
     assert big >= S * 2048 * 2 + S * 8192 * 2
-    assert ws(64, 250, 8, 512, 2) == 0       # d not a multiple of 128
+    assert ws(64, 250, 8, 512, 2) == 0       # d not a multiple of 256
+    assert ws(64, 384, 8, 512, 2) == 0
     assert ws(64, 256, 8, 500, 2) == 0       # F not a multiple of 128
     assert ws(64, 256, 8, 512, 9) == 0       # k > E
     assert ws(64, 256, 8, 512, 0) == 0
@@ -44,11 +45,12 @@ def test_workspace_size():
     assert ws(64, 256, 8, 512, 2, eps=float("nan")) == 0
 
 
-def _call(dims, k=2, ws_bytes=1 << 30, null=None, ws_ptr=1 << 20):
+def _call(dims, k=2, ws_bytes=1 << 30, null=None, ws_ptr=1 << 20, ptr=None):
     p = C.c_void_p(1 << 20)  # never dereferenced: every case below fails the checks first
     args = dict(x=p, router_w=p, w=p, s=p, alpha=p, beta=p, s_out=p, ws=C.c_void_p(ws_ptr))
     if null:
         args[null] = None
+    args.update(ptr or {})
     return B.lib().moe_layer_forward(C.byref(dims) if dims is not None else None, args["x"],
                                      args["router_w"], args["w"], args["s"], args["alpha"],
                                      args["beta"], k, args["s_out"], args["ws"], ws_bytes, None, None)
@@ -64,6 +66,9 @@ def test_argument_errors():
     assert _call(B.moe_dims_t(64, 256, 8, 512, -1.0)) == B.MOE_ERR_SHAPE
     assert _call(good, ws_bytes=1024) == B.MOE_ERR_WORKSPACE
     assert _call(good, ws_ptr=(1 << 20) + 64) == B.MOE_ERR_WORKSPACE
+    odd = C.c_void_p((1 << 20) + 8)
+    for name in ("x", "router_w", "w", "s", "alpha", "beta", "s_out"):
+        assert _call(good, ptr={name: odd}) == B.MOE_ERR_ALIGN, name
     # T = 0 is a successful no-op even with NULL buffers
     zero = B.moe_dims_t(0, 256, 8, 512, 1e-6)
     assert _call(zero, null="x") == B.MOE_OK
@@ -76,3 +81,18 @@ def test_dequant_argument_errors():
     assert f(p, p, 4, 48, p, None) == B.MOE_ERR_SHAPE
     assert f(p, p, -1, 64, p, None) == B.MOE_ERR_SHAPE
     assert f(p, p, 0, 64, p, None) == B.MOE_OK
+
+
+def test_pack_argument_errors():
+    f = B.lib().moe_pack_weights
+    p = C.c_void_p(1 << 20)
+    odd = C.c_void_p((1 << 20) + 4)
+    good = B.moe_dims_t(0, 256, 8, 512, 1e-6)
+    assert f(None, p, p, p, p, None) == B.MOE_ERR_NULL
+    assert f(C.byref(good), None, p, p, p, None) == B.MOE_ERR_NULL
+    assert f(C.byref(good), p, p, None, p, None) == B.MOE_ERR_NULL
+    assert f(C.byref(B.moe_dims_t(0, 128, 8, 512, 1e-6)), p, p, p, p, None) == B.MOE_ERR_SHAPE
+    assert f(C.byref(B.moe_dims_t(0, 256, 8, 64, 1e-6)), p, p, p, p, None) == B.MOE_ERR_SHAPE
+    assert f(C.byref(B.moe_dims_t(0, 256, 0, 512, 1e-6)), p, p, p, p, None) == B.MOE_ERR_SHAPE
+    assert f(C.byref(good), odd, p, p, p, None) == B.MOE_ERR_ALIGN
+    assert f(C.byref(good), p, p, p, odd, None) == B.MOE_ERR_ALIGN

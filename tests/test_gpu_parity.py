@@ -72,6 +72,55 @@ def test_dequant_random_rows():
     np.testing.assert_array_equal(got, oracle.dequant_rows(codes, scales, K))
 
 
+def _pack_reference(codes, scales, d, F):
+    """The packed layout of include/moe.h (moe_pack_weights) written out with
+    numpy index arrays, one expert at a time."""
+    E = codes.shape[0]
+    r = np.arange(256)
+    sw = ((r >> 1) ^ (r >> 3)) & 3
+    out_c = np.empty_like(codes)
+    out_s = np.empty_like(scales)
+
+    def tiles(mat_c, mat_s, rows_of_tile, ntiles, K):
+        nk = K // 128
+        c_parts, s_parts = [], []
+        for nt in range(ntiles):
+            rows = rows_of_tile(nt)                                  # natural row of tile row r
+            for kc in range(nk):
+                blocks = mat_c[rows, kc * 64:(kc + 1) * 64].reshape(256, 4, 16)
+                slot = np.empty_like(blocks)
+                for b in range(4):
+                    slot[np.arange(256), b ^ sw] = blocks[:, b]
+                c_parts.append(slot.reshape(-1))
+                s_parts.append(mat_s[rows, kc * 4:(kc + 1) * 4].reshape(-1))
+        return np.concatenate(c_parts), np.concatenate(s_parts)
+
+    for e in range(E):
+        w1c = codes[e, :d * F].reshape(2 * F, d // 2)
+        w1s = scales[e, :d * F // 16].reshape(2 * F, d // 32)
+        w2c = codes[e, d * F:].reshape(d, F // 2)
+        w2s = scales[e, d * F // 16:].reshape(d, F // 32)
+        f_of = lambda nt: nt * 128 + (r // 128) * 64 + (r % 64) + np.where((r // 64) % 2 == 1, F, 0)
+        c1, s1 = tiles(w1c, w1s, f_of, F // 128, d)
+        c2, s2 = tiles(w2c, w2s, lambda nt: nt * 256 + r, d // 256, F)
+        out_c[e] = np.concatenate([c1, c2])
+        out_s[e] = np.concatenate([s1, s2])
+    return out_c, out_s
+
+
+@pytest.mark.parametrize("E,d,F", [(3, 512, 256), (2, 256, 384)])
+def test_pack_weights_layout(E, d, F):
+    from mixture_experts_gemm_amd import binding as B
+    rng = np.random.default_rng(11)
+    codes = rng.integers(0, 256, size=(E, 3 * d * F // 2), dtype=np.uint8)
+    scales = rng.integers(0, 256, size=(E, 3 * d * F // 32), dtype=np.uint8)
+    _say("pack", E, d, F)
+    wp, sp = B.moe_pack_weights(torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda(), d, F)
+    want_c, want_s = _pack_reference(codes, scales, d, F)
+    np.testing.assert_array_equal(wp.cpu().numpy(), want_c)
+    np.testing.assert_array_equal(sp.cpu().numpy(), want_s)
+
+
 # ------------------------------------------------------------------ small workloads, every token
 
 @pytest.mark.parametrize("T", [64, 37, 1, 200])
