@@ -26,7 +26,7 @@ Workspace carve_workspace(const Shape &s, void *base)
         off += align256(bytes);
         return p;
     };
-    w.scores = (float *)take(sizeof(float) * (size_t)s.T * s.E);
+    w.scores = (float *)take(sizeof(float) * (size_t)router_splits(s) * s.T * s.E);
     w.ids = (int32_t *)take(sizeof(int32_t) * (size_t)S);
     w.wts = (float *)take(sizeof(float) * (size_t)S);
     w.masks = (uint64_t *)take(sizeof(uint64_t) * (size_t)(nchunks * s.E));

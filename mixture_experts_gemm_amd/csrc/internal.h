@@ -56,6 +56,18 @@ inline Plan make_plan(const Shape &s)
     return p;
 }
 
+// Slices of d the many-token router splits its sums into (partial score
+// planes added by top-k): enough workgroups of 128 tokens x 128 experts to
+// fill the device, at most 8, each slice a multiple of 32 long.
+inline int router_splits(const Shape &s)
+{
+    if (s.T <= 32) return 1;
+    const int64_t tiles = (int64_t)((s.T + 127) / 128) * ((s.E + 127) / 128);
+    int ks = 1;
+    while (ks < 8 && tiles * ks * 2 <= 512 && (s.d / (ks * 2)) % 32 == 0) ks *= 2;
+    return ks;
+}
+
 // Upper bound of the tile count for tiles of tile_rows rows (1: any plan).
 inline int64_t max_tiles(const Shape &s, int tile_rows)
 {
@@ -67,7 +79,7 @@ inline int64_t max_tiles(const Shape &s, int tile_rows)
 inline int64_t num_chunks(const Shape &s) { return (s.T + kChunkTokens - 1) / kChunkTokens; }
 
 struct Workspace {
-    float *scores;        // [T][E]
+    float *scores;        // [router_splits][T][E] partial router scores
     int32_t *ids;         // [S]
     float *wts;           // [S]
     uint64_t *masks;      // [nchunks][E] token bits of each expert in a chunk

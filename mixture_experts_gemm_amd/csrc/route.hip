@@ -97,60 +97,103 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(const uint16_t *__rest
 
 // ---------------------------------------------------------------------------
 // Router scores, many tokens: bf16 MFMA on an exact three-way bf16 split of
-// the fp32 router weights (w = hi + mid + lo exactly; x is bf16, so every
-// product is exact and the sum is accumulated in fp32 like an fp32 GEMM).
-// One wave computes a 16-token x 16-expert tile over all of d.
+// the fp32 router weights.  w = hi + mid + lo exactly (truncating splits:
+// each part keeps 8 significant bits of what is left), x is bf16, so every
+// product is exact and the sum is accumulated in fp32 like an fp32 GEMM.
+// A workgroup computes 128 tokens x 128 experts over one slice of d; its 4
+// waves take 64 x 64 each (4 x 4 MFMA blocks), operands loaded straight
+// into registers one 32-wide K step ahead.  Slice s writes its partial sums
+// to part[s][T][E]; top-k adds the slices in order.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void split3(float w, uint16_t &hi, uint16_t &mid, uint16_t &lo)
+constexpr int kRtT = 128, kRtE = 128;
+
+__device__ __forceinline__ void split3_trunc(const float4 &a, const float4 &b, uint4 &hi, uint4 &mid,
+                                             uint4 &lo)
 {
-    hi = f32_to_bf16(w);
-    float r1 = w - bf16_to_f32(hi);
-    mid = f32_to_bf16(r1);
-    float r2 = r1 - bf16_to_f32(mid);
-    lo = f32_to_bf16(r2);
+    const float w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    uint32_t h[8], m[8], l[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t wb = __float_as_uint(w[i]);
+        h[i] = wb & 0xFFFF0000u;
+        const float r1 = w[i] - __uint_as_float(h[i]);
+        m[i] = __float_as_uint(r1) & 0xFFFF0000u;
+        l[i] = __float_as_uint(r1 - __uint_as_float(m[i]));  // <= 8 significant bits: exact in bf16
+    }
+    auto pk = [](uint32_t a0, uint32_t a1) { return (a0 >> 16) | (a1 & 0xFFFF0000u); };
+    hi = make_uint4(pk(h[0], h[1]), pk(h[2], h[3]), pk(h[4], h[5]), pk(h[6], h[7]));
+    mid = make_uint4(pk(m[0], m[1]), pk(m[2], m[3]), pk(m[4], m[5]), pk(m[6], m[7]));
+    lo = make_uint4(pk(l[0], l[1]), pk(l[2], l[3]), pk(l[4], l[5]), pk(l[6], l[7]));
 }
 
-__device__ __forceinline__ uint32_t pack2(uint16_t a, uint16_t b) { return a | (uint32_t)b << 16; }
-
-__global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t *__restrict__ x,
+__global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t *__restrict__ x,
                                                           const float *__restrict__ wr,
-                                                          float *__restrict__ scores, int T,
-                                                          int d, int E, int eblocks)
+                                                          float *__restrict__ part, int T, int d,
+                                                          int E, int kslice)
 {
-    const int lane = threadIdx.x & 63;
-    const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int tb = gw / eblocks, eb = gw % eblocks;
-    const int t0 = tb * 16, e0 = eb * 16;
-    if (t0 >= T) return;
-    const int r = lane & 15, g = lane >> 4;
-    const bool tv = t0 + r < T, ev = e0 + r < E;
-    const uint16_t *xp = x + (int64_t)(tv ? t0 + r : 0) * d + g * 8;
-    const float *wp = wr + (int64_t)(ev ? e0 + r : 0) * d + g * 8;
-    floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
-    for (int k0 = 0; k0 < d; k0 += 32) {
-        uint4 xa = tv ? *reinterpret_cast<const uint4 *>(xp + k0) : make_uint4(0, 0, 0, 0);
-        float4 w0 = ev ? *reinterpret_cast<const float4 *>(wp + k0) : make_float4(0, 0, 0, 0);
-        float4 w1 = ev ? *reinterpret_cast<const float4 *>(wp + k0 + 4) : make_float4(0, 0, 0, 0);
-        float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-        uint16_t hi[8], mi[8], lo[8];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int m = lane & 15, g = lane >> 4;
+    const int t0 = blockIdx.x * kRtT + (wv & 1) * 64;
+    const int e0 = blockIdx.y * kRtE + (wv >> 1) * 64;
+    const int k0 = blockIdx.z * kslice;
+    // rows past T / E are computed on the last valid row and never stored
+    const uint16_t *xp[4];
+    const float *wp[4];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) split3(wv[i], hi[i], mi[i], lo[i]);
-        const uint4 bh = make_uint4(pack2(hi[0], hi[1]), pack2(hi[2], hi[3]), pack2(hi[4], hi[5]),
-                                    pack2(hi[6], hi[7]));
-        const uint4 bm = make_uint4(pack2(mi[0], mi[1]), pack2(mi[2], mi[3]), pack2(mi[4], mi[5]),
-                                    pack2(mi[6], mi[7]));
-        const uint4 bl = make_uint4(pack2(lo[0], lo[1]), pack2(lo[2], lo[3]), pack2(lo[4], lo[5]),
-                                    pack2(lo[6], lo[7]));
-        const bf16x8_t a = as_bf16x8(xa);
-        acc = mfma16(a, as_bf16x8(bl), acc);
-        acc = mfma16(a, as_bf16x8(bm), acc);
-        acc = mfma16(a, as_bf16x8(bh), acc);
-    }
+    for (int mb = 0; mb < 4; ++mb)
+        xp[mb] = x + (int64_t)min(t0 + mb * 16 + m, T - 1) * d + k0 + g * 8;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int t = t0 + g * 4 + i;
-        if (t < T && ev) scores[(int64_t)t * E + e0 + r] = acc[i];
+    for (int nb = 0; nb < 4; ++nb) wp[nb] = wr + (int64_t)min(e0 + nb * 16 + m, E - 1) * d + k0 + g * 8;
+
+    floatx4_t acc[4][4];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+
+    uint4 a0[4], a1[4];
+    float4 w0[4][2], w1[4][2];
+    auto load = [&](uint4 (&a)[4], float4 (&w)[4][2], int k) {
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) a[mb] = *reinterpret_cast<const uint4 *>(xp[mb] + k);
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+            w[nb][0] = *reinterpret_cast<const float4 *>(wp[nb] + k);
+            w[nb][1] = *reinterpret_cast<const float4 *>(wp[nb] + k + 4);
+        }
+    };
+    auto compute = [&](const uint4 (&a)[4], const float4 (&w)[4][2]) {
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+            uint4 hi, mid, lo;
+            split3_trunc(w[nb][0], w[nb][1], hi, mid, lo);
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb) {
+                const bf16x8_t av = as_bf16x8(a[mb]);
+                acc[mb][nb] = mfma16(av, as_bf16x8(lo), acc[mb][nb]);
+                acc[mb][nb] = mfma16(av, as_bf16x8(mid), acc[mb][nb]);
+                acc[mb][nb] = mfma16(av, as_bf16x8(hi), acc[mb][nb]);
+            }
+        }
+    };
+    load(a0, w0, 0);
+    for (int k = 0; k < kslice; k += 64) {
+        if (k + 32 < kslice) load(a1, w1, k + 32);
+        compute(a0, w0);
+        if (k + 32 >= kslice) break;
+        if (k + 64 < kslice) load(a0, w0, k + 64);
+        compute(a1, w1);
     }
+    float *out = part + (int64_t)blockIdx.z * T * E;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = t0 + mb * 16 + g * 4 + r, e = e0 + nb * 16 + m;
+                if (t < T && e < E) out[(int64_t)t * E + e] = acc[mb][nb][r];
+            }
 }
 
 hipError_t launch_router(const Shape &s, const Plan &p, const Workspace &ws, const uint16_t *x,
@@ -165,10 +208,9 @@ hipError_t launch_router(const Shape &s, const Plan &p, const Workspace &ws, con
         router_gemv_kernel<4><<<dim3(s.E, (s.T + 3) / 4), 256, 0, st>>>(
             x, wr, ws.scores, s.T, s.d, s.E, xhi, ws.xlo, ws.xshi, ws.xslo);
     } else {
-        const int eblocks = (s.E + 15) / 16;
-        const int64_t waves = (int64_t)((s.T + 15) / 16) * eblocks;
-        router_mfma_kernel<<<(unsigned)((waves + 3) / 4), 256, 0, st>>>(x, wr, ws.scores, s.T, s.d,
-                                                                          s.E, eblocks);
+        const int ks = router_splits(s);
+        dim3 grid((s.T + kRtT - 1) / kRtT, (s.E + kRtE - 1) / kRtE, ks);
+        router_gemm_kernel<<<grid, 256, 0, st>>>(x, wr, ws.scores, s.T, s.d, s.E, s.d / ks);
     }
     return hipGetLastError();
 }
@@ -214,15 +256,23 @@ __device__ __forceinline__ void wave_argmax(float &v, int &id)
     id = bi;
 }
 
+// l: the token's scores, or its first partial-score plane when the router
+// split its sums over nsplit slices of d (planes `stride` floats apart,
+// added in slice order).
 template <int SLOTS>
 __device__ void topk_row(const float *__restrict__ l, int E, int k, int32_t *__restrict__ ids_out,
-                         float *__restrict__ w_out, int32_t *sid_out, int lane)
+                         float *__restrict__ w_out, int32_t *sid_out, int lane, int nsplit,
+                         int64_t stride)
 {
     float v[SLOTS];
 #pragma unroll
     for (int q = 0; q < SLOTS; ++q) {
         const int e = lane + 64 * q;
-        const float x = e < E ? l[e] : -INFINITY;
+        float x = -INFINITY;
+        if (e < E) {
+            x = l[e];
+            for (int sp = 1; sp < nsplit; ++sp) x += l[sp * stride + e];
+        }
         v[q] = x == x ? x : -INFINITY;
     }
     uint32_t avail = 0;
@@ -271,13 +321,14 @@ __device__ void topk_row(const float *__restrict__ l, int E, int k, int32_t *__r
 template <int SLOTS>
 __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ scores,
                                                    int32_t *__restrict__ ids,
-                                                   float *__restrict__ wts, int T, int E, int k)
+                                                   float *__restrict__ wts, int T, int E, int k,
+                                                   int nsplit)
 {
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
     topk_row<SLOTS>(scores + (int64_t)t * E, E, k, ids + (int64_t)t * k, wts + (int64_t)t * k,
-                    nullptr, lane);
+                    nullptr, lane, nsplit, (int64_t)T * E);
 }
 
 // ---------------------------------------------------------------------------
@@ -360,7 +411,7 @@ __global__ __launch_bounds__(256) void route_small_kernel(
     const float *__restrict__ scores, int32_t *__restrict__ ids, float *__restrict__ wts,
     int32_t *__restrict__ counts, int32_t *__restrict__ offsets, int32_t *__restrict__ perm,
     int32_t *__restrict__ inv, Tile *__restrict__ tiles, int32_t *__restrict__ ntiles, int T,
-    int E, int k, int tile_rows)
+    int E, int k, int tile_rows, int nsplit)
 {
     __shared__ unsigned long long mask[1024];
     __shared__ int32_t sid[4096];
@@ -372,7 +423,7 @@ __global__ __launch_bounds__(256) void route_small_kernel(
     for (int e = tid; e < E; e += 256) mask[e] = 0ull;
     for (int t = wv; t < T; t += 4)
         topk_row<SLOTS>(scores + (int64_t)t * E, E, k, ids + (int64_t)t * k, wts + (int64_t)t * k,
-                        sid + t * k, lane);
+                        sid + t * k, lane, nsplit, (int64_t)T * E);
     __syncthreads();
     for (int s = tid; s < S; s += 256) atomicOr(&mask[sid[s]], 1ull << (s / k));
     __syncthreads();
@@ -417,12 +468,18 @@ __global__ __launch_bounds__(256) void group_scan_kernel(
     __shared__ int32_t cnt[1024];
     __shared__ int32_t toff[1024];
     __shared__ int32_t wtot[4];
+    // two passes over the masks (counts, then bases); loads go out in batches
+    // of 16 so the walk over the chunks is not a chain of dependent reads
+    constexpr int B = 16;
     const int tid = threadIdx.x;
     for (int e = tid; e < E; e += 256) {
         int run = 0;
-        for (int c = 0; c < nchunks; ++c) {
-            chunk_base[(int64_t)c * E + e] = run;
-            run += __popcll(masks[(int64_t)c * E + e]);
+        for (int c0 = 0; c0 < nchunks; c0 += B) {
+            uint64_t mv[B];
+#pragma unroll
+            for (int i = 0; i < B; ++i) mv[i] = c0 + i < nchunks ? masks[(int64_t)(c0 + i) * E + e] : 0ull;
+#pragma unroll
+            for (int i = 0; i < B; ++i) run += __popcll(mv[i]);
         }
         cnt[e] = run;
     }
@@ -430,8 +487,18 @@ __global__ __launch_bounds__(256) void group_scan_kernel(
     int c_own[4];
     finish_offsets(cnt, toff, wtot, E, tile_rows, counts, offsets, tiles, ntiles, c_own);
     for (int e = tid; e < E; e += 256) {
-        const int base = cnt[e];
-        for (int c = 0; c < nchunks; ++c) chunk_base[(int64_t)c * E + e] += base;
+        int run = cnt[e];
+        for (int c0 = 0; c0 < nchunks; c0 += B) {
+            uint64_t mv[B];
+#pragma unroll
+            for (int i = 0; i < B; ++i) mv[i] = c0 + i < nchunks ? masks[(int64_t)(c0 + i) * E + e] : 0ull;
+#pragma unroll
+            for (int i = 0; i < B; ++i)
+                if (c0 + i < nchunks) {
+                    chunk_base[(int64_t)(c0 + i) * E + e] = run;
+                    run += __popcll(mv[i]);
+                }
+        }
     }
 }
 
@@ -461,9 +528,11 @@ static void launch_topk_slots(const Shape &s, const Plan &p, const Workspace &ws
     if (p.small_route) {
         route_small_kernel<SLOTS><<<1, 256, 0, st>>>(ws.scores, ws.ids, ws.wts, ws.counts,
                                                      ws.offsets, ws.perm, ws.inv, ws.tiles,
-                                                     ws.ntiles, s.T, s.E, s.k, p.tile_rows);
+                                                     ws.ntiles, s.T, s.E, s.k, p.tile_rows,
+                                                     router_splits(s));
     } else {
-        topk_kernel<SLOTS><<<(s.T + 3) / 4, 256, 0, st>>>(ws.scores, ws.ids, ws.wts, s.T, s.E, s.k);
+        topk_kernel<SLOTS><<<(s.T + 3) / 4, 256, 0, st>>>(ws.scores, ws.ids, ws.wts, s.T, s.E, s.k,
+                                                          router_splits(s));
     }
 }
 
