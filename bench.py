@@ -47,6 +47,9 @@ def parse():
                     help="comma list of extra workloads timed after the main one ('' for none)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="run one plain device copy of this many MiB first (a known-size kernel "
+                         "to scale hardware byte counters against)")
     return ap.parse_args()
 
 
@@ -190,6 +193,15 @@ def main():
         sys.exit(1)
     device = "cuda:0"
     torch.cuda.set_device(0)
+    if args.calib_copy_mib > 0:
+        n = args.calib_copy_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=device)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy: {n} bytes read, {n} bytes written")
+        del src, dst
     decode = args.workload.startswith("decode")
     steps = args.steps or (200 if decode else 20)
     warmup = args.warmup if args.warmup is not None else (10 if decode else 3)

@@ -352,8 +352,13 @@ __global__ __launch_bounds__(64 * NW) void gemm_mx_kernel(const MxArgs pa)
     const int d = pa.d, F = pa.F;
     int idx;
     if (!xcd_tile(*pa.ntiles * pa.ntn, idx)) return;
-    const int mt = idx / pa.ntn, nt = idx - mt * pa.ntn;
-    const Tile tl = pa.tiles[mt];
+    // Work order: expert by expert, and inside an expert N-tile-major, so the
+    // workgroups of an expert's row tiles that read the same weight tile run
+    // side by side on one XCD and the second read can hit its L2.
+    Tile tl = pa.tiles[idx / pa.ntn];
+    const int r = idx - tl.first * pa.ntn;
+    const int nt = r / tl.count, mt = tl.first + (r - nt * tl.count);
+    if (mt != idx / pa.ntn) tl = pa.tiles[mt];
     const int K = GATE_UP ? d : F;
     auto src_row = [&](int r) -> int64_t {
         const int rr = r < tl.nrows ? r : 0;  // rows past nrows re-read row 0 (never stored)

@@ -9,12 +9,15 @@
 namespace moe {
 
 // One row range of one expert's grouped segment: rows [row0, row0+nrows)
-// of the grouped order all belong to `expert`.
+// of the grouped order all belong to `expert`, whose tiles are the `count`
+// consecutive entries of the tile list starting at `first`.
 struct Tile {
     int32_t expert;
     int32_t row0;
     int32_t nrows;
-    int32_t pad;
+    int32_t first;
+    int32_t count;
+    int32_t pad[3];
 };
 
 // Tokens per chunk of the counting sort (one 64-bit token mask per expert).

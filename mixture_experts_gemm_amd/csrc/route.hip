@@ -390,13 +390,18 @@ __device__ void finish_offsets(int32_t *cnt, int32_t *toff, int32_t *wtot, int E
         const int c = c_out[q];
         counts[e] = c;
         offsets[e] = cnt[e];
+        // an expert's rows are spread evenly over its tiles, so its tiles
+        // (which read the same weights) advance at the same pace
         const int nt = (c + tile_rows - 1) / tile_rows;
+        const int per = nt > 0 ? (c + nt - 1) / nt : 0;
         for (int i = 0; i < nt; ++i) {
             Tile tl;
             tl.expert = e;
-            tl.row0 = cnt[e] + i * tile_rows;
-            tl.nrows = min(tile_rows, c - i * tile_rows);
-            tl.pad = 0;
+            tl.row0 = cnt[e] + i * per;
+            tl.nrows = min(per, c - i * per);
+            tl.first = toff[e];
+            tl.count = nt;
+            tl.pad[0] = tl.pad[1] = tl.pad[2] = 0;
             tiles[toff[e] + i] = tl;
         }
     }
