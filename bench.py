@@ -90,6 +90,20 @@ def make_sets(name, nsets, device):
     return w, host, sets, x
 
 
+# the gate/up kernel each workload runs (the dominant kernel of the layer)
+GATE_UP_KERNEL = {
+    "decode1": "gemm1_stream_kernel (gate/up + SwiGLU, persistent, MX MFMA)",
+    "decode4": "gemm1_stream_kernel (gate/up + SwiGLU, persistent, MX MFMA)",
+    "prefill": "gemm_mx_kernel<true> (gate/up + SwiGLU, 128x256 tiles, MX MFMA)",
+    "skewed": "gemm_mx_kernel<true> (gate/up + SwiGLU, 128x256 tiles, MX MFMA)",
+}
+
+
+def counter_summary(name):
+    """Committed HBM byte-counter summary of the gate/up kernel on this workload."""
+    return os.path.join(ROOT, "profiles", f"gate_up_{name}_hbm_counters.md")
+
+
 def time_workload(name, steps, warmup, device):
     import torch
 
@@ -146,8 +160,9 @@ def time_workload(name, steps, warmup, device):
         nbytes = sum(R.mxfp4_w1_bytes(s.d, s.F) * u + T * s.d * 2 + S * s.F * 2 for u in U) / steps
         achieved = nbytes / (g1_ms * 1e-3)
         res["roofline"] = dict(bound="hbm", achieved=achieved / 1e9, peak=R.MI355X_HBM_BYTES_PER_S / 1e9,
-                               unit="GB/s", frac=achieved / R.MI355X_HBM_BYTES_PER_S, traffic=None,
-                               kernel="gemm1_kernel (gate/up + SwiGLU)",
+                               unit="GB/s", frac=achieved / R.MI355X_HBM_BYTES_PER_S,
+                               traffic=R.recorded_traffic(counter_summary(name)),
+                               kernel=GATE_UP_KERNEL[name],
                                algorithmic_bytes_per_launch=nbytes)
         lb = sum(R.layer_bytes(T, s.d, s.E, s.F, u) for u in U) / steps
         res["layer_hbm_frac"] = lb / (elapsed / steps) / R.MI355X_HBM_BYTES_PER_S
@@ -155,8 +170,9 @@ def time_workload(name, steps, warmup, device):
         flops = R.gemm1_flops(S, s.d, s.F)
         achieved = flops / (g1_ms * 1e-3)
         res["roofline"] = dict(bound="mfma", achieved=achieved / 1e12, peak=R.MI355X_BF16_FLOPS_PER_S / 1e12,
-                               unit="TFLOP/s", frac=achieved / R.MI355X_BF16_FLOPS_PER_S, traffic=None,
-                               kernel="gemm1_kernel (gate/up + SwiGLU)",
+                               unit="TFLOP/s", frac=achieved / R.MI355X_BF16_FLOPS_PER_S,
+                               traffic=R.recorded_traffic(counter_summary(name)),
+                               kernel=GATE_UP_KERNEL[name],
                                algorithmic_flops_per_launch=flops)
         res["layer_mfma_frac"] = R.layer_flops(T, s.d, s.k, s.F) / (elapsed / steps) / R.MI355X_BF16_FLOPS_PER_S
     log(json.dumps(res))

@@ -90,7 +90,9 @@ enum {
  *   inv     int32 [T*k]   grouped position of each slot (inverse of perm)
  * and optional timing events (hipEvent_t handles created by the caller, any
  * may be NULL): stage_begin[s] / stage_end[s] are recorded on the stream
- * right before the first and right after the last kernel of stage s.
+ * right before the first and right after the last kernel of stage s.  The
+ * gate/up stage is a single kernel and its two events are recorded by that
+ * kernel's own dispatch, so they bracket exactly its execution.
  */
 typedef struct moe_debug {
     int32_t *ids;

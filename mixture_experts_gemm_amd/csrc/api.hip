@@ -96,6 +96,13 @@ static int check_arch()
     return st == 1 ? MOE_OK : MOE_ERR_ARCH;
 }
 
+// Caller's event for the begin or end of a stage (null when absent).
+static hipEvent_t stage_event(const moe_debug_t *debug, int stage, bool begin)
+{
+    if (!debug) return nullptr;
+    return static_cast<hipEvent_t>(begin ? debug->stage_begin[stage] : debug->stage_end[stage]);
+}
+
 static bool aligned16(std::initializer_list<const void *> ptrs)
 {
     for (const void *p : ptrs)
@@ -147,13 +154,15 @@ extern "C" int moe_layer_forward(const moe_dims_t *dims, const void *x, const fl
         if (fn() != hipSuccess) return false;
         return mark(debug ? debug->stage_end : nullptr, id);
     };
+    auto launch_ok = [](hipError_t e) { return e == hipSuccess; };
     uint16_t *out = static_cast<uint16_t *>(s_out);
     const Plan p = make_plan(s);
     if (!stage(MOE_STAGE_ROUTER, [&] { return launch_router(s, p, ws, xb, router_w, st); }) ||
         !stage(MOE_STAGE_TOPK, [&] { return launch_topk(s, p, ws, st); }) ||
         !stage(MOE_STAGE_GROUP, [&] { return launch_group(s, p, ws, st); }) ||
-        !stage(MOE_STAGE_GEMM1,
-               [&] { return launch_gemm1(s, p, ws, xb, expert_w_packed, scales, st); }) ||
+        !launch_ok(launch_gemm1(s, p, ws, xb, expert_w_packed, scales, st,
+                                stage_event(debug, MOE_STAGE_GEMM1, true),
+                                stage_event(debug, MOE_STAGE_GEMM1, false))) ||
         !stage(MOE_STAGE_GEMM2, [&] { return launch_gemm2(s, p, ws, expert_w_packed, scales, st); }) ||
         !stage(MOE_STAGE_COMBINE,
                [&] { return launch_combine(s, p, ws, xb, alpha, beta, out, st); }))

@@ -20,6 +20,8 @@
 // B[k][n = l%16] for the 8 k of k-group l/16 and step s: k = 32*(l/16) + 8*s
 // + [0..8) inside a 128-wide K chunk.  So one 16-byte weight load per lane is
 // exactly one 32-element scale block, and four MFMA steps consume it.
+#include <hip/hip_ext.h>
+
 #include <mutex>
 #include <type_traits>
 
@@ -529,6 +531,11 @@ static hipError_t launch_split(const uint16_t *src, int64_t rows, int K, uint8_t
     return hipGetLastError();
 }
 
+hipError_t launch_split_x(const Shape &s, const Workspace &ws, const uint16_t *x, hipStream_t st)
+{
+    return launch_split(x, s.T, s.d, ws.xhi, ws.xlo, ws.xshi, ws.xslo, st);
+}
+
 // =========================================================================
 // Streaming gate/up kernel for a few tokens (decode).  The time is the read
 // of the chosen experts' FP4 weights, so the kernel is built to keep that
@@ -718,23 +725,27 @@ static int persistent_grid(const void *kfn, size_t lds)
 // ---- launchers ----------------------------------------------------------------
 
 hipError_t launch_gemm1(const Shape &s, const Plan &p, const Workspace &ws, const uint16_t *x,
-                        const uint8_t *wpk, const uint8_t *sc, hipStream_t st)
+                        const uint8_t *wpk, const uint8_t *sc, hipStream_t st, hipEvent_t ev0,
+                        hipEvent_t ev1)
 {
     if (p.tiled) {
-        hipError_t e = launch_split(x, s.T, s.d, ws.xhi, ws.xlo, ws.xshi, ws.xslo, st);
-        if (e != hipSuccess) return e;
+        // x was split into FP8 parts in the router stage (launch_split_x)
         MxArgs pa{ws.xhi, ws.xlo, ws.xshi, ws.xslo, ws.perm, ws.tiles, ws.ntiles, wpk, sc,
                   ws.h, nullptr, s.d, s.F, s.k, s.F / 128};
         const int64_t grid = 8 * ((max_tiles(s, p.tile_rows) * pa.ntn + 7) / 8);
-        gemm_mx_kernel<true, kMxWaves><<<(unsigned)grid, 64 * kMxWaves, 0, st>>>(pa);
+        hipExtLaunchKernelGGL(gemm_mx_kernel<true, kMxWaves>, dim3((unsigned)grid), dim3(64 * kMxWaves),
+                              0, st, ev0, ev1, 0, pa);
     } else if (p.stream) {
         const int R = p.tile_rows;
         const size_t lds = (size_t)R * (2 * s.d + 2 * (s.d / 32));
         auto kfn = gemm1_stream_kernel<kG1StreamU>;
         const int grid = persistent_grid(reinterpret_cast<const void *>(kfn), lds);
         if (grid <= 0) return hipErrorInvalidConfiguration;
-        kfn<<<grid, 256, lds, st>>>(ws.xhi, ws.xlo, ws.xshi, ws.xslo, ws.perm, ws.tiles, ws.ntiles,
-                                    wpk, sc, ws.h, s.d, s.F, s.k, R);
+        hipExtLaunchKernelGGL(kfn, dim3(grid), dim3(256), (uint32_t)lds, st, ev0, ev1, 0,
+                              (const uint8_t *)ws.xhi, (const uint8_t *)ws.xlo,
+                              (const uint8_t *)ws.xshi, (const uint8_t *)ws.xslo,
+                              (const int32_t *)ws.perm, (const Tile *)ws.tiles,
+                              (const int32_t *)ws.ntiles, wpk, sc, ws.h, s.d, s.F, s.k, R);
     } else {
         const int groups = s.F / 16;
         const int64_t grid = max_tiles(s, p.tile_rows) * groups;
@@ -743,8 +754,10 @@ hipError_t launch_gemm1(const Shape &s, const Plan &p, const Workspace &ws, cons
         rows_fit = rows_fit < s.T ? rows_fit : s.T;
         if (rows_fit > 16) rows_fit = 16;
         const size_t lds = (size_t)rows_fit * s.d * 2;
-        gemm1_decode_kernel<kUnroll><<<(unsigned)grid, 256, lds, st>>>(
-            x, ws.perm, ws.tiles, ws.ntiles, wpk, sc, ws.h, s.d, s.F, s.k, groups, rows_fit);
+        hipExtLaunchKernelGGL(gemm1_decode_kernel<kUnroll>, dim3((unsigned)grid), dim3(256),
+                              (uint32_t)lds, st, ev0, ev1, 0, x, (const int32_t *)ws.perm,
+                              (const Tile *)ws.tiles, (const int32_t *)ws.ntiles, wpk, sc, ws.h,
+                              s.d, s.F, s.k, groups, rows_fit);
     }
     return hipGetLastError();
 }

@@ -110,10 +110,15 @@ Workspace carve_workspace(const Shape &s, void *base);
 // ---- launchers (all asynchronous on `st`) ---------------------------------
 hipError_t launch_router(const Shape &s, const Plan &p, const Workspace &ws, const uint16_t *x,
                          const float *wr, hipStream_t st);
+// bf16 x -> FP8 hi/lo parts + E8M0 scales in the workspace (tiled plans).
+hipError_t launch_split_x(const Shape &s, const Workspace &ws, const uint16_t *x, hipStream_t st);
 hipError_t launch_topk(const Shape &s, const Plan &p, const Workspace &ws, hipStream_t st);
 hipError_t launch_group(const Shape &s, const Plan &p, const Workspace &ws, hipStream_t st);
+// The gate/up stage is one kernel; ev_begin / ev_end (may be null) are
+// recorded by its dispatch itself, so they time exactly that kernel.
 hipError_t launch_gemm1(const Shape &s, const Plan &p, const Workspace &ws, const uint16_t *x,
-                        const uint8_t *wpk, const uint8_t *sc, hipStream_t st);
+                        const uint8_t *wpk, const uint8_t *sc, hipStream_t st,
+                        hipEvent_t ev_begin, hipEvent_t ev_end);
 hipError_t launch_gemm2(const Shape &s, const Plan &p, const Workspace &ws, const uint8_t *wpk,
                         const uint8_t *sc, hipStream_t st);
 hipError_t launch_combine(const Shape &s, const Plan &p, const Workspace &ws, const uint16_t *x,

@@ -199,8 +199,8 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t *__rest
 hipError_t launch_router(const Shape &s, const Plan &p, const Workspace &ws, const uint16_t *x,
                          const float *wr, hipStream_t st)
 {
-    // the streaming gate/up kernel reads x as FP8 hi/lo parts, split here
-    uint8_t *xhi = p.stream ? ws.xhi : nullptr;
+    // the streaming and tiled gate/up kernels read x as FP8 hi/lo parts, split here
+    uint8_t *xhi = (p.stream || p.tiled) ? ws.xhi : nullptr;
     if (s.T == 1) {
         router_gemv_kernel<1><<<s.E, 256, 0, st>>>(x, wr, ws.scores, s.T, s.d, s.E, xhi, ws.xlo,
                                                    ws.xshi, ws.xslo);
@@ -211,6 +211,12 @@ hipError_t launch_router(const Shape &s, const Plan &p, const Workspace &ws, con
         const int ks = router_splits(s);
         dim3 grid((s.T + kRtT - 1) / kRtT, (s.E + kRtE - 1) / kRtE, ks);
         router_gemm_kernel<<<grid, 256, 0, st>>>(x, wr, ws.scores, s.T, s.d, s.E, s.d / ks);
+        // the tiled gate/up kernel reads x as FP8 hi/lo parts, split here
+        if (p.tiled) {
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            return launch_split_x(s, ws, x, st);
+        }
     }
     return hipGetLastError();
 }

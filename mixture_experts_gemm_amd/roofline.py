@@ -13,7 +13,10 @@ token count, and the two are equal at the crossover token count.
 """
 from __future__ import annotations
 
+import hashlib
 import math
+import os
+import re
 
 # MI355X published peaks
 MI355X_HBM_BYTES_PER_S = 8.0e12
@@ -103,3 +106,36 @@ def gemm2_flops(S: int, d: int, F: int) -> int:
 
 def combinations(n: int, r: int) -> int:
     return math.comb(n, r)
+
+
+# ---- recorded HBM traffic (hardware byte counters) ---------------------------
+
+KERNEL_SOURCES = ("csrc/expert.hip", "csrc/layout.h", "csrc/device.h", "csrc/internal.h")
+
+
+def kernel_source_digest() -> str:
+    """sha256 over the sources of the expert kernels (the counters are only
+    valid for the code they were taken on)."""
+    here = os.path.dirname(os.path.abspath(__file__))
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(here, rel), "rb") as f:
+            h.update(rel.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(path: str) -> float | None:
+    """HBM bytes per launch from a committed counter summary, or None when
+    the summary is missing or was taken on different kernel sources.
+
+    The summary holds lines 'traffic_bytes_per_launch: N' and
+    'source_sha256: H'."""
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        text = f.read()
+    mt = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    mh = re.search(r"source_sha256:\s*([0-9a-f]{64})", text)
+    if not mt or not mh or mh.group(1) != kernel_source_digest():
+        return None
+    return float(mt.group(1))

@@ -132,14 +132,16 @@ def test_tiny_layer_all_tokens(T):
     _check_tokens(L, out, np.arange(T), f"tiny T={T}")
 
 
-@pytest.mark.parametrize("k", [1, 8])
-def test_tiny_k_extremes(k):
-    w = synth.custom_workload(T=50, d=256, E=8, k=k, F=512, seed=21)
+@pytest.mark.parametrize("T,k", [(50, 1), (50, 8), (32, 8)])
+def test_tiny_k_extremes(T, k):
+    # (32, 8): k = E makes T*k large enough for the tiled kernels while the
+    # router still takes its few-token path
+    w = synth.custom_workload(T=T, d=256, E=8, k=k, F=512, seed=21)
     L = synth.make_layer(w)
-    _say("tiny k", k)
+    _say("tiny T k", T, k)
     out, dbg = run_layer(L)
-    _check_routing(L, dbg, f"k={k}")
-    _check_tokens(L, out, np.arange(50), f"k={k}")
+    _check_routing(L, dbg, f"T={T} k={k}")
+    _check_tokens(L, out, np.arange(T), f"T={T} k={k}")
 
 
 def test_all_tokens_to_one_expert_and_empty_experts():
