@@ -99,6 +99,9 @@ GATE_UP_KERNEL = {
 }
 
 
+EVENT_EVERY = 8  # timed steps between two gate/up kernel timings
+
+
 def counter_summary(name):
     """Committed HBM byte-counter summary of the gate/up kernel on this workload."""
     return os.path.join(ROOT, "profiles", f"gate_up_{name}_hbm_counters.md")
@@ -136,28 +139,35 @@ def time_workload(name, steps, warmup, device):
     assert torch.isfinite(out.float()).all(), "non-finite layer output"
     for i in range(warmup):
         call(i)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps)]
-    for a, b in evs:  # create the underlying HIP events before handing them over
+    # The gate/up kernel is timed by the HIP events its own dispatch records,
+    # on every EVENT_EVERY-th step of the timed region: recording timestamps
+    # stalls the queue for a few microseconds, so timing every step would
+    # charge that stall to the throughput.
+    timed = list(range(0, steps, EVENT_EVERY))
+    evs = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for i in timed}
+    for a, b in evs.values():  # create the underlying HIP events before handing them over
         a.record()
         b.record()
     torch.cuda.synchronize()
     log(f"timing {name}: {steps} steps after {warmup} warmup")
     t0 = time.perf_counter()
     for i in range(steps):
-        call(i, debug=dict(events={"gemm1": evs[i]}))
+        call(i, debug=dict(events={"gemm1": evs[i]}) if i in evs else None)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    g1_ms = sum(a.elapsed_time(b) for a, b in evs) / steps
+    g1_ms = sum(a.elapsed_time(b) for a, b in evs.values()) / len(evs)
     out_ok = bool(torch.isfinite(out.float()).all())
     S = T * s.k
     u_mean = sum(U) / len(U)
     res = dict(
         T=T, steps=steps, ms_per_step=elapsed / steps * 1e3, tokens_per_s=T * steps / elapsed,
-        gemm1_ms=g1_ms, distinct_experts_mean=u_mean, finite=out_ok,
+        gemm1_ms=g1_ms, gemm1_timed_launches=len(timed), distinct_experts_mean=u_mean, finite=out_ok,
     )
     if decode:
-        nbytes = sum(R.mxfp4_w1_bytes(s.d, s.F) * u + T * s.d * 2 + S * s.F * 2 for u in U) / steps
+        # bytes of the timed launches (U, the distinct experts, differs per step)
+        nbytes = sum(R.mxfp4_w1_bytes(s.d, s.F) * U[i] + T * s.d * 2 + S * s.F * 2
+                     for i in timed) / len(timed)
         achieved = nbytes / (g1_ms * 1e-3)
         res["roofline"] = dict(bound="hbm", achieved=achieved / 1e9, peak=R.MI355X_HBM_BYTES_PER_S / 1e9,
                                unit="GB/s", frac=achieved / R.MI355X_HBM_BYTES_PER_S,

@@ -33,14 +33,24 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(const uint16_t *__rest
                                                           uint8_t *__restrict__ xsh,
                                                           uint8_t *__restrict__ xsl)
 {
-    // blockIdx.x: expert; blockIdx.y: group of NT tokens.  Every load of a
+    // blockIdx.x < E: expert; blockIdx.y: group of NT tokens.  Every load of a
     // 8192-wide slice is issued before the first multiply-add.  When xhi is
-    // set, the workgroups also split the group's x rows into FP8 hi/lo parts
-    // (block j of the group by workgroup j % E) for the expert kernels.
+    // set, workgroups blockIdx.x >= E split the group's x rows into FP8 hi/lo
+    // parts for the expert kernels (one 32-block per thread), alongside the
+    // dot products.
     constexpr int R = 8;  // float4 per thread per 8192-element slice
     __shared__ float part[4][NT];
     const int e = blockIdx.x;
     const int t0 = blockIdx.y * NT;
+    if (e >= E) {
+        const int64_t nblk = (int64_t)min(NT, T - t0) * (d / 32);
+        const int64_t j = (int64_t)(e - E) * 256 + threadIdx.x;
+        if (xhi && j < nblk) {
+            const int64_t b = (int64_t)t0 * (d / 32) + j;
+            split_bf16_block(x + b * 32, xhi + b * 32, xlo + b * 32, xsh + b, xsl + b);
+        }
+        return;
+    }
     const float *w = wr + (int64_t)e * d;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     float acc[NT];
@@ -84,14 +94,6 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(const uint16_t *__rest
     if (threadIdx.x < NT && t0 + (int)threadIdx.x < T) {
         const int t = threadIdx.x;
         scores[(int64_t)(t0 + t) * E + e] = (part[0][t] + part[1][t]) + (part[2][t] + part[3][t]);
-    }
-    if (xhi) {
-        const int64_t nblk = (int64_t)min(NT, T - t0) * (d / 32);
-        const int64_t gb0 = (int64_t)t0 * (d / 32);
-        for (int64_t j = (int64_t)threadIdx.x * E + e; j < nblk; j += (int64_t)256 * E) {
-            const int64_t b = gb0 + j;
-            split_bf16_block(x + b * 32, xhi + b * 32, xlo + b * 32, xsh + b, xsl + b);
-        }
     }
 }
 
@@ -202,10 +204,12 @@ hipError_t launch_router(const Shape &s, const Plan &p, const Workspace &ws, con
     // the streaming and tiled gate/up kernels read x as FP8 hi/lo parts, split here
     uint8_t *xhi = (p.stream || p.tiled) ? ws.xhi : nullptr;
     if (s.T == 1) {
-        router_gemv_kernel<1><<<s.E, 256, 0, st>>>(x, wr, ws.scores, s.T, s.d, s.E, xhi, ws.xlo,
-                                                   ws.xshi, ws.xslo);
+        const int xs = xhi ? (s.d / 32 + 255) / 256 : 0;  // split workgroups per token group
+        router_gemv_kernel<1><<<s.E + xs, 256, 0, st>>>(x, wr, ws.scores, s.T, s.d, s.E, xhi, ws.xlo,
+                                                        ws.xshi, ws.xslo);
     } else if (s.T <= 32) {
-        router_gemv_kernel<4><<<dim3(s.E, (s.T + 3) / 4), 256, 0, st>>>(
+        const int xs = xhi ? (4 * (s.d / 32) + 255) / 256 : 0;
+        router_gemv_kernel<4><<<dim3(s.E + xs, (s.T + 3) / 4), 256, 0, st>>>(
             x, wr, ws.scores, s.T, s.d, s.E, xhi, ws.xlo, ws.xshi, ws.xslo);
     } else {
         const int ks = router_splits(s);
@@ -270,7 +274,10 @@ __device__ void topk_row(const float *__restrict__ l, int E, int k, int32_t *__r
                          float *__restrict__ w_out, int32_t *sid_out, int lane, int nsplit,
                          int64_t stride)
 {
+    // each lane keeps its SLOTS candidates (experts lane + 64q) sorted best
+    // first; a round takes the wave's best head and the owner pops it
     float v[SLOTS];
+    int id[SLOTS];
 #pragma unroll
     for (int q = 0; q < SLOTS; ++q) {
         const int e = lane + 64 * q;
@@ -280,25 +287,36 @@ __device__ void topk_row(const float *__restrict__ l, int E, int k, int32_t *__r
             for (int sp = 1; sp < nsplit; ++sp) x += l[sp * stride + e];
         }
         v[q] = x == x ? x : -INFINITY;
+        id[q] = e < E ? e : kNone;
     }
-    uint32_t avail = 0;
 #pragma unroll
-    for (int q = 0; q < SLOTS; ++q)
-        if (lane + 64 * q < E) avail |= 1u << q;
+    for (int pass = 0; pass < SLOTS; ++pass)
+#pragma unroll
+        for (int q = pass & 1; q + 1 < SLOTS; q += 2)
+            if (better(v[q + 1], id[q + 1], v[q], id[q])) {
+                const float tv = v[q];
+                const int ti = id[q];
+                v[q] = v[q + 1];
+                id[q] = id[q + 1];
+                v[q + 1] = tv;
+                id[q + 1] = ti;
+            }
     float mysc[SLOTS];
     int myid[SLOTS];
     float top0 = 0.f;
     for (int j = 0; j < k; ++j) {
-        float bv = -INFINITY;
-        int bi = kNone;
-#pragma unroll
-        for (int q = 0; q < SLOTS; ++q)
-            if (((avail >> q) & 1u) && better(v[q], lane + 64 * q, bv, bi)) {
-                bv = v[q];
-                bi = lane + 64 * q;
-            }
+        float bv = v[0];
+        int bi = id[0];
         wave_argmax(bv, bi);
-        if ((bi & 63) == lane) avail &= ~(1u << (bi >> 6));
+        if ((bi & 63) == lane) {
+#pragma unroll
+            for (int q = 0; q + 1 < SLOTS; ++q) {
+                v[q] = v[q + 1];
+                id[q] = id[q + 1];
+            }
+            v[SLOTS - 1] = -INFINITY;
+            id[SLOTS - 1] = kNone;
+        }
         if (j == 0) top0 = bv;
 #pragma unroll
         for (int q = 0; q < SLOTS; ++q)
