@@ -43,6 +43,10 @@ namespace moe {
 constexpr int kDecodeLdsBytes = MOE_DEC_LDS;
 constexpr int kG1StreamU = MOE_G1SU;
 constexpr int kMxWaves = MOE_MX_WAVES;
+#ifndef MOE_MX_WIDE
+#define MOE_MX_WIDE 1  // 128 x 512 tiles where the weight-tile count is even
+#endif
+constexpr bool kUseWide = MOE_MX_WIDE;
 constexpr int kUnroll = 4;  // chunks per weight batch of the decode kernels
 
 __device__ __forceinline__ floatx4_t mfma_chunk(const uint4 *a, uint4 b, float scale, floatx4_t acc)
@@ -96,6 +100,14 @@ template <int N>
 __device__ __forceinline__ void chunk_sync()
 {
     asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" :: "n"(N) : "memory");
+}
+
+// Wait until at most N of this wave's global loads are outstanding and its LDS
+// reads have returned, then barrier.
+template <int N>
+__device__ __forceinline__ void phase_sync()
+{
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(N) : "memory");
 }
 
 // Workgroup barrier for LDS data only: waits for this wave's LDS operations,
@@ -511,6 +523,197 @@ __global__ __launch_bounds__(64 * NW) void gemm_mx_kernel(const MxArgs pa)
     }
 }
 
+// =========================================================================
+// Wide MX tiled kernel (prefill): 128 grouped rows x 512 weight rows (two
+// packed weight tiles) per workgroup, all of K.  The per-CU vector-memory
+// return path, not the MFMA rate, bounds the 256-wide kernel above (about
+// 50 KB per K chunk for 128x256 outputs); two weight tiles per activation
+// tile cut that to 67 KB for twice the outputs.  Two-stage LDS ring (67 KB a
+// stage) filled by direct-to-LDS loads: chunk kc+1 is in flight while chunk
+// kc is multiplied.  8 waves as 2 (rows) x 4 (columns): each wave owns 64 rows
+// x 128 columns (4 x 8 blocks of 16x16, two scaled MX MFMAs per block per
+// chunk).  Used when the matrix has an even number of 256-row weight tiles.
+// =========================================================================
+template <bool GATE_UP>
+__global__ __launch_bounds__(512) void gemm_mxw_kernel(const MxArgs pa)
+{
+    constexpr int NW = 8, MB = 4, AL = 2;
+    __shared__ uint4 Ah0[kTM * 8], Ah1[kTM * 8];
+    __shared__ uint4 Al0[kTM * 8], Al1[kTM * 8];
+    __shared__ uint32_t Ac0[kTM * 2], Ac1[kTM * 2];
+    __shared__ uint4 Bs0[2 * kTN * 4], Bs1[2 * kTN * 4];
+    __shared__ uint32_t Ss0[2 * kTN], Ss1[2 * kTN];
+
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int d = pa.d, F = pa.F;
+    int idx;
+    if (!xcd_tile(*pa.ntiles * pa.ntn, idx)) return;
+    // expert by expert, N-pair-major inside an expert (pa.ntn = pairs)
+    Tile tl = pa.tiles[idx / pa.ntn];
+    const int r = idx - tl.first * pa.ntn;
+    const int np = r / tl.count, mt = tl.first + (r - np * tl.count);
+    if (mt != idx / pa.ntn) tl = pa.tiles[mt];
+    const int K = GATE_UP ? d : F;
+    const int nk = K / kKStep;
+    auto src_row = [&](int rw) -> int64_t {
+        const int rr = rw < tl.nrows ? rw : 0;  // rows past nrows re-read row 0 (never stored)
+        return GATE_UP ? (int64_t)(pa.perm[tl.row0 + rr] / pa.k) : (int64_t)(tl.row0 + rr);
+    };
+
+    // ---- load assignment ----------------------------------------------------
+    // A parts: load i of this wave fills rows 8*(8i + wv) + lane/8, stored slot
+    // lane%8.  Rows past nrows are not loaded (their LDS rows hold stale data;
+    // they only feed output rows that are never stored).  Every wait below is
+    // vmcnt(0), so loads skipped this way cannot upset a count.
+    const uint8_t *ahsrc[AL], *alsrc[AL];
+    bool aload[AL];
+#pragma unroll
+    for (int i = 0; i < AL; ++i) {
+        const int rw = 8 * (NW * i + wv) + (lane >> 3);
+        const int slot = (lane & 7) ^ (rw & 7);
+        const int64_t off = src_row(rw) * K + slot * 16;
+        ahsrc[i] = pa.ahi + off;
+        alsrc[i] = pa.alo + off;
+        aload[i] = rw < tl.nrows;
+    }
+    // A scale dword q = 32*wv + lane (lanes < 32): row q/2, hi or lo part by q%2
+    const int qa = 32 * wv + (lane & 31);
+    const uint8_t *acsrc = ((lane & 1) ? pa.aslo : pa.ashi) + src_row(qa >> 1) * (K / 32);
+    const bool acload = lane < 32 && (qa >> 1) < tl.nrows;
+    // weight tiles 2np and 2np+1: load i fills unit 64*(8i + wv) + lane of the
+    // 2048 units (tile i/2); scale dword q = 64*wv + lane of the 512 (tile q/256)
+    const WView v = GATE_UP ? w1_view(pa.wpk, pa.sc, tl.expert, d, F)
+                            : w2_view(pa.wpk, pa.sc, tl.expert, d, F);
+    // loads 2t and 2t+1 read tile t at units 64*wv + lane and 512 + 64*wv + lane
+    const uint8_t *bsrc0 = v.tile(2 * np, 0) + (64 * wv + lane) * 16;
+    const uint8_t *bsrc1 = v.tile(2 * np + 1, 0) + (64 * wv + lane) * 16;
+    const int qb = 64 * wv + lane;
+    const uint8_t *ssrc = v.stile(2 * np + (qb >> 8), 0) + (qb & 255) * 4;
+
+    const int wvu = __builtin_amdgcn_readfirstlane(wv);
+    auto issue = [&](int kc, uint4 *Ah, uint4 *Al, uint32_t *Ac, uint4 *Bs, uint32_t *Ss) {
+#pragma unroll
+        for (int i = 0; i < AL; ++i)
+            if (aload[i]) dma16(ahsrc[i] + kc * kKStep, lds_off(Ah + (NW * i + wvu) * 64));
+#pragma unroll
+        for (int i = 0; i < AL; ++i)
+            if (aload[i]) dma16(alsrc[i] + kc * kKStep, lds_off(Al + (NW * i + wvu) * 64));
+        if (acload) dma4(acsrc + kc * 4, lds_off(Ac + 32 * wvu));
+        const int64_t bo = (int64_t)kc * kWTileBytes;
+        dma16(bsrc0 + bo, lds_off(Bs + (0 + wvu) * 64));
+        dma16(bsrc0 + bo + 8192, lds_off(Bs + (NW + wvu) * 64));
+        dma16(bsrc1 + bo, lds_off(Bs + (2 * NW + wvu) * 64));
+        dma16(bsrc1 + bo + 8192, lds_off(Bs + (3 * NW + wvu) * 64));
+        dma4(ssrc + kc * kWTileScaleBytes, lds_off(Ss + 64 * wvu));
+    };
+
+    // ---- compute assignment -------------------------------------------------
+    // rows 64*wm.., columns 128*wn.. of the 512; waves w and w+4 share a SIMD
+    // and own different row halves, so a short tile's MFMAs spread over all four
+    const int wm = wv >> 2, wn = wv & 3;
+    const int n16 = lane & 15, g = lane >> 4;
+    int mb_act = (tl.nrows - wm * 64 + 15) >> 4;
+    mb_act = mb_act < 0 ? 0 : (mb_act > MB ? MB : mb_act);
+
+    floatx4_t acc[MB][8];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) acc[mb][nb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+
+    auto compute = [&](const uint4 *Ah, const uint4 *Al, const uint32_t *Ac, const uint4 *Bs,
+                       const uint32_t *Ss) {
+        uint4 bw[8];
+        uint32_t bsc[8];
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) {
+            const int rho = wn * 128 + nb * 16 + n16;  // row of the 512; bank swizzle of its tile row
+            bw[nb] = Bs[rho * 4 + (g ^ bswz(rho))];
+            bsc[nb] = (Ss[rho] >> (8 * g)) & 0xFFu;
+        }
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            // one row block's A fragments at a time (the accumulators take 128 registers)
+            __builtin_amdgcn_sched_barrier(0);
+            if (mb < mb_act) {
+                const int row = wm * 64 + mb * 16 + n16;
+                const int sw = row & 7;
+                const uint4 h0 = Ah[row * 8 + (g ^ sw)], h1 = Ah[row * 8 + ((4 + g) ^ sw)];
+                const uint4 l0 = Al[row * 8 + (g ^ sw)], l1 = Al[row * 8 + ((4 + g) ^ sw)];
+                const uint32_t sh = (Ac[row * 2] >> (8 * g)) & 0xFFu;
+                const uint32_t sl = (Ac[row * 2 + 1] >> (8 * g)) & 0xFFu;
+#pragma unroll
+                for (int nb = 0; nb < 8; ++nb) acc[mb][nb] = mfma_mx(h0, h1, bw[nb], sh, bsc[nb], acc[mb][nb]);
+#pragma unroll
+                for (int nb = 0; nb < 8; ++nb) acc[mb][nb] = mfma_mx(l0, l1, bw[nb], sl, bsc[nb], acc[mb][nb]);
+            }
+        }
+    };
+
+    // ---- pipeline: two slots; the barrier before chunk kc also waits for this
+    // wave's LDS reads of chunk kc-1, whose slot chunk kc+1 then refills ------
+    issue(0, Ah0, Al0, Ac0, Bs0, Ss0);
+    for (int kc = 0; kc < nk; kc += 2) {
+        phase_sync<0>();
+        if (kc + 1 < nk) issue(kc + 1, Ah1, Al1, Ac1, Bs1, Ss1);
+        compute(Ah0, Al0, Ac0, Bs0, Ss0);
+        if (kc + 1 < nk) {
+            phase_sync<0>();
+            if (kc + 2 < nk) issue(kc + 2, Ah0, Al0, Ac0, Bs0, Ss0);
+            compute(Ah1, Al1, Ac1, Bs1, Ss1);
+        }
+    }
+
+    // ---- epilogue: lane holds C[g*4 + r][n16] of every 16x16 block -----------
+    const int nt = 2 * np + (wn >> 1), half = wn & 1;  // weight tile, half of its 256 rows
+    if (GATE_UP) {
+        // column block nb < 4: gate features half*64 + 16nb + n16 of N-tile nt; nb + 4: up
+        const int fbase = nt * 128 + half * 64;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            if (mb >= mb_act) continue;
+#pragma unroll
+            for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    const int row = wm * 64 + mb * 16 + g * 4 + rr;
+                    if (row < tl.nrows)
+                        pa.out[(int64_t)(tl.row0 + row) * F + fbase + hb * 16 + n16] =
+                            f32_to_bf16(silu(acc[mb][hb][rr]) * acc[mb][hb + 4][rr]);
+                }
+        }
+    } else {
+        // bf16 o and the sum of o^2 over each 64-column half of the wave's columns
+        const int P = d / 64;
+        const int cbase = nt * kTN + half * 128;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            if (mb >= mb_act) continue;
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int row = wm * 64 + mb * 16 + g * 4 + rr;
+                float ss0 = 0.f, ss1 = 0.f;
+#pragma unroll
+                for (int nb = 0; nb < 4; ++nb) ss0 += acc[mb][nb][rr] * acc[mb][nb][rr];
+#pragma unroll
+                for (int nb = 4; nb < 8; ++nb) ss1 += acc[mb][nb][rr] * acc[mb][nb][rr];
+                ss0 = sum16(ss0);
+                ss1 = sum16(ss1);
+                if (row < tl.nrows) {
+#pragma unroll
+                    for (int nb = 0; nb < 8; ++nb)
+                        pa.out[(int64_t)(tl.row0 + row) * d + cbase + nb * 16 + n16] =
+                            f32_to_bf16(acc[mb][nb][rr]);
+                    if (n16 == 0) {
+                        pa.ssq[(int64_t)(tl.row0 + row) * P + cbase / 64] = ss0;
+                        pa.ssq[(int64_t)(tl.row0 + row) * P + cbase / 64 + 1] = ss1;
+                    }
+                }
+            }
+        }
+    }
+}
+
 // bf16 rows -> FP8 E4M3 hi/lo parts + E8M0 scales per 32-block (one thread per block).
 __global__ __launch_bounds__(256) void split_rows_kernel(const uint16_t *__restrict__ src,
                                                          int64_t nblk, uint8_t *__restrict__ hi,
@@ -732,9 +935,16 @@ hipError_t launch_gemm1(const Shape &s, const Plan &p, const Workspace &ws, cons
         // x was split into FP8 parts in the router stage (launch_split_x)
         MxArgs pa{ws.xhi, ws.xlo, ws.xshi, ws.xslo, ws.perm, ws.tiles, ws.ntiles, wpk, sc,
                   ws.h, nullptr, s.d, s.F, s.k, s.F / 128};
-        const int64_t grid = 8 * ((max_tiles(s, p.tile_rows) * pa.ntn + 7) / 8);
-        hipExtLaunchKernelGGL(gemm_mx_kernel<true, kMxWaves>, dim3((unsigned)grid), dim3(64 * kMxWaves),
-                              0, st, ev0, ev1, 0, pa);
+        if (kUseWide && pa.ntn % 2 == 0) {
+            pa.ntn /= 2;  // pairs of weight tiles
+            const int64_t grid = 8 * ((max_tiles(s, p.tile_rows) * pa.ntn + 7) / 8);
+            hipExtLaunchKernelGGL(gemm_mxw_kernel<true>, dim3((unsigned)grid), dim3(512), 0, st, ev0,
+                                  ev1, 0, pa);
+        } else {
+            const int64_t grid = 8 * ((max_tiles(s, p.tile_rows) * pa.ntn + 7) / 8);
+            hipExtLaunchKernelGGL(gemm_mx_kernel<true, kMxWaves>, dim3((unsigned)grid),
+                                  dim3(64 * kMxWaves), 0, st, ev0, ev1, 0, pa);
+        }
     } else if (p.stream) {
         const int R = p.tile_rows;
         const size_t lds = (size_t)R * (2 * s.d + 2 * (s.d / 32));
@@ -770,8 +980,14 @@ hipError_t launch_gemm2(const Shape &s, const Plan &p, const Workspace &ws, cons
         if (e != hipSuccess) return e;
         MxArgs pa{ws.hhi, ws.hlo, ws.hshi, ws.hslo, nullptr, ws.tiles, ws.ntiles, wpk, sc,
                   ws.o, ws.ssq, s.d, s.F, s.k, s.d / 256};
-        const int64_t grid = 8 * ((max_tiles(s, p.tile_rows) * pa.ntn + 7) / 8);
-        gemm_mx_kernel<false, kMxWaves><<<(unsigned)grid, 64 * kMxWaves, 0, st>>>(pa);
+        if (kUseWide && pa.ntn % 2 == 0) {
+            pa.ntn /= 2;
+            const int64_t grid = 8 * ((max_tiles(s, p.tile_rows) * pa.ntn + 7) / 8);
+            gemm_mxw_kernel<false><<<(unsigned)grid, 512, 0, st>>>(pa);
+        } else {
+            const int64_t grid = 8 * ((max_tiles(s, p.tile_rows) * pa.ntn + 7) / 8);
+            gemm_mx_kernel<false, kMxWaves><<<(unsigned)grid, 64 * kMxWaves, 0, st>>>(pa);
+        }
     } else {
         const int wgs = s.d / 64;
         const int64_t grid = max_tiles(s, p.tile_rows) * wgs;
