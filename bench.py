@@ -94,8 +94,8 @@ def make_sets(name, nsets, device):
 GATE_UP_KERNEL = {
     "decode1": "gemm1_stream_kernel (gate/up + SwiGLU, persistent, MX MFMA)",
     "decode4": "gemm1_stream_kernel (gate/up + SwiGLU, persistent, MX MFMA)",
-    "prefill": "gemm_mx_kernel<true> (gate/up + SwiGLU, 128x256 tiles, MX MFMA)",
-    "skewed": "gemm_mx_kernel<true> (gate/up + SwiGLU, 128x256 tiles, MX MFMA)",
+    "prefill": "gemm_mxw_kernel<true> (gate/up + SwiGLU, 128x512 tiles, MX MFMA)",
+    "skewed": "gemm_mxw_kernel<true> (gate/up + SwiGLU, 128x512 tiles, MX MFMA)",
 }
 
 
