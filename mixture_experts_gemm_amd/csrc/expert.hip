@@ -60,6 +60,17 @@ __device__ __forceinline__ floatx4_t mfma_chunk(const uint4 *a, uint4 b, float s
 
 // ---- small device helpers ---------------------------------------------------
 
+// Streaming loads of weight bytes: each is read once per layer call, so they
+// are marked non-temporal (no reuse expected in the caches).
+typedef unsigned int v4u_nt_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld_stream16(const void *p)
+{
+    const v4u_nt_t v = __builtin_nontemporal_load(reinterpret_cast<const v4u_nt_t *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint32_t ld_stream4(const uint32_t *p) { return __builtin_nontemporal_load(p); }
+
+
 // Contiguous per-XCD tile ranges (workgroup w runs on XCD w % 8, so
 // neighbouring tiles -- same rows, same expert -- share that XCD's L2);
 // returns false for surplus workgroups.
@@ -160,8 +171,8 @@ __global__ __launch_bounds__(256) void gemm1_decode_kernel(
             if (c + u < c_end) {
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) {
-                    b[u][nb] = *reinterpret_cast<const uint4 *>(v.slot(nt, c + u, rho[nb], g));
-                    sw[u][nb] = *v.scales(nt, c + u, rho[nb]);
+                    b[u][nb] = ld_stream16(v.slot(nt, c + u, rho[nb], g));
+                    sw[u][nb] = ld_stream4(v.scales(nt, c + u, rho[nb]));
                 }
             }
     };
@@ -247,8 +258,8 @@ __global__ __launch_bounds__(256) void gemm2_decode_kernel(
 #pragma unroll
         for (int u = 0; u < U; ++u)
             if (c + u < nc) {
-                b[u] = *reinterpret_cast<const uint4 *>(v.slot(nt, c + u, rho, g));
-                sw[u] = *v.scales(nt, c + u, rho);
+                b[u] = ld_stream16(v.slot(nt, c + u, rho, g));
+                sw[u] = ld_stream4(v.scales(nt, c + u, rho));
             }
     };
     load_b(0);
@@ -805,8 +816,8 @@ __global__ __launch_bounds__(256) void gemm1_stream_kernel(
             const int rho = w1_rho(f, nb == 1);
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                b[u][nb] = *reinterpret_cast<const uint4 *>(v.slot(nt, c + u, rho, g));
-                sv[u][nb] = *v.scales(nt, c + u, rho);
+                b[u][nb] = ld_stream16(v.slot(nt, c + u, rho, g));
+                sv[u][nb] = ld_stream4(v.scales(nt, c + u, rho));
             }
         }
     };
