@@ -602,20 +602,28 @@ __global__ __launch_bounds__(512) void gemm_mxw_kernel(const MxArgs pa)
     const uint8_t *ssrc = v.stile(2 * np + (qb >> 8), 0) + (qb & 255) * 4;
 
     const int wvu = __builtin_amdgcn_readfirstlane(wv);
-    auto issue = [&](int kc, uint4 *Ah, uint4 *Al, uint32_t *Ac, uint4 *Bs, uint32_t *Ss) {
+    // The loads of a chunk go out in three parts spread over the multiply of
+    // the chunk before (activations first, then the two weight tiles), so a
+    // wave is not held at the address unit while its MFMAs could be issuing.
+    auto issue_part = [&](int part, int kc, uint4 *Ah, uint4 *Al, uint32_t *Ac, uint4 *Bs, uint32_t *Ss) {
+        if (part == 0) {
 #pragma unroll
-        for (int i = 0; i < AL; ++i)
-            if (aload[i]) dma16(ahsrc[i] + kc * kKStep, lds_off(Ah + (NW * i + wvu) * 64));
+            for (int i = 0; i < AL; ++i)
+                if (aload[i]) dma16(ahsrc[i] + kc * kKStep, lds_off(Ah + (NW * i + wvu) * 64));
 #pragma unroll
-        for (int i = 0; i < AL; ++i)
-            if (aload[i]) dma16(alsrc[i] + kc * kKStep, lds_off(Al + (NW * i + wvu) * 64));
-        if (acload) dma4(acsrc + kc * 4, lds_off(Ac + 32 * wvu));
-        const int64_t bo = (int64_t)kc * kWTileBytes;
-        dma16(bsrc0 + bo, lds_off(Bs + (0 + wvu) * 64));
-        dma16(bsrc0 + bo + 8192, lds_off(Bs + (NW + wvu) * 64));
-        dma16(bsrc1 + bo, lds_off(Bs + (2 * NW + wvu) * 64));
-        dma16(bsrc1 + bo + 8192, lds_off(Bs + (3 * NW + wvu) * 64));
-        dma4(ssrc + kc * kWTileScaleBytes, lds_off(Ss + 64 * wvu));
+            for (int i = 0; i < AL; ++i)
+                if (aload[i]) dma16(alsrc[i] + kc * kKStep, lds_off(Al + (NW * i + wvu) * 64));
+            if (acload) dma4(acsrc + kc * 4, lds_off(Ac + 32 * wvu));
+        } else if (part == 1) {
+            const int64_t bo = (int64_t)kc * kWTileBytes;
+            dma16(bsrc0 + bo, lds_off(Bs + (0 + wvu) * 64));
+            dma16(bsrc0 + bo + 8192, lds_off(Bs + (NW + wvu) * 64));
+        } else {
+            const int64_t bo = (int64_t)kc * kWTileBytes;
+            dma16(bsrc1 + bo, lds_off(Bs + (2 * NW + wvu) * 64));
+            dma16(bsrc1 + bo + 8192, lds_off(Bs + (3 * NW + wvu) * 64));
+            dma4(ssrc + kc * kWTileScaleBytes, lds_off(Ss + 64 * wvu));
+        }
     };
 
     // ---- compute assignment -------------------------------------------------
@@ -632,8 +640,12 @@ __global__ __launch_bounds__(512) void gemm_mxw_kernel(const MxArgs pa)
 #pragma unroll
         for (int nb = 0; nb < 8; ++nb) acc[mb][nb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
+    // multiply the chunk in (Ah, Al, Ac, Bs, Ss); when kn >= 0 the parts of
+    // chunk kn's loads (into the other slot) are issued along the way
     auto compute = [&](const uint4 *Ah, const uint4 *Al, const uint32_t *Ac, const uint4 *Bs,
-                       const uint32_t *Ss) {
+                       const uint32_t *Ss, int kn, uint4 *Ahn, uint4 *Aln, uint32_t *Acn, uint4 *Bn,
+                       uint32_t *Sn) {
+        if (kn >= 0) issue_part(0, kn, Ahn, Aln, Acn, Bn, Sn);
         uint4 bw[8];
         uint32_t bsc[8];
 #pragma unroll
@@ -658,20 +670,21 @@ __global__ __launch_bounds__(512) void gemm_mxw_kernel(const MxArgs pa)
 #pragma unroll
                 for (int nb = 0; nb < 8; ++nb) acc[mb][nb] = mfma_mx(l0, l1, bw[nb], sl, bsc[nb], acc[mb][nb]);
             }
+            __builtin_amdgcn_sched_barrier(0);
+            if (mb < 2 && kn >= 0) issue_part(mb + 1, kn, Ahn, Aln, Acn, Bn, Sn);
         }
     };
 
     // ---- pipeline: two slots; the barrier before chunk kc also waits for this
-    // wave's LDS reads of chunk kc-1, whose slot chunk kc+1 then refills ------
-    issue(0, Ah0, Al0, Ac0, Bs0, Ss0);
+    // wave's LDS reads of chunk kc-1, whose slot chunk kc+1 then refills, and
+    // for all of this wave's loads of chunk kc ----------------------------------
+    for (int part = 0; part < 3; ++part) issue_part(part, 0, Ah0, Al0, Ac0, Bs0, Ss0);
     for (int kc = 0; kc < nk; kc += 2) {
         phase_sync<0>();
-        if (kc + 1 < nk) issue(kc + 1, Ah1, Al1, Ac1, Bs1, Ss1);
-        compute(Ah0, Al0, Ac0, Bs0, Ss0);
+        compute(Ah0, Al0, Ac0, Bs0, Ss0, kc + 1 < nk ? kc + 1 : -1, Ah1, Al1, Ac1, Bs1, Ss1);
         if (kc + 1 < nk) {
             phase_sync<0>();
-            if (kc + 2 < nk) issue(kc + 2, Ah0, Al0, Ac0, Bs0, Ss0);
-            compute(Ah1, Al1, Ac1, Bs1, Ss1);
+            compute(Ah1, Al1, Ac1, Bs1, Ss1, kc + 2 < nk ? kc + 2 : -1, Ah0, Al0, Ac0, Bs0, Ss0);
         }
     }
 
