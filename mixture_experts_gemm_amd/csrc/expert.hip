@@ -646,29 +646,60 @@ __global__ __launch_bounds__(512) void gemm_mxw_kernel(const MxArgs pa)
                        const uint32_t *Ss, int kn, uint4 *Ahn, uint4 *Aln, uint32_t *Acn, uint4 *Bn,
                        uint32_t *Sn) {
         if (kn >= 0) issue_part(0, kn, Ahn, Aln, Acn, Bn, Sn);
+        // LDS reads return in order: row block 0's A fragments first, then the
+        // weight fragments, so the first MFMAs wait for two reads, not ten
+        struct AFr {
+            uint4 h0, h1, l0, l1;
+            uint32_t sh, sl;
+        };
+        auto read_a = [&](int mb) {
+            AFr f;
+            const int row = wm * 64 + mb * 16 + n16;
+            const int sw = row & 7;
+            f.h0 = Ah[row * 8 + (g ^ sw)];
+            f.h1 = Ah[row * 8 + ((4 + g) ^ sw)];
+            f.l0 = Al[row * 8 + (g ^ sw)];
+            f.l1 = Al[row * 8 + ((4 + g) ^ sw)];
+            f.sh = (Ac[row * 2] >> (8 * g)) & 0xFFu;
+            f.sl = (Ac[row * 2 + 1] >> (8 * g)) & 0xFFu;
+            return f;
+        };
         uint4 bw[8];
         uint32_t bsc[8];
-#pragma unroll
-        for (int nb = 0; nb < 8; ++nb) {
+        auto read_b = [&](int nb) {
             const int rho = wn * 128 + nb * 16 + n16;  // row of the 512; bank swizzle of its tile row
             bw[nb] = Bs[rho * 4 + (g ^ bswz(rho))];
             bsc[nb] = (Ss[rho] >> (8 * g)) & 0xFFu;
+        };
+        // row block 0: each weight fragment is read two MFMAs before its use
+        {
+            const AFr f = read_a(0);
+            read_b(0);
+            read_b(1);
+#pragma unroll
+            for (int nb = 0; nb < 8; ++nb) {
+                __builtin_amdgcn_sched_barrier(0);
+                if (nb + 2 < 8) read_b(nb + 2);
+                if (mb_act > 0) acc[0][nb] = mfma_mx(f.h0, f.h1, bw[nb], f.sh, bsc[nb], acc[0][nb]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if (mb_act > 0) {
+#pragma unroll
+                for (int nb = 0; nb < 8; ++nb) acc[0][nb] = mfma_mx(f.l0, f.l1, bw[nb], f.sl, bsc[nb], acc[0][nb]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if (kn >= 0) issue_part(1, kn, Ahn, Aln, Acn, Bn, Sn);
         }
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
+        for (int mb = 1; mb < MB; ++mb) {
             // one row block's A fragments at a time (the accumulators take 128 registers)
             __builtin_amdgcn_sched_barrier(0);
             if (mb < mb_act) {
-                const int row = wm * 64 + mb * 16 + n16;
-                const int sw = row & 7;
-                const uint4 h0 = Ah[row * 8 + (g ^ sw)], h1 = Ah[row * 8 + ((4 + g) ^ sw)];
-                const uint4 l0 = Al[row * 8 + (g ^ sw)], l1 = Al[row * 8 + ((4 + g) ^ sw)];
-                const uint32_t sh = (Ac[row * 2] >> (8 * g)) & 0xFFu;
-                const uint32_t sl = (Ac[row * 2 + 1] >> (8 * g)) & 0xFFu;
+                const AFr f = read_a(mb);
 #pragma unroll
-                for (int nb = 0; nb < 8; ++nb) acc[mb][nb] = mfma_mx(h0, h1, bw[nb], sh, bsc[nb], acc[mb][nb]);
+                for (int nb = 0; nb < 8; ++nb) acc[mb][nb] = mfma_mx(f.h0, f.h1, bw[nb], f.sh, bsc[nb], acc[mb][nb]);
 #pragma unroll
-                for (int nb = 0; nb < 8; ++nb) acc[mb][nb] = mfma_mx(l0, l1, bw[nb], sl, bsc[nb], acc[mb][nb]);
+                for (int nb = 0; nb < 8; ++nb) acc[mb][nb] = mfma_mx(f.l0, f.l1, bw[nb], f.sl, bsc[nb], acc[mb][nb]);
             }
             __builtin_amdgcn_sched_barrier(0);
             if (mb < 2 && kn >= 0) issue_part(mb + 1, kn, Ahn, Aln, Acn, Bn, Sn);
