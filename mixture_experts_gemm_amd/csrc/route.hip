@@ -414,10 +414,15 @@ __device__ void finish_offsets(int32_t *cnt, int32_t *toff, int32_t *wtot, int E
         const int c = c_out[q];
         counts[e] = c;
         offsets[e] = cnt[e];
-        // an expert's rows are spread evenly over its tiles, so its tiles
-        // (which read the same weights) advance at the same pace
+        // an expert's rows are spread about evenly over its tiles, so its
+        // tiles (which read the same weights) advance at about the same pace;
+        // for large tiles the share is rounded up to 16 rows, the MFMA row
+        // block, so only the last tile has a partial block (140 rows: 80 + 60,
+        // 9 blocks, not 70 + 70, 10 blocks).  (nt-1)*per < c still holds:
+        // per <= tile_rows and nt = ceil(c / tile_rows).
         const int nt = (c + tile_rows - 1) / tile_rows;
-        const int per = nt > 0 ? (c + nt - 1) / nt : 0;
+        int per = nt > 0 ? (c + nt - 1) / nt : 0;
+        if (tile_rows >= 32) per = min(tile_rows, (per + 15) & ~15);
         for (int i = 0; i < nt; ++i) {
             Tile tl;
             tl.expert = e;
