@@ -226,44 +226,59 @@ hipError_t launch_router(const Shape &s, const Plan &p, const Workspace &ws, con
 }
 
 // ---------------------------------------------------------------------------
-// Top-k + softmax for one token, by one wave.  Each lane keeps SLOTS scores
-// (expert lane + 64*q); k rounds of a wave-wide arg-max under
-// (score desc, id asc) -- DPP steps inside rows of 16 lanes, then the four
-// row winners are compared from readlane.  The j-th choice is parked in lane
-// j%64, slot j/64; the softmax over the chosen scores is one wave sum.
-// NaN scores are treated as -inf so every choice is a valid expert id.
+// Top-k + softmax for one token, by one wave.  A candidate (score, expert) is
+// one 64-bit key that orders as (score desc, id asc): the score's bits made
+// order-preserving as an unsigned integer in the high word (-0 counted as +0,
+// NaN as -inf) and ~id in the low word, so a comparison is one 64-bit max.
+// Each lane keeps SLOTS keys (experts lane + 64*q) sorted best first; each of
+// the k rounds takes the wave's largest head (butterfly DPP steps inside rows
+// of 16 lanes, then row_bcast15/31 across rows; the maximum lands in lane 63)
+// and the owning lane pops it.  The j-th choice is parked in lane j%64, slot
+// j/64; the softmax over the chosen scores is one wave sum.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ bool better(float va, int ia, float vb, int ib)
-{
-    return va > vb || (va == vb && ia < ib);
-}
-
 constexpr int kNone = 0x7FFFFFFF;
 
-template <int C>
-__device__ __forceinline__ void argmax_step(float &v, int &id)
+__device__ __forceinline__ uint64_t topk_key(float v, int id)
 {
-    const float ov = dpp_f<C>(v);
-    const int oi = dpp_i<C>(id);
-    if (better(ov, oi, v, id)) { v = ov; id = oi; }
+    if (!(v == v)) v = -INFINITY;
+    if (v == 0.f) v = 0.f;  // -0 ties with +0 (then the lower id wins)
+    uint32_t b = __float_as_uint(v);
+    b = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+    return ((uint64_t)b << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)id);
 }
 
-__device__ __forceinline__ void wave_argmax(float &v, int &id)
+__device__ __forceinline__ float key_score(uint64_t key)
 {
-    argmax_step<0xB1>(v, id);
-    argmax_step<0x4E>(v, id);
-    argmax_step<0x141>(v, id);
-    argmax_step<0x140>(v, id);
-    float bv = readlane_f(v, 0);
-    int bi = __builtin_amdgcn_readlane(id, 0);
-#pragma unroll
-    for (int r = 16; r < 64; r += 16) {
-        const float ov = readlane_f(v, r);
-        const int oi = __builtin_amdgcn_readlane(id, r);
-        if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-    }
-    v = bv;
-    id = bi;
+    const uint32_t b = (uint32_t)(key >> 32);
+    return __uint_as_float((b & 0x80000000u) ? (b & 0x7FFFFFFFu) : ~b);
+}
+
+__device__ __forceinline__ int key_id(uint64_t key) { return (int)(0xFFFFFFFFu - (uint32_t)key); }
+
+// max of key and the key DPP control C brings from another lane (rows outside
+// ROW_MASK keep their own key)
+template <int C, int ROW_MASK>
+__device__ __forceinline__ uint64_t key_max_step(uint64_t key)
+{
+    const int lo = (int)(uint32_t)key, hi = (int)(uint32_t)(key >> 32);
+    const uint32_t olo = (uint32_t)__builtin_amdgcn_update_dpp(lo, lo, C, ROW_MASK, 0xF, false);
+    const uint32_t ohi = (uint32_t)__builtin_amdgcn_update_dpp(hi, hi, C, ROW_MASK, 0xF, false);
+    const uint64_t o = ((uint64_t)ohi << 32) | olo;
+    return o > key ? o : key;
+}
+
+// the wave's largest key, in every lane
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t key)
+{
+    key = key_max_step<0xB1, 0xF>(key);   // quad_perm [1,0,3,2]
+    key = key_max_step<0x4E, 0xF>(key);   // quad_perm [2,3,0,1]
+    key = key_max_step<0x141, 0xF>(key);  // row_half_mirror
+    key = key_max_step<0x140, 0xF>(key);  // row_mirror: every lane holds its row's max
+    key = key_max_step<0x142, 0xA>(key);  // row_bcast15: rows 1, 3 take rows 0, 2
+    key = key_max_step<0x143, 0xC>(key);  // row_bcast31: rows 2, 3 take row 1
+    const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)key, 63);
+    const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(key >> 32), 63);
+    return ((uint64_t)hi << 32) | lo;
 }
 
 // l: the token's scores, or its first partial-score plane when the router
@@ -274,10 +289,7 @@ __device__ void topk_row(const float *__restrict__ l, int E, int k, int32_t *__r
                          float *__restrict__ w_out, int32_t *sid_out, int lane, int nsplit,
                          int64_t stride)
 {
-    // each lane keeps its SLOTS candidates (experts lane + 64q) sorted best
-    // first; a round takes the wave's best head and the owner pops it
-    float v[SLOTS];
-    int id[SLOTS];
+    uint64_t key[SLOTS];
 #pragma unroll
     for (int q = 0; q < SLOTS; ++q) {
         const int e = lane + 64 * q;
@@ -286,47 +298,40 @@ __device__ void topk_row(const float *__restrict__ l, int E, int k, int32_t *__r
             x = l[e];
             for (int sp = 1; sp < nsplit; ++sp) x += l[sp * stride + e];
         }
-        v[q] = x == x ? x : -INFINITY;
-        id[q] = e < E ? e : kNone;
+        key[q] = topk_key(x, e < E ? e : kNone);
     }
 #pragma unroll
     for (int pass = 0; pass < SLOTS; ++pass)
 #pragma unroll
         for (int q = pass & 1; q + 1 < SLOTS; q += 2)
-            if (better(v[q + 1], id[q + 1], v[q], id[q])) {
-                const float tv = v[q];
-                const int ti = id[q];
-                v[q] = v[q + 1];
-                id[q] = id[q + 1];
-                v[q + 1] = tv;
-                id[q + 1] = ti;
+            if (key[q + 1] > key[q]) {
+                const uint64_t t = key[q];
+                key[q] = key[q + 1];
+                key[q + 1] = t;
             }
-    float mysc[SLOTS];
-    int myid[SLOTS];
-    float top0 = 0.f;
-    for (int j = 0; j < k; ++j) {
-        float bv = v[0];
-        int bi = id[0];
-        wave_argmax(bv, bi);
-        if ((bi & 63) == lane) {
+    const uint64_t none = topk_key(-INFINITY, kNone);
+    uint64_t mine[SLOTS];
 #pragma unroll
-            for (int q = 0; q + 1 < SLOTS; ++q) {
-                v[q] = v[q + 1];
-                id[q] = id[q + 1];
-            }
-            v[SLOTS - 1] = -INFINITY;
-            id[SLOTS - 1] = kNone;
+    for (int q = 0; q < SLOTS; ++q) mine[q] = none;
+    uint64_t top = none;
+    for (int j = 0; j < k; ++j) {
+        const uint64_t best = wave_max_key(key[0]);
+        if (key[0] == best) {  // keys are distinct: exactly the owner lane
+#pragma unroll
+            for (int q = 0; q + 1 < SLOTS; ++q) key[q] = key[q + 1];
+            key[SLOTS - 1] = none;
         }
-        if (j == 0) top0 = bv;
+        if (j == 0) top = best;
 #pragma unroll
         for (int q = 0; q < SLOTS; ++q)
-            if ((j >> 6) == q && (j & 63) == lane) { mysc[q] = bv; myid[q] = bi; }
+            if ((j >> 6) == q && (j & 63) == lane) mine[q] = best;
     }
+    const float top0 = key_score(top);
     float z = 0.f;
     float ex[SLOTS];
 #pragma unroll
     for (int q = 0; q < SLOTS; ++q) {
-        ex[q] = (lane + 64 * q < k) ? expf(mysc[q] - top0) : 0.f;
+        ex[q] = (lane + 64 * q < k) ? expf(key_score(mine[q]) - top0) : 0.f;
         z += ex[q];
     }
     z = wave_sum(z);
@@ -335,9 +340,10 @@ __device__ void topk_row(const float *__restrict__ l, int E, int k, int32_t *__r
     for (int q = 0; q < SLOTS; ++q) {
         const int j = lane + 64 * q;
         if (j < k) {
-            ids_out[j] = myid[q];
+            const int e = key_id(mine[q]);
+            ids_out[j] = e;
             w_out[j] = ex[q] * inv;
-            if (sid_out) sid_out[j] = myid[q];
+            if (sid_out) sid_out[j] = e;
         }
     }
 }
