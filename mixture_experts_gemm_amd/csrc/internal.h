@@ -38,6 +38,15 @@ struct Shape {
 constexpr int kStreamMaxT = 8;
 constexpr int kStreamRows = 2;
 
+#ifndef MOE_TILED_MIN_ROWS
+#define MOE_TILED_MIN_ROWS 16
+#endif
+// Average rows per expert from which the tiled (MX) kernels run.  Below
+// it the few-row kernels use 16-row tiles, which read an expert's weights
+// once per tile: from about 16 rows per expert the 128-row tiles read them
+// fewer times (measured: 753 rows over 32 experts, 586 -> 301 us).
+constexpr int kTiledMinRows = MOE_TILED_MIN_ROWS;
+
 struct Plan {
     bool tiled;
     bool stream;    // persistent streaming gate/up kernel (decode)
@@ -50,7 +59,7 @@ inline Plan make_plan(const Shape &s)
 {
     Plan p;
     const int64_t S = s.S();
-    p.tiled = S >= (int64_t)32 * s.E && s.d % 256 == 0 && s.F % 128 == 0;
+    p.tiled = S >= (int64_t)kTiledMinRows * s.E && s.d % 256 == 0 && s.F % 128 == 0;
     p.stream = !p.tiled && s.d % 2048 == 0 && s.T <= kStreamMaxT;
     p.tile_rows = p.tiled ? 128 : p.stream ? (s.T < kStreamRows ? s.T : kStreamRows) : 16;
     if (p.tile_rows < 1) p.tile_rows = 1;
