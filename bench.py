@@ -30,6 +30,10 @@ WORKLOAD_TEXT = {
     "decode1": "Muse-shaped decode, single request (T=1, d=8192, E=256, top-8, F=2048, MXFP4)",
     "prefill": "Muse-shaped prefill micro-batch (T=4096, d=8192, E=256, top-8, F=2048, MXFP4, uniform routing)",
     "skewed": "Skewed-routing prefill (T=16384, Zipf(1.2) router bias, top-8 experts ~40% of slots)",
+    "ep753": "One GPU's share under 8-way expert parallelism, 753-token batch (E=32 local experts, "
+             "753 routed rows, k=1, d=8192, F=2048, MXFP4)",
+    "ep3012": "One GPU's share under 8-way expert parallelism, 3012-token batch (E=32 local experts, "
+              "3012 routed rows, k=1, d=8192, F=2048, MXFP4)",
 }
 
 
@@ -43,7 +47,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="decode4", choices=sorted(WORKLOAD_TEXT))
-    ap.add_argument("--also", default="decode1,prefill",
+    ap.add_argument("--also", default="decode1,prefill,ep753,ep3012",
                     help="comma list of extra workloads timed after the main one ('' for none)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
@@ -96,6 +100,8 @@ GATE_UP_KERNEL = {
     "decode4": "gemm1_stream_kernel (gate/up + SwiGLU, persistent, MX MFMA)",
     "prefill": "gemm_mxw_kernel<true> (gate/up + SwiGLU, 128x512 tiles, MX MFMA)",
     "skewed": "gemm_mxw_kernel<true> (gate/up + SwiGLU, 128x512 tiles, MX MFMA)",
+    "ep753": "gemm_mxw_kernel<true> (gate/up + SwiGLU, 128x512 tiles, MX MFMA)",
+    "ep3012": "gemm_mxw_kernel<true> (gate/up + SwiGLU, 128x512 tiles, MX MFMA)",
 }
 
 
@@ -164,27 +170,31 @@ def time_workload(name, steps, warmup, device):
         T=T, steps=steps, ms_per_step=elapsed / steps * 1e3, tokens_per_s=T * steps / elapsed,
         gemm1_ms=g1_ms, gemm1_timed_launches=len(timed), distinct_experts_mean=u_mean, finite=out_ok,
     )
-    if decode:
-        # bytes of the timed launches (U, the distinct experts, differs per step)
-        nbytes = sum(R.mxfp4_w1_bytes(s.d, s.F) * U[i] + T * s.d * 2 + S * s.F * 2
-                     for i in timed) / len(timed)
+    # the gate/up kernel's algorithmic bytes (over the timed launches: U, the
+    # distinct experts, differs per step) and flops; its bound is the larger
+    # of the two times at the peaks
+    nbytes = sum(R.mxfp4_w1_bytes(s.d, s.F) * U[i] + T * s.d * 2 + S * s.F * 2
+                 for i in timed) / len(timed)
+    flops = R.gemm1_flops(S, s.d, s.F)
+    hbm_bound = nbytes / R.MI355X_HBM_BYTES_PER_S >= flops / R.MI355X_BF16_FLOPS_PER_S
+    if hbm_bound:
         achieved = nbytes / (g1_ms * 1e-3)
         res["roofline"] = dict(bound="hbm", achieved=achieved / 1e9, peak=R.MI355X_HBM_BYTES_PER_S / 1e9,
                                unit="GB/s", frac=achieved / R.MI355X_HBM_BYTES_PER_S,
                                traffic=R.recorded_traffic(counter_summary(name)),
                                kernel=GATE_UP_KERNEL[name],
                                algorithmic_bytes_per_launch=nbytes)
-        lb = sum(R.layer_bytes(T, s.d, s.E, s.F, u) for u in U) / steps
-        res["layer_hbm_frac"] = lb / (elapsed / steps) / R.MI355X_HBM_BYTES_PER_S
     else:
-        flops = R.gemm1_flops(S, s.d, s.F)
         achieved = flops / (g1_ms * 1e-3)
         res["roofline"] = dict(bound="mfma", achieved=achieved / 1e12, peak=R.MI355X_BF16_FLOPS_PER_S / 1e12,
                                unit="TFLOP/s", frac=achieved / R.MI355X_BF16_FLOPS_PER_S,
                                traffic=R.recorded_traffic(counter_summary(name)),
                                kernel=GATE_UP_KERNEL[name],
                                algorithmic_flops_per_launch=flops)
-        res["layer_mfma_frac"] = R.layer_flops(T, s.d, s.k, s.F) / (elapsed / steps) / R.MI355X_BF16_FLOPS_PER_S
+    # the whole layer against both peaks (algorithmic bytes with the realized U)
+    lb = sum(R.layer_bytes(T, s.d, s.E, s.F, u) for u in U) / len(U)
+    res["layer_hbm_frac"] = lb / (elapsed / steps) / R.MI355X_HBM_BYTES_PER_S
+    res["layer_mfma_frac"] = R.layer_flops(T, s.d, s.k, s.F) / (elapsed / steps) / R.MI355X_BF16_FLOPS_PER_S
     log(json.dumps(res))
     return res, host, T
 

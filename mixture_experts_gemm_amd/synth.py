@@ -21,6 +21,11 @@ routing (section ⑧), 4-bit block-scaled expert weights (section ⑪)):
   prefill   T=4096,  same shape, uniform routing, seed 2
   skewed    T=16384, same shape, Zipf(1.2)-biased routing, seed 3
   stack     4 chained layers, T=8192, same shape, seed 4 (substream per layer)
+  ep753     one GPU's share under 8-way expert parallelism (section ⑫: the 256
+  ep3012    experts spread over 8 GPUs, 32 each; section ⑭: 753- and
+            3,012-token batches): E=32 local experts, each routed (token,
+            expert) pair one row, so k=1 and T = 753 / 3,012 rows (about 24 /
+            94 rows per expert); seeds 5 / 6
 
 Value distributions: x = bf16(N(0,1)); router weights fp32 N(0, 0.02^2);
 expert weight bytes uniform over 0..255 (so both FP4 E2M1 nibbles are
@@ -89,6 +94,8 @@ WORKLOADS = {
     "prefill": Workload("prefill", Shape(4096, 8192, 256, 8, 2048), 2),
     "skewed": Workload("skewed", Shape(16384, 8192, 256, 8, 2048), 3, zipf=True),
     "stack": Workload("stack", Shape(8192, 8192, 256, 8, 2048), 4, layers=4),
+    "ep753": Workload("ep753", Shape(753, 8192, 32, 1, 2048), 5),
+    "ep3012": Workload("ep3012", Shape(3012, 8192, 32, 1, 2048), 6),
 }
 
 

@@ -269,6 +269,18 @@ def test_skewed_full_size():
     _check_tokens(L, out, _sample(16384, 10, 3, hot_tokens), "skewed")
 
 
+@pytest.mark.parametrize("name,n", [("ep753", 16), ("ep3012", 12)])
+def test_ep_share_full_size(name, n):
+    """One GPU's share under 8-way expert parallelism: 32 local experts, each
+    routed (token, expert) pair one row (k = 1), about 24 / 94 rows per expert."""
+    L = synth.make_layer(name)
+    _say(name, "T", L.shape.T)
+    out, dbg = run_layer(L)
+    r = _check_routing(L, dbg, name)
+    _check_tokens(L, out, _sample(L.shape.T, n, 5), name)
+    assert int(r["counts"].sum()) == L.shape.T
+
+
 def test_stack_of_four_layers():
     """Chained layers: each layer's bf16 output is the next layer's input.
 

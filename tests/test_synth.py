@@ -37,7 +37,7 @@ def _gaps(x_bits, wr, k):
 
 
 def test_router_margin_holds():
-    for name, T in (("tiny", None), ("decode4", None), ("prefill", 512), ("skewed", 256)):
+    for name, T in (("tiny", None), ("decode4", None), ("prefill", 512), ("skewed", 256), ("ep753", None)):
         w = synth.WORKLOADS[name]
         wr = synth.make_router(w)
         x = synth.make_tokens(w, wr, T=T)
