@@ -138,7 +138,7 @@ size_t moe_layer_workspace_size(const moe_dims_t *dims, int32_t k);
  *        tile row r is output row nt*256 + r;
  *   a tile row is 64 bytes: the codes of K elements 128kc..128kc+127 as four
  *   16-byte blocks of 32 elements, block b stored in slot
- *   b ^ (((r >> 1) ^ (r >> 3)) & 3);
+ *   b ^ ((r >> 1) & 3);
  *   scales: the same tiles, 1024 bytes each (W2 at byte d*F/16): tile row r
  *   holds the 4 E8M0 bytes of its blocks 4kc..4kc+3 in order.
  * Device pointers, 16-byte aligned, packed buffers of the same sizes as the

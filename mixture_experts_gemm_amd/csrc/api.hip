@@ -40,14 +40,21 @@ Workspace carve_workspace(const Shape &s, void *base)
     w.h = (uint16_t *)take(sizeof(uint16_t) * (size_t)S * s.F);
     w.o = (uint16_t *)take(sizeof(uint16_t) * (size_t)S * s.d);
     w.ssq = (float *)take(sizeof(float) * (size_t)S * (s.d / 64));
-    w.xhi = (uint8_t *)take((size_t)s.T * s.d);
-    w.xlo = (uint8_t *)take((size_t)s.T * s.d);
-    w.xshi = (uint8_t *)take((size_t)s.T * s.d / 32);
-    w.xslo = (uint8_t *)take((size_t)s.T * s.d / 32);
-    w.hhi = (uint8_t *)take((size_t)S * s.F);
-    w.hlo = (uint8_t *)take((size_t)S * s.F);
-    w.hshi = (uint8_t *)take((size_t)S * s.F / 32);
-    w.hslo = (uint8_t *)take((size_t)S * s.F / 32);
+    // one region per split: FP8 parts and scales, or the FP6 records
+    auto split_region = [&](int64_t rows, int K, uint8_t *&hi, uint8_t *&lo, uint8_t *&shi,
+                            uint8_t *&slo, uint8_t *&a6) {
+        const size_t part = align256((size_t)rows * K), sc = align256((size_t)rows * K / 32);
+        const size_t fp8 = 2 * part + 2 * sc;
+        const size_t fp6 = (size_t)rows * (K / 128) * kA6Bytes;
+        uint8_t *r = (uint8_t *)take(fp8 > fp6 ? fp8 : fp6);
+        hi = r;
+        lo = r ? r + part : nullptr;
+        shi = r ? r + 2 * part : nullptr;
+        slo = r ? r + 2 * part + sc : nullptr;
+        a6 = r;
+    };
+    split_region(s.T, s.d, w.xhi, w.xlo, w.xshi, w.xslo, w.xa6);
+    split_region(S, s.F, w.hhi, w.hlo, w.hshi, w.hslo, w.ha6);
     w.bytes = off;
     return w;
 }

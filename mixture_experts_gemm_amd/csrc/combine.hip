@@ -7,44 +7,68 @@
 //   section ③  the result is mixed into the residual stream through a gate
 //              with per-dimension alpha and beta: s <- alpha*s + beta*y.
 //
-// One workgroup per (token, 1024-column chunk).  The k slot rows of o are
-// found through inv; their sums of squares come from the partials written by
-// the down-projection kernel, added in a fixed order.  s_out may be x
+// One workgroup per (token, 2048-column chunk).  The k slot rows of o are
+// either stored in slot order (few-row path) or found through inv (tiled
+// path); their sums of squares come from the partials written by the
+// down-projection kernel, added in a fixed order.  s_out may be x
 // itself: each thread reads its x elements before writing the same elements.
 #include "device.h"
 #include "internal.h"
 
 namespace moe {
 
-constexpr int kMaxK = 64;  // slots handled per pass over the row
+constexpr int kMaxK = 64;          // slots handled per pass over the row
+constexpr int kSlotBatch = 8;       // slots per pass when o is in slot order
+constexpr int kCombineCols = 2048;  // columns per workgroup (8 per thread)
 
+// SLOT: o and the o^2 partial sums are stored in slot order (row t*k + j is
+// slot j of token t); otherwise in the grouped order, found through inv.
+template <bool SLOT>
 __global__ __launch_bounds__(256) void combine_kernel(
     const uint16_t *x, const float *__restrict__ wts, const int32_t *__restrict__ inv,
     const uint16_t *__restrict__ o, const float *__restrict__ ssq, const float *__restrict__ alpha,
     const float *__restrict__ beta, uint16_t *s_out, int d, int k, int P, float eps)
 {
-    __shared__ float coef[kMaxK];
-    __shared__ int32_t row[kMaxK];
+    constexpr int JB = SLOT ? kSlotBatch : kMaxK;  // slots per pass over the row
+    __shared__ float coef[JB];
+    __shared__ int32_t row[JB];
     const int t = blockIdx.x;
-    const int c0 = blockIdx.y * 1024 + threadIdx.x * 4;
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int c0 = blockIdx.y * kCombineCols + threadIdx.x * 8;  // 8 columns per thread
     const bool act = c0 < d;
     // independent loads first
-    uint2 xv = make_uint2(0, 0);
-    float4 a = make_float4(0, 0, 0, 0), b = a;
+    uint4 xv = make_uint4(0, 0, 0, 0);
+    float4 a0 = make_float4(0, 0, 0, 0), a1 = a0, b0 = a0, b1 = a0;
     if (act) {
-        xv = *reinterpret_cast<const uint2 *>(x + (int64_t)t * d + c0);
-        a = *reinterpret_cast<const float4 *>(alpha + c0);
-        b = *reinterpret_cast<const float4 *>(beta + c0);
+        xv = *reinterpret_cast<const uint4 *>(x + (int64_t)t * d + c0);
+        a0 = *reinterpret_cast<const float4 *>(alpha + c0);
+        a1 = *reinterpret_cast<const float4 *>(alpha + c0 + 4);
+        b0 = *reinterpret_cast<const float4 *>(beta + c0);
+        b1 = *reinterpret_cast<const float4 *>(beta + c0 + 4);
     }
-    float y[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int j0 = 0; j0 < k; j0 += kMaxK) {
-        const int kk = min(kMaxK, k - j0);
+    float y[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    auto accumulate = [&](const uint4 &ov, float cj) {
+        const uint32_t ow[4] = {ov.x, ov.y, ov.z, ov.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            y[2 * i] = fmaf(cj, __uint_as_float(ow[i] << 16), y[2 * i]);
+            y[2 * i + 1] = fmaf(cj, __uint_as_float(ow[i] & 0xFFFF0000u), y[2 * i + 1]);
+        }
+    };
+    for (int j0 = 0; j0 < k; j0 += JB) {
+        const int kk = min(JB, k - j0);
+        // slot order: the pass's o values go out together with the norms' loads
+        uint4 ov[SLOT ? kSlotBatch : 1];
+        if constexpr (SLOT) {
+#pragma unroll
+            for (int j = 0; j < kSlotBatch; ++j)
+                ov[j] = act && j < kk ? *reinterpret_cast<const uint4 *>(o + ((int64_t)t * k + j0 + j) * d + c0)
+                                      : make_uint4(0, 0, 0, 0);
+        }
         __syncthreads();
         // 16 lanes per slot: 16 slots per pass of the workgroup
         for (int j = (threadIdx.x >> 4); j < kk; j += 16) {
             const int64_t slot = (int64_t)t * k + j0 + j;
-            const int p = inv[slot];
+            const int p = SLOT ? (int)slot : inv[slot];
             float ss = 0.f;
             const float *sp = ssq + (int64_t)p * P;
 #pragma unroll 4
@@ -57,36 +81,42 @@ __global__ __launch_bounds__(256) void combine_kernel(
         }
         __syncthreads();
         if (act) {
-            for (int j = 0; j < kk; ++j) {
-                const uint2 ov = *reinterpret_cast<const uint2 *>(o + (int64_t)row[j] * d + c0);
-                const float cj = coef[j];
-                y[0] = fmaf(cj, __uint_as_float(ov.x << 16), y[0]);
-                y[1] = fmaf(cj, __uint_as_float(ov.x & 0xFFFF0000u), y[1]);
-                y[2] = fmaf(cj, __uint_as_float(ov.y << 16), y[2]);
-                y[3] = fmaf(cj, __uint_as_float(ov.y & 0xFFFF0000u), y[3]);
+            if constexpr (SLOT) {
+#pragma unroll
+                for (int j = 0; j < kSlotBatch; ++j)
+                    if (j < kk) accumulate(ov[j], coef[j]);
+            } else {
+                for (int j = 0; j < kk; ++j)
+                    accumulate(*reinterpret_cast<const uint4 *>(o + (int64_t)row[j] * d + c0), coef[j]);
             }
         }
     }
-    (void)lane;
-    (void)wv;
     if (act) {
-        const float s0 = fmaf(b.x, y[0], a.x * __uint_as_float(xv.x << 16));
-        const float s1 = fmaf(b.y, y[1], a.y * __uint_as_float(xv.x & 0xFFFF0000u));
-        const float s2 = fmaf(b.z, y[2], a.z * __uint_as_float(xv.y << 16));
-        const float s3 = fmaf(b.w, y[3], a.w * __uint_as_float(xv.y & 0xFFFF0000u));
-        uint2 out;
-        out.x = (uint32_t)f32_to_bf16(s0) | (uint32_t)f32_to_bf16(s1) << 16;
-        out.y = (uint32_t)f32_to_bf16(s2) | (uint32_t)f32_to_bf16(s3) << 16;
-        *reinterpret_cast<uint2 *>(s_out + (int64_t)t * d + c0) = out;
+        const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+        const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+        const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+        uint32_t ow[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float s0 = fmaf(bv[2 * i], y[2 * i], av[2 * i] * __uint_as_float(xw[i] << 16));
+            const float s1 = fmaf(bv[2 * i + 1], y[2 * i + 1], av[2 * i + 1] * __uint_as_float(xw[i] & 0xFFFF0000u));
+            ow[i] = (uint32_t)f32_to_bf16(s0) | (uint32_t)f32_to_bf16(s1) << 16;
+        }
+        *reinterpret_cast<uint4 *>(s_out + (int64_t)t * d + c0) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
     }
 }
 
 hipError_t launch_combine(const Shape &s, const Plan &p, const Workspace &ws, const uint16_t *x,
                           const float *alpha, const float *beta, uint16_t *s_out, hipStream_t st)
 {
-    dim3 grid(s.T, (s.d + 1023) / 1024);
-    combine_kernel<<<grid, 256, 0, st>>>(x, ws.wts, ws.inv, ws.o, ws.ssq, alpha, beta, s_out, s.d,
-                                         s.k, s.d / p.ssq_cols, s.eps);
+    dim3 grid(s.T, (s.d + kCombineCols - 1) / kCombineCols);
+    // the few-row down kernel stores in slot order, the tiled ones in the grouped order
+    if (p.tiled)
+        combine_kernel<false><<<grid, 256, 0, st>>>(x, ws.wts, ws.inv, ws.o, ws.ssq, alpha, beta, s_out,
+                                                    s.d, s.k, s.d / p.ssq_cols, s.eps);
+    else
+        combine_kernel<true><<<grid, 256, 0, st>>>(x, ws.wts, ws.inv, ws.o, ws.ssq, alpha, beta, s_out,
+                                                   s.d, s.k, s.d / p.ssq_cols, s.eps);
     return hipGetLastError();
 }
 

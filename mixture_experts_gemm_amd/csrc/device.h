@@ -138,6 +138,55 @@ __device__ __forceinline__ void split_e4m3_block(const float *v, uint32_t *hi, u
     slo = (uint32_t)(sl + 127);
 }
 
+// ---- three-part FP6 split of a 32-value block -------------------------------
+// Each part is FP6 E2M3 (sign, 2 exponent bits, 3 mantissa bits; magnitudes
+// 0 .. 7.5, steps of 1/8 below 2, 1/4 below 4, 1/2 up to 7.5) with its own
+// E8M0 scale, taken from the block's largest remaining magnitude R = 2^e*1.f:
+//   s = e - 2, or e - 1 when R / 2^(e-2) >= 7.75 (rounding would reach 8);
+//   part = RNE_e2m3(r / 2^s), r <- r - part * 2^s.
+// No part saturates, and each part's rounding error is at most 2^(s-2), so
+// the scales fall by at least 4 per part and the three-part error is at most
+// 2^(E-11), E the exponent of the block maximum.  In practice far less: a
+// part holds the top 4 significant bits of every value within three binades
+// of R, so bf16 values near the block maximum are exact after two parts and
+// nearly all after three (largest error seen on Gaussian, heavy-tailed and
+// outlier blocks: 2^-15 of the block maximum).  The hardware's scaled conversions do
+// the rounding (round to nearest even, verified on gfx950) and the inverse;
+// the 2x16 form places element i of its first operand at code 2i and of its
+// second at code 2i+1, so the even and odd elements are passed apart to get
+// the natural order (code j in bits 6j .. 6j+5, the MFMA operand layout).
+typedef int v6i_t __attribute__((__vector_size__(6 * sizeof(int))));
+typedef float v16f_t __attribute__((__vector_size__(16 * sizeof(float))));
+typedef float v32f_t __attribute__((__vector_size__(32 * sizeof(float))));
+
+__device__ __forceinline__ void split_e2m3x3_block(float (&r)[32], uint32_t (&code)[3][6],
+                                                   uint32_t (&sc)[3])
+{
+#pragma unroll
+    for (int p = 0; p < 3; ++p) {
+        float amax = 0.f;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(r[i]));
+        int s = (int)((__float_as_uint(amax) >> 23) & 0xFF) - 127 - 2;
+        if (amax >= 7.75f * pow2f(s < -126 ? -126 : s)) ++s;
+        s = s < -126 ? -126 : s;  // zero or tiny blocks: the smallest normal scale
+        const float scale = pow2f(s);
+        v16f_t ev, od;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            ev[i] = r[2 * i];
+            od[i] = r[2 * i + 1];
+        }
+        const v6i_t c = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(ev, od, scale);
+        const v32f_t q = __builtin_amdgcn_cvt_scalef32_pk32_f32_fp6(c, scale);
+#pragma unroll
+        for (int i = 0; i < 32; ++i) r[i] -= q[i];
+#pragma unroll
+        for (int w = 0; w < 6; ++w) code[p][w] = (uint32_t)c[w];
+        sc[p] = (uint32_t)(s + 127);
+    }
+}
+
 // One 32-element bf16 block -> FP8 E4M3 hi and lo parts (32 bytes each) and
 // their E8M0 scales (split_e4m3_block).
 __device__ __forceinline__ void split_bf16_block(const uint16_t *src, uint8_t *hi, uint8_t *lo,

@@ -43,10 +43,6 @@ namespace moe {
 constexpr int kDecodeLdsBytes = MOE_DEC_LDS;
 constexpr int kG1StreamU = MOE_G1SU;
 constexpr int kMxWaves = MOE_MX_WAVES;
-#ifndef MOE_MX_WIDE
-#define MOE_MX_WIDE 1  // 128 x 512 tiles where the weight-tile count is even
-#endif
-constexpr bool kUseWide = MOE_MX_WIDE;
 constexpr int kUnroll = 4;  // chunks per weight batch of the decode kernels
 
 __device__ __forceinline__ floatx4_t mfma_chunk(const uint4 *a, uint4 b, float scale, floatx4_t acc)
@@ -231,10 +227,12 @@ __global__ __launch_bounds__(256) void gemm1_decode_kernel(
 // down: a workgroup owns 64 output columns, one 16-column block per wave,
 // each wave runs all of K.  The tile's h rows (contiguous in the grouped
 // order) are copied to LDS when they fit.  Epilogue: bf16 o and the sum of
-// o^2 over the workgroup's 64 columns.
+// o^2 over the workgroup's 64 columns, both stored in slot order (grouped
+// row r goes to slot perm[r]), so the combine step finds a token's k rows at
+// slots t*k .. t*k+k-1 without a lookup.
 template <int U>
 __global__ __launch_bounds__(256) void gemm2_decode_kernel(
-    const uint16_t *__restrict__ h, const Tile *__restrict__ tiles,
+    const uint16_t *__restrict__ h, const int32_t *__restrict__ perm, const Tile *__restrict__ tiles,
     const int32_t *__restrict__ ntiles, const uint8_t *__restrict__ wpk,
     const uint8_t *__restrict__ sc, uint16_t *__restrict__ o, float *__restrict__ ssq, int d,
     int F, int wgs_per_tile, int rows_fit)
@@ -263,6 +261,12 @@ __global__ __launch_bounds__(256) void gemm2_decode_kernel(
             }
     };
     load_b(0);
+    // destination slots of the lane's 4 output rows and of the row whose
+    // o^2 sum this thread stores; in flight with the weights
+    int dst[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) dst[r] = g * 4 + r < tl.nrows ? perm[tl.row0 + g * 4 + r] : 0;
+    const int dst_ss = (int)threadIdx.x < tl.nrows && threadIdx.x < 16 ? perm[tl.row0 + threadIdx.x] : 0;
     if (use_lds) {
         const uint4 *src = reinterpret_cast<const uint4 *>(h + (int64_t)tl.row0 * F);
         for (int q = threadIdx.x; q < tl.nrows * rowq; q += 256) arows[q] = src[q];
@@ -295,7 +299,7 @@ __global__ __launch_bounds__(256) void gemm2_decode_kernel(
     for (int r = 0; r < 4; ++r) {
         const float val = acc[r];
         const int row = g * 4 + r;
-        if (row < tl.nrows) o[(int64_t)(tl.row0 + row) * d + col0 + n] = f32_to_bf16(val);
+        if (row < tl.nrows) o[(int64_t)dst[r] * d + col0 + n] = f32_to_bf16(val);
         const float ss = sum16(val * val);
         if (n == 0) wsum[wv][g * 4 + r] = ss;
     }
@@ -303,7 +307,7 @@ __global__ __launch_bounds__(256) void gemm2_decode_kernel(
     if (threadIdx.x < 16 && (int)threadIdx.x < tl.nrows) {
         const int row = threadIdx.x;
         const float t = (wsum[0][row] + wsum[1][row]) + (wsum[2][row] + wsum[3][row]);
-        ssq[(int64_t)(tl.row0 + row) * P + (int)(blockIdx.x % wgs_per_tile)] = t;
+        ssq[(int64_t)dst_ss * P + (int)(blockIdx.x % wgs_per_tile)] = t;
     }
 }
 
@@ -339,6 +343,7 @@ typedef int v8i_t __attribute__((__vector_size__(8 * sizeof(int))));
 struct MxArgs {
     const uint8_t *ahi, *alo;     // activation parts [rows][K] (FP8)
     const uint8_t *ashi, *aslo;   // their E8M0 scales [rows][K/32]
+    const uint8_t *a6;            // or three-part FP6 records [rows][K/128] (wide kernel)
     const int32_t *perm;
     const Tile *tiles;
     const int32_t *ntiles;
@@ -348,6 +353,19 @@ struct MxArgs {
     float *ssq;
     int d, F, k, ntn;
 };
+
+// FP6 E2M3 A (24 bytes/lane: the 32 values of activation block g of the
+// chunk, 6 bits each, in K order; probed on the hardware) x FP4 B.  With
+// both operands narrower than 8 bits the instruction issues at twice the
+// FP8 rate.
+__device__ __forceinline__ floatx4_t mfma_mx6(const uint2 &a0, const uint2 &a1, const uint2 &a2,
+                                              const uint4 &b, uint32_t sa, uint32_t sb, floatx4_t c)
+{
+    const v8i_t av = {(int)a0.x, (int)a0.y, (int)a1.x, (int)a1.y, (int)a2.x, (int)a2.y, 0, 0};
+    const v8i_t bv = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
+    // format codes: 2 = FP6 E2M3 (A), 4 = FP4 E2M1 (B)
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 2, 4, 0, (int)sa, 0, (int)sb);
+}
 
 __device__ __forceinline__ floatx4_t mfma_mx(const uint4 &a0, const uint4 &a1, const uint4 &b,
                                              uint32_t sa, uint32_t sb, floatx4_t c)
@@ -536,22 +554,24 @@ __global__ __launch_bounds__(64 * NW) void gemm_mx_kernel(const MxArgs pa)
 
 // =========================================================================
 // Wide MX tiled kernel (prefill): 128 grouped rows x 512 weight rows (two
-// packed weight tiles) per workgroup, all of K.  The per-CU vector-memory
-// return path, not the MFMA rate, bounds the 256-wide kernel above (about
-// 50 KB per K chunk for 128x256 outputs); two weight tiles per activation
-// tile cut that to 67 KB for twice the outputs.  Two-stage LDS ring (67 KB a
-// stage) filled by direct-to-LDS loads: chunk kc+1 is in flight while chunk
-// kc is multiplied.  8 waves as 2 (rows) x 4 (columns): each wave owns 64 rows
-// x 128 columns (4 x 8 blocks of 16x16, two scaled MX MFMAs per block per
-// chunk).  Used when the matrix has an even number of 256-row weight tiles.
+// packed weight tiles) per workgroup, all of K.  The activations arrive as
+// three FP6 E2M3 parts per value (split_e2m3x3_block), so each 16x16x128
+// block takes three scaled MFMAs that issue at twice the FP8 rate: 3/4 of
+// the matrix-core time of two FP8 parts, for 304 instead of 264 activation
+// bytes per row and chunk.  Two-stage LDS ring (72 KB a stage) filled by
+// direct-to-LDS loads: chunk kc+1 is in flight while chunk kc is multiplied.
+// A row's 304-byte record is copied whole; 304 = 76 dwords puts the 16 rows
+// of a row block on distinct LDS banks.  8 waves as 2 (rows) x 4 (columns):
+// each wave owns 64 rows x 128 columns (4 x 8 blocks of 16x16).  Used when
+// the matrix has an even number of 256-row weight tiles.
 // =========================================================================
 template <bool GATE_UP>
 __global__ __launch_bounds__(512) void gemm_mxw_kernel(const MxArgs pa)
 {
-    constexpr int NW = 8, MB = 4, AL = 2;
-    __shared__ uint4 Ah0[kTM * 8], Ah1[kTM * 8];
-    __shared__ uint4 Al0[kTM * 8], Al1[kTM * 8];
-    __shared__ uint32_t Ac0[kTM * 2], Ac1[kTM * 2];
+    constexpr int NW = 8, MB = 4;
+    constexpr int AU = kTM * kA6Units;             // 16-byte units of a stage's records
+    constexpr int AL = (AU + 64 * NW - 1) / (64 * NW);  // record loads per wave (5)
+    __shared__ uint4 As0[AU], As1[AU];
     __shared__ uint4 Bs0[2 * kTN * 4], Bs1[2 * kTN * 4];
     __shared__ uint32_t Ss0[2 * kTN], Ss1[2 * kTN];
 
@@ -572,25 +592,20 @@ __global__ __launch_bounds__(512) void gemm_mxw_kernel(const MxArgs pa)
     };
 
     // ---- load assignment ----------------------------------------------------
-    // A parts: load i of this wave fills rows 8*(8i + wv) + lane/8, stored slot
-    // lane%8.  Rows past nrows are not loaded (their LDS rows hold stale data;
-    // they only feed output rows that are never stored).  Every wait below is
-    // vmcnt(0), so loads skipped this way cannot upset a count.
-    const uint8_t *ahsrc[AL], *alsrc[AL];
+    // Records: load i of this wave fills stage unit P = 64*(8i + wv) + lane,
+    // unit P % 19 of row P / 19.  Rows past nrows are not loaded (their LDS
+    // rows hold stale data; they only feed output rows that are never
+    // stored).  Every wait below is vmcnt(0), so loads skipped this way
+    // cannot upset a count.
+    const uint8_t *asrc[AL];
     bool aload[AL];
 #pragma unroll
     for (int i = 0; i < AL; ++i) {
-        const int rw = 8 * (NW * i + wv) + (lane >> 3);
-        const int slot = (lane & 7) ^ (rw & 7);
-        const int64_t off = src_row(rw) * K + slot * 16;
-        ahsrc[i] = pa.ahi + off;
-        alsrc[i] = pa.alo + off;
-        aload[i] = rw < tl.nrows;
+        const int P = 64 * (NW * i + wv) + lane;
+        const int rw = P / kA6Units, u = P - rw * kA6Units;
+        aload[i] = P < AU && rw < tl.nrows;
+        asrc[i] = pa.a6 + (src_row(aload[i] ? rw : 0) * nk) * kA6Bytes + u * 16;
     }
-    // A scale dword q = 32*wv + lane (lanes < 32): row q/2, hi or lo part by q%2
-    const int qa = 32 * wv + (lane & 31);
-    const uint8_t *acsrc = ((lane & 1) ? pa.aslo : pa.ashi) + src_row(qa >> 1) * (K / 32);
-    const bool acload = lane < 32 && (qa >> 1) < tl.nrows;
     // weight tiles 2np and 2np+1: load i fills unit 64*(8i + wv) + lane of the
     // 2048 units (tile i/2); scale dword q = 64*wv + lane of the 512 (tile q/256)
     const WView v = GATE_UP ? w1_view(pa.wpk, pa.sc, tl.expert, d, F)
@@ -605,15 +620,11 @@ __global__ __launch_bounds__(512) void gemm_mxw_kernel(const MxArgs pa)
     // The loads of a chunk go out in three parts spread over the multiply of
     // the chunk before (activations first, then the two weight tiles), so a
     // wave is not held at the address unit while its MFMAs could be issuing.
-    auto issue_part = [&](int part, int kc, uint4 *Ah, uint4 *Al, uint32_t *Ac, uint4 *Bs, uint32_t *Ss) {
+    auto issue_part = [&](int part, int kc, uint4 *As, uint4 *Bs, uint32_t *Ss) {
         if (part == 0) {
 #pragma unroll
             for (int i = 0; i < AL; ++i)
-                if (aload[i]) dma16(ahsrc[i] + kc * kKStep, lds_off(Ah + (NW * i + wvu) * 64));
-#pragma unroll
-            for (int i = 0; i < AL; ++i)
-                if (aload[i]) dma16(alsrc[i] + kc * kKStep, lds_off(Al + (NW * i + wvu) * 64));
-            if (acload) dma4(acsrc + kc * 4, lds_off(Ac + 32 * wvu));
+                if (aload[i]) dma16(asrc[i] + kc * kA6Bytes, lds_off(As + (NW * i + wvu) * 64));
         } else if (part == 1) {
             const int64_t bo = (int64_t)kc * kWTileBytes;
             dma16(bsrc0 + bo, lds_off(Bs + (0 + wvu) * 64));
@@ -640,28 +651,36 @@ __global__ __launch_bounds__(512) void gemm_mxw_kernel(const MxArgs pa)
 #pragma unroll
         for (int nb = 0; nb < 8; ++nb) acc[mb][nb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
-    // multiply the chunk in (Ah, Al, Ac, Bs, Ss); when kn >= 0 the parts of
-    // chunk kn's loads (into the other slot) are issued along the way
-    auto compute = [&](const uint4 *Ah, const uint4 *Al, const uint32_t *Ac, const uint4 *Bs,
-                       const uint32_t *Ss, int kn, uint4 *Ahn, uint4 *Aln, uint32_t *Acn, uint4 *Bn,
-                       uint32_t *Sn) {
-        if (kn >= 0) issue_part(0, kn, Ahn, Aln, Acn, Bn, Sn);
+    // multiply the chunk in (As, Bs, Ss); when kn >= 0 the parts of chunk
+    // kn's loads (into the other slot) are issued along the way
+    auto compute = [&](const uint4 *As, const uint4 *Bs, const uint32_t *Ss, int kn, uint4 *Asn,
+                       uint4 *Bn, uint32_t *Sn) {
+        if (kn >= 0) issue_part(0, kn, Asn, Bn, Sn);
         // LDS reads return in order: row block 0's A fragments first, then the
-        // weight fragments, so the first MFMAs wait for two reads, not ten
+        // weight fragments, so the first MFMAs wait for few reads
         struct AFr {
-            uint4 h0, h1, l0, l1;
-            uint32_t sh, sl;
+            uint2 p[3][3];  // part, 8-byte piece
+            uint32_t s[3];
         };
+        // A pieces are single 8-byte reads: the compiler barrier between them
+        // keeps it from pairing them into ds_read2_b64, which runs at a
+        // quarter of the LDS read rate here (ds_read_b64 at the 304-byte row
+        // stride is conflict-free, measured)
         auto read_a = [&](int mb) {
             AFr f;
             const int row = wm * 64 + mb * 16 + n16;
-            const int sw = row & 7;
-            f.h0 = Ah[row * 8 + (g ^ sw)];
-            f.h1 = Ah[row * 8 + ((4 + g) ^ sw)];
-            f.l0 = Al[row * 8 + (g ^ sw)];
-            f.l1 = Al[row * 8 + ((4 + g) ^ sw)];
-            f.sh = (Ac[row * 2] >> (8 * g)) & 0xFFu;
-            f.sl = (Ac[row * 2 + 1] >> (8 * g)) & 0xFFu;
+            const uint2 *rp = reinterpret_cast<const uint2 *>(As + row * kA6Units);
+#pragma unroll
+            for (int p = 0; p < 3; ++p)
+#pragma unroll
+                for (int j = 0; j < 3; ++j) {
+                    f.p[p][j] = rp[12 * p + 3 * g + j];
+                    asm volatile("" ::: "memory");
+                }
+            const uint4 sv = As[row * kA6Units + 18];
+            f.s[0] = (sv.x >> (8 * g)) & 0xFFu;
+            f.s[1] = (sv.y >> (8 * g)) & 0xFFu;
+            f.s[2] = (sv.z >> (8 * g)) & 0xFFu;
             return f;
         };
         uint4 bw[8];
@@ -670,6 +689,9 @@ __global__ __launch_bounds__(512) void gemm_mxw_kernel(const MxArgs pa)
             const int rho = wn * 128 + nb * 16 + n16;  // row of the 512; bank swizzle of its tile row
             bw[nb] = Bs[rho * 4 + (g ^ bswz(rho))];
             bsc[nb] = (Ss[rho] >> (8 * g)) & 0xFFu;
+        };
+        auto mma = [&](int mb, const AFr &f, int p, int nb) {
+            acc[mb][nb] = mfma_mx6(f.p[p][0], f.p[p][1], f.p[p][2], bw[nb], f.s[p], bsc[nb], acc[mb][nb]);
         };
         // row block 0: each weight fragment is read two MFMAs before its use
         {
@@ -680,15 +702,17 @@ __global__ __launch_bounds__(512) void gemm_mxw_kernel(const MxArgs pa)
             for (int nb = 0; nb < 8; ++nb) {
                 __builtin_amdgcn_sched_barrier(0);
                 if (nb + 2 < 8) read_b(nb + 2);
-                if (mb_act > 0) acc[0][nb] = mfma_mx(f.h0, f.h1, bw[nb], f.sh, bsc[nb], acc[0][nb]);
+                if (mb_act > 0) mma(0, f, 0, nb);
             }
             __builtin_amdgcn_sched_barrier(0);
             if (mb_act > 0) {
 #pragma unroll
-                for (int nb = 0; nb < 8; ++nb) acc[0][nb] = mfma_mx(f.l0, f.l1, bw[nb], f.sl, bsc[nb], acc[0][nb]);
+                for (int p = 1; p < 3; ++p)
+#pragma unroll
+                    for (int nb = 0; nb < 8; ++nb) mma(0, f, p, nb);
             }
             __builtin_amdgcn_sched_barrier(0);
-            if (kn >= 0) issue_part(1, kn, Ahn, Aln, Acn, Bn, Sn);
+            if (kn >= 0) issue_part(1, kn, Asn, Bn, Sn);
         }
 #pragma unroll
         for (int mb = 1; mb < MB; ++mb) {
@@ -697,25 +721,25 @@ __global__ __launch_bounds__(512) void gemm_mxw_kernel(const MxArgs pa)
             if (mb < mb_act) {
                 const AFr f = read_a(mb);
 #pragma unroll
-                for (int nb = 0; nb < 8; ++nb) acc[mb][nb] = mfma_mx(f.h0, f.h1, bw[nb], f.sh, bsc[nb], acc[mb][nb]);
+                for (int p = 0; p < 3; ++p)
 #pragma unroll
-                for (int nb = 0; nb < 8; ++nb) acc[mb][nb] = mfma_mx(f.l0, f.l1, bw[nb], f.sl, bsc[nb], acc[mb][nb]);
+                    for (int nb = 0; nb < 8; ++nb) mma(mb, f, p, nb);
             }
             __builtin_amdgcn_sched_barrier(0);
-            if (mb < 2 && kn >= 0) issue_part(mb + 1, kn, Ahn, Aln, Acn, Bn, Sn);
+            if (mb < 2 && kn >= 0) issue_part(mb + 1, kn, Asn, Bn, Sn);
         }
     };
 
     // ---- pipeline: two slots; the barrier before chunk kc also waits for this
     // wave's LDS reads of chunk kc-1, whose slot chunk kc+1 then refills, and
     // for all of this wave's loads of chunk kc ----------------------------------
-    for (int part = 0; part < 3; ++part) issue_part(part, 0, Ah0, Al0, Ac0, Bs0, Ss0);
+    for (int part = 0; part < 3; ++part) issue_part(part, 0, As0, Bs0, Ss0);
     for (int kc = 0; kc < nk; kc += 2) {
         phase_sync<0>();
-        compute(Ah0, Al0, Ac0, Bs0, Ss0, kc + 1 < nk ? kc + 1 : -1, Ah1, Al1, Ac1, Bs1, Ss1);
+        compute(As0, Bs0, Ss0, kc + 1 < nk ? kc + 1 : -1, As1, Bs1, Ss1);
         if (kc + 1 < nk) {
             phase_sync<0>();
-            compute(Ah1, Al1, Ac1, Bs1, Ss1, kc + 2 < nk ? kc + 2 : -1, Ah0, Al0, Ac0, Bs0, Ss0);
+            compute(As1, Bs1, Ss1, kc + 2 < nk ? kc + 2 : -1, As0, Bs0, Ss0);
         }
     }
 
@@ -789,8 +813,50 @@ static hipError_t launch_split(const uint16_t *src, int64_t rows, int K, uint8_t
     return hipGetLastError();
 }
 
+// bf16 rows -> three-part FP6 records (one thread per 32-block; the four
+// blocks of a chunk are neighbouring threads writing one record).
+__global__ __launch_bounds__(256) void split6_rows_kernel(const uint16_t *__restrict__ src,
+                                                          int64_t nblk, uint8_t *__restrict__ dst)
+{
+    const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (b >= nblk) return;
+    const uint4 *p = reinterpret_cast<const uint4 *>(src + b * 32);
+    float v[32];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint4 w = p[q];
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[8 * q + 2 * i] = __uint_as_float(ws[i] << 16);
+            v[8 * q + 2 * i + 1] = __uint_as_float(ws[i] & 0xFFFF0000u);
+        }
+    }
+    uint32_t code[3][6], sc[3];
+    split_e2m3x3_block(v, code, sc);
+    uint8_t *rec = dst + (b >> 2) * kA6Bytes;
+    const int g = (int)(b & 3);
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+        uint2 *o = reinterpret_cast<uint2 *>(rec + 96 * q + 24 * g);
+        o[0] = make_uint2(code[q][0], code[q][1]);
+        o[1] = make_uint2(code[q][2], code[q][3]);
+        o[2] = make_uint2(code[q][4], code[q][5]);
+        rec[288 + 4 * q + g] = (uint8_t)sc[q];
+    }
+    if (g == 0) *reinterpret_cast<uint32_t *>(rec + 300) = 0u;
+}
+
+static hipError_t launch_split6(const uint16_t *src, int64_t rows, int K, uint8_t *dst, hipStream_t st)
+{
+    const int64_t nblk = rows * (K / 32);
+    split6_rows_kernel<<<(unsigned)((nblk + 255) / 256), 256, 0, st>>>(src, nblk, dst);
+    return hipGetLastError();
+}
+
 hipError_t launch_split_x(const Shape &s, const Workspace &ws, const uint16_t *x, hipStream_t st)
 {
+    if (wide_gate_up(s)) return launch_split6(x, s.T, s.d, ws.xa6, st);
     return launch_split(x, s.T, s.d, ws.xhi, ws.xlo, ws.xshi, ws.xslo, st);
 }
 
@@ -987,10 +1053,11 @@ hipError_t launch_gemm1(const Shape &s, const Plan &p, const Workspace &ws, cons
                         hipEvent_t ev1)
 {
     if (p.tiled) {
-        // x was split into FP8 parts in the router stage (launch_split_x)
-        MxArgs pa{ws.xhi, ws.xlo, ws.xshi, ws.xslo, ws.perm, ws.tiles, ws.ntiles, wpk, sc,
+        // x was split in the router stage (launch_split_x): FP6 records for
+        // the wide kernel, FP8 parts otherwise
+        MxArgs pa{ws.xhi, ws.xlo, ws.xshi, ws.xslo, ws.xa6, ws.perm, ws.tiles, ws.ntiles, wpk, sc,
                   ws.h, nullptr, s.d, s.F, s.k, s.F / 128};
-        if (kUseWide && pa.ntn % 2 == 0) {
+        if (wide_gate_up(s)) {
             pa.ntn /= 2;  // pairs of weight tiles
             const int64_t grid = 8 * ((max_tiles(s, p.tile_rows) * pa.ntn + 7) / 8);
             hipExtLaunchKernelGGL(gemm_mxw_kernel<true>, dim3((unsigned)grid), dim3(512), 0, st, ev0,
@@ -1031,11 +1098,12 @@ hipError_t launch_gemm2(const Shape &s, const Plan &p, const Workspace &ws, cons
                         const uint8_t *sc, hipStream_t st)
 {
     if (p.tiled) {
-        hipError_t e = launch_split(ws.h, s.S(), s.F, ws.hhi, ws.hlo, ws.hshi, ws.hslo, st);
+        hipError_t e = wide_down(s) ? launch_split6(ws.h, s.S(), s.F, ws.ha6, st)
+                                    : launch_split(ws.h, s.S(), s.F, ws.hhi, ws.hlo, ws.hshi, ws.hslo, st);
         if (e != hipSuccess) return e;
-        MxArgs pa{ws.hhi, ws.hlo, ws.hshi, ws.hslo, nullptr, ws.tiles, ws.ntiles, wpk, sc,
+        MxArgs pa{ws.hhi, ws.hlo, ws.hshi, ws.hslo, ws.ha6, nullptr, ws.tiles, ws.ntiles, wpk, sc,
                   ws.o, ws.ssq, s.d, s.F, s.k, s.d / 256};
-        if (kUseWide && pa.ntn % 2 == 0) {
+        if (wide_down(s)) {
             pa.ntn /= 2;
             const int64_t grid = 8 * ((max_tiles(s, p.tile_rows) * pa.ntn + 7) / 8);
             gemm_mxw_kernel<false><<<(unsigned)grid, 512, 0, st>>>(pa);
@@ -1051,7 +1119,7 @@ hipError_t launch_gemm2(const Shape &s, const Plan &p, const Workspace &ws, cons
         if (rows_fit > 16) rows_fit = 16;
         const size_t lds = (size_t)rows_fit * s.F * 2;
         gemm2_decode_kernel<kUnroll><<<(unsigned)grid, 256, lds, st>>>(
-            ws.h, ws.tiles, ws.ntiles, wpk, sc, ws.o, ws.ssq, s.d, s.F, wgs, rows_fit);
+            ws.h, ws.perm, ws.tiles, ws.ntiles, wpk, sc, ws.o, ws.ssq, s.d, s.F, wgs, rows_fit);
     }
     return hipGetLastError();
 }

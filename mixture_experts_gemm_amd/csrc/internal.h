@@ -80,6 +80,23 @@ inline int router_splits(const Shape &s)
     return ks;
 }
 
+// Activation rows for the wide tiled kernels: three FP6 E2M3 parts with E8M0
+// scales per 32-block (split_e2m3x3_block), stored per row and 128-wide K
+// chunk as one 304-byte record: part p at bytes 96p .. 96p+95 (K values in
+// order, 6 bits each, little-endian), the 12 scale bytes at 288 (part p's
+// scales of blocks 0..3 at 288 + 4p), 4 zero bytes.  Records of a row follow
+// each other: row r, chunk c at (r * K/128 + c) * 304.
+constexpr int kA6Bytes = 304;
+constexpr int kA6Units = kA6Bytes / 16;
+
+#ifndef MOE_MX_WIDE
+#define MOE_MX_WIDE 1  // 128 x 512 tiles where the weight-tile count is even
+#endif
+constexpr bool kUseWide = MOE_MX_WIDE;
+// The wide kernel runs a matrix with an even number of 256-row weight tiles.
+inline bool wide_gate_up(const Shape &s) { return kUseWide && (s.F / 128) % 2 == 0; }
+inline bool wide_down(const Shape &s) { return kUseWide && (s.d / 256) % 2 == 0; }
+
 // Upper bound of the tile count for tiles of tile_rows rows (1: any plan).
 inline int64_t max_tiles(const Shape &s, int tile_rows)
 {
@@ -105,11 +122,14 @@ struct Workspace {
     uint16_t *h;          // bf16 [S][F]
     uint16_t *o;          // bf16 [S][d]
     float *ssq;           // [S][d / 64]
-    // FP8 E4M3 hi/lo parts of x and h with E8M0 scales per 32-block
+    // FP8 E4M3 hi/lo parts of x and h with E8M0 scales per 32-block, or
+    // (same memory) their three-part FP6 records for the wide kernels
     uint8_t *xhi, *xlo;   // [T][d]
     uint8_t *xshi, *xslo; // [T][d/32]
     uint8_t *hhi, *hlo;   // [S][F]
     uint8_t *hshi, *hslo; // [S][F/32]
+    uint8_t *xa6;         // [T][d/128] records of kA6Bytes
+    uint8_t *ha6;         // [S][F/128] records of kA6Bytes
     size_t bytes;
 };
 
@@ -119,7 +139,8 @@ Workspace carve_workspace(const Shape &s, void *base);
 // ---- launchers (all asynchronous on `st`) ---------------------------------
 hipError_t launch_router(const Shape &s, const Plan &p, const Workspace &ws, const uint16_t *x,
                          const float *wr, hipStream_t st);
-// bf16 x -> FP8 hi/lo parts + E8M0 scales in the workspace (tiled plans).
+// bf16 x -> its split for the tiled gate/up kernel: FP6 records when that
+// kernel is the wide one, else FP8 hi/lo parts + E8M0 scales.
 hipError_t launch_split_x(const Shape &s, const Workspace &ws, const uint16_t *x, hipStream_t st);
 hipError_t launch_topk(const Shape &s, const Plan &p, const Workspace &ws, hipStream_t st);
 hipError_t launch_group(const Shape &s, const Plan &p, const Workspace &ws, hipStream_t st);

@@ -201,8 +201,9 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t *__rest
 hipError_t launch_router(const Shape &s, const Plan &p, const Workspace &ws, const uint16_t *x,
                          const float *wr, hipStream_t st)
 {
-    // the streaming and tiled gate/up kernels read x as FP8 hi/lo parts, split here
-    uint8_t *xhi = (p.stream || p.tiled) ? ws.xhi : nullptr;
+    // the streaming gate/up kernel reads x as FP8 hi/lo parts, split alongside
+    // the few-token router; the tiled kernels' split follows the router below
+    uint8_t *xhi = p.stream ? ws.xhi : nullptr;
     if (s.T == 1) {
         const int xs = xhi ? (s.d / 32 + 255) / 256 : 0;  // split workgroups per token group
         router_gemv_kernel<1><<<s.E + xs, 256, 0, st>>>(x, wr, ws.scores, s.T, s.d, s.E, xhi, ws.xlo,
@@ -215,12 +216,11 @@ hipError_t launch_router(const Shape &s, const Plan &p, const Workspace &ws, con
         const int ks = router_splits(s);
         dim3 grid((s.T + kRtT - 1) / kRtT, (s.E + kRtE - 1) / kRtE, ks);
         router_gemm_kernel<<<grid, 256, 0, st>>>(x, wr, ws.scores, s.T, s.d, s.E, s.d / ks);
-        // the tiled gate/up kernel reads x as FP8 hi/lo parts, split here
-        if (p.tiled) {
-            hipError_t e = hipGetLastError();
-            if (e != hipSuccess) return e;
-            return launch_split_x(s, ws, x, st);
-        }
+    }
+    if (p.tiled) {
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        return launch_split_x(s, ws, x, st);
     }
     return hipGetLastError();
 }

@@ -77,7 +77,7 @@ def _pack_reference(codes, scales, d, F):
     numpy index arrays, one expert at a time."""
     E = codes.shape[0]
     r = np.arange(256)
-    sw = ((r >> 1) ^ (r >> 3)) & 3
+    sw = (r >> 1) & 3
     out_c = np.empty_like(codes)
     out_s = np.empty_like(scales)
 
