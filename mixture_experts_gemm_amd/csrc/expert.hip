@@ -352,6 +352,7 @@ struct MxArgs {
     uint16_t *out;                // h or o (bf16)
     float *ssq;
     int d, F, k, ntn;
+    uint8_t *h6;                  // gate/up of the wide kernel: h as FP6 records here (else bf16 out)
 };
 
 // FP6 E2M3 A (24 bytes/lane: the 32 values of activation block g of the
@@ -571,9 +572,13 @@ __global__ __launch_bounds__(512) void gemm_mxw_kernel(const MxArgs pa)
     constexpr int NW = 8, MB = 4;
     constexpr int AU = kTM * kA6Units;             // 16-byte units of a stage's records
     constexpr int AL = (AU + 64 * NW - 1) / (64 * NW);  // record loads per wave (5)
-    __shared__ uint4 As0[AU], As1[AU];
-    __shared__ uint4 Bs0[2 * kTN * 4], Bs1[2 * kTN * 4];
-    __shared__ uint32_t Ss0[2 * kTN], Ss1[2 * kTN];
+    constexpr int BU = 2 * kTN * 4, SU = 2 * kTN / 4;   // weight / scale units of a stage
+    // one pool: two stages during the K loop, the fp32 h tile in the epilogue
+    __shared__ uint4 pool[2 * (AU + BU + SU)];
+    uint4 *const As0 = pool, *const As1 = pool + AU;
+    uint4 *const Bs0 = pool + 2 * AU, *const Bs1 = pool + 2 * AU + BU;
+    uint32_t *const Ss0 = reinterpret_cast<uint32_t *>(pool + 2 * AU + 2 * BU);
+    uint32_t *const Ss1 = Ss0 + 2 * kTN;
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int d = pa.d, F = pa.F;
@@ -745,7 +750,57 @@ __global__ __launch_bounds__(512) void gemm_mxw_kernel(const MxArgs pa)
 
     // ---- epilogue: lane holds C[g*4 + r][n16] of every 16x16 block -----------
     const int nt = 2 * np + (wn >> 1), half = wn & 1;  // weight tile, half of its 256 rows
-    if (GATE_UP) {
+    if (GATE_UP && pa.h6) {
+        // h = silu(gate) * up in fp32 goes through LDS (row r, feature f of
+        // the workgroup's 256 at float4 slot (f/4) ^ ((f/32) & 7) of row r, so
+        // the block reads below spread over the banks), then one thread per
+        // 32-feature block splits it into the down kernel's FP6 records: the
+        // workgroup's 256 features are whole chunks 2np and 2np+1 of h.
+        constexpr int HS = 260;  // floats per LDS row
+        float *hs = reinterpret_cast<float *>(pool);
+        __syncthreads();  // every wave is past its last LDS read of the stages
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            if (mb >= mb_act) continue;
+#pragma unroll
+            for (int hb = 0; hb < 4; ++hb) {
+                const int f = wn * 64 + hb * 16 + n16, c = f >> 2;
+                const int pos = ((c ^ ((c >> 3) & 7)) << 2) | (f & 3);
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    const int row = wm * 64 + mb * 16 + g * 4 + rr;
+                    hs[row * HS + pos] = silu(acc[mb][hb][rr]) * acc[mb][hb + 4][rr];
+                }
+            }
+        }
+        __syncthreads();
+        for (int b = tid; b < tl.nrows * 8; b += 64 * NW) {
+            const int row = b >> 3, blk = b & 7;
+            const float4 *src = reinterpret_cast<const float4 *>(hs + row * HS) + blk * 8;
+            float v[32];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const float4 t = src[q ^ blk];
+                v[4 * q] = t.x;
+                v[4 * q + 1] = t.y;
+                v[4 * q + 2] = t.z;
+                v[4 * q + 3] = t.w;
+            }
+            uint32_t code[3][6], sc[3];
+            split_e2m3x3_block(v, code, sc);
+            uint8_t *rec = pa.h6 + ((int64_t)(tl.row0 + row) * (F / kKStep) + 2 * np + (blk >> 2)) * kA6Bytes;
+            const int g4 = blk & 3;
+#pragma unroll
+            for (int q = 0; q < 3; ++q) {
+                uint2 *o = reinterpret_cast<uint2 *>(rec + 96 * q + 24 * g4);
+                o[0] = make_uint2(code[q][0], code[q][1]);
+                o[1] = make_uint2(code[q][2], code[q][3]);
+                o[2] = make_uint2(code[q][4], code[q][5]);
+                rec[288 + 4 * q + g4] = (uint8_t)sc[q];
+            }
+            if (g4 == 0) *reinterpret_cast<uint32_t *>(rec + 300) = 0u;
+        }
+    } else if (GATE_UP) {
         // column block nb < 4: gate features half*64 + 16nb + n16 of N-tile nt; nb + 4: up
         const int fbase = nt * 128 + half * 64;
 #pragma unroll
@@ -1056,8 +1111,10 @@ hipError_t launch_gemm1(const Shape &s, const Plan &p, const Workspace &ws, cons
         // x was split in the router stage (launch_split_x): FP6 records for
         // the wide kernel, FP8 parts otherwise
         MxArgs pa{ws.xhi, ws.xlo, ws.xshi, ws.xslo, ws.xa6, ws.perm, ws.tiles, ws.ntiles, wpk, sc,
-                  ws.h, nullptr, s.d, s.F, s.k, s.F / 128};
+                  ws.h, nullptr, s.d, s.F, s.k, s.F / 128, nullptr};
         if (wide_gate_up(s)) {
+            // h goes straight to the down kernel's FP6 records when that kernel is wide
+            if (wide_down(s)) pa.h6 = ws.ha6;
             pa.ntn /= 2;  // pairs of weight tiles
             const int64_t grid = 8 * ((max_tiles(s, p.tile_rows) * pa.ntn + 7) / 8);
             hipExtLaunchKernelGGL(gemm_mxw_kernel<true>, dim3((unsigned)grid), dim3(512), 0, st, ev0,
@@ -1098,11 +1155,13 @@ hipError_t launch_gemm2(const Shape &s, const Plan &p, const Workspace &ws, cons
                         const uint8_t *sc, hipStream_t st)
 {
     if (p.tiled) {
-        hipError_t e = wide_down(s) ? launch_split6(ws.h, s.S(), s.F, ws.ha6, st)
-                                    : launch_split(ws.h, s.S(), s.F, ws.hhi, ws.hlo, ws.hshi, ws.hslo, st);
+        // h records were written by the wide gate/up kernel; otherwise split h here
+        hipError_t e = hipSuccess;
+        if (!wide_down(s)) e = launch_split(ws.h, s.S(), s.F, ws.hhi, ws.hlo, ws.hshi, ws.hslo, st);
+        else if (!wide_gate_up(s)) e = launch_split6(ws.h, s.S(), s.F, ws.ha6, st);
         if (e != hipSuccess) return e;
         MxArgs pa{ws.hhi, ws.hlo, ws.hshi, ws.hslo, ws.ha6, nullptr, ws.tiles, ws.ntiles, wpk, sc,
-                  ws.o, ws.ssq, s.d, s.F, s.k, s.d / 256};
+                  ws.o, ws.ssq, s.d, s.F, s.k, s.d / 256, nullptr};
         if (wide_down(s)) {
             pa.ntn /= 2;
             const int64_t grid = 8 * ((max_tiles(s, p.tile_rows) * pa.ntn + 7) / 8);

@@ -509,17 +509,20 @@ __global__ __launch_bounds__(256) void group_scan_kernel(
     __shared__ int32_t toff[1024];
     __shared__ int32_t wtot[4];
     // two passes over the masks (counts, then bases); loads go out in batches
-    // of 16 so the walk over the chunks is not a chain of dependent reads
-    constexpr int B = 16;
+    // of 64 (all chunks of a 4096-token call at once), so each pass is one
+    // round trip to memory per batch rather than a chain of dependent reads
+    constexpr int B = 64;
     const int tid = threadIdx.x;
     for (int e = tid; e < E; e += 256) {
         int run = 0;
         for (int c0 = 0; c0 < nchunks; c0 += B) {
             uint64_t mv[B];
+            // unconditional loads (clamped index, value masked after): a
+            // conditional load would end its own basic block with a wait
 #pragma unroll
-            for (int i = 0; i < B; ++i) mv[i] = c0 + i < nchunks ? masks[(int64_t)(c0 + i) * E + e] : 0ull;
+            for (int i = 0; i < B; ++i) mv[i] = masks[(int64_t)min(c0 + i, nchunks - 1) * E + e];
 #pragma unroll
-            for (int i = 0; i < B; ++i) run += __popcll(mv[i]);
+            for (int i = 0; i < B; ++i) run += c0 + i < nchunks ? __popcll(mv[i]) : 0;
         }
         cnt[e] = run;
     }
@@ -531,7 +534,7 @@ __global__ __launch_bounds__(256) void group_scan_kernel(
         for (int c0 = 0; c0 < nchunks; c0 += B) {
             uint64_t mv[B];
 #pragma unroll
-            for (int i = 0; i < B; ++i) mv[i] = c0 + i < nchunks ? masks[(int64_t)(c0 + i) * E + e] : 0ull;
+            for (int i = 0; i < B; ++i) mv[i] = masks[(int64_t)min(c0 + i, nchunks - 1) * E + e];
 #pragma unroll
             for (int i = 0; i < B; ++i)
                 if (c0 + i < nchunks) {
