@@ -27,6 +27,9 @@ routing (section ⑧), 4-bit block-scaled expert weights (section ⑪)):
             expert) pair one row, so k=1 and T = 753 / 3,012 rows (about 24 /
             94 rows per expert); seeds 5 / 6
 
+The latent-width variant's workloads (latent_tiny, latent1/4, latent_prefill)
+are described with LATENT_WORKLOADS below.
+
 Value distributions: x = bf16(N(0,1)); router weights fp32 N(0, 0.02^2);
 expert weight bytes uniform over 0..255 (so both FP4 E2M1 nibbles are
 uniform over the 16 codes, -0 included); E8M0 scale bytes uniform over
@@ -45,7 +48,7 @@ from concurrent.futures import ThreadPoolExecutor
 import numpy as np
 
 # substream tags
-_TAG_X, _TAG_WR, _TAG_W, _TAG_S, _TAG_AB, _TAG_ZIPF, _TAG_REDRAW = range(7)
+_TAG_X, _TAG_WR, _TAG_W, _TAG_S, _TAG_AB, _TAG_ZIPF, _TAG_REDRAW, _TAG_WC, _TAG_WE = range(9)
 
 SCALE_LO, SCALE_HI = 119, 123          # E8M0 bytes: 2^-8 .. 2^-4
 GAP_DEFAULT = 1e-4
@@ -245,3 +248,86 @@ def make_layer(name_or_w, layer: int = 0, T: int | None = None, gap: float = GAP
 
 def custom_workload(T: int, d: int, E: int, k: int, F: int, seed: int, zipf: bool = False) -> Workload:
     return Workload(f"custom_T{T}_d{d}_E{E}_k{k}_F{F}_s{seed}", Shape(T, d, E, k, F), seed, zipf=zipf)
+
+
+# ---------------------------------------------------------------------------
+# Latent-width variant ("Muse Spark Open を段階的に分解する", section ⑨): the
+# token (width D) is narrowed by a shared matrix to the experts' width d,
+# the experts run at d, and a second shared matrix widens their weighted
+# sum back to D.  The page gives D = 8,192, d = 4,096 and 4,096 x 4,096
+# gate / up / down matrices.
+#
+#   latent_tiny     T=64,   D=512,  d=256,  E=8,   k=2, F=256,  seed 7
+#   latent1/4       T=1/4,  D=8192, d=4096, E=256, k=8, F=4096, seed 8
+#   latent_prefill  T=4096, same, seed 9
+#
+# Shared matrices bf16: Wc [d][D] = bf16(N(0, 1/D)), We [D][d] = bf16(N(0, 1/d)),
+# so the narrowed token and the widened sum stay near unit scale.  x, the
+# router and the experts are drawn as for the full-width workloads (the
+# router and the margin precondition at width D, the experts at width d).
+# ---------------------------------------------------------------------------
+
+@dataclasses.dataclass(frozen=True)
+class LatentWorkload:
+    name: str
+    T: int
+    D: int
+    d: int
+    E: int
+    k: int
+    F: int
+    seed: int
+
+    def token_view(self) -> Workload:
+        """The full-width view: token width D (router, tokens, gate vectors)."""
+        return Workload(self.name, Shape(self.T, self.D, self.E, self.k, self.F), self.seed)
+
+    def expert_view(self) -> Workload:
+        """The experts' view: width d (expert weights)."""
+        return Workload(self.name, Shape(self.T, self.d, self.E, self.k, self.F), self.seed)
+
+
+LATENT_WORKLOADS = {
+    "latent_tiny": LatentWorkload("latent_tiny", 64, 512, 256, 8, 2, 256, 7),
+    "latent1": LatentWorkload("latent1", 1, 8192, 4096, 256, 8, 4096, 8),
+    "latent4": LatentWorkload("latent4", 4, 8192, 4096, 256, 8, 4096, 8),
+    "latent_prefill": LatentWorkload("latent_prefill", 4096, 8192, 4096, 256, 8, 4096, 9),
+}
+
+
+@dataclasses.dataclass
+class LatentInputs:
+    w: LatentWorkload
+    x: np.ndarray          # uint16 bf16 bits [T][D]
+    router_w: np.ndarray   # float32 [E][D]
+    wc: np.ndarray         # uint16 bf16 bits [d][D]
+    w_packed: np.ndarray   # uint8 [E][3dF/2] (natural layout, width d)
+    scales: np.ndarray     # uint8 [E][3dF/32]
+    we: np.ndarray         # uint16 bf16 bits [D][d]
+    alpha: np.ndarray      # float32 [D]
+    beta: np.ndarray       # float32 [D]
+    k: int
+    eps: float = 1e-6
+
+
+def make_shared(w: LatentWorkload, layer: int = 0):
+    """The two shared matrices as bf16 bits: Wc [d][D] and We [D][d]."""
+    gc = _rng(w.seed, layer, _TAG_WC, 0)
+    wc = gc.standard_normal((w.d, w.D), dtype=np.float32) * np.float32(1.0 / math.sqrt(w.D))
+    ge = _rng(w.seed, layer, _TAG_WE, 0)
+    we = ge.standard_normal((w.D, w.d), dtype=np.float32) * np.float32(1.0 / math.sqrt(w.d))
+    return f32_to_bf16_bits(wc), f32_to_bf16_bits(we)
+
+
+def make_latent_layer(name_or_w, layer: int = 0, T: int | None = None, gap: float = GAP_DEFAULT,
+                      threads: int = 8) -> LatentInputs:
+    w = LATENT_WORKLOADS[name_or_w] if isinstance(name_or_w, str) else name_or_w
+    if T is not None:
+        w = dataclasses.replace(w, T=T)
+    tv, ev = w.token_view(), w.expert_view()
+    wr = make_router(tv, layer)
+    x = make_tokens(tv, wr, layer, gap=gap)
+    W, S = make_experts(ev, layer, threads=threads)
+    a, b = make_gates(tv, layer)
+    wc, we = make_shared(w, layer)
+    return LatentInputs(w, x, wr, wc, W, S, we, a, b, w.k)

@@ -51,6 +51,9 @@ def lib():
         L.oracle_moe_forward.argtypes = [_I, _I, _I, _I, _I, C.c_double, _P, _P, _P, _P, _P, _P,
                                          _I, _P, _P, _P, _P]
         L.oracle_moe_forward.restype = _I
+        L.oracle_latent_forward.argtypes = [_I, _I, _I, _I, _I, _I, C.c_double, _P, _P, _P, _P, _P,
+                                            _P, _P, _P, _I, _P, _P, _P, _P]
+        L.oracle_latent_forward.restype = _I
         _lib = L
     return _lib
 
@@ -176,4 +179,42 @@ def moe_forward(x_bits, wr, w_packed, scales, alpha, beta, k, eps=1e-6, F=None, 
                                   _p(s), _p(ids), _p(w))
     if rc != 0:
         raise ValueError("oracle_moe_forward: bad arguments")
+    return s, ids, w
+
+
+def latent_forward(x_bits, wr, wc_bits, w_packed, scales, we_bits, alpha, beta, k, eps=1e-6,
+                   tokens=None):
+    """L1-L5 (latent-width variant) on the listed tokens: (s float64 [n][D], ids, w).
+
+    x bf16 bits [T][D]; wr fp32 [E][D]; wc bf16 bits [d][D]; experts packed for
+    width d; we bf16 bits [D][d]; alpha, beta fp32 [D].
+    """
+    x_bits = _c(x_bits, np.uint16)
+    wr = _c(wr, np.float32)
+    wc_bits = _c(wc_bits, np.uint16)
+    we_bits = _c(we_bits, np.uint16)
+    w_packed = _c(w_packed, np.uint8)
+    scales = _c(scales, np.uint8)
+    alpha = _c(alpha, np.float32)
+    beta = _c(beta, np.float32)
+    T, D = x_bits.shape
+    d = wc_bits.shape[0]
+    E = wr.shape[0]
+    assert wc_bits.shape == (d, D) and we_bits.shape == (D, d) and wr.shape == (E, D)
+    F = w_packed.size // E * 2 // (3 * d)
+    assert w_packed.size == E * 3 * d * F // 2 and scales.size == E * 3 * d * F // 32
+    if tokens is None:
+        sel = None
+        n = T
+    else:
+        sel = _c(tokens, np.int32)
+        n = sel.size
+    s = np.empty((n, D), np.float64)
+    ids = np.empty((n, k), np.int32)
+    w = np.empty((n, k), np.float64)
+    rc = lib().oracle_latent_forward(T, D, d, E, F, k, eps, _p(x_bits), _p(wr), _p(wc_bits),
+                                     _p(w_packed), _p(scales), _p(we_bits), _p(alpha), _p(beta),
+                                     n, None if sel is None else _p(sel), _p(s), _p(ids), _p(w))
+    if rc != 0:
+        raise ValueError("oracle_latent_forward: bad arguments")
     return s, ids, w

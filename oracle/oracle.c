@@ -296,3 +296,96 @@ int oracle_moe_forward(int T, int d, int E, int F, int k, double eps,
     free(xs); free(scores); free(ids); free(w); free(n);
     return 0;
 }
+
+/* ---- latent-width variant ----------------------------------------------- */
+
+/*
+ * [MS] section ⑨: the chosen experts do not take the token at its full
+ * width.  A matrix shared by all of them first narrows the token (8,192 to
+ * 4,096 on the page); each chosen expert runs gate / up / down at that
+ * width; the outputs are normalised and summed with the router weights; a
+ * second shared matrix widens the sum back before it joins the residual.
+ *
+ *   L1  routing (O2-O4) on the full-width token x: the router reads the
+ *       token vector itself ([MS] section ⑧ figure).
+ *   L2  z = Wc x, Wc [d][D] bf16.  Reading: the shared matrices are bf16;
+ *       the pages give a 4-bit format for the expert weights only ([MS]
+ *       section ⑪).  Kept in double.
+ *   L3  O6 / O7 for each chosen expert on z, at width d.
+ *   L4  y = sum_j w_j n_j (width d, j in order), then f = We y with
+ *       We [D][d] bf16, in double.
+ *   L5  s = alpha * x + beta * f at width D (O8's gate).
+ *
+ * Arguments as oracle_moe_forward, plus D (token width), wc and we (bf16
+ * bits, row-major).  Expert weights are laid out for width d.
+ */
+int oracle_latent_forward(int T, int D, int d, int E, int F, int k, double eps,
+                          const uint16_t *x, const float *wr, const uint16_t *wc,
+                          const uint8_t *wpk, const uint8_t *sc, const uint16_t *we,
+                          const float *alpha, const float *beta, int n_sel,
+                          const int32_t *sel, double *s_out, int32_t *ids_out, double *w_out)
+{
+    if (T < 0 || D <= 0 || d <= 0 || E <= 0 || F <= 0 || k < 1 || k > E || D % 32 || d % 32 ||
+        F % 32)
+        return -1;
+    if (sel == NULL) n_sel = T;
+    if (n_sel <= 0) return 0;
+    const int64_t eb = (int64_t)3 * d * F / 2, esb = (int64_t)3 * d * F / 32;
+
+    uint16_t *xs = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)n_sel * D);
+    float *scores = (float *)malloc(sizeof(float) * (size_t)n_sel * E);
+    int32_t *ids = (int32_t *)malloc(sizeof(int32_t) * (size_t)n_sel * k);
+    double *w = (double *)malloc(sizeof(double) * (size_t)n_sel * k);
+    double *z = (double *)malloc(sizeof(double) * (size_t)n_sel * d);
+    double *n = (double *)malloc(sizeof(double) * (size_t)n_sel * k * d);
+    double *y = (double *)malloc(sizeof(double) * (size_t)n_sel * d);
+    if (!xs || !scores || !ids || !w || !z || !n || !y) {
+        free(xs); free(scores); free(ids); free(w); free(z); free(n); free(y);
+        return -1;
+    }
+    for (int r = 0; r < n_sel; ++r) {
+        int t = sel ? sel[r] : r;
+        memcpy(xs + (int64_t)r * D, x + (int64_t)t * D, sizeof(uint16_t) * (size_t)D);
+    }
+    /* L1 */
+    oracle_router_scores(n_sel, D, E, xs, wr, scores);
+    oracle_topk_softmax(n_sel, E, k, scores, ids, w);
+
+    /* L2 */
+#pragma omp parallel for schedule(static)
+    for (int64_t q = 0; q < (int64_t)n_sel * d; ++q) {
+        const int64_t r = q / d, j = q % d;
+        double acc = 0.0;
+        for (int i = 0; i < D; ++i)
+            acc += oracle_bf16_to_double(wc[j * D + i]) * oracle_bf16_to_double(xs[r * D + i]);
+        z[q] = acc;
+    }
+
+    /* L3 */
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t q = 0; q < (int64_t)n_sel * k; ++q) {
+        const int64_t r = q / k;
+        const int e = ids[q];
+        oracle_expert(d, F, wpk + (int64_t)e * eb, sc + (int64_t)e * esb, z + r * d, eps, NULL,
+                      n + q * d);
+    }
+
+    /* L4, L5 */
+    for (int64_t r = 0; r < n_sel; ++r)
+        for (int j = 0; j < d; ++j) {
+            double acc = 0.0;
+            for (int s = 0; s < k; ++s) acc += w[r * k + s] * n[(r * k + s) * d + j];
+            y[r * d + j] = acc;
+        }
+#pragma omp parallel for schedule(static)
+    for (int64_t q = 0; q < (int64_t)n_sel * D; ++q) {
+        const int64_t r = q / D, i = q % D;
+        double f = 0.0;
+        for (int j = 0; j < d; ++j) f += oracle_bf16_to_double(we[i * d + j]) * y[r * d + j];
+        s_out[q] = (double)alpha[i] * oracle_bf16_to_double(xs[r * D + i]) + (double)beta[i] * f;
+    }
+    if (ids_out) memcpy(ids_out, ids, sizeof(int32_t) * (size_t)n_sel * k);
+    if (w_out) memcpy(w_out, w, sizeof(double) * (size_t)n_sel * k);
+    free(xs); free(scores); free(ids); free(w); free(z); free(n); free(y);
+    return 0;
+}

@@ -351,3 +351,80 @@ def test_eps_inside_sqrt():
     s_small, _, _ = oracle.moe_forward(L.x, L.router_w, L.w_packed, L.scales, zero, one, L.k, eps=1e-6)
     s_big, _, _ = oracle.moe_forward(L.x, L.router_w, L.w_packed, L.scales, zero, one, L.k, eps=1e12)
     assert np.abs(s_big).max() < 1e-3 * np.abs(s_small).max()
+
+
+# ------------------------------------------------- latent-width variant (L1-L5)
+
+def _latent_experts_view(L):
+    """The experts of a latent layer in the shape _split_expert expects (width d)."""
+    from types import SimpleNamespace
+    return SimpleNamespace(shape=SimpleNamespace(d=L.w.d, F=L.w.F), w_packed=L.w_packed,
+                           scales=L.scales)
+
+
+def test_latent_equals_dense_bruteforce():
+    """torch float64 matmuls for the two shared matrices, every expert on every
+    token (golden-table decode), a routing mask on the full-width scores."""
+    L = synth.make_latent_layer("latent_tiny")
+    w = L.w
+    s, ids, _ = oracle.latent_forward(L.x, L.router_w, L.wc, L.w_packed, L.scales, L.we, L.alpha,
+                                      L.beta, w.k)
+    f64 = lambda b: torch.from_numpy(synth.bf16_bits_to_f32(b).astype(np.float64))
+    X, Wc, We = f64(L.x), f64(L.wc), f64(L.we)
+    scores = (X @ torch.from_numpy(L.router_w.astype(np.float64)).T).to(torch.float32)
+    order = np.argsort(-scores.numpy().astype(np.float64), axis=1, kind="stable")[:, : w.k]
+    wts = torch.softmax(torch.gather(scores.to(torch.float64), 1, torch.from_numpy(order)), dim=1)
+    mask = torch.zeros(w.T, w.E, dtype=torch.float64)
+    mask.scatter_(1, torch.from_numpy(order), wts)
+    Z = X @ Wc.T
+    V = _latent_experts_view(L)
+    Y = torch.zeros(w.T, w.d, dtype=torch.float64)
+    for e in range(w.E):
+        Wg, Wu, Wd = _split_expert(V, e)
+        _, N = _torch_dense_expert(Wg, Wu, Wd, Z, L.eps)
+        Y += mask[:, e:e + 1] * N
+    ref = torch.from_numpy(L.alpha.astype(np.float64)) * X + \
+        torch.from_numpy(L.beta.astype(np.float64)) * (Y @ We.T)
+    np.testing.assert_array_equal(ids, order)
+    err = np.abs(s - ref.numpy()).max() / np.abs(ref.numpy()).max()
+    assert err <= 1e-12, err
+
+
+def test_latent_with_selection_matrices_is_the_full_width_layer():
+    """Wc picks d of the D input channels in a scrambled order, We puts the d
+    sums on d scrambled output channels and the router ignores the other
+    channels: the variant is then the full-width layer (O1-O8) at width d on
+    the picked channels, plus alpha * x on every channel.  A transposed shared
+    matrix or a swapped width moves values to the wrong channels."""
+    L = synth.make_latent_layer("latent_tiny")
+    w = L.w
+    rng = np.random.default_rng(5)
+    pick = rng.permutation(w.D)[: w.d]   # latent j reads input channel pick[j]
+    put = rng.permutation(w.D)[: w.d]    # latent j lands on output channel put[j]
+    one = np.uint16(0x3F80)
+    wc = np.zeros((w.d, w.D), np.uint16)
+    wc[np.arange(w.d), pick] = one
+    we = np.zeros((w.D, w.d), np.uint16)
+    we[put, np.arange(w.d)] = one
+    wr = np.zeros_like(L.router_w)
+    wr[:, pick] = L.router_w[:, pick]
+    s, ids, wt = oracle.latent_forward(L.x, wr, wc, L.w_packed, L.scales, we, L.alpha, L.beta, w.k)
+    y, ids2, wt2 = oracle.moe_forward(np.ascontiguousarray(L.x[:, pick]),
+                                      np.ascontiguousarray(wr[:, pick]), L.w_packed, L.scales,
+                                      np.zeros(w.d, np.float32), np.ones(w.d, np.float32), w.k)
+    np.testing.assert_array_equal(ids, ids2)
+    np.testing.assert_array_equal(wt, wt2)
+    expect = L.alpha.astype(np.float64) * synth.bf16_bits_to_f32(L.x).astype(np.float64)
+    expect[:, put] += L.beta[put].astype(np.float64) * y
+    np.testing.assert_allclose(s, expect, rtol=1e-13, atol=1e-13)
+
+
+def test_latent_token_subset():
+    L = synth.make_latent_layer("latent_tiny")
+    full, ids, _ = oracle.latent_forward(L.x, L.router_w, L.wc, L.w_packed, L.scales, L.we,
+                                         L.alpha, L.beta, L.w.k)
+    sel = np.array([9, 0, 63], np.int32)
+    sub, ids2, _ = oracle.latent_forward(L.x, L.router_w, L.wc, L.w_packed, L.scales, L.we,
+                                         L.alpha, L.beta, L.w.k, tokens=sel)
+    np.testing.assert_array_equal(sub, full[sel])
+    np.testing.assert_array_equal(ids2, ids[sel])
