@@ -34,7 +34,12 @@ WORKLOAD_TEXT = {
              "753 routed rows, k=1, d=8192, F=2048, MXFP4)",
     "ep3012": "One GPU's share under 8-way expert parallelism, 3012-token batch (E=32 local experts, "
               "3012 routed rows, k=1, d=8192, F=2048, MXFP4)",
+    "latent4": "Latent-width variant, 4 concurrent requests (T=4, token width 8192 narrowed to 4096 by a "
+               "shared bf16 matrix, E=256, top-8, 4096x4096 MXFP4 experts, widened back by a second one)",
+    "latent_prefill": "Latent-width variant, prefill micro-batch (T=4096, 8192 -> 4096 -> 8192 shared bf16 "
+                      "matrices, E=256, top-8, 4096x4096 MXFP4 experts)",
 }
+LATENT = ("latent4", "latent_prefill")
 
 
 def log(*a):
@@ -47,7 +52,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="decode4", choices=sorted(WORKLOAD_TEXT))
-    ap.add_argument("--also", default="decode1,prefill,ep753,ep3012",
+    ap.add_argument("--also", default="decode1,prefill,ep753,ep3012,latent4,latent_prefill",
                     help="comma list of extra workloads timed after the main one ('' for none)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
@@ -94,6 +99,46 @@ def make_sets(name, nsets, device):
     return w, host, sets, x
 
 
+def make_latent_sets(name, nsets, device):
+    """Weight sets of the latent-width variant (set 0 from the shared
+    generator, the others' experts drawn on the GPU)."""
+    import numpy as np
+    import torch
+
+    from mixture_experts_gemm_amd import binding as B
+    from mixture_experts_gemm_amd import synth
+
+    w = synth.LATENT_WORKLOADS[name]
+    ev = w.expert_view().shape
+    pool = 256 if w.T < 64 else w.T
+    host = synth.make_latent_layer(w, layer=0, T=pool, threads=16)
+    bf16 = lambda a: torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16)
+    sets = []
+    for i in range(nsets):
+        if i == 0:
+            W = torch.from_numpy(host.w_packed).to(device)
+            S = torch.from_numpy(host.scales).to(device)
+            wr = torch.from_numpy(host.router_w).to(device)
+            a = torch.from_numpy(host.alpha).to(device)
+            b = torch.from_numpy(host.beta).to(device)
+            wc, we = bf16(host.wc), bf16(host.we)
+        else:
+            g = torch.Generator(device=device)
+            g.manual_seed(1000 * w.seed + i)
+            W = torch.randint(0, 256, (ev.E, ev.expert_bytes), dtype=torch.uint8, device=device, generator=g)
+            S = torch.randint(synth.SCALE_LO, synth.SCALE_HI + 1, (ev.E, ev.expert_scale_bytes),
+                              dtype=torch.uint8, device=device, generator=g)
+            wr = torch.from_numpy(synth.make_router(w.token_view(), layer=i)).to(device)
+            a, b = (torch.from_numpy(v).to(device) for v in synth.make_gates(w.token_view(), layer=i))
+            wc, we = (bf16(m) for m in synth.make_shared(w, layer=i))
+        Wp, Sp = B.moe_pack_weights(W, S, w.d, w.F)
+        torch.cuda.synchronize()
+        del W, S
+        sets.append(dict(w=Wp, s=Sp, wr=wr, alpha=a, beta=b, wc=wc, we=we))
+    x = bf16(host.x)
+    return w, host, sets, x
+
+
 # the gate/up kernel each workload runs (the dominant kernel of the layer)
 GATE_UP_KERNEL = {
     "decode1": "gemm1_stream_kernel (gate/up + SwiGLU, persistent, MX MFMA)",
@@ -102,6 +147,8 @@ GATE_UP_KERNEL = {
     "skewed": "gemm_mxw_kernel<true> (gate/up + SwiGLU, 128x512 tiles, MX MFMA)",
     "ep753": "gemm_mxw_kernel<true> (gate/up + SwiGLU, 128x512 tiles, MX MFMA)",
     "ep3012": "gemm_mxw_kernel<true> (gate/up + SwiGLU, 128x512 tiles, MX MFMA)",
+    "latent4": "gemm1_stream_kernel (gate/up + SwiGLU, persistent, MX MFMA)",
+    "latent_prefill": "gemm_mxw_kernel<true> (gate/up + SwiGLU, 128x512 tiles, MX MFMA)",
 }
 
 
@@ -119,22 +166,39 @@ def time_workload(name, steps, warmup, device):
     from mixture_experts_gemm_amd import binding as B
     from mixture_experts_gemm_amd import roofline as R
 
-    decode = name.startswith("decode")
+    latent = name in LATENT
+    decode = name.startswith("decode") or name == "latent4"
     nsets = 4 if decode else 1
     log(f"generating {name}: {nsets} weight set(s)")
-    w, host, sets, xpool = make_sets(name, nsets, device)
-    s = w.shape
+    if latent:
+        # the experts' view (width d) drives the expert accounting below; the
+        # token width D enters through the shared matrices and the router
+        w, host, sets, xpool = make_latent_sets(name, nsets, device)
+        s = w.expert_view().shape
+        D = w.D
+    else:
+        w, host, sets, xpool = make_sets(name, nsets, device)
+        s = w.shape
+        D = s.d
     T = s.T
     npool = xpool.shape[0] // T
-    ws = B.workspace_for(T, s.d, s.E, s.F, s.k, device=device)
-    out = torch.empty(T, s.d, dtype=torch.bfloat16, device=device)
+    if latent:
+        nws = B.moe_latent_workspace_size(T, D, s.d, s.E, s.F, s.k)
+        ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=device)
+    else:
+        ws = B.workspace_for(T, s.d, s.E, s.F, s.k, device=device)
+    out = torch.empty(T, D, dtype=torch.bfloat16, device=device)
     offsets = torch.empty(s.E + 1, dtype=torch.int32, device=device)
 
     def call(i, debug=None):
         st = sets[i % nsets]
         xb = xpool[(i % npool) * T:(i % npool + 1) * T]
-        B.moe_layer_forward(xb, st["wr"], st["w"], st["s"], st["alpha"], st["beta"], s.k, F=s.F,
-                            s_out=out, workspace=ws, debug=debug)
+        if latent:
+            B.moe_latent_forward(xb, st["wr"], st["wc"], st["w"], st["s"], st["we"], st["alpha"],
+                                 st["beta"], s.k, F=s.F, s_out=out, workspace=ws, debug=debug)
+        else:
+            B.moe_layer_forward(xb, st["wr"], st["w"], st["s"], st["alpha"], st["beta"], s.k, F=s.F,
+                                s_out=out, workspace=ws, debug=debug)
 
     # accounting pass (untimed): distinct experts per step, from the library's own grouping
     U = []
@@ -192,9 +256,14 @@ def time_workload(name, steps, warmup, device):
                                kernel=GATE_UP_KERNEL[name],
                                algorithmic_flops_per_launch=flops)
     # the whole layer against both peaks (algorithmic bytes with the realized U)
-    lb = sum(R.layer_bytes(T, s.d, s.E, s.F, u) for u in U) / len(U)
+    if latent:
+        lb = sum(R.latent_layer_bytes(T, D, s.d, s.E, s.F, u) for u in U) / len(U)
+        lf = R.latent_layer_flops(T, D, s.d, s.k, s.F)
+    else:
+        lb = sum(R.layer_bytes(T, s.d, s.E, s.F, u) for u in U) / len(U)
+        lf = R.layer_flops(T, s.d, s.k, s.F)
     res["layer_hbm_frac"] = lb / (elapsed / steps) / R.MI355X_HBM_BYTES_PER_S
-    res["layer_mfma_frac"] = R.layer_flops(T, s.d, s.k, s.F) / (elapsed / steps) / R.MI355X_BF16_FLOPS_PER_S
+    res["layer_mfma_frac"] = lf / (elapsed / steps) / R.MI355X_BF16_FLOPS_PER_S
     log(json.dumps(res))
     return res, host, T
 
@@ -244,7 +313,7 @@ def main():
     main_res, host, T = time_workload(args.workload, steps, warmup, device)
     also = {}
     for extra in [e for e in args.also.split(",") if e and e != args.workload]:
-        d2 = extra.startswith("decode")
+        d2 = extra.startswith("decode") or extra == "latent4"
         r, _, _ = time_workload(extra, 200 if d2 else 10, 10 if d2 else 2, device)
         also[extra] = r
         torch.cuda.empty_cache()

@@ -27,8 +27,9 @@
  *
  * All pointers passed to moe_layer_forward are DEVICE pointers on the
  * current HIP device unless stated otherwise; the caller allocates and owns
- * them, including the workspace.  The library allocates no device memory,
- * keeps no pointer after returning, and queues all work asynchronously on
+ * them, including the workspace.  The library allocates no device memory
+ * (except moe_latent_forward's rocBLAS handle, see there), keeps no pointer
+ * after returning, and queues all work asynchronously on
  * `stream` (a hipStream_t; NULL = the null stream).  Buffers must stay valid
  * until that work completes.  Calls on distinct workspaces are independent.
  *
@@ -187,6 +188,63 @@ int moe_layer_forward(const moe_dims_t *dims, const void *x, const float *router
  */
 int moe_dequant_mxfp4(const uint8_t *codes, const uint8_t *scales, int64_t rows, int32_t K,
                       void *out_bf16, void *stream);
+
+/*
+ * Latent-width variant ("Muse Spark Open を段階的に分解する", section ⑨: the
+ * chosen experts do not take the token at its full width; a matrix shared by
+ * them narrows it first (8,192 -> 4,096 on the page), each chosen expert
+ * runs gate / up / down at that width, and the normalised, router-weighted
+ * sum is widened back by a second shared matrix before the gated residual):
+ *
+ *   1-3. routing and grouping as moe_layer_forward, on the full-width x;
+ *   N.   z = x W_narrow^T (bf16 out, fp32 accumulation);
+ *   4-5. the experts of moe_layer_forward on z, at width d;
+ *   W.   y = sum_j w[t][j] * norm(o[t][j]) rounded to bf16, then
+ *        f = y W_widen^T (fp32 accumulation);
+ *   6.   s_out = alpha * x + beta * f at width D, rounded to bf16.
+ *
+ * Reading: the shared matrices are bf16 (the pages give a 4-bit format for
+ * the expert weights only, section ⑪); z and y are carried in bf16 like
+ * every other activation between kernels.
+ *
+ *   dims->T, E, F, eps as moe_dims_t; D the token width, d the experts'
+ *   width (d takes moe_dims_t's d rules: a positive multiple of 256; D the
+ *   same).
+ *   x               bf16 [T][D]
+ *   router_w        fp32 [E][D]
+ *   w_narrow        bf16 [d][D]: z[j] = sum_i w_narrow[j][i] * x[i]
+ *   expert_w_packed uint8 [E][3*d*F/2], scales uint8 [E][3*d*F/32]: the
+ *                   experts at width d, packed by moe_pack_weights (dims d, F)
+ *   w_widen         bf16 [D][d]: f[i] = sum_j w_widen[i][j] * y[j]
+ *   alpha, beta     fp32 [D]
+ *   s_out           bf16 [T][D]; may be the same buffer as x
+ *   workspace       moe_latent_workspace_size bytes, 256-byte aligned
+ *   stream, debug   as moe_layer_forward (debug copies and stage events
+ *                   refer to the routing and expert stages)
+ *
+ * The two shared-matrix products run in rocBLAS (gemm_ex, bf16 operands,
+ * fp32 accumulation).  Unlike moe_layer_forward this entry point therefore
+ * allocates device memory once per device: the rocBLAS handle created at its
+ * first call there, kept until the process ends.  Same status codes;
+ * MOE_ERR_HIP also covers a rocBLAS failure.  Deterministic as
+ * moe_layer_forward for a fixed rocBLAS solution choice.
+ */
+typedef struct moe_latent_dims {
+    int32_t T;   /* tokens in this call (0 = no-op)            */
+    int32_t D;   /* token width                                */
+    int32_t d;   /* experts' width                             */
+    int32_t E;   /* experts                                    */
+    int32_t F;   /* expert FFN width                           */
+    float eps;   /* RMSNorm epsilon (1e-6)                     */
+} moe_latent_dims_t;
+
+size_t moe_latent_workspace_size(const moe_latent_dims_t *dims, int32_t k);
+
+int moe_latent_forward(const moe_latent_dims_t *dims, const void *x, const float *router_w,
+                       const void *w_narrow, const uint8_t *expert_w_packed,
+                       const uint8_t *scales, const void *w_widen, const float *alpha,
+                       const float *beta, int32_t k, void *s_out, void *workspace,
+                       size_t workspace_bytes, void *stream, const moe_debug_t *debug);
 
 /* Static, human-readable text for a status code. */
 const char *moe_status_string(int status);

@@ -37,6 +37,11 @@ class moe_dims_t(C.Structure):
                 ("eps", C.c_float)]
 
 
+class moe_latent_dims_t(C.Structure):
+    _fields_ = [("T", C.c_int32), ("D", C.c_int32), ("d", C.c_int32), ("E", C.c_int32),
+                ("F", C.c_int32), ("eps", C.c_float)]
+
+
 MOE_NUM_STAGES = 6
 STAGES = ("router", "topk", "group", "gemm1", "gemm2", "combine")
 
@@ -67,6 +72,11 @@ def lib() -> C.CDLL:
         L.moe_pack_weights.restype = C.c_int
         L.moe_dequant_mxfp4.argtypes = [P, P, C.c_int64, C.c_int32, P, P]
         L.moe_dequant_mxfp4.restype = C.c_int
+        L.moe_latent_workspace_size.argtypes = [C.POINTER(moe_latent_dims_t), C.c_int32]
+        L.moe_latent_workspace_size.restype = C.c_size_t
+        L.moe_latent_forward.argtypes = [C.POINTER(moe_latent_dims_t), P, P, P, P, P, P, P, P,
+                                         C.c_int32, P, P, C.c_size_t, P, C.POINTER(moe_debug_t)]
+        L.moe_latent_forward.restype = C.c_int
         L.moe_status_string.argtypes = [C.c_int]
         L.moe_status_string.restype = C.c_char_p
         _lib = L
@@ -181,6 +191,64 @@ def moe_layer_forward(x, router_w, expert_w_packed, scales, alpha, beta, k, *, F
                                  _stream(stream), C.byref(dbg) if dbg is not None else None)
     if rc != MOE_OK:
         raise MoeError(rc, "moe_layer_forward")
+    return s_out
+
+
+def _latent_dims(T, D, d, E, F, eps) -> moe_latent_dims_t:
+    return moe_latent_dims_t(int(T), int(D), int(d), int(E), int(F), float(eps))
+
+
+def moe_latent_workspace_size(T, D, d, E, F, k, eps=1e-6) -> int:
+    return int(lib().moe_latent_workspace_size(C.byref(_latent_dims(T, D, d, E, F, eps)), int(k)))
+
+
+def _debug_struct(debug):
+    if debug is None:
+        return None
+    dbg = moe_debug_t(*(_ptr(debug.get(n)) for n in ("ids", "weights", "offsets", "perm", "inv")))
+    for i, name in enumerate(STAGES):
+        ev = debug.get("events", {}).get(name)
+        if ev is not None:
+            dbg.stage_begin[i] = ev[0].cuda_event
+            dbg.stage_end[i] = ev[1].cuda_event
+    return dbg
+
+
+def moe_latent_forward(x, router_w, w_narrow, expert_w_packed, scales, w_widen, alpha, beta, k, *,
+                       F, eps=1e-6, s_out=None, workspace=None, stream=None, debug=None):
+    """Latent-width variant; returns s_out (bf16 [T][D]).
+
+    x bf16 [T][D]; router_w fp32 [E][D]; w_narrow bf16 [d][D]; experts packed
+    for width d (uint8 [E][3dF/2], [E][3dF/32]); w_widen bf16 [D][d]; alpha,
+    beta fp32 [D].
+    """
+    T, D = x.shape
+    d = w_narrow.shape[0]
+    E = router_w.shape[0]
+    _check(x, "x", torch.bfloat16, (T, D))
+    _check(router_w, "router_w", torch.float32, (E, D))
+    _check(w_narrow, "w_narrow", torch.bfloat16, (d, D))
+    _check(expert_w_packed, "expert_w_packed", torch.uint8, (E, 3 * d * F // 2))
+    _check(scales, "scales", torch.uint8, (E, 3 * d * F // 32))
+    _check(w_widen, "w_widen", torch.bfloat16, (D, d))
+    _check(alpha, "alpha", torch.float32, (D,))
+    _check(beta, "beta", torch.float32, (D,))
+    if s_out is None:
+        s_out = torch.empty_like(x)
+    _check(s_out, "s_out", torch.bfloat16, (T, D))
+    if workspace is None:
+        n = moe_latent_workspace_size(T, D, d, E, F, k, eps)
+        if n == 0 and T != 0:
+            raise MoeError(MOE_ERR_SHAPE, "moe_latent_workspace_size")
+        workspace = torch.empty(max(n, 256), dtype=torch.uint8, device=x.device)
+    dbg = _debug_struct(debug)
+    rc = lib().moe_latent_forward(C.byref(_latent_dims(T, D, d, E, F, eps)), _ptr(x), _ptr(router_w),
+                                  _ptr(w_narrow), _ptr(expert_w_packed), _ptr(scales), _ptr(w_widen),
+                                  _ptr(alpha), _ptr(beta), int(k), _ptr(s_out), _ptr(workspace),
+                                  workspace.numel(), _stream(stream),
+                                  C.byref(dbg) if dbg is not None else None)
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_latent_forward")
     return s_out
 
 

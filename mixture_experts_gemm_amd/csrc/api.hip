@@ -193,6 +193,155 @@ extern "C" int moe_layer_forward(const moe_dims_t *dims, const void *x, const fl
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
+// ---- latent-width variant ---------------------------------------------------
+
+namespace moe {
+
+// Routing at the token width D, experts at width d.
+struct LatentShapes {
+    Shape route, expert;
+};
+
+static bool latent_ok(const moe_latent_dims_t *dm, int32_t k)
+{
+    if (dm->D <= 0 || dm->D % 256) return false;
+    const moe_dims_t e{dm->T, dm->d, dm->E, dm->F, dm->eps};
+    const moe_dims_t r{dm->T, dm->D, dm->E, dm->F, dm->eps};
+    return shape_ok(&e, k) && shape_ok(&r, k);
+}
+
+static LatentShapes latent_shapes(const moe_latent_dims_t *dm, int32_t k)
+{
+    const moe_dims_t e{dm->T, dm->d, dm->E, dm->F, dm->eps};
+    const moe_dims_t r{dm->T, dm->D, dm->E, dm->F, dm->eps};
+    return LatentShapes{to_shape(&r, k), to_shape(&e, k)};
+}
+
+// The expert path's workspace, then the router's score planes at width D,
+// z and y (bf16 [T][d]) and f (fp32 [T][D]).
+struct LatentWorkspace {
+    Workspace ws;
+    float *scores_r;
+    uint16_t *z, *y;
+    float *f;
+    size_t bytes;
+};
+
+static LatentWorkspace carve_latent(const LatentShapes &ls, void *base)
+{
+    LatentWorkspace L;
+    L.ws = carve_workspace(ls.expert, base);
+    size_t off = L.ws.bytes;
+    char *b = static_cast<char *>(base);
+    auto take = [&](size_t bytes) -> void * {
+        void *p = b ? b + off : nullptr;
+        off += align256(bytes);
+        return p;
+    };
+    const Shape &r = ls.route, &e = ls.expert;
+    L.scores_r = (float *)take(sizeof(float) * (size_t)router_splits(r) * r.T * r.E);
+    L.z = (uint16_t *)take(sizeof(uint16_t) * (size_t)e.T * e.d);
+    L.y = (uint16_t *)take(sizeof(uint16_t) * (size_t)e.T * e.d);
+    L.f = (float *)take(sizeof(float) * (size_t)r.T * r.d);
+    L.bytes = off;
+    return L;
+}
+
+}  // namespace moe
+
+extern "C" size_t moe_latent_workspace_size(const moe_latent_dims_t *dims, int32_t k)
+{
+    if (!dims || !latent_ok(dims, k)) return 0;
+    return carve_latent(latent_shapes(dims, k), nullptr).bytes;
+}
+
+extern "C" int moe_latent_forward(const moe_latent_dims_t *dims, const void *x,
+                                  const float *router_w, const void *w_narrow,
+                                  const uint8_t *expert_w_packed, const uint8_t *scales,
+                                  const void *w_widen, const float *alpha, const float *beta,
+                                  int32_t k, void *s_out, void *workspace, size_t workspace_bytes,
+                                  void *stream, const moe_debug_t *debug)
+{
+    if (!dims) return MOE_ERR_NULL;
+    if (!latent_ok(dims, k)) return MOE_ERR_SHAPE;
+    if (dims->T == 0) return MOE_OK;
+    if (!x || !router_w || !w_narrow || !expert_w_packed || !scales || !w_widen || !alpha ||
+        !beta || !s_out || !workspace)
+        return MOE_ERR_NULL;
+    if (!aligned16({x, router_w, w_narrow, expert_w_packed, scales, w_widen, alpha, beta, s_out}))
+        return MOE_ERR_ALIGN;
+    const LatentShapes ls = latent_shapes(dims, k);
+    if (workspace_bytes < carve_latent(ls, nullptr).bytes) return MOE_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return MOE_ERR_WORKSPACE;
+    int rc = check_arch();
+    if (rc != MOE_OK) return rc;
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const LatentWorkspace L = carve_latent(ls, workspace);
+    const Shape &sr = ls.route, &se = ls.expert;
+    const Plan p = make_plan(se);
+    // routing reads the full-width token: its own score planes, and no split
+    // of x (the experts read z)
+    Workspace wr = L.ws;
+    wr.scores = L.scores_r;
+    Plan pr = p;
+    pr.stream = pr.tiled = false;
+    const uint16_t *xb = static_cast<const uint16_t *>(x);
+    (void)hipGetLastError();
+
+    auto mark = [&](void *const *evs, int stage) -> bool {
+        if (!debug || !evs[stage]) return true;
+        return hipEventRecord(static_cast<hipEvent_t>(evs[stage]), st) == hipSuccess;
+    };
+    auto stage = [&](int id, auto &&fn) -> bool {
+        if (!mark(debug ? debug->stage_begin : nullptr, id)) return false;
+        if (fn() != hipSuccess) return false;
+        return mark(debug ? debug->stage_end : nullptr, id);
+    };
+    auto ok = [](hipError_t e) { return e == hipSuccess; };
+    auto narrow = [&]() -> hipError_t {
+        hipError_t e = launch_dense(xb, static_cast<const uint16_t *>(w_narrow), L.z, false, sr.T,
+                                    se.d, sr.d, st);
+        if (e != hipSuccess) return e;
+        if (p.stream) return launch_split_x_fp8(se, L.ws, L.z, st);
+        if (p.tiled) return launch_split_x(se, L.ws, L.z, st);
+        return hipSuccess;
+    };
+    auto widen = [&]() -> hipError_t {
+        hipError_t e = launch_combine_sum(se, p, L.ws, L.y, st);
+        if (e != hipSuccess) return e;
+        e = launch_dense(L.y, static_cast<const uint16_t *>(w_widen), L.f, true, sr.T, sr.d, se.d, st);
+        if (e != hipSuccess) return e;
+        return launch_gate(xb, L.f, alpha, beta, static_cast<uint16_t *>(s_out), sr.T, sr.d, st);
+    };
+    if (!stage(MOE_STAGE_ROUTER, [&] { return launch_router(sr, pr, wr, xb, router_w, st); }) ||
+        !stage(MOE_STAGE_TOPK, [&] { return launch_topk(sr, p, wr, st); }) ||
+        !stage(MOE_STAGE_GROUP, [&] { return launch_group(sr, p, wr, st); }) || !ok(narrow()) ||
+        !ok(launch_gemm1(se, p, L.ws, L.z, expert_w_packed, scales, st,
+                         stage_event(debug, MOE_STAGE_GEMM1, true),
+                         stage_event(debug, MOE_STAGE_GEMM1, false))) ||
+        !stage(MOE_STAGE_GEMM2, [&] { return launch_gemm2(se, p, L.ws, expert_w_packed, scales, st); }) ||
+        !stage(MOE_STAGE_COMBINE, widen))
+        return MOE_ERR_HIP;
+
+    if (debug) {
+        const size_t S4 = sizeof(int32_t) * (size_t)se.S();
+        struct {
+            void *dst;
+            const void *src;
+            size_t n;
+        } cp[5] = {{debug->ids, L.ws.ids, S4},
+                   {debug->weights, L.ws.wts, S4},
+                   {debug->offsets, L.ws.offsets, sizeof(int32_t) * (size_t)(se.E + 1)},
+                   {debug->perm, L.ws.perm, S4},
+                   {debug->inv, L.ws.inv, S4}};
+        for (auto &c : cp)
+            if (c.dst && hipMemcpyAsync(c.dst, c.src, c.n, hipMemcpyDeviceToDevice, st) != hipSuccess)
+                return MOE_ERR_HIP;
+    }
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
 extern "C" int moe_pack_weights(const moe_dims_t *dims, const uint8_t *codes, const uint8_t *scales,
                                 uint8_t *codes_packed, uint8_t *scales_packed, void *stream)
 {

@@ -23,7 +23,9 @@ constexpr int kCombineCols = 2048;  // columns per workgroup (8 per thread)
 
 // SLOT: o and the o^2 partial sums are stored in slot order (row t*k + j is
 // slot j of token t); otherwise in the grouped order, found through inv.
-template <bool SLOT>
+// GATE: s_out = bf16(alpha * x + beta * y); otherwise s_out = bf16(y) (the
+// latent-width variant widens y before its gate).
+template <bool SLOT, bool GATE>
 __global__ __launch_bounds__(256) void combine_kernel(
     const uint16_t *x, const float *__restrict__ wts, const int32_t *__restrict__ inv,
     const uint16_t *__restrict__ o, const float *__restrict__ ssq, const float *__restrict__ alpha,
@@ -38,7 +40,7 @@ __global__ __launch_bounds__(256) void combine_kernel(
     // independent loads first
     uint4 xv = make_uint4(0, 0, 0, 0);
     float4 a0 = make_float4(0, 0, 0, 0), a1 = a0, b0 = a0, b1 = a0;
-    if (act) {
+    if (GATE && act) {
         xv = *reinterpret_cast<const uint4 *>(x + (int64_t)t * d + c0);
         a0 = *reinterpret_cast<const float4 *>(alpha + c0);
         a1 = *reinterpret_cast<const float4 *>(alpha + c0 + 4);
@@ -91,7 +93,14 @@ __global__ __launch_bounds__(256) void combine_kernel(
             }
         }
     }
-    if (act) {
+    if (!GATE && act) {
+        uint32_t ow[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            ow[i] = (uint32_t)f32_to_bf16(y[2 * i]) | (uint32_t)f32_to_bf16(y[2 * i + 1]) << 16;
+        *reinterpret_cast<uint4 *>(s_out + (int64_t)t * d + c0) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+    }
+    if (GATE && act) {
         const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
         const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
         const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
@@ -112,11 +121,24 @@ hipError_t launch_combine(const Shape &s, const Plan &p, const Workspace &ws, co
     dim3 grid(s.T, (s.d + kCombineCols - 1) / kCombineCols);
     // the few-row down kernel stores in slot order, the tiled ones in the grouped order
     if (p.tiled)
-        combine_kernel<false><<<grid, 256, 0, st>>>(x, ws.wts, ws.inv, ws.o, ws.ssq, alpha, beta, s_out,
-                                                    s.d, s.k, s.d / p.ssq_cols, s.eps);
+        combine_kernel<false, true><<<grid, 256, 0, st>>>(x, ws.wts, ws.inv, ws.o, ws.ssq, alpha, beta,
+                                                          s_out, s.d, s.k, s.d / p.ssq_cols, s.eps);
     else
-        combine_kernel<true><<<grid, 256, 0, st>>>(x, ws.wts, ws.inv, ws.o, ws.ssq, alpha, beta, s_out,
-                                                   s.d, s.k, s.d / p.ssq_cols, s.eps);
+        combine_kernel<true, true><<<grid, 256, 0, st>>>(x, ws.wts, ws.inv, ws.o, ws.ssq, alpha, beta,
+                                                         s_out, s.d, s.k, s.d / p.ssq_cols, s.eps);
+    return hipGetLastError();
+}
+
+hipError_t launch_combine_sum(const Shape &s, const Plan &p, const Workspace &ws, uint16_t *y,
+                              hipStream_t st)
+{
+    dim3 grid(s.T, (s.d + kCombineCols - 1) / kCombineCols);
+    if (p.tiled)
+        combine_kernel<false, false><<<grid, 256, 0, st>>>(nullptr, ws.wts, ws.inv, ws.o, ws.ssq, nullptr,
+                                                           nullptr, y, s.d, s.k, s.d / p.ssq_cols, s.eps);
+    else
+        combine_kernel<true, false><<<grid, 256, 0, st>>>(nullptr, ws.wts, ws.inv, ws.o, ws.ssq, nullptr,
+                                                          nullptr, y, s.d, s.k, s.d / p.ssq_cols, s.eps);
     return hipGetLastError();
 }
 

@@ -909,6 +909,11 @@ static hipError_t launch_split6(const uint16_t *src, int64_t rows, int K, uint8_
     return hipGetLastError();
 }
 
+hipError_t launch_split_x_fp8(const Shape &s, const Workspace &ws, const uint16_t *x, hipStream_t st)
+{
+    return launch_split(x, s.T, s.d, ws.xhi, ws.xlo, ws.xshi, ws.xslo, st);
+}
+
 hipError_t launch_split_x(const Shape &s, const Workspace &ws, const uint16_t *x, hipStream_t st)
 {
     if (wide_gate_up(s)) return launch_split6(x, s.T, s.d, ws.xa6, st);

@@ -154,6 +154,19 @@ hipError_t launch_gemm2(const Shape &s, const Plan &p, const Workspace &ws, cons
 hipError_t launch_combine(const Shape &s, const Plan &p, const Workspace &ws, const uint16_t *x,
                           const float *alpha, const float *beta, uint16_t *s_out,
                           hipStream_t st);
+// Norms and weighted sum only: y = bf16(sum_j w_j * norm(o_j)) [T][d].
+hipError_t launch_combine_sum(const Shape &s, const Plan &p, const Workspace &ws, uint16_t *y,
+                              hipStream_t st);
+// bf16 x -> FP8 hi/lo parts + E8M0 scales in the workspace (the streaming
+// gate/up kernel's input when the router does not split x itself).
+hipError_t launch_split_x_fp8(const Shape &s, const Workspace &ws, const uint16_t *x, hipStream_t st);
+// c[T][N] = a[T][K] w[N][K]^T, bf16 operands, fp32 accumulation, c bf16 or
+// fp32 (rocBLAS gemm_ex).
+hipError_t launch_dense(const uint16_t *a, const uint16_t *w, void *c, bool c_fp32, int T, int N,
+                        int K, hipStream_t st);
+// s_out = bf16(alpha * x + beta * f), x bf16 [T][D], f fp32 [T][D].
+hipError_t launch_gate(const uint16_t *x, const float *f, const float *alpha, const float *beta,
+                       uint16_t *s_out, int64_t T, int D, hipStream_t st);
 hipError_t launch_pack(const uint8_t *w, const uint8_t *s, int E, int d, int F, uint8_t *wp,
                        uint8_t *sp, hipStream_t st);
 hipError_t launch_dequant(const uint8_t *codes, const uint8_t *scales, int64_t rows, int K,

@@ -82,6 +82,18 @@ def layer_flops(T: int, d: int, k: int, F: int) -> int:
     return T * k * flops_per_slot(d, F)
 
 
+def latent_layer_bytes(T: int, D: int, d: int, E: int, F: int, U: int) -> int:
+    """Latent-width variant: experts at width d, router and gate at width D,
+    plus the two shared bf16 matrices (d x D and D x d)."""
+    return (U * mxfp4_expert_bytes(d, F) + E * D * 4 + 2 * D * 4 + 2 * T * D * 2
+            + 2 * d * D * 2)
+
+
+def latent_layer_flops(T: int, D: int, d: int, k: int, F: int) -> int:
+    """Experts at width d plus the two shared products (2 T d D flops each)."""
+    return T * k * flops_per_slot(d, F) + 2 * (2 * T * d * D)
+
+
 def router_flops(T: int, d: int, E: int) -> int:
     return 2 * T * d * E
 

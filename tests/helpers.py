@@ -83,3 +83,40 @@ def run_layer(L, dev=None, debug=True, x=None, **kw):
         res["ids"] = res["ids"].reshape(T, s.k)
         res["weights"] = res["weights"].reshape(T, s.k)
     return bf16_bits(out), res
+
+
+def upload_latent(L, device="cuda"):
+    """Device copies of a generated latent-width layer (experts packed for width d)."""
+    from mixture_experts_gemm_amd import binding as B
+    w_nat = torch.from_numpy(L.w_packed).to(device)
+    s_nat = torch.from_numpy(L.scales).to(device)
+    w, s = B.moe_pack_weights(w_nat, s_nat, L.w.d, L.w.F)
+    torch.cuda.synchronize()
+    del w_nat, s_nat
+    return dict(
+        x=bf16_tensor(L.x, device),
+        router_w=torch.from_numpy(L.router_w).to(device),
+        wc=bf16_tensor(L.wc, device),
+        w=w,
+        s=s,
+        we=bf16_tensor(L.we, device),
+        alpha=torch.from_numpy(L.alpha).to(device),
+        beta=torch.from_numpy(L.beta).to(device),
+    )
+
+
+def run_latent(L, dev=None, debug=True, **kw):
+    """GPU latent-width layer through the C ABI.  Returns (s_out bits [T][D], debug dict)."""
+    from mixture_experts_gemm_amd import binding as B
+    dev = dev or upload_latent(L)
+    w = L.w
+    dbg = debug_buffers(w.T, w.E, w.k) if debug else None
+    out = B.moe_latent_forward(dev["x"], dev["router_w"], dev["wc"], dev["w"], dev["s"], dev["we"],
+                               dev["alpha"], dev["beta"], w.k, F=w.F, eps=L.eps, debug=dbg, **kw)
+    torch.cuda.synchronize()
+    res = None
+    if debug:
+        res = {n: t.cpu().numpy() for n, t in dbg.items()}
+        res["ids"] = res["ids"].reshape(w.T, w.k)
+        res["weights"] = res["weights"].reshape(w.T, w.k)
+    return bf16_bits(out), res

@@ -16,7 +16,8 @@ def L():
 def test_exports_every_declared_function(L):
     names = B.declared_functions()
     assert set(names) == {"moe_layer_workspace_size", "moe_layer_forward", "moe_pack_weights",
-                          "moe_dequant_mxfp4", "moe_status_string"}
+                          "moe_dequant_mxfp4", "moe_status_string", "moe_latent_workspace_size",
+                          "moe_latent_forward"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -96,3 +97,50 @@ def test_pack_argument_errors():
     assert f(C.byref(B.moe_dims_t(0, 256, 0, 512, 1e-6)), p, p, p, p, None) == B.MOE_ERR_SHAPE
     assert f(C.byref(good), odd, p, p, p, None) == B.MOE_ERR_ALIGN
     assert f(C.byref(good), p, p, p, odd, None) == B.MOE_ERR_ALIGN
+
+
+# ------------------------------------------------------------- latent variant
+
+def test_latent_workspace_size():
+    ws = B.moe_latent_workspace_size
+    assert ws(0, 512, 256, 8, 256, 2) > 0
+    a, b = ws(64, 512, 256, 8, 256, 2), ws(128, 512, 256, 8, 256, 2)
+    assert 0 < a < b
+    # at least the full-width layer's workspace at the experts' width, plus z, y and f
+    T = 4096
+    big = ws(T, 8192, 4096, 256, 4096, 8)
+    assert big >= B.moe_layer_workspace_size(T, 4096, 256, 4096, 8) + T * 4096 * 4 + T * 8192 * 4
+    assert ws(64, 500, 256, 8, 256, 2) == 0    # D not a multiple of 256
+    assert ws(64, 512, 200, 8, 256, 2) == 0    # d not a multiple of 256
+    assert ws(64, 512, 256, 8, 100, 2) == 0    # F not a multiple of 128
+    assert ws(64, 512, 256, 8, 256, 9) == 0    # k > E
+
+
+def _latent_call(dims, k=2, ws_bytes=1 << 30, null=None, ws_ptr=1 << 20, ptr=None):
+    p = C.c_void_p(1 << 20)  # never dereferenced: every case below fails the checks first
+    names = ("x", "router_w", "w_narrow", "w", "s", "w_widen", "alpha", "beta", "s_out")
+    args = {n: p for n in names}
+    args["ws"] = C.c_void_p(ws_ptr)
+    if null:
+        args[null] = None
+    args.update(ptr or {})
+    return B.lib().moe_latent_forward(C.byref(dims) if dims is not None else None,
+                                      *(args[n] for n in names[:8]), k, args["s_out"], args["ws"],
+                                      ws_bytes, None, None)
+
+
+def test_latent_argument_errors():
+    good = B.moe_latent_dims_t(64, 512, 256, 8, 256, 1e-6)
+    assert _latent_call(None) == B.MOE_ERR_NULL
+    for name in ("x", "router_w", "w_narrow", "w", "s", "w_widen", "alpha", "beta", "s_out", "ws"):
+        assert _latent_call(good, null=name) == B.MOE_ERR_NULL, name
+    assert _latent_call(B.moe_latent_dims_t(64, 500, 256, 8, 256, 1e-6)) == B.MOE_ERR_SHAPE
+    assert _latent_call(B.moe_latent_dims_t(64, 512, 300, 8, 256, 1e-6)) == B.MOE_ERR_SHAPE
+    assert _latent_call(good, k=9) == B.MOE_ERR_SHAPE
+    assert _latent_call(good, ws_bytes=1024) == B.MOE_ERR_WORKSPACE
+    assert _latent_call(good, ws_ptr=(1 << 20) + 64) == B.MOE_ERR_WORKSPACE
+    odd = C.c_void_p((1 << 20) + 8)
+    for name in ("x", "router_w", "w_narrow", "w", "s", "w_widen", "alpha", "beta", "s_out"):
+        assert _latent_call(good, ptr={name: odd}) == B.MOE_ERR_ALIGN, name
+    zero = B.moe_latent_dims_t(0, 512, 256, 8, 256, 1e-6)
+    assert _latent_call(zero, null="x") == B.MOE_OK

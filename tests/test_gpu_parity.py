@@ -13,8 +13,8 @@ import torch
 import oracle
 from mixture_experts_gemm_amd import synth
 
-from helpers import (WEIGHT_TOL, assert_close, bf16_bits, bf16_tensor, metrics, run_layer,
-                     upload)
+from helpers import (WEIGHT_TOL, assert_close, bf16_bits, bf16_tensor, metrics, run_latent,
+                     run_layer, upload)
 
 pytestmark = pytest.mark.gpu
 
@@ -322,3 +322,24 @@ def test_stack_of_four_layers():
         x_gpu = bf16_tensor(out)
         del dev, L
         torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------ latent-width variant
+
+@pytest.mark.parametrize("name,n", [("latent_tiny", None), ("latent1", None), ("latent4", None),
+                                    ("latent_prefill", 8)])
+def test_latent_variant(name, n):
+    """Narrowing matrix, experts at the narrow width, widening matrix: routing
+    on the full-width token bit for bit, outputs against the oracle's L1-L5
+    on every token (small sizes) or a seeded sample (prefill size)."""
+    L = synth.make_latent_layer(name)
+    w = L.w
+    _say(name, "T", w.T, "D", w.D, "d", w.d)
+    out, dbg = run_latent(L)
+    _check_routing(L, dbg, name)
+    tokens = np.arange(w.T, dtype=np.int32) if n is None else _sample(w.T, n, 6)
+    ref, _, _ = oracle.latent_forward(L.x, L.router_w, L.wc, L.w_packed, L.scales, L.we, L.alpha,
+                                      L.beta, w.k, eps=L.eps, tokens=tokens)
+    got = synth.bf16_bits_to_f32(out[tokens]).astype(np.float64)
+    m = assert_close(got, ref, name)
+    _say(name, "tokens", len(tokens), m)
