@@ -48,7 +48,8 @@ from concurrent.futures import ThreadPoolExecutor
 import numpy as np
 
 # substream tags
-_TAG_X, _TAG_WR, _TAG_W, _TAG_S, _TAG_AB, _TAG_ZIPF, _TAG_REDRAW, _TAG_WC, _TAG_WE = range(9)
+(_TAG_X, _TAG_WR, _TAG_W, _TAG_S, _TAG_AB, _TAG_ZIPF, _TAG_REDRAW, _TAG_WC, _TAG_WE,
+ _TAG_GAIN) = range(10)
 
 SCALE_LO, SCALE_HI = 119, 123          # E8M0 bytes: 2^-8 .. 2^-4
 GAP_DEFAULT = 1e-4
@@ -217,6 +218,14 @@ def make_gates(w: Workload, layer: int = 0):
     alpha = (g.random(w.shape.d, dtype=np.float32) + np.float32(0.5)).astype(np.float32)
     beta = (g.random(w.shape.d, dtype=np.float32) + np.float32(0.5)).astype(np.float32)
     return alpha, beta
+
+
+def make_norm_gains(w: Workload, layer: int = 0):
+    """Learned gains of the block's two stream norms, fp32 [d] each, U(0.5, 1.5)."""
+    g = _rng(w.seed, layer, _TAG_GAIN, 0)
+    pre = (g.random(w.shape.d, dtype=np.float32) + np.float32(0.5)).astype(np.float32)
+    post = (g.random(w.shape.d, dtype=np.float32) + np.float32(0.5)).astype(np.float32)
+    return pre, post
 
 
 @dataclasses.dataclass

@@ -54,6 +54,9 @@ def lib():
         L.oracle_latent_forward.argtypes = [_I, _I, _I, _I, _I, _I, C.c_double, _P, _P, _P, _P, _P,
                                             _P, _P, _P, _I, _P, _P, _P, _P]
         L.oracle_latent_forward.restype = _I
+        L.oracle_block_forward.argtypes = [_I, _I, _I, _I, _I, C.c_double, _P, _P, _P, _P, _P, _P,
+                                           _P, _P, _I, _P, _P, _P, _P]
+        L.oracle_block_forward.restype = _I
         _lib = L
     return _lib
 
@@ -217,4 +220,36 @@ def latent_forward(x_bits, wr, wc_bits, w_packed, scales, we_bits, alpha, beta, 
                                      n, None if sel is None else _p(sel), _p(s), _p(ids), _p(w))
     if rc != 0:
         raise ValueError("oracle_latent_forward: bad arguments")
+    return s, ids, w
+
+
+def block_forward(x_bits, gamma_pre, wr, w_packed, scales, gamma_post, alpha, beta, k, eps=1e-6,
+                  tokens=None):
+    """B1-B3 (the block with its stream norms) on the listed tokens: (s float64 [n][d], ids, w)."""
+    x_bits = _c(x_bits, np.uint16)
+    gamma_pre = _c(gamma_pre, np.float32)
+    gamma_post = _c(gamma_post, np.float32)
+    wr = _c(wr, np.float32)
+    w_packed = _c(w_packed, np.uint8)
+    scales = _c(scales, np.uint8)
+    alpha = _c(alpha, np.float32)
+    beta = _c(beta, np.float32)
+    T, d = x_bits.shape
+    E = wr.shape[0]
+    F = w_packed.size // E * 2 // (3 * d)
+    assert w_packed.size == E * 3 * d * F // 2 and scales.size == E * 3 * d * F // 32
+    if tokens is None:
+        sel = None
+        n = T
+    else:
+        sel = _c(tokens, np.int32)
+        n = sel.size
+    s = np.empty((n, d), np.float64)
+    ids = np.empty((n, k), np.int32)
+    w = np.empty((n, k), np.float64)
+    rc = lib().oracle_block_forward(T, d, E, F, k, eps, _p(x_bits), _p(gamma_pre), _p(wr),
+                                    _p(w_packed), _p(scales), _p(gamma_post), _p(alpha), _p(beta),
+                                    n, None if sel is None else _p(sel), _p(s), _p(ids), _p(w))
+    if rc != 0:
+        raise ValueError("oracle_block_forward: bad arguments")
     return s, ids, w

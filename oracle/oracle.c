@@ -389,3 +389,72 @@ int oracle_latent_forward(int T, int D, int d, int E, int F, int k, double eps,
     free(xs); free(scores); free(ids); free(w); free(z); free(n); free(y);
     return 0;
 }
+
+/* ---- the block with its stream norms -------------------------------------- */
+
+/*
+ * [MS] section ③: the MoE part of a layer does not write the residual stream
+ * s directly.  A copy of s is normalised and run through the part; the
+ * part's output is normalised as well and mixed in by the gate,
+ * s <- alpha * s + beta * norm(output).
+ *
+ *   B1  x_n = bf16(s * r_s * gamma_pre), r_s = 1 / sqrt(mean(s^2) + eps):
+ *       RMSNorm with a learned per-dimension gain.  Reading: the normalised
+ *       copy enters the block as bf16, like every activation handed between
+ *       kernels; the rounding is part of the definition because the
+ *       router's choice depends on it.
+ *   B2  O2-O7 on x_n, and y = sum_j w_j n_j (O8 without the gate), double.
+ *   B3  s_out = alpha * s + beta * (y * r_y * gamma_post),
+ *       r_y = 1 / sqrt(mean(y^2) + eps).  Kept in double.
+ *
+ * Arguments as oracle_moe_forward plus the two gains (fp32 [d]).
+ */
+int oracle_block_forward(int T, int d, int E, int F, int k, double eps, const uint16_t *x,
+                         const float *gamma_pre, const float *wr, const uint8_t *wpk,
+                         const uint8_t *sc, const float *gamma_post, const float *alpha,
+                         const float *beta, int n_sel, const int32_t *sel, double *s_out,
+                         int32_t *ids_out, double *w_out)
+{
+    if (T < 0 || d <= 0 || E <= 0 || F <= 0 || k < 1 || k > E || d % 32 || F % 32) return -1;
+    if (sel == NULL) n_sel = T;
+    if (n_sel <= 0) return 0;
+    uint16_t *xn = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)n_sel * d);
+    double *y = (double *)malloc(sizeof(double) * (size_t)n_sel * d);
+    float *zero = (float *)calloc((size_t)d, sizeof(float));
+    float *one = (float *)malloc(sizeof(float) * (size_t)d);
+    if (!xn || !y || !zero || !one) {
+        free(xn); free(y); free(zero); free(one);
+        return -1;
+    }
+    for (int i = 0; i < d; ++i) one[i] = 1.0f;
+    /* B1 */
+    for (int r = 0; r < n_sel; ++r) {
+        const int t = sel ? sel[r] : r;
+        double ss = 0.0;
+        for (int i = 0; i < d; ++i) {
+            const double v = oracle_bf16_to_double(x[(int64_t)t * d + i]);
+            ss += v * v;
+        }
+        const double rs = 1.0 / sqrt(ss / (double)d + eps);
+        for (int i = 0; i < d; ++i)
+            xn[(int64_t)r * d + i] = oracle_double_to_bf16(
+                oracle_bf16_to_double(x[(int64_t)t * d + i]) * rs * (double)gamma_pre[i]);
+    }
+    /* B2: the layer on x_n with alpha = 0, beta = 1 returns y */
+    int rc = oracle_moe_forward(n_sel, d, E, F, k, eps, xn, wr, wpk, sc, zero, one, n_sel, NULL, y,
+                                ids_out, w_out);
+    /* B3 */
+    if (rc == 0)
+        for (int r = 0; r < n_sel; ++r) {
+            const int t = sel ? sel[r] : r;
+            double ss = 0.0;
+            for (int i = 0; i < d; ++i) ss += y[(int64_t)r * d + i] * y[(int64_t)r * d + i];
+            const double ry = 1.0 / sqrt(ss / (double)d + eps);
+            for (int i = 0; i < d; ++i)
+                s_out[(int64_t)r * d + i] =
+                    (double)alpha[i] * oracle_bf16_to_double(x[(int64_t)t * d + i]) +
+                    (double)beta[i] * (y[(int64_t)r * d + i] * ry * (double)gamma_post[i]);
+        }
+    free(xn); free(y); free(zero); free(one);
+    return rc;
+}

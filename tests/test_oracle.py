@@ -428,3 +428,70 @@ def test_latent_token_subset():
                                          L.alpha, L.beta, L.w.k, tokens=sel)
     np.testing.assert_array_equal(sub, full[sel])
     np.testing.assert_array_equal(ids2, ids[sel])
+
+
+# ------------------------------------------------- block with stream norms (B1-B3)
+
+def _block_inputs(name="tiny"):
+    L = synth.make_layer(name)
+    g_pre, g_post = synth.make_norm_gains(synth.WORKLOADS[name])
+    return L, g_pre, g_post
+
+
+def test_block_is_norm_layer_norm_composition():
+    """torch float64 rms_norm for both stream norms, the pinned bf16 rounding
+    and the pinned full-width layer (alpha = 0, beta = 1 gives y) between them."""
+    L, g_pre, g_post = _block_inputs()
+    s, ids, w = oracle.block_forward(L.x, g_pre, L.router_w, L.w_packed, L.scales, g_post, L.alpha,
+                                     L.beta, L.k)
+    X = torch.from_numpy(synth.bf16_bits_to_f32(L.x).astype(np.float64))
+    Xn = torch.nn.functional.rms_norm(X, (X.shape[-1],), eps=L.eps) * \
+        torch.from_numpy(g_pre.astype(np.float64))
+    xn_bits = oracle.doubles_to_bf16(Xn.numpy())
+    d = L.shape.d
+    y, ids2, w2 = oracle.moe_forward(xn_bits, L.router_w, L.w_packed, L.scales,
+                                     np.zeros(d, np.float32), np.ones(d, np.float32), L.k)
+    np.testing.assert_array_equal(ids, ids2)
+    Y = torch.from_numpy(y)
+    P = torch.nn.functional.rms_norm(Y, (d,), eps=L.eps) * torch.from_numpy(g_post.astype(np.float64))
+    ref = torch.from_numpy(L.alpha.astype(np.float64)) * X + torch.from_numpy(L.beta.astype(np.float64)) * P
+    err = np.abs(s - ref.numpy()).max() / np.abs(ref.numpy()).max()
+    assert err <= 1e-12, err
+
+
+def test_block_stream_scale_invariance():
+    """With eps = 0 both norms remove the scale of the stream: doubling s (exact
+    in bf16) leaves the block's contribution unchanged, so s_out moves by
+    exactly alpha * s.  A dropped or misplaced pre-norm fails this."""
+    L, g_pre, g_post = _block_inputs()
+    s1, ids1, _ = oracle.block_forward(L.x, g_pre, L.router_w, L.w_packed, L.scales, g_post,
+                                       L.alpha, L.beta, L.k, eps=0.0)
+    x2 = synth.f32_to_bf16_bits(2.0 * synth.bf16_bits_to_f32(L.x))
+    s2, ids2, _ = oracle.block_forward(x2, g_pre, L.router_w, L.w_packed, L.scales, g_post,
+                                       L.alpha, L.beta, L.k, eps=0.0)
+    np.testing.assert_array_equal(ids1, ids2)
+    ax = L.alpha.astype(np.float64) * synth.bf16_bits_to_f32(L.x).astype(np.float64)
+    np.testing.assert_allclose(s2 - s1, ax, rtol=0, atol=1e-12)
+
+
+def test_block_post_gain_linearity():
+    """The block's contribution is linear in the post-norm gain (doubling is
+    exact in fp32)."""
+    L, g_pre, g_post = _block_inputs()
+    ax = L.alpha.astype(np.float64) * synth.bf16_bits_to_f32(L.x).astype(np.float64)
+    s1, _, _ = oracle.block_forward(L.x, g_pre, L.router_w, L.w_packed, L.scales, g_post, L.alpha,
+                                    L.beta, L.k)
+    s3, _, _ = oracle.block_forward(L.x, g_pre, L.router_w, L.w_packed, L.scales,
+                                    (2.0 * g_post).astype(np.float32), L.alpha, L.beta, L.k)
+    np.testing.assert_allclose(s3 - ax, 2.0 * (s1 - ax), rtol=1e-12, atol=1e-12)
+
+
+def test_block_token_subset():
+    L, g_pre, g_post = _block_inputs()
+    full, ids, _ = oracle.block_forward(L.x, g_pre, L.router_w, L.w_packed, L.scales, g_post,
+                                        L.alpha, L.beta, L.k)
+    sel = np.array([7, 0, 63, 31], np.int32)
+    sub, ids2, _ = oracle.block_forward(L.x, g_pre, L.router_w, L.w_packed, L.scales, g_post,
+                                        L.alpha, L.beta, L.k, tokens=sel)
+    np.testing.assert_array_equal(sub, full[sel])
+    np.testing.assert_array_equal(ids2, ids[sel])
