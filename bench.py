@@ -38,8 +38,14 @@ WORKLOAD_TEXT = {
                "shared bf16 matrix, E=256, top-8, 4096x4096 MXFP4 experts, widened back by a second one)",
     "latent_prefill": "Latent-width variant, prefill micro-batch (T=4096, 8192 -> 4096 -> 8192 shared bf16 "
                       "matrices, E=256, top-8, 4096x4096 MXFP4 experts)",
+    "block4": "MoE block with its stream norms (RMSNorm + gain in front, on the output before the gate), "
+              "4 concurrent requests (T=4, d=8192, E=256, top-8, F=2048, MXFP4)",
+    "block_prefill": "MoE block with its stream norms, prefill micro-batch (T=4096, d=8192, E=256, top-8, "
+                     "F=2048, MXFP4)",
 }
 LATENT = ("latent4", "latent_prefill")
+# the block with its stream norms runs on the full-width workloads' inputs
+BLOCK = {"block4": "decode4", "block_prefill": "prefill"}
 
 
 def log(*a):
@@ -52,7 +58,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="decode4", choices=sorted(WORKLOAD_TEXT))
-    ap.add_argument("--also", default="decode1,prefill,ep753,ep3012,latent4,latent_prefill",
+    ap.add_argument("--also", default="decode1,prefill,ep753,ep3012,latent4,latent_prefill,block4,"
+                                      "block_prefill",
                     help="comma list of extra workloads timed after the main one ('' for none)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
@@ -149,6 +156,8 @@ GATE_UP_KERNEL = {
     "ep3012": "gemm_mxw_kernel<true> (gate/up + SwiGLU, 128x512 tiles, MX MFMA)",
     "latent4": "gemm1_stream_kernel (gate/up + SwiGLU, persistent, MX MFMA)",
     "latent_prefill": "gemm_mxw_kernel<true> (gate/up + SwiGLU, 128x512 tiles, MX MFMA)",
+    "block4": "gemm1_stream_kernel (gate/up + SwiGLU, persistent, MX MFMA)",
+    "block_prefill": "gemm_mxw_kernel<true> (gate/up + SwiGLU, 128x512 tiles, MX MFMA)",
 }
 
 
@@ -167,7 +176,8 @@ def time_workload(name, steps, warmup, device):
     from mixture_experts_gemm_amd import roofline as R
 
     latent = name in LATENT
-    decode = name.startswith("decode") or name == "latent4"
+    block = name in BLOCK
+    decode = name.startswith("decode") or name in ("latent4", "block4")
     nsets = 4 if decode else 1
     log(f"generating {name}: {nsets} weight set(s)")
     if latent:
@@ -177,13 +187,21 @@ def time_workload(name, steps, warmup, device):
         s = w.expert_view().shape
         D = w.D
     else:
-        w, host, sets, xpool = make_sets(name, nsets, device)
+        w, host, sets, xpool = make_sets(BLOCK.get(name, name), nsets, device)
         s = w.shape
         D = s.d
+        if block:
+            from mixture_experts_gemm_amd import synth
+            for i, st in enumerate(sets):
+                st["g_pre"], st["g_post"] = (torch.from_numpy(v).to(device)
+                                             for v in synth.make_norm_gains(w, layer=i))
     T = s.T
     npool = xpool.shape[0] // T
     if latent:
         nws = B.moe_latent_workspace_size(T, D, s.d, s.E, s.F, s.k)
+        ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=device)
+    elif block:
+        nws = B.moe_block_workspace_size(T, s.d, s.E, s.F, s.k)
         ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=device)
     else:
         ws = B.workspace_for(T, s.d, s.E, s.F, s.k, device=device)
@@ -196,6 +214,9 @@ def time_workload(name, steps, warmup, device):
         if latent:
             B.moe_latent_forward(xb, st["wr"], st["wc"], st["w"], st["s"], st["we"], st["alpha"],
                                  st["beta"], s.k, F=s.F, s_out=out, workspace=ws, debug=debug)
+        elif block:
+            B.moe_block_forward(xb, st["g_pre"], st["wr"], st["w"], st["s"], st["g_post"], st["alpha"],
+                                st["beta"], s.k, F=s.F, s_out=out, workspace=ws, debug=debug)
         else:
             B.moe_layer_forward(xb, st["wr"], st["w"], st["s"], st["alpha"], st["beta"], s.k, F=s.F,
                                 s_out=out, workspace=ws, debug=debug)
@@ -276,8 +297,12 @@ def cpu_baseline(host, T, seconds):
     n = 0
     t0 = time.perf_counter()
     while True:
-        oracle.moe_forward(host.x[:T], host.router_w, host.w_packed, host.scales, host.alpha,
-                           host.beta, host.k, eps=host.eps)
+        if hasattr(host, "wc"):  # latent-width variant
+            oracle.latent_forward(host.x[:T], host.router_w, host.wc, host.w_packed, host.scales,
+                                  host.we, host.alpha, host.beta, host.k, eps=host.eps)
+        else:
+            oracle.moe_forward(host.x[:T], host.router_w, host.w_packed, host.scales, host.alpha,
+                               host.beta, host.k, eps=host.eps)
         n += 1
         el = time.perf_counter() - t0
         if el >= seconds:
@@ -307,13 +332,13 @@ def main():
         torch.cuda.synchronize()
         log(f"calibration copy: {n} bytes read, {n} bytes written")
         del src, dst
-    decode = args.workload.startswith("decode")
+    decode = args.workload.startswith("decode") or args.workload in ("latent4", "block4")
     steps = args.steps or (200 if decode else 20)
     warmup = args.warmup if args.warmup is not None else (10 if decode else 3)
     main_res, host, T = time_workload(args.workload, steps, warmup, device)
     also = {}
     for extra in [e for e in args.also.split(",") if e and e != args.workload]:
-        d2 = extra.startswith("decode") or extra == "latent4"
+        d2 = extra.startswith("decode") or extra in ("latent4", "block4")
         r, _, _ = time_workload(extra, 200 if d2 else 10, 10 if d2 else 2, device)
         also[extra] = r
         torch.cuda.empty_cache()
@@ -321,7 +346,7 @@ def main():
     if not args.no_cpu:
         log("timing the CPU oracle")
         cpu = cpu_baseline(host, T, args.cpu_seconds)
-    s = host.shape
+    s = host.w.expert_view().shape if args.workload in LATENT else host.shape
     line = {
         "metric": METRIC,
         "value": main_res["tokens_per_s"],
@@ -336,6 +361,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": WORKLOAD_TEXT[args.workload], "T": T, "d": s.d, "E": s.E,
+                   **({"D": host.w.D} if args.workload in LATENT else {}),
                    "k": s.k, "F": s.F, "weights": "MXFP4 (E2M1 + E8M0 per 32)",
                    "weight_sets": 4 if decode else 1,
                    "distinct_experts_mean": main_res["distinct_experts_mean"]},

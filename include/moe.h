@@ -246,6 +246,37 @@ int moe_latent_forward(const moe_latent_dims_t *dims, const void *x, const float
                        const float *beta, int32_t k, void *s_out, void *workspace,
                        size_t workspace_bytes, void *stream, const moe_debug_t *debug);
 
+/*
+ * The MoE block with its stream norms ("Muse Spark Open を段階的に分解する",
+ * section ③: the block reads a normalised copy of the residual stream s,
+ * its output is normalised again and mixed in by the gate
+ * s <- alpha * s + beta * norm(output)):
+ *
+ *   P.   x_n = bf16(s * r_s * gamma_pre), r_s = 1/sqrt(mean(s^2) + eps);
+ *   1-5. moe_layer_forward's steps on x_n (routing, experts, per-expert norms);
+ *   6.   y = sum_j w[t][j] * norm(o[t][j]) (fp32), and
+ *        s_out = bf16(alpha * s + beta * y * r_y * gamma_post),
+ *        r_y = 1/sqrt(mean(y^2) + eps).
+ *
+ * Reading: both norms are RMSNorm over d with a learned per-dimension gain
+ * and the layer's eps; x_n is handed to the router and the experts in bf16.
+ *
+ *   dims, k, router_w, expert_w_packed, scales, alpha, beta, s_out,
+ *   stream, debug   as moe_layer_forward (x is the stream s)
+ *   gamma_pre       fp32 [d], the gain of the norm in front of the block
+ *   gamma_post      fp32 [d], the gain of the norm on the block's output
+ *   workspace       moe_block_workspace_size bytes, 256-byte aligned
+ *
+ * Allocates nothing; same status codes and determinism as moe_layer_forward.
+ */
+size_t moe_block_workspace_size(const moe_dims_t *dims, int32_t k);
+
+int moe_block_forward(const moe_dims_t *dims, const void *x, const float *gamma_pre,
+                      const float *router_w, const uint8_t *expert_w_packed, const uint8_t *scales,
+                      const float *gamma_post, const float *alpha, const float *beta, int32_t k,
+                      void *s_out, void *workspace, size_t workspace_bytes, void *stream,
+                      const moe_debug_t *debug);
+
 /* Static, human-readable text for a status code. */
 const char *moe_status_string(int status);
 

@@ -77,6 +77,11 @@ def lib() -> C.CDLL:
         L.moe_latent_forward.argtypes = [C.POINTER(moe_latent_dims_t), P, P, P, P, P, P, P, P,
                                          C.c_int32, P, P, C.c_size_t, P, C.POINTER(moe_debug_t)]
         L.moe_latent_forward.restype = C.c_int
+        L.moe_block_workspace_size.argtypes = [C.POINTER(moe_dims_t), C.c_int32]
+        L.moe_block_workspace_size.restype = C.c_size_t
+        L.moe_block_forward.argtypes = [C.POINTER(moe_dims_t), P, P, P, P, P, P, P, P, C.c_int32, P,
+                                        P, C.c_size_t, P, C.POINTER(moe_debug_t)]
+        L.moe_block_forward.restype = C.c_int
         L.moe_status_string.argtypes = [C.c_int]
         L.moe_status_string.restype = C.c_char_p
         _lib = L
@@ -249,6 +254,48 @@ def moe_latent_forward(x, router_w, w_narrow, expert_w_packed, scales, w_widen, 
                                   C.byref(dbg) if dbg is not None else None)
     if rc != MOE_OK:
         raise MoeError(rc, "moe_latent_forward")
+    return s_out
+
+
+def moe_block_workspace_size(T, d, E, F, k, eps=1e-6) -> int:
+    return int(lib().moe_block_workspace_size(C.byref(_dims(T, d, E, F, eps)), int(k)))
+
+
+def moe_block_forward(x, gamma_pre, router_w, expert_w_packed, scales, gamma_post, alpha, beta, k, *,
+                      F=None, eps=1e-6, s_out=None, workspace=None, stream=None, debug=None):
+    """The block with its stream norms; returns s_out (bf16 [T][d]).
+
+    x (the stream) bf16 [T][d]; gamma_pre, gamma_post, alpha, beta fp32 [d];
+    router_w and the packed experts as moe_layer_forward.
+    """
+    T, d = x.shape
+    E = router_w.shape[0]
+    if F is None:
+        F = expert_w_packed.shape[1] * 2 // (3 * d)
+    _check(x, "x", torch.bfloat16, (T, d))
+    _check(gamma_pre, "gamma_pre", torch.float32, (d,))
+    _check(router_w, "router_w", torch.float32, (E, d))
+    _check(expert_w_packed, "expert_w_packed", torch.uint8, (E, 3 * d * F // 2))
+    _check(scales, "scales", torch.uint8, (E, 3 * d * F // 32))
+    _check(gamma_post, "gamma_post", torch.float32, (d,))
+    _check(alpha, "alpha", torch.float32, (d,))
+    _check(beta, "beta", torch.float32, (d,))
+    if s_out is None:
+        s_out = torch.empty_like(x)
+    _check(s_out, "s_out", torch.bfloat16, (T, d))
+    if workspace is None:
+        n = moe_block_workspace_size(T, d, E, F, k, eps)
+        if n == 0 and T != 0:
+            raise MoeError(MOE_ERR_SHAPE, "moe_block_workspace_size")
+        workspace = torch.empty(max(n, 256), dtype=torch.uint8, device=x.device)
+    dbg = _debug_struct(debug)
+    rc = lib().moe_block_forward(C.byref(_dims(T, d, E, F, eps)), _ptr(x), _ptr(gamma_pre),
+                                 _ptr(router_w), _ptr(expert_w_packed), _ptr(scales), _ptr(gamma_post),
+                                 _ptr(alpha), _ptr(beta), int(k), _ptr(s_out), _ptr(workspace),
+                                 workspace.numel(), _stream(stream),
+                                 C.byref(dbg) if dbg is not None else None)
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_block_forward")
     return s_out
 
 

@@ -110,6 +110,28 @@ static hipEvent_t stage_event(const moe_debug_t *debug, int stage, bool begin)
     return static_cast<hipEvent_t>(begin ? debug->stage_begin[stage] : debug->stage_end[stage]);
 }
 
+// The routing copies a caller asked for in `debug` (device to device, async).
+static hipError_t copy_debug(const moe_debug_t *debug, const Workspace &ws, const Shape &s,
+                             hipStream_t st)
+{
+    const size_t S4 = sizeof(int32_t) * (size_t)s.S();
+    const struct {
+        void *dst;
+        const void *src;
+        size_t n;
+    } cp[5] = {{debug->ids, ws.ids, S4},
+               {debug->weights, ws.wts, S4},
+               {debug->offsets, ws.offsets, sizeof(int32_t) * (size_t)(s.E + 1)},
+               {debug->perm, ws.perm, S4},
+               {debug->inv, ws.inv, S4}};
+    for (const auto &c : cp)
+        if (c.dst) {
+            const hipError_t e = hipMemcpyAsync(c.dst, c.src, c.n, hipMemcpyDeviceToDevice, st);
+            if (e != hipSuccess) return e;
+        }
+    return hipSuccess;
+}
+
 static bool aligned16(std::initializer_list<const void *> ptrs)
 {
     for (const void *p : ptrs)
@@ -175,21 +197,7 @@ extern "C" int moe_layer_forward(const moe_dims_t *dims, const void *x, const fl
                [&] { return launch_combine(s, p, ws, xb, alpha, beta, out, st); }))
         return MOE_ERR_HIP;
 
-    if (debug) {
-        const size_t S4 = sizeof(int32_t) * (size_t)s.S();
-        struct {
-            void *dst;
-            const void *src;
-            size_t n;
-        } cp[5] = {{debug->ids, ws.ids, S4},
-                   {debug->weights, ws.wts, S4},
-                   {debug->offsets, ws.offsets, sizeof(int32_t) * (size_t)(s.E + 1)},
-                   {debug->perm, ws.perm, S4},
-                   {debug->inv, ws.inv, S4}};
-        for (auto &c : cp)
-            if (c.dst && hipMemcpyAsync(c.dst, c.src, c.n, hipMemcpyDeviceToDevice, st) != hipSuccess)
-                return MOE_ERR_HIP;
-    }
+    if (debug && copy_debug(debug, ws, s, st) != hipSuccess) return MOE_ERR_HIP;
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
@@ -324,21 +332,103 @@ extern "C" int moe_latent_forward(const moe_latent_dims_t *dims, const void *x,
         !stage(MOE_STAGE_COMBINE, widen))
         return MOE_ERR_HIP;
 
-    if (debug) {
-        const size_t S4 = sizeof(int32_t) * (size_t)se.S();
-        struct {
-            void *dst;
-            const void *src;
-            size_t n;
-        } cp[5] = {{debug->ids, L.ws.ids, S4},
-                   {debug->weights, L.ws.wts, S4},
-                   {debug->offsets, L.ws.offsets, sizeof(int32_t) * (size_t)(se.E + 1)},
-                   {debug->perm, L.ws.perm, S4},
-                   {debug->inv, L.ws.inv, S4}};
-        for (auto &c : cp)
-            if (c.dst && hipMemcpyAsync(c.dst, c.src, c.n, hipMemcpyDeviceToDevice, st) != hipSuccess)
-                return MOE_ERR_HIP;
-    }
+    if (debug && copy_debug(debug, L.ws, se, st) != hipSuccess) return MOE_ERR_HIP;
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+// ---- the block with its stream norms -------------------------------------------
+
+namespace moe {
+
+// The layer's workspace, then x_n (bf16 [T][d]) and y (fp32 [T][d]).
+struct BlockWorkspace {
+    Workspace ws;
+    uint16_t *xn;
+    float *y;
+    size_t bytes;
+};
+
+static BlockWorkspace carve_block(const Shape &s, void *base)
+{
+    BlockWorkspace B;
+    B.ws = carve_workspace(s, base);
+    size_t off = B.ws.bytes;
+    char *b = static_cast<char *>(base);
+    B.xn = (uint16_t *)(b ? b + off : nullptr);
+    off += align256(sizeof(uint16_t) * (size_t)s.T * s.d);
+    B.y = (float *)(b ? b + off : nullptr);
+    off += align256(sizeof(float) * (size_t)s.T * s.d);
+    B.bytes = off;
+    return B;
+}
+
+}  // namespace moe
+
+extern "C" size_t moe_block_workspace_size(const moe_dims_t *dims, int32_t k)
+{
+    if (!dims || !shape_ok(dims, k)) return 0;
+    return carve_block(to_shape(dims, k), nullptr).bytes;
+}
+
+extern "C" int moe_block_forward(const moe_dims_t *dims, const void *x, const float *gamma_pre,
+                                 const float *router_w, const uint8_t *expert_w_packed,
+                                 const uint8_t *scales, const float *gamma_post, const float *alpha,
+                                 const float *beta, int32_t k, void *s_out, void *workspace,
+                                 size_t workspace_bytes, void *stream, const moe_debug_t *debug)
+{
+    if (!dims) return MOE_ERR_NULL;
+    if (!shape_ok(dims, k)) return MOE_ERR_SHAPE;
+    if (dims->T == 0) return MOE_OK;
+    if (!x || !gamma_pre || !router_w || !expert_w_packed || !scales || !gamma_post || !alpha ||
+        !beta || !s_out || !workspace)
+        return MOE_ERR_NULL;
+    if (!aligned16({x, gamma_pre, router_w, expert_w_packed, scales, gamma_post, alpha, beta, s_out}))
+        return MOE_ERR_ALIGN;
+    const Shape s = to_shape(dims, k);
+    if (workspace_bytes < carve_block(s, nullptr).bytes) return MOE_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return MOE_ERR_WORKSPACE;
+    int rc = check_arch();
+    if (rc != MOE_OK) return rc;
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const BlockWorkspace B = carve_block(s, workspace);
+    const Plan p = make_plan(s);
+    const uint16_t *xb = static_cast<const uint16_t *>(x);
+    (void)hipGetLastError();
+
+    auto mark = [&](void *const *evs, int stage) -> bool {
+        if (!debug || !evs[stage]) return true;
+        return hipEventRecord(static_cast<hipEvent_t>(evs[stage]), st) == hipSuccess;
+    };
+    auto stage = [&](int id, auto &&fn) -> bool {
+        if (!mark(debug ? debug->stage_begin : nullptr, id)) return false;
+        if (fn() != hipSuccess) return false;
+        return mark(debug ? debug->stage_end : nullptr, id);
+    };
+    auto ok = [](hipError_t e) { return e == hipSuccess; };
+    // the router reads (and, per plan, splits) the normalised copy
+    auto route = [&]() -> hipError_t {
+        hipError_t e = launch_prenorm(xb, gamma_pre, B.xn, s.T, s.d, s.eps, st);
+        if (e != hipSuccess) return e;
+        return launch_router(s, p, B.ws, B.xn, router_w, st);
+    };
+    auto finish = [&]() -> hipError_t {
+        hipError_t e = launch_combine_sum_f32(s, p, B.ws, B.y, st);
+        if (e != hipSuccess) return e;
+        return launch_postnorm_gate(xb, B.y, gamma_post, alpha, beta, static_cast<uint16_t *>(s_out),
+                                    s.T, s.d, s.eps, st);
+    };
+    if (!stage(MOE_STAGE_ROUTER, route) ||
+        !stage(MOE_STAGE_TOPK, [&] { return launch_topk(s, p, B.ws, st); }) ||
+        !stage(MOE_STAGE_GROUP, [&] { return launch_group(s, p, B.ws, st); }) ||
+        !ok(launch_gemm1(s, p, B.ws, B.xn, expert_w_packed, scales, st,
+                         stage_event(debug, MOE_STAGE_GEMM1, true),
+                         stage_event(debug, MOE_STAGE_GEMM1, false))) ||
+        !stage(MOE_STAGE_GEMM2, [&] { return launch_gemm2(s, p, B.ws, expert_w_packed, scales, st); }) ||
+        !stage(MOE_STAGE_COMBINE, finish))
+        return MOE_ERR_HIP;
+
+    if (debug && copy_debug(debug, B.ws, s, st) != hipSuccess) return MOE_ERR_HIP;
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 

@@ -23,14 +23,17 @@ constexpr int kCombineCols = 2048;  // columns per workgroup (8 per thread)
 
 // SLOT: o and the o^2 partial sums are stored in slot order (row t*k + j is
 // slot j of token t); otherwise in the grouped order, found through inv.
-// GATE: s_out = bf16(alpha * x + beta * y); otherwise s_out = bf16(y) (the
-// latent-width variant widens y before its gate).
-template <bool SLOT, bool GATE>
+// OUT: kOutGate s_out = bf16(alpha * x + beta * y); kOutBf16 s_out = bf16(y)
+// (the latent-width variant widens y before its gate); kOutF32 y_out = y
+// (the block variant normalises y before its gate).
+enum { kOutGate = 0, kOutBf16 = 1, kOutF32 = 2 };
+template <bool SLOT, int OUT>
 __global__ __launch_bounds__(256) void combine_kernel(
     const uint16_t *x, const float *__restrict__ wts, const int32_t *__restrict__ inv,
     const uint16_t *__restrict__ o, const float *__restrict__ ssq, const float *__restrict__ alpha,
-    const float *__restrict__ beta, uint16_t *s_out, int d, int k, int P, float eps)
+    const float *__restrict__ beta, uint16_t *s_out, float *y_out, int d, int k, int P, float eps)
 {
+    constexpr bool GATE = OUT == kOutGate;
     constexpr int JB = SLOT ? kSlotBatch : kMaxK;  // slots per pass over the row
     __shared__ float coef[JB];
     __shared__ int32_t row[JB];
@@ -93,7 +96,12 @@ __global__ __launch_bounds__(256) void combine_kernel(
             }
         }
     }
-    if (!GATE && act) {
+    if (OUT == kOutF32 && act) {
+        float4 *yo = reinterpret_cast<float4 *>(y_out + (int64_t)t * d + c0);
+        yo[0] = make_float4(y[0], y[1], y[2], y[3]);
+        yo[1] = make_float4(y[4], y[5], y[6], y[7]);
+    }
+    if (OUT == kOutBf16 && act) {
         uint32_t ow[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -115,30 +123,137 @@ __global__ __launch_bounds__(256) void combine_kernel(
     }
 }
 
-hipError_t launch_combine(const Shape &s, const Plan &p, const Workspace &ws, const uint16_t *x,
-                          const float *alpha, const float *beta, uint16_t *s_out, hipStream_t st)
+template <int OUT>
+static hipError_t combine_launch(const Shape &s, const Plan &p, const Workspace &ws, const uint16_t *x,
+                                 const float *alpha, const float *beta, uint16_t *s_out, float *y_out,
+                                 hipStream_t st)
 {
     dim3 grid(s.T, (s.d + kCombineCols - 1) / kCombineCols);
     // the few-row down kernel stores in slot order, the tiled ones in the grouped order
     if (p.tiled)
-        combine_kernel<false, true><<<grid, 256, 0, st>>>(x, ws.wts, ws.inv, ws.o, ws.ssq, alpha, beta,
-                                                          s_out, s.d, s.k, s.d / p.ssq_cols, s.eps);
+        combine_kernel<false, OUT><<<grid, 256, 0, st>>>(x, ws.wts, ws.inv, ws.o, ws.ssq, alpha, beta,
+                                                         s_out, y_out, s.d, s.k, s.d / p.ssq_cols, s.eps);
     else
-        combine_kernel<true, true><<<grid, 256, 0, st>>>(x, ws.wts, ws.inv, ws.o, ws.ssq, alpha, beta,
-                                                         s_out, s.d, s.k, s.d / p.ssq_cols, s.eps);
+        combine_kernel<true, OUT><<<grid, 256, 0, st>>>(x, ws.wts, ws.inv, ws.o, ws.ssq, alpha, beta,
+                                                        s_out, y_out, s.d, s.k, s.d / p.ssq_cols, s.eps);
     return hipGetLastError();
+}
+
+hipError_t launch_combine(const Shape &s, const Plan &p, const Workspace &ws, const uint16_t *x,
+                          const float *alpha, const float *beta, uint16_t *s_out, hipStream_t st)
+{
+    return combine_launch<kOutGate>(s, p, ws, x, alpha, beta, s_out, nullptr, st);
 }
 
 hipError_t launch_combine_sum(const Shape &s, const Plan &p, const Workspace &ws, uint16_t *y,
                               hipStream_t st)
 {
-    dim3 grid(s.T, (s.d + kCombineCols - 1) / kCombineCols);
-    if (p.tiled)
-        combine_kernel<false, false><<<grid, 256, 0, st>>>(nullptr, ws.wts, ws.inv, ws.o, ws.ssq, nullptr,
-                                                           nullptr, y, s.d, s.k, s.d / p.ssq_cols, s.eps);
-    else
-        combine_kernel<true, false><<<grid, 256, 0, st>>>(nullptr, ws.wts, ws.inv, ws.o, ws.ssq, nullptr,
-                                                          nullptr, y, s.d, s.k, s.d / p.ssq_cols, s.eps);
+    return combine_launch<kOutBf16>(s, p, ws, nullptr, nullptr, nullptr, y, nullptr, st);
+}
+
+hipError_t launch_combine_sum_f32(const Shape &s, const Plan &p, const Workspace &ws, float *y,
+                                  hipStream_t st)
+{
+    return combine_launch<kOutF32>(s, p, ws, nullptr, nullptr, nullptr, nullptr, y, st);
+}
+
+// ---- the block's stream norms ([MS] section ③) --------------------------------
+// One workgroup per token row: the row's sum of squares in a fixed order
+// (per-thread partials, wave sums, then the four waves in order), so the
+// result does not depend on scheduling.
+__device__ __forceinline__ float block_row_sumsq(float part)
+{
+    __shared__ float wsq[4];
+    const float v = wave_sum(part);
+    if ((threadIdx.x & 63) == 0) wsq[threadIdx.x >> 6] = v;
+    __syncthreads();
+    return (wsq[0] + wsq[1]) + (wsq[2] + wsq[3]);
+}
+
+// x_n = bf16(x * r * gamma), r = 1 / sqrt(mean(x^2) + eps); 8 columns per
+// thread and pass.
+__global__ __launch_bounds__(256) void prenorm_kernel(const uint16_t *__restrict__ x,
+                                                      const float *__restrict__ gamma,
+                                                      uint16_t *__restrict__ xn, int d, float eps)
+{
+    const int t = blockIdx.x;
+    const uint4 *row = reinterpret_cast<const uint4 *>(x + (int64_t)t * d);
+    float part = 0.f;
+    for (int c = threadIdx.x; c < d / 8; c += 256) {
+        const uint4 v = row[c];
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float a = __uint_as_float(w[i] << 16), b = __uint_as_float(w[i] & 0xFFFF0000u);
+            part = fmaf(a, a, part);
+            part = fmaf(b, b, part);
+        }
+    }
+    const float r = 1.0f / sqrtf(block_row_sumsq(part) / (float)d + eps);
+    uint4 *out = reinterpret_cast<uint4 *>(xn + (int64_t)t * d);
+    for (int c = threadIdx.x; c < d / 8; c += 256) {
+        const uint4 v = row[c];
+        const float4 g0 = *reinterpret_cast<const float4 *>(gamma + 8 * c);
+        const float4 g1 = *reinterpret_cast<const float4 *>(gamma + 8 * c + 4);
+        const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        uint32_t ow[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float a = __uint_as_float(w[i] << 16) * r * gv[2 * i];
+            const float b = __uint_as_float(w[i] & 0xFFFF0000u) * r * gv[2 * i + 1];
+            ow[i] = (uint32_t)f32_to_bf16(a) | (uint32_t)f32_to_bf16(b) << 16;
+        }
+        out[c] = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+    }
+}
+
+// s_out = bf16(alpha * x + beta * y * r * gamma), r = 1 / sqrt(mean(y^2) + eps).
+// s_out may be x: each thread reads its x elements before writing them.
+__global__ __launch_bounds__(256) void postnorm_gate_kernel(
+    const uint16_t *x, const float *__restrict__ y, const float *__restrict__ gamma,
+    const float *__restrict__ alpha, const float *__restrict__ beta, uint16_t *s_out, int d, float eps)
+{
+    const int t = blockIdx.x;
+    const float4 *yr = reinterpret_cast<const float4 *>(y + (int64_t)t * d);
+    float part = 0.f;
+    for (int c = threadIdx.x; c < d / 4; c += 256) {
+        const float4 v = yr[c];
+        part = fmaf(v.x, v.x, part);
+        part = fmaf(v.y, v.y, part);
+        part = fmaf(v.z, v.z, part);
+        part = fmaf(v.w, v.w, part);
+    }
+    const float r = 1.0f / sqrtf(block_row_sumsq(part) / (float)d + eps);
+    const uint2 *xr = reinterpret_cast<const uint2 *>(x + (int64_t)t * d);
+    uint2 *out = reinterpret_cast<uint2 *>(s_out + (int64_t)t * d);
+    for (int c = threadIdx.x; c < d / 4; c += 256) {
+        const float4 v = yr[c];
+        const uint2 xv = xr[c];
+        const float4 g = *reinterpret_cast<const float4 *>(gamma + 4 * c);
+        const float4 a = *reinterpret_cast<const float4 *>(alpha + 4 * c);
+        const float4 b = *reinterpret_cast<const float4 *>(beta + 4 * c);
+        const float s0 = fmaf(b.x, v.x * r * g.x, a.x * __uint_as_float(xv.x << 16));
+        const float s1 = fmaf(b.y, v.y * r * g.y, a.y * __uint_as_float(xv.x & 0xFFFF0000u));
+        const float s2 = fmaf(b.z, v.z * r * g.z, a.z * __uint_as_float(xv.y << 16));
+        const float s3 = fmaf(b.w, v.w * r * g.w, a.w * __uint_as_float(xv.y & 0xFFFF0000u));
+        out[c] = make_uint2((uint32_t)f32_to_bf16(s0) | (uint32_t)f32_to_bf16(s1) << 16,
+                            (uint32_t)f32_to_bf16(s2) | (uint32_t)f32_to_bf16(s3) << 16);
+    }
+}
+
+hipError_t launch_prenorm(const uint16_t *x, const float *gamma, uint16_t *xn, int T, int d, float eps,
+                          hipStream_t st)
+{
+    prenorm_kernel<<<T, 256, 0, st>>>(x, gamma, xn, d, eps);
+    return hipGetLastError();
+}
+
+hipError_t launch_postnorm_gate(const uint16_t *x, const float *y, const float *gamma,
+                                const float *alpha, const float *beta, uint16_t *s_out, int T, int d,
+                                float eps, hipStream_t st)
+{
+    postnorm_gate_kernel<<<T, 256, 0, st>>>(x, y, gamma, alpha, beta, s_out, d, eps);
     return hipGetLastError();
 }
 

@@ -157,6 +157,16 @@ hipError_t launch_combine(const Shape &s, const Plan &p, const Workspace &ws, co
 // Norms and weighted sum only: y = bf16(sum_j w_j * norm(o_j)) [T][d].
 hipError_t launch_combine_sum(const Shape &s, const Plan &p, const Workspace &ws, uint16_t *y,
                               hipStream_t st);
+// Norms and weighted sum only, fp32 y [T][d].
+hipError_t launch_combine_sum_f32(const Shape &s, const Plan &p, const Workspace &ws, float *y,
+                                  hipStream_t st);
+// The block's stream norms: x_n = bf16(x * rms(x)^-1 * gamma); s_out =
+// bf16(alpha * x + beta * y * rms(y)^-1 * gamma), one workgroup per row.
+hipError_t launch_prenorm(const uint16_t *x, const float *gamma, uint16_t *xn, int T, int d, float eps,
+                          hipStream_t st);
+hipError_t launch_postnorm_gate(const uint16_t *x, const float *y, const float *gamma,
+                                const float *alpha, const float *beta, uint16_t *s_out, int T, int d,
+                                float eps, hipStream_t st);
 // bf16 x -> FP8 hi/lo parts + E8M0 scales in the workspace (the streaming
 // gate/up kernel's input when the router does not split x itself).
 hipError_t launch_split_x_fp8(const Shape &s, const Workspace &ws, const uint16_t *x, hipStream_t st);

@@ -17,7 +17,7 @@ def test_exports_every_declared_function(L):
     names = B.declared_functions()
     assert set(names) == {"moe_layer_workspace_size", "moe_layer_forward", "moe_pack_weights",
                           "moe_dequant_mxfp4", "moe_status_string", "moe_latent_workspace_size",
-                          "moe_latent_forward"}
+                          "moe_latent_forward", "moe_block_workspace_size", "moe_block_forward"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -144,3 +144,42 @@ def test_latent_argument_errors():
         assert _latent_call(good, ptr={name: odd}) == B.MOE_ERR_ALIGN, name
     zero = B.moe_latent_dims_t(0, 512, 256, 8, 256, 1e-6)
     assert _latent_call(zero, null="x") == B.MOE_OK
+
+
+# -------------------------------------------------------- block with stream norms
+
+def test_block_workspace_size():
+    ws = B.moe_block_workspace_size
+    T = 4096
+    assert ws(T, 8192, 256, 2048, 8) >= B.moe_layer_workspace_size(T, 8192, 256, 2048, 8) + \
+        T * 8192 * 2 + T * 8192 * 4
+    assert ws(64, 250, 8, 512, 2) == 0
+    assert ws(64, 256, 8, 512, 9) == 0
+
+
+def _block_call(dims, k=2, ws_bytes=1 << 30, null=None, ws_ptr=1 << 20, ptr=None):
+    p = C.c_void_p(1 << 20)  # never dereferenced: every case below fails the checks first
+    names = ("x", "gamma_pre", "router_w", "w", "s", "gamma_post", "alpha", "beta", "s_out")
+    args = {n: p for n in names}
+    args["ws"] = C.c_void_p(ws_ptr)
+    if null:
+        args[null] = None
+    args.update(ptr or {})
+    return B.lib().moe_block_forward(C.byref(dims) if dims is not None else None,
+                                     *(args[n] for n in names[:8]), k, args["s_out"], args["ws"],
+                                     ws_bytes, None, None)
+
+
+def test_block_argument_errors():
+    good = B.moe_dims_t(64, 256, 8, 512, 1e-6)
+    assert _block_call(None) == B.MOE_ERR_NULL
+    names = ("x", "gamma_pre", "router_w", "w", "s", "gamma_post", "alpha", "beta", "s_out")
+    for name in names + ("ws",):
+        assert _block_call(good, null=name) == B.MOE_ERR_NULL, name
+    assert _block_call(B.moe_dims_t(64, 200, 8, 512, 1e-6)) == B.MOE_ERR_SHAPE
+    assert _block_call(good, k=9) == B.MOE_ERR_SHAPE
+    assert _block_call(good, ws_bytes=1024) == B.MOE_ERR_WORKSPACE
+    odd = C.c_void_p((1 << 20) + 8)
+    for name in names:
+        assert _block_call(good, ptr={name: odd}) == B.MOE_ERR_ALIGN, name
+    assert _block_call(B.moe_dims_t(0, 256, 8, 512, 1e-6), null="x") == B.MOE_OK
