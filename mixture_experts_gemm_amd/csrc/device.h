@@ -151,13 +151,34 @@ __device__ __forceinline__ void split_e4m3_block(const float *v, uint32_t *hi, u
 // of R, so bf16 values near the block maximum are exact after two parts and
 // nearly all after three (largest error seen on Gaussian, heavy-tailed and
 // outlier blocks: 2^-15 of the block maximum).  The hardware's scaled conversions do
-// the rounding (round to nearest even, verified on gfx950) and the inverse;
+// the rounding (round to nearest even, verified on gfx950) and the inverse
+// (cvt_f32x32_to_e2m3, cvt_e2m3_to_f32x32 below);
 // the 2x16 form places element i of its first operand at code 2i and of its
 // second at code 2i+1, so the even and odd elements are passed apart to get
 // the natural order (code j in bits 6j .. 6j+5, the MFMA operand layout).
 typedef int v6i_t __attribute__((__vector_size__(6 * sizeof(int))));
 typedef float v16f_t __attribute__((__vector_size__(16 * sizeof(float))));
 typedef float v32f_t __attribute__((__vector_size__(32 * sizeof(float))));
+
+// The two conversions are issued from inline asm with early-clobber outputs.
+// Through the compiler builtins the register allocator may give the result
+// registers an overlap with an input operand; on gfx950 that gave results
+// that changed from run to run (measured: about 1e-4 of the third parts of a
+// 160 MB split differed between two identical calls).  Here the result
+// registers never overlap the inputs.
+__device__ __forceinline__ v6i_t cvt_f32x32_to_e2m3(const v16f_t &even, const v16f_t &odd, float scale)
+{
+    v6i_t r;
+    asm volatile("v_cvt_scalef32_2xpk16_fp6_f32 %0, %1, %2, %3"
+                 : "=&v"(r) : "v"(even), "v"(odd), "v"(scale));
+    return r;
+}
+__device__ __forceinline__ v32f_t cvt_e2m3_to_f32x32(const v6i_t &codes, float scale)
+{
+    v32f_t r;
+    asm volatile("v_cvt_scalef32_pk32_f32_fp6 %0, %1, %2" : "=&v"(r) : "v"(codes), "v"(scale));
+    return r;
+}
 
 __device__ __forceinline__ void split_e2m3x3_block(float (&r)[32], uint32_t (&code)[3][6],
                                                    uint32_t (&sc)[3])
@@ -177,8 +198,8 @@ __device__ __forceinline__ void split_e2m3x3_block(float (&r)[32], uint32_t (&co
             ev[i] = r[2 * i];
             od[i] = r[2 * i + 1];
         }
-        const v6i_t c = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(ev, od, scale);
-        const v32f_t q = __builtin_amdgcn_cvt_scalef32_pk32_f32_fp6(c, scale);
+        const v6i_t c = cvt_f32x32_to_e2m3(ev, od, scale);
+        const v32f_t q = cvt_e2m3_to_f32x32(c, scale);
 #pragma unroll
         for (int i = 0; i < 32; ++i) r[i] -= q[i];
 #pragma unroll

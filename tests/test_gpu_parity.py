@@ -217,6 +217,24 @@ def test_in_place_and_deterministic():
     np.testing.assert_array_equal(bf16_bits(xin), outs[0])
 
 
+def test_deterministic_at_prefill_size():
+    """Two calls with fresh workspaces give bitwise equal outputs on the tiled
+    path with FP6 activations (the split once drew conversion result registers
+    overlapping their inputs, which changed results from call to call)."""
+    from mixture_experts_gemm_amd import binding as B
+    L = synth.make_layer("prefill")
+    dev = upload(L)
+    s = L.shape
+    _say("determinism at T=4096")
+    outs = []
+    for _ in range(2):
+        n = B.moe_layer_workspace_size(s.T, s.d, s.E, s.F, s.k)
+        ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
+        outs.append(run_layer(L, dev, debug=False, workspace=ws)[0])
+        del ws
+    assert np.array_equal(outs[0], outs[1]), int((outs[0] != outs[1]).sum())
+
+
 def test_down_scale_invariance():
     L = synth.make_layer("tiny")
     _say("scale invariance")
@@ -284,10 +302,13 @@ def test_ep_share_full_size(name, n):
 def test_stack_of_four_layers():
     """Chained layers: each layer's bf16 output is the next layer's input.
 
-    The oracle runs its own chain (its bf16 rounding between layers); GPU and
-    oracle inputs of layer 2+ then differ by bf16 rounding, so routing must
-    agree exactly only where the oracle's top-(k+1) margin is >= 1e-2, and
-    errors are measured on tokens whose routing agreed at every layer.
+    Routing of every layer is checked on the input the GPU actually saw: the
+    oracle's router on the GPU chain's input rows must give the same experts
+    wherever its score gaps (ranks 1..k+1) are at least 1e-4, the margin the
+    generator guarantees for fresh tokens.  The outputs are compared with the
+    oracle's own chain (its own bf16 rounding between layers), on tokens whose
+    routing agreed with that chain at every layer; the error bound grows with
+    depth.
     """
     w = synth.WORKLOADS["stack"]
     T = w.shape.T
@@ -304,18 +325,24 @@ def test_stack_of_four_layers():
         if layer == 0:
             ref_in = L.x[tokens]
             _check_routing(L, dbg, "stack layer 0")
+        # the router stage on the GPU's own input rows
+        gin = bf16_bits(xin)[tokens]
+        sc_g = oracle.router_scores(gin, L.router_w)
+        ids_g, _ = oracle.topk_softmax(sc_g, L.k)
+        top_g = -np.sort(-sc_g.astype(np.float64), axis=1)[:, : L.k + 1]
+        margin_g = (top_g[:, :-1] - top_g[:, 1:]).min(axis=1)
+        same_g = np.all(dbg["ids"][tokens] == ids_g, axis=1)
+        assert np.all(same_g[margin_g >= 1e-4]), f"layer {layer}: routing differs on the GPU's input"
+        # agreement with the oracle's own chain
         sc = oracle.router_scores(ref_in, L.router_w)
         ids_ref, _ = oracle.topk_softmax(sc, L.k)
-        top = -np.sort(-sc.astype(np.float64), axis=1)[:, : L.k + 1]
-        margin = (top[:, :-1] - top[:, 1:]).min(axis=1)
-        same = np.all(dbg["ids"][tokens] == ids_ref, axis=1)
-        assert np.all(same[margin >= 1e-2]), f"layer {layer}: confident routing differs"
-        agree &= same
+        agree &= np.all(dbg["ids"][tokens] == ids_ref, axis=1)
         s_ref, _, _ = oracle.moe_forward(ref_in, L.router_w, L.w_packed, L.scales, L.alpha,
                                          L.beta, L.k, eps=L.eps)
         got = synth.bf16_bits_to_f32(out[tokens]).astype(np.float64)
         m = metrics(got[agree], s_ref[agree])
         _say("stack layer", layer, "agree", int(agree.sum()), "of", len(tokens), m)
+        assert agree.sum() >= len(tokens) // 2, (layer, int(agree.sum()))
         bound = 5e-3 if layer == 0 else 2e-2
         assert m["normwise"] <= bound and m["rel_max"] <= 4 * bound, (layer, m)
         ref_in = oracle.doubles_to_bf16(s_ref)
