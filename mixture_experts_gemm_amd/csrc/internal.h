@@ -68,15 +68,22 @@ inline Plan make_plan(const Shape &s)
     return p;
 }
 
+// Workgroup tile of the many-token router: 128 tokens x 128 experts, or
+// 256 tokens x 64 experts when there are at most 64 experts.
+inline int router_tile_experts(int E) { return E <= 64 ? 64 : 128; }
+inline int router_tile_tokens(int E) { return E <= 64 ? 256 : 128; }
+
 // Slices of d the many-token router splits its sums into (partial score
-// planes added by top-k): enough workgroups of 128 tokens x 128 experts to
-// fill the device, at most 8, each slice a multiple of 32 long.
+// planes added by top-k): enough workgroups to fill the device (at least
+// 256, at most 512 when possible), at most 32 slices, each a multiple of 32
+// long.
 inline int router_splits(const Shape &s)
 {
     if (s.T <= 32) return 1;
-    const int64_t tiles = (int64_t)((s.T + 127) / 128) * ((s.E + 127) / 128);
+    const int tt = router_tile_tokens(s.E), te = router_tile_experts(s.E);
+    const int64_t tiles = (int64_t)((s.T + tt - 1) / tt) * ((s.E + te - 1) / te);
     int ks = 1;
-    while (ks < 8 && tiles * ks * 2 <= 512 && (s.d / (ks * 2)) % 32 == 0) ks *= 2;
+    while (ks < 32 && tiles * ks * 2 <= 512 && (s.d / (ks * 2)) % 32 == 0) ks *= 2;
     return ks;
 }
 

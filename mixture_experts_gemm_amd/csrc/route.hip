@@ -107,7 +107,6 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(const uint16_t *__rest
 // into registers one 32-wide K step ahead.  Slice s writes its partial sums
 // to part[s][T][E]; top-k adds the slices in order.
 // ---------------------------------------------------------------------------
-constexpr int kRtT = 128, kRtE = 128;
 
 __device__ __forceinline__ void split3_trunc(const float4 &a, const float4 &b, uint4 &hi, uint4 &mid,
                                              uint4 &lo)
@@ -128,15 +127,21 @@ __device__ __forceinline__ void split3_trunc(const float4 &a, const float4 &b, u
     lo = make_uint4(pk(l[0], l[1]), pk(l[2], l[3]), pk(l[4], l[5]), pk(l[6], l[7]));
 }
 
+// WE waves along the experts, 4/WE along the tokens: a workgroup covers
+// router_tile_tokens(E) x router_tile_experts(E) (internal.h); with few
+// experts (E <= 64) all four waves take tokens, so none computes only
+// padding experts.
+template <int WE>
 __global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t *__restrict__ x,
                                                           const float *__restrict__ wr,
                                                           float *__restrict__ part, int T, int d,
                                                           int E, int kslice)
 {
+    constexpr int WT = 4 / WE;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int m = lane & 15, g = lane >> 4;
-    const int t0 = blockIdx.x * kRtT + (wv & 1) * 64;
-    const int e0 = blockIdx.y * kRtE + (wv >> 1) * 64;
+    const int t0 = blockIdx.x * (64 * WT) + (wv % WT) * 64;
+    const int e0 = blockIdx.y * (64 * WE) + (wv / WT) * 64;
     const int k0 = blockIdx.z * kslice;
     // rows past T / E are computed on the last valid row and never stored
     const uint16_t *xp[4];
@@ -214,8 +219,12 @@ hipError_t launch_router(const Shape &s, const Plan &p, const Workspace &ws, con
             x, wr, ws.scores, s.T, s.d, s.E, xhi, ws.xlo, ws.xshi, ws.xslo);
     } else {
         const int ks = router_splits(s);
-        dim3 grid((s.T + kRtT - 1) / kRtT, (s.E + kRtE - 1) / kRtE, ks);
-        router_gemm_kernel<<<grid, 256, 0, st>>>(x, wr, ws.scores, s.T, s.d, s.E, s.d / ks);
+        const int tt = router_tile_tokens(s.E), te = router_tile_experts(s.E);
+        dim3 grid((s.T + tt - 1) / tt, (s.E + te - 1) / te, ks);
+        if (te == 64)
+            router_gemm_kernel<1><<<grid, 256, 0, st>>>(x, wr, ws.scores, s.T, s.d, s.E, s.d / ks);
+        else
+            router_gemm_kernel<2><<<grid, 256, 0, st>>>(x, wr, ws.scores, s.T, s.d, s.E, s.d / ks);
     }
     if (p.tiled) {
         hipError_t e = hipGetLastError();
@@ -295,8 +304,16 @@ __device__ void topk_row(const float *__restrict__ l, int E, int k, int32_t *__r
         const int e = lane + 64 * q;
         float x = -INFINITY;
         if (e < E) {
-            x = l[e];
-            for (int sp = 1; sp < nsplit; ++sp) x += l[sp * stride + e];
+            // planes in groups of 8 loads issued together, added in slice order
+            x = 0.f;
+            for (int sp = 0; sp < nsplit; sp += 8) {
+                float v[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) v[i] = l[(int64_t)min(sp + i, nsplit - 1) * stride + e];
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    if (sp + i < nsplit) x = (sp + i == 0) ? v[i] : x + v[i];
+            }
         }
         key[q] = topk_key(x, e < E ? e : kNone);
     }
