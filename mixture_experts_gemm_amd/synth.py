@@ -49,7 +49,7 @@ import numpy as np
 
 # substream tags
 (_TAG_X, _TAG_WR, _TAG_W, _TAG_S, _TAG_AB, _TAG_ZIPF, _TAG_REDRAW, _TAG_WC, _TAG_WE,
- _TAG_GAIN) = range(10)
+ _TAG_GAIN, _TAG_S16, _TAG_GS) = range(12)
 
 SCALE_LO, SCALE_HI = 119, 123          # E8M0 bytes: 2^-8 .. 2^-4
 GAP_DEFAULT = 1e-4
@@ -213,6 +213,53 @@ def make_experts(w: Workload, layer: int = 0, threads: int = 8,
     return W, S
 
 
+# ---------------------------------------------------------------------------
+# The 16-block format ("Muse Spark Open を段階的に分解する", section ⑪: one
+# small scale shared by 16 values, about 4.5 bits a value), read as one E4M3
+# byte per 16 values and one fp32 scale per matrix.  Any workload above can
+# be drawn in it: x, the router, alpha / beta and the code bytes are the
+# workload's own; the scales are drawn instead of the E8M0 bytes:
+#   E4M3 bytes: exponent field uniform over 4..8 (2^-3 .. 2^1), mantissa
+#     uniform over 0..7, positive; with probability 1/32 a subnormal byte
+#     (0x00..0x07, 0x00 a zero block) and, independently, with probability
+#     1/32 the sign bit set;
+#   matrix scales: fp32 U(0.75, 1.25) * 2^-5,
+# so the weight magnitudes match the MXFP4 draw's (2^-8 .. 2^-4 per block).
+# ---------------------------------------------------------------------------
+NV_EXP_LO, NV_EXP_HI = 4, 8
+
+
+def _expert_scales16(seed: int, layer: int, e: int, n: int) -> np.ndarray:
+    g = _rng(seed, layer, _TAG_S16, e)
+    ex = g.integers(NV_EXP_LO, NV_EXP_HI + 1, size=n, dtype=np.uint8)
+    mt = g.integers(0, 8, size=n, dtype=np.uint8)
+    b = (ex << 3) | mt
+    sub = g.random(n) < 1.0 / 32
+    b[sub] = mt[sub]
+    neg = g.random(n) < 1.0 / 32
+    b[neg] |= 0x80
+    return b.astype(np.uint8)
+
+
+def make_experts_nv(w: Workload, layer: int = 0, threads: int = 8):
+    """Codes uint8 [E][3dF/2] (the workload's own), E4M3 scales uint8 [E][3dF/16],
+    matrix scales fp32 [E][3] (gate, up, down)."""
+    s = w.shape
+    nb, ns = s.expert_bytes, 3 * s.d * s.F // 16
+    W = np.empty((s.E, nb), dtype=np.uint8)
+    S = np.empty((s.E, ns), dtype=np.uint8)
+
+    def one(e):
+        W[e] = _expert_bytes(w.seed, layer, e, nb)
+        S[e] = _expert_scales16(w.seed, layer, e, ns)
+
+    with ThreadPoolExecutor(max(1, threads)) as ex:
+        list(ex.map(one, range(s.E)))
+    g = _rng(w.seed, layer, _TAG_GS, 0)
+    G = ((g.random((s.E, 3)) * 0.5 + 0.75) * 2.0 ** -5).astype(np.float32)
+    return W, S, G
+
+
 def make_gates(w: Workload, layer: int = 0):
     g = _rng(w.seed, layer, _TAG_AB, 0)
     alpha = (g.random(w.shape.d, dtype=np.float32) + np.float32(0.5)).astype(np.float32)
@@ -253,6 +300,35 @@ def make_layer(name_or_w, layer: int = 0, T: int | None = None, gap: float = GAP
     W, S = make_experts(w, layer, threads=threads)
     a, b = make_gates(w, layer)
     return LayerInputs(s, x, wr, W, S, a, b, s.k)
+
+
+@dataclasses.dataclass
+class NvLayerInputs:
+    shape: Shape
+    x: np.ndarray          # uint16 bf16 bits [T][d]
+    router_w: np.ndarray   # float32 [E][d]
+    w_packed: np.ndarray   # uint8 [E][3dF/2] codes
+    scales16: np.ndarray   # uint8 [E][3dF/16] E4M3
+    gscale: np.ndarray     # float32 [E][3]
+    alpha: np.ndarray
+    beta: np.ndarray
+    k: int
+    eps: float = 1e-6
+
+
+def make_layer_nv(name_or_w, layer: int = 0, T: int | None = None, gap: float = GAP_DEFAULT,
+                  threads: int = 8, with_tokens: bool = True) -> NvLayerInputs:
+    """A workload's layer with its expert weights drawn in the 16-block format."""
+    w = WORKLOADS[name_or_w] if isinstance(name_or_w, str) else name_or_w
+    s = w.shape
+    if T is not None:
+        s = dataclasses.replace(s, T=T)
+        w = dataclasses.replace(w, shape=s)
+    wr = make_router(w, layer)
+    x = make_tokens(w, wr, layer, gap=gap) if with_tokens else np.zeros((0, s.d), np.uint16)
+    W, S, G = make_experts_nv(w, layer, threads=threads)
+    a, b = make_gates(w, layer)
+    return NvLayerInputs(s, x, wr, W, S, G, a, b, s.k)
 
 
 def custom_workload(T: int, d: int, E: int, k: int, F: int, seed: int, zipf: bool = False) -> Workload:

@@ -40,6 +40,15 @@ def lib():
         L.oracle_e8m0.restype = C.c_double
         L.oracle_dequant_rows.argtypes = [_I64, _I64, _P, _P, _P]
         L.oracle_dequant_rows.restype = None
+        L.oracle_e4m3.argtypes = [C.c_uint]
+        L.oracle_e4m3.restype = C.c_double
+        L.oracle_dequant_rows_nv.argtypes = [_I64, _I64, _P, _P, C.c_double, _P]
+        L.oracle_dequant_rows_nv.restype = None
+        L.oracle_expert_nv.argtypes = [_I, _I, _P, _P, _P, _P, C.c_double, _P, _P]
+        L.oracle_expert_nv.restype = C.c_double
+        L.oracle_moe_forward_nv.argtypes = [_I, _I, _I, _I, _I, C.c_double, _P, _P, _P, _P, _P,
+                                            _P, _P, _I, _P, _P, _P, _P]
+        L.oracle_moe_forward_nv.restype = _I
         L.oracle_router_scores.argtypes = [_I, _I, _I, _P, _P, _P]
         L.oracle_router_scores.restype = None
         L.oracle_topk_softmax.argtypes = [_I, _I, _I, _P, _P, _P]
@@ -101,6 +110,35 @@ def dequant_rows(codes: np.ndarray, scales: np.ndarray, K: int) -> np.ndarray:
     out = np.empty((rows, K), dtype=np.float64)
     lib().oracle_dequant_rows(rows, K, _p(codes), _p(scales), _p(out))
     return out
+
+
+def e4m3(b: int) -> float:
+    """NV1: one E4M3 scale byte -> its value."""
+    return lib().oracle_e4m3(int(b))
+
+
+def dequant_rows_nv(codes: np.ndarray, scales16: np.ndarray, K: int, g: float = 1.0) -> np.ndarray:
+    """NV2 decode: rows of K elements in the 16-block format -> float64 [rows][K]."""
+    codes = _c(codes, np.uint8)
+    scales16 = _c(scales16, np.uint8)
+    rows = codes.size // (K // 2)
+    assert codes.size == rows * K // 2 and scales16.size == rows * K // 16
+    out = np.empty((rows, K), dtype=np.float64)
+    lib().oracle_dequant_rows_nv(rows, K, _p(codes), _p(scales16), float(g), _p(out))
+    return out
+
+
+def expert_nv(w_e, s16_e, gs_e, x, d: int, F: int, eps: float = 1e-6):
+    """NV3 (O6/O7 in the 16-block format) for one expert on one token: (o, n, ms)."""
+    w_e = _c(w_e, np.uint8)
+    s16_e = _c(s16_e, np.uint8)
+    gs_e = _c(gs_e, np.float32)
+    x = _c(x, np.float64)
+    assert gs_e.size == 3
+    o = np.empty(d, np.float64)
+    n = np.empty(d, np.float64)
+    ms = lib().oracle_expert_nv(d, F, _p(w_e), _p(s16_e), _p(gs_e), _p(x), eps, _p(o), _p(n))
+    return o, n, ms
 
 
 def router_scores(x_bits: np.ndarray, wr: np.ndarray) -> np.ndarray:
@@ -182,6 +220,40 @@ def moe_forward(x_bits, wr, w_packed, scales, alpha, beta, k, eps=1e-6, F=None, 
                                   _p(s), _p(ids), _p(w))
     if rc != 0:
         raise ValueError("oracle_moe_forward: bad arguments")
+    return s, ids, w
+
+
+def moe_forward_nv(x_bits, wr, w_packed, scales16, gscale, alpha, beta, k, eps=1e-6, tokens=None):
+    """O1-O8 with 16-block expert weights (NV1-NV3): (s float64 [n][d], ids, w).
+
+    scales16: E4M3 bytes, expert e at e*(3dF/16); gscale fp32 [E][3].
+    """
+    x_bits = _c(x_bits, np.uint16)
+    wr = _c(wr, np.float32)
+    w_packed = _c(w_packed, np.uint8)
+    scales16 = _c(scales16, np.uint8)
+    gscale = _c(gscale, np.float32)
+    alpha = _c(alpha, np.float32)
+    beta = _c(beta, np.float32)
+    T, d = x_bits.shape
+    E = wr.shape[0]
+    F = w_packed.size // E * 2 // (3 * d)
+    assert w_packed.size == E * 3 * d * F // 2 and scales16.size == E * 3 * d * F // 16
+    assert gscale.size == 3 * E
+    if tokens is None:
+        sel = None
+        n = T
+    else:
+        sel = _c(tokens, np.int32)
+        n = sel.size
+    s = np.empty((n, d), np.float64)
+    ids = np.empty((n, k), np.int32)
+    w = np.empty((n, k), np.float64)
+    rc = lib().oracle_moe_forward_nv(T, d, E, F, k, eps, _p(x_bits), _p(wr), _p(w_packed),
+                                     _p(scales16), _p(gscale), _p(alpha), _p(beta), n,
+                                     None if sel is None else _p(sel), _p(s), _p(ids), _p(w))
+    if rc != 0:
+        raise ValueError("oracle_moe_forward_nv: bad arguments")
     return s, ids, w
 
 

@@ -48,6 +48,10 @@
  *   bytes  at e*(3dF/2):  gate [F][d/2] | up [F][d/2] | down [d][F/2]
  *   scales at e*(3dF/32): gate [F][d/32] | up [F][d/32] | down [d][F/32]
  *
+ * The 16-element block format (NV1-NV3 below, [MS] section ⑪) uses the same
+ * code bytes, scales at e*(3dF/16) (gate [F][d/16] | up [F][d/16] |
+ * down [d][F/16]) and three fp32 matrix scales per expert (gate, up, down).
+ *
  * Every function is deterministic for any OpenMP thread count: parallel
  * loops only run independent rows/slots and write disjoint outputs.
  */
@@ -106,13 +110,30 @@ double oracle_e8m0(unsigned s)
     return ldexp(1.0, (int)s - 127);
 }
 
-/* value tables filled from the two functions above when the library loads */
-static double e2m1_tab[16], e8m0_tab[256];
+/*
+ * NV1  [MS] section ⑪: the released 4-bit format shares one small scale per
+ *      16 values, about 4.5 bits per value (4 + 8/16: an 8-bit scale).  The
+ *      pages do not give the scale's encoding.  Reading: the scale byte is an
+ *      FP8 E4M3 number (sign bit 7, exponent bits 6..3 with bias 7, mantissa
+ *      bits 2..0; exponent 0 is subnormal, 2^-6 * m/8; exponent 15 with
+ *      mantissa 7 is NaN; no infinities), as in the published NVFP4 format.
+ */
+double oracle_e4m3(unsigned b)
+{
+    unsigned s = (b >> 7) & 1u, e = (b >> 3) & 15u, m = b & 7u;
+    if (e == 15u && m == 7u) return NAN;
+    double mag = (e == 0) ? ldexp((double)m / 8.0, -6) : ldexp(1.0 + (double)m / 8.0, (int)e - 7);
+    return s ? -mag : mag;
+}
+
+/* value tables filled from the functions above when the library loads */
+static double e2m1_tab[16], e8m0_tab[256], e4m3_tab[256];
 
 __attribute__((constructor)) static void fill_tables(void)
 {
     for (unsigned c = 0; c < 16; ++c) e2m1_tab[c] = oracle_e2m1(c);
     for (unsigned s = 0; s < 256; ++s) e8m0_tab[s] = oracle_e8m0(s);
+    for (unsigned s = 0; s < 256; ++s) e4m3_tab[s] = oracle_e4m3(s);
 }
 
 /* element i of a packed row of K elements */
@@ -129,6 +150,41 @@ void oracle_dequant_rows(int64_t rows, int64_t K, const uint8_t *codes,
     for (int64_t r = 0; r < rows; ++r)
         for (int64_t i = 0; i < K; ++i)
             out[r * K + i] = fp4_elem(codes + r * (K / 2), scales + r * (K / 32), i);
+}
+
+/*
+ * NV2  element i of a row in the 16-block format: the E2M1 code times the
+ *      E4M3 scale of its 16-block times the matrix's fp32 scale g.  Reading:
+ *      the published NVFP4 format also carries one fp32 scale per tensor;
+ *      here one per matrix of an expert (1.0 leaves the block scales alone).
+ */
+static double nv_elem(const uint8_t *row, const uint8_t *srow, double g, int64_t i)
+{
+    uint8_t byte = row[i / 2];
+    unsigned code = (i & 1) ? (unsigned)(byte >> 4) : (unsigned)(byte & 15u);
+    return e2m1_tab[code] * e4m3_tab[srow[i / 16]] * g;
+}
+
+void oracle_dequant_rows_nv(int64_t rows, int64_t K, const uint8_t *codes,
+                            const uint8_t *scales, double g, double *out)
+{
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t i = 0; i < K; ++i)
+            out[r * K + i] = nv_elem(codes + r * (K / 2), scales + r * (K / 16), g, i);
+}
+
+/* One expert matrix in either block format. */
+typedef struct {
+    const uint8_t *codes, *scales;
+    int64_t K;  /* elements per row */
+    int nv;     /* 0: E8M0 per 32, 1: E4M3 per 16 times g */
+    double g;
+} wmat_t;
+
+static double wm_elem(const wmat_t *m, int64_t row, int64_t i)
+{
+    if (m->nv) return nv_elem(m->codes + row * (m->K / 2), m->scales + row * (m->K / 16), m->g, i);
+    return fp4_elem(m->codes + row * (m->K / 2), m->scales + row * (m->K / 32), i);
 }
 
 /* ---- O2: router scores ------------------------------------------------- */
@@ -199,31 +255,25 @@ void oracle_group(int T, int E, int k, const int32_t *ids, int32_t *counts,
  * o_out (d) receives the down projection, n_out (d) its RMS-normalised form;
  * either may be NULL.  Returns the mean square of o.
  */
-double oracle_expert(int d, int F, const uint8_t *w_e, const uint8_t *s_e, const double *x,
-                     double eps, double *o_out, double *n_out)
+/* O6 / O7 on matrices of either format (see oracle_expert). */
+static double expert_mats(int d, int F, const wmat_t *gate, const wmat_t *up,
+                          const wmat_t *down, const double *x, double eps, double *o_out,
+                          double *n_out)
 {
-    const uint8_t *gate = w_e;
-    const uint8_t *up = w_e + (int64_t)F * (d / 2);
-    const uint8_t *down = w_e + (int64_t)2 * F * (d / 2);
-    const uint8_t *sgate = s_e;
-    const uint8_t *sup = s_e + (int64_t)F * (d / 32);
-    const uint8_t *sdown = s_e + (int64_t)2 * F * (d / 32);
-
     double *a = (double *)malloc(sizeof(double) * (size_t)F);
     double *o = (double *)malloc(sizeof(double) * (size_t)d);
     for (int f = 0; f < F; ++f) {
         double g = 0.0, u = 0.0;
         for (int i = 0; i < d; ++i) {
-            g += fp4_elem(gate + (int64_t)f * (d / 2), sgate + (int64_t)f * (d / 32), i) * x[i];
-            u += fp4_elem(up + (int64_t)f * (d / 2), sup + (int64_t)f * (d / 32), i) * x[i];
+            g += wm_elem(gate, f, i) * x[i];
+            u += wm_elem(up, f, i) * x[i];
         }
         a[f] = g / (1.0 + exp(-g)) * u;
     }
     double ss = 0.0;
     for (int i = 0; i < d; ++i) {
         double acc = 0.0;
-        for (int f = 0; f < F; ++f)
-            acc += fp4_elem(down + (int64_t)i * (F / 2), sdown + (int64_t)i * (F / 32), f) * a[f];
+        for (int f = 0; f < F; ++f) acc += wm_elem(down, i, f) * a[f];
         o[i] = acc;
         ss += acc * acc;
     }
@@ -238,6 +288,37 @@ double oracle_expert(int d, int F, const uint8_t *w_e, const uint8_t *s_e, const
     return ms;
 }
 
+/* the three matrices of expert e: nv = 0 MXFP4, nv = 1 the 16-block format */
+static void expert_view(int d, int F, int nv, const uint8_t *wpk, const uint8_t *sc,
+                        const float *gs, int e, wmat_t m[3])
+{
+    const uint8_t *w_e = wpk + (int64_t)e * ((int64_t)3 * d * F / 2);
+    const int64_t bs = nv ? 16 : 32;
+    const uint8_t *s_e = sc + (int64_t)e * ((int64_t)3 * d * F / bs);
+    m[0] = (wmat_t){w_e, s_e, d, nv, nv ? (double)gs[3 * e] : 1.0};
+    m[1] = (wmat_t){w_e + (int64_t)F * (d / 2), s_e + (int64_t)F * (d / bs), d, nv,
+                    nv ? (double)gs[3 * e + 1] : 1.0};
+    m[2] = (wmat_t){w_e + (int64_t)2 * F * (d / 2), s_e + (int64_t)2 * F * (d / bs), F, nv,
+                    nv ? (double)gs[3 * e + 2] : 1.0};
+}
+
+double oracle_expert(int d, int F, const uint8_t *w_e, const uint8_t *s_e, const double *x,
+                     double eps, double *o_out, double *n_out)
+{
+    wmat_t m[3];
+    expert_view(d, F, 0, w_e, s_e, NULL, 0, m);
+    return expert_mats(d, F, &m[0], &m[1], &m[2], x, eps, o_out, n_out);
+}
+
+/* NV3  O6 / O7 for one expert of the 16-block format; gs: its 3 matrix scales. */
+double oracle_expert_nv(int d, int F, const uint8_t *w_e, const uint8_t *s_e, const float *gs,
+                        const double *x, double eps, double *o_out, double *n_out)
+{
+    wmat_t m[3];
+    expert_view(d, F, 1, w_e, s_e, gs, 0, m);
+    return expert_mats(d, F, &m[0], &m[1], &m[2], x, eps, o_out, n_out);
+}
+
 /* ---- whole layer on a set of tokens -------------------------------------- */
 
 /*
@@ -246,16 +327,14 @@ double oracle_expert(int d, int F, const uint8_t *w_e, const uint8_t *s_e, const
  * and w_out [n_sel][k] receive the routing when non-NULL.
  * Returns 0, or -1 on bad arguments / allocation failure.
  */
-int oracle_moe_forward(int T, int d, int E, int F, int k, double eps,
-                       const uint16_t *x, const float *wr, const uint8_t *wpk,
-                       const uint8_t *sc, const float *alpha, const float *beta,
-                       int n_sel, const int32_t *sel, double *s_out,
-                       int32_t *ids_out, double *w_out)
+static int moe_forward(int T, int d, int E, int F, int k, double eps, const uint16_t *x,
+                       const float *wr, int nv, const uint8_t *wpk, const uint8_t *sc,
+                       const float *gs, const float *alpha, const float *beta, int n_sel,
+                       const int32_t *sel, double *s_out, int32_t *ids_out, double *w_out)
 {
     if (T < 0 || d <= 0 || E <= 0 || F <= 0 || k < 1 || k > E || d % 32 || F % 32) return -1;
     if (sel == NULL) n_sel = T;
     if (n_sel <= 0) return 0;
-    const int64_t eb = (int64_t)3 * d * F / 2, esb = (int64_t)3 * d * F / 32;
 
     uint16_t *xs = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)n_sel * d);
     float *scores = (float *)malloc(sizeof(float) * (size_t)n_sel * E);
@@ -279,8 +358,9 @@ int oracle_moe_forward(int T, int d, int E, int F, int k, double eps,
         int e = ids[q];
         double *xd = (double *)malloc(sizeof(double) * (size_t)d);
         for (int i = 0; i < d; ++i) xd[i] = oracle_bf16_to_double(xs[r * d + i]);
-        oracle_expert(d, F, wpk + (int64_t)e * eb, sc + (int64_t)e * esb, xd, eps, NULL,
-                      n + q * d);
+        wmat_t m[3];
+        expert_view(d, F, nv, wpk, sc, gs, e, m);
+        expert_mats(d, F, &m[0], &m[1], &m[2], xd, eps, NULL, n + q * d);
         free(xd);
     }
 
@@ -295,6 +375,32 @@ int oracle_moe_forward(int T, int d, int E, int F, int k, double eps,
     if (w_out) memcpy(w_out, w, sizeof(double) * (size_t)n_sel * k);
     free(xs); free(scores); free(ids); free(w); free(n);
     return 0;
+}
+
+int oracle_moe_forward(int T, int d, int E, int F, int k, double eps,
+                       const uint16_t *x, const float *wr, const uint8_t *wpk,
+                       const uint8_t *sc, const float *alpha, const float *beta,
+                       int n_sel, const int32_t *sel, double *s_out,
+                       int32_t *ids_out, double *w_out)
+{
+    return moe_forward(T, d, E, F, k, eps, x, wr, 0, wpk, sc, NULL, alpha, beta, n_sel, sel,
+                       s_out, ids_out, w_out);
+}
+
+/*
+ * The layer (O1-O8) with expert weights in the 16-block format (NV1-NV3):
+ * codes as oracle_moe_forward, sc16 E4M3 bytes at e*(3dF/16), gs fp32 [E][3]
+ * (gate, up, down).  Same arguments otherwise.
+ */
+int oracle_moe_forward_nv(int T, int d, int E, int F, int k, double eps,
+                          const uint16_t *x, const float *wr, const uint8_t *wpk,
+                          const uint8_t *sc16, const float *gs, const float *alpha,
+                          const float *beta, int n_sel, const int32_t *sel, double *s_out,
+                          int32_t *ids_out, double *w_out)
+{
+    if (!gs || d % 16 || F % 16) return -1;
+    return moe_forward(T, d, E, F, k, eps, x, wr, 1, wpk, sc16, gs, alpha, beta, n_sel, sel,
+                       s_out, ids_out, w_out);
 }
 
 /* ---- latent-width variant ----------------------------------------------- */
