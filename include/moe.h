@@ -178,6 +178,59 @@ int moe_layer_forward(const moe_dims_t *dims, const void *x, const float *router
                       const moe_debug_t *debug);
 
 /*
+ * The 16-block weight format ("Muse Spark Open を段階的に分解する"
+ * (animemo.app), section ⑪: the released expert weights share one small
+ * scale per 16 values, about 4.5 bits per value).  The pages do not give the
+ * scale's encoding; here, as in the published NVFP4 format, it is one FP8
+ * E4M3 byte per 16 values (sign bit 7, exponent bits 6..3 with bias 7,
+ * mantissa bits 2..0, exponent 0 subnormal: 2^-6 * m/8; the byte 0x7F or
+ * 0xFF is NaN and gives undefined results) plus one fp32 scale per matrix.
+ * Element value = E2M1 code * E4M3 block scale * matrix scale.
+ *
+ * Natural layout (the input of moe_pack_weights_nvfp4):
+ *   codes    exactly as for moe_pack_weights (expert e at e*(3*d*F/2));
+ *   scales16 uint8 E4M3, expert e at byte offset e*(3*d*F/16):
+ *              gate [F][d/16] | up [F][d/16] | down [d][F/16]
+ *            byte j of a row scales its elements 16j .. 16j+15.
+ * Per expert: 3dF/2 + 3dF/16 bytes + 12 (the three matrix scales): at
+ * d = 8192, F = 2048 that is 28,311,564 bytes, the page's 28.3 MB.
+ *
+ * Rearranges E experts' natural weights into the packed layout that
+ * moe_layer_forward_nvfp4 reads: the code tiles exactly as
+ * moe_pack_weights writes them, and scale tiles of 256 rows x 8 bytes per
+ * 128-element K chunk (2048 bytes; W1 tiles (nt, kc) at
+ * (nt*(d/128) + kc)*2048, W2's from byte d*F/8 of the expert): tile row r
+ * holds the 8 E4M3 bytes of its 16-blocks 8kc .. 8kc+7, in order, and is
+ * the same weight row as row r of the code tile.  Device pointers, 16-byte
+ * aligned, packed buffers of the natural sizes, not overlapping the inputs.
+ * Asynchronous on `stream`.
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (d, F, E rules of moe_layer_forward),
+ * MOE_ERR_ALIGN, MOE_ERR_ARCH, MOE_ERR_HIP.
+ */
+int moe_pack_weights_nvfp4(const moe_dims_t *dims, const uint8_t *codes, const uint8_t *scales16,
+                           uint8_t *codes_packed, uint8_t *scales_packed, void *stream);
+
+/*
+ * The expert layer (steps 1-6 above) on weights in the 16-block format:
+ * arguments as moe_layer_forward, with
+ *   expert_w_packed, scales16  the packed codes and scale tiles written by
+ *                   moe_pack_weights_nvfp4
+ *   gscale          fp32 [E][3]: the matrix scales of each expert's gate,
+ *                   up and down matrices (device pointer)
+ * and the same workspace size (moe_layer_workspace_size).  The pages' own
+ * design widens the 4-bit weights for the multiply (section ⑪); here they
+ * are widened exactly to fp16 in registers and multiplied with fp16
+ * activations (each row of x and of the SwiGLU output carried with its own
+ * power-of-two scale; exact except elements below 2^-32 of their row's
+ * largest) on the fp16 MFMA with fp32 accumulation.  Deterministic.
+ */
+int moe_layer_forward_nvfp4(const moe_dims_t *dims, const void *x, const float *router_w,
+                            const uint8_t *expert_w_packed, const uint8_t *scales16,
+                            const float *gscale, const float *alpha, const float *beta,
+                            int32_t k, void *s_out, void *workspace, size_t workspace_bytes,
+                            void *stream, const moe_debug_t *debug);
+
+/*
  * Expands `rows` rows of K MXFP4 elements in the natural layout (one matrix
  * of the moe_pack_weights input: codes [rows][K/2], scales [rows][K/32],
  * device pointers) into bf16 out [rows][K] (device), with the conversion the

@@ -82,6 +82,12 @@ def lib() -> C.CDLL:
         L.moe_block_forward.argtypes = [C.POINTER(moe_dims_t), P, P, P, P, P, P, P, P, C.c_int32, P,
                                         P, C.c_size_t, P, C.POINTER(moe_debug_t)]
         L.moe_block_forward.restype = C.c_int
+        L.moe_pack_weights_nvfp4.argtypes = [C.POINTER(moe_dims_t), P, P, P, P, P]
+        L.moe_pack_weights_nvfp4.restype = C.c_int
+        L.moe_layer_forward_nvfp4.argtypes = [C.POINTER(moe_dims_t), P, P, P, P, P, P, P,
+                                              C.c_int32, P, P, C.c_size_t, P,
+                                              C.POINTER(moe_debug_t)]
+        L.moe_layer_forward_nvfp4.restype = C.c_int
         L.moe_status_string.argtypes = [C.c_int]
         L.moe_status_string.restype = C.c_char_p
         _lib = L
@@ -196,6 +202,63 @@ def moe_layer_forward(x, router_w, expert_w_packed, scales, alpha, beta, k, *, F
                                  _stream(stream), C.byref(dbg) if dbg is not None else None)
     if rc != MOE_OK:
         raise MoeError(rc, "moe_layer_forward")
+    return s_out
+
+
+def moe_pack_weights_nvfp4(codes, scales16, d, F, *, codes_packed=None, scales_packed=None,
+                           stream=None):
+    """Natural 16-block expert weights -> the packed layout moe_layer_forward_nvfp4 reads.
+
+    codes uint8 [E][3dF/2] (as for moe_pack_weights), scales16 uint8 E4M3
+    [E][3dF/16]; returns (codes_packed, scales_packed) of the same shapes.
+    """
+    E = codes.shape[0]
+    _check(codes, "codes", torch.uint8, (E, 3 * d * F // 2))
+    _check(scales16, "scales16", torch.uint8, (E, 3 * d * F // 16))
+    if codes_packed is None:
+        codes_packed = torch.empty_like(codes)
+    if scales_packed is None:
+        scales_packed = torch.empty_like(scales16)
+    _check(codes_packed, "codes_packed", torch.uint8, (E, 3 * d * F // 2))
+    _check(scales_packed, "scales_packed", torch.uint8, (E, 3 * d * F // 16))
+    rc = lib().moe_pack_weights_nvfp4(C.byref(_dims(0, d, E, F, 1e-6)), _ptr(codes), _ptr(scales16),
+                                      _ptr(codes_packed), _ptr(scales_packed), _stream(stream))
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_pack_weights_nvfp4")
+    return codes_packed, scales_packed
+
+
+def moe_layer_forward_nvfp4(x, router_w, expert_w_packed, scales16, gscale, alpha, beta, k, *,
+                            F=None, eps=1e-6, s_out=None, workspace=None, stream=None, debug=None):
+    """The layer on 16-block weights; returns s_out (bf16 [T][d]).
+
+    As moe_layer_forward, with scales16 uint8 [E][3dF/16] from
+    moe_pack_weights_nvfp4 and gscale fp32 [E][3] (gate, up, down).
+    """
+    T, d = x.shape
+    E = router_w.shape[0]
+    if F is None:
+        F = expert_w_packed.shape[1] * 2 // (3 * d)
+    _check(x, "x", torch.bfloat16, (T, d))
+    _check(router_w, "router_w", torch.float32, (E, d))
+    _check(expert_w_packed, "expert_w_packed", torch.uint8, (E, 3 * d * F // 2))
+    _check(scales16, "scales16", torch.uint8, (E, 3 * d * F // 16))
+    _check(gscale, "gscale", torch.float32, (E, 3))
+    _check(alpha, "alpha", torch.float32, (d,))
+    _check(beta, "beta", torch.float32, (d,))
+    if s_out is None:
+        s_out = torch.empty_like(x)
+    _check(s_out, "s_out", torch.bfloat16, (T, d))
+    if workspace is None:
+        workspace = workspace_for(T, d, E, F, k, eps, device=x.device)
+    dbg = _debug_struct(debug)
+    rc = lib().moe_layer_forward_nvfp4(C.byref(_dims(T, d, E, F, eps)), _ptr(x), _ptr(router_w),
+                                       _ptr(expert_w_packed), _ptr(scales16), _ptr(gscale),
+                                       _ptr(alpha), _ptr(beta), int(k), _ptr(s_out),
+                                       _ptr(workspace), workspace.numel(), _stream(stream),
+                                       C.byref(dbg) if dbg is not None else None)
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_layer_forward_nvfp4")
     return s_out
 
 

@@ -452,6 +452,92 @@ extern "C" int moe_pack_weights(const moe_dims_t *dims, const uint8_t *codes, co
     return MOE_OK;
 }
 
+extern "C" int moe_pack_weights_nvfp4(const moe_dims_t *dims, const uint8_t *codes,
+                                      const uint8_t *scales16, uint8_t *codes_packed,
+                                      uint8_t *scales_packed, void *stream)
+{
+    if (!dims) return MOE_ERR_NULL;
+    if (dims->d <= 0 || dims->F <= 0 || dims->d % 256 || dims->F % 128 || dims->E < 1 ||
+        dims->E > 1024)
+        return MOE_ERR_SHAPE;
+    if ((int64_t)dims->E * 3 * dims->d * (int64_t)dims->F / 16 >= ((int64_t)1 << 40))
+        return MOE_ERR_SHAPE;
+    if (!codes || !scales16 || !codes_packed || !scales_packed) return MOE_ERR_NULL;
+    if (!aligned16({codes, scales16, codes_packed, scales_packed})) return MOE_ERR_ALIGN;
+    int rc = check_arch();
+    if (rc != MOE_OK) return rc;
+    (void)hipGetLastError();
+    if (launch_pack_nv(codes, scales16, dims->E, dims->d, dims->F, codes_packed, scales_packed,
+                       static_cast<hipStream_t>(stream)) != hipSuccess)
+        return MOE_ERR_HIP;
+    return MOE_OK;
+}
+
+extern "C" int moe_layer_forward_nvfp4(const moe_dims_t *dims, const void *x, const float *router_w,
+                                       const uint8_t *expert_w_packed, const uint8_t *scales16,
+                                       const float *gscale, const float *alpha, const float *beta,
+                                       int32_t k, void *s_out, void *workspace,
+                                       size_t workspace_bytes, void *stream,
+                                       const moe_debug_t *debug)
+{
+    if (!dims) return MOE_ERR_NULL;
+    if (!shape_ok(dims, k)) return MOE_ERR_SHAPE;
+    if (dims->T == 0) return MOE_OK;
+    if (!x || !router_w || !expert_w_packed || !scales16 || !gscale || !alpha || !beta || !s_out ||
+        !workspace)
+        return MOE_ERR_NULL;
+    if (!aligned16({x, router_w, expert_w_packed, scales16, gscale, alpha, beta, s_out}))
+        return MOE_ERR_ALIGN;
+    const Shape s = to_shape(dims, k);
+    if (workspace_bytes < carve_workspace(s, nullptr).bytes) return MOE_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return MOE_ERR_WORKSPACE;
+    int rc = check_arch();
+    if (rc != MOE_OK) return rc;
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const Workspace ws = carve_workspace(s, workspace);
+    const uint16_t *xb = static_cast<const uint16_t *>(x);
+    (void)hipGetLastError();
+
+    auto mark = [&](void *const *evs, int stage) -> bool {
+        if (!debug || !evs[stage]) return true;
+        return hipEventRecord(static_cast<hipEvent_t>(evs[stage]), st) == hipSuccess;
+    };
+    auto stage = [&](int id, auto &&fn) -> bool {
+        if (!mark(debug ? debug->stage_begin : nullptr, id)) return false;
+        if (fn() != hipSuccess) return false;
+        return mark(debug ? debug->stage_end : nullptr, id);
+    };
+    auto ok = [](hipError_t e) { return e == hipSuccess; };
+    // the 16-block kernels: 128-row tiles or 16-row tiles (no streaming
+    // kernel); the router does not split x, x is converted to fp16 instead
+    Plan p = make_plan(s);
+    p.stream = false;
+    p.tile_rows = p.tiled ? 128 : 16;
+    Plan pr = p;
+    pr.tiled = false;
+    auto route = [&]() -> hipError_t {
+        hipError_t e = launch_router(s, pr, ws, xb, router_w, st);
+        if (e != hipSuccess) return e;
+        return launch_f16_rows(xb, s.T, s.d, reinterpret_cast<uint16_t *>(ws.xhi),
+                               reinterpret_cast<float *>(ws.xshi), st);
+    };
+    if (!stage(MOE_STAGE_ROUTER, route) ||
+        !stage(MOE_STAGE_TOPK, [&] { return launch_topk(s, p, ws, st); }) ||
+        !stage(MOE_STAGE_GROUP, [&] { return launch_group(s, p, ws, st); }) ||
+        !ok(launch_gemm1_nv(s, p, ws, expert_w_packed, scales16, gscale, st,
+                            stage_event(debug, MOE_STAGE_GEMM1, true),
+                            stage_event(debug, MOE_STAGE_GEMM1, false))) ||
+        !stage(MOE_STAGE_GEMM2,
+               [&] { return launch_gemm2_nv(s, p, ws, expert_w_packed, scales16, gscale, st); }) ||
+        !stage(MOE_STAGE_COMBINE, [&] {
+            return launch_combine(s, p, ws, xb, alpha, beta, static_cast<uint16_t *>(s_out), st);
+        }))
+        return MOE_ERR_HIP;
+    if (debug && copy_debug(debug, ws, s, st) != hipSuccess) return MOE_ERR_HIP;
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
 extern "C" int moe_dequant_mxfp4(const uint8_t *codes, const uint8_t *scales, int64_t rows,
                                  int32_t K, void *out_bf16, void *stream)
 {

@@ -11,6 +11,8 @@ namespace moe {
 typedef __bf16 bf16x8_t __attribute__((__vector_size__(8 * sizeof(__bf16))));
 typedef __bf16 bf16x2_t __attribute__((__vector_size__(2 * sizeof(__bf16))));
 typedef float floatx4_t __attribute__((__vector_size__(4 * sizeof(float))));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 
@@ -57,6 +59,50 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_ca
 __device__ __forceinline__ floatx4_t mfma16(bf16x8_t a, bf16x8_t b, floatx4_t c)
 {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// ---- the 16-block format: E2M1 codes, one E4M3 scale per 16 values --------
+// An E4M3 scale byte b (sign bit 7, exponent bits 6..3 bias 7, mantissa bits
+// 2..0; exponent 0 subnormal) as a power of two p and a factor m with
+// scale = p * m: p = 2^(E-7), m = 1 + M/8 for E > 0; p = 2^-9, m = M for
+// E = 0; the sign goes into m.  The scaled convert applies only the exponent
+// of its fp32 scale operand (measured on gfx950), so p goes there and m is
+// one packed fp16 multiply.  code * p is an fp16 normal (2^-10 .. 1536) and
+// code * p * m has at most 6 significant bits (<= 2880): both exact in fp16.
+// Exponent 15 with mantissa 7 (NaN in the format) is undefined input.
+struct E4m3Parts {
+    float p;
+    f16x2_t m;
+};
+__device__ __forceinline__ E4m3Parts e4m3_parts(uint32_t b)
+{
+    const uint32_t e = (b >> 3) & 15u, mt = b & 7u;
+    E4m3Parts r;
+    r.p = __uint_as_float((e ? e + 120u : 118u) << 23);
+    float m = e ? 1.0f + 0.125f * (float)mt : (float)mt;
+    m = (b & 0x80u) ? -m : m;
+    const _Float16 mh = (_Float16)m;  // exact: at most 4 significant bits
+    r.m = f16x2_t{mh, mh};
+    return r;
+}
+
+// Eight codes (one dword, element 2b in the low nibble of byte b) of one
+// 16-block -> eight fp16 in element order, code * scale exactly.
+__device__ __forceinline__ f16x8_t fp4x8_to_f16(uint32_t codes, const E4m3Parts &s)
+{
+    const f16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, s.p, 0) * s.m;
+    const f16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, s.p, 1) * s.m;
+    const f16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, s.p, 2) * s.m;
+    const f16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, s.p, 3) * s.m;
+    return f16x8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+__device__ __forceinline__ f16x8_t as_f16x8(uint4 v) { return __builtin_bit_cast(f16x8_t, v); }
+
+// 16x16x32 fp16 MFMA, fp32 accumulate; operand layout as mfma16.
+__device__ __forceinline__ floatx4_t mfma16h(f16x8_t a, f16x8_t b, floatx4_t c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
 // ---- cross-lane reductions on DPP (no LDS round trips) --------------------

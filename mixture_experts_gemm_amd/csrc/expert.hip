@@ -54,6 +54,19 @@ __device__ __forceinline__ floatx4_t mfma_chunk(const uint4 *a, uint4 b, float s
     return acc;
 }
 
+// The same K chunk with weights in the 16-block format: the lane's 32 codes
+// are two 16-blocks (b.x, b.y and b.z, b.w) with the E4M3 scale bytes in
+// s2's low and high byte, expanded exactly to fp16; a holds fp16 activations.
+__device__ __forceinline__ floatx4_t mfma_chunk_nv(const uint4 *a, uint4 b, uint32_t s2, floatx4_t acc)
+{
+    const E4m3Parts lo = e4m3_parts(s2 & 0xFFu), hi = e4m3_parts((s2 >> 8) & 0xFFu);
+    acc = mfma16h(as_f16x8(a[0]), fp4x8_to_f16(b.x, lo), acc);
+    acc = mfma16h(as_f16x8(a[1]), fp4x8_to_f16(b.y, lo), acc);
+    acc = mfma16h(as_f16x8(a[2]), fp4x8_to_f16(b.z, hi), acc);
+    acc = mfma16h(as_f16x8(a[3]), fp4x8_to_f16(b.w, hi), acc);
+    return acc;
+}
+
 // ---- small device helpers ---------------------------------------------------
 
 // Streaming loads of weight bytes: each is read once per layer call, so they
@@ -134,13 +147,15 @@ __device__ __forceinline__ void lds_barrier()
 
 // gate/up: a workgroup owns 16 features (their gate block and up block); its
 // 4 waves take quarters of the K chunks and their partial sums are added in
-// LDS in a fixed order.
-template <int U>
+// LDS in a fixed order.  NV: weights in the 16-block format, x in fp16 with
+// per-token scales xs, matrix scales gs [E][3]; else MXFP4 and bf16 x.
+template <int U, bool NV>
 __global__ __launch_bounds__(256) void gemm1_decode_kernel(
     const uint16_t *__restrict__ x, const int32_t *__restrict__ perm,
     const Tile *__restrict__ tiles, const int32_t *__restrict__ ntiles,
     const uint8_t *__restrict__ wpk, const uint8_t *__restrict__ sc, uint16_t *__restrict__ h,
-    int d, int F, int k, int groups, int rows_fit)
+    int d, int F, int k, int groups, int rows_fit, const float *__restrict__ xs,
+    const float *__restrict__ gs)
 {
     constexpr int NB = 2;  // gate block, up block
     extern __shared__ uint4 arows[];  // [rows_fit][d/8]
@@ -151,7 +166,8 @@ __global__ __launch_bounds__(256) void gemm1_decode_kernel(
     if (tile >= *ntiles) return;
     const Tile tl = tiles[tile];
     const int n = lane & 15, g = lane >> 4;
-    const WView v = w1_view(wpk, sc, tl.expert, d, F);
+    const WView v = NV ? w1_codes(wpk, tl.expert, d, F) : w1_view(wpk, sc, tl.expert, d, F);
+    const NvScales vs = w1_nv_scales(sc, tl.expert, d, F);
     const int f = grp * 16 + n, nt = f >> 7;
     const int rho[NB] = {w1_rho(f, false), w1_rho(f, true)};
     const bool valid = n < tl.nrows;
@@ -168,7 +184,10 @@ __global__ __launch_bounds__(256) void gemm1_decode_kernel(
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) {
                     b[u][nb] = ld_stream16(v.slot(nt, c + u, rho[nb], g));
-                    sw[u][nb] = ld_stream4(v.scales(nt, c + u, rho[nb]));
+                    if constexpr (NV)
+                        sw[u][nb] = __builtin_nontemporal_load(vs.pair(nt, c + u, rho[nb], g));
+                    else
+                        sw[u][nb] = ld_stream4(v.scales(nt, c + u, rho[nb]));
                 }
             }
     };
@@ -200,9 +219,13 @@ __global__ __launch_bounds__(256) void gemm1_decode_kernel(
                     else a[s] = *reinterpret_cast<const uint4 *>(ap + (c + u) * kKStep + s * 8);
                 }
 #pragma unroll
-                for (int nb = 0; nb < NB; ++nb)
-                    acc[nb] = mfma_chunk(a, b[u][nb], e8m0_to_f32((sw[u][nb] >> (8 * g)) & 0xFFu),
-                                         acc[nb]);
+                for (int nb = 0; nb < NB; ++nb) {
+                    if constexpr (NV)
+                        acc[nb] = mfma_chunk_nv(a, b[u][nb], sw[u][nb], acc[nb]);
+                    else
+                        acc[nb] = mfma_chunk(a, b[u][nb], e8m0_to_f32((sw[u][nb] >> (8 * g)) & 0xFFu),
+                                             acc[nb]);
+                }
             }
         if (c + U < c_end) load_b(c + U);
     }
@@ -219,8 +242,15 @@ __global__ __launch_bounds__(256) void gemm1_decode_kernel(
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int row = g * 4 + r;
-        if (row < tl.nrows)
-            h[(int64_t)(tl.row0 + row) * F + f] = f32_to_bf16(silu(acc[0][r]) * acc[1][r]);
+        if (row < tl.nrows) {
+            float gv = acc[0][r], uv = acc[1][r];
+            if constexpr (NV) {
+                const float xr = xs[perm[tl.row0 + row] / k];
+                gv *= xr * gs[3 * tl.expert];
+                uv *= xr * gs[3 * tl.expert + 1];
+            }
+            h[(int64_t)(tl.row0 + row) * F + f] = f32_to_bf16(silu(gv) * uv);
+        }
     }
 }
 
@@ -230,12 +260,14 @@ __global__ __launch_bounds__(256) void gemm1_decode_kernel(
 // o^2 over the workgroup's 64 columns, both stored in slot order (grouped
 // row r goes to slot perm[r]), so the combine step finds a token's k rows at
 // slots t*k .. t*k+k-1 without a lookup.
-template <int U>
+// NV: the 16-block format with fp16 h rows and their scales hs (grouped
+// order), as gemm1_decode_kernel.
+template <int U, bool NV>
 __global__ __launch_bounds__(256) void gemm2_decode_kernel(
     const uint16_t *__restrict__ h, const int32_t *__restrict__ perm, const Tile *__restrict__ tiles,
     const int32_t *__restrict__ ntiles, const uint8_t *__restrict__ wpk,
     const uint8_t *__restrict__ sc, uint16_t *__restrict__ o, float *__restrict__ ssq, int d,
-    int F, int wgs_per_tile, int rows_fit)
+    int F, int wgs_per_tile, int rows_fit, const float *__restrict__ hs, const float *__restrict__ gs)
 {
     extern __shared__ uint4 arows[];  // [rows_fit][F/8]
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -244,7 +276,8 @@ __global__ __launch_bounds__(256) void gemm2_decode_kernel(
     if (tile >= *ntiles) return;
     const Tile tl = tiles[tile];
     const int n = lane & 15, g = lane >> 4;
-    const WView v = w2_view(wpk, sc, tl.expert, d, F);
+    const WView v = NV ? w2_codes(wpk, tl.expert, d, F) : w2_view(wpk, sc, tl.expert, d, F);
+    const NvScales vs = w2_nv_scales(sc, tl.expert, d, F);
     const int orow = col0 + n, nt = orow >> 8, rho = orow & 255;
     const bool valid = n < tl.nrows;
     const bool use_lds = tl.nrows <= rows_fit;
@@ -257,7 +290,10 @@ __global__ __launch_bounds__(256) void gemm2_decode_kernel(
         for (int u = 0; u < U; ++u)
             if (c + u < nc) {
                 b[u] = ld_stream16(v.slot(nt, c + u, rho, g));
-                sw[u] = ld_stream4(v.scales(nt, c + u, rho));
+                if constexpr (NV)
+                    sw[u] = __builtin_nontemporal_load(vs.pair(nt, c + u, rho, g));
+                else
+                    sw[u] = ld_stream4(v.scales(nt, c + u, rho));
             }
     };
     load_b(0);
@@ -287,7 +323,10 @@ __global__ __launch_bounds__(256) void gemm2_decode_kernel(
                     else if (use_lds) a[s] = al[(c + u) * (kKStep / 8) + s];
                     else a[s] = *reinterpret_cast<const uint4 *>(ap + (c + u) * kKStep + s * 8);
                 }
-                acc = mfma_chunk(a, b[u], e8m0_to_f32((sw[u] >> (8 * g)) & 0xFFu), acc);
+                if constexpr (NV)
+                    acc = mfma_chunk_nv(a, b[u], sw[u], acc);
+                else
+                    acc = mfma_chunk(a, b[u], e8m0_to_f32((sw[u] >> (8 * g)) & 0xFFu), acc);
             }
         if (c + U < nc) load_b(c + U);
     }
@@ -295,10 +334,13 @@ __global__ __launch_bounds__(256) void gemm2_decode_kernel(
     // (DPP within 16-lane rows), then the four waves in LDS in a fixed order
     __shared__ float wsum[4][16];
     const int P = d / 64;
+    float gd = 1.0f;
+    if constexpr (NV) gd = gs[3 * tl.expert + 2];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        const float val = acc[r];
         const int row = g * 4 + r;
+        float val = acc[r];
+        if constexpr (NV) val *= hs[tl.row0 + (row < tl.nrows ? row : 0)] * gd;
         if (row < tl.nrows) o[(int64_t)dst[r] * d + col0 + n] = f32_to_bf16(val);
         const float ss = sum16(val * val);
         if (n == 0) wsum[wv][g * 4 + r] = ss;
@@ -848,6 +890,264 @@ __global__ __launch_bounds__(512) void gemm_mxw_kernel(const MxArgs pa)
     }
 }
 
+// =========================================================================
+// The 16-block format (prefill): tiles of <= 128 grouped rows x 256 weight
+// rows, all of K, on the fp16 MFMA (16x16x32).  The scaled MX MFMA takes one
+// power-of-two scale per 32 values, so it cannot take these weights; they
+// are expanded in registers instead ("Muse Spark Open を段階的に分解する",
+// section ⑪: the 4-bit weights are widened for the multiply), exactly, to
+// fp16 (fp4x8_to_f16: one convert and one packed multiply per two values).
+// The activations are fp16 rows with a power-of-two scale per row
+// (f16_rows_kernel), applied with the matrix scale in the epilogue.
+//
+// Three-stage LDS ring per 128-wide K chunk, filled by direct-to-LDS loads:
+// A 128 rows x 256 bytes (16-byte slot q of row r at q ^ (r & 7)), the
+// chunk's code tile and scale tile copied linearly (the packed layout is the
+// LDS layout); 50 KB a stage.  8 waves as 2 (rows) x 4 (columns): each wave
+// owns 64 rows x 64 weight rows (4 x 4 blocks of 16x16), so each wave
+// expands a weight value once per 64 rows it multiplies.  For gate/up a
+// wave's 64 weight rows are 32 gate features and the same 32 up features,
+// so SwiGLU is formed in registers.
+// =========================================================================
+struct NvArgs {
+    const uint16_t *a;   // fp16 rows: x [T][d] (gate/up, gathered by perm) or h [S][F] (down)
+    const float *as;     // their per-row scales
+    const int32_t *perm;
+    const Tile *tiles;
+    const int32_t *ntiles;
+    const uint8_t *wpk;  // packed code tiles
+    const uint8_t *sc;   // packed E4M3 scale tiles
+    const float *gs;     // matrix scales [E][3]: gate, up, down
+    uint16_t *out;       // h [S][F] or o [S][d] (bf16, grouped order)
+    float *ssq;
+    int d, F, k, ntn;
+};
+
+template <bool GATE_UP>
+__global__ __launch_bounds__(512) void gemm_nv_kernel(const NvArgs pa)
+{
+    constexpr int NW = 8;
+    constexpr int AU = kTM * 16;  // 16-byte units of an A stage
+    constexpr int BU = kTN * 4;   // of a code tile
+    constexpr int AL = AU / (64 * NW), BL = BU / (64 * NW);
+    constexpr int NLOADS = AL + BL + 1;
+    __shared__ uint4 A0[AU], A1[AU], A2[AU];
+    __shared__ uint4 B0[BU], B1[BU], B2[BU];
+    __shared__ uint32_t S0[kTN * 2], S1[kTN * 2], S2[kTN * 2];
+
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int d = pa.d, F = pa.F;
+    int idx;
+    if (!xcd_tile(*pa.ntiles * pa.ntn, idx)) return;
+    // work order as gemm_mx_kernel: expert by expert, N-tile-major inside one
+    Tile tl = pa.tiles[idx / pa.ntn];
+    const int r0 = idx - tl.first * pa.ntn;
+    const int nt = r0 / tl.count, mt = tl.first + (r0 - nt * tl.count);
+    if (mt != idx / pa.ntn) tl = pa.tiles[mt];
+    const int K = GATE_UP ? d : F;
+    auto src_row = [&](int r) -> int64_t {
+        const int rr = r < tl.nrows ? r : 0;  // rows past nrows re-read row 0 (never stored)
+        return GATE_UP ? (int64_t)(pa.perm[tl.row0 + rr] / pa.k) : (int64_t)(tl.row0 + rr);
+    };
+
+    // ---- load assignment ----------------------------------------------------
+    // A: load i of this wave fills units 64*(NW*i + wv) + lane: row
+    // 4*(NW*i + wv) + lane/16, stored slot lane%16 = global slot ^ (row & 7)
+    const uint16_t *asrc[AL];
+#pragma unroll
+    for (int i = 0; i < AL; ++i) {
+        const int r = 4 * (NW * i + wv) + (lane >> 4);
+        const int q = (lane & 15) ^ (r & 7);
+        asrc[i] = pa.a + src_row(r) * K + q * 8;
+    }
+    const WView v = GATE_UP ? w1_codes(pa.wpk, tl.expert, d, F) : w2_codes(pa.wpk, tl.expert, d, F);
+    const NvScales vs = GATE_UP ? w1_nv_scales(pa.sc, tl.expert, d, F)
+                                : w2_nv_scales(pa.sc, tl.expert, d, F);
+    const uint8_t *bsrc = v.tile(nt, 0) + (64 * wv + lane) * 16;
+    const uint8_t *ssrc = vs.stile(nt, 0) + tid * 4;
+    const int nk = K / kKStep;
+    const int wvu = __builtin_amdgcn_readfirstlane(wv);
+    auto issue = [&](int kc, uint4 *A, uint4 *B, uint32_t *S) {
+#pragma unroll
+        for (int i = 0; i < AL; ++i) dma16(asrc[i] + kc * kKStep, lds_off(A + (NW * i + wvu) * 64));
+#pragma unroll
+        for (int i = 0; i < BL; ++i)
+            dma16(bsrc + (int64_t)kc * kWTileBytes + i * NW * 1024, lds_off(B + (NW * i + wvu) * 64));
+        dma4(ssrc + (int64_t)kc * kNvTileScaleBytes, lds_off(S + 64 * wvu));
+    };
+
+    // ---- compute assignment -------------------------------------------------
+    const int wm = wv & 1, wn = wv >> 1;
+    const int n16 = lane & 15, g = lane >> 4;
+    int mb_act = (tl.nrows - wm * 64 + 15) >> 4;
+    mb_act = mb_act < 0 ? 0 : (mb_act > 4 ? 4 : mb_act);
+    // packed weight rows of the wave's 4 column blocks; gate/up: blocks 0, 1
+    // gate features, 2, 3 the same up features
+    int rho[4];
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+        rho[nb] = GATE_UP ? (wn >> 1) * 128 + (wn & 1) * 32 + (nb >> 1) * 64 + (nb & 1) * 16 + n16
+                          : wn * 64 + nb * 16 + n16;
+
+    floatx4_t acc[4][4];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+
+    auto compute = [&](const uint4 *A, const uint4 *B, const uint32_t *S, auto full) {
+        constexpr bool F_ = decltype(full)::value;
+        f16x8_t bh[4][4];
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+            const uint4 bw = B[rho[nb] * 4 + (g ^ bswz(rho[nb]))];
+            const uint32_t s2 = reinterpret_cast<const uint16_t *>(S)[rho[nb] * 4 + g];
+            const E4m3Parts lo = e4m3_parts(s2 & 0xFFu), hi = e4m3_parts(s2 >> 8);
+            bh[nb][0] = fp4x8_to_f16(bw.x, lo);
+            bh[nb][1] = fp4x8_to_f16(bw.y, lo);
+            bh[nb][2] = fp4x8_to_f16(bw.z, hi);
+            bh[nb][3] = fp4x8_to_f16(bw.w, hi);
+        }
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+            if (F_ || mb < mb_act) {
+                const int row = wm * 64 + mb * 16 + n16;
+                const int sw = row & 7;
+#pragma unroll
+                for (int st = 0; st < 4; ++st) {
+                    const f16x8_t a = as_f16x8(A[row * 16 + ((4 * g + st) ^ sw)]);
+#pragma unroll
+                    for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = mfma16h(a, bh[nb][st], acc[mb][nb]);
+                }
+            }
+        }
+    };
+
+    // ---- pipeline --------------------------------------------------------------
+    issue(0, A0, B0, S0);
+    if (nk > 1) issue(1, A1, B1, S1);
+    const bool full = mb_act == 4;
+    auto step = [&](int kc, uint4 *Ac, uint4 *Bc, uint32_t *Sc, uint4 *An, uint4 *Bn, uint32_t *Sn) {
+        if (kc + 1 < nk) chunk_sync<NLOADS>();
+        else chunk_sync<0>();
+        if (kc + 2 < nk) issue(kc + 2, An, Bn, Sn);
+        if (full) compute(Ac, Bc, Sc, std::true_type{});
+        else if (mb_act > 0) compute(Ac, Bc, Sc, std::false_type{});
+    };
+    for (int kc = 0; kc < nk; kc += 3) {
+        step(kc, A0, B0, S0, A2, B2, S2);
+        if (kc + 1 < nk) step(kc + 1, A1, B1, S1, A0, B0, S0);
+        if (kc + 2 < nk) step(kc + 2, A2, B2, S2, A1, B1, S1);
+    }
+
+    // ---- epilogue ----------------------------------------------------------------
+    // lane holds C[g*4 + r][n16] of every 16x16 block
+    if (GATE_UP) {
+        const float gg = pa.gs[3 * tl.expert], gu = pa.gs[3 * tl.expert + 1];
+        const int fbase = nt * 128 + (wn >> 1) * 64 + (wn & 1) * 32;
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+            if (mb >= mb_act) continue;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = wm * 64 + mb * 16 + g * 4 + r;
+                if (row < tl.nrows) {
+                    const float xr = pa.as[pa.perm[tl.row0 + row] / pa.k];
+#pragma unroll
+                    for (int nb = 0; nb < 2; ++nb)
+                        pa.out[(int64_t)(tl.row0 + row) * F + fbase + nb * 16 + n16] = f32_to_bf16(
+                            silu(acc[mb][nb][r] * (xr * gg)) * (acc[mb][nb + 2][r] * (xr * gu)));
+                }
+            }
+        }
+    } else {
+        // bf16 o and the sum of o^2 over the wave's 64 columns
+        const float gd = pa.gs[3 * tl.expert + 2];
+        const int P = d / 64;
+        const int cbase = nt * kTN + wn * 64;
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+            if (mb >= mb_act) continue;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = wm * 64 + mb * 16 + g * 4 + r;
+                const float hr = pa.as[tl.row0 + (row < tl.nrows ? row : 0)] * gd;
+                float ov[4], ss = 0.f;
+#pragma unroll
+                for (int nb = 0; nb < 4; ++nb) {
+                    ov[nb] = acc[mb][nb][r] * hr;
+                    ss += ov[nb] * ov[nb];
+                }
+                ss = sum16(ss);
+                if (row < tl.nrows) {
+#pragma unroll
+                    for (int nb = 0; nb < 4; ++nb)
+                        pa.out[(int64_t)(tl.row0 + row) * d + cbase + nb * 16 + n16] = f32_to_bf16(ov[nb]);
+                    if (n16 == 0) pa.ssq[(int64_t)(tl.row0 + row) * P + cbase / 64] = ss;
+                }
+            }
+        }
+    }
+}
+
+// bf16 rows -> fp16 rows for the 16-block kernels: row r is multiplied by
+// 2^q, q chosen so its largest magnitude lands in [2^14, 2^15) (q <= 126),
+// and scale[r] = 2^-q.  Exact for every element down to 2^-32 of the row's
+// largest (fp16 keeps 11 significant bits, bf16 has 8); smaller ones round
+// to the fp16 subnormal grid.  One workgroup per row, K a multiple of 8.
+__global__ __launch_bounds__(256) void f16_rows_kernel(const uint16_t *__restrict__ src, int K,
+                                                       uint16_t *__restrict__ dst,
+                                                       float *__restrict__ scale)
+{
+    const int64_t row = blockIdx.x;
+    const uint4 *s4 = reinterpret_cast<const uint4 *>(src + row * K);
+    uint4 *d4 = reinterpret_cast<uint4 *>(dst + row * K);
+    const int n = K / 8;
+    uint32_t mx = 0;
+    for (int i = threadIdx.x; i < n; i += 256) {
+        const uint4 v = s4[i];
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            mx = max(mx, w[j] & 0x7FFFu);
+            mx = max(mx, (w[j] >> 16) & 0x7FFFu);
+        }
+    }
+    // magnitudes of bf16 order as their bit patterns: an integer max
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, off));
+    __shared__ uint32_t wmax[4];
+    if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = mx;
+    __syncthreads();
+    mx = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+    const int eb = (int)(mx >> 7);  // biased exponent of the largest magnitude
+    int q = mx == 0 ? 0 : (eb == 0 ? 126 : 14 - (eb - 127));
+    q = q > 126 ? 126 : q;
+    const float f = pow2f(q);
+    for (int i = threadIdx.x; i < n; i += 256) {
+        const uint4 v = s4[i];
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        uint32_t o[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const _Float16 lo = (_Float16)(bf16_to_f32((uint16_t)(w[j] & 0xFFFFu)) * f);
+            const _Float16 hi = (_Float16)(bf16_to_f32((uint16_t)(w[j] >> 16)) * f);
+            o[j] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+        }
+        d4[i] = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+    if (threadIdx.x == 0) scale[row] = pow2f(-q);
+}
+
+hipError_t launch_f16_rows(const uint16_t *src, int64_t rows, int K, uint16_t *dst, float *scale,
+                           hipStream_t st)
+{
+    if (rows <= 0) return hipSuccess;
+    f16_rows_kernel<<<(unsigned)rows, 256, 0, st>>>(src, K, dst, scale);
+    return hipGetLastError();
+}
+
+
 // bf16 rows -> FP8 E4M3 hi/lo parts + E8M0 scales per 32-block (one thread per block).
 __global__ __launch_bounds__(256) void split_rows_kernel(const uint16_t *__restrict__ src,
                                                          int64_t nblk, uint8_t *__restrict__ hi,
@@ -1148,10 +1448,11 @@ hipError_t launch_gemm1(const Shape &s, const Plan &p, const Workspace &ws, cons
         rows_fit = rows_fit < s.T ? rows_fit : s.T;
         if (rows_fit > 16) rows_fit = 16;
         const size_t lds = (size_t)rows_fit * s.d * 2;
-        hipExtLaunchKernelGGL(gemm1_decode_kernel<kUnroll>, dim3((unsigned)grid), dim3(256),
+        hipExtLaunchKernelGGL(gemm1_decode_kernel<kUnroll, false>, dim3((unsigned)grid), dim3(256),
                               (uint32_t)lds, st, ev0, ev1, 0, x, (const int32_t *)ws.perm,
                               (const Tile *)ws.tiles, (const int32_t *)ws.ntiles, wpk, sc, ws.h,
-                              s.d, s.F, s.k, groups, rows_fit);
+                              s.d, s.F, s.k, groups, rows_fit, (const float *)nullptr,
+                              (const float *)nullptr);
     }
     return hipGetLastError();
 }
@@ -1182,8 +1483,65 @@ hipError_t launch_gemm2(const Shape &s, const Plan &p, const Workspace &ws, cons
         rows_fit = rows_fit < s.T ? rows_fit : s.T;
         if (rows_fit > 16) rows_fit = 16;
         const size_t lds = (size_t)rows_fit * s.F * 2;
-        gemm2_decode_kernel<kUnroll><<<(unsigned)grid, 256, lds, st>>>(
-            ws.h, ws.perm, ws.tiles, ws.ntiles, wpk, sc, ws.o, ws.ssq, s.d, s.F, wgs, rows_fit);
+        gemm2_decode_kernel<kUnroll, false><<<(unsigned)grid, 256, lds, st>>>(
+            ws.h, ws.perm, ws.tiles, ws.ntiles, wpk, sc, ws.o, ws.ssq, s.d, s.F, wgs, rows_fit,
+            nullptr, nullptr);
+    }
+    return hipGetLastError();
+}
+
+// ---- the 16-block format --------------------------------------------------------
+
+// x was converted to fp16 rows (ws.xhi) with scales (ws.xshi) after the router.
+hipError_t launch_gemm1_nv(const Shape &s, const Plan &p, const Workspace &ws, const uint8_t *wpk,
+                           const uint8_t *sc, const float *gs, hipStream_t st, hipEvent_t ev0,
+                           hipEvent_t ev1)
+{
+    const uint16_t *x16 = reinterpret_cast<const uint16_t *>(ws.xhi);
+    const float *xs = reinterpret_cast<const float *>(ws.xshi);
+    if (p.tiled) {
+        NvArgs pa{x16, xs, ws.perm, ws.tiles, ws.ntiles, wpk, sc, gs, ws.h, nullptr,
+                  s.d, s.F, s.k, s.F / 128};
+        const int64_t grid = 8 * ((max_tiles(s, p.tile_rows) * pa.ntn + 7) / 8);
+        hipExtLaunchKernelGGL(gemm_nv_kernel<true>, dim3((unsigned)grid), dim3(512), 0, st, ev0, ev1,
+                              0, pa);
+    } else {
+        const int groups = s.F / 16;
+        const int64_t grid = max_tiles(s, p.tile_rows) * groups;
+        int rows_fit = kDecodeLdsBytes / (s.d * 2);
+        rows_fit = rows_fit < s.T ? rows_fit : s.T;
+        if (rows_fit > 16) rows_fit = 16;
+        const size_t lds = (size_t)rows_fit * s.d * 2;
+        hipExtLaunchKernelGGL(gemm1_decode_kernel<kUnroll, true>, dim3((unsigned)grid), dim3(256),
+                              (uint32_t)lds, st, ev0, ev1, 0, x16, (const int32_t *)ws.perm,
+                              (const Tile *)ws.tiles, (const int32_t *)ws.ntiles, wpk, sc, ws.h,
+                              s.d, s.F, s.k, groups, rows_fit, xs, gs);
+    }
+    return hipGetLastError();
+}
+
+// h (bf16, from the gate/up kernel) -> fp16 rows + scales, then the down product.
+hipError_t launch_gemm2_nv(const Shape &s, const Plan &p, const Workspace &ws, const uint8_t *wpk,
+                           const uint8_t *sc, const float *gs, hipStream_t st)
+{
+    uint16_t *h16 = reinterpret_cast<uint16_t *>(ws.hhi);
+    float *hs = reinterpret_cast<float *>(ws.hshi);
+    hipError_t e = launch_f16_rows(ws.h, s.S(), s.F, h16, hs, st);
+    if (e != hipSuccess) return e;
+    if (p.tiled) {
+        NvArgs pa{h16, hs, nullptr, ws.tiles, ws.ntiles, wpk, sc, gs, ws.o, ws.ssq,
+                  s.d, s.F, s.k, s.d / 256};
+        const int64_t grid = 8 * ((max_tiles(s, p.tile_rows) * pa.ntn + 7) / 8);
+        gemm_nv_kernel<false><<<(unsigned)grid, 512, 0, st>>>(pa);
+    } else {
+        const int wgs = s.d / 64;
+        const int64_t grid = max_tiles(s, p.tile_rows) * wgs;
+        int rows_fit = kDecodeLdsBytes / (s.F * 2);
+        rows_fit = rows_fit < s.T ? rows_fit : s.T;
+        if (rows_fit > 16) rows_fit = 16;
+        const size_t lds = (size_t)rows_fit * s.F * 2;
+        gemm2_decode_kernel<kUnroll, true><<<(unsigned)grid, 256, lds, st>>>(
+            h16, ws.perm, ws.tiles, ws.ntiles, wpk, sc, ws.o, ws.ssq, s.d, s.F, wgs, rows_fit, hs, gs);
     }
     return hipGetLastError();
 }

@@ -186,6 +186,18 @@ hipError_t launch_gate(const uint16_t *x, const float *f, const float *alpha, co
                        uint16_t *s_out, int64_t T, int D, hipStream_t st);
 hipError_t launch_pack(const uint8_t *w, const uint8_t *s, int E, int d, int F, uint8_t *wp,
                        uint8_t *sp, hipStream_t st);
+// The 16-block format (one E4M3 scale per 16 values, matrix scales gs [E][3]).
+hipError_t launch_pack_nv(const uint8_t *w, const uint8_t *s16, int E, int d, int F, uint8_t *wp,
+                          uint8_t *sp, hipStream_t st);
+// bf16 rows -> fp16 rows times a per-row power of two, scale[r] = its inverse.
+hipError_t launch_f16_rows(const uint16_t *src, int64_t rows, int K, uint16_t *dst, float *scale,
+                           hipStream_t st);
+// Expects x converted by launch_f16_rows into ws.xhi (rows) / ws.xshi (scales).
+hipError_t launch_gemm1_nv(const Shape &s, const Plan &p, const Workspace &ws, const uint8_t *wpk,
+                           const uint8_t *sc, const float *gs, hipStream_t st, hipEvent_t ev_begin,
+                           hipEvent_t ev_end);
+hipError_t launch_gemm2_nv(const Shape &s, const Plan &p, const Workspace &ws, const uint8_t *wpk,
+                           const uint8_t *sc, const float *gs, hipStream_t st);
 hipError_t launch_dequant(const uint8_t *codes, const uint8_t *scales, int64_t rows, int K,
                           uint16_t *out, hipStream_t st);
 

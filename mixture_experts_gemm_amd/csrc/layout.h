@@ -70,6 +70,44 @@ struct WView {
     }
 };
 
+// The 16-block format (one E4M3 scale per 16 values): the code tiles are
+// laid out exactly as above; the scale tiles hold 256 rows x 8 bytes per
+// chunk (2048 bytes): row rho's bytes are the scales of its 16-blocks
+// 8kc .. 8kc+7, in order.  Per expert the scales take 3dF/16 bytes, W2's at
+// byte dF/8.
+constexpr int kNvTileScaleBytes = kWRows * 8;
+
+struct NvScales {
+    const uint8_t *s;
+    int nk;
+    __device__ __forceinline__ const uint8_t *stile(int nt, int kc) const
+    {
+        return s + ((int64_t)nt * nk + kc) * kNvTileScaleBytes;
+    }
+    // the two scale bytes of natural 32-block g of packed row rho
+    __device__ __forceinline__ const uint16_t *pair(int nt, int kc, int rho, int g) const
+    {
+        return reinterpret_cast<const uint16_t *>(stile(nt, kc) + rho * 8 + g * 2);
+    }
+};
+
+__device__ __forceinline__ WView w1_codes(const uint8_t *wpk, int e, int d, int F)
+{
+    return WView{wpk + e * ((int64_t)3 * d * F / 2), nullptr, d / kKStep};
+}
+__device__ __forceinline__ WView w2_codes(const uint8_t *wpk, int e, int d, int F)
+{
+    return WView{wpk + e * ((int64_t)3 * d * F / 2) + (int64_t)d * F, nullptr, F / kKStep};
+}
+__device__ __forceinline__ NvScales w1_nv_scales(const uint8_t *sc, int e, int d, int F)
+{
+    return NvScales{sc + e * ((int64_t)3 * d * F / 16), d / kKStep};
+}
+__device__ __forceinline__ NvScales w2_nv_scales(const uint8_t *sc, int e, int d, int F)
+{
+    return NvScales{sc + e * ((int64_t)3 * d * F / 16) + (int64_t)d * F / 8, F / kKStep};
+}
+
 __device__ __forceinline__ WView w1_view(const uint8_t *wpk, const uint8_t *sc, int e, int d, int F)
 {
     const int64_t eb = (int64_t)3 * d * F / 2, es = (int64_t)3 * d * F / 32;

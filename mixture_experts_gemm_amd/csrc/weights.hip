@@ -81,6 +81,46 @@ hipError_t launch_pack(const uint8_t *w, const uint8_t *s, int E, int d, int F, 
     return hipGetLastError();
 }
 
+// The 16-block format's scales: one thread per 8-byte unit of the packed
+// scale tiles (the E4M3 bytes of one row's eight 16-blocks of one chunk).
+// The code bytes are packed by pack_codes_kernel, unchanged.
+__global__ __launch_bounds__(256) void pack_scales16_kernel(const uint8_t *__restrict__ nat,
+                                                            uint8_t *__restrict__ out, int64_t total,
+                                                            int d, int F)
+{
+    const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (u >= total) return;
+    const int64_t per_e = (int64_t)3 * d * F / 128;  // units per expert
+    const int64_t e = u / per_e, r = u - e * per_e;
+    const int64_t w1_units = (int64_t)d * F / 64;
+    const int64_t r2 = r < w1_units ? r : r - w1_units;
+    const int64_t t = r2 >> 8;
+    const int rho = (int)(r2 & 255);
+    const uint8_t *src = nat + e * ((int64_t)3 * d * F / 16);
+    if (r < w1_units) {
+        const int nk = d / kKStep;
+        const int nt = (int)(t / nk), kc = (int)(t % nk);
+        const int f = nt * 128 + (rho >> 7) * 64 + (rho & 63);
+        const int64_t row = ((rho >> 6) & 1) ? (int64_t)F + f : (int64_t)f;
+        src += row * (d / 16) + kc * 8;
+    } else {
+        const int nk = F / kKStep;
+        const int nt = (int)(t / nk), kc = (int)(t % nk);
+        const int64_t row = (int64_t)nt * kWRows + rho;
+        src += (int64_t)d * F / 8 + row * (F / 16) + kc * 8;
+    }
+    reinterpret_cast<uint2 *>(out)[u] = *reinterpret_cast<const uint2 *>(src);
+}
+
+hipError_t launch_pack_nv(const uint8_t *w, const uint8_t *s16, int E, int d, int F, uint8_t *wp,
+                          uint8_t *sp, hipStream_t st)
+{
+    const int64_t nc = (int64_t)E * 3 * d * F / 32, ns = (int64_t)E * 3 * d * F / 128;
+    pack_codes_kernel<<<(unsigned)((nc + 255) / 256), 256, 0, st>>>(w, wp, nc, d, F);
+    pack_scales16_kernel<<<(unsigned)((ns + 255) / 256), 256, 0, st>>>(s16, sp, ns, d, F);
+    return hipGetLastError();
+}
+
 // MXFP4 rows -> bf16 rows with the conversion the few-row kernels use.
 __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t *__restrict__ codes,
                                                       const uint8_t *__restrict__ scales,

@@ -120,3 +120,41 @@ def run_latent(L, dev=None, debug=True, **kw):
         res["ids"] = res["ids"].reshape(w.T, w.k)
         res["weights"] = res["weights"].reshape(w.T, w.k)
     return bf16_bits(out), res
+
+
+def upload_nv(L, device="cuda"):
+    """Device copies of a generated layer in the 16-block format, packed by the
+    library's entry point."""
+    from mixture_experts_gemm_amd import binding as B
+    w_nat = torch.from_numpy(L.w_packed).to(device)
+    s_nat = torch.from_numpy(L.scales16).to(device)
+    w, s = B.moe_pack_weights_nvfp4(w_nat, s_nat, L.shape.d, L.shape.F)
+    torch.cuda.synchronize()
+    del w_nat, s_nat
+    return dict(
+        x=bf16_tensor(L.x, device),
+        router_w=torch.from_numpy(L.router_w).to(device),
+        w=w,
+        s=s,
+        gs=torch.from_numpy(L.gscale).to(device),
+        alpha=torch.from_numpy(L.alpha).to(device),
+        beta=torch.from_numpy(L.beta).to(device),
+    )
+
+
+def run_nv(L, dev=None, debug=True, **kw):
+    """GPU layer on 16-block weights through the C ABI: (s_out bits, debug dict)."""
+    from mixture_experts_gemm_amd import binding as B
+    dev = dev or upload_nv(L)
+    s = L.shape
+    T = dev["x"].shape[0]
+    dbg = debug_buffers(T, s.E, s.k) if debug else None
+    out = B.moe_layer_forward_nvfp4(dev["x"], dev["router_w"], dev["w"], dev["s"], dev["gs"],
+                                    dev["alpha"], dev["beta"], s.k, F=s.F, eps=L.eps, debug=dbg, **kw)
+    torch.cuda.synchronize()
+    res = None
+    if debug:
+        res = {n: t.cpu().numpy() for n, t in dbg.items()}
+        res["ids"] = res["ids"].reshape(T, s.k)
+        res["weights"] = res["weights"].reshape(T, s.k)
+    return bf16_bits(out), res

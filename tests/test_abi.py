@@ -17,7 +17,8 @@ def test_exports_every_declared_function(L):
     names = B.declared_functions()
     assert set(names) == {"moe_layer_workspace_size", "moe_layer_forward", "moe_pack_weights",
                           "moe_dequant_mxfp4", "moe_status_string", "moe_latent_workspace_size",
-                          "moe_latent_forward", "moe_block_workspace_size", "moe_block_forward"}
+                          "moe_latent_forward", "moe_block_workspace_size", "moe_block_forward",
+                          "moe_pack_weights_nvfp4", "moe_layer_forward_nvfp4"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -183,3 +184,47 @@ def test_block_argument_errors():
     for name in names:
         assert _block_call(good, ptr={name: odd}) == B.MOE_ERR_ALIGN, name
     assert _block_call(B.moe_dims_t(0, 256, 8, 512, 1e-6), null="x") == B.MOE_OK
+
+
+# ------------------------------------------------------------ 16-block format
+
+def _nv_call(dims, k=2, ws_bytes=1 << 30, null=None, ws_ptr=1 << 20, ptr=None):
+    p = C.c_void_p(1 << 20)  # never dereferenced: every case below fails the checks first
+    names = ("x", "router_w", "w", "s16", "gscale", "alpha", "beta", "s_out")
+    args = {n: p for n in names}
+    args["ws"] = C.c_void_p(ws_ptr)
+    if null:
+        args[null] = None
+    args.update(ptr or {})
+    return B.lib().moe_layer_forward_nvfp4(C.byref(dims) if dims is not None else None,
+                                           *(args[n] for n in names[:7]), k, args["s_out"], args["ws"],
+                                           ws_bytes, None, None)
+
+
+def test_nv_forward_argument_errors():
+    good = B.moe_dims_t(64, 256, 8, 512, 1e-6)
+    assert _nv_call(None) == B.MOE_ERR_NULL
+    for name in ("x", "router_w", "w", "s16", "gscale", "alpha", "beta", "s_out", "ws"):
+        assert _nv_call(good, null=name) == B.MOE_ERR_NULL, name
+    assert _nv_call(B.moe_dims_t(64, 250, 8, 512, 1e-6)) == B.MOE_ERR_SHAPE
+    assert _nv_call(B.moe_dims_t(64, 256, 8, 500, 1e-6)) == B.MOE_ERR_SHAPE
+    assert _nv_call(good, k=9) == B.MOE_ERR_SHAPE
+    assert _nv_call(good, ws_bytes=1024) == B.MOE_ERR_WORKSPACE
+    assert _nv_call(good, ws_ptr=(1 << 20) + 64) == B.MOE_ERR_WORKSPACE
+    odd = C.c_void_p((1 << 20) + 8)
+    for name in ("x", "router_w", "w", "s16", "gscale", "alpha", "beta", "s_out"):
+        assert _nv_call(good, ptr={name: odd}) == B.MOE_ERR_ALIGN, name
+    assert _nv_call(B.moe_dims_t(0, 256, 8, 512, 1e-6), null="x") == B.MOE_OK
+
+
+def test_nv_pack_argument_errors():
+    p = C.c_void_p(1 << 20)
+    pack = B.lib().moe_pack_weights_nvfp4
+    assert pack(None, p, p, p, p, None) == B.MOE_ERR_NULL
+    assert pack(C.byref(B.moe_dims_t(0, 250, 8, 512, 1e-6)), p, p, p, p, None) == B.MOE_ERR_SHAPE
+    assert pack(C.byref(B.moe_dims_t(0, 256, 8, 500, 1e-6)), p, p, p, p, None) == B.MOE_ERR_SHAPE
+    assert pack(C.byref(B.moe_dims_t(0, 256, 0, 512, 1e-6)), p, p, p, p, None) == B.MOE_ERR_SHAPE
+    dims = C.byref(B.moe_dims_t(0, 256, 8, 512, 1e-6))
+    assert pack(dims, None, p, p, p, None) == B.MOE_ERR_NULL
+    assert pack(dims, p, None, p, p, None) == B.MOE_ERR_NULL
+    assert pack(dims, p, p, p, C.c_void_p((1 << 20) + 4), None) == B.MOE_ERR_ALIGN
