@@ -42,10 +42,17 @@ WORKLOAD_TEXT = {
               "4 concurrent requests (T=4, d=8192, E=256, top-8, F=2048, MXFP4)",
     "block_prefill": "MoE block with its stream norms, prefill micro-batch (T=4096, d=8192, E=256, top-8, "
                      "F=2048, MXFP4)",
+    "nv4": "Muse-shaped decode, 4 concurrent requests, expert weights in the 16-block format "
+           "(T=4, d=8192, E=256, top-8, F=2048, E2M1 + E4M3 per 16 + fp32 per matrix)",
+    "nv_prefill": "Muse-shaped prefill micro-batch, expert weights in the 16-block format "
+                  "(T=4096, d=8192, E=256, top-8, F=2048, E2M1 + E4M3 per 16 + fp32 per matrix)",
 }
 LATENT = ("latent4", "latent_prefill")
 # the block with its stream norms runs on the full-width workloads' inputs
 BLOCK = {"block4": "decode4", "block_prefill": "prefill"}
+# the 16-block weight format on the full-width workloads' tokens and router
+NV = {"nv4": "decode4", "nv_prefill": "prefill"}
+DECODE_LIKE = ("latent4", "block4", "nv4")
 
 
 def log(*a):
@@ -59,7 +66,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="decode4", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--also", default="decode1,prefill,ep753,ep3012,latent4,latent_prefill,block4,"
-                                      "block_prefill",
+                                      "block_prefill,nv4,nv_prefill",
                     help="comma list of extra workloads timed after the main one ('' for none)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
@@ -102,6 +109,48 @@ def make_sets(name, nsets, device):
         torch.cuda.synchronize()
         del W, S
         sets.append(dict(w=Wp, s=Sp, wr=wr, alpha=a, beta=b))
+    x = torch.from_numpy(host.x.view(np.int16)).to(device).view(torch.bfloat16)
+    return w, host, sets, x
+
+
+def make_nv_sets(name, nsets, device):
+    """Weight sets in the 16-block format (set 0 from the shared generator,
+    the rest drawn on the GPU with the same distributions)."""
+    import numpy as np
+    import torch
+
+    from mixture_experts_gemm_amd import binding as B
+    from mixture_experts_gemm_amd import synth
+
+    w = synth.WORKLOADS[NV[name]]
+    s = w.shape
+    pool = 256 if s.T < 64 else s.T
+    host = synth.make_layer_nv(w, layer=0, T=pool, threads=16)
+    ns = 3 * s.d * s.F // 16
+    sets = []
+    for i in range(nsets):
+        if i == 0:
+            W = torch.from_numpy(host.w_packed).to(device)
+            S = torch.from_numpy(host.scales16).to(device)
+            G = torch.from_numpy(host.gscale).to(device)
+            wr = torch.from_numpy(host.router_w).to(device)
+            a = torch.from_numpy(host.alpha).to(device)
+            b = torch.from_numpy(host.beta).to(device)
+        else:
+            g = torch.Generator(device=device)
+            g.manual_seed(1000 * w.seed + 500 + i)
+            W = torch.randint(0, 256, (s.E, s.expert_bytes), dtype=torch.uint8, device=device, generator=g)
+            ex = torch.randint(synth.NV_EXP_LO, synth.NV_EXP_HI + 1, (s.E, ns), dtype=torch.uint8,
+                               device=device, generator=g)
+            mt = torch.randint(0, 8, (s.E, ns), dtype=torch.uint8, device=device, generator=g)
+            S = (ex << 3) | mt
+            G = (torch.rand(s.E, 3, device=device, generator=g) * 0.5 + 0.75) * 2.0 ** -5
+            wr = torch.from_numpy(synth.make_router(w, layer=i)).to(device)
+            a, b = (torch.from_numpy(v).to(device) for v in synth.make_gates(w, layer=i))
+        Wp, Sp = B.moe_pack_weights_nvfp4(W, S, s.d, s.F)
+        torch.cuda.synchronize()
+        del W, S
+        sets.append(dict(w=Wp, s=Sp, gs=G.contiguous(), wr=wr, alpha=a, beta=b))
     x = torch.from_numpy(host.x.view(np.int16)).to(device).view(torch.bfloat16)
     return w, host, sets, x
 
@@ -158,6 +207,8 @@ GATE_UP_KERNEL = {
     "latent_prefill": "gemm_mxw_kernel<true> (gate/up + SwiGLU, 128x512 tiles, MX MFMA)",
     "block4": "gemm1_stream_kernel (gate/up + SwiGLU, persistent, MX MFMA)",
     "block_prefill": "gemm_mxw_kernel<true> (gate/up + SwiGLU, 128x512 tiles, MX MFMA)",
+    "nv4": "gemm1_decode_kernel<4, true> (gate/up + SwiGLU, 16-row tiles, fp16 MFMA, 16-block weights)",
+    "nv_prefill": "gemm_nv_kernel<true> (gate/up + SwiGLU, 128x256 tiles, fp16 MFMA, 16-block weights)",
 }
 
 
@@ -177,7 +228,8 @@ def time_workload(name, steps, warmup, device):
 
     latent = name in LATENT
     block = name in BLOCK
-    decode = name.startswith("decode") or name in ("latent4", "block4")
+    nv = name in NV
+    decode = name.startswith("decode") or name in DECODE_LIKE
     nsets = 4 if decode else 1
     log(f"generating {name}: {nsets} weight set(s)")
     if latent:
@@ -186,6 +238,10 @@ def time_workload(name, steps, warmup, device):
         w, host, sets, xpool = make_latent_sets(name, nsets, device)
         s = w.expert_view().shape
         D = w.D
+    elif nv:
+        w, host, sets, xpool = make_nv_sets(name, nsets, device)
+        s = w.shape
+        D = s.d
     else:
         w, host, sets, xpool = make_sets(BLOCK.get(name, name), nsets, device)
         s = w.shape
@@ -217,6 +273,9 @@ def time_workload(name, steps, warmup, device):
         elif block:
             B.moe_block_forward(xb, st["g_pre"], st["wr"], st["w"], st["s"], st["g_post"], st["alpha"],
                                 st["beta"], s.k, F=s.F, s_out=out, workspace=ws, debug=debug)
+        elif nv:
+            B.moe_layer_forward_nvfp4(xb, st["wr"], st["w"], st["s"], st["gs"], st["alpha"], st["beta"],
+                                      s.k, F=s.F, s_out=out, workspace=ws, debug=debug)
         else:
             B.moe_layer_forward(xb, st["wr"], st["w"], st["s"], st["alpha"], st["beta"], s.k, F=s.F,
                                 s_out=out, workspace=ws, debug=debug)
@@ -258,8 +317,8 @@ def time_workload(name, steps, warmup, device):
     # the gate/up kernel's algorithmic bytes (over the timed launches: U, the
     # distinct experts, differs per step) and flops; its bound is the larger
     # of the two times at the peaks
-    nbytes = sum(R.mxfp4_w1_bytes(s.d, s.F) * U[i] + T * s.d * 2 + S * s.F * 2
-                 for i in timed) / len(timed)
+    w1b = R.nvfp4_w1_bytes(s.d, s.F) if nv else R.mxfp4_w1_bytes(s.d, s.F)
+    nbytes = sum(w1b * U[i] + T * s.d * 2 + S * s.F * 2 for i in timed) / len(timed)
     flops = R.gemm1_flops(S, s.d, s.F)
     hbm_bound = nbytes / R.MI355X_HBM_BYTES_PER_S >= flops / R.MI355X_BF16_FLOPS_PER_S
     if hbm_bound:
@@ -281,7 +340,7 @@ def time_workload(name, steps, warmup, device):
         lb = sum(R.latent_layer_bytes(T, D, s.d, s.E, s.F, u) for u in U) / len(U)
         lf = R.latent_layer_flops(T, D, s.d, s.k, s.F)
     else:
-        lb = sum(R.layer_bytes(T, s.d, s.E, s.F, u) for u in U) / len(U)
+        lb = sum(R.layer_bytes(T, s.d, s.E, s.F, u, nv=nv) for u in U) / len(U)
         lf = R.layer_flops(T, s.d, s.k, s.F)
     res["layer_hbm_frac"] = lb / (elapsed / steps) / R.MI355X_HBM_BYTES_PER_S
     res["layer_mfma_frac"] = lf / (elapsed / steps) / R.MI355X_BF16_FLOPS_PER_S
@@ -297,7 +356,10 @@ def cpu_baseline(host, T, seconds):
     n = 0
     t0 = time.perf_counter()
     while True:
-        if hasattr(host, "wc"):  # latent-width variant
+        if hasattr(host, "scales16"):  # 16-block weight format
+            oracle.moe_forward_nv(host.x[:T], host.router_w, host.w_packed, host.scales16, host.gscale,
+                                  host.alpha, host.beta, host.k, eps=host.eps)
+        elif hasattr(host, "wc"):  # latent-width variant
             oracle.latent_forward(host.x[:T], host.router_w, host.wc, host.w_packed, host.scales,
                                   host.we, host.alpha, host.beta, host.k, eps=host.eps)
         else:
@@ -332,13 +394,13 @@ def main():
         torch.cuda.synchronize()
         log(f"calibration copy: {n} bytes read, {n} bytes written")
         del src, dst
-    decode = args.workload.startswith("decode") or args.workload in ("latent4", "block4")
+    decode = args.workload.startswith("decode") or args.workload in DECODE_LIKE
     steps = args.steps or (200 if decode else 20)
     warmup = args.warmup if args.warmup is not None else (10 if decode else 3)
     main_res, host, T = time_workload(args.workload, steps, warmup, device)
     also = {}
     for extra in [e for e in args.also.split(",") if e and e != args.workload]:
-        d2 = extra.startswith("decode") or extra in ("latent4", "block4")
+        d2 = extra.startswith("decode") or extra in DECODE_LIKE
         r, _, _ = time_workload(extra, 200 if d2 else 10, 10 if d2 else 2, device)
         also[extra] = r
         torch.cuda.empty_cache()
@@ -362,7 +424,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": WORKLOAD_TEXT[args.workload], "T": T, "d": s.d, "E": s.E,
                    **({"D": host.w.D} if args.workload in LATENT else {}),
-                   "k": s.k, "F": s.F, "weights": "MXFP4 (E2M1 + E8M0 per 32)",
+                   "k": s.k, "F": s.F,
+                   "weights": ("E2M1 + E4M3 per 16 + fp32 per matrix" if args.workload in NV
+                               else "MXFP4 (E2M1 + E8M0 per 32)"),
                    "weight_sets": 4 if decode else 1,
                    "distinct_experts_mean": main_res["distinct_experts_mean"]},
         "roofline": {k: v for k, v in main_res["roofline"].items()

@@ -513,7 +513,7 @@ extern "C" int moe_layer_forward_nvfp4(const moe_dims_t *dims, const void *x, co
     // kernel); the router does not split x, x is converted to fp16 instead
     Plan p = make_plan(s);
     p.stream = false;
-    p.tile_rows = p.tiled ? 128 : 16;
+    p.tile_rows = p.tiled ? kNvTileRows : 16;
     Plan pr = p;
     pr.tiled = false;
     auto route = [&]() -> hipError_t {

@@ -923,17 +923,36 @@ struct NvArgs {
     int d, F, k, ntn;
 };
 
-template <bool GATE_UP>
+// E4M3 scale byte -> (the scaled convert's fp32 power of two, the fp16
+// factor pair) for all 256 bytes, one entry per thread of the first 256.
+__device__ __forceinline__ void fill_e4m3_table(uint2 *lut)
+{
+    if (threadIdx.x < 256) {
+        const E4m3Parts e = e4m3_parts(threadIdx.x);
+        lut[threadIdx.x] = make_uint2(__float_as_uint(e.p), __builtin_bit_cast(uint32_t, e.m));
+    }
+}
+
+__device__ __forceinline__ E4m3Parts e4m3_lookup(const uint2 *lut, uint32_t b)
+{
+    const uint2 v = lut[b];
+    return E4m3Parts{__uint_as_float(v.x), __builtin_bit_cast(f16x2_t, v.y)};
+}
+
+template <bool GATE_UP, int MR>
 __global__ __launch_bounds__(512) void gemm_nv_kernel(const NvArgs pa)
 {
     constexpr int NW = 8;
-    constexpr int AU = kTM * 16;  // 16-byte units of an A stage
-    constexpr int BU = kTN * 4;   // of a code tile
+    constexpr int ST = MR == 128 ? 3 : 2;  // ring stages (LDS: 50 KB or 66 KB a stage)
+    constexpr int MB = MR / 32;            // row blocks of 16 per wave
+    constexpr int AU = MR * 16;            // 16-byte units of an A stage
+    constexpr int BU = kTN * 4;            // of a code tile
     constexpr int AL = AU / (64 * NW), BL = BU / (64 * NW);
     constexpr int NLOADS = AL + BL + 1;
-    __shared__ uint4 A0[AU], A1[AU], A2[AU];
-    __shared__ uint4 B0[BU], B1[BU], B2[BU];
-    __shared__ uint32_t S0[kTN * 2], S1[kTN * 2], S2[kTN * 2];
+    __shared__ uint4 As[ST][AU];
+    __shared__ uint4 Bs[ST][BU];
+    __shared__ uint32_t Ss[ST][kTN * 2];
+    __shared__ uint2 lut[256];
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int d = pa.d, F = pa.F;
@@ -967,20 +986,24 @@ __global__ __launch_bounds__(512) void gemm_nv_kernel(const NvArgs pa)
     const uint8_t *ssrc = vs.stile(nt, 0) + tid * 4;
     const int nk = K / kKStep;
     const int wvu = __builtin_amdgcn_readfirstlane(wv);
-    auto issue = [&](int kc, uint4 *A, uint4 *B, uint32_t *S) {
+    auto issue = [&](int kc) {
+        const int b = kc % ST;
 #pragma unroll
-        for (int i = 0; i < AL; ++i) dma16(asrc[i] + kc * kKStep, lds_off(A + (NW * i + wvu) * 64));
+        for (int i = 0; i < AL; ++i) dma16(asrc[i] + kc * kKStep, lds_off(&As[b][(NW * i + wvu) * 64]));
 #pragma unroll
         for (int i = 0; i < BL; ++i)
-            dma16(bsrc + (int64_t)kc * kWTileBytes + i * NW * 1024, lds_off(B + (NW * i + wvu) * 64));
-        dma4(ssrc + (int64_t)kc * kNvTileScaleBytes, lds_off(S + 64 * wvu));
+            dma16(bsrc + (int64_t)kc * kWTileBytes + i * NW * 1024, lds_off(&Bs[b][(NW * i + wvu) * 64]));
+        dma4(ssrc + (int64_t)kc * kNvTileScaleBytes, lds_off(&Ss[b][64 * wvu]));
     };
 
     // ---- compute assignment -------------------------------------------------
+    // 8 waves as 2 (rows) x 4 (columns); wave row wm takes the row blocks
+    // 2j + wm (interleaved, so a partly filled tile keeps both busy)
     const int wm = wv & 1, wn = wv >> 1;
     const int n16 = lane & 15, g = lane >> 4;
-    int mb_act = (tl.nrows - wm * 64 + 15) >> 4;
-    mb_act = mb_act < 0 ? 0 : (mb_act > 4 ? 4 : mb_act);
+    const int nblk = (tl.nrows + 15) >> 4;
+    int mb_act = (nblk - wm + 1) >> 1;
+    mb_act = mb_act < 0 ? 0 : (mb_act > MB ? MB : mb_act);
     // packed weight rows of the wave's 4 column blocks; gate/up: blocks 0, 1
     // gate features, 2, 3 the same up features
     int rho[4];
@@ -989,29 +1012,32 @@ __global__ __launch_bounds__(512) void gemm_nv_kernel(const NvArgs pa)
         rho[nb] = GATE_UP ? (wn >> 1) * 128 + (wn & 1) * 32 + (nb >> 1) * 64 + (nb & 1) * 16 + n16
                           : wn * 64 + nb * 16 + n16;
 
-    floatx4_t acc[4][4];
+    floatx4_t acc[MB][4];
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
-    auto compute = [&](const uint4 *A, const uint4 *B, const uint32_t *S, auto full) {
+    auto compute = [&](int b, auto full) {
         constexpr bool F_ = decltype(full)::value;
+        const uint4 *A = As[b];
+        const uint4 *B = Bs[b];
+        const uint16_t *S = reinterpret_cast<const uint16_t *>(Ss[b]);
         f16x8_t bh[4][4];
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) {
             const uint4 bw = B[rho[nb] * 4 + (g ^ bswz(rho[nb]))];
-            const uint32_t s2 = reinterpret_cast<const uint16_t *>(S)[rho[nb] * 4 + g];
-            const E4m3Parts lo = e4m3_parts(s2 & 0xFFu), hi = e4m3_parts(s2 >> 8);
+            const uint32_t s2 = S[rho[nb] * 4 + g];
+            const E4m3Parts lo = e4m3_lookup(lut, s2 & 0xFFu), hi = e4m3_lookup(lut, s2 >> 8);
             bh[nb][0] = fp4x8_to_f16(bw.x, lo);
             bh[nb][1] = fp4x8_to_f16(bw.y, lo);
             bh[nb][2] = fp4x8_to_f16(bw.z, hi);
             bh[nb][3] = fp4x8_to_f16(bw.w, hi);
         }
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
+        for (int mb = 0; mb < MB; ++mb) {
             if (F_ || mb < mb_act) {
-                const int row = wm * 64 + mb * 16 + n16;
+                const int row = (2 * mb + wm) * 16 + n16;
                 const int sw = row & 7;
 #pragma unroll
                 for (int st = 0; st < 4; ++st) {
@@ -1024,20 +1050,20 @@ __global__ __launch_bounds__(512) void gemm_nv_kernel(const NvArgs pa)
     };
 
     // ---- pipeline --------------------------------------------------------------
-    issue(0, A0, B0, S0);
-    if (nk > 1) issue(1, A1, B1, S1);
-    const bool full = mb_act == 4;
-    auto step = [&](int kc, uint4 *Ac, uint4 *Bc, uint32_t *Sc, uint4 *An, uint4 *Bn, uint32_t *Sn) {
-        if (kc + 1 < nk) chunk_sync<NLOADS>();
+    // The scale table is written before the first barrier of the ring.
+    fill_e4m3_table(lut);
+    lds_barrier();
+    issue(0);
+    if (ST == 3 && nk > 1) issue(1);
+    const bool full = mb_act == MB;
+    for (int kc = 0; kc < nk; ++kc) {
+        // three stages: chunk kc+1's loads may stay in flight; two: none are
+        if (ST == 3 && kc + 1 < nk) chunk_sync<NLOADS>();
         else chunk_sync<0>();
-        if (kc + 2 < nk) issue(kc + 2, An, Bn, Sn);
-        if (full) compute(Ac, Bc, Sc, std::true_type{});
-        else if (mb_act > 0) compute(Ac, Bc, Sc, std::false_type{});
-    };
-    for (int kc = 0; kc < nk; kc += 3) {
-        step(kc, A0, B0, S0, A2, B2, S2);
-        if (kc + 1 < nk) step(kc + 1, A1, B1, S1, A0, B0, S0);
-        if (kc + 2 < nk) step(kc + 2, A2, B2, S2, A1, B1, S1);
+        // the stage refilled now was last read in step kc-1, before the barrier
+        if (kc + ST - 1 < nk) issue(kc + ST - 1);
+        if (full) compute(kc % ST, std::true_type{});
+        else if (mb_act > 0) compute(kc % ST, std::false_type{});
     }
 
     // ---- epilogue ----------------------------------------------------------------
@@ -1046,11 +1072,11 @@ __global__ __launch_bounds__(512) void gemm_nv_kernel(const NvArgs pa)
         const float gg = pa.gs[3 * tl.expert], gu = pa.gs[3 * tl.expert + 1];
         const int fbase = nt * 128 + (wn >> 1) * 64 + (wn & 1) * 32;
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
+        for (int mb = 0; mb < MB; ++mb) {
             if (mb >= mb_act) continue;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int row = wm * 64 + mb * 16 + g * 4 + r;
+                const int row = (2 * mb + wm) * 16 + g * 4 + r;
                 if (row < tl.nrows) {
                     const float xr = pa.as[pa.perm[tl.row0 + row] / pa.k];
 #pragma unroll
@@ -1066,11 +1092,11 @@ __global__ __launch_bounds__(512) void gemm_nv_kernel(const NvArgs pa)
         const int P = d / 64;
         const int cbase = nt * kTN + wn * 64;
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
+        for (int mb = 0; mb < MB; ++mb) {
             if (mb >= mb_act) continue;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int row = wm * 64 + mb * 16 + g * 4 + r;
+                const int row = (2 * mb + wm) * 16 + g * 4 + r;
                 const float hr = pa.as[tl.row0 + (row < tl.nrows ? row : 0)] * gd;
                 float ov[4], ss = 0.f;
 #pragma unroll
@@ -1503,8 +1529,8 @@ hipError_t launch_gemm1_nv(const Shape &s, const Plan &p, const Workspace &ws, c
         NvArgs pa{x16, xs, ws.perm, ws.tiles, ws.ntiles, wpk, sc, gs, ws.h, nullptr,
                   s.d, s.F, s.k, s.F / 128};
         const int64_t grid = 8 * ((max_tiles(s, p.tile_rows) * pa.ntn + 7) / 8);
-        hipExtLaunchKernelGGL(gemm_nv_kernel<true>, dim3((unsigned)grid), dim3(512), 0, st, ev0, ev1,
-                              0, pa);
+        hipExtLaunchKernelGGL(gemm_nv_kernel<true, kNvTileRows>, dim3((unsigned)grid), dim3(512), 0, st,
+                              ev0, ev1, 0, pa);
     } else {
         const int groups = s.F / 16;
         const int64_t grid = max_tiles(s, p.tile_rows) * groups;
@@ -1532,7 +1558,7 @@ hipError_t launch_gemm2_nv(const Shape &s, const Plan &p, const Workspace &ws, c
         NvArgs pa{h16, hs, nullptr, ws.tiles, ws.ntiles, wpk, sc, gs, ws.o, ws.ssq,
                   s.d, s.F, s.k, s.d / 256};
         const int64_t grid = 8 * ((max_tiles(s, p.tile_rows) * pa.ntn + 7) / 8);
-        gemm_nv_kernel<false><<<(unsigned)grid, 512, 0, st>>>(pa);
+        gemm_nv_kernel<false, kNvTileRows><<<(unsigned)grid, 512, 0, st>>>(pa);
     } else {
         const int wgs = s.d / 64;
         const int64_t grid = max_tiles(s, p.tile_rows) * wgs;

@@ -104,6 +104,14 @@ constexpr bool kUseWide = MOE_MX_WIDE;
 inline bool wide_gate_up(const Shape &s) { return kUseWide && (s.F / 128) % 2 == 0; }
 inline bool wide_down(const Shape &s) { return kUseWide && (s.d / 256) % 2 == 0; }
 
+#ifndef MOE_NV_TILE_ROWS
+#define MOE_NV_TILE_ROWS 192
+#endif
+// Rows per tile of the 16-block format's tiled kernels (128 or 192): 192 keeps
+// an expert's prefill rows (about 128 +- 40) in one tile, so its weights are
+// loaded and widened once.
+constexpr int kNvTileRows = MOE_NV_TILE_ROWS;
+
 // Upper bound of the tile count for tiles of tile_rows rows (1: any plan).
 inline int64_t max_tiles(const Shape &s, int tile_rows)
 {

@@ -54,6 +54,17 @@ def mxfp4_w2_bytes(d: int, F: int) -> int:
     return d * F // 2 + d * F // 32
 
 
+def nvfp4_expert_bytes(d: int, F: int) -> int:
+    """16-block format: codes + E4M3 scales (16 values per scale) + three fp32 matrix scales."""
+    p = expert_params(d, F)
+    return p // 2 + p // 16 + 12
+
+
+def nvfp4_w1_bytes(d: int, F: int) -> int:
+    """gate + up part of one expert in the 16-block format."""
+    return 2 * F * d // 2 + 2 * F * d // 16 + 8
+
+
 def flops_per_slot(d: int, F: int) -> int:
     return 2 * expert_params(d, F)
 
@@ -71,9 +82,10 @@ def crossover_tokens(d: int, F: int, bits_per_value: float, bw: float, rate: flo
     return read_time(expert_bytes(d, F, bits_per_value), bw) / compute_time(flops_per_slot(d, F), rate)
 
 
-def layer_bytes(T: int, d: int, E: int, F: int, U: int) -> int:
-    """Whole-layer algorithmic bytes with U distinct experts used."""
-    return (U * mxfp4_expert_bytes(d, F) + E * d * 4  # experts + fp32 router
+def layer_bytes(T: int, d: int, E: int, F: int, U: int, nv: bool = False) -> int:
+    """Whole-layer algorithmic bytes with U distinct experts used (nv: 16-block weights)."""
+    per_expert = nvfp4_expert_bytes(d, F) if nv else mxfp4_expert_bytes(d, F)
+    return (U * per_expert + E * d * 4                 # experts + fp32 router
             + 2 * d * 4                                # alpha, beta
             + 2 * T * d * 2)                           # x in, s_out out (bf16)
 
