@@ -181,10 +181,13 @@ typedef struct {
     double g;
 } wmat_t;
 
-static double wm_elem(const wmat_t *m, int64_t row, int64_t i)
+/* element i of row `row` of a matrix; nv is the matrix's format, passed
+ * separately so the loops below test it once per row, not per element */
+static inline double wm_get(const wmat_t *m, int nv, int64_t row, int64_t i)
 {
-    if (m->nv) return nv_elem(m->codes + row * (m->K / 2), m->scales + row * (m->K / 16), m->g, i);
-    return fp4_elem(m->codes + row * (m->K / 2), m->scales + row * (m->K / 32), i);
+    const uint8_t *c = m->codes + row * (m->K / 2);
+    return nv ? nv_elem(c, m->scales + row * (m->K / 16), m->g, i)
+              : fp4_elem(c, m->scales + row * (m->K / 32), i);
 }
 
 /* ---- O2: router scores ------------------------------------------------- */
@@ -262,18 +265,28 @@ static double expert_mats(int d, int F, const wmat_t *gate, const wmat_t *up,
 {
     double *a = (double *)malloc(sizeof(double) * (size_t)F);
     double *o = (double *)malloc(sizeof(double) * (size_t)d);
+    const int nv = gate->nv;  /* the three matrices share one format */
     for (int f = 0; f < F; ++f) {
         double g = 0.0, u = 0.0;
-        for (int i = 0; i < d; ++i) {
-            g += wm_elem(gate, f, i) * x[i];
-            u += wm_elem(up, f, i) * x[i];
-        }
+        if (nv)
+            for (int i = 0; i < d; ++i) {
+                g += wm_get(gate, 1, f, i) * x[i];
+                u += wm_get(up, 1, f, i) * x[i];
+            }
+        else
+            for (int i = 0; i < d; ++i) {
+                g += wm_get(gate, 0, f, i) * x[i];
+                u += wm_get(up, 0, f, i) * x[i];
+            }
         a[f] = g / (1.0 + exp(-g)) * u;
     }
     double ss = 0.0;
     for (int i = 0; i < d; ++i) {
         double acc = 0.0;
-        for (int f = 0; f < F; ++f) acc += wm_elem(down, i, f) * a[f];
+        if (nv)
+            for (int f = 0; f < F; ++f) acc += wm_get(down, 1, i, f) * a[f];
+        else
+            for (int f = 0; f < F; ++f) acc += wm_get(down, 0, i, f) * a[f];
         o[i] = acc;
         ss += acc * acc;
     }
