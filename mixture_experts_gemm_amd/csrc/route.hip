@@ -20,6 +20,17 @@
 
 namespace moe {
 
+#ifndef MOE_ROUTER_LDS
+#define MOE_ROUTER_LDS 1  // many-token router through LDS (router_gemm_lds_kernel)
+#endif
+constexpr bool kRouterLds = MOE_ROUTER_LDS;
+
+// LDS byte address of a __shared__ object.
+__device__ __forceinline__ uint32_t lds_addr(const void *p)
+{
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void *)p;
+}
+
 // ---------------------------------------------------------------------------
 // Router scores, few tokens: one workgroup per expert streams that expert's
 // fp32 router row; all tokens are accumulated in registers and reduced once.
@@ -203,6 +214,112 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t *__rest
             }
 }
 
+// The same product with the workgroup's operands staged through LDS: each
+// 32-wide K step of the tile's x rows (64 B a row) and router rows (128 B a
+// row, fp32) is copied once by direct-to-LDS loads into a three-stage ring
+// and read by every wave that needs it (16-byte slot q of an x row r at
+// q ^ ((r >> 1) & 3), of a router row at q ^ (r & 7): the fragment reads of
+// 16 consecutive rows then fall on distinct banks).  Same products, same
+// accumulation order per output as router_gemm_kernel.
+__device__ __forceinline__ void rdma16(const void *g, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :: "s"(lds), "v"(g) : "memory", "m0");
+}
+
+template <int WE>
+__global__ __launch_bounds__(256) void router_gemm_lds_kernel(const uint16_t *__restrict__ x,
+                                                              const float *__restrict__ wr,
+                                                              float *__restrict__ part, int T, int d,
+                                                              int E, int kslice)
+{
+    constexpr int WT = 4 / WE;
+    constexpr int TT = 64 * WT, TE = 64 * WE;        // tile tokens, tile experts
+    constexpr int XU = TT * 4, WU = TE * 8;          // 16-byte units per stage
+    constexpr int NL = (XU + WU) / 256;              // loads per thread per stage (6)
+    __shared__ uint4 Xs[3][XU];
+    __shared__ uint4 Ws[3][WU];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int m = lane & 15, g = lane >> 4;
+    const int T0 = blockIdx.x * TT, E0 = blockIdx.y * TE;
+    const int k0 = blockIdx.z * kslice;
+    const int nk = kslice / 32;
+    // load j of this thread: unit u = 256 j + tid of the stage (x units first)
+    const void *src[NL];
+    uint32_t dst[NL];
+    bool isx[NL];
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+        const int u = 256 * j + tid;
+        isx[j] = u < XU;
+        if (u < XU) {
+            const int r = u >> 2, p = u & 3, q = p ^ ((r >> 1) & 3);
+            src[j] = x + (int64_t)min(T0 + r, T - 1) * d + k0 + q * 8;
+        } else {
+            const int v = u - XU, r = v >> 3, p = v & 7, q = p ^ (r & 7);
+            src[j] = wr + (int64_t)min(E0 + r, E - 1) * d + k0 + q * 4;
+        }
+        dst[j] = (uint32_t)(256 * j + wv * 64);  // unit of lane 0 of this wave
+    }
+    auto issue = [&](int kc) {
+        const int b = kc % 3;
+#pragma unroll
+        for (int j = 0; j < NL; ++j) {
+            const uint32_t base = isx[j] ? lds_addr(&Xs[b][dst[j]]) : lds_addr(&Ws[b][dst[j] - XU]);
+            const int64_t off = isx[j] ? (int64_t)kc * 64 : (int64_t)kc * 128;
+            rdma16(static_cast<const uint8_t *>(src[j]) + off,
+                   __builtin_amdgcn_readfirstlane(base));
+        }
+    };
+
+    const int tr0 = (wv % WT) * 64, er0 = (wv / WT) * 64;  // the wave's rows inside the tile
+    floatx4_t acc[4][4];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+
+    issue(0);
+    if (nk > 1) issue(1);
+    for (int kc = 0; kc < nk; ++kc) {
+        if (kc + 1 < nk) asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" :: "n"(NL) : "memory");
+        else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+        if (kc + 2 < nk) issue(kc + 2);
+        const uint4 *X = Xs[kc % 3];
+        const uint4 *W = Ws[kc % 3];
+        uint4 a[4];
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+            const int r = tr0 + mb * 16 + m;
+            a[mb] = X[r * 4 + (g ^ ((r >> 1) & 3))];
+        }
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+            const int r = er0 + nb * 16 + m;
+            const uint4 w0 = W[r * 8 + ((2 * g) ^ (r & 7))], w1 = W[r * 8 + ((2 * g + 1) ^ (r & 7))];
+            uint4 hi, mid, lo;
+            split3_trunc(__builtin_bit_cast(float4, w0), __builtin_bit_cast(float4, w1), hi, mid, lo);
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb) {
+                const bf16x8_t av = as_bf16x8(a[mb]);
+                acc[mb][nb] = mfma16(av, as_bf16x8(lo), acc[mb][nb]);
+                acc[mb][nb] = mfma16(av, as_bf16x8(mid), acc[mb][nb]);
+                acc[mb][nb] = mfma16(av, as_bf16x8(hi), acc[mb][nb]);
+            }
+        }
+    }
+    float *out = part + (int64_t)blockIdx.z * T * E;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = T0 + tr0 + mb * 16 + g * 4 + r, e = E0 + er0 + nb * 16 + m;
+                if (t < T && e < E) out[(int64_t)t * E + e] = acc[mb][nb][r];
+            }
+}
+
 hipError_t launch_router(const Shape &s, const Plan &p, const Workspace &ws, const uint16_t *x,
                          const float *wr, hipStream_t st)
 {
@@ -221,7 +338,12 @@ hipError_t launch_router(const Shape &s, const Plan &p, const Workspace &ws, con
         const int ks = router_splits(s);
         const int tt = router_tile_tokens(s.E), te = router_tile_experts(s.E);
         dim3 grid((s.T + tt - 1) / tt, (s.E + te - 1) / te, ks);
-        if (te == 64)
+        if (kRouterLds) {
+            if (te == 64)
+                router_gemm_lds_kernel<1><<<grid, 256, 0, st>>>(x, wr, ws.scores, s.T, s.d, s.E, s.d / ks);
+            else
+                router_gemm_lds_kernel<2><<<grid, 256, 0, st>>>(x, wr, ws.scores, s.T, s.d, s.E, s.d / ks);
+        } else if (te == 64)
             router_gemm_kernel<1><<<grid, 256, 0, st>>>(x, wr, ws.scores, s.T, s.d, s.E, s.d / ks);
         else
             router_gemm_kernel<2><<<grid, 256, 0, st>>>(x, wr, ws.scores, s.T, s.d, s.E, s.d / ks);
