@@ -509,13 +509,13 @@ extern "C" int moe_layer_forward_nvfp4(const moe_dims_t *dims, const void *x, co
         return mark(debug ? debug->stage_end : nullptr, id);
     };
     auto ok = [](hipError_t e) { return e == hipSuccess; };
-    // the 16-block kernels: 128-row tiles or 16-row tiles (no streaming
-    // kernel); the router does not split x, x is converted to fp16 instead
+    // the 16-block kernels: tiled (kNvTileRows-row tiles), streaming or
+    // 16-row tiles as the plan says; the router does not split x, x is
+    // converted to fp16 instead
     Plan p = make_plan(s);
-    p.stream = false;
-    p.tile_rows = p.tiled ? kNvTileRows : 16;
+    if (p.tiled) p.tile_rows = kNvTileRows;
     Plan pr = p;
-    pr.tiled = false;
+    pr.tiled = pr.stream = false;
     auto route = [&]() -> hipError_t {
         hipError_t e = launch_router(s, pr, ws, xb, router_w, st);
         if (e != hipSuccess) return e;

@@ -1265,13 +1265,18 @@ hipError_t launch_split_x(const Shape &s, const Workspace &ws, const uint16_t *x
 // silu(gate) * up.  Requirements (checked by the plan): d % 2048 == 0,
 // tiles of at most R rows.
 // =========================================================================
-template <int U>
+// NV: weights in the 16-block format, the activations fp16 rows (ghi, as
+// f16_rows_kernel writes them; glo, gsh, gsl unused) with per-token scales
+// xsc, matrix scales gs [E][3]; the chunk is multiplied by four fp16 MFMAs on
+// weights widened in registers (mfma_chunk_nv) instead of the scaled MX MFMA.
+template <int U, bool NV>
 __global__ __launch_bounds__(256) void gemm1_stream_kernel(
     const uint8_t *__restrict__ ghi, const uint8_t *__restrict__ glo,
     const uint8_t *__restrict__ gsh, const uint8_t *__restrict__ gsl,
     const int32_t *__restrict__ perm, const Tile *__restrict__ tiles,
     const int32_t *__restrict__ ntiles, const uint8_t *__restrict__ wpk,
-    const uint8_t *__restrict__ sc, uint16_t *__restrict__ h, int d, int F, int k, int R)
+    const uint8_t *__restrict__ sc, uint16_t *__restrict__ h, int d, int F, int k, int R,
+    const float *__restrict__ xsc, const float *__restrict__ gs)
 {
     constexpr int NB = 2;  // gate block, up block
     extern __shared__ uint4 xs4[];
@@ -1304,7 +1309,8 @@ __global__ __launch_bounds__(256) void gemm1_stream_kernel(
             l_tl = tiles[ti];
             l_ti = ti;
         }
-        const WView v = w1_view(wpk, sc, l_tl.expert, d, F);
+        const WView v = NV ? w1_codes(wpk, l_tl.expert, d, F) : w1_view(wpk, sc, l_tl.expert, d, F);
+        const NvScales vs = w1_nv_scales(sc, l_tl.expert, d, F);
         const int c = c_begin + bt * U;
         const int f = grp * 16 + n, nt = f >> 7;
 #pragma unroll
@@ -1313,7 +1319,8 @@ __global__ __launch_bounds__(256) void gemm1_stream_kernel(
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 b[u][nb] = ld_stream16(v.slot(nt, c + u, rho, g));
-                sv[u][nb] = ld_stream4(v.scales(nt, c + u, rho));
+                if constexpr (NV) sv[u][nb] = __builtin_nontemporal_load(vs.pair(nt, c + u, rho, g));
+                else sv[u][nb] = ld_stream4(v.scales(nt, c + u, rho));
             }
         }
     };
@@ -1325,6 +1332,17 @@ __global__ __launch_bounds__(256) void gemm1_stream_kernel(
         c_tl = tiles[ti];
         c_ti = ti;
         const int q = d / 16, qs = d / 32 / 16;  // 16-byte units per part row / scale row
+        if constexpr (NV) {
+            // fp16 rows of 2d bytes: the space of both FP8 parts
+            for (int r = 0; r < c_tl.nrows; ++r) {
+                const int64_t tok = perm[c_tl.row0 + r] / k;
+                const uint4 *src = reinterpret_cast<const uint4 *>(ghi + tok * 2 * d);
+                uint4 *dst = reinterpret_cast<uint4 *>(xs + (size_t)r * 2 * d);
+                for (int j = threadIdx.x; j < 2 * q; j += 256) dst[j] = src[j];
+            }
+            lds_barrier();
+            return;
+        }
         for (int r = 0; r < c_tl.nrows; ++r) {
             const int64_t tok = perm[c_tl.row0 + r] / k;
             const uint4 *sh = reinterpret_cast<const uint4 *>(ghi + tok * d);
@@ -1357,6 +1375,16 @@ __global__ __launch_bounds__(256) void gemm1_stream_kernel(
         if (ti != c_ti) stage(ti);
         const int m = n < c_tl.nrows ? n : 0;  // rows past nrows are computed on row 0, never stored
         const int c = c_begin + bt * U;
+        if constexpr (NV) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint4 *ap = reinterpret_cast<const uint4 *>(xs + (size_t)m * 2 * d) +
+                                  (c + u) * (kKStep / 8) + g * 4;
+                const uint4 a[4] = {ap[0], ap[1], ap[2], ap[3]};
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) acc[nb] = mfma_chunk_nv(a, b[u][nb], sv[u][nb], acc[nb]);
+            }
+        } else
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const uint4 *hp = reinterpret_cast<const uint4 *>(xhi + (size_t)m * d + (c + u) * kKStep);
@@ -1386,8 +1414,15 @@ __global__ __launch_bounds__(256) void gemm1_stream_kernel(
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int row = g * 4 + r;
-                    if (row < c_tl.nrows)
-                        h[(int64_t)(c_tl.row0 + row) * F + fcol] = f32_to_bf16(silu(acc[0][r]) * acc[1][r]);
+                    if (row < c_tl.nrows) {
+                        float gv = acc[0][r], uv = acc[1][r];
+                        if constexpr (NV) {
+                            const float xr = xsc[perm[c_tl.row0 + row] / k];
+                            gv *= xr * gs[3 * c_tl.expert];
+                            uv *= xr * gs[3 * c_tl.expert + 1];
+                        }
+                        h[(int64_t)(c_tl.row0 + row) * F + fcol] = f32_to_bf16(silu(gv) * uv);
+                    }
                 }
             }
 #pragma unroll
@@ -1458,14 +1493,15 @@ hipError_t launch_gemm1(const Shape &s, const Plan &p, const Workspace &ws, cons
     } else if (p.stream) {
         const int R = p.tile_rows;
         const size_t lds = (size_t)R * (2 * s.d + 2 * (s.d / 32));
-        auto kfn = gemm1_stream_kernel<kG1StreamU>;
+        auto kfn = gemm1_stream_kernel<kG1StreamU, false>;
         const int grid = persistent_grid(reinterpret_cast<const void *>(kfn), lds);
         if (grid <= 0) return hipErrorInvalidConfiguration;
         hipExtLaunchKernelGGL(kfn, dim3(grid), dim3(256), (uint32_t)lds, st, ev0, ev1, 0,
                               (const uint8_t *)ws.xhi, (const uint8_t *)ws.xlo,
                               (const uint8_t *)ws.xshi, (const uint8_t *)ws.xslo,
                               (const int32_t *)ws.perm, (const Tile *)ws.tiles,
-                              (const int32_t *)ws.ntiles, wpk, sc, ws.h, s.d, s.F, s.k, R);
+                              (const int32_t *)ws.ntiles, wpk, sc, ws.h, s.d, s.F, s.k, R,
+                              (const float *)nullptr, (const float *)nullptr);
     } else {
         const int groups = s.F / 16;
         const int64_t grid = max_tiles(s, p.tile_rows) * groups;
@@ -1531,6 +1567,18 @@ hipError_t launch_gemm1_nv(const Shape &s, const Plan &p, const Workspace &ws, c
         const int64_t grid = 8 * ((max_tiles(s, p.tile_rows) * pa.ntn + 7) / 8);
         hipExtLaunchKernelGGL(gemm_nv_kernel<true, kNvTileRows>, dim3((unsigned)grid), dim3(512), 0, st,
                               ev0, ev1, 0, pa);
+    } else if (p.stream) {
+        // the persistent streaming kernel on fp16 rows (staged in the space
+        // of the FP8 parts)
+        const int R = p.tile_rows;
+        const size_t lds = (size_t)R * (2 * s.d + 2 * (s.d / 32));
+        auto kfn = gemm1_stream_kernel<kG1StreamU, true>;
+        const int grid = persistent_grid(reinterpret_cast<const void *>(kfn), lds);
+        if (grid <= 0) return hipErrorInvalidConfiguration;
+        const uint8_t *xb = reinterpret_cast<const uint8_t *>(x16);
+        hipExtLaunchKernelGGL(kfn, dim3(grid), dim3(256), (uint32_t)lds, st, ev0, ev1, 0, xb, xb, xb,
+                              xb, (const int32_t *)ws.perm, (const Tile *)ws.tiles,
+                              (const int32_t *)ws.ntiles, wpk, sc, ws.h, s.d, s.F, s.k, R, xs, gs);
     } else {
         const int groups = s.F / 16;
         const int64_t grid = max_tiles(s, p.tile_rows) * groups;

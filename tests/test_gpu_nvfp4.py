@@ -150,3 +150,19 @@ def test_nv_full_size(name, n):
     r = _check_routing(L, dbg, "nv " + name)
     assert int(r["counts"].sum()) == L.shape.T * L.shape.k
     _check_tokens(L, out, _sample(L.shape.T, n, 7), "nv " + name)
+
+
+@pytest.mark.parametrize("T,d", [(3, 2048), (8, 4096)])
+def test_nv_few_tokens_hot_expert(T, d):
+    # every token picks expert 3 first: on the streaming gate/up kernel its
+    # segment is cut into several 2-row tiles
+    w = synth.custom_workload(T=T, d=d, E=16, k=4, F=256, seed=43 + T, zipf=True)
+    L = synth.make_layer_nv(w, with_tokens=False)
+    L.router_w[:, 0] = 0.0
+    L.router_w[3, 0] = 50.0
+    L.x = synth.make_tokens(w, L.router_w)
+    _say("nv few tokens hot expert", T, d)
+    out, dbg = run_nv(L)
+    _check_routing(L, dbg, f"nv hot T={T} d={d}")
+    assert np.all(dbg["ids"][:, 0] == 3)
+    _check_tokens(L, out, np.arange(T), f"nv hot T={T} d={d}")
