@@ -207,8 +207,8 @@ GATE_UP_KERNEL = {
     "latent_prefill": "gemm_mxw_kernel<true> (gate/up + SwiGLU, 128x512 tiles, MX MFMA)",
     "block4": "gemm1_stream_kernel (gate/up + SwiGLU, persistent, MX MFMA)",
     "block_prefill": "gemm_mxw_kernel<true> (gate/up + SwiGLU, 128x512 tiles, MX MFMA)",
-    "nv4": "gemm1_decode_kernel<4, true> (gate/up + SwiGLU, 16-row tiles, fp16 MFMA, 16-block weights)",
-    "nv_prefill": "gemm_nv_kernel<true> (gate/up + SwiGLU, 128x256 tiles, fp16 MFMA, 16-block weights)",
+    "nv4": "gemm1_stream_kernel<4, true> (gate/up + SwiGLU, persistent, fp16 MFMA, 16-block weights)",
+    "nv_prefill": "gemm_nv_kernel<true, 192> (gate/up + SwiGLU, 192x256 tiles, fp16 MFMA, 16-block weights)",
 }
 
 
