@@ -54,12 +54,30 @@ __device__ __forceinline__ floatx4_t mfma_chunk(const uint4 *a, uint4 b, float s
     return acc;
 }
 
+// E4M3 scale byte -> (the scaled convert's fp32 power of two, the fp16
+// factor pair) for all 256 bytes, one entry per thread of the first 256.
+__device__ __forceinline__ void fill_e4m3_table(uint2 *lut)
+{
+    if (threadIdx.x < 256) {
+        const E4m3Parts e = e4m3_parts(threadIdx.x);
+        lut[threadIdx.x] = make_uint2(__float_as_uint(e.p), __builtin_bit_cast(uint32_t, e.m));
+    }
+}
+
+__device__ __forceinline__ E4m3Parts e4m3_lookup(const uint2 *lut, uint32_t b)
+{
+    const uint2 v = lut[b];
+    return E4m3Parts{__uint_as_float(v.x), __builtin_bit_cast(f16x2_t, v.y)};
+}
+
 // The same K chunk with weights in the 16-block format: the lane's 32 codes
 // are two 16-blocks (b.x, b.y and b.z, b.w) with the E4M3 scale bytes in
-// s2's low and high byte, expanded exactly to fp16; a holds fp16 activations.
-__device__ __forceinline__ floatx4_t mfma_chunk_nv(const uint4 *a, uint4 b, uint32_t s2, floatx4_t acc)
+// s2's low and high byte (decoded through the table lut, fill_e4m3_table),
+// expanded exactly to fp16; a holds fp16 activations.
+__device__ __forceinline__ floatx4_t mfma_chunk_nv(const uint4 *a, uint4 b, uint32_t s2, const uint2 *lut,
+                                                   floatx4_t acc)
 {
-    const E4m3Parts lo = e4m3_parts(s2 & 0xFFu), hi = e4m3_parts((s2 >> 8) & 0xFFu);
+    const E4m3Parts lo = e4m3_lookup(lut, s2 & 0xFFu), hi = e4m3_lookup(lut, (s2 >> 8) & 0xFFu);
     acc = mfma16h(as_f16x8(a[0]), fp4x8_to_f16(b.x, lo), acc);
     acc = mfma16h(as_f16x8(a[1]), fp4x8_to_f16(b.y, lo), acc);
     acc = mfma16h(as_f16x8(a[2]), fp4x8_to_f16(b.z, hi), acc);
@@ -193,14 +211,16 @@ __global__ __launch_bounds__(256) void gemm1_decode_kernel(
     };
     // the first batch of weight loads goes out before the activations are staged
     load_b(c_begin);
+    __shared__ uint2 lut[NV ? 256 : 1];
+    if constexpr (NV) fill_e4m3_table(lut);
     if (use_lds) {
         for (int q = threadIdx.x; q < tl.nrows * rowq; q += 256) {
             const int r = q / rowq, c = q - r * rowq;
             const int tok = perm[tl.row0 + r] / k;
             arows[q] = *reinterpret_cast<const uint4 *>(x + (int64_t)tok * d + c * 8);
         }
-        __syncthreads();
     }
+    if (NV || use_lds) __syncthreads();
     const uint16_t *ap = x + (int64_t)(valid ? perm[tl.row0 + n] / k : 0) * d + g * 32;
     const uint4 *al = arows + n * rowq + g * 4;
 
@@ -221,7 +241,7 @@ __global__ __launch_bounds__(256) void gemm1_decode_kernel(
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) {
                     if constexpr (NV)
-                        acc[nb] = mfma_chunk_nv(a, b[u][nb], sw[u][nb], acc[nb]);
+                        acc[nb] = mfma_chunk_nv(a, b[u][nb], sw[u][nb], lut, acc[nb]);
                     else
                         acc[nb] = mfma_chunk(a, b[u][nb], e8m0_to_f32((sw[u][nb] >> (8 * g)) & 0xFFu),
                                              acc[nb]);
@@ -303,11 +323,13 @@ __global__ __launch_bounds__(256) void gemm2_decode_kernel(
 #pragma unroll
     for (int r = 0; r < 4; ++r) dst[r] = g * 4 + r < tl.nrows ? perm[tl.row0 + g * 4 + r] : 0;
     const int dst_ss = (int)threadIdx.x < tl.nrows && threadIdx.x < 16 ? perm[tl.row0 + threadIdx.x] : 0;
+    __shared__ uint2 lut[NV ? 256 : 1];
+    if constexpr (NV) fill_e4m3_table(lut);
     if (use_lds) {
         const uint4 *src = reinterpret_cast<const uint4 *>(h + (int64_t)tl.row0 * F);
         for (int q = threadIdx.x; q < tl.nrows * rowq; q += 256) arows[q] = src[q];
-        __syncthreads();
     }
+    if (NV || use_lds) __syncthreads();
     const uint16_t *ap = h + (int64_t)(tl.row0 + (valid ? n : 0)) * F + g * 32;
     const uint4 *al = arows + n * rowq + g * 4;
 
@@ -324,7 +346,7 @@ __global__ __launch_bounds__(256) void gemm2_decode_kernel(
                     else a[s] = *reinterpret_cast<const uint4 *>(ap + (c + u) * kKStep + s * 8);
                 }
                 if constexpr (NV)
-                    acc = mfma_chunk_nv(a, b[u], sw[u], acc);
+                    acc = mfma_chunk_nv(a, b[u], sw[u], lut, acc);
                 else
                     acc = mfma_chunk(a, b[u], e8m0_to_f32((sw[u] >> (8 * g)) & 0xFFu), acc);
             }
@@ -923,22 +945,6 @@ struct NvArgs {
     int d, F, k, ntn;
 };
 
-// E4M3 scale byte -> (the scaled convert's fp32 power of two, the fp16
-// factor pair) for all 256 bytes, one entry per thread of the first 256.
-__device__ __forceinline__ void fill_e4m3_table(uint2 *lut)
-{
-    if (threadIdx.x < 256) {
-        const E4m3Parts e = e4m3_parts(threadIdx.x);
-        lut[threadIdx.x] = make_uint2(__float_as_uint(e.p), __builtin_bit_cast(uint32_t, e.m));
-    }
-}
-
-__device__ __forceinline__ E4m3Parts e4m3_lookup(const uint2 *lut, uint32_t b)
-{
-    const uint2 v = lut[b];
-    return E4m3Parts{__uint_as_float(v.x), __builtin_bit_cast(f16x2_t, v.y)};
-}
-
 template <bool GATE_UP, int MR>
 __global__ __launch_bounds__(512) void gemm_nv_kernel(const NvArgs pa)
 {
@@ -1363,6 +1369,10 @@ __global__ __launch_bounds__(256) void gemm1_stream_kernel(
         lds_barrier();
     };
 
+    // NV: the scale table, written before the first stage() barrier
+    __shared__ uint2 lut[NV ? 256 : 1];
+    if constexpr (NV) fill_e4m3_table(lut);
+
     floatx4_t acc[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[nb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
@@ -1382,7 +1392,7 @@ __global__ __launch_bounds__(256) void gemm1_stream_kernel(
                                   (c + u) * (kKStep / 8) + g * 4;
                 const uint4 a[4] = {ap[0], ap[1], ap[2], ap[3]};
 #pragma unroll
-                for (int nb = 0; nb < NB; ++nb) acc[nb] = mfma_chunk_nv(a, b[u][nb], sv[u][nb], acc[nb]);
+                for (int nb = 0; nb < NB; ++nb) acc[nb] = mfma_chunk_nv(a, b[u][nb], sv[u][nb], lut, acc[nb]);
             }
         } else
 #pragma unroll
