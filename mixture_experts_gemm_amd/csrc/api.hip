@@ -518,14 +518,14 @@ extern "C" int moe_layer_forward_nvfp4(const moe_dims_t *dims, const void *x, co
     pr.tiled = pr.stream = false;
     auto route = [&]() -> hipError_t {
         hipError_t e = launch_router(s, pr, ws, xb, router_w, st);
-        if (e != hipSuccess) return e;
+        if (e != hipSuccess || p.stream) return e;  // the streaming kernel converts x itself
         return launch_f16_rows(xb, s.T, s.d, reinterpret_cast<uint16_t *>(ws.xhi),
                                reinterpret_cast<float *>(ws.xshi), st);
     };
     if (!stage(MOE_STAGE_ROUTER, route) ||
         !stage(MOE_STAGE_TOPK, [&] { return launch_topk(s, p, ws, st); }) ||
         !stage(MOE_STAGE_GROUP, [&] { return launch_group(s, p, ws, st); }) ||
-        !ok(launch_gemm1_nv(s, p, ws, expert_w_packed, scales16, gscale, st,
+        !ok(launch_gemm1_nv(s, p, ws, xb, expert_w_packed, scales16, gscale, st,
                             stage_event(debug, MOE_STAGE_GEMM1, true),
                             stage_event(debug, MOE_STAGE_GEMM1, false))) ||
         !stage(MOE_STAGE_GEMM2,

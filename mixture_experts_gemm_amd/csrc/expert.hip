@@ -44,6 +44,7 @@ constexpr int kDecodeLdsBytes = MOE_DEC_LDS;
 constexpr int kG1StreamU = MOE_G1SU;
 constexpr int kMxWaves = MOE_MX_WAVES;
 constexpr int kUnroll = 4;  // chunks per weight batch of the decode kernels
+constexpr size_t kNvFuseLds = 64 * 1024;  // LDS the 16-block down kernel may take for its own h rows
 
 __device__ __forceinline__ floatx4_t mfma_chunk(const uint4 *a, uint4 b, float scale, floatx4_t acc)
 {
@@ -83,6 +84,63 @@ __device__ __forceinline__ floatx4_t mfma_chunk_nv(const uint4 *a, uint4 b, uint
     acc = mfma16h(as_f16x8(a[2]), fp4x8_to_f16(b.z, hi), acc);
     acc = mfma16h(as_f16x8(a[3]), fp4x8_to_f16(b.w, hi), acc);
     return acc;
+}
+
+// bf16 rows -> fp16 rows for the 16-block kernels: a row is multiplied by
+// 2^q, q chosen so its largest magnitude lands in [2^14, 2^15) (q <= 126),
+// and its scale is 2^-q.  Exact for every element down to 2^-32 of the row's
+// largest (fp16 keeps 11 significant bits, bf16 has 8); smaller ones round
+// to the fp16 subnormal grid.  One row of n 16-byte units by the whole
+// 256-thread workgroup (every thread calls it); dst may be global or LDS;
+// wmax is 4 words of LDS.  Returns the row's scale.
+__device__ float f16_row_block(const uint4 *__restrict__ s4, uint4 *d4, int n, uint32_t *wmax)
+{
+    uint32_t mx = 0;
+    for (int i = threadIdx.x; i < n; i += 256) {
+        const uint4 v = s4[i];
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            mx = max(mx, w[j] & 0x7FFFu);
+            mx = max(mx, (w[j] >> 16) & 0x7FFFu);
+        }
+    }
+    // magnitudes of bf16 order as their bit patterns: an integer max
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, off));
+    if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = mx;
+    __syncthreads();
+    mx = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+    const int eb = (int)(mx >> 7);  // biased exponent of the largest magnitude
+    int q = mx == 0 ? 0 : (eb == 0 ? 126 : 14 - (eb - 127));
+    q = q > 126 ? 126 : q;
+    const float f = pow2f(q);
+    for (int i = threadIdx.x; i < n; i += 256) {
+        const uint4 v = s4[i];
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        uint32_t o[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const _Float16 lo = (_Float16)(bf16_to_f32((uint16_t)(w[j] & 0xFFFFu)) * f);
+            const _Float16 hi = (_Float16)(bf16_to_f32((uint16_t)(w[j] >> 16)) * f);
+            o[j] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+        }
+        d4[i] = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+    __syncthreads();  // wmax is free again, dst complete
+    return pow2f(-q);
+}
+
+// One workgroup per row, K a multiple of 8.
+__global__ __launch_bounds__(256) void f16_rows_kernel(const uint16_t *__restrict__ src, int K,
+                                                       uint16_t *__restrict__ dst,
+                                                       float *__restrict__ scale)
+{
+    __shared__ uint32_t wmax[4];
+    const int64_t row = blockIdx.x;
+    const float sc = f16_row_block(reinterpret_cast<const uint4 *>(src + row * K),
+                                   reinterpret_cast<uint4 *>(dst + row * K), K / 8, wmax);
+    if (threadIdx.x == 0) scale[row] = sc;
 }
 
 // ---- small device helpers ---------------------------------------------------
@@ -281,13 +339,16 @@ __global__ __launch_bounds__(256) void gemm1_decode_kernel(
 // row r goes to slot perm[r]), so the combine step finds a token's k rows at
 // slots t*k .. t*k+k-1 without a lookup.
 // NV: the 16-block format with fp16 h rows and their scales hs (grouped
-// order), as gemm1_decode_kernel.
+// order), as gemm1_decode_kernel; with fuse, h is the bf16 rows and each
+// workgroup converts its tile's rows into LDS itself (f16_row_block; every
+// tile's rows must fit: rows_fit >= its rows).
 template <int U, bool NV>
 __global__ __launch_bounds__(256) void gemm2_decode_kernel(
     const uint16_t *__restrict__ h, const int32_t *__restrict__ perm, const Tile *__restrict__ tiles,
     const int32_t *__restrict__ ntiles, const uint8_t *__restrict__ wpk,
     const uint8_t *__restrict__ sc, uint16_t *__restrict__ o, float *__restrict__ ssq, int d,
-    int F, int wgs_per_tile, int rows_fit, const float *__restrict__ hs, const float *__restrict__ gs)
+    int F, int wgs_per_tile, int rows_fit, const float *__restrict__ hs, const float *__restrict__ gs,
+    bool fuse)
 {
     extern __shared__ uint4 arows[];  // [rows_fit][F/8]
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -324,8 +385,16 @@ __global__ __launch_bounds__(256) void gemm2_decode_kernel(
     for (int r = 0; r < 4; ++r) dst[r] = g * 4 + r < tl.nrows ? perm[tl.row0 + g * 4 + r] : 0;
     const int dst_ss = (int)threadIdx.x < tl.nrows && threadIdx.x < 16 ? perm[tl.row0 + threadIdx.x] : 0;
     __shared__ uint2 lut[NV ? 256 : 1];
+    __shared__ uint32_t wmax[4];
+    __shared__ float rsc[16];
     if constexpr (NV) fill_e4m3_table(lut);
-    if (use_lds) {
+    if (NV && fuse) {
+        for (int r = 0; r < tl.nrows; ++r) {
+            const float sc = f16_row_block(reinterpret_cast<const uint4 *>(h + (int64_t)(tl.row0 + r) * F),
+                                           arows + r * rowq, rowq, wmax);
+            if (threadIdx.x == 0) rsc[r] = sc;
+        }
+    } else if (use_lds) {
         const uint4 *src = reinterpret_cast<const uint4 *>(h + (int64_t)tl.row0 * F);
         for (int q = threadIdx.x; q < tl.nrows * rowq; q += 256) arows[q] = src[q];
     }
@@ -362,7 +431,10 @@ __global__ __launch_bounds__(256) void gemm2_decode_kernel(
     for (int r = 0; r < 4; ++r) {
         const int row = g * 4 + r;
         float val = acc[r];
-        if constexpr (NV) val *= hs[tl.row0 + (row < tl.nrows ? row : 0)] * gd;
+        if constexpr (NV) {
+            const int rr = row < tl.nrows ? row : 0;
+            val *= (fuse ? rsc[rr] : hs[tl.row0 + rr]) * gd;
+        }
         if (row < tl.nrows) o[(int64_t)dst[r] * d + col0 + n] = f32_to_bf16(val);
         const float ss = sum16(val * val);
         if (n == 0) wsum[wv][g * 4 + r] = ss;
@@ -1122,55 +1194,6 @@ __global__ __launch_bounds__(512) void gemm_nv_kernel(const NvArgs pa)
     }
 }
 
-// bf16 rows -> fp16 rows for the 16-block kernels: row r is multiplied by
-// 2^q, q chosen so its largest magnitude lands in [2^14, 2^15) (q <= 126),
-// and scale[r] = 2^-q.  Exact for every element down to 2^-32 of the row's
-// largest (fp16 keeps 11 significant bits, bf16 has 8); smaller ones round
-// to the fp16 subnormal grid.  One workgroup per row, K a multiple of 8.
-__global__ __launch_bounds__(256) void f16_rows_kernel(const uint16_t *__restrict__ src, int K,
-                                                       uint16_t *__restrict__ dst,
-                                                       float *__restrict__ scale)
-{
-    const int64_t row = blockIdx.x;
-    const uint4 *s4 = reinterpret_cast<const uint4 *>(src + row * K);
-    uint4 *d4 = reinterpret_cast<uint4 *>(dst + row * K);
-    const int n = K / 8;
-    uint32_t mx = 0;
-    for (int i = threadIdx.x; i < n; i += 256) {
-        const uint4 v = s4[i];
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            mx = max(mx, w[j] & 0x7FFFu);
-            mx = max(mx, (w[j] >> 16) & 0x7FFFu);
-        }
-    }
-    // magnitudes of bf16 order as their bit patterns: an integer max
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, off));
-    __shared__ uint32_t wmax[4];
-    if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = mx;
-    __syncthreads();
-    mx = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
-    const int eb = (int)(mx >> 7);  // biased exponent of the largest magnitude
-    int q = mx == 0 ? 0 : (eb == 0 ? 126 : 14 - (eb - 127));
-    q = q > 126 ? 126 : q;
-    const float f = pow2f(q);
-    for (int i = threadIdx.x; i < n; i += 256) {
-        const uint4 v = s4[i];
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-        uint32_t o[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const _Float16 lo = (_Float16)(bf16_to_f32((uint16_t)(w[j] & 0xFFFFu)) * f);
-            const _Float16 hi = (_Float16)(bf16_to_f32((uint16_t)(w[j] >> 16)) * f);
-            o[j] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
-        }
-        d4[i] = make_uint4(o[0], o[1], o[2], o[3]);
-    }
-    if (threadIdx.x == 0) scale[row] = pow2f(-q);
-}
-
 hipError_t launch_f16_rows(const uint16_t *src, int64_t rows, int K, uint16_t *dst, float *scale,
                            hipStream_t st)
 {
@@ -1271,9 +1294,9 @@ hipError_t launch_split_x(const Shape &s, const Workspace &ws, const uint16_t *x
 // silu(gate) * up.  Requirements (checked by the plan): d % 2048 == 0,
 // tiles of at most R rows.
 // =========================================================================
-// NV: weights in the 16-block format, the activations fp16 rows (ghi, as
-// f16_rows_kernel writes them; glo, gsh, gsl unused) with per-token scales
-// xsc, matrix scales gs [E][3]; the chunk is multiplied by four fp16 MFMAs on
+// NV: weights in the 16-block format, the activations the bf16 rows of x
+// (ghi; glo, gsh, gsl, xsc unused), converted to fp16 with a scale per row
+// as the tile is staged (f16_row_block), matrix scales gs [E][3]; the chunk is multiplied by four fp16 MFMAs on
 // weights widened in registers (mfma_chunk_nv) instead of the scaled MX MFMA.
 template <int U, bool NV>
 __global__ __launch_bounds__(256) void gemm1_stream_kernel(
@@ -1287,6 +1310,11 @@ __global__ __launch_bounds__(256) void gemm1_stream_kernel(
     constexpr int NB = 2;  // gate block, up block
     extern __shared__ uint4 xs4[];
     __shared__ floatx4_t red[2][3][NB][64];
+    // NV: the E4M3 table and the staged rows' scales (R <= 16, checked by
+    // the launcher)
+    __shared__ uint2 lut[NV ? 256 : 1];
+    __shared__ uint32_t wmax[4];
+    __shared__ float rsc[16];
     uint8_t *xs = reinterpret_cast<uint8_t *>(xs4);
     uint8_t *xhi = xs, *xlo = xs + (size_t)R * d;
     uint8_t *xsh = xs + (size_t)2 * R * d, *xsl = xsh + (size_t)R * (d / 32);
@@ -1339,12 +1367,14 @@ __global__ __launch_bounds__(256) void gemm1_stream_kernel(
         c_ti = ti;
         const int q = d / 16, qs = d / 32 / 16;  // 16-byte units per part row / scale row
         if constexpr (NV) {
-            // fp16 rows of 2d bytes: the space of both FP8 parts
+            // the bf16 rows converted here (f16_row_block) into fp16 rows of
+            // 2d bytes, the space of both FP8 parts, with their scales
             for (int r = 0; r < c_tl.nrows; ++r) {
                 const int64_t tok = perm[c_tl.row0 + r] / k;
-                const uint4 *src = reinterpret_cast<const uint4 *>(ghi + tok * 2 * d);
-                uint4 *dst = reinterpret_cast<uint4 *>(xs + (size_t)r * 2 * d);
-                for (int j = threadIdx.x; j < 2 * q; j += 256) dst[j] = src[j];
+                const float sc = f16_row_block(reinterpret_cast<const uint4 *>(ghi + tok * 2 * d),
+                                               reinterpret_cast<uint4 *>(xs + (size_t)r * 2 * d), 2 * q,
+                                               wmax);
+                if (threadIdx.x == 0) rsc[r] = sc;
             }
             lds_barrier();
             return;
@@ -1370,7 +1400,6 @@ __global__ __launch_bounds__(256) void gemm1_stream_kernel(
     };
 
     // NV: the scale table, written before the first stage() barrier
-    __shared__ uint2 lut[NV ? 256 : 1];
     if constexpr (NV) fill_e4m3_table(lut);
 
     floatx4_t acc[NB];
@@ -1427,7 +1456,7 @@ __global__ __launch_bounds__(256) void gemm1_stream_kernel(
                     if (row < c_tl.nrows) {
                         float gv = acc[0][r], uv = acc[1][r];
                         if constexpr (NV) {
-                            const float xr = xsc[perm[c_tl.row0 + row] / k];
+                            const float xr = rsc[row];
                             gv *= xr * gs[3 * c_tl.expert];
                             uv *= xr * gs[3 * c_tl.expert + 1];
                         }
@@ -1557,7 +1586,7 @@ hipError_t launch_gemm2(const Shape &s, const Plan &p, const Workspace &ws, cons
         const size_t lds = (size_t)rows_fit * s.F * 2;
         gemm2_decode_kernel<kUnroll, false><<<(unsigned)grid, 256, lds, st>>>(
             ws.h, ws.perm, ws.tiles, ws.ntiles, wpk, sc, ws.o, ws.ssq, s.d, s.F, wgs, rows_fit,
-            nullptr, nullptr);
+            nullptr, nullptr, false);
     }
     return hipGetLastError();
 }
@@ -1565,9 +1594,9 @@ hipError_t launch_gemm2(const Shape &s, const Plan &p, const Workspace &ws, cons
 // ---- the 16-block format --------------------------------------------------------
 
 // x was converted to fp16 rows (ws.xhi) with scales (ws.xshi) after the router.
-hipError_t launch_gemm1_nv(const Shape &s, const Plan &p, const Workspace &ws, const uint8_t *wpk,
-                           const uint8_t *sc, const float *gs, hipStream_t st, hipEvent_t ev0,
-                           hipEvent_t ev1)
+hipError_t launch_gemm1_nv(const Shape &s, const Plan &p, const Workspace &ws, const uint16_t *x,
+                           const uint8_t *wpk, const uint8_t *sc, const float *gs, hipStream_t st,
+                           hipEvent_t ev0, hipEvent_t ev1)
 {
     const uint16_t *x16 = reinterpret_cast<const uint16_t *>(ws.xhi);
     const float *xs = reinterpret_cast<const float *>(ws.xshi);
@@ -1578,14 +1607,15 @@ hipError_t launch_gemm1_nv(const Shape &s, const Plan &p, const Workspace &ws, c
         hipExtLaunchKernelGGL(gemm_nv_kernel<true, kNvTileRows>, dim3((unsigned)grid), dim3(512), 0, st,
                               ev0, ev1, 0, pa);
     } else if (p.stream) {
-        // the persistent streaming kernel on fp16 rows (staged in the space
-        // of the FP8 parts)
+        // the persistent streaming kernel: it converts the bf16 x rows of a
+        // tile into fp16 as it stages them (in the space of the FP8 parts)
         const int R = p.tile_rows;
+        if (R > 16) return hipErrorInvalidConfiguration;
         const size_t lds = (size_t)R * (2 * s.d + 2 * (s.d / 32));
         auto kfn = gemm1_stream_kernel<kG1StreamU, true>;
         const int grid = persistent_grid(reinterpret_cast<const void *>(kfn), lds);
         if (grid <= 0) return hipErrorInvalidConfiguration;
-        const uint8_t *xb = reinterpret_cast<const uint8_t *>(x16);
+        const uint8_t *xb = reinterpret_cast<const uint8_t *>(x);
         hipExtLaunchKernelGGL(kfn, dim3(grid), dim3(256), (uint32_t)lds, st, ev0, ev1, 0, xb, xb, xb,
                               xb, (const int32_t *)ws.perm, (const Tile *)ws.tiles,
                               (const int32_t *)ws.ntiles, wpk, sc, ws.h, s.d, s.F, s.k, R, xs, gs);
@@ -1610,8 +1640,15 @@ hipError_t launch_gemm2_nv(const Shape &s, const Plan &p, const Workspace &ws, c
 {
     uint16_t *h16 = reinterpret_cast<uint16_t *>(ws.hhi);
     float *hs = reinterpret_cast<float *>(ws.hshi);
-    hipError_t e = launch_f16_rows(ws.h, s.S(), s.F, h16, hs, st);
-    if (e != hipSuccess) return e;
+    // few-row tiles hold at most min(T, tile_rows) rows (a token picks an
+    // expert once); when they fit in kNvFuseLds the down kernel converts h
+    // itself, else h is converted first
+    const int mr = s.T < p.tile_rows ? s.T : p.tile_rows;
+    const bool fuse = !p.tiled && mr <= 16 && (size_t)mr * s.F * 2 <= kNvFuseLds;
+    if (!fuse) {
+        const hipError_t e = launch_f16_rows(ws.h, s.S(), s.F, h16, hs, st);
+        if (e != hipSuccess) return e;
+    }
     if (p.tiled) {
         NvArgs pa{h16, hs, nullptr, ws.tiles, ws.ntiles, wpk, sc, gs, ws.o, ws.ssq,
                   s.d, s.F, s.k, s.d / 256};
@@ -1623,9 +1660,11 @@ hipError_t launch_gemm2_nv(const Shape &s, const Plan &p, const Workspace &ws, c
         int rows_fit = kDecodeLdsBytes / (s.F * 2);
         rows_fit = rows_fit < s.T ? rows_fit : s.T;
         if (rows_fit > 16) rows_fit = 16;
+        if (fuse) rows_fit = mr;
         const size_t lds = (size_t)rows_fit * s.F * 2;
         gemm2_decode_kernel<kUnroll, true><<<(unsigned)grid, 256, lds, st>>>(
-            h16, ws.perm, ws.tiles, ws.ntiles, wpk, sc, ws.o, ws.ssq, s.d, s.F, wgs, rows_fit, hs, gs);
+            fuse ? ws.h : h16, ws.perm, ws.tiles, ws.ntiles, wpk, sc, ws.o, ws.ssq, s.d, s.F, wgs,
+            rows_fit, hs, gs, fuse);
     }
     return hipGetLastError();
 }

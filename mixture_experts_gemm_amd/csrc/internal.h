@@ -200,10 +200,11 @@ hipError_t launch_pack_nv(const uint8_t *w, const uint8_t *s16, int E, int d, in
 // bf16 rows -> fp16 rows times a per-row power of two, scale[r] = its inverse.
 hipError_t launch_f16_rows(const uint16_t *src, int64_t rows, int K, uint16_t *dst, float *scale,
                            hipStream_t st);
-// Expects x converted by launch_f16_rows into ws.xhi (rows) / ws.xshi (scales).
-hipError_t launch_gemm1_nv(const Shape &s, const Plan &p, const Workspace &ws, const uint8_t *wpk,
-                           const uint8_t *sc, const float *gs, hipStream_t st, hipEvent_t ev_begin,
-                           hipEvent_t ev_end);
+// The streaming plan reads the bf16 x itself; the others expect x converted
+// by launch_f16_rows into ws.xhi (rows) / ws.xshi (scales).
+hipError_t launch_gemm1_nv(const Shape &s, const Plan &p, const Workspace &ws, const uint16_t *x,
+                           const uint8_t *wpk, const uint8_t *sc, const float *gs, hipStream_t st,
+                           hipEvent_t ev_begin, hipEvent_t ev_end);
 hipError_t launch_gemm2_nv(const Shape &s, const Plan &p, const Workspace &ws, const uint8_t *wpk,
                            const uint8_t *sc, const float *gs, hipStream_t st);
 hipError_t launch_dequant(const uint8_t *codes, const uint8_t *scales, int64_t rows, int K,
