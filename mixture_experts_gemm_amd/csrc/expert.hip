@@ -985,8 +985,8 @@ __global__ __launch_bounds__(512) void gemm_mxw_kernel(const MxArgs pa)
 }
 
 // =========================================================================
-// The 16-block format (prefill): tiles of <= 128 grouped rows x 256 weight
-// rows, all of K, on the fp16 MFMA (16x16x32).  The scaled MX MFMA takes one
+// The 16-block format (prefill): tiles of <= MR (192, or 128) grouped rows x
+// 256 weight rows, all of K, on the fp16 MFMA (16x16x32).  The scaled MX MFMA takes one
 // power-of-two scale per 32 values, so it cannot take these weights; they
 // are expanded in registers instead ("Muse Spark Open を段階的に分解する",
 // section ⑪: the 4-bit weights are widened for the multiply), exactly, to
@@ -994,14 +994,16 @@ __global__ __launch_bounds__(512) void gemm_mxw_kernel(const MxArgs pa)
 // The activations are fp16 rows with a power-of-two scale per row
 // (f16_rows_kernel), applied with the matrix scale in the epilogue.
 //
-// Three-stage LDS ring per 128-wide K chunk, filled by direct-to-LDS loads:
-// A 128 rows x 256 bytes (16-byte slot q of row r at q ^ (r & 7)), the
-// chunk's code tile and scale tile copied linearly (the packed layout is the
-// LDS layout); 50 KB a stage.  8 waves as 2 (rows) x 4 (columns): each wave
-// owns 64 rows x 64 weight rows (4 x 4 blocks of 16x16), so each wave
-// expands a weight value once per 64 rows it multiplies.  For gate/up a
-// wave's 64 weight rows are 32 gate features and the same 32 up features,
-// so SwiGLU is formed in registers.
+// LDS ring per 128-wide K chunk, filled by direct-to-LDS loads: A MR rows x
+// 256 bytes (16-byte slot q of row r at q ^ (r & 7)), the chunk's code tile
+// and scale tile copied linearly (the packed layout is the LDS layout);
+// 66 KB a stage and two stages for MR = 192 (one expert's prefill rows in
+// one tile, so its weights are loaded and widened once), 50 KB and three
+// for MR = 128.  8 waves as 2 (rows) x 4 (columns): wave row wm takes the
+// 16-row blocks 2j + wm, each wave 64 weight rows (4 column blocks), so a
+// wave widens a weight value once per chunk for all the rows it multiplies.
+// For gate/up a wave's 64 weight rows are 32 gate features and the same 32
+// up features, so SwiGLU is formed in registers.
 // =========================================================================
 struct NvArgs {
     const uint16_t *a;   // fp16 rows: x [T][d] (gate/up, gathered by perm) or h [S][F] (down)
