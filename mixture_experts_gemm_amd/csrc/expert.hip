@@ -9,7 +9,10 @@
 //              kernels expand FP4 E2M1 x E8M0 into bf16 MFMA operands with the
 //              gfx950 scaled convert; the streaming and tiled kernels feed the
 //              codes and scales unexpanded to the scaled MX MFMA, with the
-//              bf16 activations split exactly into two FP8 parts;
+//              bf16 activations split exactly into FP8 or FP6 parts.  The
+//              16-block format (one E4M3 scale per 16 values) is expanded
+//              exactly to fp16 and multiplied with fp16 activations
+//              (gemm_nv_kernel and the NV forms of the few-row kernels);
 //   section ⑬  below ~58 tokens per expert the time is the weight read, above
 //              it the multiply: the decode kernels are built to keep weight
 //              bytes in flight, the tiled kernels to keep the MFMA pipe busy.
