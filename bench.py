@@ -310,9 +310,22 @@ def time_workload(name, steps, warmup, device):
     out_ok = bool(torch.isfinite(out.float()).all())
     S = T * s.k
     u_mean = sum(U) / len(U)
+    # Per-step latency distribution, in a separate pass after the timed
+    # region (events around every call stall the queue a little, so these
+    # steps are not part of `value`): p10, median and p90 over n steps.
+    n_lat = min(steps, 50)
+    lat = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_lat)]
+    for i, (a, b) in enumerate(lat):
+        a.record()
+        call(i)
+        b.record()
+    torch.cuda.synchronize()
+    step_us = sorted(a.elapsed_time(b) * 1e3 for a, b in lat)
+    pct = lambda q: step_us[min(len(step_us) - 1, int(round(q * (len(step_us) - 1))))]
     res = dict(
         T=T, steps=steps, ms_per_step=elapsed / steps * 1e3, tokens_per_s=T * steps / elapsed,
         gemm1_ms=g1_ms, gemm1_timed_launches=len(timed), distinct_experts_mean=u_mean, finite=out_ok,
+        step_us_p10_p50_p90=[pct(0.1), pct(0.5), pct(0.9)], step_us_samples=n_lat,
     )
     # the gate/up kernel's algorithmic bytes (over the timed launches: U, the
     # distinct experts, differs per step) and flops; its bound is the larger
@@ -431,6 +444,7 @@ def main():
                    "distinct_experts_mean": main_res["distinct_experts_mean"]},
         "roofline": {k: v for k, v in main_res["roofline"].items()
                      if k in ("bound", "achieved", "peak", "unit", "frac", "traffic")},
+        "step_us_p10_p50_p90": main_res["step_us_p10_p50_p90"],
         "cpu_baseline": cpu,
         "also": {k: {kk: vv for kk, vv in v.items()} for k, v in also.items()},
     }
