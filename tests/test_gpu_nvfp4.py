@@ -166,3 +166,17 @@ def test_nv_few_tokens_hot_expert(T, d):
     _check_routing(L, dbg, f"nv hot T={T} d={d}")
     assert np.all(dbg["ids"][:, 0] == 3)
     _check_tokens(L, out, np.arange(T), f"nv hot T={T} d={d}")
+
+
+def test_nv_skewed_full_size():
+    # Zipf-biased routing: the hottest expert's segment spans dozens of
+    # 192-row tiles; tokens routed to it are among those checked
+    L = synth.make_layer_nv("skewed", threads=16)
+    _say("nv skewed T", L.shape.T)
+    out, dbg = run_nv(L)
+    r = _check_routing(L, dbg, "nv skewed")
+    hot = int(np.argmax(r["counts"]))
+    _say("nv skewed largest segment", int(r["counts"].max()))
+    hot_tokens = np.nonzero(np.any(r["ids"] == hot, axis=1))[0][:4]
+    tokens = np.array(sorted(set(_sample(L.shape.T, 8, 9).tolist()) | set(hot_tokens.tolist())), np.int32)
+    _check_tokens(L, out, tokens, "nv skewed")
