@@ -180,3 +180,33 @@ def test_nv_skewed_full_size():
     hot_tokens = np.nonzero(np.any(r["ids"] == hot, axis=1))[0][:4]
     tokens = np.array(sorted(set(_sample(L.shape.T, 8, 9).tolist()) | set(hot_tokens.tolist())), np.int32)
     _check_tokens(L, out, tokens, "nv skewed")
+
+
+def _scaled_rows(L):
+    """Rows of x multiplied by 1, 2^6, 2^13, 2^20 in turn (exact in bf16;
+    scaling up only widens the router margins), alpha = 0 so the output is
+    beta * y alone.  Returns the layer and the row scales."""
+    f = synth.bf16_bits_to_f32(L.x).astype(np.float32)
+    scale = np.array([1.0, 2.0 ** 6, 2.0 ** 13, 2.0 ** 20], np.float32)[np.arange(L.x.shape[0]) % 4]
+    L.x = synth.f32_to_bf16_bits(f * scale[:, None])
+    L.alpha[:] = 0.0
+    return L, scale
+
+
+def _check_scaled_routing(L, dbg, scale, label):
+    """Routing bit-exact; weights to 1e-5 times the row's scale (the fp32
+    scores and their rounding differences grow with the row)."""
+    r = oracle.route(L.x, L.router_w, L.k)
+    for n in ("ids", "offsets", "perm", "inv"):
+        np.testing.assert_array_equal(dbg[n], r[n], err_msg=label)
+    assert np.all(np.abs(dbg["weights"] - r["w"]) <= WEIGHT_TOL * np.maximum(scale, 1.0)[:, None]), label
+
+
+def test_nv_rows_of_very_different_magnitude():
+    for name, T in (("tiny", 64), ("prefill", 256), ("decode4", None)):
+        L, scale = _scaled_rows(synth.make_layer_nv(name, T=T))
+        _say("nv scaled rows", name, L.shape.T)
+        out, dbg = run_nv(L)
+        _check_scaled_routing(L, dbg, scale, f"nv scaled rows {name}")
+        tokens = np.arange(L.shape.T) if L.shape.T <= 64 else _sample(L.shape.T, 12, 4)
+        _check_tokens(L, out, tokens, f"nv scaled rows {name}")

@@ -421,3 +421,31 @@ def _oracle_prenorm(x_bits, gamma, eps):
     x = synth.bf16_bits_to_f32(x_bits).astype(np.float64)
     r = 1.0 / np.sqrt(np.mean(x * x, axis=1, keepdims=True) + eps)
     return x * r * gamma.astype(np.float64)
+
+
+def _check_scaled_routing(L, dbg, scale, label):
+    """Routing bit-exact; weights to 1e-5 times the row's scale: the fp32
+    scores (and the few ulps by which two summation orders differ) grow with
+    the row, and so do the softmax weights' differences."""
+    r = oracle.route(L.x, L.router_w, L.k)
+    for n in ("ids", "offsets", "perm", "inv"):
+        np.testing.assert_array_equal(dbg[n], r[n], err_msg=label)
+    tol = WEIGHT_TOL * np.maximum(scale, 1.0)[:, None]
+    assert np.all(np.abs(dbg["weights"] - r["w"]) <= tol), label
+
+
+def test_rows_of_very_different_magnitude():
+    """Rows of x multiplied by 1, 2^6, 2^13, 2^20 in turn (exact in bf16;
+    scaling up only widens the router margins), alpha = 0 so the output is
+    beta * y alone: the activation splits work per block, at any scale."""
+    for name, T in (("tiny", 64), ("prefill", 256), ("decode4", None)):
+        L = synth.make_layer(name, T=T)
+        f = synth.bf16_bits_to_f32(L.x).astype(np.float32)
+        scale = np.array([1.0, 2.0 ** 6, 2.0 ** 13, 2.0 ** 20], np.float32)[np.arange(L.x.shape[0]) % 4]
+        L.x = synth.f32_to_bf16_bits(f * scale[:, None])
+        L.alpha[:] = 0.0
+        _say("scaled rows", name, L.shape.T)
+        out, dbg = run_layer(L)
+        _check_scaled_routing(L, dbg, scale, f"scaled rows {name}")
+        _check_tokens(L, out, np.arange(L.shape.T) if L.shape.T <= 64 else _sample(L.shape.T, 12, 4),
+                      f"scaled rows {name}")
