@@ -94,6 +94,9 @@ enum {
  * right before the first and right after the last kernel of stage s.  The
  * gate/up stage is a single kernel and its two events are recorded by that
  * kernel's own dispatch, so they bracket exactly its execution.
+ *   xn      bf16  [T][d]  moe_block_forward only: the normalised rows x_n
+ *                         the router and the experts read (ignored by the
+ *                         other entry points)
  */
 typedef struct moe_debug {
     int32_t *ids;
@@ -103,6 +106,7 @@ typedef struct moe_debug {
     int32_t *inv;
     void *stage_begin[MOE_NUM_STAGES];
     void *stage_end[MOE_NUM_STAGES];
+    void *xn;
 } moe_debug_t;
 
 /*

@@ -50,7 +50,8 @@ class moe_debug_t(C.Structure):
     _fields_ = [("ids", C.c_void_p), ("weights", C.c_void_p), ("offsets", C.c_void_p),
                 ("perm", C.c_void_p), ("inv", C.c_void_p),
                 ("stage_begin", C.c_void_p * MOE_NUM_STAGES),
-                ("stage_end", C.c_void_p * MOE_NUM_STAGES)]
+                ("stage_end", C.c_void_p * MOE_NUM_STAGES),
+                ("xn", C.c_void_p)]
 
 
 _lib = None
@@ -188,14 +189,7 @@ def moe_layer_forward(x, router_w, expert_w_packed, scales, alpha, beta, k, *, F
     _check(s_out, "s_out", torch.bfloat16, (T, d))
     if workspace is None:
         workspace = workspace_for(T, d, E, F, k, eps, device=x.device)
-    dbg = None
-    if debug is not None:
-        dbg = moe_debug_t(*(_ptr(debug.get(n)) for n in ("ids", "weights", "offsets", "perm", "inv")))
-        for i, name in enumerate(STAGES):
-            ev = debug.get("events", {}).get(name)
-            if ev is not None:  # (begin, end) torch.cuda.Event pair, already created
-                dbg.stage_begin[i] = ev[0].cuda_event
-                dbg.stage_end[i] = ev[1].cuda_event
+    dbg = _debug_struct(debug)
     rc = lib().moe_layer_forward(C.byref(_dims(T, d, E, F, eps)), _ptr(x), _ptr(router_w),
                                  _ptr(expert_w_packed), _ptr(scales), _ptr(alpha), _ptr(beta),
                                  int(k), _ptr(s_out), _ptr(workspace), workspace.numel(),
@@ -271,6 +265,9 @@ def moe_latent_workspace_size(T, D, d, E, F, k, eps=1e-6) -> int:
 
 
 def _debug_struct(debug):
+    """moe_debug_t from a dict of preallocated device tensors (ids, weights,
+    offsets, perm, inv, xn) and "events": {stage: (begin, end)} pairs of
+    torch.cuda.Event whose HIP events already exist."""
     if debug is None:
         return None
     dbg = moe_debug_t(*(_ptr(debug.get(n)) for n in ("ids", "weights", "offsets", "perm", "inv")))
@@ -279,6 +276,7 @@ def _debug_struct(debug):
         if ev is not None:
             dbg.stage_begin[i] = ev[0].cuda_event
             dbg.stage_end[i] = ev[1].cuda_event
+    dbg.xn = _ptr(debug.get("xn"))
     return dbg
 
 

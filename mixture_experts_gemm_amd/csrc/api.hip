@@ -3,7 +3,6 @@
 #include <math.h>
 #include <string.h>
 
-#include <atomic>
 #include <initializer_list>
 
 #include "../../include/moe.h"
@@ -85,22 +84,16 @@ static Shape to_shape(const moe_dims_t *dm, int32_t k)
     return s;
 }
 
-// gfx950 check, cached per device (0 unknown, 1 ok, 2 other arch).
-static std::atomic<int> g_arch_ok[64];
-
+// The current device must be gfx950 (GFX 9.5), the only target the library
+// is built for.  Two attribute queries per call; nothing is cached.
 static int check_arch()
 {
-    int dev = 0;
+    int dev = 0, major = 0, minor = 0;
     if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
-    if (dev < 0 || dev >= 64) return MOE_ERR_ARCH;
-    int st = g_arch_ok[dev].load(std::memory_order_relaxed);
-    if (st == 0) {
-        hipDeviceProp_t prop;
-        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MOE_ERR_HIP;
-        st = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
-        g_arch_ok[dev].store(st, std::memory_order_relaxed);
-    }
-    return st == 1 ? MOE_OK : MOE_ERR_ARCH;
+    if (hipDeviceGetAttribute(&major, hipDeviceAttributeComputeCapabilityMajor, dev) != hipSuccess ||
+        hipDeviceGetAttribute(&minor, hipDeviceAttributeComputeCapabilityMinor, dev) != hipSuccess)
+        return MOE_ERR_HIP;
+    return major == 9 && minor == 5 ? MOE_OK : MOE_ERR_ARCH;
 }
 
 // Caller's event for the begin or end of a stage (null when absent).
@@ -429,6 +422,10 @@ extern "C" int moe_block_forward(const moe_dims_t *dims, const void *x, const fl
         return MOE_ERR_HIP;
 
     if (debug && copy_debug(debug, B.ws, s, st) != hipSuccess) return MOE_ERR_HIP;
+    if (debug && debug->xn &&
+        hipMemcpyAsync(debug->xn, B.xn, sizeof(uint16_t) * (size_t)s.T * s.d, hipMemcpyDeviceToDevice,
+                       st) != hipSuccess)
+        return MOE_ERR_HIP;
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 

@@ -25,7 +25,6 @@
 // exactly one 32-element scale block, and four MFMA steps consume it.
 #include <hip/hip_ext.h>
 
-#include <mutex>
 #include <type_traits>
 
 #include "device.h"
@@ -34,18 +33,8 @@
 
 namespace moe {
 
-#ifndef MOE_DEC_LDS
-#define MOE_DEC_LDS (32 * 1024)  // LDS for the staged activation rows of the decode kernels
-#endif
-#ifndef MOE_G1SU
-#define MOE_G1SU 4  // chunks per weight batch of the streaming gate/up kernel
-#endif
-#ifndef MOE_MX_WAVES
-#define MOE_MX_WAVES 8  // waves per workgroup of the MX tiled kernel (4 or 8)
-#endif
-constexpr int kDecodeLdsBytes = MOE_DEC_LDS;
-constexpr int kG1StreamU = MOE_G1SU;
-constexpr int kMxWaves = MOE_MX_WAVES;
+constexpr int kDecodeLdsBytes = 32 * 1024;  // LDS for the staged activation rows of the decode kernels
+constexpr int kG1StreamU = 4;               // chunks per weight batch of the streaming gate/up kernel
 constexpr int kUnroll = 4;  // chunks per weight batch of the decode kernels
 constexpr size_t kNvFuseLds = 64 * 1024;  // LDS the 16-block down kernel may take for its own h rows
 
@@ -181,17 +170,22 @@ __device__ __forceinline__ uint32_t lds_off(const void *p)
 // guard later LDS reads with a blanket vmcnt(0) (it cannot tell the ring
 // stages apart); every wait on these loads is the explicit one in
 // chunk_sync().  lds (wave-uniform) is the byte offset the lane-0 data lands
-// at; lane i's data lands at lds + i*size.  The kernels using these read no
-// M0-dependent instruction of their own.
+// at; lane i's data lands at lds + i*size.  The load takes its LDS base from
+// M0, which the compiler reserves: its value is saved in an SGPR and put
+// back inside the same statement, so M0 is unchanged across it.
 __device__ __forceinline__ void dma16(const void *g, uint32_t lds)
 {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-                 :: "s"(lds), "v"(g) : "memory", "m0");
+    uint32_t saved;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+                 "global_load_lds_dwordx4 %2, off\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved) : "s"(lds), "v"(g) : "memory");
 }
 __device__ __forceinline__ void dma4(const void *g, uint32_t lds)
 {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
-                 :: "s"(lds), "v"(g) : "memory", "m0");
+    uint32_t saved;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+                 "global_load_lds_dword %2, off\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved) : "s"(lds), "v"(g) : "memory");
 }
 
 // Wait until at most N of this wave's loads are outstanding, then barrier.
@@ -517,14 +511,14 @@ __device__ __forceinline__ floatx4_t mfma_mx(const uint4 &a0, const uint4 &a1, c
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 0, 4, 0, (int)sa, 0, (int)sb);
 }
 
-template <bool GATE_UP, int NW>
-__global__ __launch_bounds__(64 * NW) void gemm_mx_kernel(const MxArgs pa)
+template <bool GATE_UP>
+__global__ __launch_bounds__(512) void gemm_mx_kernel(const MxArgs pa)
 {
-    // NW waves: WM along M (rows), 2 along N; each wave owns RW rows x 128 columns
-    constexpr int WM = NW / 2, RW = kTM / WM, MB = RW / 16;
+    // 8 waves: 4 along M (rows), 2 along N; each wave owns 32 rows x 128 columns
+    constexpr int NW = 8, WM = NW / 2, RW = kTM / WM, MB = RW / 16;
     constexpr int AL = kTM * 8 / (64 * NW);  // A-part loads per thread per chunk (each part)
     constexpr int BL = kTN * 4 / (64 * NW);  // weight-tile loads per thread per chunk
-    constexpr int NLOADS = 2 * AL + BL + (NW == 4 ? 2 : 1);
+    constexpr int NLOADS = 2 * AL + BL + 1;
     __shared__ uint4 Ah0[kTM * 8], Ah1[kTM * 8], Ah2[kTM * 8];
     __shared__ uint4 Al0[kTM * 8], Al1[kTM * 8], Al2[kTM * 8];
     __shared__ uint32_t Ac0[kTM * 2], Ac1[kTM * 2], Ac2[kTM * 2];
@@ -563,25 +557,25 @@ __global__ __launch_bounds__(64 * NW) void gemm_mx_kernel(const MxArgs pa)
     const WView v = GATE_UP ? w1_view(pa.wpk, pa.sc, tl.expert, d, F)
                             : w2_view(pa.wpk, pa.sc, tl.expert, d, F);
     const uint8_t *bsrc = v.tile(nt, 0) + (64 * wv + lane) * 16;
-    // scales: A dword q = (row q/2, hi or lo part by q%2); B dword q = row q.
-    // 4 waves: every thread loads one of each; 8 waves: waves 0-3 A, 4-7 B.
-    const int q = (NW == 4 ? 64 * wv : 64 * (wv & 3)) + lane;
+    // scales: A dword q = (row q/2, hi or lo part by q%2); B dword q = row q;
+    // waves 0-3 load the A scales, waves 4-7 the B scales.
+    const int q = 64 * (wv & 3) + lane;
     const uint8_t *acsrc = ((lane & 1) ? pa.aslo : pa.ashi) + src_row(q >> 1) * (K / 32);
     const uint8_t *ssrc = v.stile(nt, 0) + q * 4;
     const int nk = K / kKStep;
 
     const int wvu = __builtin_amdgcn_readfirstlane(wv);
-    const int qwu = NW == 4 ? wvu : (wvu & 3);
+    const int qwu = wvu & 3;
     auto issue = [&](int kc, uint4 *Ah, uint4 *Al, uint32_t *Ac, uint4 *Bs, uint32_t *Ss) {
 #pragma unroll
         for (int i = 0; i < AL; ++i) dma16(ahsrc[i] + kc * kKStep, lds_off(Ah + (NW * i + wvu) * 64));
 #pragma unroll
         for (int i = 0; i < AL; ++i) dma16(alsrc[i] + kc * kKStep, lds_off(Al + (NW * i + wvu) * 64));
-        if (NW == 4 || wvu < 4) dma4(acsrc + kc * 4, lds_off(Ac + 64 * qwu));
+        if (wvu < 4) dma4(acsrc + kc * 4, lds_off(Ac + 64 * qwu));
 #pragma unroll
         for (int i = 0; i < BL; ++i)
             dma16(bsrc + (int64_t)kc * kWTileBytes + i * NW * 1024, lds_off(Bs + (NW * i + wvu) * 64));
-        if (NW == 4 || wvu >= 4) dma4(ssrc + kc * kWTileScaleBytes, lds_off(Ss + 64 * qwu));
+        if (wvu >= 4) dma4(ssrc + kc * kWTileScaleBytes, lds_off(Ss + 64 * qwu));
     };
 
     // ---- compute assignment -------------------------------------------------
@@ -988,7 +982,7 @@ __global__ __launch_bounds__(512) void gemm_mxw_kernel(const MxArgs pa)
 }
 
 // =========================================================================
-// The 16-block format (prefill): tiles of <= MR (192, or 128) grouped rows x
+// The 16-block format (prefill): tiles of <= 192 grouped rows x
 // 256 weight rows, all of K, on the fp16 MFMA (16x16x32).  The scaled MX MFMA takes one
 // power-of-two scale per 32 values, so it cannot take these weights; they
 // are expanded in registers instead ("Muse Spark Open を段階的に分解する",
@@ -997,12 +991,11 @@ __global__ __launch_bounds__(512) void gemm_mxw_kernel(const MxArgs pa)
 // The activations are fp16 rows with a power-of-two scale per row
 // (f16_rows_kernel), applied with the matrix scale in the epilogue.
 //
-// LDS ring per 128-wide K chunk, filled by direct-to-LDS loads: A MR rows x
+// LDS ring per 128-wide K chunk, filled by direct-to-LDS loads: A 192 rows x
 // 256 bytes (16-byte slot q of row r at q ^ (r & 7)), the chunk's code tile
 // and scale tile copied linearly (the packed layout is the LDS layout);
-// 66 KB a stage and two stages for MR = 192 (one expert's prefill rows in
-// one tile, so its weights are loaded and widened once), 50 KB and three
-// for MR = 128.  8 waves as 2 (rows) x 4 (columns): wave row wm takes the
+// 66 KB a stage, two stages (192 rows keep one expert's prefill rows in one
+// tile, so its weights are loaded and widened once).  8 waves as 2 (rows) x 4 (columns): wave row wm takes the
 // 16-row blocks 2j + wm, each wave 64 weight rows (4 column blocks), so a
 // wave widens a weight value once per chunk for all the rows it multiplies.
 // For gate/up a wave's 64 weight rows are 32 gate features and the same 32
@@ -1022,16 +1015,16 @@ struct NvArgs {
     int d, F, k, ntn;
 };
 
-template <bool GATE_UP, int MR>
+template <bool GATE_UP>
 __global__ __launch_bounds__(512) void gemm_nv_kernel(const NvArgs pa)
 {
     constexpr int NW = 8;
-    constexpr int ST = MR == 128 ? 3 : 2;  // ring stages (LDS: 50 KB or 66 KB a stage)
+    constexpr int MR = kNvTileRows;        // rows per tile (192)
+    constexpr int ST = 2;                  // ring stages (66 KB a stage)
     constexpr int MB = MR / 32;            // row blocks of 16 per wave
     constexpr int AU = MR * 16;            // 16-byte units of an A stage
     constexpr int BU = kTN * 4;            // of a code tile
     constexpr int AL = AU / (64 * NW), BL = BU / (64 * NW);
-    constexpr int NLOADS = AL + BL + 1;
     __shared__ uint4 As[ST][AU];
     __shared__ uint4 Bs[ST][BU];
     __shared__ uint32_t Ss[ST][kTN * 2];
@@ -1137,12 +1130,10 @@ __global__ __launch_bounds__(512) void gemm_nv_kernel(const NvArgs pa)
     fill_e4m3_table(lut);
     lds_barrier();
     issue(0);
-    if (ST == 3 && nk > 1) issue(1);
     const bool full = mb_act == MB;
     for (int kc = 0; kc < nk; ++kc) {
-        // three stages: chunk kc+1's loads may stay in flight; two: none are
-        if (ST == 3 && kc + 1 < nk) chunk_sync<NLOADS>();
-        else chunk_sync<0>();
+        // two stages: every load of chunk kc has landed before it is read
+        chunk_sync<0>();
         // the stage refilled now was last read in step kc-1, before the barrier
         if (kc + ST - 1 < nk) issue(kc + ST - 1);
         if (full) compute(kc % ST, std::true_type{});
@@ -1487,28 +1478,15 @@ __global__ __launch_bounds__(256) void gemm1_stream_kernel(
 }
 
 // Workgroups that fit on the device at once for a 256-thread kernel with
-// `lds` bytes of dynamic LDS (cached per device, kernel and size; 0 on error).
+// `lds` bytes of dynamic LDS (0 on error).  Queried on every call: nothing
+// is cached, so the library keeps no state between calls.
 static int persistent_grid(const void *kfn, size_t lds)
 {
-    struct Entry {
-        const void *fn;
-        size_t lds;
-        int dev, grid;
-    };
-    static std::mutex mu;
-    static Entry cache[32];
-    static int used = 0;
-    int dev = 0;
+    int dev = 0, per_cu = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
-    std::lock_guard<std::mutex> lock(mu);
-    for (int i = 0; i < used; ++i)
-        if (cache[i].fn == kfn && cache[i].lds == lds && cache[i].dev == dev) return cache[i].grid;
-    int per_cu = 0, cus = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kfn, 256, lds) != hipSuccess) return 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    const int grid = per_cu * cus;
-    if (used < 32) cache[used++] = Entry{kfn, lds, dev, grid};
-    return grid;
+    return per_cu * cus;
 }
 
 // ---- launchers ----------------------------------------------------------------
@@ -1531,8 +1509,8 @@ hipError_t launch_gemm1(const Shape &s, const Plan &p, const Workspace &ws, cons
                                   ev1, 0, pa);
         } else {
             const int64_t grid = 8 * ((max_tiles(s, p.tile_rows) * pa.ntn + 7) / 8);
-            hipExtLaunchKernelGGL(gemm_mx_kernel<true, kMxWaves>, dim3((unsigned)grid),
-                                  dim3(64 * kMxWaves), 0, st, ev0, ev1, 0, pa);
+            hipExtLaunchKernelGGL(gemm_mx_kernel<true>, dim3((unsigned)grid), dim3(512), 0, st, ev0,
+                                  ev1, 0, pa);
         }
     } else if (p.stream) {
         const int R = p.tile_rows;
@@ -1580,7 +1558,7 @@ hipError_t launch_gemm2(const Shape &s, const Plan &p, const Workspace &ws, cons
             gemm_mxw_kernel<false><<<(unsigned)grid, 512, 0, st>>>(pa);
         } else {
             const int64_t grid = 8 * ((max_tiles(s, p.tile_rows) * pa.ntn + 7) / 8);
-            gemm_mx_kernel<false, kMxWaves><<<(unsigned)grid, 64 * kMxWaves, 0, st>>>(pa);
+            gemm_mx_kernel<false><<<(unsigned)grid, 512, 0, st>>>(pa);
         }
     } else {
         const int wgs = s.d / 64;
@@ -1609,7 +1587,7 @@ hipError_t launch_gemm1_nv(const Shape &s, const Plan &p, const Workspace &ws, c
         NvArgs pa{x16, xs, ws.perm, ws.tiles, ws.ntiles, wpk, sc, gs, ws.h, nullptr,
                   s.d, s.F, s.k, s.F / 128};
         const int64_t grid = 8 * ((max_tiles(s, p.tile_rows) * pa.ntn + 7) / 8);
-        hipExtLaunchKernelGGL(gemm_nv_kernel<true, kNvTileRows>, dim3((unsigned)grid), dim3(512), 0, st,
+        hipExtLaunchKernelGGL(gemm_nv_kernel<true>, dim3((unsigned)grid), dim3(512), 0, st,
                               ev0, ev1, 0, pa);
     } else if (p.stream) {
         // the persistent streaming kernel: it converts the bf16 x rows of a
@@ -1658,7 +1636,7 @@ hipError_t launch_gemm2_nv(const Shape &s, const Plan &p, const Workspace &ws, c
         NvArgs pa{h16, hs, nullptr, ws.tiles, ws.ntiles, wpk, sc, gs, ws.o, ws.ssq,
                   s.d, s.F, s.k, s.d / 256};
         const int64_t grid = 8 * ((max_tiles(s, p.tile_rows) * pa.ntn + 7) / 8);
-        gemm_nv_kernel<false, kNvTileRows><<<(unsigned)grid, 512, 0, st>>>(pa);
+        gemm_nv_kernel<false><<<(unsigned)grid, 512, 0, st>>>(pa);
     } else {
         const int wgs = s.d / 64;
         const int64_t grid = max_tiles(s, p.tile_rows) * wgs;

@@ -38,14 +38,11 @@ struct Shape {
 constexpr int kStreamMaxT = 8;
 constexpr int kStreamRows = 2;
 
-#ifndef MOE_TILED_MIN_ROWS
-#define MOE_TILED_MIN_ROWS 16
-#endif
 // Average rows per expert from which the tiled (MX) kernels run.  Below
 // it the few-row kernels use 16-row tiles, which read an expert's weights
 // once per tile: from about 16 rows per expert the 128-row tiles read them
 // fewer times (measured: 753 rows over 32 experts, 586 -> 301 us).
-constexpr int kTiledMinRows = MOE_TILED_MIN_ROWS;
+constexpr int kTiledMinRows = 16;
 
 struct Plan {
     bool tiled;
@@ -96,21 +93,15 @@ inline int router_splits(const Shape &s)
 constexpr int kA6Bytes = 304;
 constexpr int kA6Units = kA6Bytes / 16;
 
-#ifndef MOE_MX_WIDE
-#define MOE_MX_WIDE 1  // 128 x 512 tiles where the weight-tile count is even
-#endif
-constexpr bool kUseWide = MOE_MX_WIDE;
-// The wide kernel runs a matrix with an even number of 256-row weight tiles.
-inline bool wide_gate_up(const Shape &s) { return kUseWide && (s.F / 128) % 2 == 0; }
-inline bool wide_down(const Shape &s) { return kUseWide && (s.d / 256) % 2 == 0; }
+// The wide kernel (128 x 512 tiles) runs a matrix with an even number of
+// 256-row weight tiles; an odd count runs on the 128 x 256 kernel.
+inline bool wide_gate_up(const Shape &s) { return (s.F / 128) % 2 == 0; }
+inline bool wide_down(const Shape &s) { return (s.d / 256) % 2 == 0; }
 
-#ifndef MOE_NV_TILE_ROWS
-#define MOE_NV_TILE_ROWS 192
-#endif
-// Rows per tile of the 16-block format's tiled kernels (128 or 192): 192 keeps
-// an expert's prefill rows (about 128 +- 40) in one tile, so its weights are
+// Rows per tile of the 16-block format's tiled kernel: 192 keeps an
+// expert's prefill rows (about 128 +- 40) in one tile, so its weights are
 // loaded and widened once.
-constexpr int kNvTileRows = MOE_NV_TILE_ROWS;
+constexpr int kNvTileRows = 192;
 
 // Upper bound of the tile count for tiles of tile_rows rows (1: any plan).
 inline int64_t max_tiles(const Shape &s, int tile_rows)

@@ -20,11 +20,6 @@
 
 namespace moe {
 
-#ifndef MOE_ROUTER_LDS
-#define MOE_ROUTER_LDS 1  // many-token router through LDS (router_gemm_lds_kernel)
-#endif
-constexpr bool kRouterLds = MOE_ROUTER_LDS;
-
 // LDS byte address of a __shared__ object.
 __device__ __forceinline__ uint32_t lds_addr(const void *p)
 {
@@ -113,10 +108,10 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(const uint16_t *__rest
 // the fp32 router weights.  w = hi + mid + lo exactly (truncating splits:
 // each part keeps 8 significant bits of what is left), x is bf16, so every
 // product is exact and the sum is accumulated in fp32 like an fp32 GEMM.
-// A workgroup computes 128 tokens x 128 experts over one slice of d; its 4
-// waves take 64 x 64 each (4 x 4 MFMA blocks), operands loaded straight
-// into registers one 32-wide K step ahead.  Slice s writes its partial sums
-// to part[s][T][E]; top-k adds the slices in order.
+// A workgroup computes 128 tokens x 128 experts (256 x 64 when E <= 64)
+// over one slice of d; its 4 waves take 64 x 64 each (4 x 4 MFMA blocks).
+// Slice s writes its partial sums to part[s][T][E]; top-k adds the slices
+// in order.
 // ---------------------------------------------------------------------------
 
 __device__ __forceinline__ void split3_trunc(const float4 &a, const float4 &b, uint4 &hi, uint4 &mid,
@@ -138,93 +133,20 @@ __device__ __forceinline__ void split3_trunc(const float4 &a, const float4 &b, u
     lo = make_uint4(pk(l[0], l[1]), pk(l[2], l[3]), pk(l[4], l[5]), pk(l[6], l[7]));
 }
 
-// WE waves along the experts, 4/WE along the tokens: a workgroup covers
-// router_tile_tokens(E) x router_tile_experts(E) (internal.h); with few
-// experts (E <= 64) all four waves take tokens, so none computes only
-// padding experts.
-template <int WE>
-__global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t *__restrict__ x,
-                                                          const float *__restrict__ wr,
-                                                          float *__restrict__ part, int T, int d,
-                                                          int E, int kslice)
-{
-    constexpr int WT = 4 / WE;
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const int m = lane & 15, g = lane >> 4;
-    const int t0 = blockIdx.x * (64 * WT) + (wv % WT) * 64;
-    const int e0 = blockIdx.y * (64 * WE) + (wv / WT) * 64;
-    const int k0 = blockIdx.z * kslice;
-    // rows past T / E are computed on the last valid row and never stored
-    const uint16_t *xp[4];
-    const float *wp[4];
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-        xp[mb] = x + (int64_t)min(t0 + mb * 16 + m, T - 1) * d + k0 + g * 8;
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) wp[nb] = wr + (int64_t)min(e0 + nb * 16 + m, E - 1) * d + k0 + g * 8;
-
-    floatx4_t acc[4][4];
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-
-    uint4 a0[4], a1[4];
-    float4 w0[4][2], w1[4][2];
-    auto load = [&](uint4 (&a)[4], float4 (&w)[4][2], int k) {
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb) a[mb] = *reinterpret_cast<const uint4 *>(xp[mb] + k);
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-            w[nb][0] = *reinterpret_cast<const float4 *>(wp[nb] + k);
-            w[nb][1] = *reinterpret_cast<const float4 *>(wp[nb] + k + 4);
-        }
-    };
-    auto compute = [&](const uint4 (&a)[4], const float4 (&w)[4][2]) {
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-            uint4 hi, mid, lo;
-            split3_trunc(w[nb][0], w[nb][1], hi, mid, lo);
-#pragma unroll
-            for (int mb = 0; mb < 4; ++mb) {
-                const bf16x8_t av = as_bf16x8(a[mb]);
-                acc[mb][nb] = mfma16(av, as_bf16x8(lo), acc[mb][nb]);
-                acc[mb][nb] = mfma16(av, as_bf16x8(mid), acc[mb][nb]);
-                acc[mb][nb] = mfma16(av, as_bf16x8(hi), acc[mb][nb]);
-            }
-        }
-    };
-    load(a0, w0, 0);
-    for (int k = 0; k < kslice; k += 64) {
-        if (k + 32 < kslice) load(a1, w1, k + 32);
-        compute(a0, w0);
-        if (k + 32 >= kslice) break;
-        if (k + 64 < kslice) load(a0, w0, k + 64);
-        compute(a1, w1);
-    }
-    float *out = part + (int64_t)blockIdx.z * T * E;
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = t0 + mb * 16 + g * 4 + r, e = e0 + nb * 16 + m;
-                if (t < T && e < E) out[(int64_t)t * E + e] = acc[mb][nb][r];
-            }
-}
-
-// The same product with the workgroup's operands staged through LDS: each
-// 32-wide K step of the tile's x rows (64 B a row) and router rows (128 B a
-// row, fp32) is copied once by direct-to-LDS loads into a three-stage ring
-// and read by every wave that needs it (16-byte slot q of an x row r at
+// The workgroup's operands are staged through LDS: each 32-wide K step of
+// the tile's x rows (64 B a row) and router rows (128 B a row, fp32) is
+// copied once by direct-to-LDS loads into a three-stage ring and read by
+// every wave that needs it (16-byte slot q of an x row r at
 // q ^ ((r >> 1) & 3), of a router row at q ^ (r & 7): the fragment reads of
-// 16 consecutive rows then fall on distinct banks).  Same products, same
-// accumulation order per output as router_gemm_kernel.
+// 16 consecutive rows then fall on distinct banks).  WE waves along the
+// experts, 4/WE along the tokens.  The load takes its LDS base from M0,
+// which is saved and restored inside the asm statement.
 __device__ __forceinline__ void rdma16(const void *g, uint32_t lds)
 {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-                 :: "s"(lds), "v"(g) : "memory", "m0");
+    uint32_t saved;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+                 "global_load_lds_dwordx4 %2, off\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved) : "s"(lds), "v"(g) : "memory");
 }
 
 template <int WE>
@@ -338,15 +260,10 @@ hipError_t launch_router(const Shape &s, const Plan &p, const Workspace &ws, con
         const int ks = router_splits(s);
         const int tt = router_tile_tokens(s.E), te = router_tile_experts(s.E);
         dim3 grid((s.T + tt - 1) / tt, (s.E + te - 1) / te, ks);
-        if (kRouterLds) {
-            if (te == 64)
-                router_gemm_lds_kernel<1><<<grid, 256, 0, st>>>(x, wr, ws.scores, s.T, s.d, s.E, s.d / ks);
-            else
-                router_gemm_lds_kernel<2><<<grid, 256, 0, st>>>(x, wr, ws.scores, s.T, s.d, s.E, s.d / ks);
-        } else if (te == 64)
-            router_gemm_kernel<1><<<grid, 256, 0, st>>>(x, wr, ws.scores, s.T, s.d, s.E, s.d / ks);
+        if (te == 64)
+            router_gemm_lds_kernel<1><<<grid, 256, 0, st>>>(x, wr, ws.scores, s.T, s.d, s.E, s.d / ks);
         else
-            router_gemm_kernel<2><<<grid, 256, 0, st>>>(x, wr, ws.scores, s.T, s.d, s.E, s.d / ks);
+            router_gemm_lds_kernel<2><<<grid, 256, 0, st>>>(x, wr, ws.scores, s.T, s.d, s.E, s.d / ks);
     }
     if (p.tiled) {
         hipError_t e = hipGetLastError();

@@ -49,7 +49,7 @@ import numpy as np
 
 # substream tags
 (_TAG_X, _TAG_WR, _TAG_W, _TAG_S, _TAG_AB, _TAG_ZIPF, _TAG_REDRAW, _TAG_WC, _TAG_WE,
- _TAG_GAIN, _TAG_S16, _TAG_GS) = range(12)
+ _TAG_GAIN, _TAG_S16, _TAG_GS, _TAG_OUTLIER) = range(13)
 
 SCALE_LO, SCALE_HI = 119, 123          # E8M0 bytes: 2^-8 .. 2^-4
 GAP_DEFAULT = 1e-4
@@ -160,13 +160,44 @@ def make_router(w: Workload, layer: int = 0) -> np.ndarray:
     return wr
 
 
+def outlier_rows(x_bits: np.ndarray, seed: int, layer: int, tokens: np.ndarray,
+                 attempt: int = 0) -> np.ndarray:
+    """Hard activation blocks for the block-scaled activation splits, applied
+    to bf16 rows (powers of two only, so every value stays exact):
+      * in every 32-value block one seeded channel is multiplied by 2^u,
+        u uniform over 8..12 (one large value per block, as in activation
+        outlier channels);
+      * in a seeded quarter of the blocks, half of the other values are
+        multiplied by 2^-14 (values far below the block maximum).
+    Row r is transformed from its own substream (seed, layer, token, attempt)."""
+    out = x_bits.copy()
+    T, d = out.shape
+    nb = d // 32
+    for r in range(T):
+        g = _rng(seed, layer, _TAG_OUTLIER, int(tokens[r]), attempt)
+        f = bf16_bits_to_f32(out[r]).reshape(nb, 32).astype(np.float32)
+        ch = g.integers(0, 32, size=nb)
+        up = g.integers(8, 13, size=nb)
+        f[np.arange(nb), ch] *= np.exp2(up).astype(np.float32)
+        low = g.random(nb) < 0.25
+        half = g.random((nb, 32)) < 0.5
+        half[np.arange(nb), ch] = False
+        f[low[:, None] & half] *= np.float32(2.0 ** -14)
+        out[r] = f32_to_bf16_bits(f.reshape(d))
+    return out
+
+
 def make_tokens(w: Workload, wr: np.ndarray, layer: int = 0, T: int | None = None,
-                gap: float = GAP_DEFAULT, max_attempts: int = 64) -> np.ndarray:
-    """x as bf16 bits [T][d], every row meeting the router margin precondition."""
+                gap: float = GAP_DEFAULT, max_attempts: int = 64,
+                outliers: bool = False) -> np.ndarray:
+    """x as bf16 bits [T][d], every row meeting the router margin precondition
+    (with outliers=True, after outlier_rows; redrawn rows are transformed too)."""
     s = w.shape
     T = s.T if T is None else T
     g = _rng(w.seed, layer, _TAG_X, 0)
     x = f32_to_bf16_bits(g.standard_normal((T, s.d), dtype=np.float32))
+    if outliers:
+        x = outlier_rows(x, w.seed, layer, np.arange(T))
     if w.zipf:
         x[:, 0] = 0x3F80  # 1.0: the bias channel
     if gap <= 0:
@@ -176,6 +207,8 @@ def make_tokens(w: Workload, wr: np.ndarray, layer: int = 0, T: int | None = Non
     while len(bad) and attempt < max_attempts:
         attempt += 1
         rows = _draw_x_rows(w.seed, layer, s.d, bad, np.full(len(bad), attempt))
+        if outliers:
+            rows = outlier_rows(rows, w.seed, layer, bad, attempt)
         if w.zipf:
             rows[:, 0] = 0x3F80
         x[bad] = rows
@@ -289,14 +322,15 @@ class LayerInputs:
 
 
 def make_layer(name_or_w, layer: int = 0, T: int | None = None, gap: float = GAP_DEFAULT,
-               threads: int = 8, with_tokens: bool = True) -> LayerInputs:
+               threads: int = 8, with_tokens: bool = True, outliers: bool = False) -> LayerInputs:
     w = WORKLOADS[name_or_w] if isinstance(name_or_w, str) else name_or_w
     s = w.shape
     if T is not None:
         s = dataclasses.replace(s, T=T)
         w = dataclasses.replace(w, shape=s)
     wr = make_router(w, layer)
-    x = make_tokens(w, wr, layer, gap=gap) if with_tokens else np.zeros((0, s.d), np.uint16)
+    x = (make_tokens(w, wr, layer, gap=gap, outliers=outliers) if with_tokens
+         else np.zeros((0, s.d), np.uint16))
     W, S = make_experts(w, layer, threads=threads)
     a, b = make_gates(w, layer)
     return LayerInputs(s, x, wr, W, S, a, b, s.k)
@@ -317,7 +351,7 @@ class NvLayerInputs:
 
 
 def make_layer_nv(name_or_w, layer: int = 0, T: int | None = None, gap: float = GAP_DEFAULT,
-                  threads: int = 8, with_tokens: bool = True) -> NvLayerInputs:
+                  threads: int = 8, with_tokens: bool = True, outliers: bool = False) -> NvLayerInputs:
     """A workload's layer with its expert weights drawn in the 16-block format."""
     w = WORKLOADS[name_or_w] if isinstance(name_or_w, str) else name_or_w
     s = w.shape
@@ -325,7 +359,8 @@ def make_layer_nv(name_or_w, layer: int = 0, T: int | None = None, gap: float = 
         s = dataclasses.replace(s, T=T)
         w = dataclasses.replace(w, shape=s)
     wr = make_router(w, layer)
-    x = make_tokens(w, wr, layer, gap=gap) if with_tokens else np.zeros((0, s.d), np.uint16)
+    x = (make_tokens(w, wr, layer, gap=gap, outliers=outliers) if with_tokens
+         else np.zeros((0, s.d), np.uint16))
     W, S, G = make_experts_nv(w, layer, threads=threads)
     a, b = make_gates(w, layer)
     return NvLayerInputs(s, x, wr, W, S, G, a, b, s.k)

@@ -64,8 +64,10 @@ def lib():
                                             _P, _P, _P, _I, _P, _P, _P, _P]
         L.oracle_latent_forward.restype = _I
         L.oracle_block_forward.argtypes = [_I, _I, _I, _I, _I, C.c_double, _P, _P, _P, _P, _P, _P,
-                                           _P, _P, _I, _P, _P, _P, _P]
+                                           _P, _P, _I, _P, _P, _P, _P, _P]
         L.oracle_block_forward.restype = _I
+        L.oracle_block_prenorm.argtypes = [_I, _I, C.c_double, _P, _P, _I, _P, _P]
+        L.oracle_block_prenorm.restype = _I
         _lib = L
     return _lib
 
@@ -295,9 +297,28 @@ def latent_forward(x_bits, wr, wc_bits, w_packed, scales, we_bits, alpha, beta, 
     return s, ids, w
 
 
+def block_prenorm(x_bits, gamma_pre, eps=1e-6, tokens=None):
+    """B1 on the listed tokens (all when None): the normalised rows as bf16 bits [n][d]."""
+    x_bits = _c(x_bits, np.uint16)
+    gamma_pre = _c(gamma_pre, np.float32)
+    T, d = x_bits.shape
+    sel = None if tokens is None else _c(tokens, np.int32)
+    n = T if sel is None else sel.size
+    xn = np.empty((n, d), np.uint16)
+    rc = lib().oracle_block_prenorm(T, d, eps, _p(x_bits), _p(gamma_pre), n,
+                                    None if sel is None else _p(sel), _p(xn))
+    if rc != 0:
+        raise ValueError("oracle_block_prenorm: bad arguments")
+    return xn
+
+
 def block_forward(x_bits, gamma_pre, wr, w_packed, scales, gamma_post, alpha, beta, k, eps=1e-6,
-                  tokens=None):
-    """B1-B3 (the block with its stream norms) on the listed tokens: (s float64 [n][d], ids, w)."""
+                  tokens=None, xn=None):
+    """B1-B3 (the block with its stream norms) on the listed tokens: (s float64 [n][d], ids, w).
+
+    xn: optional normalised rows (bf16 bits [n][d], one per listed token) used
+    in place of B1's own, to check B2-B3 on exactly the rows another
+    implementation computed."""
     x_bits = _c(x_bits, np.uint16)
     gamma_pre = _c(gamma_pre, np.float32)
     gamma_post = _c(gamma_post, np.float32)
@@ -319,9 +340,13 @@ def block_forward(x_bits, gamma_pre, wr, w_packed, scales, gamma_post, alpha, be
     s = np.empty((n, d), np.float64)
     ids = np.empty((n, k), np.int32)
     w = np.empty((n, k), np.float64)
+    if xn is not None:
+        xn = _c(xn, np.uint16)
+        assert xn.shape == (n, d)
     rc = lib().oracle_block_forward(T, d, E, F, k, eps, _p(x_bits), _p(gamma_pre), _p(wr),
                                     _p(w_packed), _p(scales), _p(gamma_post), _p(alpha), _p(beta),
-                                    n, None if sel is None else _p(sel), _p(s), _p(ids), _p(w))
+                                    n, None if sel is None else _p(sel),
+                                    None if xn is None else _p(xn), _p(s), _p(ids), _p(w))
     if rc != 0:
         raise ValueError("oracle_block_forward: bad arguments")
     return s, ids, w

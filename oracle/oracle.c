@@ -525,14 +525,40 @@ int oracle_latent_forward(int T, int D, int d, int E, int F, int k, double eps,
  *   B2  O2-O7 on x_n, and y = sum_j w_j n_j (O8 without the gate), double.
  *   B3  s_out = alpha * s + beta * (y * r_y * gamma_post),
  *       r_y = 1 / sqrt(mean(y^2) + eps).  Kept in double.
- *
- * Arguments as oracle_moe_forward plus the two gains (fp32 [d]).
+ */
+
+/* B1 on the rows listed in sel (all T when sel == NULL): xn [n_sel][d]. */
+int oracle_block_prenorm(int T, int d, double eps, const uint16_t *x, const float *gamma_pre,
+                         int n_sel, const int32_t *sel, uint16_t *xn)
+{
+    if (T < 0 || d <= 0) return -1;
+    if (sel == NULL) n_sel = T;
+    for (int r = 0; r < n_sel; ++r) {
+        const int t = sel ? sel[r] : r;
+        double ss = 0.0;
+        for (int i = 0; i < d; ++i) {
+            const double v = oracle_bf16_to_double(x[(int64_t)t * d + i]);
+            ss += v * v;
+        }
+        const double rs = 1.0 / sqrt(ss / (double)d + eps);
+        for (int i = 0; i < d; ++i)
+            xn[(int64_t)r * d + i] = oracle_double_to_bf16(
+                oracle_bf16_to_double(x[(int64_t)t * d + i]) * rs * (double)gamma_pre[i]);
+    }
+    return 0;
+}
+
+/*
+ * B1-B3.  Arguments as oracle_moe_forward plus the two gains (fp32 [d]).
+ * xn_in: NULL, or the normalised rows [n_sel][d] to use in place of B1's
+ * (the rows another implementation computed, so that B2-B3 can be checked
+ * on exactly the input it saw).
  */
 int oracle_block_forward(int T, int d, int E, int F, int k, double eps, const uint16_t *x,
                          const float *gamma_pre, const float *wr, const uint8_t *wpk,
                          const uint8_t *sc, const float *gamma_post, const float *alpha,
-                         const float *beta, int n_sel, const int32_t *sel, double *s_out,
-                         int32_t *ids_out, double *w_out)
+                         const float *beta, int n_sel, const int32_t *sel, const uint16_t *xn_in,
+                         double *s_out, int32_t *ids_out, double *w_out)
 {
     if (T < 0 || d <= 0 || E <= 0 || F <= 0 || k < 1 || k > E || d % 32 || F % 32) return -1;
     if (sel == NULL) n_sel = T;
@@ -547,18 +573,10 @@ int oracle_block_forward(int T, int d, int E, int F, int k, double eps, const ui
     }
     for (int i = 0; i < d; ++i) one[i] = 1.0f;
     /* B1 */
-    for (int r = 0; r < n_sel; ++r) {
-        const int t = sel ? sel[r] : r;
-        double ss = 0.0;
-        for (int i = 0; i < d; ++i) {
-            const double v = oracle_bf16_to_double(x[(int64_t)t * d + i]);
-            ss += v * v;
-        }
-        const double rs = 1.0 / sqrt(ss / (double)d + eps);
-        for (int i = 0; i < d; ++i)
-            xn[(int64_t)r * d + i] = oracle_double_to_bf16(
-                oracle_bf16_to_double(x[(int64_t)t * d + i]) * rs * (double)gamma_pre[i]);
-    }
+    if (xn_in)
+        memcpy(xn, xn_in, sizeof(uint16_t) * (size_t)n_sel * d);
+    else
+        oracle_block_prenorm(T, d, eps, x, gamma_pre, n_sel, sel, xn);
     /* B2: the layer on x_n with alpha = 0, beta = 1 returns y */
     int rc = oracle_moe_forward(n_sel, d, E, F, k, eps, xn, wr, wpk, sc, zero, one, n_sel, NULL, y,
                                 ids_out, w_out);

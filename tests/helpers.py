@@ -57,6 +57,37 @@ def upload(L, device="cuda"):
     )
 
 
+def tile_edge_rows(offsets, R):
+    """Grouped rows at the first and the last row of every tile the library's
+    tiled expert kernels cut the segments into: an expert with c rows gets
+    nt = ceil(c / R) tiles of `per` rows each (the last one ragged), per =
+    ceil(c / nt) rounded up to a multiple of 16 (the MFMA row block) and at
+    most R (R = 128 for MXFP4 weights, 192 for the 16-block format)."""
+    rows = []
+    for e in range(len(offsets) - 1):
+        a, c = int(offsets[e]), int(offsets[e + 1] - offsets[e])
+        if c == 0:
+            continue
+        nt = -(-c // R)
+        per = min(R, ((-(-c // nt)) + 15) // 16 * 16)
+        for i in range(nt):
+            r0 = i * per
+            rows += [a + r0, a + min(c, r0 + per) - 1]
+    return np.unique(np.asarray(rows, np.int64))
+
+
+def parity_tokens(T, dbg, k, R, n=512, seed=0):
+    """Tokens to compare at full size: n seeded tokens (all when T <= n),
+    token 0 and T-1, and the tokens behind the first and last row of every
+    tile (tile_edge_rows)."""
+    rng = np.random.default_rng(seed)
+    pick = set(range(T)) if T <= n else set(rng.choice(T, size=n, replace=False).tolist())
+    pick |= {0, T - 1}
+    rows = tile_edge_rows(dbg["offsets"], R)
+    pick |= set((dbg["perm"][rows] // k).tolist())
+    return np.array(sorted(pick), np.int32)
+
+
 def debug_buffers(T, E, k, device="cuda"):
     S = T * k
     return dict(ids=torch.empty(S, dtype=torch.int32, device=device),

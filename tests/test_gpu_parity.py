@@ -2,9 +2,12 @@
 
 Routing (ids, offsets, perm, inv) must match bit for bit, weights to 1e-5,
 and the layer output within rel_max 2e-2 / normwise 5e-3 (tests/helpers.py).
-Small workloads are compared on every token; the full-size ones on every
-token for routing and on a seeded sample of tokens for the output (the layer
-is token-separable, so a sampled row is checked exactly as in a full run).
+Small workloads are compared on every token.  Full-size ones are compared on
+every token for routing; for the output on every token where the oracle
+finishes in about a minute, else on at least 512 seeded tokens plus the
+tokens behind the first and the last row of every tile of the tiled expert
+kernels (the layer is token-separable, so each compared row is checked
+exactly as in a full run).
 """
 import numpy as np
 import pytest
@@ -13,8 +16,8 @@ import torch
 import oracle
 from mixture_experts_gemm_amd import synth
 
-from helpers import (WEIGHT_TOL, assert_close, bf16_bits, bf16_tensor, metrics, run_latent,
-                     run_layer, upload)
+from helpers import (WEIGHT_TOL, assert_close, bf16_bits, bf16_tensor, debug_buffers, metrics,
+                     parity_tokens, run_latent, run_layer, upload)
 
 pytestmark = pytest.mark.gpu
 
@@ -266,105 +269,125 @@ def _sample(T, n, seed, extra=()):
     return np.array(sorted(pick), np.int32)
 
 
+@pytest.mark.timeout(900)
 def test_prefill_full_size():
-    L = synth.make_layer("prefill")
+    """T=4096: routing and the output on every token (32,768 slot rows, every
+    row of every tile)."""
+    L = synth.make_layer("prefill", threads=16)
     _say("prefill T=4096")
     out, dbg = run_layer(L)
     r = _check_routing(L, dbg, "prefill")
-    _check_tokens(L, out, _sample(4096, 14, 2), "prefill")
     assert int(r["counts"].sum()) == 4096 * 8
+    _check_tokens(L, out, np.arange(4096, dtype=np.int32), "prefill all tokens")
 
 
+@pytest.mark.timeout(900)
 def test_skewed_full_size():
-    L = synth.make_layer("skewed")
+    L = synth.make_layer("skewed", threads=16)
     _say("skewed T=16384")
     out, dbg = run_layer(L)
     r = _check_routing(L, dbg, "skewed")
-    hot = int(np.argmax(r["counts"]))
     share = np.sort(r["counts"])[::-1][:8].sum() / (16384 * 8)
     _say("skewed top-8 share", share, "largest segment", r["counts"].max())
-    hot_tokens = np.nonzero(np.any(r["ids"] == hot, axis=1))[0][:4]
-    _check_tokens(L, out, _sample(16384, 10, 3, hot_tokens), "skewed")
+    tokens = parity_tokens(16384, dbg, 8, 128, n=512, seed=3)
+    _check_tokens(L, out, tokens, "skewed")
 
 
-@pytest.mark.parametrize("name,n", [("ep753", 16), ("ep3012", 12)])
-def test_ep_share_full_size(name, n):
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["ep753", "ep3012"])
+def test_ep_share_full_size(name):
     """One GPU's share under 8-way expert parallelism: 32 local experts, each
-    routed (token, expert) pair one row (k = 1), about 24 / 94 rows per expert."""
-    L = synth.make_layer(name)
+    routed (token, expert) pair one row (k = 1), about 24 / 94 rows per
+    expert; every token compared."""
+    L = synth.make_layer(name, threads=16)
     _say(name, "T", L.shape.T)
     out, dbg = run_layer(L)
     r = _check_routing(L, dbg, name)
-    _check_tokens(L, out, _sample(L.shape.T, n, 5), name)
     assert int(r["counts"].sum()) == L.shape.T
+    _check_tokens(L, out, np.arange(L.shape.T, dtype=np.int32), name)
 
 
+def _margins(scores, k):
+    top = -np.sort(-scores.astype(np.float64), axis=1)[:, : k + 1]
+    return (top[:, :-1] - top[:, 1:]).min(axis=1)
+
+
+@pytest.mark.timeout(1200)
 def test_stack_of_four_layers():
     """Chained layers: each layer's bf16 output is the next layer's input.
 
-    Routing of every layer is checked on the input the GPU actually saw: the
-    oracle's router on the GPU chain's input rows must give the same experts
-    wherever its score gaps (ranks 1..k+1) are at least 1e-4, the margin the
-    generator guarantees for fresh tokens.  The outputs are compared with the
-    oracle's own chain (its own bf16 rounding between layers), on tokens whose
-    routing agreed with that chain at every layer; the error bound grows with
-    depth.
-    """
+    Teacher-forced, at every layer: the oracle runs on the very input rows
+    the GPU saw (its own previous output).  Routing must then be bit-exact on
+    every token whose score gaps (ranks 1..k+1) on those rows are at least
+    1e-4, the generator's margin for fresh tokens (tokens below it are
+    reported and left out), and the outputs must meet the layer tolerance on
+    at least 512 tokens plus every tile's first and last row.  The oracle's
+    own free-running chain (its own bf16 rounding between layers) gives the
+    error growth, reported per layer on 512 tokens."""
     w = synth.WORKLOADS["stack"]
     T = w.shape.T
-    tokens = _sample(T, 12, 4)
+    chain_tokens = _sample(T, 512, 4)
     x_gpu = None
     ref_in = None
-    agree = np.ones(len(tokens), bool)
+    growth = []
     for layer in range(w.layers):
         _say("stack layer", layer)
-        L = synth.make_layer(w, layer=layer, with_tokens=(layer == 0))
+        L = synth.make_layer(w, layer=layer, with_tokens=(layer == 0), threads=16)
         dev = upload(L)
         xin = dev["x"] if layer == 0 else x_gpu
         out, dbg = run_layer(L, dev, x=xin)
+        gin = bf16_bits(xin)
         if layer == 0:
-            ref_in = L.x[tokens]
+            ref_in = L.x[chain_tokens]
             _check_routing(L, dbg, "stack layer 0")
-        # the router stage on the GPU's own input rows
-        gin = bf16_bits(xin)[tokens]
-        sc_g = oracle.router_scores(gin, L.router_w)
-        ids_g, _ = oracle.topk_softmax(sc_g, L.k)
-        top_g = -np.sort(-sc_g.astype(np.float64), axis=1)[:, : L.k + 1]
-        margin_g = (top_g[:, :-1] - top_g[:, 1:]).min(axis=1)
-        same_g = np.all(dbg["ids"][tokens] == ids_g, axis=1)
-        assert np.all(same_g[margin_g >= 1e-4]), f"layer {layer}: routing differs on the GPU's input"
-        # agreement with the oracle's own chain
-        sc = oracle.router_scores(ref_in, L.router_w)
-        ids_ref, _ = oracle.topk_softmax(sc, L.k)
-        agree &= np.all(dbg["ids"][tokens] == ids_ref, axis=1)
-        s_ref, _, _ = oracle.moe_forward(ref_in, L.router_w, L.w_packed, L.scales, L.alpha,
-                                         L.beta, L.k, eps=L.eps)
+        # teacher-forced routing on every token
+        sc = oracle.router_scores(gin, L.router_w)
+        ids_g, _ = oracle.topk_softmax(sc, L.k)
+        margin = _margins(sc, L.k)
+        same = np.all(dbg["ids"] == ids_g, axis=1)
+        assert np.all(same[margin >= 1e-4]), f"layer {layer}: routing differs on the GPU's input"
+        _say("stack layer", layer, "tokens below the 1e-4 margin", int((margin < 1e-4).sum()),
+             "routed differently", int((~same).sum()))
+        # teacher-forced outputs
+        tokens = parity_tokens(T, dbg, L.k, 128, n=512, seed=40 + layer)
+        tokens = tokens[same[tokens]]
+        ref_tf, _, _ = oracle.moe_forward(gin, L.router_w, L.w_packed, L.scales, L.alpha, L.beta,
+                                          L.k, eps=L.eps, tokens=tokens)
         got = synth.bf16_bits_to_f32(out[tokens]).astype(np.float64)
-        m = metrics(got[agree], s_ref[agree])
-        _say("stack layer", layer, "agree", int(agree.sum()), "of", len(tokens), m)
-        assert agree.sum() >= len(tokens) // 2, (layer, int(agree.sum()))
-        bound = 5e-3 if layer == 0 else 2e-2
-        assert m["normwise"] <= bound and m["rel_max"] <= 4 * bound, (layer, m)
+        m = assert_close(got, ref_tf, f"stack layer {layer} teacher-forced")
+        _say("stack layer", layer, "teacher-forced tokens", len(tokens), m)
+        # the oracle's own chain: error growth
+        s_ref, ids_ref, _ = oracle.moe_forward(ref_in, L.router_w, L.w_packed, L.scales, L.alpha,
+                                               L.beta, L.k, eps=L.eps)
+        agree = np.all(dbg["ids"][chain_tokens] == ids_ref, axis=1)
+        mg = metrics(synth.bf16_bits_to_f32(out[chain_tokens][agree]).astype(np.float64), s_ref[agree])
+        growth.append(mg)
+        _say("stack layer", layer, "free-running chain: routing agrees on", int(agree.sum()), "of",
+             len(chain_tokens), mg)
+        assert mg["normwise"] <= 2e-2, (layer, mg)  # sanity bound on the chain's drift
         ref_in = oracle.doubles_to_bf16(s_ref)
         x_gpu = bf16_tensor(out)
         del dev, L
         torch.cuda.empty_cache()
+    _say("stack error growth (normwise per layer)", [round(g["normwise"], 6) for g in growth])
 
 
 # ------------------------------------------------------------ latent-width variant
 
-@pytest.mark.parametrize("name,n", [("latent_tiny", None), ("latent1", None), ("latent4", None),
-                                    ("latent_prefill", 8)])
-def test_latent_variant(name, n):
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name,full", [("latent_tiny", True), ("latent1", True), ("latent4", True),
+                                       ("latent_prefill", False)])
+def test_latent_variant(name, full):
     """Narrowing matrix, experts at the narrow width, widening matrix: routing
     on the full-width token bit for bit, outputs against the oracle's L1-L5
-    on every token (small sizes) or a seeded sample (prefill size)."""
-    L = synth.make_latent_layer(name)
+    on every token (small sizes) or 512 tokens plus every tile's first and
+    last row (prefill size)."""
+    L = synth.make_latent_layer(name, threads=16)
     w = L.w
     _say(name, "T", w.T, "D", w.D, "d", w.d)
     out, dbg = run_latent(L)
     _check_routing(L, dbg, name)
-    tokens = np.arange(w.T, dtype=np.int32) if n is None else _sample(w.T, n, 6)
+    tokens = np.arange(w.T, dtype=np.int32) if full else parity_tokens(w.T, dbg, w.k, 128, seed=6)
     ref, _, _ = oracle.latent_forward(L.x, L.router_w, L.wc, L.w_packed, L.scales, L.we, L.alpha,
                                       L.beta, w.k, eps=L.eps, tokens=tokens)
     got = synth.bf16_bits_to_f32(out[tokens]).astype(np.float64)
@@ -376,62 +399,68 @@ def test_latent_variant(name, n):
 
 def _run_block(L, g_pre, g_post):
     from mixture_experts_gemm_amd import binding as B
-    from helpers import debug_buffers
     dev = upload(L)
     s = L.shape
     dbg = debug_buffers(s.T, s.E, s.k)
+    dbg["xn"] = torch.empty(s.T, s.d, dtype=torch.bfloat16, device="cuda")
     out = B.moe_block_forward(dev["x"], torch.from_numpy(g_pre).cuda(), dev["router_w"], dev["w"],
                               dev["s"], torch.from_numpy(g_post).cuda(), dev["alpha"], dev["beta"],
                               s.k, F=s.F, eps=L.eps, debug=dbg)
     torch.cuda.synchronize()
-    res = {n: t.cpu().numpy() for n, t in dbg.items()}
-    return bf16_bits(out), res["ids"].reshape(s.T, s.k)
+    res = {n: t.cpu().numpy() for n, t in dbg.items() if n != "xn"}
+    res["ids"] = res["ids"].reshape(s.T, s.k)
+    res["xn"] = bf16_bits(dbg["xn"])
+    return bf16_bits(out), res
 
 
-@pytest.mark.parametrize("name,n", [("tiny", None), ("decode4", None), ("prefill", 10)])
-def test_block_with_stream_norms(name, n):
-    """Pre-norm into the block, post-norm into the gate.  The router reads the
-    bf16 normalised copy, which GPU (fp32 norm) and oracle (double) may round
-    one bf16 step apart in rare elements, so routing must agree exactly where
-    the oracle's top-(k+1) margin is >= 1e-2 (as for chained layers), and
-    outputs are compared on tokens whose routing agreed."""
-    L = synth.make_layer(name)
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name,full", [("tiny", True), ("decode4", True), ("prefill", False)])
+def test_block_with_stream_norms(name, full):
+    """Pre-norm into the block, post-norm into the gate, teacher-forced.
+
+    The GPU's normalised copy x_n (a debug output) is within one bf16 step of
+    the oracle's B1 in every element.  On that copy the oracle's router must
+    choose the GPU's experts on every token whose score gaps are at least
+    1e-4, and the oracle's B2-B3 on the same rows must meet the layer
+    tolerance on every token (small sizes) or 512 tokens plus every tile's
+    first and last row."""
+    L = synth.make_layer(name, threads=16)
     g_pre, g_post = synth.make_norm_gains(synth.WORKLOADS[name])
     s = L.shape
     _say("block", name, "T", s.T)
-    out, ids = _run_block(L, g_pre, g_post)
-    tokens = np.arange(s.T, dtype=np.int32) if n is None else _sample(s.T, n, 7)
-    ref, ref_ids, _ = oracle.block_forward(L.x, g_pre, L.router_w, L.w_packed, L.scales, g_post,
-                                           L.alpha, L.beta, s.k, eps=L.eps, tokens=tokens)
-    # the oracle's margins on its own normalised copy
-    xn = oracle.doubles_to_bf16(_oracle_prenorm(L.x[tokens], g_pre, L.eps))
-    sc = oracle.router_scores(xn, L.router_w).astype(np.float64)
-    top = -np.sort(-sc, axis=1)[:, : s.k + 1]
-    safe = np.all(top[:, :-1] - top[:, 1:] >= 1e-2, axis=1)
-    agree = np.all(ids[tokens] == ref_ids, axis=1)
-    assert np.all(agree[safe]), (name, np.nonzero(~agree & safe))
-    assert agree.mean() >= 0.9, agree.mean()
-    got = synth.bf16_bits_to_f32(out[tokens][agree]).astype(np.float64)
-    m = assert_close(got, ref[agree], name)
-    _say("block", name, "tokens", int(agree.sum()), "of", len(tokens), m)
+    out, dbg = _run_block(L, g_pre, g_post)
+    xn_ref = oracle.block_prenorm(L.x, g_pre, eps=L.eps)
+    step = np.abs(dbg["xn"].astype(np.int32) - xn_ref.astype(np.int32))
+    assert step.max() <= 1, int(step.max())  # same sign: bf16 bit patterns one step apart
+    _say("block", name, "x_n elements one bf16 step from the oracle's", int((step == 1).sum()),
+         "of", step.size)
+    sc = oracle.router_scores(dbg["xn"], L.router_w)
+    ids_g, w_g = oracle.topk_softmax(sc, s.k)
+    margin = _margins(sc, s.k)
+    same = np.all(dbg["ids"] == ids_g, axis=1)
+    assert np.all(same[margin >= 1e-4]), (name, np.nonzero(~same & (margin >= 1e-4)))
+    assert np.all(np.abs(dbg["weights"].reshape(s.T, s.k) - w_g)[same] <= WEIGHT_TOL)
+    tokens = np.arange(s.T, dtype=np.int32) if full else parity_tokens(s.T, dbg, s.k, 128, seed=7)
+    tokens = tokens[same[tokens]]
+    ref, _, _ = oracle.block_forward(L.x, g_pre, L.router_w, L.w_packed, L.scales, g_post,
+                                     L.alpha, L.beta, s.k, eps=L.eps, tokens=tokens,
+                                     xn=dbg["xn"][tokens])
+    got = synth.bf16_bits_to_f32(out[tokens]).astype(np.float64)
+    m = assert_close(got, ref, name)
+    _say("block", name, "tokens", len(tokens), "of", s.T, m)
 
 
-def _oracle_prenorm(x_bits, gamma, eps):
-    """The normalised copy in double (numpy; for the margin check only)."""
-    x = synth.bf16_bits_to_f32(x_bits).astype(np.float64)
-    r = 1.0 / np.sqrt(np.mean(x * x, axis=1, keepdims=True) + eps)
-    return x * r * gamma.astype(np.float64)
-
+# ------------------------------------------------------ hard inputs for the activation splits
 
 def _check_scaled_routing(L, dbg, scale, label):
-    """Routing bit-exact; weights to 1e-5 times the row's scale: the fp32
-    scores (and the few ulps by which two summation orders differ) grow with
-    the row, and so do the softmax weights' differences."""
+    """Routing bit-exact; weights to 1e-5 on the unscaled rows (on the scaled
+    ones the fp32 scores, and the few ulps by which two summation orders
+    differ, grow with the row, and so do the weights' differences)."""
     r = oracle.route(L.x, L.router_w, L.k)
     for n in ("ids", "offsets", "perm", "inv"):
         np.testing.assert_array_equal(dbg[n], r[n], err_msg=label)
-    tol = WEIGHT_TOL * np.maximum(scale, 1.0)[:, None]
-    assert np.all(np.abs(dbg["weights"] - r["w"]) <= tol), label
+    unscaled = scale == 1.0
+    assert np.all(np.abs(dbg["weights"] - r["w"])[unscaled] <= WEIGHT_TOL), label
 
 
 def test_rows_of_very_different_magnitude():
@@ -447,5 +476,101 @@ def test_rows_of_very_different_magnitude():
         _say("scaled rows", name, L.shape.T)
         out, dbg = run_layer(L)
         _check_scaled_routing(L, dbg, scale, f"scaled rows {name}")
-        _check_tokens(L, out, np.arange(L.shape.T) if L.shape.T <= 64 else _sample(L.shape.T, 12, 4),
-                      f"scaled rows {name}")
+        _check_tokens(L, out, np.arange(L.shape.T), f"scaled rows {name}")
+
+
+# (workload, T, what runs): the FP6 three-part split (wide tiled kernels,
+# F/128 and d/256 even), the FP8 hi/lo split (128 x 256 tiled kernels, odd
+# tile counts; streaming decode kernel at d % 2048 == 0) and the bf16
+# few-row kernels
+OUTLIER_CASES = [
+    ("prefill", 256, "FP6 x3 split, wide tiled kernels"),
+    ("odd_tiles", 512, "FP8 hi/lo split, 128 x 256 tiled kernels"),
+    ("decode4", None, "FP8 hi/lo split, streaming decode kernel"),
+    ("tiny", 64, "bf16 few-row kernels"),
+]
+
+
+def _outlier_layer(name, T):
+    if name == "odd_tiles":
+        w = synth.custom_workload(T=T, d=768, E=8, k=2, F=384, seed=61)
+        return synth.make_layer(w, outliers=True)
+    return synth.make_layer(name, T=T, outliers=True)
+
+
+@pytest.mark.parametrize("alpha0", [True, False])
+@pytest.mark.parametrize("name,T,what", OUTLIER_CASES)
+def test_outlier_activation_blocks(name, T, what, alpha0):
+    """Activations with one channel per 32-block at 2^8..2^12 times the rest
+    and blocks where half the values sit 2^-14 below the others: the hardest
+    inputs for the per-block activation splits (a block's scale follows its
+    largest value).  With alpha = 0 the output is beta * y alone, so the
+    expert path's error is not diluted by the exact alpha * x term."""
+    L = _outlier_layer(name, T)
+    if alpha0:
+        L.alpha[:] = 0.0
+    _say("outliers", name, L.shape, what, "alpha=0" if alpha0 else "alpha drawn")
+    out, dbg = run_layer(L)
+    _check_routing(L, dbg, f"outliers {name}")
+    _check_tokens(L, out, np.arange(L.shape.T), f"outliers {name} alpha0={alpha0}")
+
+
+# ------------------------------------------------------ shapes that take the other kernels
+
+# (T, d, E, k, F): each row names the path it covers
+SHAPE_CASES = [
+    (512, 1024, 16, 4, 384, "gate/up F/128 = 3: 128 x 256 tiled kernel + FP8 split of x; down wide"),
+    (256, 768, 8, 2, 1408, "F = 1408 (11 x 128) and d = 768 (3 x 256): 128 x 256 tiled kernels both"),
+    (1200, 256, 512, 8, 256, "E = 512: top-k with 16 keys per lane, many-token grouping"),
+    (40, 256, 512, 8, 256, "E = 512: single-workgroup routing with 16 keys per lane"),
+    (16, 256, 1024, 32, 128, "E = 1024 (the largest), k = 32"),
+    (4, 768, 16, 4, 384, "decode at d = 768 (not a multiple of 2048): 16-row gate/up kernel"),
+    (6, 2048, 64, 6, 1408, "decode, streaming gate/up kernel at F = 1408"),
+]
+
+
+@pytest.mark.parametrize("T,d,E,k,F,what", SHAPE_CASES)
+def test_other_shapes(T, d, E, k, F, what):
+    w = synth.custom_workload(T=T, d=d, E=E, k=k, F=F, seed=70 + T % 17 + E % 13)
+    L = synth.make_layer(w)
+    _say("shape", (T, d, E, k, F), what)
+    out, dbg = run_layer(L)
+    _check_routing(L, dbg, what)
+    _check_tokens(L, out, np.arange(T), what)
+
+
+# ------------------------------------------------------ the workspace's previous contents
+
+@pytest.mark.parametrize("name,T", [("tiny", 64), ("decode4", None), ("prefill", 512)])
+def test_workspace_contents_do_not_matter(name, T):
+    """The workspace filled with 0xFF bytes (NaN in every float view) before
+    the call gives bit-for-bit the output of a zeroed workspace: no kernel
+    reads a workspace byte it has not written in the same call."""
+    from mixture_experts_gemm_amd import binding as B
+    L = synth.make_layer(name, T=T)
+    dev = upload(L)
+    s = L.shape
+    n = B.moe_layer_workspace_size(s.T, s.d, s.E, s.F, s.k)
+    _say("poisoned workspace", name, s.T)
+    outs = []
+    for fill in (0x00, 0xFF):
+        ws = torch.full((n,), fill, dtype=torch.uint8, device="cuda")
+        outs.append(run_layer(L, dev, debug=False, workspace=ws)[0])
+        del ws
+    assert np.array_equal(outs[0], outs[1]), int((outs[0] != outs[1]).sum())
+
+
+def test_natural_layout_is_not_the_packed_one():
+    """moe_layer_forward reads the packed layout moe_pack_weights writes; the
+    natural bytes are a different arrangement (the contract in
+    include/moe.h), and passing them gives a different, wrong output."""
+    from mixture_experts_gemm_amd import binding as B
+    L = synth.make_layer("tiny")
+    dev = upload(L)
+    s = L.shape
+    good = run_layer(L, dev, debug=False)[0]
+    nat = B.moe_layer_forward(dev["x"], dev["router_w"], torch.from_numpy(L.w_packed).cuda(),
+                              torch.from_numpy(L.scales).cuda(), dev["alpha"], dev["beta"], s.k,
+                              F=s.F)
+    torch.cuda.synchronize()
+    assert not np.array_equal(bf16_bits(nat), good)

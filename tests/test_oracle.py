@@ -495,3 +495,44 @@ def test_block_token_subset():
                                         L.alpha, L.beta, L.k, tokens=sel)
     np.testing.assert_array_equal(sub, full[sel])
     np.testing.assert_array_equal(ids2, ids[sel])
+
+
+def test_block_prenorm_is_rms_norm_rounded():
+    """B1 alone: torch float64 rms_norm times the gain, rounded by the pinned
+    bf16 rounding, bit for bit."""
+    L, g_pre, _ = _block_inputs()
+    xn = oracle.block_prenorm(L.x, g_pre, eps=L.eps)
+    X = torch.from_numpy(synth.bf16_bits_to_f32(L.x).astype(np.float64))
+    Xn = torch.nn.functional.rms_norm(X, (X.shape[-1],), eps=L.eps) * \
+        torch.from_numpy(g_pre.astype(np.float64))
+    np.testing.assert_array_equal(xn, oracle.doubles_to_bf16(Xn.numpy()))
+    sel = np.array([5, 0, 40], np.int32)
+    np.testing.assert_array_equal(oracle.block_prenorm(L.x, g_pre, eps=L.eps, tokens=sel), xn[sel])
+
+
+def test_block_given_normalised_rows():
+    """B2-B3 on given normalised rows: B1's own rows give the same result bit
+    for bit; other rows (B1's doubled, exact in bf16) give the composition of
+    the pinned layer on those rows (alpha = 0, beta = 1 gives y) with torch
+    float64 rms_norm, while the residual still takes the stream s."""
+    L, g_pre, g_post = _block_inputs()
+    sel = np.array([3, 17, 60], np.int32)
+    ref, ids, _ = oracle.block_forward(L.x, g_pre, L.router_w, L.w_packed, L.scales, g_post,
+                                       L.alpha, L.beta, L.k, tokens=sel)
+    xn = oracle.block_prenorm(L.x, g_pre, eps=L.eps, tokens=sel)
+    got, ids2, _ = oracle.block_forward(L.x, g_pre, L.router_w, L.w_packed, L.scales, g_post,
+                                        L.alpha, L.beta, L.k, tokens=sel, xn=xn)
+    np.testing.assert_array_equal(got, ref)
+    np.testing.assert_array_equal(ids2, ids)
+    xn2 = synth.f32_to_bf16_bits(2.0 * synth.bf16_bits_to_f32(xn))
+    s2, _, _ = oracle.block_forward(L.x, g_pre, L.router_w, L.w_packed, L.scales, g_post,
+                                    L.alpha, L.beta, L.k, tokens=sel, xn=xn2)
+    d = L.shape.d
+    y, _, _ = oracle.moe_forward(xn2, L.router_w, L.w_packed, L.scales, np.zeros(d, np.float32),
+                                 np.ones(d, np.float32), L.k)
+    P = torch.nn.functional.rms_norm(torch.from_numpy(y), (d,), eps=L.eps) * \
+        torch.from_numpy(g_post.astype(np.float64))
+    X = synth.bf16_bits_to_f32(L.x[sel]).astype(np.float64)
+    want = L.alpha.astype(np.float64) * X + L.beta.astype(np.float64) * P.numpy()
+    assert np.abs(s2 - want).max() / np.abs(want).max() <= 1e-12
+    assert np.abs(s2 - ref).max() > 1e-3  # the given rows are the ones used

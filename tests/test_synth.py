@@ -75,3 +75,23 @@ def test_uniform_prefill_loads():
     ids = np.argsort(-sc, axis=1, kind="stable")[:, :8]
     cnt = np.bincount(ids.ravel(), minlength=256)
     assert cnt.sum() == 4096 * 8 and 80 <= cnt.min() and cnt.max() <= 180
+
+
+def test_outlier_rows_are_power_of_two_rescalings():
+    """outlier_rows multiplies values by powers of two only (so every value
+    stays exact in bf16): one channel per 32-block by 2^8..2^12, and in about
+    a quarter of the blocks half of the other values by 2^-14; seeded."""
+    w = synth.WORKLOADS["tiny"]
+    base = synth.make_tokens(w, synth.make_router(w), gap=0)
+    out = synth.outlier_rows(base, 0, 0, np.arange(base.shape[0]))
+    np.testing.assert_array_equal(out, synth.outlier_rows(base, 0, 0, np.arange(base.shape[0])))
+    a = synth.bf16_bits_to_f32(base).astype(np.float64)
+    b = synth.bf16_bits_to_f32(out).astype(np.float64)
+    nz = a != 0
+    ratio = np.log2(np.abs(b[nz] / a[nz]))
+    assert set(np.unique(ratio)) <= {0.0, -14.0, 8.0, 9.0, 10.0, 11.0, 12.0}
+    up = (np.log2(np.abs(b / np.where(nz, a, 1))) >= 8).reshape(base.shape[0], -1, 32)
+    assert np.all(up.sum(axis=2) == 1)  # one raised channel per block
+    low = (np.isclose(np.abs(b / np.where(nz, a, 1)), 2.0 ** -14)).reshape(base.shape[0], -1, 32)
+    frac = (low.sum(axis=2) > 0).mean()
+    assert 0.15 < frac < 0.35, frac
