@@ -29,7 +29,7 @@
  * current HIP device unless stated otherwise; the caller allocates and owns
  * them, including the workspace.  The library allocates no device memory
  * (except moe_latent_forward's rocBLAS handle, see there), keeps no pointer
- * after returning, and queues all work asynchronously on
+ * to the caller's buffers after returning, and queues all work asynchronously on
  * `stream` (a hipStream_t; NULL = the null stream).  Buffers must stay valid
  * until that work completes.  Calls on distinct workspaces are independent.
  *
@@ -59,7 +59,9 @@ enum {
     MOE_ERR_WORKSPACE = -3, /* workspace_bytes below moe_layer_workspace_size()  */
     MOE_ERR_ARCH = -4,      /* current device is not gfx950                      */
     MOE_ERR_HIP = -5,       /* a HIP runtime call or kernel launch failed        */
-    MOE_ERR_ALIGN = -6      /* a device pointer is not 16-byte aligned           */
+    MOE_ERR_ALIGN = -6,     /* a device pointer is not 16-byte aligned           */
+    MOE_ERR_SCRATCH = -7    /* moe_layer_forward_noalloc: the sizes need more
+                               than MOE_STATIC_SCRATCH_BYTES of scratch          */
 };
 
 typedef struct moe_dims {
@@ -180,6 +182,31 @@ int moe_layer_forward(const moe_dims_t *dims, const void *x, const float *router
                       const float *alpha, const float *beta, int32_t k, void *s_out,
                       void *workspace, size_t workspace_bytes, void *stream,
                       const moe_debug_t *debug);
+
+/*
+ * For callers that cannot allocate device memory at all -- code being
+ * captured into a HIP graph, tight serving loops, harnesses that forbid
+ * hipMalloc: moe_layer_forward without the workspace argument.  Its
+ * intermediate buffers live in a static device array of the library
+ * (MOE_STATIC_SCRATCH_BYTES, 32 MiB, 256-byte aligned), one per GPU, part of
+ * the library's device code and held until the process ends; the call
+ * itself allocates nothing.  32 MiB holds every call whose
+ * moe_layer_workspace_size(dims, k) is at most that size: at d = 8192,
+ * E = 256, k = 8, F = 2048 up to T = 128 tokens.  Larger sizes return
+ * MOE_ERR_SCRATCH before anything is queued.
+ *
+ * Arguments, errors, determinism and output as moe_layer_forward.  Every
+ * call on one GPU uses that GPU's single array, and no kernel reads scratch
+ * it has not written in the same call, so consecutive calls on one stream
+ * are independent; calls that can overlap on one GPU (two streams, two host
+ * threads) race on the array and give undefined results: serialise them.
+ */
+#define MOE_STATIC_SCRATCH_BYTES (32u << 20)
+
+int moe_layer_forward_noalloc(const moe_dims_t *dims, const void *x, const float *router_w,
+                              const uint8_t *expert_w_packed, const uint8_t *scales,
+                              const float *alpha, const float *beta, int32_t k, void *s_out,
+                              void *stream, const moe_debug_t *debug);
 
 /*
  * The 16-block weight format ("Muse Spark Open を段階的に分解する"

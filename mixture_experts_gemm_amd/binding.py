@@ -24,6 +24,8 @@ MOE_ERR_WORKSPACE = -3
 MOE_ERR_ARCH = -4
 MOE_ERR_HIP = -5
 MOE_ERR_ALIGN = -6
+MOE_ERR_SCRATCH = -7
+MOE_STATIC_SCRATCH_BYTES = 32 << 20
 
 
 class MoeError(RuntimeError):
@@ -69,6 +71,9 @@ def lib() -> C.CDLL:
         L.moe_layer_forward.argtypes = [C.POINTER(moe_dims_t), P, P, P, P, P, P, C.c_int32, P, P,
                                         C.c_size_t, P, C.POINTER(moe_debug_t)]
         L.moe_layer_forward.restype = C.c_int
+        L.moe_layer_forward_noalloc.argtypes = [C.POINTER(moe_dims_t), P, P, P, P, P, P, C.c_int32,
+                                                P, P, C.POINTER(moe_debug_t)]
+        L.moe_layer_forward_noalloc.restype = C.c_int
         L.moe_pack_weights.argtypes = [C.POINTER(moe_dims_t), P, P, P, P, P]
         L.moe_pack_weights.restype = C.c_int
         L.moe_dequant_mxfp4.argtypes = [P, P, C.c_int64, C.c_int32, P, P]
@@ -196,6 +201,34 @@ def moe_layer_forward(x, router_w, expert_w_packed, scales, alpha, beta, k, *, F
                                  _stream(stream), C.byref(dbg) if dbg is not None else None)
     if rc != MOE_OK:
         raise MoeError(rc, "moe_layer_forward")
+    return s_out
+
+
+def moe_layer_forward_noalloc(x, router_w, expert_w_packed, scales, alpha, beta, k, *, F=None,
+                              eps=1e-6, s_out=None, stream=None, debug=None):
+    """moe_layer_forward on the library's static scratch (no workspace, no
+    allocation in the call; sizes up to MOE_STATIC_SCRATCH_BYTES of
+    workspace).  Returns s_out (bf16 [T][d])."""
+    T, d = x.shape
+    E = router_w.shape[0]
+    if F is None:
+        F = expert_w_packed.shape[1] * 2 // (3 * d)
+    _check(x, "x", torch.bfloat16, (T, d))
+    _check(router_w, "router_w", torch.float32, (E, d))
+    _check(expert_w_packed, "expert_w_packed", torch.uint8, (E, 3 * d * F // 2))
+    _check(scales, "scales", torch.uint8, (E, 3 * d * F // 32))
+    _check(alpha, "alpha", torch.float32, (d,))
+    _check(beta, "beta", torch.float32, (d,))
+    if s_out is None:
+        s_out = torch.empty_like(x)
+    _check(s_out, "s_out", torch.bfloat16, (T, d))
+    dbg = _debug_struct(debug)
+    rc = lib().moe_layer_forward_noalloc(C.byref(_dims(T, d, E, F, eps)), _ptr(x), _ptr(router_w),
+                                         _ptr(expert_w_packed), _ptr(scales), _ptr(alpha),
+                                         _ptr(beta), int(k), _ptr(s_out), _stream(stream),
+                                         C.byref(dbg) if dbg is not None else None)
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_layer_forward_noalloc")
     return s_out
 
 

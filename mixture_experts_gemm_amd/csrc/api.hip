@@ -4,6 +4,7 @@
 #include <string.h>
 
 #include <initializer_list>
+#include <mutex>
 
 #include "../../include/moe.h"
 #include "internal.h"
@@ -142,26 +143,15 @@ extern "C" size_t moe_layer_workspace_size(const moe_dims_t *dims, int32_t k)
     return carve_workspace(to_shape(dims, k), nullptr).bytes;
 }
 
-extern "C" int moe_layer_forward(const moe_dims_t *dims, const void *x, const float *router_w,
-                                 const uint8_t *expert_w_packed, const uint8_t *scales,
-                                 const float *alpha, const float *beta, int32_t k, void *s_out,
-                                 void *workspace, size_t workspace_bytes, void *stream,
-                                 const moe_debug_t *debug)
-{
-    if (!dims) return MOE_ERR_NULL;
-    if (!shape_ok(dims, k)) return MOE_ERR_SHAPE;
-    if (dims->T == 0) return MOE_OK;
-    if (!x || !router_w || !expert_w_packed || !scales || !alpha || !beta || !s_out || !workspace)
-        return MOE_ERR_NULL;
-    if (!aligned16({x, router_w, expert_w_packed, scales, alpha, beta, s_out}))
-        return MOE_ERR_ALIGN;
-    const Shape s = to_shape(dims, k);
-    const Workspace need = carve_workspace(s, nullptr);
-    if (workspace_bytes < need.bytes) return MOE_ERR_WORKSPACE;
-    if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return MOE_ERR_WORKSPACE;
-    int rc = check_arch();
-    if (rc != MOE_OK) return rc;
+namespace moe {
 
+// The layer's kernel sequence on a checked shape and a workspace that is
+// large enough and 256-byte aligned.
+static int layer_forward(const Shape &s, const void *x, const float *router_w,
+                         const uint8_t *expert_w_packed, const uint8_t *scales, const float *alpha,
+                         const float *beta, void *s_out, void *workspace, void *stream,
+                         const moe_debug_t *debug)
+{
     hipStream_t st = static_cast<hipStream_t>(stream);
     const Workspace ws = carve_workspace(s, workspace);
     const uint16_t *xb = static_cast<const uint16_t *>(x);
@@ -192,6 +182,102 @@ extern "C" int moe_layer_forward(const moe_dims_t *dims, const void *x, const fl
 
     if (debug && copy_debug(debug, ws, s, st) != hipSuccess) return MOE_ERR_HIP;
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+// Argument checks of moe_layer_forward except the workspace's.
+static int layer_args_ok(const moe_dims_t *dims, const void *x, const float *router_w,
+                         const uint8_t *expert_w_packed, const uint8_t *scales, const float *alpha,
+                         const float *beta, int32_t k, void *s_out)
+{
+    if (!dims) return MOE_ERR_NULL;
+    if (!shape_ok(dims, k)) return MOE_ERR_SHAPE;
+    if (dims->T == 0) return MOE_OK;
+    if (!x || !router_w || !expert_w_packed || !scales || !alpha || !beta || !s_out)
+        return MOE_ERR_NULL;
+    if (!aligned16({x, router_w, expert_w_packed, scales, alpha, beta, s_out}))
+        return MOE_ERR_ALIGN;
+    return MOE_OK;
+}
+
+}  // namespace moe
+
+extern "C" int moe_layer_forward(const moe_dims_t *dims, const void *x, const float *router_w,
+                                 const uint8_t *expert_w_packed, const uint8_t *scales,
+                                 const float *alpha, const float *beta, int32_t k, void *s_out,
+                                 void *workspace, size_t workspace_bytes, void *stream,
+                                 const moe_debug_t *debug)
+{
+    int rc = layer_args_ok(dims, x, router_w, expert_w_packed, scales, alpha, beta, k, s_out);
+    if (rc != MOE_OK || dims->T == 0) return rc;
+    if (!workspace) return MOE_ERR_NULL;
+    const Shape s = to_shape(dims, k);
+    if (workspace_bytes < carve_workspace(s, nullptr).bytes) return MOE_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return MOE_ERR_WORKSPACE;
+    rc = check_arch();
+    if (rc != MOE_OK) return rc;
+    return layer_forward(s, x, router_w, expert_w_packed, scales, alpha, beta, s_out, workspace,
+                         stream, debug);
+}
+
+// ---- the variant without a workspace argument ---------------------------------
+
+namespace moe {
+
+// The scratch memory of moe_layer_forward_noalloc: one array per GPU, part
+// of the library's device code object, held until the process ends.  Host
+// code never uses this name as an address (on the host it is a stand-in
+// symbol); it uses the device address scratch_address() looked up once per
+// device.
+static __device__ __align__(256) uint8_t scratch[MOE_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void *g_scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on the current device (looked up at the first
+// call on that device, with it current), or NULL with *err set.
+static void *scratch_address(int *err)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        *err = MOE_ERR_HIP;
+        return nullptr;
+    }
+    if (dev < 0 || dev >= kMaxDevices) {
+        *err = MOE_ERR_HIP;
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+            (void)hipGetLastError();
+            *err = MOE_ERR_HIP;
+            return nullptr;
+        }
+        g_scratch_ptr[dev] = ptr;
+    }
+    return g_scratch_ptr[dev];
+}
+
+}  // namespace moe
+
+extern "C" int moe_layer_forward_noalloc(const moe_dims_t *dims, const void *x,
+                                         const float *router_w, const uint8_t *expert_w_packed,
+                                         const uint8_t *scales, const float *alpha,
+                                         const float *beta, int32_t k, void *s_out, void *stream,
+                                         const moe_debug_t *debug)
+{
+    int rc = layer_args_ok(dims, x, router_w, expert_w_packed, scales, alpha, beta, k, s_out);
+    if (rc != MOE_OK || dims->T == 0) return rc;
+    const Shape s = to_shape(dims, k);
+    if (carve_workspace(s, nullptr).bytes > (size_t)MOE_STATIC_SCRATCH_BYTES) return MOE_ERR_SCRATCH;
+    rc = check_arch();
+    if (rc != MOE_OK) return rc;
+    void *ws = scratch_address(&rc);
+    if (!ws) return rc;
+    return layer_forward(s, x, router_w, expert_w_packed, scales, alpha, beta, s_out, ws, stream,
+                         debug);
 }
 
 // ---- latent-width variant ---------------------------------------------------
@@ -560,6 +646,9 @@ extern "C" const char *moe_status_string(int status)
     case MOE_ERR_ARCH: return "current device is not gfx950";
     case MOE_ERR_HIP: return "HIP runtime or kernel launch error";
     case MOE_ERR_ALIGN: return "a device pointer is not 16-byte aligned";
+    case MOE_ERR_SCRATCH:
+        return "the sizes need more scratch than the library's static scratch holds "
+               "(MOE_STATIC_SCRATCH_BYTES)";
     default: return "unknown status";
     }
 }

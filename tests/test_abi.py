@@ -18,15 +18,17 @@ def test_exports_every_declared_function(L):
     assert set(names) == {"moe_layer_workspace_size", "moe_layer_forward", "moe_pack_weights",
                           "moe_dequant_mxfp4", "moe_status_string", "moe_latent_workspace_size",
                           "moe_latent_forward", "moe_block_workspace_size", "moe_block_forward",
-                          "moe_pack_weights_nvfp4", "moe_layer_forward_nvfp4"}
+                          "moe_pack_weights_nvfp4", "moe_layer_forward_nvfp4",
+                          "moe_layer_forward_noalloc"}
     for n in names:
         assert hasattr(L, n), n
 
 
 def test_status_strings():
-    for code in (0, -1, -2, -3, -4, -5, -6):
+    for code in (0, -1, -2, -3, -4, -5, -6, -7):
         assert B.moe_status_string(code) and B.moe_status_string(code) != "unknown status"
     assert B.moe_status_string(7) == "unknown status"
+    assert B.moe_status_string(-8) == "unknown status"
 
 
 def test_workspace_size():
@@ -228,3 +230,34 @@ def test_nv_pack_argument_errors():
     assert pack(dims, None, p, p, p, None) == B.MOE_ERR_NULL
     assert pack(dims, p, None, p, p, None) == B.MOE_ERR_NULL
     assert pack(dims, p, p, p, C.c_void_p((1 << 20) + 4), None) == B.MOE_ERR_ALIGN
+
+
+# ------------------------------------------------- the variant without a workspace
+
+def test_noalloc_argument_errors():
+    """Argument errors of moe_layer_forward_noalloc, all returned before any
+    HIP call: NULL pointers, bad sizes, misaligned pointers, and sizes whose
+    workspace would exceed the static scratch (MOE_ERR_SCRATCH)."""
+    f = B.lib().moe_layer_forward_noalloc
+    p = C.c_void_p(1 << 20)
+    odd = C.c_void_p((1 << 20) + 8)
+    good = B.moe_dims_t(64, 256, 8, 512, 1e-6)
+
+    def call(dims, k=2, **repl):
+        a = dict(x=p, router_w=p, w=p, s=p, alpha=p, beta=p, s_out=p)
+        a.update(repl)
+        return f(C.byref(dims) if dims is not None else None, a["x"], a["router_w"], a["w"], a["s"],
+                 a["alpha"], a["beta"], k, a["s_out"], None, None)
+
+    assert call(None) == B.MOE_ERR_NULL
+    for name in ("x", "router_w", "w", "s", "alpha", "beta", "s_out"):
+        assert call(good, **{name: None}) == B.MOE_ERR_NULL, name
+        assert call(good, **{name: odd}) == B.MOE_ERR_ALIGN, name
+    assert call(B.moe_dims_t(64, 200, 8, 512, 1e-6)) == B.MOE_ERR_SHAPE
+    assert call(good, k=9) == B.MOE_ERR_SHAPE
+    assert call(B.moe_dims_t(0, 256, 8, 512, 1e-6), x=None) == B.MOE_OK
+    # the Muse shape fits up to T = 128; T = 130 needs more than 32 MiB
+    assert B.moe_layer_workspace_size(128, 8192, 256, 2048, 8) <= B.MOE_STATIC_SCRATCH_BYTES
+    assert B.moe_layer_workspace_size(130, 8192, 256, 2048, 8) > B.MOE_STATIC_SCRATCH_BYTES
+    assert call(B.moe_dims_t(130, 8192, 256, 2048, 1e-6), k=8) == B.MOE_ERR_SCRATCH
+    assert call(B.moe_dims_t(4096, 8192, 256, 2048, 1e-6), k=8) == B.MOE_ERR_SCRATCH
