@@ -1,18 +1,20 @@
 #!/usr/bin/env python3
 """Throughput of the MoE expert layer on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload decode4|decode1|prefill|skewed]
+    python bench.py [--steps K] [--warmup W] [--workload decode4|decode1|prefill|skewed|stack|...]
 
 One step = one moe_layer_forward call (router, top-k, grouping, gate/up +
 SwiGLU, down + row sums of squares, RMSNorm/combine/gate) over one batch of
-synthetic tokens whose inputs already sit in HBM.  Decode steps rotate over
-four independent weight sets (27 GB) and a pool of token rows, so the 256 MB
-Infinity Cache cannot serve the expert weights.
+synthetic tokens whose inputs already sit in HBM; for the `stack` workload
+one step is four chained calls on four weight sets.  Decode steps rotate
+over four independent weight sets (27 GB) and a pool of token rows, so the
+256 MB Infinity Cache cannot serve the expert weights.
 
 Prints ONE JSON line: tokens/s for the named workload, the roofline of the
 dominant kernel (gate/up), measured live with HIP events recorded by the
-library on the benchmark's stream, the CPU oracle on a bounded sample, and
-the other shapes under "also".
+library on the benchmark's stream, beside the whole layer's fraction; the
+CPU oracle on a bounded sample; and the other shapes under "also", each with
+its own roofline, oracle baseline and three-rerun determinism flag.
 """
 import argparse
 import json
@@ -29,7 +31,10 @@ WORKLOAD_TEXT = {
     "decode4": "Muse-shaped decode, 4 concurrent requests (T=4, d=8192, E=256, top-8, F=2048, MXFP4)",
     "decode1": "Muse-shaped decode, single request (T=1, d=8192, E=256, top-8, F=2048, MXFP4)",
     "prefill": "Muse-shaped prefill micro-batch (T=4096, d=8192, E=256, top-8, F=2048, MXFP4, uniform routing)",
-    "skewed": "Skewed-routing prefill (T=16384, Zipf(1.2) router bias, top-8 experts ~40% of slots)",
+    "skewed": "Skewed-routing prefill (T=16384, d=8192, E=256, top-8, F=2048, MXFP4, Zipf(1.2) router "
+              "bias, top-8 experts ~40% of slots)",
+    "stack": "Stack of 4 chained MoE layers with independent weights (T=8192, d=8192, E=256, top-8, "
+             "F=2048, MXFP4, per-expert RMSNorm + alpha/beta gated residual between layers)",
     "ep753": "One GPU's share under 8-way expert parallelism, 753-token batch (E=32 local experts, "
              "753 routed rows, k=1, d=8192, F=2048, MXFP4)",
     "ep3012": "One GPU's share under 8-way expert parallelism, 3012-token batch (E=32 local experts, "
@@ -65,11 +70,15 @@ def parse():
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="decode4", choices=sorted(WORKLOAD_TEXT))
-    ap.add_argument("--also", default="decode1,prefill,ep753,ep3012,latent4,latent_prefill,block4,"
-                                      "block_prefill,nv4,nv_prefill",
+    ap.add_argument("--also", default="decode1,prefill,skewed,stack,ep753,ep3012,latent4,latent_prefill,"
+                                      "block4,block_prefill,nv4,nv_prefill",
                     help="comma list of extra workloads timed after the main one ('' for none)")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="oracle time on the main workload")
+    ap.add_argument("--cpu-also-seconds", type=float, default=3.0,
+                    help="oracle time on each extra workload and each one-thread run")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the copy / GEMM peak probes")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (a known-size kernel "
                          "to scale hardware byte counters against)")
@@ -201,6 +210,7 @@ GATE_UP_KERNEL = {
     "decode4": "gemm1_stream_kernel (gate/up + SwiGLU, persistent, MX MFMA)",
     "prefill": "gemm_mxw_kernel<true> (gate/up + SwiGLU, 128x512 tiles, MX MFMA)",
     "skewed": "gemm_mxw_kernel<true> (gate/up + SwiGLU, 128x512 tiles, MX MFMA)",
+    "stack": "gemm_mxw_kernel<true> (gate/up + SwiGLU, 128x512 tiles, MX MFMA)",
     "ep753": "gemm_mxw_kernel<true> (gate/up + SwiGLU, 128x512 tiles, MX MFMA)",
     "ep3012": "gemm_mxw_kernel<true> (gate/up + SwiGLU, 128x512 tiles, MX MFMA)",
     "latent4": "gemm1_stream_kernel (gate/up + SwiGLU, persistent, MX MFMA)",
@@ -208,7 +218,16 @@ GATE_UP_KERNEL = {
     "block4": "gemm1_stream_kernel (gate/up + SwiGLU, persistent, MX MFMA)",
     "block_prefill": "gemm_mxw_kernel<true> (gate/up + SwiGLU, 128x512 tiles, MX MFMA)",
     "nv4": "gemm1_stream_kernel<4, true> (gate/up + SwiGLU, persistent, fp16 MFMA, 16-block weights)",
-    "nv_prefill": "gemm_nv_kernel<true, 192> (gate/up + SwiGLU, 192x256 tiles, fp16 MFMA, 16-block weights)",
+    "nv_prefill": "gemm_nv_kernel<true> (gate/up + SwiGLU, 192x256 tiles, fp16 MFMA, 16-block weights)",
+}
+# How the gate/up kernel issues one bf16 x FP4 product on the matrix cores:
+# (MFMAs per product, operand types, that instruction's dense peak in
+# TFLOP/s).  The streaming decode kernel splits x into two FP8 parts, the
+# wide prefill kernel into three FP6 parts; the 16-block kernels run fp16.
+MX_ISSUE = {
+    "gemm1_stream_kernel": (2, "fp8 x fp4 (two FP8 parts of x)", 5000.0),
+    "gemm_mxw_kernel": (3, "fp6 x fp4 (three FP6 parts of x)", 10100.0),
+    "gemm_nv_kernel": (1, "fp16 x fp16 (weights widened)", 2500.0),
 }
 
 
@@ -218,6 +237,33 @@ EVENT_EVERY = 8  # timed steps between two gate/up kernel timings
 def counter_summary(name):
     """Committed HBM byte-counter summary of the gate/up kernel on this workload."""
     return os.path.join(ROOT, "profiles", f"gate_up_{name}_hbm_counters.md")
+
+
+def _pct(vals, q):
+    v = sorted(vals)
+    return v[min(len(v) - 1, int(round(q * (len(v) - 1))))]
+
+
+def _roofline(name, nbytes, flops, g1_ms, R):
+    """The gate/up kernel against the bound of its shape (the larger of the
+    byte time at the HBM peak and the flop time at the bf16 peak)."""
+    hbm_bound = nbytes / R.MI355X_HBM_BYTES_PER_S >= flops / R.MI355X_BF16_FLOPS_PER_S
+    kern = GATE_UP_KERNEL[name]
+    out = dict(kernel=kern, traffic=R.recorded_traffic(counter_summary(name)))
+    if hbm_bound:
+        achieved = nbytes / (g1_ms * 1e-3)
+        out.update(bound="hbm", achieved=achieved / 1e9, peak=R.MI355X_HBM_BYTES_PER_S / 1e9, unit="GB/s",
+                   frac=achieved / R.MI355X_HBM_BYTES_PER_S, algorithmic_bytes_per_launch=nbytes)
+    else:
+        achieved = flops / (g1_ms * 1e-3)
+        out.update(bound="mfma", achieved=achieved / 1e12, peak=R.MI355X_BF16_FLOPS_PER_S / 1e12,
+                   unit="TFLOP/s", frac=achieved / R.MI355X_BF16_FLOPS_PER_S,
+                   algorithmic_flops_per_launch=flops)
+        parts, what, peak = MX_ISSUE[kern.split(" ")[0].split("<")[0]]
+        issued = parts * flops / (g1_ms * 1e-3)
+        out["mx_issue"] = dict(mfma_per_product=parts, operands=what, issued_TFLOPs=issued / 1e12,
+                               peak_TFLOPs=peak, frac=issued / (peak * 1e12))
+    return out
 
 
 def time_workload(name, steps, warmup, device):
@@ -251,6 +297,7 @@ def time_workload(name, steps, warmup, device):
             for i, st in enumerate(sets):
                 st["g_pre"], st["g_post"] = (torch.from_numpy(v).to(device)
                                              for v in synth.make_norm_gains(w, layer=i))
+            host.g_pre, host.g_post = sets[0]["g_pre"].cpu().numpy(), sets[0]["g_post"].cpu().numpy()
     T = s.T
     npool = xpool.shape[0] // T
     if latent:
@@ -264,21 +311,21 @@ def time_workload(name, steps, warmup, device):
     out = torch.empty(T, D, dtype=torch.bfloat16, device=device)
     offsets = torch.empty(s.E + 1, dtype=torch.int32, device=device)
 
-    def call(i, debug=None):
+    def call(i, debug=None, dst=out):
         st = sets[i % nsets]
         xb = xpool[(i % npool) * T:(i % npool + 1) * T]
         if latent:
             B.moe_latent_forward(xb, st["wr"], st["wc"], st["w"], st["s"], st["we"], st["alpha"],
-                                 st["beta"], s.k, F=s.F, s_out=out, workspace=ws, debug=debug)
+                                 st["beta"], s.k, F=s.F, s_out=dst, workspace=ws, debug=debug)
         elif block:
             B.moe_block_forward(xb, st["g_pre"], st["wr"], st["w"], st["s"], st["g_post"], st["alpha"],
-                                st["beta"], s.k, F=s.F, s_out=out, workspace=ws, debug=debug)
+                                st["beta"], s.k, F=s.F, s_out=dst, workspace=ws, debug=debug)
         elif nv:
             B.moe_layer_forward_nvfp4(xb, st["wr"], st["w"], st["s"], st["gs"], st["alpha"], st["beta"],
-                                      s.k, F=s.F, s_out=out, workspace=ws, debug=debug)
+                                      s.k, F=s.F, s_out=dst, workspace=ws, debug=debug)
         else:
             B.moe_layer_forward(xb, st["wr"], st["w"], st["s"], st["alpha"], st["beta"], s.k, F=s.F,
-                                s_out=out, workspace=ws, debug=debug)
+                                s_out=dst, workspace=ws, debug=debug)
 
     # accounting pass (untimed): distinct experts per step, from the library's own grouping
     U = []
@@ -287,6 +334,13 @@ def time_workload(name, steps, warmup, device):
         off = offsets.cpu()
         U.append(int(((off[1:] - off[:-1]) > 0).sum()))
     assert torch.isfinite(out.float()).all(), "non-finite layer output"
+    # determinism: the same step three times, outputs compared bit for bit
+    reruns = [torch.empty_like(out) for _ in range(3)]
+    for r in reruns:
+        call(0, dst=r)
+    torch.cuda.synchronize()
+    deterministic = all(torch.equal(reruns[0], r) for r in reruns[1:])
+    del reruns
     for i in range(warmup):
         call(i)
     # The gate/up kernel is timed by the HIP events its own dispatch records,
@@ -320,34 +374,19 @@ def time_workload(name, steps, warmup, device):
         call(i)
         b.record()
     torch.cuda.synchronize()
-    step_us = sorted(a.elapsed_time(b) * 1e3 for a, b in lat)
-    pct = lambda q: step_us[min(len(step_us) - 1, int(round(q * (len(step_us) - 1))))]
+    step_us = [a.elapsed_time(b) * 1e3 for a, b in lat]
     res = dict(
         T=T, steps=steps, ms_per_step=elapsed / steps * 1e3, tokens_per_s=T * steps / elapsed,
         gemm1_ms=g1_ms, gemm1_timed_launches=len(timed), distinct_experts_mean=u_mean, finite=out_ok,
-        step_us_p10_p50_p90=[pct(0.1), pct(0.5), pct(0.9)], step_us_samples=n_lat,
+        bitwise_identical_3_reruns=deterministic,
+        step_us_p10_p50_p90=[_pct(step_us, 0.1), _pct(step_us, 0.5), _pct(step_us, 0.9)],
+        step_us_samples=n_lat,
     )
     # the gate/up kernel's algorithmic bytes (over the timed launches: U, the
-    # distinct experts, differs per step) and flops; its bound is the larger
-    # of the two times at the peaks
+    # distinct experts, differs per step) and flops
     w1b = R.nvfp4_w1_bytes(s.d, s.F) if nv else R.mxfp4_w1_bytes(s.d, s.F)
     nbytes = sum(w1b * U[i] + T * s.d * 2 + S * s.F * 2 for i in timed) / len(timed)
-    flops = R.gemm1_flops(S, s.d, s.F)
-    hbm_bound = nbytes / R.MI355X_HBM_BYTES_PER_S >= flops / R.MI355X_BF16_FLOPS_PER_S
-    if hbm_bound:
-        achieved = nbytes / (g1_ms * 1e-3)
-        res["roofline"] = dict(bound="hbm", achieved=achieved / 1e9, peak=R.MI355X_HBM_BYTES_PER_S / 1e9,
-                               unit="GB/s", frac=achieved / R.MI355X_HBM_BYTES_PER_S,
-                               traffic=R.recorded_traffic(counter_summary(name)),
-                               kernel=GATE_UP_KERNEL[name],
-                               algorithmic_bytes_per_launch=nbytes)
-    else:
-        achieved = flops / (g1_ms * 1e-3)
-        res["roofline"] = dict(bound="mfma", achieved=achieved / 1e12, peak=R.MI355X_BF16_FLOPS_PER_S / 1e12,
-                               unit="TFLOP/s", frac=achieved / R.MI355X_BF16_FLOPS_PER_S,
-                               traffic=R.recorded_traffic(counter_summary(name)),
-                               kernel=GATE_UP_KERNEL[name],
-                               algorithmic_flops_per_launch=flops)
+    res["roofline"] = _roofline(name, nbytes, R.gemm1_flops(S, s.d, s.F), g1_ms, R)
     # the whole layer against both peaks (algorithmic bytes with the realized U)
     if latent:
         lb = sum(R.latent_layer_bytes(T, D, s.d, s.E, s.F, u) for u in U) / len(U)
@@ -357,33 +396,210 @@ def time_workload(name, steps, warmup, device):
         lf = R.layer_flops(T, s.d, s.k, s.F)
     res["layer_hbm_frac"] = lb / (elapsed / steps) / R.MI355X_HBM_BYTES_PER_S
     res["layer_mfma_frac"] = lf / (elapsed / steps) / R.MI355X_BF16_FLOPS_PER_S
+    res["layer_bytes"] = lb
+    res["layer_flops"] = lf
     log(json.dumps(res))
     return res, host, T
 
 
-def cpu_baseline(host, T, seconds):
-    """The oracle as it is, on the host cores, over whole steps of the same workload."""
+def make_stack_sets(device):
+    """The four layers of the stack workload from the shared generator (host
+    copies kept for the oracle's chain), packed on the GPU."""
+    import numpy as np
+    import torch
+
+    from mixture_experts_gemm_amd import binding as B
+    from mixture_experts_gemm_amd import synth
+
+    w = synth.WORKLOADS["stack"]
+    s = w.shape
+    hosts, sets = [], []
+    for layer in range(w.layers):
+        h = synth.make_layer(w, layer=layer, with_tokens=(layer == 0), threads=16)
+        Wp, Sp = B.moe_pack_weights(torch.from_numpy(h.w_packed).to(device),
+                                    torch.from_numpy(h.scales).to(device), s.d, s.F)
+        torch.cuda.synchronize()
+        sets.append(dict(w=Wp, s=Sp, wr=torch.from_numpy(h.router_w).to(device),
+                         alpha=torch.from_numpy(h.alpha).to(device),
+                         beta=torch.from_numpy(h.beta).to(device)))
+        hosts.append(h)
+    x = torch.from_numpy(hosts[0].x.view(np.int16)).to(device).view(torch.bfloat16)
+    return w, hosts, sets, x
+
+
+def time_stack(steps, warmup, device, sample=32):
+    """Four chained layers per step (each layer's bf16 output is the next
+    one's input).  Also reports, on `sample` seeded tokens, each layer's
+    error against the oracle run on the GPU's own layer input
+    (teacher-forced) and against the oracle's own free-running chain (the
+    error growth through the gated residual)."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from mixture_experts_gemm_amd import binding as B
+    from mixture_experts_gemm_amd import roofline as R
+    from mixture_experts_gemm_amd import synth
+
+    log("generating stack: 4 layers")
+    w, hosts, sets, x = make_stack_sets(device)
+    s = w.shape
+    T = s.T
+    ws = B.workspace_for(T, s.d, s.E, s.F, s.k, device=device)
+    bufs = [torch.empty(T, s.d, dtype=torch.bfloat16, device=device) for _ in range(2)]
+
+    def step(keep=None, ev=None):
+        cur = x
+        for layer, st in enumerate(sets):
+            dst = keep[layer] if keep is not None else bufs[layer % 2]
+            dbg = dict(events={"gemm1": ev[layer]}) if ev is not None else None
+            B.moe_layer_forward(cur, st["wr"], st["w"], st["s"], st["alpha"], st["beta"], s.k, F=s.F,
+                                s_out=dst, workspace=ws, debug=dbg)
+            cur = dst
+        return cur
+
+    # every layer's output of one step, then the determinism reruns
+    outs = [torch.empty(T, s.d, dtype=torch.bfloat16, device=device) for _ in range(4)]
+    step(keep=outs)
+    reruns = []
+    for _ in range(2):
+        o2 = [torch.empty_like(o) for o in outs]
+        step(keep=o2)
+        reruns.append(o2)
+    torch.cuda.synchronize()
+    deterministic = all(torch.equal(a, b) for r in reruns for a, b in zip(outs, r))
+    del reruns
+    for _ in range(warmup):
+        step()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(4)]
+    for a, b in ev:
+        a.record()
+        b.record()
+    torch.cuda.synchronize()
+    log(f"timing stack: {steps} steps after {warmup} warmup")
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(ev=ev if i == steps - 1 else None)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    g1_ms = sum(a.elapsed_time(b) for a, b in ev) / 4
+    S = T * s.k
+    flops = 4 * R.layer_flops(T, s.d, s.k, s.F)
+    res = dict(T=T, layers=4, steps=steps, ms_per_step=elapsed / steps * 1e3,
+               tokens_per_s=T * steps / elapsed, gemm1_ms=g1_ms, bitwise_identical_3_reruns=deterministic,
+               layer_mfma_frac=flops / (elapsed / steps) / R.MI355X_BF16_FLOPS_PER_S)
+    res["roofline"] = _roofline("stack", 0, R.gemm1_flops(S, s.d, s.F), g1_ms, R)
+    # per-layer error on a token sample
+    tok = np.sort(np.random.default_rng(4).choice(T, size=sample, replace=False)).astype(np.int32)
+    got = [synth.bf16_bits_to_f32(o.view(torch.int16).cpu().numpy().view(np.uint16)[tok]).astype(np.float64)
+           for o in outs]
+    gin = [hosts[0].x] + [o.view(torch.int16).cpu().numpy().view(np.uint16) for o in outs[:-1]]
+    ref_chain = hosts[0].x[tok]
+    err = []
+    for layer, h in enumerate(hosts):
+        tf, _, _ = oracle.moe_forward(gin[layer], h.router_w, h.w_packed, h.scales, h.alpha, h.beta, h.k,
+                                      eps=h.eps, tokens=tok)
+        fr, _, _ = oracle.moe_forward(ref_chain, h.router_w, h.w_packed, h.scales, h.alpha, h.beta, h.k,
+                                      eps=h.eps)
+        m_tf, m_fr = _metrics(got[layer], tf), _metrics(got[layer], fr)
+        err.append(dict(layer=layer, teacher_forced=m_tf, free_running=m_fr))
+        ref_chain = oracle.doubles_to_bf16(fr)
+    res["per_layer_error"] = err
+    res["error_sample_tokens"] = sample
+    log(json.dumps(res))
+    return res, hosts, T
+
+
+def _metrics(a, b):
+    import numpy as np
+    rms = np.sqrt(np.mean(b * b, axis=-1, keepdims=True))
+    return dict(rel_max=float((np.abs(a - b) / np.maximum(np.abs(b), rms)).max()),
+                normwise=float(np.linalg.norm(a - b) / np.linalg.norm(b)))
+
+
+def cpu_baseline(host, T, seconds, name, threads=None):
+    """The oracle as it is, on the host cores, timed on a bounded sample of
+    the same workload: whole steps for few-token workloads, else seeded
+    token subsets (the layer is token-separable), scaled to tokens/s."""
+    import numpy as np
+
     import oracle
 
-    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    full = T <= 64
+    if threads is not None:
+        prev = oracle.max_threads()
+        oracle.set_num_threads(threads)
+    cores = oracle.max_threads()
+    rng = np.random.default_rng(17)
     n = 0
     t0 = time.perf_counter()
     while True:
-        if hasattr(host, "scales16"):  # 16-block weight format
+        tok = None if full else rng.choice(T, size=min(16, T), replace=False).astype(np.int32)
+        nt = T if full else len(tok)
+        if name == "stack":
+            xin = host[0].x if tok is None else host[0].x[tok]
+            for h in host:
+                y, _, _ = oracle.moe_forward(xin, h.router_w, h.w_packed, h.scales, h.alpha, h.beta, h.k,
+                                             eps=h.eps)
+                xin = oracle.doubles_to_bf16(y)
+        elif hasattr(host, "scales16"):  # 16-block weight format
             oracle.moe_forward_nv(host.x[:T], host.router_w, host.w_packed, host.scales16, host.gscale,
-                                  host.alpha, host.beta, host.k, eps=host.eps)
+                                  host.alpha, host.beta, host.k, eps=host.eps, tokens=tok)
         elif hasattr(host, "wc"):  # latent-width variant
             oracle.latent_forward(host.x[:T], host.router_w, host.wc, host.w_packed, host.scales,
-                                  host.we, host.alpha, host.beta, host.k, eps=host.eps)
+                                  host.we, host.alpha, host.beta, host.k, eps=host.eps, tokens=tok)
+        elif hasattr(host, "g_pre"):  # the block with its stream norms
+            oracle.block_forward(host.x[:T], host.g_pre, host.router_w, host.w_packed, host.scales,
+                                 host.g_post, host.alpha, host.beta, host.k, eps=host.eps, tokens=tok)
         else:
             oracle.moe_forward(host.x[:T], host.router_w, host.w_packed, host.scales, host.alpha,
-                               host.beta, host.k, eps=host.eps)
-        n += 1
+                               host.beta, host.k, eps=host.eps, tokens=tok)
+        n += nt
         el = time.perf_counter() - t0
         if el >= seconds:
             break
-    return dict(value=n * T / el, unit="tokens/s", cores=cores, kind="oracle",
-                sample=f"{n} full steps of the workload ({n * T} tokens, weight set 0), {el:.1f} s")
+    if threads is not None:
+        oracle.set_num_threads(prev)
+    what = "whole steps" if full else "seeded 16-token subsets"
+    return dict(value=n / el, unit="tokens/s", cores=cores, kind="oracle",
+                sample=f"{n} tokens in {what} of the workload (weight set 0), {el:.1f} s")
+
+
+def measured_peaks(device):
+    """What this GPU reaches on plain library work, as context for the
+    fractions: a 2 GiB device copy (bytes read + written per second) and a
+    bf16 8192^3 matrix product (torch.matmul)."""
+    import torch
+
+    n = 2 << 30
+    a = torch.empty(n, dtype=torch.uint8, device=device)
+    b = torch.empty_like(a)
+    a.fill_(1)
+    for _ in range(2):
+        b.copy_(a)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_bps = 5 * 2 * n / (e0.elapsed_time(e1) * 1e-3)
+    del a, b
+    m = 8192
+    x = torch.randn(m, m, dtype=torch.bfloat16, device=device)
+    y = torch.randn(m, m, dtype=torch.bfloat16, device=device)
+    for _ in range(2):
+        torch.matmul(x, y)
+    e0.record()
+    for _ in range(5):
+        torch.matmul(x, y)
+    e1.record()
+    torch.cuda.synchronize()
+    gemm = 5 * 2 * m ** 3 / (e0.elapsed_time(e1) * 1e-3)
+    del x, y
+    torch.cuda.empty_cache()
+    return dict(copy_GBps=copy_bps / 1e9, bf16_gemm_TFLOPs=gemm / 1e12,
+                note="2 GiB torch device copy (read + write bytes); torch.matmul bf16 8192^3")
 
 
 def main():
@@ -407,21 +623,55 @@ def main():
         torch.cuda.synchronize()
         log(f"calibration copy: {n} bytes read, {n} bytes written")
         del src, dst
-    decode = args.workload.startswith("decode") or args.workload in DECODE_LIKE
-    steps = args.steps or (200 if decode else 20)
-    warmup = args.warmup if args.warmup is not None else (10 if decode else 3)
-    main_res, host, T = time_workload(args.workload, steps, warmup, device)
-    also = {}
-    for extra in [e for e in args.also.split(",") if e and e != args.workload]:
-        d2 = extra.startswith("decode") or extra in DECODE_LIKE
-        r, _, _ = time_workload(extra, 200 if d2 else 10, 10 if d2 else 2, device)
-        also[extra] = r
-        torch.cuda.empty_cache()
+
+    def run(name, steps=None, warmup=None):
+        d = name.startswith("decode") or name in DECODE_LIKE
+        st = steps or (200 if d else (5 if name == "stack" else 20))
+        wu = warmup if warmup is not None else (10 if d else 2)
+        if name == "stack":
+            return time_stack(st, wu, device) + (st, wu)
+        return time_workload(name, st, wu, device) + (st, wu)
+
+    main_res, host, T, steps, warmup = run(args.workload, args.steps, args.warmup)
     cpu = None
     if not args.no_cpu:
         log("timing the CPU oracle")
-        cpu = cpu_baseline(host, T, args.cpu_seconds)
-    s = host.w.expert_view().shape if args.workload in LATENT else host.shape
+        cpu = cpu_baseline(host, T, args.cpu_seconds, args.workload)
+    also = {}
+    hosts = {args.workload: (host, T)}
+    for extra in [e for e in args.also.split(",") if e and e != args.workload]:
+        r, h, t, _, _ = run(extra, None if extra != "stack" else 5)
+        if not args.no_cpu:
+            log(f"timing the CPU oracle on {extra}")
+            r["cpu_baseline"] = cpu_baseline(h, t, args.cpu_also_seconds, extra)
+        if extra in ("decode1", "decode4"):  # kept for the one-thread oracle runs
+            hosts.setdefault(extra, (h, t))
+        also[extra] = r
+        del h
+        torch.cuda.empty_cache()
+    single = None
+    if not args.no_cpu:
+        # the oracle on one host thread, for the tiny and the decode workloads
+        from mixture_experts_gemm_amd import synth
+        single = {"tiny": cpu_baseline(synth.make_layer("tiny"), 64, args.cpu_also_seconds, "tiny", threads=1)}
+        for name in ("decode1", "decode4"):
+            if name in hosts:
+                h, t = hosts[name]
+                single[name] = cpu_baseline(h, t, args.cpu_also_seconds, name, threads=1)
+    peaks = None if args.no_peaks else measured_peaks(device)
+    s = (host[0].shape if args.workload == "stack" else
+         host.w.expert_view().shape if args.workload in LATENT else host.shape)
+    roof = main_res["roofline"]
+    layer_bound = "hbm" if roof["bound"] == "hbm" else "mfma"
+    layer = dict(bound=layer_bound,
+                 frac=main_res["layer_hbm_frac"] if layer_bound == "hbm" else main_res["layer_mfma_frac"],
+                 note="the whole layer (all kernels, host launch gaps included) over ms_per_step: "
+                      "algorithmic bytes (hbm) or flops (mfma) at the same peak")
+    if peaks:
+        if roof["bound"] == "hbm":
+            roof["frac_of_measured_copy_rate"] = roof["achieved"] / peaks["copy_GBps"]
+        else:
+            roof["frac_of_measured_bf16_gemm_rate"] = roof["achieved"] / peaks["bf16_gemm_TFLOPs"]
     line = {
         "metric": METRIC,
         "value": main_res["tokens_per_s"],
@@ -433,20 +683,30 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "mxfp4 x bf16",
+        "dtype_note": ("MXFP4 weights (E2M1 + E8M0 per 32) times bf16 activations, fp32 accumulation; on the "
+                       "matrix cores the bf16 activations enter as exact block-scaled FP8 (two parts) or "
+                       "FP6 (three parts) splits"),
         "data": "synthetic",
         "config": {"workload": WORKLOAD_TEXT[args.workload], "T": T, "d": s.d, "E": s.E,
                    **({"D": host.w.D} if args.workload in LATENT else {}),
                    "k": s.k, "F": s.F,
                    "weights": ("E2M1 + E4M3 per 16 + fp32 per matrix" if args.workload in NV
                                else "MXFP4 (E2M1 + E8M0 per 32)"),
-                   "weight_sets": 4 if decode else 1,
-                   "distinct_experts_mean": main_res["distinct_experts_mean"]},
-        "roofline": {k: v for k, v in main_res["roofline"].items()
-                     if k in ("bound", "achieved", "peak", "unit", "frac", "traffic")},
-        "step_us_p10_p50_p90": main_res["step_us_p10_p50_p90"],
+                   "weight_sets": 4 if (args.workload.startswith("decode") or args.workload in DECODE_LIKE)
+                   else 1,
+                   "distinct_experts_mean": main_res.get("distinct_experts_mean")},
+        "roofline": {**{k: v for k, v in roof.items()
+                        if k in ("bound", "achieved", "peak", "unit", "frac", "traffic", "kernel",
+                                 "frac_of_measured_copy_rate", "frac_of_measured_bf16_gemm_rate",
+                                 "mx_issue")},
+                     "layer": layer},
+        "step_us_p10_p50_p90": main_res.get("step_us_p10_p50_p90"),
+        "bitwise_identical_3_reruns": main_res["bitwise_identical_3_reruns"],
         "cpu_baseline": cpu,
-        "also": {k: {kk: vv for kk, vv in v.items()} for k, v in also.items()},
+        "cpu_baseline_1_thread": single,
+        "measured_peaks": peaks,
+        "also": also,
     }
     print(json.dumps(line), flush=True)
 

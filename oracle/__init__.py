@@ -68,8 +68,22 @@ def lib():
         L.oracle_block_forward.restype = _I
         L.oracle_block_prenorm.argtypes = [_I, _I, C.c_double, _P, _P, _I, _P, _P]
         L.oracle_block_prenorm.restype = _I
+        L.oracle_set_num_threads.argtypes = [_I]
+        L.oracle_set_num_threads.restype = None
+        L.oracle_max_threads.argtypes = []
+        L.oracle_max_threads.restype = _I
         _lib = L
     return _lib
+
+
+def set_num_threads(n: int) -> None:
+    """Host threads of the oracle's parallel loops from now on."""
+    lib().oracle_set_num_threads(int(n))
+
+
+def max_threads() -> int:
+    """Host threads the oracle's parallel loops use."""
+    return int(lib().oracle_max_threads())
 
 
 def _p(a: np.ndarray):

@@ -56,9 +56,19 @@
  * loops only run independent rows/slots and write disjoint outputs.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+
+/* Threads the parallel loops below use from now on (n >= 1), and the
+ * current count; for timing the oracle on a given number of host cores. */
+void oracle_set_num_threads(int n)
+{
+    if (n >= 1) omp_set_num_threads(n);
+}
+
+int oracle_max_threads(void) { return omp_get_max_threads(); }
 
 /* ---- O1 / O6: number formats ------------------------------------------ */
 
