@@ -27,9 +27,9 @@
  *
  * All pointers passed to moe_layer_forward are DEVICE pointers on the
  * current HIP device unless stated otherwise; the caller allocates and owns
- * them, including the workspace.  The library allocates no device memory
- * (except moe_latent_forward's rocBLAS handle, see there), keeps no pointer
- * to the caller's buffers after returning, and queues all work asynchronously on
+ * them, including the workspace.  The library allocates no device memory,
+ * keeps no pointer to the caller's buffers after returning, and queues all
+ * work asynchronously on
  * `stream` (a hipStream_t; NULL = the null stream).  Buffers must stay valid
  * until that work completes.  Calls on distinct workspaces are independent.
  *
@@ -306,12 +306,10 @@ int moe_dequant_mxfp4(const uint8_t *codes, const uint8_t *scales, int64_t rows,
  *   stream, debug   as moe_layer_forward (debug copies and stage events
  *                   refer to the routing and expert stages)
  *
- * The two shared-matrix products run in rocBLAS (gemm_ex, bf16 operands,
- * fp32 accumulation).  Unlike moe_layer_forward this entry point therefore
- * allocates device memory once per device: the rocBLAS handle created at its
- * first call there, kept until the process ends.  Same status codes;
- * MOE_ERR_HIP also covers a rocBLAS failure.  Deterministic as
- * moe_layer_forward for a fixed rocBLAS solution choice.
+ * The two shared-matrix products run in the library's own kernels (bf16
+ * MFMA, fp32 accumulation: a weight-streaming kernel for T <= 8, LDS-tiled
+ * 256 x 256 tiles otherwise).  Allocates nothing; same status codes and
+ * determinism as moe_layer_forward.
  */
 typedef struct moe_latent_dims {
     int32_t T;   /* tokens in this call (0 = no-op)            */

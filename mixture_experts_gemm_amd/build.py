@@ -17,7 +17,6 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 SOURCES = ["api.hip", "route.hip", "expert.hip", "combine.hip", "weights.hip", "latent.hip"]
-ROCM_LIB = "/opt/rocm/lib"
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I", os.path.join(os.path.dirname(HERE), "include")]
@@ -43,8 +42,7 @@ def build(verbose: bool = False) -> str:
     with ThreadPoolExecutor(len(SOURCES)) as ex:
         list(ex.map(lambda a: _compile(a[0], a[1], verbose), zip(SOURCES, objs)))
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp,
-           "-L" + ROCM_LIB, "-lrocblas", "-Wl,-rpath," + ROCM_LIB]
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

@@ -137,57 +137,6 @@ __global__ __launch_bounds__(256) void f16_rows_kernel(const uint16_t *__restric
 
 // ---- small device helpers ---------------------------------------------------
 
-// Streaming loads of weight bytes: each is read once per layer call, so they
-// are marked non-temporal (no reuse expected in the caches).
-typedef unsigned int v4u_nt_t __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ uint4 ld_stream16(const void *p)
-{
-    const v4u_nt_t v = __builtin_nontemporal_load(reinterpret_cast<const v4u_nt_t *>(p));
-    return make_uint4(v.x, v.y, v.z, v.w);
-}
-__device__ __forceinline__ uint32_t ld_stream4(const uint32_t *p) { return __builtin_nontemporal_load(p); }
-
-
-// Contiguous per-XCD tile ranges (workgroup w runs on XCD w % 8, so
-// neighbouring tiles -- same rows, same expert -- share that XCD's L2);
-// returns false for surplus workgroups.
-__device__ __forceinline__ bool xcd_tile(int total, int &idx)
-{
-    const int per = (total + 7) >> 3;
-    const int local = (int)(blockIdx.x >> 3);
-    if (local >= per) return false;
-    idx = (int)(blockIdx.x & 7) * per + local;
-    return idx < total;
-}
-
-// LDS byte offset of a __shared__ object.
-__device__ __forceinline__ uint32_t lds_off(const void *p)
-{
-    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void *)p;
-}
-
-// Direct-to-LDS loads.  Issued from inline asm so the compiler does not
-// guard later LDS reads with a blanket vmcnt(0) (it cannot tell the ring
-// stages apart); every wait on these loads is the explicit one in
-// chunk_sync().  lds (wave-uniform) is the byte offset the lane-0 data lands
-// at; lane i's data lands at lds + i*size.  The load takes its LDS base from
-// M0, which the compiler reserves: its value is saved in an SGPR and put
-// back inside the same statement, so M0 is unchanged across it.
-__device__ __forceinline__ void dma16(const void *g, uint32_t lds)
-{
-    uint32_t saved;
-    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
-                 "global_load_lds_dwordx4 %2, off\n\ts_mov_b32 m0, %0"
-                 : "=&s"(saved) : "s"(lds), "v"(g) : "memory");
-}
-__device__ __forceinline__ void dma4(const void *g, uint32_t lds)
-{
-    uint32_t saved;
-    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
-                 "global_load_lds_dword %2, off\n\ts_mov_b32 m0, %0"
-                 : "=&s"(saved) : "s"(lds), "v"(g) : "memory");
-}
-
 // Wait until at most N of this wave's loads are outstanding, then barrier.
 template <int N>
 __device__ __forceinline__ void chunk_sync()

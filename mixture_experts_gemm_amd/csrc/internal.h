@@ -177,7 +177,7 @@ hipError_t launch_postnorm_gate(const uint16_t *x, const float *y, const float *
 // gate/up kernel's input when the router does not split x itself).
 hipError_t launch_split_x_fp8(const Shape &s, const Workspace &ws, const uint16_t *x, hipStream_t st);
 // c[T][N] = a[T][K] w[N][K]^T, bf16 operands, fp32 accumulation, c bf16 or
-// fp32 (rocBLAS gemm_ex).
+// fp32, on the bf16 MFMA (the latent-width variant's shared matrices).
 hipError_t launch_dense(const uint16_t *a, const uint16_t *w, void *c, bool c_fp32, int T, int N,
                         int K, hipStream_t st);
 // s_out = bf16(alpha * x + beta * f), x bf16 [T][D], f fp32 [T][D].

@@ -6,43 +6,258 @@
 // widens their weighted sum after them; section ③: the widened sum joins
 // the residual through the per-dimension gate s <- alpha*s + beta*(.).
 //
-// The products are plain dense GEMMs (bf16 operands, fp32 accumulation) and
-// run in rocBLAS; the gate is an elementwise pass here.
-#include <mutex>
-
-#include <rocblas/rocblas.h>
-
+// Both products are C[T][N] = A[T][K] W[N][K]^T with bf16 A and W (K
+// contiguous in both), fp32 accumulation on the bf16 MFMA, and C bf16 (the
+// narrowed token z, rounded to nearest even) or fp32 (the widened sum f).
+// Few tokens: each matrix row is read once from HBM, so the product is a
+// weight stream (dense_stream_kernel).  Many tokens: 256 x 256 output tiles
+// staged through LDS (dense_gemm_kernel).
 #include "device.h"
 #include "internal.h"
+#include "layout.h"
 
 namespace moe {
 
-// One rocBLAS handle per device, created at first use and kept until the
-// process ends.  The stream is set under the lock for each call, so calls
-// from several threads cannot interleave a stream change with a launch.
-static std::mutex g_blas_mu;
-static rocblas_handle g_blas[64];
+// ---- few tokens: the weight stream ---------------------------------------------
+// One workgroup per 16 rows of W (16 output columns), all T <= 8 tokens.
+// The NW waves (4, or 8 when K >= 8192) take equal parts of K in 128-wide
+// chunks.  Each load instruction
+// reads 8 rows x 128 contiguous bytes (whole cache lines): lane l takes row
+// 8o + l%8 of the octet o and the 8 K values 64h + 8(l/8) .. +7 of the
+// chunk's half h.  A fragments follow the same lane map (token l%8, same 8
+// K values), so one 16x16x32 MFMA per (half, octet) pairs A lane m + 16g
+// with B lane n + 16g on equal K values wherever m and n are both below 8
+// (K groups 2g) or both at least 8 (K groups 2g+1): C[t][j] + C[t+8][j+8]
+// is token t times row 8o + j over the whole half, and the off-diagonal
+// blocks are discarded.  Two batches of kDenseU chunks are in flight while
+// one is multiplied.  A is copied to LDS by direct-to-LDS loads issued
+// between the first two weight batches and waited for once (16-byte unit u
+// of row m at u ^ (m & 7): the 8 tokens' reads at one K offset fall on
+// distinct banks); tokens >= T enter as zeros.  The waves' partial sums meet
+// in LDS in a fixed order.  Needs K a multiple of 512 * NW (the A copy) and
+// at least 1024 * NW (every wave then runs two or more whole batches).  HBM bound:
+// N*K*2 bytes of W per launch.
+constexpr int kDenseStreamMaxT = 8;
+constexpr int kDenseU = 4;
+
+template <bool OUT_F32, int NW>
+__global__ __launch_bounds__(64 * NW) void dense_stream_kernel(const uint16_t *__restrict__ A,
+                                                               const uint16_t *__restrict__ W, void *C,
+                                                               int T, int N, int K)
+{
+    extern __shared__ uint4 as4[];  // [T][K/8] swizzled units
+    __shared__ floatx4_t red[NW - 1][2][64];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int r8 = lane & 7, kg = lane >> 3;  // row in the octet / token; K group of 8
+    const int row0 = blockIdx.x * 16;
+    const int nc = K / kKStep;
+    const int c0 = wv * nc / NW, c1 = (wv + 1) * nc / NW;
+    // loads (half h, octet o) of chunk c: W[row0 + 8o + r8][128c + 64h + 8kg .. +7]
+    const uint16_t *wp = W + (int64_t)(row0 + r8) * K + 8 * kg;
+    const int64_t oct = (int64_t)8 * K;
+    uint4 b0[kDenseU][4], b1[kDenseU][4];  // [chunk][2h + o]
+    auto load = [&](uint4 (&b)[kDenseU][4], int c) {
+#pragma unroll
+        for (int u = 0; u < kDenseU; ++u)
+            if (c + u < c1) {
+                const uint16_t *p = wp + (int64_t)(c + u) * kKStep;
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int o = 0; o < 2; ++o) b[u][2 * h + o] = ld_stream16(p + o * oct + 64 * h);
+            }
+    };
+    load(b0, c0);
+    // A: LDS unit P = 64 * (NW j + wv) + lane holds logical unit (P % ku) ^ (m & 7)
+    // of row m = P / ku (ku = K/8 is a multiple of 64, so a wave's 64 units
+    // lie in one row)
+    const int ku = K / 8;
+    const int wvu = __builtin_amdgcn_readfirstlane(wv);
+    for (int j = 0; j < T * ku / (64 * NW); ++j) {
+        const int P0 = 64 * (NW * j + wvu);
+        const int m = P0 / ku, cu = P0 - m * ku + lane;
+        dma16(A + (int64_t)m * K + (cu ^ (m & 7)) * 8, lds_off(as4 + P0));
+    }
+    load(b1, c0 + kDenseU);
+    // A and the first batch have landed once at most the second batch's
+    // kDenseU * 4 loads are outstanding
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" :: "n"(kDenseU * 4) : "memory");
+    floatx4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    const bool arow = r8 < T;
+    auto consume = [&](const uint4 (&b)[kDenseU][4], int c) {
+#pragma unroll
+        for (int u = 0; u < kDenseU; ++u)
+            if (c + u < c1) {
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int unit = 16 * (c + u) + 8 * h + kg;
+                    const uint4 a = arow ? as4[r8 * ku + (unit ^ r8)] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+                    for (int o = 0; o < 2; ++o) acc[o] = mfma16(as_bf16x8(a), as_bf16x8(b[u][2 * h + o]), acc[o]);
+                }
+            }
+    };
+    for (int c = c0; c < c1; c += 2 * kDenseU) {
+        consume(b0, c);
+        if (c + 2 * kDenseU < c1) load(b0, c + 2 * kDenseU);
+        if (c + kDenseU < c1) {
+            consume(b1, c + kDenseU);
+            if (c + 3 * kDenseU < c1) load(b1, c + 3 * kDenseU);
+        }
+    }
+    // the two diagonal blocks: lane L (L % 16 < 8, L < 32) adds lane L + 40
+    // and then holds token 4(L/16) + r, row 8o + L%16
+#pragma unroll
+    for (int o = 0; o < 2; ++o)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[o][r] += __shfl_down(acc[o][r], 40);
+    if (wv > 0) {
+        red[wv - 1][0][lane] = acc[0];
+        red[wv - 1][1][lane] = acc[1];
+    }
+    __syncthreads();
+    if (wv != 0 || (lane & 15) >= 8 || lane >= 32) return;
+#pragma unroll
+    for (int o = 0; o < 2; ++o) {
+        floatx4_t v = acc[o];
+#pragma unroll
+        for (int w = 0; w < NW - 1; ++w) v += red[w][o][lane];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = 4 * (lane >> 4) + r;
+            if (t < T) {
+                const int64_t idx = (int64_t)t * N + row0 + 8 * o + (lane & 7);
+                if constexpr (OUT_F32) static_cast<float *>(C)[idx] = v[r];
+                else static_cast<uint16_t *>(C)[idx] = f32_to_bf16(v[r]);
+            }
+        }
+    }
+}
+
+// ---- many tokens: LDS-tiled bf16 MFMA GEMM ----------------------------------------
+// 256 tokens x 256 output columns per workgroup, K in steps of 32, a
+// four-stage LDS ring filled by direct-to-LDS loads (each stage 256 A rows
+// and 256 W rows of 64 bytes; 16-byte slot q of row r at q ^ ((r >> 1) & 3),
+// so the fragment reads of 16 consecutive rows fall on distinct banks).  8
+// waves as 2 (tokens) x 4 (columns), 128 x 64 each: 8 x 4 blocks of 16 x 16,
+// 32 MFMAs per K step.  Token rows past T are loaded as row T-1 and never
+// stored.  Tiles are spread over the XCDs in contiguous ranges, row-major,
+// so the workgroups sharing an A row panel run on one XCD.  MFMA bound:
+// 2*T*N*K flops.
+constexpr int kGemmTile = 256;
+constexpr int kGemmStages = 4;
+
+template <bool OUT_F32>
+__global__ __launch_bounds__(512) void dense_gemm_kernel(const uint16_t *__restrict__ A,
+                                                         const uint16_t *__restrict__ W, void *C,
+                                                         int T, int N, int K, int tiles_m, int tiles_n)
+{
+    constexpr int AU = kGemmTile * 4, BU = kGemmTile * 4;  // 16-byte units per stage
+    constexpr int NL = (AU + BU) / 512;                    // loads per thread per stage (4)
+    __shared__ uint4 As[kGemmStages][AU];
+    __shared__ uint4 Bs[kGemmStages][BU];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    int tile;
+    if (!xcd_tile(tiles_m * tiles_n, tile)) return;
+    const int tm = tile / tiles_n, tn = tile - tm * tiles_n;
+    const int M0 = tm * kGemmTile, N0 = tn * kGemmTile;
+    const int nk = K / 32;
+    // load j of this thread: stage unit u = 512 j + tid (A units first)
+    const uint16_t *src[NL];
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+        const int u = 512 * j + tid;
+        const int v = u < AU ? u : u - AU;
+        const int r = v >> 2, q = (v & 3) ^ ((r >> 1) & 3);
+        src[j] = u < AU ? A + (int64_t)min(M0 + r, T - 1) * K + q * 8
+                        : W + (int64_t)(N0 + r) * K + q * 8;
+    }
+    const int wvu = __builtin_amdgcn_readfirstlane(wv);
+    auto issue = [&](int kc) {
+        const int b = kc % kGemmStages;
+#pragma unroll
+        for (int j = 0; j < NL; ++j) {
+            const int u0 = 512 * j + 64 * wvu;  // unit of lane 0
+            const uint32_t dst = u0 < AU ? lds_off(&As[b][u0]) : lds_off(&Bs[b][u0 - AU]);
+            dma16(src[j] + kc * 32, dst);
+        }
+    };
+    const int wm = wv & 1, wn = wv >> 1;
+    const int m16 = lane & 15, g = lane >> 4;
+    floatx4_t acc[8][4];
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+
+    for (int s = 0; s < kGemmStages - 1 && s < nk; ++s) issue(s);
+    for (int kc = 0; kc < nk; ++kc) {
+        // stage kc complete; the stages issued after it may stay in flight
+        const int ahead = min(kGemmStages - 2, nk - 1 - kc);
+        if (ahead >= 2) asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(2 * NL) : "memory");
+        else if (ahead == 1) asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(NL) : "memory");
+        else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        // the slot refilled now was last read in step kc-1, before the barrier
+        if (kc + kGemmStages - 1 < nk) issue(kc + kGemmStages - 1);
+        const uint4 *Ab = As[kc % kGemmStages];
+        const uint4 *Bb = Bs[kc % kGemmStages];
+        uint4 bw[4], a[8];
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+            const int r = wn * 64 + nb * 16 + m16;
+            bw[nb] = Bb[r * 4 + (g ^ ((r >> 1) & 3))];
+        }
+#pragma unroll
+        for (int mb = 0; mb < 8; ++mb) {
+            const int r = wm * 128 + mb * 16 + m16;
+            a[mb] = Ab[r * 4 + (g ^ ((r >> 1) & 3))];
+        }
+#pragma unroll
+        for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = mfma16(as_bf16x8(a[mb]), as_bf16x8(bw[nb]), acc[mb][nb]);
+    }
+    // lane holds C[token g*4 + r][column m16] of every 16 x 16 block
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = M0 + wm * 128 + mb * 16 + g * 4 + r;
+            if (t >= T) continue;
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) {
+                const int64_t o = (int64_t)t * N + N0 + wn * 64 + nb * 16 + m16;
+                if constexpr (OUT_F32) static_cast<float *>(C)[o] = acc[mb][nb][r];
+                else static_cast<uint16_t *>(C)[o] = f32_to_bf16(acc[mb][nb][r]);
+            }
+        }
+}
 
 hipError_t launch_dense(const uint16_t *a, const uint16_t *w, void *c, bool c_fp32, int T, int N,
                         int K, hipStream_t st)
 {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-    std::lock_guard<std::mutex> lock(g_blas_mu);
-    if (!g_blas[dev] && rocblas_create_handle(&g_blas[dev]) != rocblas_status_success) {
-        g_blas[dev] = nullptr;
-        return hipErrorUnknown;
+    if (T <= 0) return hipSuccess;
+    // few tokens with their rows in LDS (at most 128 KB): the weight stream
+    const size_t lds = (size_t)T * K * 2;
+    // the A copy needs T*K/8 divisible by 64 * NW for any T: K % (512 * NW) == 0
+    if (T <= kDenseStreamMaxT && lds <= 128 * 1024 && N % 16 == 0 && K % 2048 == 0 && K >= 4096) {
+        if (K % 4096 == 0 && K >= 8192) {  // 8 waves
+            if (c_fp32) dense_stream_kernel<true, 8><<<N / 16, 512, lds, st>>>(a, w, c, T, N, K);
+            else dense_stream_kernel<false, 8><<<N / 16, 512, lds, st>>>(a, w, c, T, N, K);
+        } else {
+            if (c_fp32) dense_stream_kernel<true, 4><<<N / 16, 256, lds, st>>>(a, w, c, T, N, K);
+            else dense_stream_kernel<false, 4><<<N / 16, 256, lds, st>>>(a, w, c, T, N, K);
+        }
+        return hipGetLastError();
     }
-    rocblas_handle h = g_blas[dev];
-    if (rocblas_set_stream(h, st) != rocblas_status_success) return hipErrorUnknown;
-    // column-major view: C^T [N][T] = W [N][K] (stored K-major, so op = T) x A^T [K][T]
-    const float one = 1.0f, zero = 0.0f;
-    const rocblas_datatype ct = c_fp32 ? rocblas_datatype_f32_r : rocblas_datatype_bf16_r;
-    const rocblas_status r = rocblas_gemm_ex(
-        h, rocblas_operation_transpose, rocblas_operation_none, N, T, K, &one, w,
-        rocblas_datatype_bf16_r, K, a, rocblas_datatype_bf16_r, K, &zero, c, ct, N, c, ct, N,
-        rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0, 0);
-    return r == rocblas_status_success ? hipSuccess : hipErrorUnknown;
+    if (N % kGemmTile != 0 || K % 32 != 0) return hipErrorInvalidValue;
+    const int tiles_m = (T + kGemmTile - 1) / kGemmTile, tiles_n = N / kGemmTile;
+    const int64_t grid = 8 * (((int64_t)tiles_m * tiles_n + 7) / 8);
+    if (c_fp32)
+        dense_gemm_kernel<true><<<(unsigned)grid, 512, 0, st>>>(a, w, c, T, N, K, tiles_m, tiles_n);
+    else
+        dense_gemm_kernel<false><<<(unsigned)grid, 512, 0, st>>>(a, w, c, T, N, K, tiles_m, tiles_n);
+    return hipGetLastError();
 }
 
 // 8 columns per thread: x (16 B), f (32 B), alpha, beta (32 B each) in,

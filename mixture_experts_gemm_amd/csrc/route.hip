@@ -20,12 +20,6 @@
 
 namespace moe {
 
-// LDS byte address of a __shared__ object.
-__device__ __forceinline__ uint32_t lds_addr(const void *p)
-{
-    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void *)p;
-}
-
 // ---------------------------------------------------------------------------
 // Router scores, few tokens: one workgroup per expert streams that expert's
 // fp32 router row; all tokens are accumulated in registers and reduced once.
@@ -139,16 +133,7 @@ __device__ __forceinline__ void split3_trunc(const float4 &a, const float4 &b, u
 // every wave that needs it (16-byte slot q of an x row r at
 // q ^ ((r >> 1) & 3), of a router row at q ^ (r & 7): the fragment reads of
 // 16 consecutive rows then fall on distinct banks).  WE waves along the
-// experts, 4/WE along the tokens.  The load takes its LDS base from M0,
-// which is saved and restored inside the asm statement.
-__device__ __forceinline__ void rdma16(const void *g, uint32_t lds)
-{
-    uint32_t saved;
-    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
-                 "global_load_lds_dwordx4 %2, off\n\ts_mov_b32 m0, %0"
-                 : "=&s"(saved) : "s"(lds), "v"(g) : "memory");
-}
-
+// experts, 4/WE along the tokens.
 template <int WE>
 __global__ __launch_bounds__(256) void router_gemm_lds_kernel(const uint16_t *__restrict__ x,
                                                               const float *__restrict__ wr,
@@ -187,9 +172,9 @@ __global__ __launch_bounds__(256) void router_gemm_lds_kernel(const uint16_t *__
         const int b = kc % 3;
 #pragma unroll
         for (int j = 0; j < NL; ++j) {
-            const uint32_t base = isx[j] ? lds_addr(&Xs[b][dst[j]]) : lds_addr(&Ws[b][dst[j] - XU]);
+            const uint32_t base = isx[j] ? lds_off(&Xs[b][dst[j]]) : lds_off(&Ws[b][dst[j] - XU]);
             const int64_t off = isx[j] ? (int64_t)kc * 64 : (int64_t)kc * 128;
-            rdma16(static_cast<const uint8_t *>(src[j]) + off,
+            dma16(static_cast<const uint8_t *>(src[j]) + off,
                    __builtin_amdgcn_readfirstlane(base));
         }
     };
