@@ -264,10 +264,12 @@ hipError_t launch_router(const Shape &s, const Plan &p, const Workspace &ws, con
 // order-preserving as an unsigned integer in the high word (-0 counted as +0,
 // NaN as -inf) and ~id in the low word, so a comparison is one 64-bit max.
 // Each lane keeps SLOTS keys (experts lane + 64*q) sorted best first; each of
-// the k rounds takes the wave's largest head (butterfly DPP steps inside rows
-// of 16 lanes, then row_bcast15/31 across rows; the maximum lands in lane 63)
-// and the owning lane pops it.  The j-th choice is parked in lane j%64, slot
-// j/64; the softmax over the chosen scores is one wave sum.
+// the k rounds takes the wave's largest head (a 32-bit max over the score
+// words by DPP steps inside rows of 16 lanes, then row_bcast15/31 across
+// rows, the maximum landing in lane 63; ties of the score word, rare, are
+// settled by a second max over the id words) and the owning lane pops it.
+// The j-th choice is parked in lane j%64, slot j/64; the softmax over the
+// chosen scores is one wave sum.
 // ---------------------------------------------------------------------------
 constexpr int kNone = 0x7FFFFFFF;
 
@@ -288,31 +290,42 @@ __device__ __forceinline__ float key_score(uint64_t key)
 
 __device__ __forceinline__ int key_id(uint64_t key) { return (int)(0xFFFFFFFFu - (uint32_t)key); }
 
-// max of key and the key DPP control C brings from another lane (rows outside
-// ROW_MASK keep their own key)
+// max of a 32-bit value over the wave, in every lane: max steps within rows
+// of 16 lanes (quad_perm, half_mirror, mirror), then row_bcast15 / 31 (the
+// maximum lands in lane 63), read back from lane 63
 template <int C, int ROW_MASK>
-__device__ __forceinline__ uint64_t key_max_step(uint64_t key)
+__device__ __forceinline__ uint32_t u32_max_step(uint32_t v)
 {
-    const int lo = (int)(uint32_t)key, hi = (int)(uint32_t)(key >> 32);
-    const uint32_t olo = (uint32_t)__builtin_amdgcn_update_dpp(lo, lo, C, ROW_MASK, 0xF, false);
-    const uint32_t ohi = (uint32_t)__builtin_amdgcn_update_dpp(hi, hi, C, ROW_MASK, 0xF, false);
-    const uint64_t o = ((uint64_t)ohi << 32) | olo;
-    return o > key ? o : key;
+    const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, C, ROW_MASK, 0xF, false);
+    return o > v ? o : v;
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
+{
+    v = u32_max_step<0xB1, 0xF>(v);
+    v = u32_max_step<0x4E, 0xF>(v);
+    v = u32_max_step<0x141, 0xF>(v);
+    v = u32_max_step<0x140, 0xF>(v);
+    v = u32_max_step<0x142, 0xA>(v);
+    v = u32_max_step<0x143, 0xC>(v);
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
-// the wave's largest key, in every lane
-__device__ __forceinline__ uint64_t wave_max_key(uint64_t key)
+// The wave's largest key, in every lane, as a 32-bit max over the high
+// words (the order-preserving score) and, only when several lanes hold that
+// score, a second one over their low words (~id: the lowest id wins): the
+// same result as a 64-bit max, in about half the dependent steps.
+__device__ __forceinline__ uint64_t wave_max_key_split(uint64_t key)
 {
-    key = key_max_step<0xB1, 0xF>(key);   // quad_perm [1,0,3,2]
-    key = key_max_step<0x4E, 0xF>(key);   // quad_perm [2,3,0,1]
-    key = key_max_step<0x141, 0xF>(key);  // row_half_mirror
-    key = key_max_step<0x140, 0xF>(key);  // row_mirror: every lane holds its row's max
-    key = key_max_step<0x142, 0xA>(key);  // row_bcast15: rows 1, 3 take rows 0, 2
-    key = key_max_step<0x143, 0xC>(key);  // row_bcast31: rows 2, 3 take row 1
-    const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)key, 63);
-    const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(key >> 32), 63);
-    return ((uint64_t)hi << 32) | lo;
+    const uint32_t hi = (uint32_t)(key >> 32), lo = (uint32_t)key;
+    const uint32_t mh = wave_max_u32(hi);
+    const bool tie = hi == mh;
+    const uint64_t ties = __ballot(tie);
+    uint32_t ml;
+    if (__popcll(ties) == 1) ml = (uint32_t)__builtin_amdgcn_readlane((int)lo, (int)__ffsll((long long)ties) - 1);
+    else ml = wave_max_u32(tie ? lo : 0u);
+    return ((uint64_t)mh << 32) | ml;
 }
+
 
 // l: the token's scores, or its first partial-score plane when the router
 // split its sums over nsplit slices of d (planes `stride` floats apart,
@@ -356,7 +369,7 @@ __device__ void topk_row(const float *__restrict__ l, int E, int k, int32_t *__r
     for (int q = 0; q < SLOTS; ++q) mine[q] = none;
     uint64_t top = none;
     for (int j = 0; j < k; ++j) {
-        const uint64_t best = wave_max_key(key[0]);
+        const uint64_t best = wave_max_key_split(key[0]);
         if (key[0] == best) {  // keys are distinct: exactly the owner lane
 #pragma unroll
             for (int q = 0; q + 1 < SLOTS; ++q) key[q] = key[q + 1];
@@ -403,37 +416,54 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ sco
 }
 
 // ---------------------------------------------------------------------------
-// Block-wide exclusive prefix sum of a[0..n), n <= 1024, in LDS, by 256
-// threads; returns the total.  Integer, so order-free.
+// Block-wide exclusive prefix sums of a[0..n) and b[0..n) together, n <= 1024,
+// in LDS, by 256 threads (one pass, two barriers); returns both totals.
+// Integer, so order-free.
 // ---------------------------------------------------------------------------
-__device__ int block_exclusive_scan(int32_t *a, int n, int32_t *wtot)
+__device__ int2 block_exclusive_scan2(int32_t *a, int32_t *b, int n, int32_t (*wtot)[4])
 {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    int v[4];
-    int sum = 0;
+    int va[4], vb[4];
+    int sa = 0, sb = 0;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int i = tid * 4 + q;
-        v[q] = i < n ? a[i] : 0;
-        sum += v[q];
+        va[q] = i < n ? a[i] : 0;
+        vb[q] = i < n ? b[i] : 0;
+        sa += va[q];
+        sb += vb[q];
     }
-    int incl = sum;
+    int ia = sa, ib = sb;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(incl, off);
-        if (lane >= off) incl += y;
+        const int ya = __shfl_up(ia, off), yb = __shfl_up(ib, off);
+        if (lane >= off) {
+            ia += ya;
+            ib += yb;
+        }
     }
-    if (lane == 63) wtot[wv] = incl;
+    if (lane == 63) {
+        wtot[0][wv] = ia;
+        wtot[1][wv] = ib;
+    }
     __syncthreads();
-    int base = 0;
-    for (int w = 0; w < wv; ++w) base += wtot[w];
-    const int total = wtot[0] + wtot[1] + wtot[2] + wtot[3];
-    int run = base + incl - sum;
+    int basea = 0, baseb = 0;
+    for (int w = 0; w < wv; ++w) {
+        basea += wtot[0][w];
+        baseb += wtot[1][w];
+    }
+    const int2 total = make_int2(wtot[0][0] + wtot[0][1] + wtot[0][2] + wtot[0][3],
+                                 wtot[1][0] + wtot[1][1] + wtot[1][2] + wtot[1][3]);
+    int ra = basea + ia - sa, rb = baseb + ib - sb;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int i = tid * 4 + q;
-        if (i < n) a[i] = run;
-        run += v[q];
+        if (i < n) {
+            a[i] = ra;
+            b[i] = rb;
+        }
+        ra += va[q];
+        rb += vb[q];
     }
     __syncthreads();
     return total;
@@ -441,7 +471,7 @@ __device__ int block_exclusive_scan(int32_t *a, int n, int32_t *wtot)
 
 // offsets / counts / tile list from per-expert counts cnt[] (LDS, E entries);
 // cnt is replaced by the exclusive offsets.
-__device__ void finish_offsets(int32_t *cnt, int32_t *toff, int32_t *wtot, int E, int tile_rows,
+__device__ void finish_offsets(int32_t *cnt, int32_t *toff, int32_t (*wtot)[4], int E, int tile_rows,
                                int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
                                Tile *__restrict__ tiles, int32_t *__restrict__ ntiles, int *c_out)
 {
@@ -451,8 +481,8 @@ __device__ void finish_offsets(int32_t *cnt, int32_t *toff, int32_t *wtot, int E
         toff[e] = (cnt[e] + tile_rows - 1) / tile_rows;
     }
     __syncthreads();
-    const int total = block_exclusive_scan(cnt, E, wtot);
-    const int ntot = block_exclusive_scan(toff, E, wtot);
+    const int2 tot = block_exclusive_scan2(cnt, toff, E, wtot);
+    const int total = tot.x, ntot = tot.y;
     if (tid == 0) {
         offsets[E] = total;
         *ntiles = ntot;
@@ -498,7 +528,7 @@ __global__ __launch_bounds__(256) void route_small_kernel(
     __shared__ int32_t sid[4096];
     __shared__ int32_t cnt[1024];
     __shared__ int32_t toff[1024];
-    __shared__ int32_t wtot[4];
+    __shared__ int32_t wtot[2][4];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int S = T * k;
     for (int e = tid; e < E; e += 256) mask[e] = 0ull;
@@ -548,7 +578,7 @@ __global__ __launch_bounds__(256) void group_scan_kernel(
 {
     __shared__ int32_t cnt[1024];
     __shared__ int32_t toff[1024];
-    __shared__ int32_t wtot[4];
+    __shared__ int32_t wtot[2][4];
     // two passes over the masks (counts, then bases); loads go out in batches
     // of 64 (all chunks of a 4096-token call at once), so each pass is one
     // round trip to memory per batch rather than a chain of dependent reads

@@ -195,6 +195,32 @@ def test_few_tokens_hot_expert(T, d):
     _check_tokens(L, out, np.arange(T), f"hot T={T} d={d}")
 
 
+@pytest.mark.parametrize("E,pair", [(16, (3, 5)), (256, (7, 135)), (256, (9, 73))])
+def test_exact_score_ties(E, pair):
+    """Two experts with the same router row score every token identically;
+    bias channel 0 puts them far above the rest, so they are the top 2 and
+    the lower id must come first (the oracle's order).  (7, 135): different
+    lanes of the top-k wave; (9, 73): the same lane (experts lane + 64 q)."""
+    w = synth.custom_workload(T=20, d=256, E=E, k=2, F=256, seed=24 + E, zipf=True)
+    wr = synth.make_router(w)
+    wr[:, 0] = 0.0
+    a, b = pair
+    wr[b] = wr[a]
+    wr[a, 0] = wr[b, 0] = 50.0
+    x = synth.make_tokens(w, wr, gap=0)
+    sc = oracle.router_scores(x, wr).astype(np.float64)
+    top = -np.sort(-sc, axis=1)[:, :3]
+    assert np.all(top[:, 0] == top[:, 1]) and np.all(top[:, 1] - top[:, 2] > 1.0)
+    W, S = synth.make_experts(w)
+    al, be = synth.make_gates(w)
+    L = synth.LayerInputs(w.shape, x, wr, W, S, al, be, w.shape.k)
+    _say("exact ties", E, pair)
+    out, dbg = run_layer(L)
+    r = _check_routing(L, dbg, f"ties {pair}")
+    assert np.all(r["ids"] == np.array(pair))
+    _check_tokens(L, out, np.arange(20), f"ties {pair}")
+
+
 # ------------------------------------------------------------------ invariants
 
 def test_gate_identity_bitwise():
