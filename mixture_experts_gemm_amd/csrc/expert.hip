@@ -996,12 +996,18 @@ __global__ __launch_bounds__(512) void gemm_nv_kernel(const NvArgs pa)
 
     // ---- load assignment ----------------------------------------------------
     // A: load i of this wave fills units 64*(NW*i + wv) + lane: row
-    // 4*(NW*i + wv) + lane/16, stored slot lane%16 = global slot ^ (row & 7)
+    // 4*(NW*i + wv) + lane/16, stored slot lane%16 = global slot ^ (row & 7).
+    // Rows past nrows are not loaded (their LDS rows hold stale data and only
+    // feed output rows that are never stored); every wait below is vmcnt(0),
+    // so loads skipped this way cannot upset a count.
+    static_assert(AL == 6 && BL == 2, "the load parts below assume 6 + 2 loads a wave");
     const uint16_t *asrc[AL];
+    bool aload[AL];
 #pragma unroll
     for (int i = 0; i < AL; ++i) {
         const int r = 4 * (NW * i + wv) + (lane >> 4);
         const int q = (lane & 15) ^ (r & 7);
+        aload[i] = r < tl.nrows;
         asrc[i] = pa.a + src_row(r) * K + q * 8;
     }
     const WView v = GATE_UP ? w1_codes(pa.wpk, tl.expert, d, F) : w2_codes(pa.wpk, tl.expert, d, F);
@@ -1011,14 +1017,22 @@ __global__ __launch_bounds__(512) void gemm_nv_kernel(const NvArgs pa)
     const uint8_t *ssrc = vs.stile(nt, 0) + tid * 4;
     const int nk = K / kKStep;
     const int wvu = __builtin_amdgcn_readfirstlane(wv);
-    auto issue = [&](int kc) {
-        const int b = kc % ST;
+    // The loads of a chunk go out in three parts spread over the multiply of
+    // the chunk before (two halves of the activation rows, then the code and
+    // scale tiles), so a wave is not held at the address unit while its
+    // MFMAs could be issuing.
+    auto issue_part = [&](int part, int kc, int b) {
+        if (part < 2) {
 #pragma unroll
-        for (int i = 0; i < AL; ++i) dma16(asrc[i] + kc * kKStep, lds_off(&As[b][(NW * i + wvu) * 64]));
+            for (int i = 3 * part; i < 3 * part + 3; ++i)
+                if (aload[i]) dma16(asrc[i] + kc * kKStep, lds_off(&As[b][(NW * i + wvu) * 64]));
+        } else {
 #pragma unroll
-        for (int i = 0; i < BL; ++i)
-            dma16(bsrc + (int64_t)kc * kWTileBytes + i * NW * 1024, lds_off(&Bs[b][(NW * i + wvu) * 64]));
-        dma4(ssrc + (int64_t)kc * kNvTileScaleBytes, lds_off(&Ss[b][64 * wvu]));
+            for (int i = 0; i < BL; ++i)
+                dma16(bsrc + (int64_t)kc * kWTileBytes + i * NW * 1024,
+                      lds_off(&Bs[b][(NW * i + wvu) * 64]));
+            dma4(ssrc + (int64_t)kc * kNvTileScaleBytes, lds_off(&Ss[b][64 * wvu]));
+        }
     };
 
     // ---- compute assignment -------------------------------------------------
@@ -1043,50 +1057,96 @@ __global__ __launch_bounds__(512) void gemm_nv_kernel(const NvArgs pa)
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
-    auto compute = [&](int b, auto full) {
-        constexpr bool F_ = decltype(full)::value;
+    // Multiply the chunk in stage b with NA active row blocks (a wave's count
+    // is fixed for the tile, so each count is its own unrolled loop with no
+    // branch between MFMAs).  K step st+1's activation fragments are read and
+    // its weights widened while step st's MFMAs run.  When kn >= 0 the parts
+    // of chunk kn's loads (into the other stage) are issued along the way.
+    auto compute = [&](int b, int kn, auto na) {
+        constexpr int NA = decltype(na)::value;
         const uint4 *A = As[b];
         const uint4 *B = Bs[b];
         const uint16_t *S = reinterpret_cast<const uint16_t *>(Ss[b]);
-        f16x8_t bh[4][4];
+        uint4 bw[4];
+        E4m3Parts sp[4][2];
+        f16x8_t bcur[4], bnxt[4];
+        f16x8_t acur[NA > 0 ? NA : 1], anxt[NA > 0 ? NA : 1];
+        auto read_a = [&](int st, f16x8_t *a) {
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-            const uint4 bw = B[rho[nb] * 4 + (g ^ bswz(rho[nb]))];
-            const uint32_t s2 = S[rho[nb] * 4 + g];
-            const E4m3Parts lo = e4m3_lookup(lut, s2 & 0xFFu), hi = e4m3_lookup(lut, s2 >> 8);
-            bh[nb][0] = fp4x8_to_f16(bw.x, lo);
-            bh[nb][1] = fp4x8_to_f16(bw.y, lo);
-            bh[nb][2] = fp4x8_to_f16(bw.z, hi);
-            bh[nb][3] = fp4x8_to_f16(bw.w, hi);
-        }
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-            if (F_ || mb < mb_act) {
+            for (int mb = 0; mb < NA; ++mb) {
                 const int row = (2 * mb + wm) * 16 + n16;
-                const int sw = row & 7;
+                a[mb] = as_f16x8(A[row * 16 + ((4 * g + st) ^ (row & 7))]);
+            }
+        };
+        auto widen = [&](int st, f16x8_t *bh) {
 #pragma unroll
-                for (int st = 0; st < 4; ++st) {
-                    const f16x8_t a = as_f16x8(A[row * 16 + ((4 * g + st) ^ sw)]);
+            for (int nb = 0; nb < 4; ++nb) {
+                const uint32_t c = st == 0 ? bw[nb].x : st == 1 ? bw[nb].y : st == 2 ? bw[nb].z : bw[nb].w;
+                bh[nb] = fp4x8_to_f16(c, sp[nb][st >> 1]);
+            }
+        };
+        if (NA > 0) {
 #pragma unroll
-                    for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = mfma16h(a, bh[nb][st], acc[mb][nb]);
+            for (int nb = 0; nb < 4; ++nb) {
+                bw[nb] = B[rho[nb] * 4 + (g ^ bswz(rho[nb]))];
+                const uint32_t s2 = S[rho[nb] * 4 + g];
+                sp[nb][0] = e4m3_lookup(lut, s2 & 0xFFu);
+                sp[nb][1] = e4m3_lookup(lut, s2 >> 8);
+            }
+            read_a(0, acur);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (kn >= 0) issue_part(0, kn, b ^ 1);
+        __builtin_amdgcn_sched_barrier(0);
+        if (NA > 0) widen(0, bcur);
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            __builtin_amdgcn_sched_barrier(0);
+            if (NA > 0) {
+                if (st < 3) {
+                    read_a(st + 1, anxt);
+                    widen(st + 1, bnxt);
                 }
+#pragma unroll
+                for (int mb = 0; mb < NA; ++mb)
+#pragma unroll
+                    for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = mfma16h(acur[mb], bcur[nb], acc[mb][nb]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if (st < 2 && kn >= 0) issue_part(st + 1, kn, b ^ 1);
+            if (NA > 0 && st < 3) {
+#pragma unroll
+                for (int mb = 0; mb < NA; ++mb) acur[mb] = anxt[mb];
+#pragma unroll
+                for (int nb = 0; nb < 4; ++nb) bcur[nb] = bnxt[nb];
             }
         }
     };
 
     // ---- pipeline --------------------------------------------------------------
-    // The scale table is written before the first barrier of the ring.
+    // The scale table is written before the first barrier of the ring.  The
+    // barrier before chunk kc waits for all of this wave's loads of chunk kc;
+    // the stage chunk kc+1 then refills was last read in step kc-1, whose LDS
+    // reads every wave consumed before reaching that barrier.
     fill_e4m3_table(lut);
     lds_barrier();
-    issue(0);
-    const bool full = mb_act == MB;
-    for (int kc = 0; kc < nk; ++kc) {
-        // two stages: every load of chunk kc has landed before it is read
-        chunk_sync<0>();
-        // the stage refilled now was last read in step kc-1, before the barrier
-        if (kc + ST - 1 < nk) issue(kc + ST - 1);
-        if (full) compute(kc % ST, std::true_type{});
-        else if (mb_act > 0) compute(kc % ST, std::false_type{});
+#pragma unroll
+    for (int part = 0; part < 3; ++part) issue_part(part, 0, 0);
+    auto kloop = [&](auto na) {
+        for (int kc = 0; kc < nk; ++kc) {
+            chunk_sync<0>();
+            compute(kc & 1, kc + 1 < nk ? kc + 1 : -1, na);
+        }
+    };
+    static_assert(MB == 6, "one K loop per active row-block count");
+    switch (mb_act) {
+    case 6: kloop(std::integral_constant<int, 6>{}); break;
+    case 5: kloop(std::integral_constant<int, 5>{}); break;
+    case 4: kloop(std::integral_constant<int, 4>{}); break;
+    case 3: kloop(std::integral_constant<int, 3>{}); break;
+    case 2: kloop(std::integral_constant<int, 2>{}); break;
+    case 1: kloop(std::integral_constant<int, 1>{}); break;
+    default: kloop(std::integral_constant<int, 0>{}); break;
     }
 
     // ---- epilogue ----------------------------------------------------------------
