@@ -37,6 +37,7 @@ Workspace carve_workspace(const Shape &s, void *base)
     w.inv = (int32_t *)take(sizeof(int32_t) * (size_t)S);
     w.tiles = (Tile *)take(sizeof(Tile) * (size_t)max_tiles(s, 1));
     w.ntiles = (int32_t *)take(sizeof(int32_t) * 4);
+    if (make_plan(s).tiled) w.sched = (SchedItem *)take(sizeof(SchedItem) * (size_t)sched_entries(s));
     w.h = (uint16_t *)take(sizeof(uint16_t) * (size_t)S * s.F);
     w.o = (uint16_t *)take(sizeof(uint16_t) * (size_t)S * s.d);
     w.ssq = (float *)take(sizeof(float) * (size_t)S * (s.d / 64));
@@ -596,7 +597,7 @@ extern "C" int moe_layer_forward_nvfp4(const moe_dims_t *dims, const void *x, co
     // 16-row tiles as the plan says; the router does not split x, x is
     // converted to fp16 instead
     Plan p = make_plan(s);
-    if (p.tiled) p.tile_rows = kNvTileRows;
+    nv_plan(s, p);
     Plan pr = p;
     pr.tiled = pr.stream = false;
     auto route = [&]() -> hipError_t {

@@ -422,12 +422,56 @@ constexpr int kTN = 256;  // weight rows per tile (one packed weight tile)
 
 typedef int v8i_t __attribute__((__vector_size__(8 * sizeof(int))));
 
+// The rows and N-tile of the item a tiled kernel's workgroup takes.  The
+// gate/up kernels take it from the schedule the tile-list code wrote
+// (SchedItem, sched_pos), loading the entry and the tile count side by side;
+// false past the last item.
+struct ItemRows {
+    int expert, row0, nrows, ntile;
+};
+__device__ __forceinline__ bool sched_take(const SchedItem *sched, const int32_t *ntiles, int ntn,
+                                           ItemRows &tl)
+{
+    const SchedItem it = sched[blockIdx.x];
+    if (sched_pos((int)blockIdx.x, sched_shape(2 * ntn, *ntiles * ntn)) < 0) return false;
+    tl.row0 = it.row0;
+    tl.expert = (int)(it.packed & 1023u);
+    tl.nrows = (int)((it.packed >> 10) & 255u);
+    tl.ntile = (int)(it.packed >> 18);
+    return true;
+}
+// The down kernels take contiguous ranges of the tile list per XCD
+// (xcd_tile): expert by expert, N-tile-major inside an expert, so the
+// workgroups of an expert's row tiles that read the same weight tile run
+// side by side on one XCD and the second read can hit its L2.
+__device__ __forceinline__ bool tile_take(const Tile *tiles, const int32_t *ntiles, int ntn,
+                                          ItemRows &tl)
+{
+    int idx;
+    if (!xcd_tile(*ntiles * ntn, idx)) return false;
+    Tile t = tiles[idx / ntn];
+    const int r = idx - t.first * ntn;
+    const int nt = r / t.count, mt = t.first + (r - nt * t.count);
+    if (mt != idx / ntn) t = tiles[mt];
+    tl.expert = t.expert;
+    tl.row0 = t.row0;
+    tl.nrows = t.nrows;
+    tl.ntile = nt;
+    return true;
+}
+__device__ __forceinline__ bool item_take(const SchedItem *sched, const Tile *tiles,
+                                          const int32_t *ntiles, int ntn, ItemRows &tl)
+{
+    return sched ? sched_take(sched, ntiles, ntn, tl) : tile_take(tiles, ntiles, ntn, tl);
+}
+
 struct MxArgs {
     const uint8_t *ahi, *alo;     // activation parts [rows][K] (FP8)
     const uint8_t *ashi, *aslo;   // their E8M0 scales [rows][K/32]
     const uint8_t *a6;            // or three-part FP6 records [rows][K/128] (wide kernel)
     const int32_t *perm;
     const Tile *tiles;
+    const SchedItem *sched;       // gate/up: the workgroups' items (down: null, tile ranges)
     const int32_t *ntiles;
     const uint8_t *wpk;
     const uint8_t *sc;
@@ -476,15 +520,13 @@ __global__ __launch_bounds__(512) void gemm_mx_kernel(const MxArgs pa)
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int d = pa.d, F = pa.F;
-    int idx;
-    if (!xcd_tile(*pa.ntiles * pa.ntn, idx)) return;
-    // Work order: expert by expert, and inside an expert N-tile-major, so the
+    // The item comes from the schedule the tile-list code wrote (longest
+    // first, an expert's items together on one XCD, N-tile-major, so the
     // workgroups of an expert's row tiles that read the same weight tile run
-    // side by side on one XCD and the second read can hit its L2.
-    Tile tl = pa.tiles[idx / pa.ntn];
-    const int r = idx - tl.first * pa.ntn;
-    const int nt = r / tl.count, mt = tl.first + (r - nt * tl.count);
-    if (mt != idx / pa.ntn) tl = pa.tiles[mt];
+    // side by side and the second read can hit the L2).
+    ItemRows tl;
+    if (!item_take(pa.sched, pa.tiles, pa.ntiles, pa.ntn, tl)) return;
+    const int nt = tl.ntile;
     const int K = GATE_UP ? d : F;
     auto src_row = [&](int r) -> int64_t {
         const int rr = r < tl.nrows ? r : 0;  // rows past nrows re-read row 0 (never stored)
@@ -664,13 +706,10 @@ __global__ __launch_bounds__(512) void gemm_mxw_kernel(const MxArgs pa)
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int d = pa.d, F = pa.F;
-    int idx;
-    if (!xcd_tile(*pa.ntiles * pa.ntn, idx)) return;
-    // expert by expert, N-pair-major inside an expert (pa.ntn = pairs)
-    Tile tl = pa.tiles[idx / pa.ntn];
-    const int r = idx - tl.first * pa.ntn;
-    const int np = r / tl.count, mt = tl.first + (r - np * tl.count);
-    if (mt != idx / pa.ntn) tl = pa.tiles[mt];
+    // the item from the schedule (as gemm_mx_kernel; N-tiles are pairs)
+    ItemRows tl;
+    if (!item_take(pa.sched, pa.tiles, pa.ntiles, pa.ntn, tl)) return;
+    const int np = tl.ntile;
     const int K = GATE_UP ? d : F;
     const int nk = K / kKStep;
     auto src_row = [&](int rw) -> int64_t {
@@ -955,6 +994,7 @@ struct NvArgs {
     const float *as;     // their per-row scales
     const int32_t *perm;
     const Tile *tiles;
+    const SchedItem *sched;  // gate/up: the workgroups' items (down: null, tile ranges)
     const int32_t *ntiles;
     const uint8_t *wpk;  // packed code tiles
     const uint8_t *sc;   // packed E4M3 scale tiles
@@ -981,13 +1021,10 @@ __global__ __launch_bounds__(512) void gemm_nv_kernel(const NvArgs pa)
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int d = pa.d, F = pa.F;
-    int idx;
-    if (!xcd_tile(*pa.ntiles * pa.ntn, idx)) return;
-    // work order as gemm_mx_kernel: expert by expert, N-tile-major inside one
-    Tile tl = pa.tiles[idx / pa.ntn];
-    const int r0 = idx - tl.first * pa.ntn;
-    const int nt = r0 / tl.count, mt = tl.first + (r0 - nt * tl.count);
-    if (mt != idx / pa.ntn) tl = pa.tiles[mt];
+    // the item from the schedule (as gemm_mx_kernel)
+    ItemRows tl;
+    if (!item_take(pa.sched, pa.tiles, pa.ntiles, pa.ntn, tl)) return;
+    const int nt = tl.ntile;
     const int K = GATE_UP ? d : F;
     auto src_row = [&](int r) -> int64_t {
         const int rr = r < tl.nrows ? r : 0;  // rows past nrows re-read row 0 (never stored)
@@ -1507,19 +1544,17 @@ hipError_t launch_gemm1(const Shape &s, const Plan &p, const Workspace &ws, cons
     if (p.tiled) {
         // x was split in the router stage (launch_split_x): FP6 records for
         // the wide kernel, FP8 parts otherwise
-        MxArgs pa{ws.xhi, ws.xlo, ws.xshi, ws.xslo, ws.xa6, ws.perm, ws.tiles, ws.ntiles, wpk, sc,
-                  ws.h, nullptr, s.d, s.F, s.k, s.F / 128, nullptr};
+        // workgroups and their items as the tile-list code scheduled them
+        if (!ws.sched || p.grid1 <= 0) return hipErrorInvalidValue;
+        MxArgs pa{ws.xhi, ws.xlo, ws.xshi, ws.xslo, ws.xa6, ws.perm, ws.tiles, ws.sched, ws.ntiles, wpk,
+                  sc, ws.h, nullptr, s.d, s.F, s.k, p.ntn1, nullptr};
+        const dim3 grid((unsigned)p.grid1);
         if (wide_gate_up(s)) {
             // h goes straight to the down kernel's FP6 records when that kernel is wide
             if (wide_down(s)) pa.h6 = ws.ha6;
-            pa.ntn /= 2;  // pairs of weight tiles
-            const int64_t grid = 8 * ((max_tiles(s, p.tile_rows) * pa.ntn + 7) / 8);
-            hipExtLaunchKernelGGL(gemm_mxw_kernel<true>, dim3((unsigned)grid), dim3(512), 0, st, ev0,
-                                  ev1, 0, pa);
+            hipExtLaunchKernelGGL(gemm_mxw_kernel<true>, grid, dim3(512), 0, st, ev0, ev1, 0, pa);
         } else {
-            const int64_t grid = 8 * ((max_tiles(s, p.tile_rows) * pa.ntn + 7) / 8);
-            hipExtLaunchKernelGGL(gemm_mx_kernel<true>, dim3((unsigned)grid), dim3(512), 0, st, ev0,
-                                  ev1, 0, pa);
+            hipExtLaunchKernelGGL(gemm_mx_kernel<true>, grid, dim3(512), 0, st, ev0, ev1, 0, pa);
         }
     } else if (p.stream) {
         const int R = p.tile_rows;
@@ -1559,16 +1594,11 @@ hipError_t launch_gemm2(const Shape &s, const Plan &p, const Workspace &ws, cons
         if (!wide_down(s)) e = launch_split(ws.h, s.S(), s.F, ws.hhi, ws.hlo, ws.hshi, ws.hslo, st);
         else if (!wide_gate_up(s)) e = launch_split6(ws.h, s.S(), s.F, ws.ha6, st);
         if (e != hipSuccess) return e;
-        MxArgs pa{ws.hhi, ws.hlo, ws.hshi, ws.hslo, ws.ha6, nullptr, ws.tiles, ws.ntiles, wpk, sc,
-                  ws.o, ws.ssq, s.d, s.F, s.k, s.d / 256, nullptr};
-        if (wide_down(s)) {
-            pa.ntn /= 2;
-            const int64_t grid = 8 * ((max_tiles(s, p.tile_rows) * pa.ntn + 7) / 8);
-            gemm_mxw_kernel<false><<<(unsigned)grid, 512, 0, st>>>(pa);
-        } else {
-            const int64_t grid = 8 * ((max_tiles(s, p.tile_rows) * pa.ntn + 7) / 8);
-            gemm_mx_kernel<false><<<(unsigned)grid, 512, 0, st>>>(pa);
-        }
+        MxArgs pa{ws.hhi, ws.hlo, ws.hshi, ws.hslo, ws.ha6, nullptr, ws.tiles, nullptr, ws.ntiles, wpk,
+                  sc, ws.o, ws.ssq, s.d, s.F, s.k, wide_down(s) ? s.d / 512 : s.d / 256, nullptr};
+        const int64_t grid = 8 * ((max_tiles(s, p.tile_rows) * pa.ntn + 7) / 8);
+        if (wide_down(s)) gemm_mxw_kernel<false><<<(unsigned)grid, 512, 0, st>>>(pa);
+        else gemm_mx_kernel<false><<<(unsigned)grid, 512, 0, st>>>(pa);
     } else {
         const int wgs = s.d / 64;
         const int64_t grid = max_tiles(s, p.tile_rows) * wgs;
@@ -1593,10 +1623,10 @@ hipError_t launch_gemm1_nv(const Shape &s, const Plan &p, const Workspace &ws, c
     const uint16_t *x16 = reinterpret_cast<const uint16_t *>(ws.xhi);
     const float *xs = reinterpret_cast<const float *>(ws.xshi);
     if (p.tiled) {
-        NvArgs pa{x16, xs, ws.perm, ws.tiles, ws.ntiles, wpk, sc, gs, ws.h, nullptr,
-                  s.d, s.F, s.k, s.F / 128};
-        const int64_t grid = 8 * ((max_tiles(s, p.tile_rows) * pa.ntn + 7) / 8);
-        hipExtLaunchKernelGGL(gemm_nv_kernel<true>, dim3((unsigned)grid), dim3(512), 0, st,
+        if (!ws.sched || p.grid1 <= 0) return hipErrorInvalidValue;
+        NvArgs pa{x16, xs, ws.perm, ws.tiles, ws.sched, ws.ntiles, wpk, sc, gs, ws.h, nullptr,
+                  s.d, s.F, s.k, p.ntn1};
+        hipExtLaunchKernelGGL(gemm_nv_kernel<true>, dim3((unsigned)p.grid1), dim3(512), 0, st,
                               ev0, ev1, 0, pa);
     } else if (p.stream) {
         // the persistent streaming kernel: it converts the bf16 x rows of a
@@ -1642,7 +1672,7 @@ hipError_t launch_gemm2_nv(const Shape &s, const Plan &p, const Workspace &ws, c
         if (e != hipSuccess) return e;
     }
     if (p.tiled) {
-        NvArgs pa{h16, hs, nullptr, ws.tiles, ws.ntiles, wpk, sc, gs, ws.o, ws.ssq,
+        NvArgs pa{h16, hs, nullptr, ws.tiles, nullptr, ws.ntiles, wpk, sc, gs, ws.o, ws.ssq,
                   s.d, s.F, s.k, s.d / 256};
         const int64_t grid = 8 * ((max_tiles(s, p.tile_rows) * pa.ntn + 7) / 8);
         gemm_nv_kernel<false><<<(unsigned)grid, 512, 0, st>>>(pa);

@@ -20,6 +20,66 @@ struct Tile {
     int32_t pad[3];
 };
 
+// One workgroup's item of a tiled product: rows [row0, row0+nrows) of the
+// grouped order, all of `expert`, times the expert's N-tile `ntile`; packed
+// as row0 and expert | nrows << 10 | ntile << 18 (E <= 1024, nrows <= 255,
+// ntile < 2048).  The tile-list code writes one per item (the schedule).
+struct SchedItem {
+    int32_t row0;
+    uint32_t packed;
+};
+__host__ __device__ inline SchedItem sched_item(int expert, int row0, int nrows, int ntile)
+{
+    return SchedItem{row0, (uint32_t)expert | (uint32_t)nrows << 10 | (uint32_t)ntile << 18};
+}
+
+// Where the items of the tiled gate/up product go.  The items, longest
+// first, are cut into runs of `run`; each round deals 8 runs to the 8 XCDs
+// in snake order (round r gives XCD x run 8r + x, or 8r + 7 - x when r is
+// odd), and the items left after the last full round are split evenly over
+// the 8 XCDs in the same way.  Workgroup b runs on XCD b % 8 (the
+// dispatcher's order), so XCD x's workgroups take its runs in order.
+// Item counts fit int32 (they are bounded by S * F / 128).
+struct SchedShape {
+    int run;     // items per run
+    int full;    // items in the full rounds (a multiple of 8 * run)
+    int rem;     // items after them
+    int lr;      // items per XCD in the last round, ceil(rem / 8)
+};
+__host__ __device__ inline SchedShape sched_shape(int run, int nitems)
+{
+    SchedShape q;
+    q.run = run;
+    q.full = nitems / (8 * run) * 8 * run;
+    q.rem = nitems - q.full;
+    q.lr = (q.rem + 7) / 8;
+    return q;
+}
+__host__ __device__ inline int sched_snake(int round, int x) { return (round & 1) ? 7 - x : x; }
+// workgroup b -> sorted item, or -1 when b has none
+__host__ __device__ inline int sched_pos(int b, const SchedShape &q)
+{
+    const int p = b >> 3, x = b & 7, full_p = q.full / 8;  // positions of the full rounds
+    if (p < full_p) {
+        const int round = p / q.run, o = p - round * q.run;
+        return (round * 8 + sched_snake(round, x)) * q.run + o;
+    }
+    const int o = p - full_p;
+    if (o >= q.lr) return -1;
+    const int i = sched_snake(q.full / (8 * q.run), x) * q.lr + o;
+    return i < q.rem ? q.full + i : -1;
+}
+// sorted item s (< nitems) -> its workgroup
+__host__ __device__ inline int sched_slot(int s, const SchedShape &q)
+{
+    if (s < q.full) {
+        const int rid = s / q.run, o = s - rid * q.run, round = rid >> 3;
+        return 8 * (round * q.run + o) + sched_snake(round, rid & 7);
+    }
+    const int i = s - q.full, xr = i / q.lr, o = i - xr * q.lr;
+    return 8 * (q.full / 8 + o) + sched_snake(q.full / (8 * q.run), xr);
+}
+
 // Tokens per chunk of the counting sort (one 64-bit token mask per expert).
 constexpr int kChunkTokens = 64;
 
@@ -50,7 +110,39 @@ struct Plan {
     int tile_rows;  // rows per tile of the tile list
     int ssq_cols;   // columns of o per partial sum of squares
     bool small_route;  // single-workgroup routing (T <= 64 and T*k <= 4096)
+    // tiled plans: the gate/up kernel's workgroups per tile and its launch
+    // (the schedule the tile-list code writes, Sched)
+    int ntn1;
+    int grid1;
 };
+
+// Upper bound of the tile count for tiles of tile_rows rows (1: any plan).
+inline int64_t max_tiles(const Shape &s, int tile_rows)
+{
+    int64_t S = s.S();
+    int64_t u = S < s.E ? S : s.E;
+    return S / tile_rows + u + 1;
+}
+
+// The wide kernel (128 x 512 tiles) runs a matrix with an even number of
+// 256-row weight tiles; an odd count runs on the 128 x 256 kernel.
+inline bool wide_gate_up(const Shape &s) { return (s.F / 128) % 2 == 0; }
+inline bool wide_down(const Shape &s) { return (s.d / 256) % 2 == 0; }
+
+// Workgroups of the tiled gate/up launch: runs of 2*ntn items dealt to the
+// 8 XCDs in rounds, enough rounds for every item of the largest tile list.
+inline int64_t sched_grid(const Shape &s, int tile_rows, int ntn)
+{
+    const int64_t run = 2 * (int64_t)ntn;
+    const int64_t items = max_tiles(s, tile_rows) * ntn;
+    return 8 * run * ((items + 8 * run - 1) / (8 * run));
+}
+
+inline void set_schedule(const Shape &s, Plan &p, int ntn_gate_up)
+{
+    p.ntn1 = ntn_gate_up;
+    p.grid1 = (int)sched_grid(s, p.tile_rows, ntn_gate_up);
+}
 
 inline Plan make_plan(const Shape &s)
 {
@@ -62,6 +154,9 @@ inline Plan make_plan(const Shape &s)
     if (p.tile_rows < 1) p.tile_rows = 1;
     p.ssq_cols = 64;  // both down kernels reduce o^2 over 64-column groups
     p.small_route = s.T <= kChunkTokens && S <= 4096;
+    p.ntn1 = p.grid1 = 0;
+    // MXFP4 tiled gate/up kernel: pairs of 256-row weight tiles (wide) or single ones
+    if (p.tiled) set_schedule(s, p, wide_gate_up(s) ? s.F / 256 : s.F / 128);
     return p;
 }
 
@@ -93,23 +188,23 @@ inline int router_splits(const Shape &s)
 constexpr int kA6Bytes = 304;
 constexpr int kA6Units = kA6Bytes / 16;
 
-// The wide kernel (128 x 512 tiles) runs a matrix with an even number of
-// 256-row weight tiles; an odd count runs on the 128 x 256 kernel.
-inline bool wide_gate_up(const Shape &s) { return (s.F / 128) % 2 == 0; }
-inline bool wide_down(const Shape &s) { return (s.d / 256) % 2 == 0; }
-
 // Rows per tile of the 16-block format's tiled kernel: 192 keeps an
 // expert's prefill rows (about 128 +- 40) in one tile, so its weights are
 // loaded and widened once.
 constexpr int kNvTileRows = 192;
 
-// Upper bound of the tile count for tiles of tile_rows rows (1: any plan).
-inline int64_t max_tiles(const Shape &s, int tile_rows)
+// The 16-block format's tiled kernels: kNvTileRows-row tiles, one 256-row
+// weight tile per workgroup.
+inline void nv_plan(const Shape &s, Plan &p)
 {
-    int64_t S = s.S();
-    int64_t u = S < s.E ? S : s.E;
-    return S / tile_rows + u + 1;
+    if (!p.tiled) return;
+    p.tile_rows = kNvTileRows;
+    set_schedule(s, p, s.F / 128);
 }
+
+// Entries of the workspace's schedule: enough for any tiled plan (128-row
+// tiles and single weight tiles give the most workgroups).
+inline int64_t sched_entries(const Shape &s) { return sched_grid(s, 128, s.F / 128); }
 
 inline int64_t num_chunks(const Shape &s) { return (s.T + kChunkTokens - 1) / kChunkTokens; }
 
@@ -125,6 +220,7 @@ struct Workspace {
     int32_t *inv;         // [S]
     Tile *tiles;          // [max_tiles]
     int32_t *ntiles;      // [1]
+    SchedItem *sched;     // tiled plans: the gate/up kernel's item per workgroup, else null
     uint16_t *h;          // bf16 [S][F]
     uint16_t *o;          // bf16 [S][d]
     float *ssq;           // [S][d / 64]

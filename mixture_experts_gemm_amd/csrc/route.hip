@@ -469,13 +469,38 @@ __device__ int2 block_exclusive_scan2(int32_t *a, int32_t *b, int n, int32_t (*w
     return total;
 }
 
+// The order in which the tiled gate/up kernel's workgroups take the tiles.
+// Every workgroup handles one (tile, N-tile) item, described in full by
+// out[workgroup] (SchedItem), so it starts with one load.  Items go
+// longest first (experts by rows per tile, descending, then by id), an
+// expert's items together and N-tile-major as in the tile list; the
+// sequence is cut into runs of 2 * ntn items dealt to the XCDs as sched_pos
+// describes.  So each XCD holds about an eighth of the work, an expert's
+// items share an XCD's L2 (a run is two tiles' worth), and the last
+// workgroups an XCD starts are its shortest: the tail of the launch is
+// short.
+struct Sched {
+    SchedItem *out;  // null: not a tiled plan
+    int ntn;         // workgroups per tile (weight-tile groups); runs of 2 * ntn items
+};
+
 // offsets / counts / tile list from per-expert counts cnt[] (LDS, E entries);
-// cnt is replaced by the exclusive offsets.
+// cnt is replaced by the exclusive offsets.  With a schedule (sc.out set)
+// also the tiled gate/up kernel's work order.
 __device__ void finish_offsets(int32_t *cnt, int32_t *toff, int32_t (*wtot)[4], int E, int tile_rows,
                                int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
-                               Tile *__restrict__ tiles, int32_t *__restrict__ ntiles, int *c_out)
+                               Tile *__restrict__ tiles, int32_t *__restrict__ ntiles, int *c_out,
+                               const Sched &sc)
 {
-    const int tid = threadIdx.x;
+    __shared__ int32_t skey[1024];   // expert -> rows per tile / 16 (0: no rows)
+    __shared__ int32_t srank[1024];  // expert -> ranked position
+    __shared__ int32_t stn[1024];    // ranked position -> tiles, then their exclusive prefix
+    __shared__ int32_t sdum[1024];
+    __shared__ int32_t bcnt[16][16]; // [64-expert chunk][bin] experts of the bin
+    __shared__ int32_t bpre[16][16]; // the same, summed over the earlier chunks
+    __shared__ int32_t btot[16];     // experts of a bin
+    __shared__ int32_t bstart[16];   // ranked position of a bin's first expert
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     for (int e = tid; e < E; e += 256) {
         c_out[e / 256] = cnt[e];
         toff[e] = (cnt[e] + tile_rows - 1) / tile_rows;
@@ -510,6 +535,92 @@ __device__ void finish_offsets(int32_t *cnt, int32_t *toff, int32_t (*wtot)[4], 
             tl.pad[0] = tl.pad[1] = tl.pad[2] = 0;
             tiles[toff[e] + i] = tl;
         }
+        skey[e] = nt > 0 ? (per + 15) >> 4 : 0;
+    }
+    if (!sc.out) return;
+
+    // ---- rank the experts: bins of rows per tile, descending; by id inside
+    // a bin (ballots over 64-expert chunks, chunk q*4 + wave of expert
+    // q*256 + tid) ----
+    reinterpret_cast<int32_t *>(bcnt)[tid] = 0;
+    __syncthreads();
+    const int NB = min(16, (tile_rows + 15) / 16 + 1);
+    const int NQ = (E + 255) >> 8;
+    int my_bin[4], my_within[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        if (q >= NQ) break;
+        const int e = q * 256 + tid;
+        const int b = e < E ? min(skey[e], NB - 1) : -1;
+        my_bin[q] = b;
+        my_within[q] = 0;
+        for (int bb = 0; bb < NB; ++bb) {
+            const uint64_t m = __ballot(b == bb);
+            if (lane == 0) bcnt[q * 4 + wv][bb] = __popcll(m);
+            if (b == bb) my_within[q] = __popcll(m & ((1ull << lane) - 1ull));
+        }
+    }
+    __syncthreads();
+    {
+        // thread (bin tid/16, chunk tid%16): prefix over the chunks of its
+        // bin by shuffles within 16 lanes; the bin's total in chunk 15
+        const int bb = tid >> 4, c = tid & 15;
+        const int own = bb < NB ? bcnt[c][bb] : 0;
+        int v = own;
+#pragma unroll
+        for (int dd = 1; dd < 16; dd <<= 1) {
+            const int u = __shfl_up(v, dd, 16);
+            if (c >= dd) v += u;
+        }
+        bpre[c][bb] = v - own;
+        if (c == 15) btot[bb] = v;
+    }
+    __syncthreads();
+    if (tid < 64) {
+        // a bin's first ranked position: the experts of all higher bins
+        const int own = tid < NB ? btot[tid] : 0;
+        int v = own;
+#pragma unroll
+        for (int dd = 1; dd < 16; dd <<= 1) {
+            const int u = __shfl_down(v, dd, 16);
+            if (tid + dd < 16) v += u;
+        }
+        if (tid < 16) bstart[tid] = v - own;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int e = q * 256 + tid;
+        if (q >= NQ || e >= E) continue;
+        const int b = my_bin[q], chunk = q * 4 + wv;
+        const int r = bstart[b] + bpre[chunk][b] + my_within[q];
+        srank[e] = r;
+        stn[r] = (c_out[q] + tile_rows - 1) / tile_rows;
+        sdum[r] = 0;
+    }
+    __syncthreads();
+    (void)block_exclusive_scan2(stn, sdum, E, wtot);  // totals: ntot tiles
+
+    // ---- deal the items: one thread per tile (original order).  Tile mo
+    // of expert e (ranked r) holds items j = np * nte + mo of the expert's
+    // N-tile-major sequence, sorted position stn[r] * ntn + j. ----
+    const int ntn = sc.ntn;
+    const SchedShape q = sched_shape(2 * ntn, ntot * ntn);
+    for (int t = tid; t < ntot; t += 256) {
+        int e = 0, hi = E;  // the last expert with toff[e] <= t (it has tiles)
+        while (hi - e > 1) {
+            const int mid = (e + hi) >> 1;
+            if (toff[mid] <= t) e = mid;
+            else hi = mid;
+        }
+        const int r = srank[e];
+        const int nte = (e + 1 < E ? toff[e + 1] : ntot) - toff[e], mo = t - toff[e];
+        const int per = skey[e] << 4;
+        const int ce = (e + 1 < E ? cnt[e + 1] : total) - cnt[e];
+        const int row0 = cnt[e] + mo * per, nrows = min(per, ce - mo * per);
+        const int base = stn[r] * ntn;
+        for (int np = 0; np < ntn; ++np)
+            sc.out[sched_slot(base + np * nte + mo, q)] = sched_item(e, row0, nrows, np);
     }
 }
 
@@ -522,7 +633,7 @@ __global__ __launch_bounds__(256) void route_small_kernel(
     const float *__restrict__ scores, int32_t *__restrict__ ids, float *__restrict__ wts,
     int32_t *__restrict__ counts, int32_t *__restrict__ offsets, int32_t *__restrict__ perm,
     int32_t *__restrict__ inv, Tile *__restrict__ tiles, int32_t *__restrict__ ntiles, int T,
-    int E, int k, int tile_rows, int nsplit)
+    int E, int k, int tile_rows, int nsplit, const Sched sc)
 {
     __shared__ unsigned long long mask[1024];
     __shared__ int32_t sid[4096];
@@ -541,7 +652,7 @@ __global__ __launch_bounds__(256) void route_small_kernel(
     for (int e = tid; e < E; e += 256) cnt[e] = __popcll(mask[e]);
     __syncthreads();
     int c_own[4];
-    finish_offsets(cnt, toff, wtot, E, tile_rows, counts, offsets, tiles, ntiles, c_own);
+    finish_offsets(cnt, toff, wtot, E, tile_rows, counts, offsets, tiles, ntiles, c_own, sc);
     for (int s = tid; s < S; s += 256) {
         const int e = sid[s];
         const int t = s / k;
@@ -574,7 +685,7 @@ __global__ __launch_bounds__(256) void group_mask_kernel(const int32_t *__restri
 __global__ __launch_bounds__(256) void group_scan_kernel(
     const uint64_t *__restrict__ masks, int32_t *__restrict__ chunk_base,
     int32_t *__restrict__ counts, int32_t *__restrict__ offsets, Tile *__restrict__ tiles,
-    int32_t *__restrict__ ntiles, int E, int nchunks, int tile_rows)
+    int32_t *__restrict__ ntiles, int E, int nchunks, int tile_rows, const Sched sc)
 {
     __shared__ int32_t cnt[1024];
     __shared__ int32_t toff[1024];
@@ -599,7 +710,7 @@ __global__ __launch_bounds__(256) void group_scan_kernel(
     }
     __syncthreads();
     int c_own[4];
-    finish_offsets(cnt, toff, wtot, E, tile_rows, counts, offsets, tiles, ntiles, c_own);
+    finish_offsets(cnt, toff, wtot, E, tile_rows, counts, offsets, tiles, ntiles, c_own, sc);
     for (int e = tid; e < E; e += 256) {
         int run = cnt[e];
         for (int c0 = 0; c0 < nchunks; c0 += B) {
@@ -636,6 +747,17 @@ __global__ __launch_bounds__(256) void group_scatter_kernel(
     }
 }
 
+// The tiled gate/up kernel's schedule the tile-list code writes (none for
+// the few-row plans).
+static Sched schedule(const Plan &p, const Workspace &ws)
+{
+    Sched sc{};
+    if (!p.tiled || !ws.sched) return sc;
+    sc.out = ws.sched;
+    sc.ntn = p.ntn1;
+    return sc;
+}
+
 template <int SLOTS>
 static void launch_topk_slots(const Shape &s, const Plan &p, const Workspace &ws, hipStream_t st)
 {
@@ -643,7 +765,7 @@ static void launch_topk_slots(const Shape &s, const Plan &p, const Workspace &ws
         route_small_kernel<SLOTS><<<1, 256, 0, st>>>(ws.scores, ws.ids, ws.wts, ws.counts,
                                                      ws.offsets, ws.perm, ws.inv, ws.tiles,
                                                      ws.ntiles, s.T, s.E, s.k, p.tile_rows,
-                                                     router_splits(s));
+                                                     router_splits(s), schedule(p, ws));
     } else {
         topk_kernel<SLOTS><<<(s.T + 3) / 4, 256, 0, st>>>(ws.scores, ws.ids, ws.wts, s.T, s.E, s.k,
                                                           router_splits(s));
@@ -664,7 +786,7 @@ hipError_t launch_group(const Shape &s, const Plan &p, const Workspace &ws, hipS
     const int nchunks = (int)num_chunks(s);
     group_mask_kernel<<<nchunks, 256, 0, st>>>(ws.ids, ws.masks, s.T, s.E, s.k);
     group_scan_kernel<<<1, 256, 0, st>>>(ws.masks, ws.chunk_base, ws.counts, ws.offsets, ws.tiles,
-                                         ws.ntiles, s.E, nchunks, p.tile_rows);
+                                         ws.ntiles, s.E, nchunks, p.tile_rows, schedule(p, ws));
     group_scatter_kernel<<<nchunks, 256, 0, st>>>(ws.ids, ws.masks, ws.chunk_base, ws.perm, ws.inv,
                                                   s.T, s.E, s.k);
     return hipGetLastError();
