@@ -249,7 +249,8 @@ def _roofline(name, nbytes, flops, g1_ms, R):
     byte time at the HBM peak and the flop time at the bf16 peak)."""
     hbm_bound = nbytes / R.MI355X_HBM_BYTES_PER_S >= flops / R.MI355X_BF16_FLOPS_PER_S
     kern = GATE_UP_KERNEL[name]
-    out = dict(kernel=kern, traffic=R.recorded_traffic(counter_summary(name)))
+    out = dict(kernel=kern, traffic=R.recorded_traffic(counter_summary(name)),
+               kernel_us_per_launch=g1_ms * 1e3)
     if hbm_bound:
         achieved = nbytes / (g1_ms * 1e-3)
         out.update(bound="hbm", achieved=achieved / 1e9, peak=R.MI355X_HBM_BYTES_PER_S / 1e9, unit="GB/s",
@@ -698,6 +699,8 @@ def main():
                    "distinct_experts_mean": main_res.get("distinct_experts_mean")},
         "roofline": {**{k: v for k, v in roof.items()
                         if k in ("bound", "achieved", "peak", "unit", "frac", "traffic", "kernel",
+                                 "kernel_us_per_launch", "algorithmic_bytes_per_launch",
+                                 "algorithmic_flops_per_launch",
                                  "frac_of_measured_copy_rate", "frac_of_measured_bf16_gemm_rate",
                                  "mx_issue")},
                      "layer": layer},
