@@ -59,6 +59,37 @@ __global__ __launch_bounds__(256) void combine_kernel(
             y[2 * i + 1] = fmaf(cj, __uint_as_float(ow[i] & 0xFFFF0000u), y[2 * i + 1]);
         }
     };
+    if (SLOT && k <= kSlotBatch) {
+        // few-row path, one pass: the o rows and every norm partial go out
+        // together with x, alpha, beta, so the workgroup waits on memory once
+        uint4 ov[kSlotBatch];
+#pragma unroll
+        for (int j = 0; j < kSlotBatch; ++j)
+            ov[j] = act && j < k ? *reinterpret_cast<const uint4 *>(o + ((int64_t)t * k + j) * d + c0)
+                                 : make_uint4(0, 0, 0, 0);
+        // 16 lanes per slot; lane l of slot j adds partials l, l+16, ... in
+        // that order (loads at a clamped index, masked after, so they are
+        // all issued before the first add)
+        const int j = threadIdx.x >> 4, l = threadIdx.x & 15;
+        const bool js = j < k;
+        const float *sp = ssq + ((int64_t)t * k + (js ? j : 0)) * P;
+        float ss = 0.f;
+        for (int q0 = 0; q0 < P; q0 += 128) {
+            float pv[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) pv[i] = sp[min(q0 + 16 * i + l, P - 1)];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) ss += q0 + 16 * i + l < P ? pv[i] : 0.f;
+        }
+        ss = sum16(ss);
+        if (js && l == 0) coef[j] = wts[(int64_t)t * k + j] * (1.0f / sqrtf(ss / (float)d + eps));
+        __syncthreads();
+        if (act) {
+#pragma unroll
+            for (int jj = 0; jj < kSlotBatch; ++jj)
+                if (jj < k) accumulate(ov[jj], coef[jj]);
+        }
+    } else
     for (int j0 = 0; j0 < k; j0 += JB) {
         const int kk = min(JB, k - j0);
         // slot order: the pass's o values go out together with the norms' loads
