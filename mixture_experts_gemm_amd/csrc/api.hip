@@ -311,7 +311,6 @@ struct LatentWorkspace {
     Workspace ws;
     float *scores_r;
     uint16_t *z, *y;
-    float *f;
     size_t bytes;
 };
 
@@ -330,7 +329,6 @@ static LatentWorkspace carve_latent(const LatentShapes &ls, void *base)
     L.scores_r = (float *)take(sizeof(float) * (size_t)router_splits(r) * r.T * r.E);
     L.z = (uint16_t *)take(sizeof(uint16_t) * (size_t)e.T * e.d);
     L.y = (uint16_t *)take(sizeof(uint16_t) * (size_t)e.T * e.d);
-    L.f = (float *)take(sizeof(float) * (size_t)r.T * r.d);
     L.bytes = off;
     return L;
 }
@@ -388,7 +386,7 @@ extern "C" int moe_latent_forward(const moe_latent_dims_t *dims, const void *x,
     };
     auto ok = [](hipError_t e) { return e == hipSuccess; };
     auto narrow = [&]() -> hipError_t {
-        hipError_t e = launch_dense(xb, static_cast<const uint16_t *>(w_narrow), L.z, false, sr.T,
+        hipError_t e = launch_dense(xb, static_cast<const uint16_t *>(w_narrow), L.z, kDenseBf16, sr.T,
                                     se.d, sr.d, st);
         if (e != hipSuccess) return e;
         if (p.stream) return launch_split_x_fp8(se, L.ws, L.z, st);
@@ -398,9 +396,9 @@ extern "C" int moe_latent_forward(const moe_latent_dims_t *dims, const void *x,
     auto widen = [&]() -> hipError_t {
         hipError_t e = launch_combine_sum(se, p, L.ws, L.y, st);
         if (e != hipSuccess) return e;
-        e = launch_dense(L.y, static_cast<const uint16_t *>(w_widen), L.f, true, sr.T, sr.d, se.d, st);
-        if (e != hipSuccess) return e;
-        return launch_gate(xb, L.f, alpha, beta, static_cast<uint16_t *>(s_out), sr.T, sr.d, st);
+        // the widening product stores the gated residual itself
+        return launch_dense(L.y, static_cast<const uint16_t *>(w_widen), s_out, kDenseGate, sr.T, sr.d,
+                            se.d, st, DenseGate{xb, alpha, beta});
     };
     if (!stage(MOE_STAGE_ROUTER, [&] { return launch_router(sr, pr, wr, xb, router_w, st); }) ||
         !stage(MOE_STAGE_TOPK, [&] { return launch_topk(sr, p, wr, st); }) ||

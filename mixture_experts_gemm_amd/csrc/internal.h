@@ -272,13 +272,18 @@ hipError_t launch_postnorm_gate(const uint16_t *x, const float *y, const float *
 // bf16 x -> FP8 hi/lo parts + E8M0 scales in the workspace (the streaming
 // gate/up kernel's input when the router does not split x itself).
 hipError_t launch_split_x_fp8(const Shape &s, const Workspace &ws, const uint16_t *x, hipStream_t st);
-// c[T][N] = a[T][K] w[N][K]^T, bf16 operands, fp32 accumulation, c bf16 or
-// fp32, on the bf16 MFMA (the latent-width variant's shared matrices).
-hipError_t launch_dense(const uint16_t *a, const uint16_t *w, void *c, bool c_fp32, int T, int N,
-                        int K, hipStream_t st);
-// s_out = bf16(alpha * x + beta * f), x bf16 [T][D], f fp32 [T][D].
-hipError_t launch_gate(const uint16_t *x, const float *f, const float *alpha, const float *beta,
-                       uint16_t *s_out, int64_t T, int D, hipStream_t st);
+// c[T][N] = a[T][K] w[N][K]^T, bf16 operands, fp32 accumulation on the bf16
+// MFMA (the latent-width variant's shared matrices); c is stored as bf16
+// (kDenseBf16), fp32 (kDenseF32) or as the gated residual
+// bf16(alpha[n] * x[t][n] + beta[n] * c[t][n]) (kDenseGate, x bf16 [T][N],
+// c may be x).
+enum { kDenseBf16 = 0, kDenseF32 = 1, kDenseGate = 2 };
+struct DenseGate {
+    const uint16_t *x;
+    const float *alpha, *beta;
+};
+hipError_t launch_dense(const uint16_t *a, const uint16_t *w, void *c, int out, int T, int N, int K,
+                        hipStream_t st, const DenseGate &g = DenseGate{nullptr, nullptr, nullptr});
 hipError_t launch_pack(const uint8_t *w, const uint8_t *s, int E, int d, int F, uint8_t *wp,
                        uint8_t *sp, hipStream_t st);
 // The 16-block format (one E4M3 scale per 16 values, matrix scales gs [E][3]).

@@ -8,7 +8,9 @@
 //
 // Both products are C[T][N] = A[T][K] W[N][K]^T with bf16 A and W (K
 // contiguous in both), fp32 accumulation on the bf16 MFMA, and C bf16 (the
-// narrowed token z, rounded to nearest even) or fp32 (the widened sum f).
+// narrowed token z, rounded to nearest even) or, for the widened sum f, the
+// gated residual s_out = bf16(alpha * x + beta * f) formed in the epilogue
+// (f never leaves the registers).
 // Few tokens: each matrix row is read once from HBM, so the product is a
 // weight stream (dense_stream_kernel).  Many tokens: 256 x 256 output tiles
 // staged through LDS (dense_gemm_kernel).
@@ -17,6 +19,23 @@
 #include "layout.h"
 
 namespace moe {
+
+// One output element: c bf16 (kDenseBf16), fp32 (kDenseF32), or, for the
+// widening product, the gated residual s_out = bf16(alpha * x + beta * c)
+// at the same place of [T][N] (kDenseGate; x is read before s_out is
+// written by the same thread, so s_out may be x).
+template <int OUT>
+__device__ __forceinline__ void store_dense(void *C, int64_t idx, int col, float v, const DenseGate &g)
+{
+    if constexpr (OUT == kDenseF32) {
+        static_cast<float *>(C)[idx] = v;
+    } else if constexpr (OUT == kDenseGate) {
+        const float xf = __uint_as_float((uint32_t)g.x[idx] << 16);
+        static_cast<uint16_t *>(C)[idx] = f32_to_bf16(fmaf(g.beta[col], v, g.alpha[col] * xf));
+    } else {
+        static_cast<uint16_t *>(C)[idx] = f32_to_bf16(v);
+    }
+}
 
 // ---- few tokens: the weight stream ---------------------------------------------
 // One workgroup per 16 rows of W (16 output columns), all T <= 8 tokens.
@@ -40,10 +59,10 @@ namespace moe {
 constexpr int kDenseStreamMaxT = 8;
 constexpr int kDenseU = 4;
 
-template <bool OUT_F32, int NW>
+template <int OUT, int NW>
 __global__ __launch_bounds__(64 * NW) void dense_stream_kernel(const uint16_t *__restrict__ A,
                                                                const uint16_t *__restrict__ W, void *C,
-                                                               int T, int N, int K)
+                                                               int T, int N, int K, const DenseGate gate)
 {
     extern __shared__ uint4 as4[];  // [T][K/8] swizzled units
     __shared__ floatx4_t red[NW - 1][2][64];
@@ -126,9 +145,9 @@ __global__ __launch_bounds__(64 * NW) void dense_stream_kernel(const uint16_t *_
         for (int r = 0; r < 4; ++r) {
             const int t = 4 * (lane >> 4) + r;
             if (t < T) {
-                const int64_t idx = (int64_t)t * N + row0 + 8 * o + (lane & 7);
-                if constexpr (OUT_F32) static_cast<float *>(C)[idx] = v[r];
-                else static_cast<uint16_t *>(C)[idx] = f32_to_bf16(v[r]);
+                const int col = row0 + 8 * o + (lane & 7);
+                const int64_t idx = (int64_t)t * N + col;
+                store_dense<OUT>(C, idx, col, v[r], gate);
             }
         }
     }
@@ -147,10 +166,11 @@ __global__ __launch_bounds__(64 * NW) void dense_stream_kernel(const uint16_t *_
 constexpr int kGemmTile = 256;
 constexpr int kGemmStages = 4;
 
-template <bool OUT_F32>
+template <int OUT>
 __global__ __launch_bounds__(512) void dense_gemm_kernel(const uint16_t *__restrict__ A,
                                                          const uint16_t *__restrict__ W, void *C,
-                                                         int T, int N, int K, int tiles_m, int tiles_n)
+                                                         int T, int N, int K, int tiles_m, int tiles_n,
+                                                         const DenseGate gate)
 {
     constexpr int AU = kGemmTile * 4, BU = kGemmTile * 4;  // 16-byte units per stage
     constexpr int NL = (AU + BU) / 512;                    // loads per thread per stage (4)
@@ -226,77 +246,41 @@ __global__ __launch_bounds__(512) void dense_gemm_kernel(const uint16_t *__restr
             if (t >= T) continue;
 #pragma unroll
             for (int nb = 0; nb < 4; ++nb) {
-                const int64_t o = (int64_t)t * N + N0 + wn * 64 + nb * 16 + m16;
-                if constexpr (OUT_F32) static_cast<float *>(C)[o] = acc[mb][nb][r];
-                else static_cast<uint16_t *>(C)[o] = f32_to_bf16(acc[mb][nb][r]);
+                const int col = N0 + wn * 64 + nb * 16 + m16;
+                store_dense<OUT>(C, (int64_t)t * N + col, col, acc[mb][nb][r], gate);
             }
         }
 }
 
-hipError_t launch_dense(const uint16_t *a, const uint16_t *w, void *c, bool c_fp32, int T, int N,
-                        int K, hipStream_t st)
+template <int OUT>
+static hipError_t launch_dense_out(const uint16_t *a, const uint16_t *w, void *c, int T, int N, int K,
+                                   hipStream_t st, const DenseGate &g)
 {
     if (T <= 0) return hipSuccess;
     // few tokens with their rows in LDS (at most 128 KB): the weight stream
     const size_t lds = (size_t)T * K * 2;
     // the A copy needs T*K/8 divisible by 64 * NW for any T: K % (512 * NW) == 0
     if (T <= kDenseStreamMaxT && lds <= 128 * 1024 && N % 16 == 0 && K % 2048 == 0 && K >= 4096) {
-        if (K % 4096 == 0 && K >= 8192) {  // 8 waves
-            if (c_fp32) dense_stream_kernel<true, 8><<<N / 16, 512, lds, st>>>(a, w, c, T, N, K);
-            else dense_stream_kernel<false, 8><<<N / 16, 512, lds, st>>>(a, w, c, T, N, K);
-        } else {
-            if (c_fp32) dense_stream_kernel<true, 4><<<N / 16, 256, lds, st>>>(a, w, c, T, N, K);
-            else dense_stream_kernel<false, 4><<<N / 16, 256, lds, st>>>(a, w, c, T, N, K);
-        }
+        if (K % 4096 == 0 && K >= 8192)  // 8 waves
+            dense_stream_kernel<OUT, 8><<<N / 16, 512, lds, st>>>(a, w, c, T, N, K, g);
+        else
+            dense_stream_kernel<OUT, 4><<<N / 16, 256, lds, st>>>(a, w, c, T, N, K, g);
         return hipGetLastError();
     }
     if (N % kGemmTile != 0 || K % 32 != 0) return hipErrorInvalidValue;
     const int tiles_m = (T + kGemmTile - 1) / kGemmTile, tiles_n = N / kGemmTile;
     const int64_t grid = 8 * (((int64_t)tiles_m * tiles_n + 7) / 8);
-    if (c_fp32)
-        dense_gemm_kernel<true><<<(unsigned)grid, 512, 0, st>>>(a, w, c, T, N, K, tiles_m, tiles_n);
-    else
-        dense_gemm_kernel<false><<<(unsigned)grid, 512, 0, st>>>(a, w, c, T, N, K, tiles_m, tiles_n);
+    dense_gemm_kernel<OUT><<<(unsigned)grid, 512, 0, st>>>(a, w, c, T, N, K, tiles_m, tiles_n, g);
     return hipGetLastError();
 }
 
-// 8 columns per thread: x (16 B), f (32 B), alpha, beta (32 B each) in,
-// 16 B out.
-__global__ __launch_bounds__(256) void gate_kernel(const uint16_t *x, const float *__restrict__ f,
-                                                   const float *__restrict__ alpha,
-                                                   const float *__restrict__ beta, uint16_t *s_out,
-                                                   int64_t n8, int D)
+hipError_t launch_dense(const uint16_t *a, const uint16_t *w, void *c, int out, int T, int N, int K,
+                        hipStream_t st, const DenseGate &g)
 {
-    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (q >= n8) return;
-    const int c0 = (int)((q * 8) % D);
-    const uint4 xv = reinterpret_cast<const uint4 *>(x)[q];
-    const float4 f0 = reinterpret_cast<const float4 *>(f)[2 * q];
-    const float4 f1 = reinterpret_cast<const float4 *>(f)[2 * q + 1];
-    const float4 a0 = *reinterpret_cast<const float4 *>(alpha + c0);
-    const float4 a1 = *reinterpret_cast<const float4 *>(alpha + c0 + 4);
-    const float4 b0 = *reinterpret_cast<const float4 *>(beta + c0);
-    const float4 b1 = *reinterpret_cast<const float4 *>(beta + c0 + 4);
-    const float fv[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
-    const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-    const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-    const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
-    uint32_t ow[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const float s0 = fmaf(bv[2 * i], fv[2 * i], av[2 * i] * __uint_as_float(xw[i] << 16));
-        const float s1 = fmaf(bv[2 * i + 1], fv[2 * i + 1], av[2 * i + 1] * __uint_as_float(xw[i] & 0xFFFF0000u));
-        ow[i] = (uint32_t)f32_to_bf16(s0) | (uint32_t)f32_to_bf16(s1) << 16;
-    }
-    reinterpret_cast<uint4 *>(s_out)[q] = make_uint4(ow[0], ow[1], ow[2], ow[3]);
-}
-
-hipError_t launch_gate(const uint16_t *x, const float *f, const float *alpha, const float *beta,
-                       uint16_t *s_out, int64_t T, int D, hipStream_t st)
-{
-    const int64_t n8 = T * D / 8;
-    gate_kernel<<<(unsigned)((n8 + 255) / 256), 256, 0, st>>>(x, f, alpha, beta, s_out, n8, D);
-    return hipGetLastError();
+    if (out == kDenseGate && (!g.x || !g.alpha || !g.beta)) return hipErrorInvalidValue;
+    if (out == kDenseF32) return launch_dense_out<kDenseF32>(a, w, c, T, N, K, st, g);
+    if (out == kDenseGate) return launch_dense_out<kDenseGate>(a, w, c, T, N, K, st, g);
+    return launch_dense_out<kDenseBf16>(a, w, c, T, N, K, st, g);
 }
 
 }  // namespace moe
