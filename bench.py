@@ -208,15 +208,15 @@ def make_latent_sets(name, nsets, device):
 GATE_UP_KERNEL = {
     "decode1": "gemm1_stream_kernel (gate/up + SwiGLU, persistent, MX MFMA)",
     "decode4": "gemm1_stream_kernel (gate/up + SwiGLU, persistent, MX MFMA)",
-    "prefill": "gemm_mxw_kernel<true> (gate/up + SwiGLU, 128x512 tiles, MX MFMA)",
-    "skewed": "gemm_mxw_kernel<true> (gate/up + SwiGLU, 128x512 tiles, MX MFMA)",
-    "stack": "gemm_mxw_kernel<true> (gate/up + SwiGLU, 128x512 tiles, MX MFMA)",
-    "ep753": "gemm_mxw_kernel<true> (gate/up + SwiGLU, 128x512 tiles, MX MFMA)",
-    "ep3012": "gemm_mxw_kernel<true> (gate/up + SwiGLU, 128x512 tiles, MX MFMA)",
+    "prefill": "gemm_mxw_kernel<true, 128> (gate/up + SwiGLU, 128x512 tiles, MX MFMA)",
+    "skewed": "gemm_mxw_kernel<true, 128> (gate/up + SwiGLU, 128x512 tiles, MX MFMA)",
+    "stack": "gemm_mxw_kernel<true, 128> (gate/up + SwiGLU, 128x512 tiles, MX MFMA)",
+    "ep753": "gemm_mxw_kernel<true, 64> (gate/up + SwiGLU, 64x512 tiles, three stages, MX MFMA)",
+    "ep3012": "gemm_mxw_kernel<true, 128> (gate/up + SwiGLU, 128x512 tiles, MX MFMA)",
     "latent4": "gemm1_stream_kernel (gate/up + SwiGLU, persistent, MX MFMA)",
-    "latent_prefill": "gemm_mxw_kernel<true> (gate/up + SwiGLU, 128x512 tiles, MX MFMA)",
+    "latent_prefill": "gemm_mxw_kernel<true, 128> (gate/up + SwiGLU, 128x512 tiles, MX MFMA)",
     "block4": "gemm1_stream_kernel (gate/up + SwiGLU, persistent, MX MFMA)",
-    "block_prefill": "gemm_mxw_kernel<true> (gate/up + SwiGLU, 128x512 tiles, MX MFMA)",
+    "block_prefill": "gemm_mxw_kernel<true, 128> (gate/up + SwiGLU, 128x512 tiles, MX MFMA)",
     "nv4": "gemm1_stream_kernel<4, true> (gate/up + SwiGLU, persistent, fp16 MFMA, 16-block weights)",
     "nv_prefill": "gemm_nv_kernel<true> (gate/up + SwiGLU, 192x256 tiles, fp16 MFMA, 16-block weights)",
 }

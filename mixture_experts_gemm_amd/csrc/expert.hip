@@ -678,30 +678,34 @@ __global__ __launch_bounds__(512) void gemm_mx_kernel(const MxArgs pa)
 }
 
 // =========================================================================
-// Wide MX tiled kernel (prefill): 128 grouped rows x 512 weight rows (two
+// Wide MX tiled kernel (prefill): MR grouped rows x 512 weight rows (two
 // packed weight tiles) per workgroup, all of K.  The activations arrive as
 // three FP6 E2M3 parts per value (split_e2m3x3_block), so each 16x16x128
 // block takes three scaled MFMAs that issue at twice the FP8 rate: 3/4 of
 // the matrix-core time of two FP8 parts, for 304 instead of 264 activation
-// bytes per row and chunk.  Two-stage LDS ring (72 KB a stage) filled by
-// direct-to-LDS loads: chunk kc+1 is in flight while chunk kc is multiplied.
+// bytes per row and chunk.  LDS ring filled by direct-to-LDS loads: 128-row
+// tiles take two stages of 72 KB (chunk kc+1 in flight while chunk kc is
+// multiplied), 64-row tiles three of 53 KB (chunks kc+1 and kc+2 in flight:
+// few rows per expert make the multiply short next to the weight loads).
 // A row's 304-byte record is copied whole; 304 = 76 dwords puts the 16 rows
 // of a row block on distinct LDS banks.  8 waves as 2 (rows) x 4 (columns):
-// each wave owns 64 rows x 128 columns (4 x 8 blocks of 16x16).  Used when
-// the matrix has an even number of 256-row weight tiles.
+// each wave owns MR/2 rows x 128 columns (MR/32 x 8 blocks of 16x16).  Used
+// when the matrix has an even number of 256-row weight tiles.
 // =========================================================================
-template <bool GATE_UP>
+template <bool GATE_UP, int MR>
 __global__ __launch_bounds__(512) void gemm_mxw_kernel(const MxArgs pa)
 {
-    constexpr int NW = 8, MB = 4;
-    constexpr int AU = kTM * kA6Units;             // 16-byte units of a stage's records
-    constexpr int AL = (AU + 64 * NW - 1) / (64 * NW);  // record loads per wave (5)
+    static_assert(MR == 128 || MR == 64, "128-row tiles on two stages, 64-row tiles on three");
+    constexpr int NW = 8, MB = MR / 32, RH = MR / 2;  // row blocks per wave, rows per wave row
+    constexpr int ST = MR == 128 ? 2 : 3;             // ring stages
+    constexpr int AU = MR * kA6Units;                 // 16-byte units of a stage's records
+    constexpr int AL = (AU + 64 * NW - 1) / (64 * NW);  // record loads per wave (5 or 3)
     constexpr int BU = 2 * kTN * 4, SU = 2 * kTN / 4;   // weight / scale units of a stage
-    // one pool: two stages during the K loop, the fp32 h tile in the epilogue
-    __shared__ uint4 pool[2 * (AU + BU + SU)];
+    // one pool: the stages during the K loop, the fp32 h tile in the epilogue
+    __shared__ uint4 pool[ST * (AU + BU + SU)];
     uint4 *const As0 = pool, *const As1 = pool + AU;
-    uint4 *const Bs0 = pool + 2 * AU, *const Bs1 = pool + 2 * AU + BU;
-    uint32_t *const Ss0 = reinterpret_cast<uint32_t *>(pool + 2 * AU + 2 * BU);
+    uint4 *const Bs0 = pool + ST * AU, *const Bs1 = Bs0 + BU;
+    uint32_t *const Ss0 = reinterpret_cast<uint32_t *>(pool + ST * (AU + BU));
     uint32_t *const Ss1 = Ss0 + 2 * kTN;
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -719,17 +723,21 @@ __global__ __launch_bounds__(512) void gemm_mxw_kernel(const MxArgs pa)
 
     // ---- load assignment ----------------------------------------------------
     // Records: load i of this wave fills stage unit P = 64*(8i + wv) + lane,
-    // unit P % 19 of row P / 19.  Rows past nrows are not loaded (their LDS
-    // rows hold stale data; they only feed output rows that are never
-    // stored).  Every wait below is vmcnt(0), so loads skipped this way
-    // cannot upset a count.
+    // unit P % 19 of row P / 19.  Two stages: rows past nrows are not loaded
+    // (their LDS rows hold stale data; they only feed output rows that are
+    // never stored), and every wait is vmcnt(0), so loads skipped this way
+    // cannot upset a count.  Three stages: the waits leave the next chunk's
+    // loads in flight by count, so every wave issues a fixed number of
+    // whole-wave loads (rows past nrows re-read row 0 and are never stored).
+    const int wvu = __builtin_amdgcn_readfirstlane(wv);
+    const int na = ST == 2 ? AL : (64 * (NW * (AL - 1) + wvu) < AU ? AL : AL - 1);
     const uint8_t *asrc[AL];
     bool aload[AL];
 #pragma unroll
     for (int i = 0; i < AL; ++i) {
         const int P = 64 * (NW * i + wv) + lane;
         const int rw = P / kA6Units, u = P - rw * kA6Units;
-        aload[i] = P < AU && rw < tl.nrows;
+        aload[i] = ST == 2 ? (P < AU && rw < tl.nrows) : i < na;
         asrc[i] = pa.a6 + (src_row(aload[i] ? rw : 0) * nk) * kA6Bytes + u * 16;
     }
     // weight tiles 2np and 2np+1: load i fills unit 64*(8i + wv) + lane of the
@@ -742,7 +750,6 @@ __global__ __launch_bounds__(512) void gemm_mxw_kernel(const MxArgs pa)
     const int qb = 64 * wv + lane;
     const uint8_t *ssrc = v.stile(2 * np + (qb >> 8), 0) + (qb & 255) * 4;
 
-    const int wvu = __builtin_amdgcn_readfirstlane(wv);
     // The loads of a chunk go out in three parts spread over the multiply of
     // the chunk before (activations first, then the two weight tiles), so a
     // wave is not held at the address unit while its MFMAs could be issuing.
@@ -764,11 +771,11 @@ __global__ __launch_bounds__(512) void gemm_mxw_kernel(const MxArgs pa)
     };
 
     // ---- compute assignment -------------------------------------------------
-    // rows 64*wm.., columns 128*wn.. of the 512; waves w and w+4 share a SIMD
+    // rows RH*wm.., columns 128*wn.. of the 512; waves w and w+4 share a SIMD
     // and own different row halves, so a short tile's MFMAs spread over all four
     const int wm = wv >> 2, wn = wv & 3;
     const int n16 = lane & 15, g = lane >> 4;
-    int mb_act = (tl.nrows - wm * 64 + 15) >> 4;
+    int mb_act = (tl.nrows - wm * RH + 15) >> 4;
     mb_act = mb_act < 0 ? 0 : (mb_act > MB ? MB : mb_act);
 
     floatx4_t acc[MB][8];
@@ -794,7 +801,7 @@ __global__ __launch_bounds__(512) void gemm_mxw_kernel(const MxArgs pa)
         // stride is conflict-free, measured)
         auto read_a = [&](int mb) {
             AFr f;
-            const int row = wm * 64 + mb * 16 + n16;
+            const int row = wm * RH + mb * 16 + n16;
             const uint2 *rp = reinterpret_cast<const uint2 *>(As + row * kA6Units);
 #pragma unroll
             for (int p = 0; p < 3; ++p)
@@ -856,16 +863,38 @@ __global__ __launch_bounds__(512) void gemm_mxw_kernel(const MxArgs pa)
         }
     };
 
-    // ---- pipeline: two slots; the barrier before chunk kc also waits for this
-    // wave's LDS reads of chunk kc-1, whose slot chunk kc+1 then refills, and
-    // for all of this wave's loads of chunk kc ----------------------------------
-    for (int part = 0; part < 3; ++part) issue_part(part, 0, As0, Bs0, Ss0);
-    for (int kc = 0; kc < nk; kc += 2) {
-        phase_sync<0>();
-        compute(As0, Bs0, Ss0, kc + 1 < nk ? kc + 1 : -1, As1, Bs1, Ss1);
-        if (kc + 1 < nk) {
+    if constexpr (ST == 2) {
+        // ---- pipeline: two slots; the barrier before chunk kc also waits for
+        // this wave's LDS reads of chunk kc-1, whose slot chunk kc+1 then
+        // refills, and for all of this wave's loads of chunk kc -------------
+        for (int part = 0; part < 3; ++part) issue_part(part, 0, As0, Bs0, Ss0);
+        for (int kc = 0; kc < nk; kc += 2) {
             phase_sync<0>();
-            compute(As1, Bs1, Ss1, kc + 2 < nk ? kc + 2 : -1, As0, Bs0, Ss0);
+            compute(As0, Bs0, Ss0, kc + 1 < nk ? kc + 1 : -1, As1, Bs1, Ss1);
+            if (kc + 1 < nk) {
+                phase_sync<0>();
+                compute(As1, Bs1, Ss1, kc + 2 < nk ? kc + 2 : -1, As0, Bs0, Ss0);
+            }
+        }
+    } else {
+        // ---- pipeline: three slots, two chunks ahead.  A wave issues na + 5
+        // loads a chunk (records, two weight pairs, the scales), so the wait
+        // before chunk kc leaves chunk kc+1's loads in flight and no more;
+        // the barrier also waits for every wave's LDS reads of chunk kc-1,
+        // whose slot chunk kc+2 then refills --------------------------------
+        static_assert(AL == 3, "the waits below count 3 or 2 record loads a wave");
+        for (int part = 0; part < 3; ++part) issue_part(part, 0, As0, Bs0, Ss0);
+        if (nk > 1)
+            for (int part = 0; part < 3; ++part) issue_part(part, 1, As1, Bs1, Ss1);
+        int slot = 0;
+        for (int kc = 0; kc < nk; ++kc) {
+            if (kc + 1 >= nk) phase_sync<0>();
+            else if (na == AL) phase_sync<AL + 5>();
+            else phase_sync<AL + 4>();
+            const int nslot = slot == 0 ? 2 : slot - 1;  // (kc + 2) % 3
+            compute(As0 + slot * AU, Bs0 + slot * BU, Ss0 + slot * 2 * kTN, kc + 2 < nk ? kc + 2 : -1,
+                    As0 + nslot * AU, Bs0 + nslot * BU, Ss0 + nslot * 2 * kTN);
+            slot = slot == 2 ? 0 : slot + 1;
         }
     }
 
@@ -889,7 +918,7 @@ __global__ __launch_bounds__(512) void gemm_mxw_kernel(const MxArgs pa)
                 const int pos = ((c ^ ((c >> 3) & 7)) << 2) | (f & 3);
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr) {
-                    const int row = wm * 64 + mb * 16 + g * 4 + rr;
+                    const int row = wm * RH + mb * 16 + g * 4 + rr;
                     hs[row * HS + pos] = silu(acc[mb][hb][rr]) * acc[mb][hb + 4][rr];
                 }
             }
@@ -931,7 +960,7 @@ __global__ __launch_bounds__(512) void gemm_mxw_kernel(const MxArgs pa)
             for (int hb = 0; hb < 4; ++hb)
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr) {
-                    const int row = wm * 64 + mb * 16 + g * 4 + rr;
+                    const int row = wm * RH + mb * 16 + g * 4 + rr;
                     if (row < tl.nrows)
                         pa.out[(int64_t)(tl.row0 + row) * F + fbase + hb * 16 + n16] =
                             f32_to_bf16(silu(acc[mb][hb][rr]) * acc[mb][hb + 4][rr]);
@@ -946,7 +975,7 @@ __global__ __launch_bounds__(512) void gemm_mxw_kernel(const MxArgs pa)
             if (mb >= mb_act) continue;
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
-                const int row = wm * 64 + mb * 16 + g * 4 + rr;
+                const int row = wm * RH + mb * 16 + g * 4 + rr;
                 float ss0 = 0.f, ss1 = 0.f;
 #pragma unroll
                 for (int nb = 0; nb < 4; ++nb) ss0 += acc[mb][nb][rr] * acc[mb][nb][rr];
@@ -1552,7 +1581,10 @@ hipError_t launch_gemm1(const Shape &s, const Plan &p, const Workspace &ws, cons
         if (wide_gate_up(s)) {
             // h goes straight to the down kernel's FP6 records when that kernel is wide
             if (wide_down(s)) pa.h6 = ws.ha6;
-            hipExtLaunchKernelGGL(gemm_mxw_kernel<true>, grid, dim3(512), 0, st, ev0, ev1, 0, pa);
+            if (p.tile_rows == 64)
+                hipExtLaunchKernelGGL(gemm_mxw_kernel<true, 64>, grid, dim3(512), 0, st, ev0, ev1, 0, pa);
+            else
+                hipExtLaunchKernelGGL(gemm_mxw_kernel<true, 128>, grid, dim3(512), 0, st, ev0, ev1, 0, pa);
         } else {
             hipExtLaunchKernelGGL(gemm_mx_kernel<true>, grid, dim3(512), 0, st, ev0, ev1, 0, pa);
         }
@@ -1597,7 +1629,8 @@ hipError_t launch_gemm2(const Shape &s, const Plan &p, const Workspace &ws, cons
         MxArgs pa{ws.hhi, ws.hlo, ws.hshi, ws.hslo, ws.ha6, nullptr, ws.tiles, nullptr, ws.ntiles, wpk,
                   sc, ws.o, ws.ssq, s.d, s.F, s.k, wide_down(s) ? s.d / 512 : s.d / 256, nullptr};
         const int64_t grid = 8 * ((max_tiles(s, p.tile_rows) * pa.ntn + 7) / 8);
-        if (wide_down(s)) gemm_mxw_kernel<false><<<(unsigned)grid, 512, 0, st>>>(pa);
+        if (wide_down(s) && p.tile_rows == 64) gemm_mxw_kernel<false, 64><<<(unsigned)grid, 512, 0, st>>>(pa);
+        else if (wide_down(s)) gemm_mxw_kernel<false, 128><<<(unsigned)grid, 512, 0, st>>>(pa);
         else gemm_mx_kernel<false><<<(unsigned)grid, 512, 0, st>>>(pa);
     } else {
         const int wgs = s.d / 64;

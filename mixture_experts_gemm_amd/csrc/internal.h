@@ -104,6 +104,11 @@ constexpr int kStreamRows = 2;
 // fewer times (measured: 753 rows over 32 experts, 586 -> 301 us).
 constexpr int kTiledMinRows = 16;
 
+// Average rows per expert below which the wide kernels take 64-row tiles on
+// a three-stage ring: with so few rows a workgroup's multiply is short next
+// to its loads, and a third stage keeps two chunks of weights in flight.
+constexpr int kShortTileMaxRows = 48;
+
 struct Plan {
     bool tiled;
     bool stream;    // persistent streaming gate/up kernel (decode)
@@ -151,6 +156,8 @@ inline Plan make_plan(const Shape &s)
     p.tiled = S >= (int64_t)kTiledMinRows * s.E && s.d % 256 == 0 && s.F % 128 == 0;
     p.stream = !p.tiled && s.d % 2048 == 0 && s.T <= kStreamMaxT;
     p.tile_rows = p.tiled ? 128 : p.stream ? (s.T < kStreamRows ? s.T : kStreamRows) : 16;
+    if (p.tiled && wide_gate_up(s) && wide_down(s) && S < (int64_t)kShortTileMaxRows * s.E)
+        p.tile_rows = 64;
     if (p.tile_rows < 1) p.tile_rows = 1;
     p.ssq_cols = 64;  // both down kernels reduce o^2 over 64-column groups
     p.small_route = s.T <= kChunkTokens && S <= 4096;

@@ -44,6 +44,7 @@ int main()
         }
     // the launch and the workspace's schedule hold the largest tile list of
     // every plan (MXFP4 and the 16-block format)
+    long short_cases = 0;
     const int Ts[] = {16, 64, 200, 753, 3012, 4096, 16384};
     const int ds[] = {256, 768, 2048, 8192};
     const int Fs[] = {128, 384, 1408, 2048, 4096};
@@ -64,9 +65,12 @@ int main()
                             if (p.grid1 < items || p.grid1 % (16 * p.ntn1))
                                 return fail("launch smaller than the items", T, d, F);
                             if (sched_entries(s) < p.grid1) return fail("schedule entries", T, d, F);
+                            if (p.tile_rows == 64) ++short_cases;
                             ++cases;
                         }
                     }
-    std::printf("ok %ld\n", cases);
+    // the sweep reaches the 64-row tiles of shapes with few rows per expert
+    if (short_cases == 0) return fail("no 64-row plan in the sweep", 0, 0, 0);
+    std::printf("ok %ld (%ld with 64-row tiles)\n", cases, short_cases);
     return 0;
 }

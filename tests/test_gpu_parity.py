@@ -565,6 +565,22 @@ def test_other_shapes(T, d, E, k, F, what):
     _check_tokens(L, out, np.arange(T), what)
 
 
+@pytest.mark.parametrize("T,zipf", [(200, False), (300, True), (3012, False)])
+def test_short_tiles(T, zipf):
+    """Few rows per expert with both matrices wide (d = 512, F = 256, E = 16,
+    k = 2: about 25 and 38 rows per expert) run the wide kernels on 64-row
+    tiles with a three-stage ring; the skewed routing cuts its hot experts'
+    segments into several ragged 64-row tiles.  T = 3012 (about 376 rows per
+    expert) is the same shape on 128-row tiles.  Every token compared."""
+    w = synth.custom_workload(T=T, d=512, E=16, k=2, F=256, seed=90 + T % 7, zipf=zipf)
+    L = synth.make_layer(w)
+    _say("short tiles", T, "zipf" if zipf else "uniform")
+    out, dbg = run_layer(L)
+    r = _check_routing(L, dbg, f"short tiles T={T}")
+    _say("short tiles largest segment", int(r["counts"].max()))
+    _check_tokens(L, out, np.arange(T), f"short tiles T={T}")
+
+
 # ------------------------------------------------------ the workspace's previous contents
 
 @pytest.mark.parametrize("name,T", [("tiny", 64), ("decode4", None), ("prefill", 512)])
