@@ -327,32 +327,100 @@ __device__ __forceinline__ uint64_t wave_max_key_split(uint64_t key)
 }
 
 
+// The k rounds: each takes the wave's largest head key and the owning lane
+// pops it; choice j is parked in mine[j / 64] of lane j % 64.  MS = 1 when
+// k <= 64 (every choice in one register).
+template <int SLOTS, int MS>
+__device__ __forceinline__ void topk_rounds(uint64_t (&key)[SLOTS], uint64_t (&mine)[MS], int k, int lane)
+{
+    const uint64_t none = topk_key(-INFINITY, kNone);
+#pragma unroll
+    for (int q = 0; q < MS; ++q) mine[q] = none;
+    for (int j = 0; j < k; ++j) {
+        const uint64_t best = wave_max_key_split(key[0]);
+        if (key[0] == best) {  // keys are distinct: exactly the owner lane
+#pragma unroll
+            for (int q = 0; q + 1 < SLOTS; ++q) key[q] = key[q + 1];
+            key[SLOTS - 1] = none;
+        }
+        if (MS == 1) {
+            if (j == lane) mine[0] = best;
+        } else {
+#pragma unroll
+            for (int q = 0; q < MS; ++q)
+                if ((j >> 6) == q && (j & 63) == lane) mine[q] = best;
+        }
+    }
+}
+
+// Softmax over the parked choices (relative to the first, the largest) and
+// the stores of choice j = lane + 64q.
+template <int MS>
+__device__ __forceinline__ void topk_store(const uint64_t (&mine)[MS], int k, int lane,
+                                           int32_t *__restrict__ ids_out, float *__restrict__ w_out,
+                                           int32_t *sid_out)
+{
+    const uint32_t th = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(mine[0] >> 32), 0);
+    const float top0 = key_score((uint64_t)th << 32);
+    float z = 0.f;
+    float ex[MS];
+#pragma unroll
+    for (int q = 0; q < MS; ++q) {
+        ex[q] = (lane + 64 * q < k) ? expf(key_score(mine[q]) - top0) : 0.f;
+        z += ex[q];
+    }
+    z = wave_sum(z);
+    const float inv = 1.0f / z;
+#pragma unroll
+    for (int q = 0; q < MS; ++q) {
+        const int j = lane + 64 * q;
+        if (j < k) {
+            const int e = key_id(mine[q]);
+            ids_out[j] = e;
+            w_out[j] = ex[q] * inv;
+            if (sid_out) sid_out[j] = e;
+        }
+    }
+}
+
 // l: the token's scores, or its first partial-score plane when the router
 // split its sums over nsplit slices of d (planes `stride` floats apart,
-// added in slice order).
+// added in slice order).  The loads of every slot go out together (one
+// round trip for a single plane; PG planes of all slots at a time
+// otherwise).
 template <int SLOTS>
-__device__ void topk_row(const float *__restrict__ l, int E, int k, int32_t *__restrict__ ids_out,
-                         float *__restrict__ w_out, int32_t *sid_out, int lane, int nsplit,
-                         int64_t stride)
+__device__ __forceinline__ void topk_row(const float *__restrict__ l, int E, int k,
+                                         int32_t *__restrict__ ids_out, float *__restrict__ w_out,
+                                         int32_t *sid_out, int lane, int nsplit, int64_t stride)
 {
+    constexpr int PG = SLOTS <= 4 ? 8 : 2;
+    float x[SLOTS];
+    if (nsplit == 1) {
+#pragma unroll
+        for (int q = 0; q < SLOTS; ++q) x[q] = l[min(lane + 64 * q, E - 1)];
+    } else {
+#pragma unroll
+        for (int q = 0; q < SLOTS; ++q) x[q] = 0.f;
+        for (int sp = 0; sp < nsplit; sp += PG) {
+            float v[SLOTS][PG];
+#pragma unroll
+            for (int i = 0; i < PG; ++i) {
+                const float *pl = l + (int64_t)min(sp + i, nsplit - 1) * stride;
+#pragma unroll
+                for (int q = 0; q < SLOTS; ++q) v[q][i] = pl[min(lane + 64 * q, E - 1)];
+            }
+#pragma unroll
+            for (int q = 0; q < SLOTS; ++q)
+#pragma unroll
+                for (int i = 0; i < PG; ++i)
+                    if (sp + i < nsplit) x[q] = (sp + i == 0) ? v[q][i] : x[q] + v[q][i];
+        }
+    }
     uint64_t key[SLOTS];
 #pragma unroll
     for (int q = 0; q < SLOTS; ++q) {
         const int e = lane + 64 * q;
-        float x = -INFINITY;
-        if (e < E) {
-            // planes in groups of 8 loads issued together, added in slice order
-            x = 0.f;
-            for (int sp = 0; sp < nsplit; sp += 8) {
-                float v[8];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) v[i] = l[(int64_t)min(sp + i, nsplit - 1) * stride + e];
-#pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    if (sp + i < nsplit) x = (sp + i == 0) ? v[i] : x + v[i];
-            }
-        }
-        key[q] = topk_key(x, e < E ? e : kNone);
+        key[q] = topk_key(e < E ? x[q] : -INFINITY, e < E ? e : kNone);
     }
 #pragma unroll
     for (int pass = 0; pass < SLOTS; ++pass)
@@ -363,42 +431,14 @@ __device__ void topk_row(const float *__restrict__ l, int E, int k, int32_t *__r
                 key[q] = key[q + 1];
                 key[q + 1] = t;
             }
-    const uint64_t none = topk_key(-INFINITY, kNone);
-    uint64_t mine[SLOTS];
-#pragma unroll
-    for (int q = 0; q < SLOTS; ++q) mine[q] = none;
-    uint64_t top = none;
-    for (int j = 0; j < k; ++j) {
-        const uint64_t best = wave_max_key_split(key[0]);
-        if (key[0] == best) {  // keys are distinct: exactly the owner lane
-#pragma unroll
-            for (int q = 0; q + 1 < SLOTS; ++q) key[q] = key[q + 1];
-            key[SLOTS - 1] = none;
-        }
-        if (j == 0) top = best;
-#pragma unroll
-        for (int q = 0; q < SLOTS; ++q)
-            if ((j >> 6) == q && (j & 63) == lane) mine[q] = best;
-    }
-    const float top0 = key_score(top);
-    float z = 0.f;
-    float ex[SLOTS];
-#pragma unroll
-    for (int q = 0; q < SLOTS; ++q) {
-        ex[q] = (lane + 64 * q < k) ? expf(key_score(mine[q]) - top0) : 0.f;
-        z += ex[q];
-    }
-    z = wave_sum(z);
-    const float inv = 1.0f / z;
-#pragma unroll
-    for (int q = 0; q < SLOTS; ++q) {
-        const int j = lane + 64 * q;
-        if (j < k) {
-            const int e = key_id(mine[q]);
-            ids_out[j] = e;
-            w_out[j] = ex[q] * inv;
-            if (sid_out) sid_out[j] = e;
-        }
+    if (SLOTS == 1 || k <= 64) {
+        uint64_t mine[1];
+        topk_rounds<SLOTS, 1>(key, mine, k, lane);
+        topk_store<1>(mine, k, lane, ids_out, w_out, sid_out);
+    } else {
+        uint64_t mine[SLOTS];
+        topk_rounds<SLOTS, SLOTS>(key, mine, k, lane);
+        topk_store<SLOTS>(mine, k, lane, ids_out, w_out, sid_out);
     }
 }
 
@@ -420,6 +460,33 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ sco
 // in LDS, by 256 threads (one pass, two barriers); returns both totals.
 // Integer, so order-free.
 // ---------------------------------------------------------------------------
+// Inclusive prefix sums of a and b over the wave: shift-and-add steps by
+// DPP row_shr inside rows of 16 lanes (lanes shifted in from outside the
+// row read 0), then the totals of the earlier rows (lanes 15, 31, 47) added.
+template <int N>
+__device__ __forceinline__ int row_shr_add(int v)
+{
+    return v + __builtin_amdgcn_update_dpp(0, v, 0x110 + N, 0xF, 0xF, false);
+}
+__device__ __forceinline__ void wave_incl_scan2(int &a, int &b, int lane)
+{
+    a = row_shr_add<1>(a);
+    b = row_shr_add<1>(b);
+    a = row_shr_add<2>(a);
+    b = row_shr_add<2>(b);
+    a = row_shr_add<4>(a);
+    b = row_shr_add<4>(b);
+    a = row_shr_add<8>(a);
+    b = row_shr_add<8>(b);
+    const int a15 = __builtin_amdgcn_readlane(a, 15), a31 = __builtin_amdgcn_readlane(a, 31),
+              a47 = __builtin_amdgcn_readlane(a, 47);
+    const int b15 = __builtin_amdgcn_readlane(b, 15), b31 = __builtin_amdgcn_readlane(b, 31),
+              b47 = __builtin_amdgcn_readlane(b, 47);
+    const int row = lane >> 4;
+    a += (row >= 1 ? a15 : 0) + (row >= 2 ? a31 : 0) + (row >= 3 ? a47 : 0);
+    b += (row >= 1 ? b15 : 0) + (row >= 2 ? b31 : 0) + (row >= 3 ? b47 : 0);
+}
+
 __device__ int2 block_exclusive_scan2(int32_t *a, int32_t *b, int n, int32_t (*wtot)[4])
 {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -434,14 +501,7 @@ __device__ int2 block_exclusive_scan2(int32_t *a, int32_t *b, int n, int32_t (*w
         sb += vb[q];
     }
     int ia = sa, ib = sb;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int ya = __shfl_up(ia, off), yb = __shfl_up(ib, off);
-        if (lane >= off) {
-            ia += ya;
-            ib += yb;
-        }
-    }
+    wave_incl_scan2(ia, ib, lane);
     if (lane == 63) {
         wtot[0][wv] = ia;
         wtot[1][wv] = ib;
