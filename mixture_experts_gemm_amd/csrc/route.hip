@@ -742,6 +742,54 @@ __global__ __launch_bounds__(256) void group_mask_kernel(const int32_t *__restri
     for (int e = threadIdx.x; e < E; e += 256) masks[(int64_t)c * E + e] = mask[e];
 }
 
+// Rows of expert e in chunks c0 .. c0+B-1 (clamped loads, value masked
+// after: a conditional load would end its own basic block with a wait).
+template <int B>
+__device__ __forceinline__ void chunk_popcounts(const uint64_t *__restrict__ masks, int E, int e,
+                                                int nchunks, int c0, int (&pc)[B])
+{
+    uint64_t mv[B];
+#pragma unroll
+    for (int i = 0; i < B; ++i) mv[i] = masks[(int64_t)min(c0 + i, nchunks - 1) * E + e];
+#pragma unroll
+    for (int i = 0; i < B; ++i) pc[i] = c0 + i < nchunks ? __popcll(mv[i]) : 0;
+}
+
+// One expert per thread (E <= 256) and all chunks in one batch of B: the
+// per-chunk row counts stay in registers from the count pass to the base
+// pass, so the masks are read once.
+template <int B>
+__device__ __forceinline__ void group_scan_resident(const uint64_t *__restrict__ masks,
+                                                    int32_t *__restrict__ chunk_base, int32_t *cnt,
+                                                    int32_t *toff, int32_t (*wtot)[4],
+                                                    int32_t *__restrict__ counts,
+                                                    int32_t *__restrict__ offsets, Tile *__restrict__ tiles,
+                                                    int32_t *__restrict__ ntiles, int E, int nchunks,
+                                                    int tile_rows, const Sched &sc)
+{
+    const int tid = threadIdx.x;
+    int pc[B];
+    if (tid < E) {
+        chunk_popcounts<B>(masks, E, tid, nchunks, 0, pc);
+        int run = 0;
+#pragma unroll
+        for (int i = 0; i < B; ++i) run += pc[i];
+        cnt[tid] = run;
+    }
+    __syncthreads();
+    int c_own[4];
+    finish_offsets(cnt, toff, wtot, E, tile_rows, counts, offsets, tiles, ntiles, c_own, sc);
+    if (tid < E) {
+        int run = cnt[tid];
+#pragma unroll
+        for (int i = 0; i < B; ++i)
+            if (i < nchunks) {
+                chunk_base[(int64_t)i * E + tid] = run;
+                run += pc[i];
+            }
+    }
+}
+
 __global__ __launch_bounds__(256) void group_scan_kernel(
     const uint64_t *__restrict__ masks, int32_t *__restrict__ chunk_base,
     int32_t *__restrict__ counts, int32_t *__restrict__ offsets, Tile *__restrict__ tiles,
@@ -750,6 +798,16 @@ __global__ __launch_bounds__(256) void group_scan_kernel(
     __shared__ int32_t cnt[1024];
     __shared__ int32_t toff[1024];
     __shared__ int32_t wtot[2][4];
+    if (E <= 256 && nchunks <= 16) {
+        group_scan_resident<16>(masks, chunk_base, cnt, toff, wtot, counts, offsets, tiles, ntiles, E,
+                                nchunks, tile_rows, sc);
+        return;
+    }
+    if (E <= 256 && nchunks <= 64) {
+        group_scan_resident<64>(masks, chunk_base, cnt, toff, wtot, counts, offsets, tiles, ntiles, E,
+                                nchunks, tile_rows, sc);
+        return;
+    }
     // two passes over the masks (counts, then bases); loads go out in batches
     // of 64 (all chunks of a 4096-token call at once), so each pass is one
     // round trip to memory per batch rather than a chain of dependent reads
@@ -758,13 +816,10 @@ __global__ __launch_bounds__(256) void group_scan_kernel(
     for (int e = tid; e < E; e += 256) {
         int run = 0;
         for (int c0 = 0; c0 < nchunks; c0 += B) {
-            uint64_t mv[B];
-            // unconditional loads (clamped index, value masked after): a
-            // conditional load would end its own basic block with a wait
+            int pc[B];
+            chunk_popcounts<B>(masks, E, e, nchunks, c0, pc);
 #pragma unroll
-            for (int i = 0; i < B; ++i) mv[i] = masks[(int64_t)min(c0 + i, nchunks - 1) * E + e];
-#pragma unroll
-            for (int i = 0; i < B; ++i) run += c0 + i < nchunks ? __popcll(mv[i]) : 0;
+            for (int i = 0; i < B; ++i) run += pc[i];
         }
         cnt[e] = run;
     }
@@ -774,14 +829,13 @@ __global__ __launch_bounds__(256) void group_scan_kernel(
     for (int e = tid; e < E; e += 256) {
         int run = cnt[e];
         for (int c0 = 0; c0 < nchunks; c0 += B) {
-            uint64_t mv[B];
-#pragma unroll
-            for (int i = 0; i < B; ++i) mv[i] = masks[(int64_t)min(c0 + i, nchunks - 1) * E + e];
+            int pc[B];
+            chunk_popcounts<B>(masks, E, e, nchunks, c0, pc);
 #pragma unroll
             for (int i = 0; i < B; ++i)
                 if (c0 + i < nchunks) {
                     chunk_base[(int64_t)(c0 + i) * E + e] = run;
-                    run += __popcll(mv[i]);
+                    run += pc[i];
                 }
         }
     }
