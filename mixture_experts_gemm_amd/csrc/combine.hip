@@ -28,7 +28,7 @@ constexpr int kCombineCols = 2048;  // columns per workgroup (8 per thread)
 // (the block variant normalises y before its gate).
 enum { kOutGate = 0, kOutBf16 = 1, kOutF32 = 2 };
 template <bool SLOT, int OUT>
-__global__ __launch_bounds__(256) void combine_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SLOT ? 1 : 8))) void combine_kernel(
     const uint16_t *x, const float *__restrict__ wts, const int32_t *__restrict__ inv,
     const uint16_t *__restrict__ o, const float *__restrict__ ssq, const float *__restrict__ alpha,
     const float *__restrict__ beta, uint16_t *s_out, float *y_out, int d, int k, int P, float eps)
@@ -105,14 +105,23 @@ __global__ __launch_bounds__(256) void combine_kernel(
         for (int j = (threadIdx.x >> 4); j < kk; j += 16) {
             const int64_t slot = (int64_t)t * k + j0 + j;
             const int p = SLOT ? (int)slot : inv[slot];
+            const float wj = wts[slot];  // loaded beside inv, not after the sums
+            // lane l adds partials l, l+16, ... in that order; eight loads
+            // go out at a time (clamped index, masked after)
+            const int l = threadIdx.x & 15;
             float ss = 0.f;
             const float *sp = ssq + (int64_t)p * P;
-#pragma unroll 4
-            for (int q = (threadIdx.x & 15); q < P; q += 16) ss += sp[q];
+            for (int q0 = 0; q0 < P; q0 += 128) {
+                float pv[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) pv[i] = sp[min(q0 + 16 * i + l, P - 1)];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) ss += q0 + 16 * i + l < P ? pv[i] : 0.f;
+            }
             ss = sum16(ss);
-            if ((threadIdx.x & 15) == 0) {
+            if (l == 0) {
                 row[j] = p;
-                coef[j] = wts[slot] * (1.0f / sqrtf(ss / (float)d + eps));
+                coef[j] = wj * (1.0f / sqrtf(ss / (float)d + eps));
             }
         }
         __syncthreads();
