@@ -606,8 +606,8 @@ def measured_peaks(device):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
-              "the layer's multi-GPU sharding is described in DESIGN.md but not built", file=sys.stderr)
+        print(f"bench.py: the layer runs on one GPU only (asked for --gpus {args.gpus}); "
+              "sharding it over several GPUs is not implemented", file=sys.stderr)
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():
