@@ -238,6 +238,40 @@ __global__ __launch_bounds__(512) void dense_gemm_kernel(const uint16_t *__restr
             for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = mfma16(as_bf16x8(a[mb]), as_bf16x8(bw[nb]), acc[mb][nb]);
     }
     // lane holds C[token g*4 + r][column m16] of every 16 x 16 block
+    if constexpr (OUT == kDenseGate) {
+        // the gated residual: alpha and beta once per column, and each row
+        // block's 16 x values loaded together before its stores
+        float al[4], be[4];
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+            const int col = N0 + wn * 64 + nb * 16 + m16;
+            al[nb] = gate.alpha[col];
+            be[nb] = gate.beta[col];
+        }
+#pragma unroll
+        for (int mb = 0; mb < 8; ++mb) {
+            uint32_t xv[4][4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = min(M0 + wm * 128 + mb * 16 + g * 4 + r, T - 1);  // rows past T: read, not stored
+#pragma unroll
+                for (int nb = 0; nb < 4; ++nb) xv[r][nb] = gate.x[(int64_t)t * N + N0 + wn * 64 + nb * 16 + m16];
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = M0 + wm * 128 + mb * 16 + g * 4 + r;
+                if (t >= T) continue;
+#pragma unroll
+                for (int nb = 0; nb < 4; ++nb) {
+                    const int col = N0 + wn * 64 + nb * 16 + m16;
+                    const float xf = __uint_as_float(xv[r][nb] << 16);
+                    static_cast<uint16_t *>(C)[(int64_t)t * N + col] =
+                        f32_to_bf16(fmaf(be[nb], acc[mb][nb][r], al[nb] * xf));
+                }
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
