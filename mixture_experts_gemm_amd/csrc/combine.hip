@@ -282,6 +282,119 @@ __global__ __launch_bounds__(256) void postnorm_gate_kernel(
     }
 }
 
+// The block's combine and post-norm in one pass, for rows of at most
+// kBlockPasses * 2048 = kBlockFusedMaxD columns and at most kBlockFusedMaxK
+// slots: one workgroup per token row.  Every slot's
+// coefficient w / sqrt(mean(o^2) + eps) first (as combine_kernel), then y =
+// sum over the slots of coef * o in slot order (the same sums as
+// combine_kernel's), kept in registers, 8 columns per thread and pass; the
+// row's sum of squares of y in a fixed order (block_row_sumsq); then
+// s_out = bf16(alpha * x + beta * y * r * gamma).  s_out may be x: each
+// thread reads its x elements before writing them.
+constexpr int kBlockPasses = 8;
+static_assert(kBlockPasses * 2048 == kBlockFusedMaxD, "one pass is 256 threads x 8 columns");
+
+template <bool SLOT>
+__global__ __launch_bounds__(256) void combine_postnorm_kernel(
+    const uint16_t *x, const float *__restrict__ wts, const int32_t *__restrict__ inv,
+    const uint16_t *__restrict__ o, const float *__restrict__ ssq, const float *__restrict__ gamma,
+    const float *__restrict__ alpha, const float *__restrict__ beta, uint16_t *s_out, int d, int k, int P,
+    float eps)
+{
+    __shared__ float coef[kBlockFusedMaxK];
+    __shared__ int32_t row[kBlockFusedMaxK];
+    const int t = blockIdx.x;
+    for (int j = threadIdx.x >> 4; j < k; j += 16) {
+        const int64_t slot = (int64_t)t * k + j;
+        const int p = SLOT ? (int)slot : inv[slot];
+        const float wj = wts[slot];
+        // lane l adds partials l, l+16, ... in that order, eight loads at a time
+        const int l = threadIdx.x & 15;
+        float ss = 0.f;
+        const float *sp = ssq + (int64_t)p * P;
+        for (int q0 = 0; q0 < P; q0 += 128) {
+            float pv[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) pv[i] = sp[min(q0 + 16 * i + l, P - 1)];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) ss += q0 + 16 * i + l < P ? pv[i] : 0.f;
+        }
+        ss = sum16(ss);
+        if (l == 0) {
+            row[j] = p;
+            coef[j] = wj * (1.0f / sqrtf(ss / (float)d + eps));
+        }
+    }
+    __syncthreads();
+    float y[kBlockPasses][8];
+    float part = 0.f;
+#pragma unroll
+    for (int ps = 0; ps < kBlockPasses; ++ps) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) y[ps][i] = 0.f;
+        const int c0 = ps * 2048 + threadIdx.x * 8;
+        if (c0 >= d) continue;
+        for (int j0 = 0; j0 < k; j0 += kSlotBatch) {
+            // up to kSlotBatch o rows in flight at once (clamped index, masked)
+            uint4 ov[kSlotBatch];
+#pragma unroll
+            for (int jj = 0; jj < kSlotBatch; ++jj)
+                ov[jj] = *reinterpret_cast<const uint4 *>(o + (int64_t)row[min(j0 + jj, k - 1)] * d + c0);
+#pragma unroll
+            for (int jj = 0; jj < kSlotBatch; ++jj) {
+                if (j0 + jj >= k) break;
+                const float cj = coef[j0 + jj];
+                const uint32_t ow[4] = {ov[jj].x, ov[jj].y, ov[jj].z, ov[jj].w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    y[ps][2 * i] = fmaf(cj, __uint_as_float(ow[i] << 16), y[ps][2 * i]);
+                    y[ps][2 * i + 1] = fmaf(cj, __uint_as_float(ow[i] & 0xFFFF0000u), y[ps][2 * i + 1]);
+                }
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) part = fmaf(y[ps][i], y[ps][i], part);
+    }
+    const float r = 1.0f / sqrtf(block_row_sumsq(part) / (float)d + eps);
+#pragma unroll
+    for (int ps = 0; ps < kBlockPasses; ++ps) {
+        const int c0 = ps * 2048 + threadIdx.x * 8;
+        if (c0 >= d) continue;
+        const uint4 xv = *reinterpret_cast<const uint4 *>(x + (int64_t)t * d + c0);
+        const float4 g0 = *reinterpret_cast<const float4 *>(gamma + c0), g1 = *reinterpret_cast<const float4 *>(gamma + c0 + 4);
+        const float4 a0 = *reinterpret_cast<const float4 *>(alpha + c0), a1 = *reinterpret_cast<const float4 *>(alpha + c0 + 4);
+        const float4 b0 = *reinterpret_cast<const float4 *>(beta + c0), b1 = *reinterpret_cast<const float4 *>(beta + c0 + 4);
+        const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+        const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+        const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+        const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+        uint32_t ow[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float s0 = fmaf(bv[2 * i], y[ps][2 * i] * r * gv[2 * i], av[2 * i] * __uint_as_float(xw[i] << 16));
+            const float s1 = fmaf(bv[2 * i + 1], y[ps][2 * i + 1] * r * gv[2 * i + 1],
+                                  av[2 * i + 1] * __uint_as_float(xw[i] & 0xFFFF0000u));
+            ow[i] = (uint32_t)f32_to_bf16(s0) | (uint32_t)f32_to_bf16(s1) << 16;
+        }
+        *reinterpret_cast<uint4 *>(s_out + (int64_t)t * d + c0) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+    }
+}
+
+hipError_t launch_combine_postnorm(const Shape &s, const Plan &p, const Workspace &ws, const uint16_t *x,
+                                   const float *gamma, const float *alpha, const float *beta,
+                                   uint16_t *s_out, hipStream_t st)
+{
+    if (s.d > kBlockFusedMaxD || s.d % 8 != 0 || s.k > kBlockFusedMaxK) return hipErrorInvalidValue;
+    // the few-row down kernel stores in slot order, the tiled ones in the grouped order
+    if (p.tiled)
+        combine_postnorm_kernel<false><<<s.T, 256, 0, st>>>(x, ws.wts, ws.inv, ws.o, ws.ssq, gamma, alpha, beta,
+                                                            s_out, s.d, s.k, s.d / p.ssq_cols, s.eps);
+    else
+        combine_postnorm_kernel<true><<<s.T, 256, 0, st>>>(x, ws.wts, ws.inv, ws.o, ws.ssq, gamma, alpha, beta,
+                                                           s_out, s.d, s.k, s.d / p.ssq_cols, s.eps);
+    return hipGetLastError();
+}
+
 hipError_t launch_prenorm(const uint16_t *x, const float *gamma, uint16_t *xn, int T, int d, float eps,
                           hipStream_t st)
 {

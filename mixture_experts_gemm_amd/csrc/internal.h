@@ -276,6 +276,15 @@ hipError_t launch_prenorm(const uint16_t *x, const float *gamma, uint16_t *xn, i
 hipError_t launch_postnorm_gate(const uint16_t *x, const float *y, const float *gamma,
                                 const float *alpha, const float *beta, uint16_t *s_out, int T, int d,
                                 float eps, hipStream_t st);
+// The block's combine and post-norm gate in one kernel, for rows of at most
+// kBlockFusedMaxD columns and at most kBlockFusedMaxK slots per token
+// (hipErrorInvalidValue otherwise; the caller then takes fp32 y and
+// launch_postnorm_gate).
+hipError_t launch_combine_postnorm(const Shape &s, const Plan &p, const Workspace &ws, const uint16_t *x,
+                                   const float *gamma, const float *alpha, const float *beta,
+                                   uint16_t *s_out, hipStream_t st);
+constexpr int kBlockFusedMaxD = 16384;
+constexpr int kBlockFusedMaxK = 64;
 // bf16 x -> FP8 hi/lo parts + E8M0 scales in the workspace (the streaming
 // gate/up kernel's input when the router does not split x itself).
 hipError_t launch_split_x_fp8(const Shape &s, const Workspace &ws, const uint16_t *x, hipStream_t st);
