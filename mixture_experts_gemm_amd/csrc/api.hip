@@ -491,11 +491,9 @@ extern "C" int moe_block_forward(const moe_dims_t *dims, const void *x, const fl
         return launch_router(s, p, B.ws, B.xn, router_w, st);
     };
     auto finish = [&]() -> hipError_t {
-        // many tokens: one kernel (one workgroup per row) for rows that fit it;
-        // few tokens, or wider rows: fp32 y over more workgroups, then the
-        // norm and gate (measured: the fused kernel took block T=4096 3.13 ->
-        // 3.08 ms but T=4 163.7 -> 169.5 us, four workgroups for four rows)
-        if (p.tiled && s.d <= kBlockFusedMaxD && s.k <= kBlockFusedMaxK)
+        // one kernel (one workgroup per row) for rows that fit it; wider
+        // rows or more slots: fp32 y, then the norm and gate
+        if (s.d <= kBlockFusedMaxD && s.k <= kBlockFusedMaxK)
             return launch_combine_postnorm(s, p, B.ws, xb, gamma_post, alpha, beta,
                                            static_cast<uint16_t *>(s_out), st);
         hipError_t e = launch_combine_sum_f32(s, p, B.ws, B.y, st);

@@ -283,8 +283,9 @@ __global__ __launch_bounds__(256) void postnorm_gate_kernel(
 }
 
 // The block's combine and post-norm in one pass, for rows of at most
-// kBlockPasses * 2048 = kBlockFusedMaxD columns and at most kBlockFusedMaxK
-// slots: one workgroup per token row.  Every slot's
+// kBlockFusedMaxD columns and at most kBlockFusedMaxK slots: one workgroup
+// of NT threads per token row (256 for many rows; 1024 for few, so a row
+// of up to 8192 columns is one pass).  Every slot's
 // coefficient w / sqrt(mean(o^2) + eps) first (as combine_kernel), then y =
 // sum over the slots of coef * o in slot order (the same sums as
 // combine_kernel's), kept in registers, 8 columns per thread and pass; the
@@ -292,10 +293,24 @@ __global__ __launch_bounds__(256) void postnorm_gate_kernel(
 // s_out = bf16(alpha * x + beta * y * r * gamma).  s_out may be x: each
 // thread reads its x elements before writing them.
 constexpr int kBlockPasses = 8;
-static_assert(kBlockPasses * 2048 == kBlockFusedMaxD, "one pass is 256 threads x 8 columns");
+static_assert(kBlockPasses * 2048 == kBlockFusedMaxD, "a pass of 256 threads is 2048 columns");
 
-template <bool SLOT>
-__global__ __launch_bounds__(256) void combine_postnorm_kernel(
+// the row's sum of squares over NW waves in a fixed order
+template <int NW>
+__device__ __forceinline__ float block_row_sumsq_n(float part)
+{
+    __shared__ float wsq[NW];
+    const float v = wave_sum(part);
+    if ((threadIdx.x & 63) == 0) wsq[threadIdx.x >> 6] = v;
+    __syncthreads();
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) s += wsq[w];
+    return s;
+}
+
+template <bool SLOT, int NT>
+__global__ __launch_bounds__(NT) void combine_postnorm_kernel(
     const uint16_t *x, const float *__restrict__ wts, const int32_t *__restrict__ inv,
     const uint16_t *__restrict__ o, const float *__restrict__ ssq, const float *__restrict__ gamma,
     const float *__restrict__ alpha, const float *__restrict__ beta, uint16_t *s_out, int d, int k, int P,
@@ -304,7 +319,7 @@ __global__ __launch_bounds__(256) void combine_postnorm_kernel(
     __shared__ float coef[kBlockFusedMaxK];
     __shared__ int32_t row[kBlockFusedMaxK];
     const int t = blockIdx.x;
-    for (int j = threadIdx.x >> 4; j < k; j += 16) {
+    for (int j = threadIdx.x >> 4; j < k; j += NT / 16) {
         const int64_t slot = (int64_t)t * k + j;
         const int p = SLOT ? (int)slot : inv[slot];
         const float wj = wts[slot];
@@ -326,13 +341,14 @@ __global__ __launch_bounds__(256) void combine_postnorm_kernel(
         }
     }
     __syncthreads();
-    float y[kBlockPasses][8];
+    constexpr int NP = kBlockFusedMaxD / (NT * 8);  // passes
+    float y[NP][8];
     float part = 0.f;
 #pragma unroll
-    for (int ps = 0; ps < kBlockPasses; ++ps) {
+    for (int ps = 0; ps < NP; ++ps) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) y[ps][i] = 0.f;
-        const int c0 = ps * 2048 + threadIdx.x * 8;
+        const int c0 = ps * NT * 8 + threadIdx.x * 8;
         if (c0 >= d) continue;
         for (int j0 = 0; j0 < k; j0 += kSlotBatch) {
             // up to kSlotBatch o rows in flight at once (clamped index, masked)
@@ -355,10 +371,10 @@ __global__ __launch_bounds__(256) void combine_postnorm_kernel(
 #pragma unroll
         for (int i = 0; i < 8; ++i) part = fmaf(y[ps][i], y[ps][i], part);
     }
-    const float r = 1.0f / sqrtf(block_row_sumsq(part) / (float)d + eps);
+    const float r = 1.0f / sqrtf(block_row_sumsq_n<NT / 64>(part) / (float)d + eps);
 #pragma unroll
-    for (int ps = 0; ps < kBlockPasses; ++ps) {
-        const int c0 = ps * 2048 + threadIdx.x * 8;
+    for (int ps = 0; ps < NP; ++ps) {
+        const int c0 = ps * NT * 8 + threadIdx.x * 8;
         if (c0 >= d) continue;
         const uint4 xv = *reinterpret_cast<const uint4 *>(x + (int64_t)t * d + c0);
         const float4 g0 = *reinterpret_cast<const float4 *>(gamma + c0), g1 = *reinterpret_cast<const float4 *>(gamma + c0 + 4);
@@ -387,11 +403,11 @@ hipError_t launch_combine_postnorm(const Shape &s, const Plan &p, const Workspac
     if (s.d > kBlockFusedMaxD || s.d % 8 != 0 || s.k > kBlockFusedMaxK) return hipErrorInvalidValue;
     // the few-row down kernel stores in slot order, the tiled ones in the grouped order
     if (p.tiled)
-        combine_postnorm_kernel<false><<<s.T, 256, 0, st>>>(x, ws.wts, ws.inv, ws.o, ws.ssq, gamma, alpha, beta,
-                                                            s_out, s.d, s.k, s.d / p.ssq_cols, s.eps);
+        combine_postnorm_kernel<false, 256><<<s.T, 256, 0, st>>>(x, ws.wts, ws.inv, ws.o, ws.ssq, gamma, alpha,
+                                                                 beta, s_out, s.d, s.k, s.d / p.ssq_cols, s.eps);
     else
-        combine_postnorm_kernel<true><<<s.T, 256, 0, st>>>(x, ws.wts, ws.inv, ws.o, ws.ssq, gamma, alpha, beta,
-                                                           s_out, s.d, s.k, s.d / p.ssq_cols, s.eps);
+        combine_postnorm_kernel<true, 1024><<<s.T, 1024, 0, st>>>(x, ws.wts, ws.inv, ws.o, ws.ssq, gamma, alpha,
+                                                                  beta, s_out, s.d, s.k, s.d / p.ssq_cols, s.eps);
     return hipGetLastError();
 }
 
