@@ -439,8 +439,18 @@ def _run_block(L, g_pre, g_post):
     return bf16_bits(out), res
 
 
+# block cases beyond the named workloads: k = 24 on a tiled plan (the fused
+# combine + post-norm kernel's slot batches), k = 72 on a few-row plan (more
+# slots than the fused kernel takes: fp32 y, then the norm-and-gate kernel)
+BLOCK_CUSTOM = {
+    "k24": dict(T=40, d=256, E=32, k=24, F=128, seed=31),
+    "k72": dict(T=24, d=256, E=128, k=72, F=128, seed=32),
+}
+
+
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("name,full", [("tiny", True), ("decode4", True), ("prefill", False)])
+@pytest.mark.parametrize("name,full", [("tiny", True), ("decode4", True), ("prefill", False),
+                                       ("k24", True), ("k72", True)])
 def test_block_with_stream_norms(name, full):
     """Pre-norm into the block, post-norm into the gate, teacher-forced.
 
@@ -450,8 +460,9 @@ def test_block_with_stream_norms(name, full):
     1e-4, and the oracle's B2-B3 on the same rows must meet the layer
     tolerance on every token (small sizes) or 512 tokens plus every tile's
     first and last row."""
-    L = synth.make_layer(name, threads=16)
-    g_pre, g_post = synth.make_norm_gains(synth.WORKLOADS[name])
+    w = synth.custom_workload(**BLOCK_CUSTOM[name]) if name in BLOCK_CUSTOM else synth.WORKLOADS[name]
+    L = synth.make_layer(w, threads=16)
+    g_pre, g_post = synth.make_norm_gains(w)
     s = L.shape
     _say("block", name, "T", s.T)
     out, dbg = _run_block(L, g_pre, g_post)
