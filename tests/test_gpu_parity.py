@@ -561,6 +561,7 @@ SHAPE_CASES = [
     (1200, 256, 512, 8, 256, "E = 512: top-k with 16 keys per lane, many-token grouping"),
     (40, 256, 512, 8, 256, "E = 512: single-workgroup routing with 16 keys per lane"),
     (16, 256, 1024, 32, 128, "E = 1024 (the largest), k = 32"),
+    (100, 256, 128, 72, 128, "k = 72: many-token top-k with more than 64 choices"),
     (4, 768, 16, 4, 384, "decode at d = 768 (not a multiple of 2048): 16-row gate/up kernel"),
     (6, 2048, 64, 6, 1408, "decode, streaming gate/up kernel at F = 1408"),
 ]
