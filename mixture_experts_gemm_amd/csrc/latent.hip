@@ -54,10 +54,11 @@ __device__ __forceinline__ void store_dense(void *C, int64_t idx, int col, float
 // of row m at u ^ (m & 7): the 8 tokens' reads at one K offset fall on
 // distinct banks); tokens >= T enter as zeros.  The waves' partial sums meet
 // in LDS in a fixed order.  Needs K a multiple of 512 * NW (the A copy) and
-// at least 1024 * NW (every wave then runs two or more whole batches).  HBM bound:
+// at least 2 * kDenseU * kKStep * NW (every wave then runs two or more whole
+// batches; the launcher asks for K >= 4096).  HBM bound:
 // N*K*2 bytes of W per launch.
 constexpr int kDenseStreamMaxT = 8;
-constexpr int kDenseU = 4;
+constexpr int kDenseU = 1;  // chunks per batch (1 measured 4% faster than 2 or 4: fewer bytes in flight)
 
 template <int OUT, int NW>
 __global__ __launch_bounds__(64 * NW) void dense_stream_kernel(const uint16_t *__restrict__ A,
