@@ -129,8 +129,8 @@ inline int64_t max_tiles(const Shape &s, int tile_rows)
     return S / tile_rows + u + 1;
 }
 
-// The wide kernel (128 x 512 tiles) runs a matrix with an even number of
-// 256-row weight tiles; an odd count runs on the 128 x 256 kernel.
+// The wide kernel (128 x 512 or 64 x 512 tiles) runs a matrix with an even
+// number of 256-row weight tiles; an odd count runs on the 128 x 256 kernel.
 inline bool wide_gate_up(const Shape &s) { return (s.F / 128) % 2 == 0; }
 inline bool wide_down(const Shape &s) { return (s.d / 256) % 2 == 0; }
 
