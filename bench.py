@@ -207,25 +207,26 @@ def make_latent_sets(name, nsets, device):
 # the gate/up kernel each workload runs (the dominant kernel of the layer)
 GATE_UP_KERNEL = {
     "decode1": "gemm1_stream_kernel (gate/up + SwiGLU, persistent, MX MFMA)",
-    "decode4": "gemm1_stream_kernel (gate/up + SwiGLU, persistent, MX MFMA)",
+    "decode4": "gemm1_col_kernel (gate/up + SwiGLU, persistent, whole 128-feature tile columns, MX MFMA)",
     "prefill": "gemm_mxw_kernel<true, 128> (gate/up + SwiGLU, 128x512 tiles, MX MFMA)",
     "skewed": "gemm_mxw_kernel<true, 128> (gate/up + SwiGLU, 128x512 tiles, MX MFMA)",
     "stack": "gemm_mxw_kernel<true, 128> (gate/up + SwiGLU, 128x512 tiles, MX MFMA)",
     "ep753": "gemm_mxw_kernel<true, 64> (gate/up + SwiGLU, 64x512 tiles, three stages, MX MFMA)",
     "ep3012": "gemm_mxw_kernel<true, 128> (gate/up + SwiGLU, 128x512 tiles, MX MFMA)",
-    "latent4": "gemm1_stream_kernel (gate/up + SwiGLU, persistent, MX MFMA)",
+    "latent4": "gemm1_col_kernel (gate/up + SwiGLU, persistent, whole 128-feature tile columns, MX MFMA)",
     "latent_prefill": "gemm_mxw_kernel<true, 128> (gate/up + SwiGLU, 128x512 tiles, MX MFMA)",
-    "block4": "gemm1_stream_kernel (gate/up + SwiGLU, persistent, MX MFMA)",
+    "block4": "gemm1_col_kernel (gate/up + SwiGLU, persistent, whole 128-feature tile columns, MX MFMA)",
     "block_prefill": "gemm_mxw_kernel<true, 128> (gate/up + SwiGLU, 128x512 tiles, MX MFMA)",
     "nv4": "gemm1_stream_kernel<4, true> (gate/up + SwiGLU, persistent, fp16 MFMA, 16-block weights)",
     "nv_prefill": "gemm_nv_kernel<true> (gate/up + SwiGLU, 192x256 tiles, fp16 MFMA, 16-block weights)",
 }
 # How the gate/up kernel issues one bf16 x FP4 product on the matrix cores:
 # (MFMAs per product, operand types, that instruction's dense peak in
-# TFLOP/s).  The streaming decode kernel splits x into two FP8 parts, the
+# TFLOP/s).  The streaming decode kernels split x into two FP8 parts, the
 # wide prefill kernel into three FP6 parts; the 16-block kernels run fp16.
 MX_ISSUE = {
     "gemm1_stream_kernel": (2, "fp8 x fp4 (two FP8 parts of x)", 5000.0),
+    "gemm1_col_kernel": (2, "fp8 x fp4 (two FP8 parts of x)", 5000.0),
     "gemm_mxw_kernel": (3, "fp6 x fp4 (three FP6 parts of x)", 10100.0),
     "gemm_nv_kernel": (1, "fp16 x fp16 (weights widened)", 2500.0),
 }

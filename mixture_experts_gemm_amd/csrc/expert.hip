@@ -1559,6 +1559,155 @@ __global__ __launch_bounds__(256) void gemm1_stream_kernel(
     }
 }
 
+// =========================================================================
+// Few tokens over many experts (decode at T >= 2 with E = 256, k = 8): the
+// streaming gate/up kernel on whole weight tile columns.  An item is (tile,
+// weight tile nt): the gate and up rows of 128 features over all of K.  The
+// workgroup's 4 waves split it 2 x 2: wave w reads tile rows 128(w & 1) ..
+// +127 (the gate and up rows of 64 features: 8 KB contiguous a chunk) over
+// K half w >> 1, so the workgroup reads every 16 KB code tile and 1 KB scale
+// tile of its column whole and the chip's loads stay close together in
+// memory.  Measured on the address stream alone (no arithmetic), 540 MB at
+// decode T=4: 83 us this way against 92 us for 16-feature items.  One chunk
+// per batch, two batches in flight; x's FP8 parts staged in LDS per tile
+// (as gemm1_stream_kernel); the two K halves meet in LDS in a fixed order
+// and the first half's waves write h.  Tiles of at most R rows.
+// =========================================================================
+__global__ __launch_bounds__(256) void gemm1_col_kernel(
+    const uint8_t *__restrict__ ghi, const uint8_t *__restrict__ glo,
+    const uint8_t *__restrict__ gsh, const uint8_t *__restrict__ gsl,
+    const int32_t *__restrict__ perm, const Tile *__restrict__ tiles,
+    const int32_t *__restrict__ ntiles, const uint8_t *__restrict__ wpk,
+    const uint8_t *__restrict__ sc, uint16_t *__restrict__ h, int d, int F, int k, int R)
+{
+    constexpr int NB = 8;  // row blocks a wave: 4 gate, then the same 4 up
+    extern __shared__ uint4 xs4[];
+    __shared__ floatx4_t red[2][2][NB][64];  // [item parity][row half][block][lane]
+    uint8_t *xs = reinterpret_cast<uint8_t *>(xs4);
+    uint8_t *xhi = xs, *xlo = xs + (size_t)R * d;
+    uint8_t *xsh = xs + (size_t)2 * R * d, *xsl = xsh + (size_t)R * (d / 32);
+
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int n = lane & 15, g = lane >> 4;
+    const int half = wv & 1, kh = wv >> 1;
+    const int cols = F / 128;  // items per tile
+    const int64_t nitems = (int64_t)*ntiles * cols;
+    const int i0 = (int)(nitems * blockIdx.x / gridDim.x);
+    const int i1 = (int)(nitems * (blockIdx.x + 1) / gridDim.x);
+    if (i0 >= i1) return;
+    const int ch = d / kKStep / 2;  // chunks per K half
+    const int total = (i1 - i0) * ch;
+    // ---- weight loads: one chunk of the wave's 8 row blocks ----------------
+    // row block i of half h: packed rows 128h + 16i .. +15, i.e. feature
+    // 128nt + 64h + 16(i & 3) + n of the gate (i < 4) or up matrix
+    uint4 b0[NB], b1[NB];
+    uint32_t s0[NB], s1[NB];
+    int l_ti = -1;
+    Tile l_tl{0, 0, 0, 0};
+    auto load = [&](uint4 (&b)[NB], uint32_t (&sv)[NB], int st) {
+        const int it = i0 + st / ch, c = kh * ch + st % ch;
+        const int ti = it / cols, nt = it - ti * cols;
+        if (ti != l_ti) {
+            l_tl = tiles[ti];
+            l_ti = ti;
+        }
+        const WView v = w1_view(wpk, sc, l_tl.expert, d, F);
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            const int rho = 128 * half + 16 * i + n;
+            b[i] = ld_stream16(v.slot(nt, c, rho, g));
+            sv[i] = ld_stream4(v.scales(nt, c, rho));
+        }
+    };
+    // ---- activation staging: the tile's FP8 rows and scales -> LDS --------
+    int c_ti = -1;
+    Tile c_tl{0, 0, 0, 0};
+    auto stage = [&](int ti) {
+        c_tl = tiles[ti];
+        c_ti = ti;
+        const int q = d / 16, qs = d / 32 / 16;  // 16-byte units per part row / scale row
+        for (int r = 0; r < c_tl.nrows; ++r) {
+            const int64_t tok = perm[c_tl.row0 + r] / k;
+            const uint4 *sh = reinterpret_cast<const uint4 *>(ghi + tok * d);
+            const uint4 *sl = reinterpret_cast<const uint4 *>(glo + tok * d);
+            uint4 *dh = reinterpret_cast<uint4 *>(xhi + (size_t)r * d);
+            uint4 *dl = reinterpret_cast<uint4 *>(xlo + (size_t)r * d);
+            for (int j = threadIdx.x; j < q; j += 256) {
+                dh[j] = sh[j];
+                dl[j] = sl[j];
+            }
+            const uint4 *ssh = reinterpret_cast<const uint4 *>(gsh + tok * (d / 32));
+            const uint4 *ssl = reinterpret_cast<const uint4 *>(gsl + tok * (d / 32));
+            if ((int)threadIdx.x < qs) {
+                reinterpret_cast<uint4 *>(xsh + (size_t)r * (d / 32))[threadIdx.x] = ssh[threadIdx.x];
+                reinterpret_cast<uint4 *>(xsl + (size_t)r * (d / 32))[threadIdx.x] = ssl[threadIdx.x];
+            }
+        }
+        lds_barrier();
+    };
+    floatx4_t acc[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) acc[i] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    auto consume = [&](const uint4 (&b)[NB], const uint32_t (&sv)[NB], int st) {
+        const int it = i0 + st / ch, bt = st % ch;
+        const int ti = it / cols, nt = it - ti * cols;
+        // a new tile's rows replace the old ones: every wave has passed the
+        // previous item's barrier, so no wave still reads them
+        if (ti != c_ti) stage(ti);
+        const int m = n < c_tl.nrows ? n : 0;  // rows past nrows are computed on row 0, never stored
+        const int c = kh * ch + bt;
+        const uint4 *hp = reinterpret_cast<const uint4 *>(xhi + (size_t)m * d + c * kKStep);
+        const uint4 *lp = reinterpret_cast<const uint4 *>(xlo + (size_t)m * d + c * kKStep);
+        const uint4 h0 = hp[g], h1 = hp[4 + g], l0 = lp[g], l1 = lp[4 + g];
+        const int sidx = m * (d / 32) + c * 4 + g;
+        const uint32_t sah = xsh[sidx], sal = xsl[sidx];
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            const uint32_t sb = (sv[i] >> (8 * g)) & 0xFFu;
+            acc[i] = mfma_mx(h0, h1, b[i], sah, sb, acc[i]);
+            acc[i] = mfma_mx(l0, l1, b[i], sal, sb, acc[i]);
+        }
+        if (bt == ch - 1) {
+            // the item's two K halves meet: the second writes, the first adds
+            // (one order) and stores h = silu(gate) * up
+            const int par = (it - i0) & 1;
+            if (kh == 1) {
+#pragma unroll
+                for (int i = 0; i < NB; ++i) red[par][half][i][lane] = acc[i];
+            }
+            lds_barrier();
+            if (kh == 0) {
+#pragma unroll
+                for (int i = 0; i < NB; ++i) acc[i] += red[par][half][i][lane];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int fcol = nt * 128 + half * 64 + 16 * q + n;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int row = g * 4 + r;
+                        if (row < c_tl.nrows)
+                            h[(int64_t)(c_tl.row0 + row) * F + fcol] =
+                                f32_to_bf16(silu(acc[q][r]) * acc[q + 4][r]);
+                    }
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < NB; ++i) acc[i] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+        }
+    };
+
+    load(b0, s0, 0);
+    if (total > 1) load(b1, s1, 1);
+    for (int st = 0; st < total; st += 2) {
+        consume(b0, s0, st);
+        if (st + 2 < total) load(b0, s0, st + 2);
+        if (st + 1 < total) {
+            consume(b1, s1, st + 1);
+            if (st + 3 < total) load(b1, s1, st + 3);
+        }
+    }
+}
+
 // Workgroups that fit on the device at once for a 256-thread kernel with
 // `lds` bytes of dynamic LDS (0 on error).  Queried on every call: nothing
 // is cached, so the library keeps no state between calls.
@@ -1598,6 +1747,21 @@ hipError_t launch_gemm1(const Shape &s, const Plan &p, const Workspace &ws, cons
     } else if (p.stream) {
         const int R = p.tile_rows;
         const size_t lds = (size_t)R * (2 * s.d + 2 * (s.d / 32));
+        // whole tile columns when there are enough of them for the device
+        // and the kernel's larger LDS fits (else the 16-feature items below)
+        const int cgrid = stream_columns(s)
+                              ? persistent_grid(reinterpret_cast<const void *>(gemm1_col_kernel), lds)
+                              : 0;
+        if (cgrid > 0) {
+            hipExtLaunchKernelGGL(gemm1_col_kernel, dim3(cgrid), dim3(256), (uint32_t)lds, st, ev0, ev1, 0,
+                                  (const uint8_t *)ws.xhi, (const uint8_t *)ws.xlo,
+                                  (const uint8_t *)ws.xshi, (const uint8_t *)ws.xslo,
+                                  (const int32_t *)ws.perm, (const Tile *)ws.tiles,
+                                  (const int32_t *)ws.ntiles, wpk, sc, ws.h, s.d, s.F, s.k, R);
+            return hipGetLastError();
+        }
+        // a refused occupancy query must not surface as this launch's error
+        if (stream_columns(s)) (void)hipGetLastError();
         auto kfn = gemm1_stream_kernel<kG1StreamU, false>;
         const int grid = persistent_grid(reinterpret_cast<const void *>(kfn), lds);
         if (grid <= 0) return hipErrorInvalidConfiguration;

@@ -149,6 +149,19 @@ inline void set_schedule(const Shape &s, Plan &p, int ntn_gate_up)
     p.grid1 = (int)sched_grid(s, p.tile_rows, ntn_gate_up);
 }
 
+// The streaming gate/up path on whole tile columns (gemm1_col_kernel) when
+// the expected number of (tile, 128-feature column) items fills the device:
+// E (1 - (1 - k/E)^T) distinct experts, F/128 columns each (at T = 1 with
+// E = 256, k = 8 there are 128 items and the 16-feature items of
+// gemm1_stream_kernel run faster).
+inline bool stream_columns(const Shape &s)
+{
+    if (s.F % 128 != 0 || (s.d / 128) % 2 != 0) return false;
+    double miss = 1.0;  // probability that a given expert is chosen by no token
+    for (int t = 0; t < s.T; ++t) miss *= 1.0 - (double)s.k / s.E;
+    return s.E * (1.0 - miss) * (s.F / 128) >= 192.0;
+}
+
 inline Plan make_plan(const Shape &s)
 {
     Plan p;

@@ -176,11 +176,14 @@ def test_decode_all_tokens(name):
     _check_tokens(L, out, np.arange(L.shape.T), name)
 
 
-@pytest.mark.parametrize("T,d", [(3, 2048), (5, 2048), (8, 4096)])
-def test_few_tokens_hot_expert(T, d):
+# (T, d, E, k, F): E = 16 runs the streaming kernel on 16-feature items;
+# E = 256, k = 8 on whole tile columns (enough distinct experts for them)
+@pytest.mark.parametrize("T,d,E,k,F", [(3, 2048, 16, 4, 256), (5, 2048, 16, 4, 256), (8, 4096, 16, 4, 256),
+                                       (6, 2048, 256, 8, 2048), (3, 4096, 256, 8, 1408)])
+def test_few_tokens_hot_expert(T, d, E, k, F):
     # every token picks expert 3 first, so its segment holds all T tokens and
     # is cut into several tiles on the few-token (streaming) path
-    w = synth.custom_workload(T=T, d=d, E=16, k=4, F=256, seed=23 + T, zipf=True)
+    w = synth.custom_workload(T=T, d=d, E=E, k=k, F=F, seed=23 + T, zipf=True)
     wr = synth.make_router(w)
     wr[:, 0] = 0.0
     wr[3, 0] = 50.0
