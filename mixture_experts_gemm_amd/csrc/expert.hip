@@ -1661,12 +1661,16 @@ __global__ __launch_bounds__(256) void gemm1_col_kernel(
         const uint4 h0 = hp[g], h1 = hp[4 + g], l0 = lp[g], l1 = lp[4 + g];
         const int sidx = m * (d / 32) + c * 4 + g;
         const uint32_t sah = xsh[sidx], sal = xsl[sidx];
+        // all hi products, then all lo products: no MFMA waits on the one
+        // before it (each block still adds hi before lo)
+        uint32_t sb[NB];
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
-            const uint32_t sb = (sv[i] >> (8 * g)) & 0xFFu;
-            acc[i] = mfma_mx(h0, h1, b[i], sah, sb, acc[i]);
-            acc[i] = mfma_mx(l0, l1, b[i], sal, sb, acc[i]);
+            sb[i] = (sv[i] >> (8 * g)) & 0xFFu;
+            acc[i] = mfma_mx(h0, h1, b[i], sah, sb[i], acc[i]);
         }
+#pragma unroll
+        for (int i = 0; i < NB; ++i) acc[i] = mfma_mx(l0, l1, b[i], sal, sb[i], acc[i]);
         if (bt == ch - 1) {
             // the item's two K halves meet: the second writes, the first adds
             // (one order) and stores h = silu(gate) * up
@@ -1696,15 +1700,19 @@ __global__ __launch_bounds__(256) void gemm1_col_kernel(
         }
     };
 
+    // total is even (d % 512 = 0: an even number of chunks per K half), so
+    // every load is unconditional (past the end they re-read chunk total - 1):
+    // with the same loads on every path the compiler's waits before a chunk's
+    // MFMAs leave the other buffer's loads in flight; a skipped load on one
+    // path made every chunk wait for both buffers
+    const int last = total - 1;
     load(b0, s0, 0);
-    if (total > 1) load(b1, s1, 1);
+    load(b1, s1, 1);
     for (int st = 0; st < total; st += 2) {
         consume(b0, s0, st);
-        if (st + 2 < total) load(b0, s0, st + 2);
-        if (st + 1 < total) {
-            consume(b1, s1, st + 1);
-            if (st + 3 < total) load(b1, s1, st + 3);
-        }
+        load(b0, s0, min(st + 2, last));
+        consume(b1, s1, st + 1);
+        load(b1, s1, min(st + 3, last));
     }
 }
 

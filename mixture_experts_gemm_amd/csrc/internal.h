@@ -156,7 +156,7 @@ inline void set_schedule(const Shape &s, Plan &p, int ntn_gate_up)
 // gemm1_stream_kernel run faster).
 inline bool stream_columns(const Shape &s)
 {
-    if (s.F % 128 != 0 || (s.d / 128) % 2 != 0) return false;
+    if (s.F % 128 != 0 || s.d % 512 != 0) return false;  // an even number of chunks per K half
     double miss = 1.0;  // probability that a given expert is chosen by no token
     for (int t = 0; t < s.T; ++t) miss *= 1.0 - (double)s.k / s.E;
     return s.E * (1.0 - miss) * (s.F / 128) >= 192.0;
