@@ -206,7 +206,7 @@ def make_latent_sets(name, nsets, device):
 
 # the gate/up kernel each workload runs (the dominant kernel of the layer)
 GATE_UP_KERNEL = {
-    "decode1": "gemm1_stream_kernel (gate/up + SwiGLU, persistent, MX MFMA)",
+    "decode1": "gemm1_stream_kernel (routing prologue + gate/up + SwiGLU, persistent, MX MFMA)",
     "decode4": "gemm1_col_kernel (gate/up + SwiGLU, persistent, whole 128-feature tile columns, MX MFMA)",
     "prefill": "gemm_mxw_kernel<true, 128> (gate/up + SwiGLU, 128x512 tiles, MX MFMA)",
     "skewed": "gemm_mxw_kernel<true, 128> (gate/up + SwiGLU, 128x512 tiles, MX MFMA)",

@@ -95,7 +95,11 @@ enum {
  * may be NULL): stage_begin[s] / stage_end[s] are recorded on the stream
  * right before the first and right after the last kernel of stage s.  The
  * gate/up stage is a single kernel and its two events are recorded by that
- * kernel's own dispatch, so they bracket exactly its execution.
+ * kernel's own dispatch, so they bracket exactly its execution.  With very
+ * few tokens (T*k <= 16, E <= 256, d a multiple of 2048) the gate/up kernel does
+ * the top-k and the grouping itself, in its prologue: the top-k and group
+ * stages then launch nothing, their events bracket no work, and the gate/up
+ * events include the routing.
  *   xn      bf16  [T][d]  moe_block_forward only: the normalised rows x_n
  *                         the router and the experts read (ignored by the
  *                         other entry points)

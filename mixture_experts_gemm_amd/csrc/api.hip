@@ -370,6 +370,9 @@ extern "C" int moe_latent_forward(const moe_latent_dims_t *dims, const void *x,
     // of x (the experts read z)
     Workspace wr = L.ws;
     wr.scores = L.scores_r;
+    // the gate/up kernel reads the router's scores when it routes itself
+    Workspace we = L.ws;
+    we.scores = L.scores_r;
     Plan pr = p;
     pr.stream = pr.tiled = false;
     const uint16_t *xb = static_cast<const uint16_t *>(x);
@@ -403,7 +406,7 @@ extern "C" int moe_latent_forward(const moe_latent_dims_t *dims, const void *x,
     if (!stage(MOE_STAGE_ROUTER, [&] { return launch_router(sr, pr, wr, xb, router_w, st); }) ||
         !stage(MOE_STAGE_TOPK, [&] { return launch_topk(sr, p, wr, st); }) ||
         !stage(MOE_STAGE_GROUP, [&] { return launch_group(sr, p, wr, st); }) || !ok(narrow()) ||
-        !ok(launch_gemm1(se, p, L.ws, L.z, expert_w_packed, scales, st,
+        !ok(launch_gemm1(se, p, we, L.z, expert_w_packed, scales, st,
                          stage_event(debug, MOE_STAGE_GEMM1, true),
                          stage_event(debug, MOE_STAGE_GEMM1, false))) ||
         !stage(MOE_STAGE_GEMM2, [&] { return launch_gemm2(se, p, L.ws, expert_w_packed, scales, st); }) ||

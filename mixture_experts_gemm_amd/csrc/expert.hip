@@ -30,6 +30,7 @@
 #include "device.h"
 #include "internal.h"
 #include "layout.h"
+#include "topk.h"
 
 namespace moe {
 
@@ -38,6 +39,21 @@ constexpr int kG1StreamU = 4;               // chunks per weight batch of the st
 constexpr int kUnroll = 4;  // chunks per weight batch of the decode kernels
 constexpr int kDownU = 2;   // the MXFP4 few-row down kernel's (T=1 15.5 -> 14.7 us; T=4 the same as 4)
 constexpr size_t kNvFuseLds = 64 * 1024;  // LDS the 16-block down kernel may take for its own h rows
+
+// A tile read from LDS at a workgroup-uniform index, its fields moved to
+// scalar registers (the weight addresses then stay scalar, as after a
+// scalar load of the global tile list).
+__device__ __forceinline__ Tile uniform_tile(const Tile &t)
+{
+    Tile u;
+    u.expert = __builtin_amdgcn_readfirstlane(t.expert);
+    u.row0 = __builtin_amdgcn_readfirstlane(t.row0);
+    u.nrows = __builtin_amdgcn_readfirstlane(t.nrows);
+    u.first = __builtin_amdgcn_readfirstlane(t.first);
+    u.count = __builtin_amdgcn_readfirstlane(t.count);
+    u.pad[0] = u.pad[1] = u.pad[2] = 0;
+    return u;
+}
 
 __device__ __forceinline__ floatx4_t mfma_chunk(const uint4 *a, uint4 b, float scale, floatx4_t acc)
 {
@@ -1376,15 +1392,16 @@ hipError_t launch_split_x(const Shape &s, const Workspace &ws, const uint16_t *x
 // (ghi; glo, gsh, gsl, xsc unused), converted to fp16 with a scale per row
 // as the tile is staged (f16_row_block), matrix scales gs [E][3]; the chunk is multiplied by four fp16 MFMAs on
 // weights widened in registers (mfma_chunk_nv) instead of the scaled MX MFMA.
-template <int U, bool NV>
+template <int U, bool NV, bool ROUTE>
 __global__ __launch_bounds__(256) void gemm1_stream_kernel(
     const uint8_t *__restrict__ ghi, const uint8_t *__restrict__ glo,
     const uint8_t *__restrict__ gsh, const uint8_t *__restrict__ gsl,
-    const int32_t *__restrict__ perm, const Tile *__restrict__ tiles,
-    const int32_t *__restrict__ ntiles, const uint8_t *__restrict__ wpk,
+    int32_t *__restrict__ perm, Tile *__restrict__ tiles,
+    int32_t *__restrict__ ntiles, const uint8_t *__restrict__ wpk,
     const uint8_t *__restrict__ sc, uint16_t *__restrict__ h, int d, int F, int k, int R,
-    const float *__restrict__ xsc, const float *__restrict__ gs)
+    const float *__restrict__ xsc, const float *__restrict__ gs, const RouteArgs ra)
 {
+    static_assert(!(NV && ROUTE), "the 16-block path reads the routing kernel's tile list");
     constexpr int NB = 2;  // gate block, up block
     extern __shared__ uint4 xs4[];
     __shared__ floatx4_t red[2][3][NB][64];
@@ -1400,10 +1417,34 @@ __global__ __launch_bounds__(256) void gemm1_stream_kernel(
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int n = lane & 15, g = lane >> 4;
     const int groups = F / 16;
-    const int64_t nitems = (int64_t)*ntiles * groups;
+    // ROUTE: the call's routing, computed here (route_few) instead of read
+    __shared__ typename std::conditional<ROUTE, FewRoute, char>::type fr;
+    if constexpr (ROUTE) route_few(ra.scores, ra.T, ra.E, k, R, fr);
+    // workgroup 0 stores the routing for the later kernels when it is done
+    auto store_route = [&]() {
+        if constexpr (ROUTE)
+            if (blockIdx.x == 0)
+                route_few_store(fr, ra.T, ra.E, k, ra.ids, ra.wts, ra.counts, ra.offsets, perm, ra.inv, tiles,
+                                ntiles);
+    };
+    auto tile_at = [&](int ti) -> Tile {
+        if constexpr (ROUTE) return uniform_tile(fr.tiles[ti]);
+        else return tiles[ti];
+    };
+    auto perm_at = [&](int row) -> int {
+        if constexpr (ROUTE) return __builtin_amdgcn_readfirstlane(fr.perm[row]);
+        else return perm[row];
+    };
+    int ntl;
+    if constexpr (ROUTE) ntl = fr.ntiles;
+    else ntl = *ntiles;
+    const int64_t nitems = (int64_t)ntl * groups;
     const int i0 = (int)(nitems * blockIdx.x / gridDim.x);
     const int i1 = (int)(nitems * (blockIdx.x + 1) / gridDim.x);
-    if (i0 >= i1) return;
+    if (i0 >= i1) {
+        store_route();
+        return;
+    }
     const int cw = d / kKStep / 4;  // chunks per wave
     const int c_begin = wv * cw;
     const int nbat = cw / U;
@@ -1418,7 +1459,7 @@ __global__ __launch_bounds__(256) void gemm1_stream_kernel(
         const int it = i0 + st / nbat, bt = st % nbat;
         const int ti = it / groups, grp = it - ti * groups;
         if (ti != l_ti) {
-            l_tl = tiles[ti];
+            l_tl = tile_at(ti);
             l_ti = ti;
         }
         const WView v = NV ? w1_codes(wpk, l_tl.expert, d, F) : w1_view(wpk, sc, l_tl.expert, d, F);
@@ -1441,14 +1482,14 @@ __global__ __launch_bounds__(256) void gemm1_stream_kernel(
     int c_ti = -1;
     Tile c_tl{0, 0, 0, 0};
     auto stage = [&](int ti) {
-        c_tl = tiles[ti];
+        c_tl = tile_at(ti);
         c_ti = ti;
         const int q = d / 16, qs = d / 32 / 16;  // 16-byte units per part row / scale row
         if constexpr (NV) {
             // the bf16 rows converted here (f16_row_block) into fp16 rows of
             // 2d bytes, the space of both FP8 parts, with their scales
             for (int r = 0; r < c_tl.nrows; ++r) {
-                const int64_t tok = perm[c_tl.row0 + r] / k;
+                const int64_t tok = perm_at(c_tl.row0 + r) / k;
                 const float sc = f16_row_block(reinterpret_cast<const uint4 *>(ghi + tok * 2 * d),
                                                reinterpret_cast<uint4 *>(xs + (size_t)r * 2 * d), 2 * q,
                                                wmax);
@@ -1458,7 +1499,7 @@ __global__ __launch_bounds__(256) void gemm1_stream_kernel(
             return;
         }
         for (int r = 0; r < c_tl.nrows; ++r) {
-            const int64_t tok = perm[c_tl.row0 + r] / k;
+            const int64_t tok = perm_at(c_tl.row0 + r) / k;
             const uint4 *sh = reinterpret_cast<const uint4 *>(ghi + tok * d);
             const uint4 *sl = reinterpret_cast<const uint4 *>(glo + tok * d);
             uint4 *dh = reinterpret_cast<uint4 *>(xhi + (size_t)r * d);
@@ -1557,6 +1598,7 @@ __global__ __launch_bounds__(256) void gemm1_stream_kernel(
             if (st + 3 < total) load(b1, s1, st + 3);
         }
     }
+    store_route();
 }
 
 // =========================================================================
@@ -1573,12 +1615,14 @@ __global__ __launch_bounds__(256) void gemm1_stream_kernel(
 // (as gemm1_stream_kernel); the two K halves meet in LDS in a fixed order
 // and the first half's waves write h.  Tiles of at most R rows.
 // =========================================================================
+template <bool ROUTE>
 __global__ __launch_bounds__(256) void gemm1_col_kernel(
     const uint8_t *__restrict__ ghi, const uint8_t *__restrict__ glo,
     const uint8_t *__restrict__ gsh, const uint8_t *__restrict__ gsl,
-    const int32_t *__restrict__ perm, const Tile *__restrict__ tiles,
-    const int32_t *__restrict__ ntiles, const uint8_t *__restrict__ wpk,
-    const uint8_t *__restrict__ sc, uint16_t *__restrict__ h, int d, int F, int k, int R)
+    int32_t *__restrict__ perm, Tile *__restrict__ tiles,
+    int32_t *__restrict__ ntiles, const uint8_t *__restrict__ wpk,
+    const uint8_t *__restrict__ sc, uint16_t *__restrict__ h, int d, int F, int k, int R,
+    const RouteArgs ra)
 {
     constexpr int NB = 8;  // row blocks a wave: 4 gate, then the same 4 up
     extern __shared__ uint4 xs4[];
@@ -1591,10 +1635,34 @@ __global__ __launch_bounds__(256) void gemm1_col_kernel(
     const int n = lane & 15, g = lane >> 4;
     const int half = wv & 1, kh = wv >> 1;
     const int cols = F / 128;  // items per tile
-    const int64_t nitems = (int64_t)*ntiles * cols;
+    // ROUTE: the call's routing, computed here (route_few) instead of read
+    __shared__ typename std::conditional<ROUTE, FewRoute, char>::type fr;
+    if constexpr (ROUTE) route_few(ra.scores, ra.T, ra.E, k, R, fr);
+    // workgroup 0 stores the routing for the later kernels when it is done
+    auto store_route = [&]() {
+        if constexpr (ROUTE)
+            if (blockIdx.x == 0)
+                route_few_store(fr, ra.T, ra.E, k, ra.ids, ra.wts, ra.counts, ra.offsets, perm, ra.inv, tiles,
+                                ntiles);
+    };
+    auto tile_at = [&](int ti) -> Tile {
+        if constexpr (ROUTE) return uniform_tile(fr.tiles[ti]);
+        else return tiles[ti];
+    };
+    auto perm_at = [&](int row) -> int {
+        if constexpr (ROUTE) return __builtin_amdgcn_readfirstlane(fr.perm[row]);
+        else return perm[row];
+    };
+    int ntl;
+    if constexpr (ROUTE) ntl = fr.ntiles;
+    else ntl = *ntiles;
+    const int64_t nitems = (int64_t)ntl * cols;
     const int i0 = (int)(nitems * blockIdx.x / gridDim.x);
     const int i1 = (int)(nitems * (blockIdx.x + 1) / gridDim.x);
-    if (i0 >= i1) return;
+    if (i0 >= i1) {
+        store_route();
+        return;
+    }
     const int ch = d / kKStep / 2;  // chunks per K half
     const int total = (i1 - i0) * ch;
     // ---- weight loads: one chunk of the wave's 8 row blocks ----------------
@@ -1608,7 +1676,7 @@ __global__ __launch_bounds__(256) void gemm1_col_kernel(
         const int it = i0 + st / ch, c = kh * ch + st % ch;
         const int ti = it / cols, nt = it - ti * cols;
         if (ti != l_ti) {
-            l_tl = tiles[ti];
+            l_tl = tile_at(ti);
             l_ti = ti;
         }
         const WView v = w1_view(wpk, sc, l_tl.expert, d, F);
@@ -1623,11 +1691,11 @@ __global__ __launch_bounds__(256) void gemm1_col_kernel(
     int c_ti = -1;
     Tile c_tl{0, 0, 0, 0};
     auto stage = [&](int ti) {
-        c_tl = tiles[ti];
+        c_tl = tile_at(ti);
         c_ti = ti;
         const int q = d / 16, qs = d / 32 / 16;  // 16-byte units per part row / scale row
         for (int r = 0; r < c_tl.nrows; ++r) {
-            const int64_t tok = perm[c_tl.row0 + r] / k;
+            const int64_t tok = perm_at(c_tl.row0 + r) / k;
             const uint4 *sh = reinterpret_cast<const uint4 *>(ghi + tok * d);
             const uint4 *sl = reinterpret_cast<const uint4 *>(glo + tok * d);
             uint4 *dh = reinterpret_cast<uint4 *>(xhi + (size_t)r * d);
@@ -1714,6 +1782,7 @@ __global__ __launch_bounds__(256) void gemm1_col_kernel(
         consume(b1, s1, st + 1);
         load(b1, s1, min(st + 3, last));
     }
+    store_route();
 }
 
 // Workgroups that fit on the device at once for a 256-thread kernel with
@@ -1729,6 +1798,38 @@ static int persistent_grid(const void *kfn, size_t lds)
 }
 
 // ---- launchers ----------------------------------------------------------------
+
+// The streaming gate/up kernels (few tokens): whole tile columns when there
+// are enough of them for the device and the kernel's larger LDS fits, else
+// 16-feature items.  ROUTE: the kernel routes in its prologue.
+template <bool ROUTE>
+static hipError_t launch_stream_gate_up(const Shape &s, const Plan &p, const Workspace &ws,
+                                        const uint8_t *wpk, const uint8_t *sc, const RouteArgs &ra,
+                                        hipStream_t st, hipEvent_t ev0, hipEvent_t ev1)
+{
+    const int R = p.tile_rows;
+    const size_t lds = (size_t)R * (2 * s.d + 2 * (s.d / 32));
+    const int cgrid = stream_columns(s)
+                          ? persistent_grid(reinterpret_cast<const void *>(gemm1_col_kernel<ROUTE>), lds)
+                          : 0;
+    if (cgrid > 0) {
+        hipExtLaunchKernelGGL(gemm1_col_kernel<ROUTE>, dim3(cgrid), dim3(256), (uint32_t)lds, st, ev0, ev1, 0,
+                              (const uint8_t *)ws.xhi, (const uint8_t *)ws.xlo, (const uint8_t *)ws.xshi,
+                              (const uint8_t *)ws.xslo, ws.perm, ws.tiles, ws.ntiles, wpk, sc, ws.h, s.d,
+                              s.F, s.k, R, ra);
+        return hipGetLastError();
+    }
+    // a refused occupancy query must not surface as this launch's error
+    if (stream_columns(s)) (void)hipGetLastError();
+    auto kfn = gemm1_stream_kernel<kG1StreamU, false, ROUTE>;
+    const int grid = persistent_grid(reinterpret_cast<const void *>(kfn), lds);
+    if (grid <= 0) return hipErrorInvalidConfiguration;
+    hipExtLaunchKernelGGL(kfn, dim3(grid), dim3(256), (uint32_t)lds, st, ev0, ev1, 0,
+                          (const uint8_t *)ws.xhi, (const uint8_t *)ws.xlo, (const uint8_t *)ws.xshi,
+                          (const uint8_t *)ws.xslo, ws.perm, ws.tiles, ws.ntiles, wpk, sc, ws.h, s.d, s.F,
+                          s.k, R, (const float *)nullptr, (const float *)nullptr, ra);
+    return hipGetLastError();
+}
 
 hipError_t launch_gemm1(const Shape &s, const Plan &p, const Workspace &ws, const uint16_t *x,
                         const uint8_t *wpk, const uint8_t *sc, hipStream_t st, hipEvent_t ev0,
@@ -1753,32 +1854,9 @@ hipError_t launch_gemm1(const Shape &s, const Plan &p, const Workspace &ws, cons
             hipExtLaunchKernelGGL(gemm_mx_kernel<true>, grid, dim3(512), 0, st, ev0, ev1, 0, pa);
         }
     } else if (p.stream) {
-        const int R = p.tile_rows;
-        const size_t lds = (size_t)R * (2 * s.d + 2 * (s.d / 32));
-        // whole tile columns when there are enough of them for the device
-        // and the kernel's larger LDS fits (else the 16-feature items below)
-        const int cgrid = stream_columns(s)
-                              ? persistent_grid(reinterpret_cast<const void *>(gemm1_col_kernel), lds)
-                              : 0;
-        if (cgrid > 0) {
-            hipExtLaunchKernelGGL(gemm1_col_kernel, dim3(cgrid), dim3(256), (uint32_t)lds, st, ev0, ev1, 0,
-                                  (const uint8_t *)ws.xhi, (const uint8_t *)ws.xlo,
-                                  (const uint8_t *)ws.xshi, (const uint8_t *)ws.xslo,
-                                  (const int32_t *)ws.perm, (const Tile *)ws.tiles,
-                                  (const int32_t *)ws.ntiles, wpk, sc, ws.h, s.d, s.F, s.k, R);
-            return hipGetLastError();
-        }
-        // a refused occupancy query must not surface as this launch's error
-        if (stream_columns(s)) (void)hipGetLastError();
-        auto kfn = gemm1_stream_kernel<kG1StreamU, false>;
-        const int grid = persistent_grid(reinterpret_cast<const void *>(kfn), lds);
-        if (grid <= 0) return hipErrorInvalidConfiguration;
-        hipExtLaunchKernelGGL(kfn, dim3(grid), dim3(256), (uint32_t)lds, st, ev0, ev1, 0,
-                              (const uint8_t *)ws.xhi, (const uint8_t *)ws.xlo,
-                              (const uint8_t *)ws.xshi, (const uint8_t *)ws.xslo,
-                              (const int32_t *)ws.perm, (const Tile *)ws.tiles,
-                              (const int32_t *)ws.ntiles, wpk, sc, ws.h, s.d, s.F, s.k, R,
-                              (const float *)nullptr, (const float *)nullptr);
+        const RouteArgs ra{ws.scores, s.T, s.E, ws.ids, ws.wts, ws.counts, ws.offsets, ws.inv};
+        return p.fuse_route ? launch_stream_gate_up<true>(s, p, ws, wpk, sc, ra, st, ev0, ev1)
+                            : launch_stream_gate_up<false>(s, p, ws, wpk, sc, ra, st, ev0, ev1);
     } else {
         const int groups = s.F / 16;
         const int64_t grid = max_tiles(s, p.tile_rows) * groups;
@@ -1846,13 +1924,13 @@ hipError_t launch_gemm1_nv(const Shape &s, const Plan &p, const Workspace &ws, c
         const int R = p.tile_rows;
         if (R > 16) return hipErrorInvalidConfiguration;
         const size_t lds = (size_t)R * (2 * s.d + 2 * (s.d / 32));
-        auto kfn = gemm1_stream_kernel<kG1StreamU, true>;
+        auto kfn = gemm1_stream_kernel<kG1StreamU, true, false>;
         const int grid = persistent_grid(reinterpret_cast<const void *>(kfn), lds);
         if (grid <= 0) return hipErrorInvalidConfiguration;
         const uint8_t *xb = reinterpret_cast<const uint8_t *>(x);
         hipExtLaunchKernelGGL(kfn, dim3(grid), dim3(256), (uint32_t)lds, st, ev0, ev1, 0, xb, xb, xb,
-                              xb, (const int32_t *)ws.perm, (const Tile *)ws.tiles,
-                              (const int32_t *)ws.ntiles, wpk, sc, ws.h, s.d, s.F, s.k, R, xs, gs);
+                              xb, ws.perm, ws.tiles, ws.ntiles, wpk, sc, ws.h, s.d, s.F, s.k, R, xs, gs,
+                              RouteArgs{});
     } else {
         const int groups = s.F / 16;
         const int64_t grid = max_tiles(s, p.tile_rows) * groups;

@@ -109,12 +109,36 @@ constexpr int kTiledMinRows = 16;
 // to its loads, and a third stage keeps two chunks of weights in flight.
 constexpr int kShortTileMaxRows = 48;
 
+// Slots (T*k) up to which the streaming gate/up kernel routes a call in its
+// prologue (route_few) instead of a routing kernel running before it.  Every
+// workgroup routes, so the prologue's time is on the kernel's critical path:
+// at decode T=1 (8 slots) the step is 2.3 us shorter, at T=4 (32 slots) the
+// same as with the routing kernel.
+constexpr int kFewSlots = 16;
+
+// What a gate/up kernel that routes in its prologue reads (the router's
+// scores, one plane) and stores besides perm / tiles / ntiles (workgroup 0).
+struct RouteArgs {
+    const float *scores;
+    int T, E;
+    int32_t *ids;
+    float *wts;
+    int32_t *counts;
+    int32_t *offsets;
+    int32_t *inv;
+};
+
 struct Plan {
     bool tiled;
     bool stream;    // persistent streaming gate/up kernel (decode)
     int tile_rows;  // rows per tile of the tile list
     int ssq_cols;   // columns of o per partial sum of squares
     bool small_route;  // single-workgroup routing (T <= 64 and T*k <= 4096)
+    // the streaming gate/up kernel routes in its prologue (route_few, every
+    // workgroup alike; workgroup 0 stores the routing for the later kernels)
+    // and no routing kernel runs: streaming plans with T*k <= kFewSlots and
+    // E <= 256 (MXFP4 weights)
+    bool fuse_route;
     // tiled plans: the gate/up kernel's workgroups per tile and its launch
     // (the schedule the tile-list code writes, Sched)
     int ntn1;
@@ -174,6 +198,7 @@ inline Plan make_plan(const Shape &s)
     if (p.tile_rows < 1) p.tile_rows = 1;
     p.ssq_cols = 64;  // both down kernels reduce o^2 over 64-column groups
     p.small_route = s.T <= kChunkTokens && S <= 4096;
+    p.fuse_route = p.stream && S <= kFewSlots && s.E <= 256;
     p.ntn1 = p.grid1 = 0;
     // MXFP4 tiled gate/up kernel: pairs of 256-row weight tiles (wide) or single ones
     if (p.tiled) set_schedule(s, p, wide_gate_up(s) ? s.F / 256 : s.F / 128);
@@ -217,6 +242,7 @@ constexpr int kNvTileRows = 192;
 // weight tile per workgroup.
 inline void nv_plan(const Shape &s, Plan &p)
 {
+    p.fuse_route = false;  // the 16-block kernels read the routing kernel's tile list
     if (!p.tiled) return;
     p.tile_rows = kNvTileRows;
     set_schedule(s, p, s.F / 128);

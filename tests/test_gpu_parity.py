@@ -198,6 +198,47 @@ def test_few_tokens_hot_expert(T, d, E, k, F):
     _check_tokens(L, out, np.arange(T), f"hot T={T} d={d}")
 
 
+# (T, d, E, k, F) with T*k <= 16, E <= 256 and d % 2048 = 0: the gate/up
+# kernel routes in its prologue and no routing kernel runs.  16-feature items
+# (E <= 64: one score per lane; E = 200: a partial last score slot; E = 16,
+# T = 4: experts cut into two tiles) and whole tile columns (2, 256, 8, 2048).
+PROLOGUE_ROUTING = [(1, 2048, 256, 8, 512), (2, 2048, 256, 8, 256), (2, 4096, 64, 8, 256),
+                    (4, 2048, 16, 4, 256), (1, 2048, 8, 2, 256), (3, 2048, 200, 5, 384),
+                    (2, 2048, 256, 8, 2048)]
+
+
+@pytest.mark.parametrize("T,d,E,k,F", PROLOGUE_ROUTING)
+def test_prologue_routing(T, d, E, k, F):
+    w = synth.custom_workload(T=T, d=d, E=E, k=k, F=F, seed=41 + T * k + E, zipf=True)
+    wr = synth.make_router(w)
+    x = synth.make_tokens(w, wr)
+    W, S = synth.make_experts(w)
+    a, b = synth.make_gates(w)
+    L = synth.LayerInputs(w.shape, x, wr, W, S, a, b, w.shape.k)
+    _say("prologue routing", T, d, E, k, F)
+    out, dbg = run_layer(L)
+    _check_routing(L, dbg, f"prologue T={T} E={E} k={k}")
+    _check_tokens(L, out, np.arange(T), f"prologue T={T} E={E} k={k}")
+
+
+def test_prologue_routing_ties():
+    """Exact score ties on the prologue path: two experts with the same router
+    row are the top 2 of both tokens, the lower id first."""
+    w = synth.custom_workload(T=2, d=2048, E=16, k=2, F=256, seed=45, zipf=True)
+    wr = synth.make_router(w)
+    wr[:, 0] = 0.0
+    wr[11] = wr[6]
+    wr[6, 0] = wr[11, 0] = 50.0
+    x = synth.make_tokens(w, wr, gap=0)
+    W, S = synth.make_experts(w)
+    al, be = synth.make_gates(w)
+    L = synth.LayerInputs(w.shape, x, wr, W, S, al, be, w.shape.k)
+    out, dbg = run_layer(L)
+    r = _check_routing(L, dbg, "prologue ties")
+    assert np.all(r["ids"] == np.array((6, 11)))
+    _check_tokens(L, out, np.arange(2), "prologue ties")
+
+
 @pytest.mark.parametrize("E,pair", [(16, (3, 5)), (256, (7, 135)), (256, (9, 73))])
 def test_exact_score_ties(E, pair):
     """Two experts with the same router row score every token identically;
@@ -444,16 +485,18 @@ def _run_block(L, g_pre, g_post):
 
 # block cases beyond the named workloads: k = 24 on a tiled plan (the fused
 # combine + post-norm kernel's slot batches), k = 72 on a few-row plan (more
-# slots than the fused kernel takes: fp32 y, then the norm-and-gate kernel)
+# slots than the fused kernel takes: fp32 y, then the norm-and-gate kernel),
+# T = 1 (the gate/up kernel routes in its prologue)
 BLOCK_CUSTOM = {
     "k24": dict(T=40, d=256, E=32, k=24, F=128, seed=31),
     "k72": dict(T=24, d=256, E=128, k=72, F=128, seed=32),
+    "t1": dict(T=1, d=2048, E=64, k=8, F=256, seed=33),
 }
 
 
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("name,full", [("tiny", True), ("decode4", True), ("prefill", False),
-                                       ("k24", True), ("k72", True)])
+                                       ("k24", True), ("k72", True), ("t1", True)])
 def test_block_with_stream_norms(name, full):
     """Pre-norm into the block, post-norm into the gate, teacher-forced.
 
