@@ -1605,18 +1605,21 @@ __global__ __launch_bounds__(256) void gemm1_stream_kernel(
 // Few tokens over many experts (decode at T >= 2 with E = 256, k = 8): the
 // streaming gate/up kernel on whole weight tile columns.  An item is (tile,
 // weight tile nt): the gate and up rows of 128 features over all of K.  The
-// workgroup's 4 waves split it 2 x 2: wave w reads tile rows 128(w & 1) ..
-// +127 (the gate and up rows of 64 features: 8 KB contiguous a chunk) over
-// K half w >> 1, so the workgroup reads every 16 KB code tile and 1 KB scale
+// workgroup's 8 waves split it 4 x 2: wave w reads the gate and the up rows
+// of 32 features (quarter w & 3: two 2 KB runs of the tile a chunk) over K
+// half w >> 2, so the workgroup reads every 16 KB code tile and 1 KB scale
 // tile of its column whole and the chip's loads stay close together in
 // memory.  Measured on the address stream alone (no arithmetic), 540 MB at
 // decode T=4: 83 us this way against 92 us for 16-feature items.  One chunk
-// per batch, two batches in flight; x's FP8 parts staged in LDS per tile
-// (as gemm1_stream_kernel); the two K halves meet in LDS in a fixed order
-// and the first half's waves write h.  Tiles of at most R rows.
+// per batch, two batches in flight; with 4 row blocks a wave (116 VGPRs,
+// four waves per SIMD) a chunk's MFMAs hide behind the stream better than
+// with 8 on half as many waves (decode T=4 89.7 -> 86.8 us).  x's FP8 parts
+// staged in LDS per tile (as gemm1_stream_kernel); the two K halves meet in
+// LDS in a fixed order and the first half's waves write h.  Tiles of at most
+// R rows.
 // =========================================================================
 template <bool ROUTE>
-__global__ __launch_bounds__(256) void gemm1_col_kernel(
+__global__ __launch_bounds__(512) void gemm1_col_kernel(
     const uint8_t *__restrict__ ghi, const uint8_t *__restrict__ glo,
     const uint8_t *__restrict__ gsh, const uint8_t *__restrict__ gsl,
     int32_t *__restrict__ perm, Tile *__restrict__ tiles,
@@ -1624,16 +1627,16 @@ __global__ __launch_bounds__(256) void gemm1_col_kernel(
     const uint8_t *__restrict__ sc, uint16_t *__restrict__ h, int d, int F, int k, int R,
     const RouteArgs ra)
 {
-    constexpr int NB = 8;  // row blocks a wave: 4 gate, then the same 4 up
+    constexpr int NB = 4;  // row blocks a wave: 2 gate, then the same 2 up
     extern __shared__ uint4 xs4[];
-    __shared__ floatx4_t red[2][2][NB][64];  // [item parity][row half][block][lane]
+    __shared__ floatx4_t red[2][4][NB][64];  // [item parity][row quarter][block][lane]
     uint8_t *xs = reinterpret_cast<uint8_t *>(xs4);
     uint8_t *xhi = xs, *xlo = xs + (size_t)R * d;
     uint8_t *xsh = xs + (size_t)2 * R * d, *xsl = xsh + (size_t)R * (d / 32);
 
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int n = lane & 15, g = lane >> 4;
-    const int half = wv & 1, kh = wv >> 1;
+    const int quarter = wv & 3, kh = wv >> 2;
     const int cols = F / 128;  // items per tile
     // ROUTE: the call's routing, computed here (route_few) instead of read
     __shared__ typename std::conditional<ROUTE, FewRoute, char>::type fr;
@@ -1665,9 +1668,10 @@ __global__ __launch_bounds__(256) void gemm1_col_kernel(
     }
     const int ch = d / kKStep / 2;  // chunks per K half
     const int total = (i1 - i0) * ch;
-    // ---- weight loads: one chunk of the wave's 8 row blocks ----------------
-    // row block i of half h: packed rows 128h + 16i .. +15, i.e. feature
-    // 128nt + 64h + 16(i & 3) + n of the gate (i < 4) or up matrix
+    // ---- weight loads: one chunk of the wave's 4 row blocks ----------------
+    // row block i of quarter q: packed rows 128(q >> 1) + 32(q & 1) +
+    // 64(i >> 1) + 16(i & 1) .. +15, i.e. feature 128nt + 64(q >> 1) +
+    // 32(q & 1) + 16(i & 1) + n of the gate (i < 2) or up matrix
     uint4 b0[NB], b1[NB];
     uint32_t s0[NB], s1[NB];
     int l_ti = -1;
@@ -1682,7 +1686,7 @@ __global__ __launch_bounds__(256) void gemm1_col_kernel(
         const WView v = w1_view(wpk, sc, l_tl.expert, d, F);
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
-            const int rho = 128 * half + 16 * i + n;
+            const int rho = 128 * (quarter >> 1) + 32 * (quarter & 1) + 64 * (i >> 1) + 16 * (i & 1) + n;
             b[i] = ld_stream16(v.slot(nt, c, rho, g));
             sv[i] = ld_stream4(v.scales(nt, c, rho));
         }
@@ -1700,7 +1704,7 @@ __global__ __launch_bounds__(256) void gemm1_col_kernel(
             const uint4 *sl = reinterpret_cast<const uint4 *>(glo + tok * d);
             uint4 *dh = reinterpret_cast<uint4 *>(xhi + (size_t)r * d);
             uint4 *dl = reinterpret_cast<uint4 *>(xlo + (size_t)r * d);
-            for (int j = threadIdx.x; j < q; j += 256) {
+            for (int j = threadIdx.x; j < q; j += (int)blockDim.x) {
                 dh[j] = sh[j];
                 dl[j] = sl[j];
             }
@@ -1745,21 +1749,21 @@ __global__ __launch_bounds__(256) void gemm1_col_kernel(
             const int par = (it - i0) & 1;
             if (kh == 1) {
 #pragma unroll
-                for (int i = 0; i < NB; ++i) red[par][half][i][lane] = acc[i];
+                for (int i = 0; i < NB; ++i) red[par][quarter][i][lane] = acc[i];
             }
             lds_barrier();
             if (kh == 0) {
 #pragma unroll
-                for (int i = 0; i < NB; ++i) acc[i] += red[par][half][i][lane];
+                for (int i = 0; i < NB; ++i) acc[i] += red[par][quarter][i][lane];
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int fcol = nt * 128 + half * 64 + 16 * q + n;
+                for (int q = 0; q < 2; ++q) {
+                    const int fcol = nt * 128 + 64 * (quarter >> 1) + 32 * (quarter & 1) + 16 * q + n;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int row = g * 4 + r;
                         if (row < c_tl.nrows)
                             h[(int64_t)(c_tl.row0 + row) * F + fcol] =
-                                f32_to_bf16(silu(acc[q][r]) * acc[q + 4][r]);
+                                f32_to_bf16(silu(acc[q][r]) * acc[q + 2][r]);
                     }
                 }
             }
@@ -1785,14 +1789,14 @@ __global__ __launch_bounds__(256) void gemm1_col_kernel(
     store_route();
 }
 
-// Workgroups that fit on the device at once for a 256-thread kernel with
-// `lds` bytes of dynamic LDS (0 on error).  Queried on every call: nothing
+// Workgroups that fit on the device at once for a kernel of `threads`
+// threads with `lds` bytes of dynamic LDS (0 on error).  Queried on every call: nothing
 // is cached, so the library keeps no state between calls.
-static int persistent_grid(const void *kfn, size_t lds)
+static int persistent_grid(const void *kfn, size_t lds, int threads = 256)
 {
     int dev = 0, per_cu = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kfn, 256, lds) != hipSuccess) return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kfn, threads, lds) != hipSuccess) return 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
     return per_cu * cus;
 }
@@ -1810,10 +1814,10 @@ static hipError_t launch_stream_gate_up(const Shape &s, const Plan &p, const Wor
     const int R = p.tile_rows;
     const size_t lds = (size_t)R * (2 * s.d + 2 * (s.d / 32));
     const int cgrid = stream_columns(s)
-                          ? persistent_grid(reinterpret_cast<const void *>(gemm1_col_kernel<ROUTE>), lds)
+                          ? persistent_grid(reinterpret_cast<const void *>(gemm1_col_kernel<ROUTE>), lds, 512)
                           : 0;
     if (cgrid > 0) {
-        hipExtLaunchKernelGGL(gemm1_col_kernel<ROUTE>, dim3(cgrid), dim3(256), (uint32_t)lds, st, ev0, ev1, 0,
+        hipExtLaunchKernelGGL(gemm1_col_kernel<ROUTE>, dim3(cgrid), dim3(512), (uint32_t)lds, st, ev0, ev1, 0,
                               (const uint8_t *)ws.xhi, (const uint8_t *)ws.xlo, (const uint8_t *)ws.xshi,
                               (const uint8_t *)ws.xslo, ws.perm, ws.tiles, ws.ntiles, wpk, sc, ws.h, s.d,
                               s.F, s.k, R, ra);

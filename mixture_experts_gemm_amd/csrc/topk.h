@@ -200,8 +200,8 @@ __device__ __forceinline__ void topk_row(const float *__restrict__ l, int E, int
 
 // ---------------------------------------------------------------------------
 // The routing of a call with few slots (S = T*k <= kFewSlots, E <= 256,
-// T <= 64, the scores in one plane) by one workgroup of 256 threads, into
-// LDS: top-k and weights per token (topk_row, wave t % 4), then wave 0 with
+// T <= 64, the scores in one plane) by one workgroup (of whole waves), into
+// LDS: top-k and weights per token (topk_row, one wave a token), then wave 0 with
 // slot s in lane s: the stable grouping by expert (row of slot s: the slots
 // of lower experts, then the earlier slots of its own expert -- a token picks
 // an expert once, so that is token order) and the tile list (an expert's rows
@@ -223,8 +223,8 @@ struct FewRoute {
 __device__ __forceinline__ void route_few(const float *__restrict__ scores, int T, int E, int k,
                                           int tile_rows, FewRoute &r)
 {
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    for (int t = wv; t < T; t += 4) {
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, nw = (int)blockDim.x >> 6;
+    for (int t = wv; t < T; t += nw) {
         const float *l = scores + (int64_t)t * E;
         if (E <= 64) topk_row<1>(l, E, k, r.ids + t * k, r.wts + t * k, r.sid + t * k, lane, 1, (int64_t)T * E);
         else topk_row<4>(l, E, k, r.ids + t * k, r.wts + t * k, r.sid + t * k, lane, 1, (int64_t)T * E);
@@ -294,7 +294,7 @@ __device__ __forceinline__ void route_few_store(const FewRoute &r, int T, int E,
     }
     if (tid < r.ntiles) tiles[tid] = r.tiles[tid];
     if (tid == 0) *ntiles = r.ntiles;
-    for (int e = tid; e <= E; e += 256) {
+    for (int e = tid; e <= E; e += (int)blockDim.x) {
         int lo = 0, hi = S;  // first row of an expert >= e
         while (lo < hi) {
             const int mid = (lo + hi) >> 1;
