@@ -24,6 +24,24 @@ def test_exports_every_declared_function(L):
         assert hasattr(L, n), n
 
 
+def test_library_imports_no_allocator(L):
+    """No entry point allocates: the library imports no HIP allocation or
+    free routine at all (its workspace comes from the caller, or from the
+    static scratch array of the no-allocation entry point)."""
+    import shutil
+    import subprocess
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm not available")
+    out = subprocess.run([nm, "-D", "--undefined-only", B.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    imported = {line.split()[-1].split("@")[0] for line in out.splitlines() if line.strip()}
+    hip = sorted(n for n in imported if n.startswith("hip"))
+    assert hip, "no HIP imports found: not the HIP library?"
+    banned = [n for n in hip if "Malloc" in n or "Free" in n or "MemPool" in n or "HostRegister" in n]
+    assert not banned, banned
+
+
 def test_status_strings():
     for code in (0, -1, -2, -3, -4, -5, -6, -7):
         assert B.moe_status_string(code) and B.moe_status_string(code) != "unknown status"
