@@ -221,6 +221,25 @@ def test_prologue_routing(T, d, E, k, F):
     _check_tokens(L, out, np.arange(T), f"prologue T={T} E={E} k={k}")
 
 
+@pytest.mark.timeout(900)
+def test_large_d_column_fallback():
+    """d = 32768 at T = 2, E = 8, k = 8, F = 3072: whole tile columns would
+    be chosen (8 experts x 24 columns), but that kernel's staged rows and
+    partial sums (168 KB of LDS) do not fit a CU, so the launcher falls back
+    to the 16-feature streaming kernel (147 KB) without reporting the refused
+    occupancy query.  1.2 GB of expert weights."""
+    w = synth.custom_workload(T=2, d=32768, E=8, k=8, F=3072, seed=47, zipf=False)
+    wr = synth.make_router(w)
+    x = synth.make_tokens(w, wr)
+    W, S = synth.make_experts(w)
+    a, b = synth.make_gates(w)
+    L = synth.LayerInputs(w.shape, x, wr, W, S, a, b, w.shape.k)
+    _say("large d column fallback", w.shape.d)
+    out, dbg = run_layer(L)
+    _check_routing(L, dbg, "large d")
+    _check_tokens(L, out, np.arange(2), "large d")
+
+
 def test_prologue_routing_ties():
     """Exact score ties on the prologue path: two experts with the same router
     row are the top 2 of both tokens, the lower id first."""
