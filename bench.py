@@ -217,7 +217,7 @@ GATE_UP_KERNEL = {
     "latent_prefill": "gemm_mxw_kernel<true, 128> (gate/up + SwiGLU, 128x512 tiles, MX MFMA)",
     "block4": "gemm1_col_kernel (gate/up + SwiGLU, persistent, whole 128-feature tile columns, MX MFMA)",
     "block_prefill": "gemm_mxw_kernel<true, 128> (gate/up + SwiGLU, 128x512 tiles, MX MFMA)",
-    "nv4": "gemm1_stream_kernel<4, true> (gate/up + SwiGLU, persistent, fp16 MFMA, 16-block weights)",
+    "nv4": "gemm1_col_kernel<false, true> (gate/up + SwiGLU, persistent, whole 128-feature tile columns, fp16 MFMA, 16-block weights)",
     "nv_prefill": "gemm_nv_kernel<true> (gate/up + SwiGLU, 192x256 tiles, fp16 MFMA, 16-block weights)",
 }
 # How the gate/up kernel issues one bf16 x FP4 product on the matrix cores:

@@ -100,12 +100,13 @@ __device__ __forceinline__ floatx4_t mfma_chunk_nv(const uint4 *a, uint4 b, uint
 // and its scale is 2^-q.  Exact for every element down to 2^-32 of the row's
 // largest (fp16 keeps 11 significant bits, bf16 has 8); smaller ones round
 // to the fp16 subnormal grid.  One row of n 16-byte units by the whole
-// 256-thread workgroup (every thread calls it); dst may be global or LDS;
-// wmax is 4 words of LDS.  Returns the row's scale.
+// workgroup (every thread calls it); dst may be global or LDS; wmax is one
+// word of LDS per wave.  Returns the row's scale.
 __device__ float f16_row_block(const uint4 *__restrict__ s4, uint4 *d4, int n, uint32_t *wmax)
 {
+    const int nt = (int)blockDim.x, nw = nt >> 6;
     uint32_t mx = 0;
-    for (int i = threadIdx.x; i < n; i += 256) {
+    for (int i = threadIdx.x; i < n; i += nt) {
         const uint4 v = s4[i];
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -119,12 +120,13 @@ __device__ float f16_row_block(const uint4 *__restrict__ s4, uint4 *d4, int n, u
     for (int off = 32; off > 0; off >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, off));
     if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = mx;
     __syncthreads();
-    mx = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+    mx = wmax[0];
+    for (int w = 1; w < nw; ++w) mx = max(mx, wmax[w]);
     const int eb = (int)(mx >> 7);  // biased exponent of the largest magnitude
     int q = mx == 0 ? 0 : (eb == 0 ? 126 : 14 - (eb - 127));
     q = q > 126 ? 126 : q;
     const float f = pow2f(q);
-    for (int i = threadIdx.x; i < n; i += 256) {
+    for (int i = threadIdx.x; i < n; i += nt) {
         const uint4 v = s4[i];
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
         uint32_t o[4];
@@ -1618,18 +1620,25 @@ __global__ __launch_bounds__(256) void gemm1_stream_kernel(
 // LDS in a fixed order and the first half's waves write h.  Tiles of at most
 // R rows.
 // =========================================================================
-template <bool ROUTE>
+template <bool ROUTE, bool NV>
 __global__ __launch_bounds__(512) void gemm1_col_kernel(
     const uint8_t *__restrict__ ghi, const uint8_t *__restrict__ glo,
     const uint8_t *__restrict__ gsh, const uint8_t *__restrict__ gsl,
     int32_t *__restrict__ perm, Tile *__restrict__ tiles,
     int32_t *__restrict__ ntiles, const uint8_t *__restrict__ wpk,
     const uint8_t *__restrict__ sc, uint16_t *__restrict__ h, int d, int F, int k, int R,
-    const RouteArgs ra)
+    const float *__restrict__ gs, const RouteArgs ra)
 {
+    static_assert(!(NV && ROUTE), "the 16-block path reads the routing kernel's tile list");
     constexpr int NB = 4;  // row blocks a wave: 2 gate, then the same 2 up
     extern __shared__ uint4 xs4[];
     __shared__ floatx4_t red[2][4][NB][64];  // [item parity][row quarter][block][lane]
+    // NV: the E4M3 table, the per-wave maxima of the row conversion and the
+    // staged rows' scales (R <= 16, checked by the launcher)
+    __shared__ uint2 lut[NV ? 256 : 1];
+    __shared__ uint32_t wmax[8];
+    __shared__ float rsc[NV ? 16 : 1];
+    if constexpr (NV) fill_e4m3_table(lut);  // read after the first stage() barrier
     uint8_t *xs = reinterpret_cast<uint8_t *>(xs4);
     uint8_t *xhi = xs, *xlo = xs + (size_t)R * d;
     uint8_t *xsh = xs + (size_t)2 * R * d, *xsl = xsh + (size_t)R * (d / 32);
@@ -1683,12 +1692,14 @@ __global__ __launch_bounds__(512) void gemm1_col_kernel(
             l_tl = tile_at(ti);
             l_ti = ti;
         }
-        const WView v = w1_view(wpk, sc, l_tl.expert, d, F);
+        const WView v = NV ? w1_codes(wpk, l_tl.expert, d, F) : w1_view(wpk, sc, l_tl.expert, d, F);
+        const NvScales vs = w1_nv_scales(sc, l_tl.expert, d, F);
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
             const int rho = 128 * (quarter >> 1) + 32 * (quarter & 1) + 64 * (i >> 1) + 16 * (i & 1) + n;
             b[i] = ld_stream16(v.slot(nt, c, rho, g));
-            sv[i] = ld_stream4(v.scales(nt, c, rho));
+            if constexpr (NV) sv[i] = __builtin_nontemporal_load(vs.pair(nt, c, rho, g));
+            else sv[i] = ld_stream4(v.scales(nt, c, rho));
         }
     };
     // ---- activation staging: the tile's FP8 rows and scales -> LDS --------
@@ -1698,6 +1709,18 @@ __global__ __launch_bounds__(512) void gemm1_col_kernel(
         c_tl = tile_at(ti);
         c_ti = ti;
         const int q = d / 16, qs = d / 32 / 16;  // 16-byte units per part row / scale row
+        if constexpr (NV) {
+            // the bf16 rows (ghi) converted here (f16_row_block) into fp16
+            // rows of 2d bytes, the space of both FP8 parts, with their scales
+            for (int r = 0; r < c_tl.nrows; ++r) {
+                const int64_t tok = perm_at(c_tl.row0 + r) / k;
+                const float scr = f16_row_block(reinterpret_cast<const uint4 *>(ghi + tok * 2 * d),
+                                                reinterpret_cast<uint4 *>(xs + (size_t)r * 2 * d), 2 * q, wmax);
+                if (threadIdx.x == 0) rsc[r] = scr;
+            }
+            lds_barrier();
+            return;
+        }
         for (int r = 0; r < c_tl.nrows; ++r) {
             const int64_t tok = perm_at(c_tl.row0 + r) / k;
             const uint4 *sh = reinterpret_cast<const uint4 *>(ghi + tok * d);
@@ -1728,21 +1751,30 @@ __global__ __launch_bounds__(512) void gemm1_col_kernel(
         if (ti != c_ti) stage(ti);
         const int m = n < c_tl.nrows ? n : 0;  // rows past nrows are computed on row 0, never stored
         const int c = kh * ch + bt;
-        const uint4 *hp = reinterpret_cast<const uint4 *>(xhi + (size_t)m * d + c * kKStep);
-        const uint4 *lp = reinterpret_cast<const uint4 *>(xlo + (size_t)m * d + c * kKStep);
-        const uint4 h0 = hp[g], h1 = hp[4 + g], l0 = lp[g], l1 = lp[4 + g];
-        const int sidx = m * (d / 32) + c * 4 + g;
-        const uint32_t sah = xsh[sidx], sal = xsl[sidx];
-        // all hi products, then all lo products: no MFMA waits on the one
-        // before it (each block still adds hi before lo)
-        uint32_t sb[NB];
+        if constexpr (NV) {
+            // the lane's 32 fp16 activations of K block g; four fp16 MFMAs
+            // per row block on the weights expanded through the table
+            const uint4 *ap = reinterpret_cast<const uint4 *>(xs + (size_t)m * 2 * d) + c * (kKStep / 8) + g * 4;
+            const uint4 a[4] = {ap[0], ap[1], ap[2], ap[3]};
 #pragma unroll
-        for (int i = 0; i < NB; ++i) {
-            sb[i] = (sv[i] >> (8 * g)) & 0xFFu;
-            acc[i] = mfma_mx(h0, h1, b[i], sah, sb[i], acc[i]);
+            for (int i = 0; i < NB; ++i) acc[i] = mfma_chunk_nv(a, b[i], sv[i], lut, acc[i]);
+        } else {
+            const uint4 *hp = reinterpret_cast<const uint4 *>(xhi + (size_t)m * d + c * kKStep);
+            const uint4 *lp = reinterpret_cast<const uint4 *>(xlo + (size_t)m * d + c * kKStep);
+            const uint4 h0 = hp[g], h1 = hp[4 + g], l0 = lp[g], l1 = lp[4 + g];
+            const int sidx = m * (d / 32) + c * 4 + g;
+            const uint32_t sah = xsh[sidx], sal = xsl[sidx];
+            // all hi products, then all lo products: no MFMA waits on the one
+            // before it (each block still adds hi before lo)
+            uint32_t sb[NB];
+#pragma unroll
+            for (int i = 0; i < NB; ++i) {
+                sb[i] = (sv[i] >> (8 * g)) & 0xFFu;
+                acc[i] = mfma_mx(h0, h1, b[i], sah, sb[i], acc[i]);
+            }
+#pragma unroll
+            for (int i = 0; i < NB; ++i) acc[i] = mfma_mx(l0, l1, b[i], sal, sb[i], acc[i]);
         }
-#pragma unroll
-        for (int i = 0; i < NB; ++i) acc[i] = mfma_mx(l0, l1, b[i], sal, sb[i], acc[i]);
         if (bt == ch - 1) {
             // the item's two K halves meet: the second writes, the first adds
             // (one order) and stores h = silu(gate) * up
@@ -1761,9 +1793,15 @@ __global__ __launch_bounds__(512) void gemm1_col_kernel(
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int row = g * 4 + r;
-                        if (row < c_tl.nrows)
-                            h[(int64_t)(c_tl.row0 + row) * F + fcol] =
-                                f32_to_bf16(silu(acc[q][r]) * acc[q + 2][r]);
+                        if (row < c_tl.nrows) {
+                            float gv = acc[q][r], uv = acc[q + 2][r];
+                            if constexpr (NV) {
+                                const float xr = rsc[row];
+                                gv *= xr * gs[3 * c_tl.expert];
+                                uv *= xr * gs[3 * c_tl.expert + 1];
+                            }
+                            h[(int64_t)(c_tl.row0 + row) * F + fcol] = f32_to_bf16(silu(gv) * uv);
+                        }
                     }
                 }
             }
@@ -1814,13 +1852,13 @@ static hipError_t launch_stream_gate_up(const Shape &s, const Plan &p, const Wor
     const int R = p.tile_rows;
     const size_t lds = (size_t)R * (2 * s.d + 2 * (s.d / 32));
     const int cgrid = stream_columns(s)
-                          ? persistent_grid(reinterpret_cast<const void *>(gemm1_col_kernel<ROUTE>), lds, 512)
+                          ? persistent_grid(reinterpret_cast<const void *>(gemm1_col_kernel<ROUTE, false>), lds, 512)
                           : 0;
     if (cgrid > 0) {
-        hipExtLaunchKernelGGL(gemm1_col_kernel<ROUTE>, dim3(cgrid), dim3(512), (uint32_t)lds, st, ev0, ev1, 0,
-                              (const uint8_t *)ws.xhi, (const uint8_t *)ws.xlo, (const uint8_t *)ws.xshi,
+        hipExtLaunchKernelGGL(gemm1_col_kernel<ROUTE, false>, dim3(cgrid), dim3(512), (uint32_t)lds, st, ev0, ev1,
+                              0, (const uint8_t *)ws.xhi, (const uint8_t *)ws.xlo, (const uint8_t *)ws.xshi,
                               (const uint8_t *)ws.xslo, ws.perm, ws.tiles, ws.ntiles, wpk, sc, ws.h, s.d,
-                              s.F, s.k, R, ra);
+                              s.F, s.k, R, (const float *)nullptr, ra);
         return hipGetLastError();
     }
     // a refused occupancy query must not surface as this launch's error
@@ -1928,10 +1966,22 @@ hipError_t launch_gemm1_nv(const Shape &s, const Plan &p, const Workspace &ws, c
         const int R = p.tile_rows;
         if (R > 16) return hipErrorInvalidConfiguration;
         const size_t lds = (size_t)R * (2 * s.d + 2 * (s.d / 32));
+        const uint8_t *xb = reinterpret_cast<const uint8_t *>(x);
+        // whole tile columns when there are enough of them and the LDS fits
+        // (as for MXFP4 weights), else 16-feature items
+        const int cgrid = stream_columns(s)
+                              ? persistent_grid(reinterpret_cast<const void *>(gemm1_col_kernel<false, true>), lds, 512)
+                              : 0;
+        if (cgrid > 0) {
+            hipExtLaunchKernelGGL(gemm1_col_kernel<false, true>, dim3(cgrid), dim3(512), (uint32_t)lds, st, ev0,
+                                  ev1, 0, xb, xb, xb, xb, ws.perm, ws.tiles, ws.ntiles, wpk, sc, ws.h, s.d, s.F,
+                                  s.k, R, gs, RouteArgs{});
+            return hipGetLastError();
+        }
+        if (stream_columns(s)) (void)hipGetLastError();
         auto kfn = gemm1_stream_kernel<kG1StreamU, true, false>;
         const int grid = persistent_grid(reinterpret_cast<const void *>(kfn), lds);
         if (grid <= 0) return hipErrorInvalidConfiguration;
-        const uint8_t *xb = reinterpret_cast<const uint8_t *>(x);
         hipExtLaunchKernelGGL(kfn, dim3(grid), dim3(256), (uint32_t)lds, st, ev0, ev1, 0, xb, xb, xb,
                               xb, ws.perm, ws.tiles, ws.ntiles, wpk, sc, ws.h, s.d, s.F, s.k, R, xs, gs,
                               RouteArgs{});
