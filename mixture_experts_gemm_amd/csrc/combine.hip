@@ -23,6 +23,9 @@ constexpr int kCombineCols = 2048;  // columns per workgroup (8 per thread)
 
 // SLOT: o and the o^2 partial sums are stored in slot order (row t*k + j is
 // slot j of token t); otherwise in the grouped order, found through inv.
+// o is read once, by non-temporal loads, so it does not displace the x,
+// alpha and beta slices the workgroups share in L2 (prefill combine
+// 135.5 -> 124.2 us).
 // OUT: kOutGate s_out = bf16(alpha * x + beta * y); kOutBf16 s_out = bf16(y)
 // (the latent-width variant widens y before its gate); kOutF32 y_out = y
 // (the block variant normalises y before its gate).
@@ -65,7 +68,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SLOT ? 1 : 
         uint4 ov[kSlotBatch];
 #pragma unroll
         for (int j = 0; j < kSlotBatch; ++j)
-            ov[j] = act && j < k ? *reinterpret_cast<const uint4 *>(o + ((int64_t)t * k + j) * d + c0)
+            ov[j] = act && j < k ? ld_stream16(o + ((int64_t)t * k + j) * d + c0)
                                  : make_uint4(0, 0, 0, 0);
         // 16 lanes per slot; lane l of slot j adds partials l, l+16, ... in
         // that order (loads at a clamped index, masked after, so they are
@@ -97,7 +100,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SLOT ? 1 : 
         if constexpr (SLOT) {
 #pragma unroll
             for (int j = 0; j < kSlotBatch; ++j)
-                ov[j] = act && j < kk ? *reinterpret_cast<const uint4 *>(o + ((int64_t)t * k + j0 + j) * d + c0)
+                ov[j] = act && j < kk ? ld_stream16(o + ((int64_t)t * k + j0 + j) * d + c0)
                                       : make_uint4(0, 0, 0, 0);
         }
         __syncthreads();
@@ -132,7 +135,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SLOT ? 1 : 
                     if (j < kk) accumulate(ov[j], coef[j]);
             } else {
                 for (int j = 0; j < kk; ++j)
-                    accumulate(*reinterpret_cast<const uint4 *>(o + (int64_t)row[j] * d + c0), coef[j]);
+                    accumulate(ld_stream16(o + (int64_t)row[j] * d + c0), coef[j]);
             }
         }
     }
@@ -355,7 +358,7 @@ __global__ __launch_bounds__(NT) void combine_postnorm_kernel(
             uint4 ov[kSlotBatch];
 #pragma unroll
             for (int jj = 0; jj < kSlotBatch; ++jj)
-                ov[jj] = *reinterpret_cast<const uint4 *>(o + (int64_t)row[min(j0 + jj, k - 1)] * d + c0);
+                ov[jj] = ld_stream16(o + (int64_t)row[min(j0 + jj, k - 1)] * d + c0);
 #pragma unroll
             for (int jj = 0; jj < kSlotBatch; ++jj) {
                 if (j0 + jj >= k) break;
