@@ -158,11 +158,14 @@ def test_nv_full_size(name):
     _check_tokens(L, out, parity_tokens(L.shape.T, dbg, L.shape.k, 192, n=n, seed=7), "nv " + name)
 
 
-@pytest.mark.parametrize("T,d", [(3, 2048), (8, 4096)])
-def test_nv_few_tokens_hot_expert(T, d):
-    # every token picks expert 3 first: on the streaming gate/up kernel its
+# (T, d, E, k, F): E = 16 runs the 16-feature streaming kernel; E = 256,
+# k = 8 the whole-column kernel (712 and 256 column items; F/128 odd)
+@pytest.mark.parametrize("T,d,E,k,F", [(3, 2048, 16, 4, 256), (8, 4096, 16, 4, 256),
+                                       (6, 2048, 256, 8, 2048), (3, 4096, 256, 8, 1408)])
+def test_nv_few_tokens_hot_expert(T, d, E, k, F):
+    # every token picks expert 3 first: on the streaming gate/up kernels its
     # segment is cut into several 2-row tiles
-    w = synth.custom_workload(T=T, d=d, E=16, k=4, F=256, seed=43 + T, zipf=True)
+    w = synth.custom_workload(T=T, d=d, E=E, k=k, F=F, seed=43 + T, zipf=True)
     L = synth.make_layer_nv(w, with_tokens=False)
     L.router_w[:, 0] = 0.0
     L.router_w[3, 0] = 50.0
