@@ -71,6 +71,43 @@ int main()
                     }
     // the sweep reaches the 64-row tiles of shapes with few rows per expert
     if (short_cases == 0) return fail("no 64-row plan in the sweep", 0, 0, 0);
-    std::printf("ok %ld (%ld with 64-row tiles)\n", cases, short_cases);
+
+    // few-token plans: the gate/up kernel routes in its prologue only on a
+    // streaming plan with at most kFewSlots slots and 256 experts, reading
+    // one score plane, never for the 16-block weights; whole tile columns
+    // only with an even number of chunks per K half (the column kernel's
+    // loads assume it); and the decode thresholds the kernels were measured
+    // on (E = 256, k = 8, F = 2048, d = 8192: 16-feature items at T = 1,
+    // whole columns from T = 2)
+    long few_cases = 0, fused = 0;
+    for (int T = 1; T <= 64; ++T)
+        for (int d : {256, 2048, 4096, 6144, 8192})
+            for (int E : {8, 16, 64, 200, 256, 512})
+                for (int k : {1, 2, 4, 8, 16})
+                    for (int F : {256, 384, 1408, 2048}) {
+                        if (k > E) continue;
+                        Shape s{T, d, E, F, k, 1e-6f};
+                        Plan p = make_plan(s);
+                        if (p.fuse_route) {
+                            if (!p.stream || !p.small_route || s.S() > kFewSlots || E > 256)
+                                return fail("prologue routing outside its limits", T, d, E);
+                            if (router_splits(s) != 1) return fail("prologue routing on split scores", T, d, E);
+                            ++fused;
+                        }
+                        Plan q = p;
+                        nv_plan(s, q);
+                        if (q.fuse_route) return fail("16-block plan routes in the prologue", T, d, E);
+                        if (p.stream && stream_columns(s) && (d / 128 / 2) % 2 != 0)  // 128-wide K chunks
+                            return fail("whole columns with an odd chunk count per K half", T, d, E);
+                        ++few_cases;
+                    }
+    if (fused == 0) return fail("no prologue-routing plan in the sweep", 0, 0, 0);
+    for (int T = 1; T <= 8; ++T) {
+        Shape s{T, 8192, 256, 2048, 8, 1e-6f};
+        if (stream_columns(s) != (T >= 2)) return fail("decode column threshold", T, 8192, 256);
+        if (make_plan(s).fuse_route != (T * 8 <= kFewSlots)) return fail("decode prologue routing", T, 8192, 256);
+    }
+    std::printf("ok %ld (%ld with 64-row tiles; %ld few-token plans, %ld routing in the prologue)\n", cases,
+                short_cases, few_cases, fused);
     return 0;
 }

@@ -1,7 +1,9 @@
-"""The tiled gate/up kernel's work schedule, on the CPU: the item <-> workgroup
-maps of csrc/internal.h are exact inverses, leave no item out and none
+"""The plans of csrc/internal.h, on the CPU: the tiled gate/up kernel's
+item <-> workgroup maps are exact inverses, leave no item out and none
 twice, stay inside the launch and the workspace for every plan, and keep the
-eight XCDs' shares within one last-round share (host build of
+eight XCDs' shares within one last-round share; the few-token plans route in
+the gate/up kernel's prologue only within its limits and choose whole tile
+columns only where that kernel's loads hold (host build of
 tests/sched/sched_check.cpp, with UBSan on the host pass)."""
 import os
 import subprocess
