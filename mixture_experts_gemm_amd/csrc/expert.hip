@@ -307,18 +307,24 @@ __global__ __launch_bounds__(256) void gemm1_decode_kernel(
 // order), as gemm1_decode_kernel; with fuse, h is the bf16 rows and each
 // workgroup converts its tile's rows into LDS itself (f16_row_block; every
 // tile's rows must fit: rows_fit >= its rows).
-template <int U, bool NV>
-__global__ __launch_bounds__(256) void gemm2_decode_kernel(
+// KS = 2: 8 waves, the four column blocks over two K halves each (twice the
+// loads in flight a workgroup: the few-row down product waits on load
+// latency, not bandwidth); the halves meet in LDS in a fixed order and the
+// first half's waves store.
+template <int U, bool NV, int KS = 1>
+__global__ __launch_bounds__(256 * KS) void gemm2_decode_kernel(
     const uint16_t *__restrict__ h, const int32_t *__restrict__ perm, const Tile *__restrict__ tiles,
     const int32_t *__restrict__ ntiles, const uint8_t *__restrict__ wpk,
     const uint8_t *__restrict__ sc, uint16_t *__restrict__ o, float *__restrict__ ssq, int d,
     int F, int wgs_per_tile, int rows_fit, const float *__restrict__ hs, const float *__restrict__ gs,
     bool fuse)
 {
+    static_assert(KS == 1 || KS == 2, "one or two K parts");
     extern __shared__ uint4 arows[];  // [rows_fit][F/8]
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int cw = KS > 1 ? wv & 3 : wv, kh = KS > 1 ? wv >> 2 : 0;
     const int64_t tile = blockIdx.x / wgs_per_tile;
-    const int col0 = ((int)(blockIdx.x % wgs_per_tile) * 4 + wv) * 16;
+    const int col0 = ((int)(blockIdx.x % wgs_per_tile) * 4 + cw) * 16;
     if (tile >= *ntiles) return;
     const Tile tl = tiles[tile];
     const int n = lane & 15, g = lane >> 4;
@@ -329,12 +335,13 @@ __global__ __launch_bounds__(256) void gemm2_decode_kernel(
     const bool use_lds = tl.nrows <= rows_fit;
     const int rowq = F / 8;
     const int nc = F / kKStep;
+    const int c_lo = kh * nc / KS, c_hi = (kh + 1) * nc / KS;  // the wave's chunks
     uint4 b[U];
     uint32_t sw[U];
     auto load_b = [&](int c) {
 #pragma unroll
         for (int u = 0; u < U; ++u)
-            if (c + u < nc) {
+            if (c + u < c_hi) {
                 b[u] = ld_stream16(v.slot(nt, c + u, rho, g));
                 if constexpr (NV)
                     sw[u] = __builtin_nontemporal_load(vs.pair(nt, c + u, rho, g));
@@ -342,7 +349,7 @@ __global__ __launch_bounds__(256) void gemm2_decode_kernel(
                     sw[u] = ld_stream4(v.scales(nt, c + u, rho));
             }
     };
-    load_b(0);
+    load_b(c_lo);
     // destination slots of the lane's 4 output rows and of the row whose
     // o^2 sum this thread stores; in flight with the weights
     int dst[4];
@@ -350,7 +357,7 @@ __global__ __launch_bounds__(256) void gemm2_decode_kernel(
     for (int r = 0; r < 4; ++r) dst[r] = g * 4 + r < tl.nrows ? perm[tl.row0 + g * 4 + r] : 0;
     const int dst_ss = (int)threadIdx.x < tl.nrows && threadIdx.x < 16 ? perm[tl.row0 + threadIdx.x] : 0;
     __shared__ uint2 lut[NV ? 256 : 1];
-    __shared__ uint32_t wmax[4];
+    __shared__ uint32_t wmax[4 * KS];
     __shared__ float rsc[16];
     if constexpr (NV) fill_e4m3_table(lut);
     if (NV && fuse) {
@@ -361,17 +368,17 @@ __global__ __launch_bounds__(256) void gemm2_decode_kernel(
         }
     } else if (use_lds) {
         const uint4 *src = reinterpret_cast<const uint4 *>(h + (int64_t)tl.row0 * F);
-        for (int q = threadIdx.x; q < tl.nrows * rowq; q += 256) arows[q] = src[q];
+        for (int q = threadIdx.x; q < tl.nrows * rowq; q += 256 * KS) arows[q] = src[q];
     }
     if (NV || use_lds) __syncthreads();
     const uint16_t *ap = h + (int64_t)(tl.row0 + (valid ? n : 0)) * F + g * 32;
     const uint4 *al = arows + n * rowq + g * 4;
 
     floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
-    for (int c = 0; c < nc; c += U) {
+    for (int c = c_lo; c < c_hi; c += U) {
 #pragma unroll
         for (int u = 0; u < U; ++u)
-            if (c + u < nc) {
+            if (c + u < c_hi) {
                 uint4 a[4];
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
@@ -384,7 +391,16 @@ __global__ __launch_bounds__(256) void gemm2_decode_kernel(
                 else
                     acc = mfma_chunk(a, b[u], e8m0_to_f32((sw[u] >> (8 * g)) & 0xFFu), acc);
             }
-        if (c + U < nc) load_b(c + U);
+        if (c + U < c_hi) load_b(c + U);
+    }
+    if constexpr (KS > 1) {
+        __shared__ floatx4_t red[KS - 1][4][64];
+        if (kh > 0) red[kh - 1][cw][lane] = acc;
+        __syncthreads();
+        if (kh == 0) {
+#pragma unroll
+            for (int j = 0; j < KS - 1; ++j) acc += red[j][cw][lane];
+        }
     }
     // sum of o^2 over the workgroup's 64 columns: per wave over its block
     // (DPP within 16-lane rows), then the four waves in LDS in a fixed order
@@ -392,17 +408,19 @@ __global__ __launch_bounds__(256) void gemm2_decode_kernel(
     const int P = d / 64;
     float gd = 1.0f;
     if constexpr (NV) gd = gs[3 * tl.expert + 2];
+    if (kh == 0) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int row = g * 4 + r;
-        float val = acc[r];
-        if constexpr (NV) {
-            const int rr = row < tl.nrows ? row : 0;
-            val *= (fuse ? rsc[rr] : hs[tl.row0 + rr]) * gd;
+        for (int r = 0; r < 4; ++r) {
+            const int row = g * 4 + r;
+            float val = acc[r];
+            if constexpr (NV) {
+                const int rr = row < tl.nrows ? row : 0;
+                val *= (fuse ? rsc[rr] : hs[tl.row0 + rr]) * gd;
+            }
+            if (row < tl.nrows) o[(int64_t)dst[r] * d + col0 + n] = f32_to_bf16(val);
+            const float ss = sum16(val * val);
+            if (n == 0) wsum[cw][g * 4 + r] = ss;
         }
-        if (row < tl.nrows) o[(int64_t)dst[r] * d + col0 + n] = f32_to_bf16(val);
-        const float ss = sum16(val * val);
-        if (n == 0) wsum[wv][g * 4 + r] = ss;
     }
     __syncthreads();
     if (threadIdx.x < 16 && (int)threadIdx.x < tl.nrows) {
@@ -1938,7 +1956,7 @@ hipError_t launch_gemm2(const Shape &s, const Plan &p, const Workspace &ws, cons
         rows_fit = rows_fit < s.T ? rows_fit : s.T;
         if (rows_fit > 16) rows_fit = 16;
         const size_t lds = (size_t)rows_fit * s.F * 2;
-        gemm2_decode_kernel<kDownU, false><<<(unsigned)grid, 256, lds, st>>>(
+        gemm2_decode_kernel<kDownU, false, 2><<<(unsigned)grid, 512, lds, st>>>(
             ws.h, ws.perm, ws.tiles, ws.ntiles, wpk, sc, ws.o, ws.ssq, s.d, s.F, wgs, rows_fit,
             nullptr, nullptr, false);
     }
